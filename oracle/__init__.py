@@ -74,6 +74,12 @@ def _bind(lib):
     lib.orc_padding_rows.restype = i64
     lib.orc_ffn_rows.argtypes = [i64, vp, vp, i32, i32, i32, vp, vp, vp, vp]
     lib.orc_ffn_rows.restype = i32
+    lib.orc_ffn_rows_ex.argtypes = [i64, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp]
+    lib.orc_bf16_toward_n.argtypes = [i64, vp, vp, vp]
+    lib.orc_bf16_toward_n.restype = None
+    lib.orc_ffn_rows_ex.restype = i32
+    lib.orc_round_bf16_n.argtypes = [i64, vp, vp]
+    lib.orc_round_bf16_n.restype = None
     lib.orc_deliver.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
     lib.orc_deliver.restype = i32
     lib.orc_combine.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp]
@@ -167,6 +173,55 @@ def ffn_rows(src_row, expert, x, w_gate_up, w_down, is_bf16: bool, lib=None) -> 
     if rc != 0:
         raise ValueError("orc_ffn_rows failed")
     return y
+
+
+def ffn_rows_ex(src_row, expert, x, w_gate_up, w_down, is_bf16: bool, max_cand: int = 64, want_h: bool = False,
+                lib=None) -> dict:
+    """FFN rows plus, in bf16 mode, the roundings of h that an fp32 evaluation does not decide.
+
+    Returns y (float64 [n, d], rounded as the path rounds), y_unr (y before its final rounding), y_delta (bound
+    of an fp32 evaluation's error in y_unr), optionally h (the rounded hidden rows [n, f]), and per row
+    up to ``max_cand`` alternative roundings: cand_count [n], cand_n [n, max_cand] (hidden index),
+    cand_vec [n, max_cand, d] (exact change of y_unr when h takes the other bf16 candidate).
+    """
+    lib = lib or load()
+    src_row = np.ascontiguousarray(src_row, dtype=np.int32)
+    expert = np.ascontiguousarray(expert, dtype=np.int32)
+    x = np.ascontiguousarray(x)
+    w_gate_up = np.ascontiguousarray(w_gate_up)
+    w_down = np.ascontiguousarray(w_down)
+    d = x.shape[1]
+    f = w_down.shape[2]
+    n = src_row.size
+    out = {"y": np.empty((n, d)), "y_unr": np.empty((n, d)), "cand_count": np.zeros(n, np.int32),
+           "cand_n": np.zeros((n, max_cand), np.int32), "cand_vec": np.zeros((n, max_cand, d)),
+           "y_delta": np.empty((n, d))}
+    if want_h:
+        out["h"] = np.empty((n, f))
+    rc = lib.orc_ffn_rows_ex(n, _p(src_row), _p(expert), d, f, int(is_bf16), _p(x), _p(w_gate_up), _p(w_down),
+                             _p(out["y"]), _p(out["y_unr"]), max_cand, _p(out["cand_count"]), _p(out["cand_n"]),
+                             _p(out["cand_vec"]), _p(out["h"]) if want_h else None, _p(out["y_delta"]))
+    if rc != 0:
+        raise ValueError("orc_ffn_rows_ex failed")
+    return out
+
+
+def round_bf16_array(a: np.ndarray, lib=None) -> np.ndarray:
+    lib = lib or load()
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    out = np.empty_like(a)
+    lib.orc_round_bf16_n(a.size, _p(a), _p(out))
+    return out
+
+
+def bf16_toward(h: np.ndarray, v: np.ndarray, lib=None) -> np.ndarray:
+    """The bf16 neighbour of each bf16 value h in the direction of v (h where v == h)."""
+    lib = lib or load()
+    h = np.ascontiguousarray(h, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty_like(h)
+    lib.orc_bf16_toward_n(h.size, _p(h), _p(v), _p(out))
+    return out
 
 
 def ffn_layout(lay: dict, x, w_gate_up, w_down, is_bf16: bool, M: int, lib=None) -> np.ndarray:

@@ -269,40 +269,127 @@ static inline double orc_ld(const void* p, int64_t i, int is_bf16) {
   return is_bf16 ? orc_bf16_to_double(((const uint16_t*)p)[i]) : (double)((const float*)p)[i];
 }
 
-int orc_ffn_rows(int64_t nrows, const int32_t* src_row, const int32_t* expert, int d, int f, int is_bf16,
-                 const void* x, const void* w_gate_up, const void* w_down, double* y_out) {
+/* The bf16 value next to bf16 value h, above (up = 1) or below (up = 0). */
+static double orc_bf16_step(double h, int up) {
+  uint16_t b = orc_bf16_bits(h);
+  if (h == 0.0) b = up ? 0x0001 : 0x8001;
+  else if ((h > 0.0) == (up != 0)) b = (uint16_t)(b + 1);
+  else b = (uint16_t)(b - 1);
+  return orc_bf16_to_double(b);
+}
+
+typedef struct {
+  double ratio; /* sort key */
+  int n;
+  double dh;    /* other bf16 candidate minus the rounded h */
+} orc_cand;
+
+static int orc_cand_cmp(const void* a, const void* b) {
+  double x = ((const orc_cand*)a)->ratio, y = ((const orc_cand*)b)->ratio;
+  return (x > y) - (x < y);
+}
+
+/*
+ * orc_ffn_rows_ex: as orc_ffn_rows, and in bf16 mode also reports where rounding h to bf16 is not decided
+ * by the kernel's fp32 arithmetic.  An fp32 evaluation of h_n = silu(g_n) u_n differs from the exact value
+ * by accumulated rounding; its bound here is
+ *   delta_n = 2^-21 sqrt(d) (|silu'(g_n) u_n| Qg_n + |silu(g_n)| Qu_n) + 2^-20 |h_n|,
+ * Qg_n = sqrt(sum_c (x_c Wg[n][c])^2) and likewise Qu_n.  The first term bounds the rounding error of a
+ * d-term fp32 sum: each addition errs by at most 2^-24 of its partial sum, the errors add like a random
+ * walk, so their sum has a standard deviation near 0.4 * 2^-24 sqrt(d) Q; the bound is some twenty
+ * standard deviations.  The second term allows for the evaluation of silu and the product.
+ * When the exact h_n is within delta_n of the midpoint between its bf16 rounding and the neighbouring bf16
+ * value, either rounding is a correct result; the row then lists n, the step dh to the other candidate
+ * and the resulting change of y, dh * Wd[e][:, n], exactly.  Up to max_cand candidates per row are kept,
+ * largest |dh| first.  y_unr receives y before its final rounding; h_out (optional, [nrows][f]) the
+ * rounded hidden row; y_delta (optional, [nrows][d]) the same kind of bound for the fp32 evaluation of y
+ * itself, 2^-21 sqrt(f) Qy_m + 2^-22 |y_m| with Qy_m = sqrt(sum_n (h_n Wd[e][m][n])^2): where y_unr lies
+ * within y_delta of a bf16 rounding midpoint, both neighbouring bf16 values are correct results for y.
+ */
+int orc_ffn_rows_ex(int64_t nrows, const int32_t* src_row, const int32_t* expert, int d, int f, int is_bf16,
+                    const void* x, const void* w_gate_up, const void* w_down, double* y_out, double* y_unr,
+                    int max_cand, int32_t* cand_count, int32_t* cand_n, double* cand_vec, double* h_out,
+                    double* y_delta) {
   if (nrows < 0 || d <= 0 || f <= 0) return -1;
 #pragma omp parallel
   {
     double* xr = (double*)malloc(sizeof(double) * (size_t)d);
     double* h = (double*)malloc(sizeof(double) * (size_t)f);
+    orc_cand* cands = (orc_cand*)malloc(sizeof(orc_cand) * (size_t)f);
 #pragma omp for schedule(dynamic, 1)
     for (int64_t i = 0; i < nrows; ++i) {
       const int64_t tok = src_row[i];
       const int64_t e = expert[i];
+      int nc = 0;
       for (int c = 0; c < d; ++c) xr[c] = orc_ld(x, tok * d + c, is_bf16);
       const int64_t wg0 = e * 2 * (int64_t)f * d;          /* gate row 0 of expert e */
       const int64_t wu0 = wg0 + (int64_t)f * d;            /* up row 0 */
       for (int n = 0; n < f; ++n) {
-        double g = 0.0, u = 0.0;
+        double g = 0.0, u = 0.0, qg = 0.0, qu = 0.0;
         for (int c = 0; c < d; ++c) {
-          g += xr[c] * orc_ld(w_gate_up, wg0 + (int64_t)n * d + c, is_bf16);
-          u += xr[c] * orc_ld(w_gate_up, wu0 + (int64_t)n * d + c, is_bf16);
+          const double tg = xr[c] * orc_ld(w_gate_up, wg0 + (int64_t)n * d + c, is_bf16);
+          const double tu = xr[c] * orc_ld(w_gate_up, wu0 + (int64_t)n * d + c, is_bf16);
+          g += tg;
+          u += tu;
+          qg += tg * tg;
+          qu += tu * tu;
         }
-        double hv = (g / (1.0 + exp(-g))) * u;
-        h[n] = is_bf16 ? orc_round_bf16(hv) : hv;
+        const double hv = (g / (1.0 + exp(-g))) * u;         /* silu(g) u */
+        if (!is_bf16) {
+          h[n] = hv;
+          continue;
+        }
+        h[n] = orc_round_bf16(hv);
+        if (cand_count != NULL && hv != h[n]) {
+          const double sg = 1.0 / (1.0 + exp(-g)); /* sigmoid; silu'(g) = sg (1 + g (1 - sg)) */
+          const double dsilu = sg * (1.0 + g * (1.0 - sg));
+          const double delta = ldexp(sqrt((double)d) * (fabs(dsilu * u) * sqrt(qg) + fabs(g * sg) * sqrt(qu)), -21) +
+                               ldexp(fabs(hv), -20);
+          const double other = orc_bf16_step(h[n], hv > h[n]);
+          const double margin = fabs(hv - 0.5 * (h[n] + other));
+          if (margin <= delta) {
+            cands[nc].ratio = -fabs(other - h[n]); /* sort key: largest step first */
+            cands[nc].n = n;
+            cands[nc].dh = other - h[n];
+            ++nc;
+          }
+        }
       }
+      if (h_out != NULL) memcpy(h_out + i * (int64_t)f, h, sizeof(double) * (size_t)f);
       const int64_t wd0 = e * (int64_t)d * f;
       for (int m = 0; m < d; ++m) {
-        double acc = 0.0;
-        for (int n = 0; n < f; ++n) acc += h[n] * orc_ld(w_down, wd0 + (int64_t)m * f + n, is_bf16);
+        double acc = 0.0, qy = 0.0;
+        for (int n = 0; n < f; ++n) {
+          const double t = h[n] * orc_ld(w_down, wd0 + (int64_t)m * f + n, is_bf16);
+          acc += t;
+          qy += t * t;
+        }
+        if (y_unr != NULL) y_unr[i * d + m] = acc;
+        if (y_delta != NULL) y_delta[i * d + m] = ldexp(sqrt((double)f) * sqrt(qy), -21) + ldexp(fabs(acc), -22);
         y_out[i * d + m] = is_bf16 ? orc_round_bf16(acc) : acc;
+      }
+      if (cand_count != NULL) {
+        if (nc > max_cand) qsort(cands, (size_t)nc, sizeof(orc_cand), orc_cand_cmp);
+        if (nc > max_cand) nc = max_cand;
+        cand_count[i] = nc;
+        for (int q = 0; q < nc; ++q) {
+          cand_n[i * max_cand + q] = cands[q].n;
+          double* v = cand_vec + ((int64_t)i * max_cand + q) * d;
+          for (int m = 0; m < d; ++m) v[m] = cands[q].dh * orc_ld(w_down, wd0 + (int64_t)m * f + cands[q].n, is_bf16);
+        }
       }
     }
     free(xr);
     free(h);
+    free(cands);
   }
   return 0;
+}
+
+int orc_ffn_rows(int64_t nrows, const int32_t* src_row, const int32_t* expert, int d, int f, int is_bf16,
+                 const void* x, const void* w_gate_up, const void* w_down, double* y_out) {
+  return orc_ffn_rows_ex(nrows, src_row, expert, d, f, is_bf16, x, w_gate_up, w_down, y_out, NULL, 0, NULL, NULL,
+                         NULL, NULL, NULL);
 }
 
 /* ------------------------------------------------------------------------------------------------ */
@@ -343,4 +430,14 @@ int orc_combine(int R, int T_o, int k, int d, int is_bf16, const int32_t* plan, 
         for (int c = 0; c < d; ++c) o[c] = orc_round_bf16(o[c]);
     }
   return 0;
+}
+
+/* out[i] = bf16 rounding of in[i], i < n */
+void orc_round_bf16_n(int64_t n, const double* in, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_round_bf16(in[i]);
+}
+
+/* Neighbouring bf16 value of bf16 value h toward v (h itself if v == h). */
+void orc_bf16_toward_n(int64_t n, const double* h, const double* v, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = v[i] == h[i] ? h[i] : orc_bf16_step(h[i], v[i] > h[i]);
 }
