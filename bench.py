@@ -1,0 +1,222 @@
+"""Benchmark of the MoE expert-compute-plus-return path on one MI355X.
+
+A step is one pass of the whole path over one batch already resident in HBM: layout build (histogram, scans,
+scatter, row gather) -> expert SwiGLU FFN with tile-signalled return of finished row-band segments to the R owner
+buffers (producer and consumer overlapped on disjoint CU partitions) -> top-k weighted combine.  Routing is the
+path's input and runs once before the timed region.
+
+Prints one JSON line.  ``value`` is useful (algorithmic) TFLOP/s of the whole step, 6 * M_real * d * f flops per
+step; the line also carries the FFN-only TFLOP/s and % of the bf16 dense MFMA peak, the return-copy overlap ratio,
+the sequential-vs-overlapped comparison, a roofline entry for the dominant kernel and the CPU oracle's rate.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+MFMA_F32_PEAK_TFLOPS = 157.3
+HBM_PEAK_GBS = 8000.0
+METRIC = "grouped expert-FFN TFLOP/s (% bf16 MFMA peak) + return-copy overlap ratio %"
+
+
+def workload_name(s) -> str:
+    return ("%s: R=%d owners x %d tokens, G=%d experts top-%d, %d local, d=%d, f=%d, tile M=%d, %s, mgb=%d"
+            % (s.name, s.R, s.T_o, s.G, s.k, s.E_l, s.d, s.f, s.M, s.dtype, s.mgb))
+
+
+def overlap_stats(ts: np.ndarray, n_segs: int, tick_ns: float = 10.0) -> dict:
+    """Fraction of consumer copy time inside [first producer item start, last flag publish]."""
+    p0, p1 = int(ts[0]), int(ts[1])
+    s = ts[2:2 + 2 * n_segs:2].astype(np.int64)
+    e = ts[3:3 + 2 * n_segs:2].astype(np.int64)
+    dur = np.maximum(e - s, 0)
+    inter = np.maximum(np.minimum(e, p1) - np.maximum(s, p0), 0)
+    tot = dur.sum()
+    return {
+        "overlap_ratio": float(inter.sum() / tot) if tot > 0 else None,
+        "producer_span_us": (p1 - p0) * tick_ns / 1e3,
+        "copy_time_us": float(tot) * tick_ns / 1e3,
+        "exposed_tail_us": max(0, int(e.max()) - p1) * tick_ns / 1e3 if n_segs else 0.0,
+        "first_copy_after_start_us": (int(s.min()) - p0) * tick_ns / 1e3 if n_segs else None,
+    }
+
+
+def cpu_baseline(s, inp, lay_rows, target_s: float):
+    """The CPU oracle's FFN rate on a bounded sample of real rows of the same workload (useful TFLOP/s)."""
+    import oracle
+
+    oracle.load()
+    idx, _ = oracle.route(inp["logits"], s.k)
+    t0 = time.perf_counter()
+    lay = oracle.layout(idx, s.R, s.T_o, s.G, s.E_l, s.k, s.M, s.mgb, 0)
+    t_layout = time.perf_counter() - t0
+    real = np.nonzero(lay["row_src"] >= 0)[0]
+    rng = np.random.default_rng(1)
+    n = 8
+    while True:
+        rows = rng.choice(real, min(n, real.size), replace=False)
+        t0 = time.perf_counter()
+        oracle.ffn_rows(lay["row_src"][rows], lay["tile_expert"][rows // s.M], inp["x"], inp["w_gate_up"],
+                        inp["w_down"], s.dtype == "bf16")
+        dt = time.perf_counter() - t0
+        if dt >= target_s or n >= real.size:
+            break
+        n = min(real.size, int(n * max(2.0, 1.2 * target_s / max(dt, 1e-3))))
+    flops = 6.0 * rows.size * s.d * s.f
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "oracle FFN (fp64, h and y rounded to bf16) on %d of %d real rows, %.1f s; oracle layout of "
+                      "the full batch %.3f s" % (rows.size, real.size, dt, t_layout)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="mixtral")
+    ap.add_argument("--consumer-cus", type=int, default=16)
+    ap.add_argument("--mgb", type=int, default=1)
+    ap.add_argument("--band-window", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--kernels-only", action="store_true", help="timed loop only (for profiler runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this path runs on a single MI355X (the owner ranks are receive buffers in "
+              "its HBM); --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import moe_inputs as mi
+    from expert_output_overlap_amd import binding as B
+    from expert_output_overlap_amd.runtime import MoePath, to_device
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    s = mi.spec(args.config, mgb=args.mgb)
+    t0 = time.perf_counter()
+    inp = mi.inputs(s)
+    t_gen = time.perf_counter() - t0
+    print("inputs generated in %.1f s" % t_gen, file=sys.stderr, flush=True)
+    P = MoePath.from_spec(s)
+    dev = {k: to_device(v, s.dtype) for k, v in inp.items()}
+    P.route(dev["logits"])
+    torch.cuda.synchronize()
+    w1, w2 = dev["w_gate_up"], dev["w_down"]
+    cus = args.consumer_cus
+
+    def step(mode=0, timestamps=False):
+        P.layout(dev["x"])
+        P.ffn(w1, w2, mode=mode, consumer_cus=cus, band_window=args.band_window, timestamps=timestamps)
+        P.combine()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert P.status() == B.MOE_OK, "device status %d" % P.status()
+    sc = P.scalars()
+    M_real = int(sum(sc["N_r"]))
+    M_pad = sc["M_pad"]
+    useful = 6.0 * M_real * s.d * s.f
+
+    # timed region: K whole steps, kernel events recorded on the streams the kernels run on
+    B.moe_set_kernel_timing(True)
+    B.moe_kernel_times()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    g1_ms, g2_ms, cons_ms, ncalls = B.moe_kernel_times()
+    B.moe_set_kernel_timing(False)
+    assert P.status() == B.MOE_OK
+    ms_step = wall * 1e3 / args.steps
+    print("timed %d steps: %.3f ms/step" % (args.steps, ms_step), file=sys.stderr, flush=True)
+    if args.kernels_only:
+        print(json.dumps({"ms_per_step": ms_step}))
+        return
+
+    # FFN call alone, overlapped and sequential (events on the caller stream around the call)
+    def time_ffn(mode, reps):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        P.ffn(w1, w2, mode=mode, consumer_cus=cus, band_window=args.band_window)
+        ts = []
+        for _ in range(reps):
+            ev0.record()
+            P.ffn(w1, w2, mode=mode, consumer_cus=cus, band_window=args.band_window)
+            ev1.record()
+            ev1.synchronize()
+            ts.append(ev0.elapsed_time(ev1))
+        return float(np.median(ts)), float(np.min(ts)), float(np.max(ts))
+
+    reps = max(5, args.steps)
+    t_ovl = time_ffn(0, reps)
+    t_seq = time_ffn(1, reps)
+    B.moe_set_kernel_timing(True)
+    B.moe_kernel_times()
+    for _ in range(reps):
+        P.ffn(w1, w2, mode=1, consumer_cus=cus, band_window=args.band_window)
+    torch.cuda.synchronize()
+    s1, s2, sc_ms, sn = B.moe_kernel_times()
+    B.moe_set_kernel_timing(False)
+    copy_seq_ms = sc_ms / sn
+    # overlap ratio from device timestamps (100 MHz clock), median over reps
+    ovl = []
+    for _ in range(reps):
+        P.ffn(w1, w2, mode=0, consumer_cus=cus, band_window=args.band_window, timestamps=True)
+        torch.cuda.synchronize()
+        ovl.append(overlap_stats(P.timestamps.cpu().numpy().view(np.uint64), sc["n_segs"]))
+    ratio = float(np.median([o["overlap_ratio"] for o in ovl if o["overlap_ratio"] is not None]))
+    o_med = {k: float(np.median([o[k] for o in ovl])) for k in ("producer_span_us", "copy_time_us",
+                                                                   "exposed_tail_us")}
+    torch.cuda.synchronize()
+    assert P.status() == B.MOE_OK
+
+    g1_avg, g2_avg = g1_ms / ncalls, g2_ms / ncalls
+    gemm1_flops = 4.0 * M_real * s.d * s.f
+    ffn_tflops = useful / (t_ovl[0] * 1e-3) / 1e12
+    copy_bytes = 2.0 * M_real * s.d * (2 if s.dtype == "bf16" else 4)
+    peak = MFMA_BF16_PEAK_TFLOPS if s.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    value = useful / (ms_step * 1e-3) / 1e12
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": s.dtype, "data": "synthetic",
+        "config": {"workload": workload_name(s), "M_real": M_real, "M_pad": M_pad, "consumer_cus": cus,
+                   "band_window": args.band_window or 4, "mode": "overlapped"},
+        "pct_bf16_peak_step": round(100 * value / peak, 2),
+        "ffn_tflops_overlapped": round(ffn_tflops, 2),
+        "pct_bf16_peak_ffn": round(100 * ffn_tflops / peak, 2),
+        "overlap_ratio_pct": round(100 * ratio, 2),
+        "ffn_ms_overlapped": [round(v, 4) for v in t_ovl],
+        "ffn_ms_sequential": [round(v, 4) for v in t_seq],
+        "speedup_seq_over_ovl": round(t_seq[0] / t_ovl[0], 4),
+        "copy_ms_sequential": round(copy_seq_ms, 4),
+        "copy_gbs_sequential": round(copy_bytes / (copy_seq_ms * 1e-3) / 1e9, 1),
+        "hidden_copy_fraction": round((t_seq[0] - t_ovl[0]) / copy_seq_ms, 3) if copy_seq_ms > 0 else None,
+        "timestamps_us": {k: round(v, 2) for k, v in o_med.items()},
+        "kernel_ms_avg": {"gemm1_swiglu": round(g1_avg, 4), "gemm2_publish": round(g2_avg, 4),
+                          "consumer": round(cons_ms / ncalls, 4)},
+        "executed_pad_pct": round(100.0 * (M_pad - M_real) / max(M_real, 1), 2),
+        "roofline": {"bound": "mfma", "kernel": "k_gemm gate/up + SwiGLU (first GEMM)",
+                     "achieved": round(gemm1_flops / (g1_avg * 1e-3) / 1e12, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(gemm1_flops / (g1_avg * 1e-3) / 1e12 / peak, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(s, inp, M_real, args.cpu_seconds)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

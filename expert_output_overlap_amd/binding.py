@@ -1,0 +1,169 @@
+"""ctypes binding of libmoe_overlap.so: the C-ABI entry points under the same names (argument marshalling only).
+
+Tensors are torch tensors on the GPU (device memory); streams are torch streams (their hipStream_t is passed).
+Every computation runs in the library's HIP kernels; there is no fallback: if the library is missing this
+module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_overlap.so")
+
+MOE_OK, MOE_EINVAL, MOE_ECAPACITY, MOE_EHIP, MOE_ETIMEOUT = 0, -1, -2, -3, -4
+MOE_BF16, MOE_F32 = 0, 1
+MOE_SEG_FIELDS = 8
+MT_FIELDS = 18
+EXPORTS = ["moe_last_error", "moe_version", "moe_route", "moe_layout_capacity_rows", "moe_layout_workspace_bytes",
+           "moe_layout_bind", "moe_layout_build", "moe_read_status", "moe_ffn_flags_count", "moe_expert_ffn_overlap",
+           "moe_combine", "moe_set_kernel_timing", "moe_kernel_times"]
+
+
+class moe_shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("R", "tokens_per_owner", "num_global_experts", "num_local_experts",
+                                               "top_k", "self_rank", "d", "f", "tile_m", "seg_bands", "dtype")]
+
+
+LAYOUT_ARRAYS = ["counts", "padded_off", "recv_off", "tile_owner", "tile_expert", "tile_valid", "tile_order",
+                 "seg_desc", "row_src", "combine_plan", "scalars", "status", "mtile_desc", "seg_mtiles",
+                 "chunk_counts"]
+
+
+class moe_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYOUT_ARRAYS] + [
+        ("cap_rows", ctypes.c_int64), ("cap_tiles", ctypes.c_int64), ("cap_mtiles", ctypes.c_int64)]
+
+
+class moe_overlap_cfg(ctypes.Structure):
+    _fields_ = [("consumer_cus", ctypes.c_int32), ("mode", ctypes.c_int32), ("epoch", ctypes.c_uint32),
+                ("band_window", ctypes.c_int32), ("watchdog_ticks", ctypes.c_uint64),
+                ("timestamps", ctypes.c_void_p)]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__("%s failed (%d): %s" % (fn, code, msg))
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library.  Raises if it has not been built: there is no other implementation to fall to."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libmoe_overlap.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        ps, pl, pc = ctypes.POINTER(moe_shape), ctypes.POINTER(moe_layout), ctypes.POINTER(moe_overlap_cfg)
+        sig = {
+            "moe_last_error": ([], ctypes.c_char_p), "moe_version": ([], ctypes.c_char_p),
+            "moe_route": ([ps, vp, vp, vp, vp], i32),
+            "moe_layout_capacity_rows": ([ps], i64), "moe_layout_workspace_bytes": ([ps], i64),
+            "moe_layout_bind": ([ps, vp, i64, pl], i32),
+            "moe_layout_build": ([ps, vp, vp, pl, vp, vp], i32),
+            "moe_read_status": ([pl, vp], i32), "moe_ffn_flags_count": ([ps], i64),
+            "moe_expert_ffn_overlap": ([ps, pl, vp, vp, vp, vp, vp, vp, vp, pc, vp], i32),
+            "moe_combine": ([ps, pl, vp, vp, vp, vp], i32),
+            "moe_set_kernel_timing": ([i32], i32), "moe_kernel_times": ([ctypes.POINTER(ctypes.c_double)], i32),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn: str, rc: int) -> int:
+    if rc != MOE_OK:
+        raise MoeError(fn, rc, moe_last_error())
+    return rc
+
+
+def _ptr_array(tensors):
+    arr = (ctypes.c_void_p * max(1, len(tensors)))()
+    for i, t in enumerate(tensors):
+        arr[i] = t.data_ptr()
+    return arr
+
+
+# ---- entry points --------------------------------------------------------------------------------------------
+
+def moe_last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def moe_version() -> str:
+    return lib().moe_version().decode()
+
+
+def moe_route(shape: moe_shape, logits, topk_idx, topk_w, stream=None) -> int:
+    return _check("moe_route", lib().moe_route(ctypes.byref(shape), _ptr(logits), _ptr(topk_idx), _ptr(topk_w),
+                                               _stream(stream)))
+
+
+def moe_layout_capacity_rows(shape: moe_shape) -> int:
+    return lib().moe_layout_capacity_rows(ctypes.byref(shape))
+
+
+def moe_layout_workspace_bytes(shape: moe_shape) -> int:
+    return lib().moe_layout_workspace_bytes(ctypes.byref(shape))
+
+
+def moe_layout_bind(shape: moe_shape, workspace, layout: moe_layout) -> int:
+    return _check("moe_layout_bind", lib().moe_layout_bind(ctypes.byref(shape), _ptr(workspace),
+                                                           workspace.numel() * workspace.element_size(),
+                                                           ctypes.byref(layout)))
+
+
+def moe_layout_build(shape: moe_shape, topk_idx, x, layout: moe_layout, x_pad, stream=None) -> int:
+    return _check("moe_layout_build", lib().moe_layout_build(ctypes.byref(shape), _ptr(topk_idx), _ptr(x),
+                                                             ctypes.byref(layout), _ptr(x_pad), _stream(stream)))
+
+
+def moe_read_status(layout: moe_layout, stream=None) -> int:
+    return lib().moe_read_status(ctypes.byref(layout), _stream(stream))
+
+
+def moe_ffn_flags_count(shape: moe_shape) -> int:
+    return lib().moe_ffn_flags_count(ctypes.byref(shape))
+
+
+def moe_expert_ffn_overlap(shape: moe_shape, layout: moe_layout, x_pad, w_gate_up, w_down, h_ws, y_pad, recv,
+                           flags, cfg: moe_overlap_cfg, stream=None) -> int:
+    return _check("moe_expert_ffn_overlap", lib().moe_expert_ffn_overlap(
+        ctypes.byref(shape), ctypes.byref(layout), _ptr(x_pad), _ptr(w_gate_up), _ptr(w_down), _ptr(h_ws),
+        _ptr(y_pad), _ptr_array(recv), _ptr(flags), ctypes.byref(cfg), _stream(stream)))
+
+
+def moe_combine(shape: moe_shape, layout: moe_layout, topk_w, recv, out, stream=None) -> int:
+    return _check("moe_combine", lib().moe_combine(ctypes.byref(shape), ctypes.byref(layout), _ptr(topk_w),
+                                                   _ptr_array(recv), _ptr(out), _stream(stream)))
+
+
+def moe_set_kernel_timing(enable: bool) -> int:
+    return _check("moe_set_kernel_timing", lib().moe_set_kernel_timing(int(bool(enable))))
+
+
+def moe_kernel_times():
+    """(gemm1 ms, gemm2 ms, consumer ms, calls) summed since the last query."""
+    out = (ctypes.c_double * 4)()
+    _check("moe_kernel_times", lib().moe_kernel_times(out))
+    return out[0], out[1], out[2], int(out[3])

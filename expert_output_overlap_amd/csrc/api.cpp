@@ -1,0 +1,344 @@
+// C ABI of the MoE expert-compute-plus-return path (declarations and contracts in include/moe_overlap.h).
+// Host side only: argument checks, workspace carving, launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/moe_overlap.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+// Returns "" when the shape is valid.
+std::string check_shape(const moe_shape* s) {
+  if (s == nullptr) return "null shape";
+  if (s->R < 1 || s->R > MOE_MAX_OWNERS) return "R must be in [1, 16]";
+  if (s->tokens_per_owner < 0) return "tokens_per_owner must be >= 0";
+  if (s->num_local_experts < 1 || s->num_local_experts > MOE_MAX_LOCAL_EXPERTS) return "num_local_experts in [1, 64]";
+  if (s->num_global_experts < 1 || s->num_global_experts > 1024) return "num_global_experts in [1, 1024]";
+  if (s->num_global_experts % s->num_local_experts) return "num_global_experts % num_local_experts != 0";
+  if (s->top_k < 1 || s->top_k > 16 || s->top_k > s->num_global_experts) return "top_k in [1, min(G, 16)]";
+  if (s->self_rank < 0 || s->self_rank >= s->R ||
+      (int64_t)(s->self_rank + 1) * s->num_local_experts > s->num_global_experts)
+    return "self_rank out of range";
+  if (s->d < 64 || s->d % 64) return "d must be a positive multiple of 64";
+  if (s->f < 64 || s->f % 64) return "f must be a positive multiple of 64";
+  if (s->tile_m < 16 || s->tile_m > 256 || s->tile_m % 16) return "tile_m must be a multiple of 16 in [16, 256]";
+  if (s->seg_bands < 1) return "seg_bands must be >= 1";
+  if (s->dtype != MOE_BF16 && s->dtype != MOE_F32) return "dtype must be MOE_BF16 or MOE_F32";
+  const int64_t T = (int64_t)s->R * s->tokens_per_owner;
+  if (T * s->top_k >= (1ll << 31)) return "T*k too large";
+  const int64_t cap = (T * std::min(s->top_k, s->num_local_experts) +
+                       (int64_t)s->num_local_experts * s->R * (s->tile_m - 1));
+  if (cap >= (1ll << 30)) return "padded row capacity too large";
+  return "";
+}
+
+int64_t capacity_rows(const moe_shape* s) {
+  const int64_t T = (int64_t)s->R * s->tokens_per_owner;
+  const int64_t bound = T * std::min(s->top_k, s->num_local_experts) +
+                        (int64_t)s->num_local_experts * s->R * (s->tile_m - 1);
+  return round_up(bound, s->tile_m);
+}
+
+struct Carve {
+  int64_t off = 0;
+  int64_t take(int64_t elems, int64_t esize) {
+    const int64_t o = off;
+    off = round_up(off + elems * esize, 256);
+    return o;
+  }
+};
+
+struct Offsets {
+  int64_t counts, padded_off, recv_off, tile_owner, tile_expert, tile_valid, tile_order, seg_desc, row_src,
+      combine_plan, scalars, status, mtile_desc, seg_mtiles, chunk_counts, total;
+  int64_t cap_rows, cap_tiles, cap_mtiles;
+};
+
+Offsets layout_offsets(const moe_shape* s) {
+  Offsets o;
+  const int64_t NG = (int64_t)s->num_local_experts * s->R;
+  const int64_t T = (int64_t)s->R * s->tokens_per_owner;
+  o.cap_rows = capacity_rows(s);
+  o.cap_tiles = o.cap_rows / s->tile_m;
+  const int mt_sub = ffn_gemm_bm(s->dtype) / 16;
+  o.cap_mtiles = (o.cap_rows / 16 + mt_sub - 1) / mt_sub + NG + 1;
+  const int64_t n_chunks = (s->tokens_per_owner + 63) / 64;
+  Carve c;
+  o.counts = c.take(NG, 4);
+  o.padded_off = c.take(NG, 4);
+  o.recv_off = c.take(NG, 4);
+  o.tile_owner = c.take(o.cap_tiles, 4);
+  o.tile_expert = c.take(o.cap_tiles, 4);
+  o.tile_valid = c.take(o.cap_tiles, 4);
+  o.tile_order = c.take(o.cap_tiles, 4);
+  o.seg_desc = c.take(o.cap_tiles * MOE_SEG_FIELDS, 4);
+  o.row_src = c.take(o.cap_rows, 4);
+  o.combine_plan = c.take(T * s->top_k, 4);
+  o.scalars = c.take(4 + s->R, 4);
+  o.status = c.take(1, 4);
+  o.mtile_desc = c.take(o.cap_mtiles * (2 + 16), 4);
+  o.seg_mtiles = c.take(o.cap_tiles * 2, 4);
+  o.chunk_counts = c.take((int64_t)s->R * n_chunks * s->num_local_experts, 4);
+  o.total = c.off;
+  return o;
+}
+
+std::mutex g_mu;
+
+int device_cus(int dev) {
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  return n;
+}
+
+// Optional kernel timing: per call, events around GEMM1, GEMM2 (producer stream) and the consumer.
+struct CallEvents {
+  hipEvent_t e[5];  // gemm1 start, gemm1 end / gemm2 start, gemm2 end, consumer start, consumer end
+};
+bool g_timing = false;
+std::vector<CallEvents> g_events;
+
+int timing_begin(CallEvents* ce) {
+  for (int i = 0; i < 5; ++i)
+    if (hipEventCreate(&ce->e[i]) != hipSuccess) return -1;
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_set_kernel_timing(int enable) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_timing = enable != 0;
+  return MOE_OK;
+}
+
+int moe_kernel_times(double* out4) {
+  if (!out4) return fail(MOE_EINVAL, "null pointer");
+  std::lock_guard<std::mutex> lk(g_mu);
+  double t[3] = {0, 0, 0};
+  int rc = MOE_OK;
+  for (auto& ce : g_events) {
+    float ms = 0;
+    for (int i = 0; i < 5; ++i)
+      if (hipEventSynchronize(ce.e[i]) != hipSuccess) rc = MOE_EHIP;
+    if (hipEventElapsedTime(&ms, ce.e[0], ce.e[1]) == hipSuccess) t[0] += ms; else rc = MOE_EHIP;
+    if (hipEventElapsedTime(&ms, ce.e[1], ce.e[2]) == hipSuccess) t[1] += ms; else rc = MOE_EHIP;
+    if (hipEventElapsedTime(&ms, ce.e[3], ce.e[4]) == hipSuccess) t[2] += ms; else rc = MOE_EHIP;
+    for (int i = 0; i < 5; ++i) hipEventDestroy(ce.e[i]);
+  }
+  out4[0] = t[0];
+  out4[1] = t[1];
+  out4[2] = t[2];
+  out4[3] = (double)g_events.size();
+  g_events.clear();
+  if (rc != MOE_OK) return fail(rc, "event timing failed");
+  return MOE_OK;
+}
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+const char* moe_version(void) { return "moe_overlap gfx950 1"; }
+
+int moe_route(const moe_shape* s, const float* logits, int32_t* topk_idx, float* topk_w, void* stream) {
+  const std::string e = check_shape(s);
+  if (!e.empty()) return fail(MOE_EINVAL, e);
+  const int64_t T = (int64_t)s->R * s->tokens_per_owner;
+  if (T > 0 && (!logits || !topk_idx || !topk_w)) return fail(MOE_EINVAL, "null pointer");
+  if (launch_route((int)T, s->num_global_experts, s->top_k, logits, topk_idx, topk_w, (hipStream_t)stream))
+    return fail(MOE_EHIP, "route launch failed");
+  return MOE_OK;
+}
+
+int64_t moe_layout_capacity_rows(const moe_shape* s) {
+  if (!check_shape(s).empty()) return -1;
+  return capacity_rows(s);
+}
+
+int64_t moe_layout_workspace_bytes(const moe_shape* s) {
+  if (!check_shape(s).empty()) return -1;
+  return layout_offsets(s).total;
+}
+
+int moe_layout_bind(const moe_shape* s, void* workspace, int64_t workspace_bytes, moe_layout* L) {
+  const std::string e = check_shape(s);
+  if (!e.empty()) return fail(MOE_EINVAL, e);
+  if (!workspace || !L) return fail(MOE_EINVAL, "null pointer");
+  if (((uintptr_t)workspace) % 256) return fail(MOE_EINVAL, "workspace must be 256-byte aligned");
+  const Offsets o = layout_offsets(s);
+  if (workspace_bytes < o.total) return fail(MOE_EINVAL, "workspace too small");
+  char* b = (char*)workspace;
+  L->counts = (int32_t*)(b + o.counts);
+  L->padded_off = (int32_t*)(b + o.padded_off);
+  L->recv_off = (int32_t*)(b + o.recv_off);
+  L->tile_owner = (int32_t*)(b + o.tile_owner);
+  L->tile_expert = (int32_t*)(b + o.tile_expert);
+  L->tile_valid = (int32_t*)(b + o.tile_valid);
+  L->tile_order = (int32_t*)(b + o.tile_order);
+  L->seg_desc = (int32_t*)(b + o.seg_desc);
+  L->row_src = (int32_t*)(b + o.row_src);
+  L->combine_plan = (int32_t*)(b + o.combine_plan);
+  L->scalars = (int32_t*)(b + o.scalars);
+  L->status = (int32_t*)(b + o.status);
+  L->mtile_desc = (int32_t*)(b + o.mtile_desc);
+  L->seg_mtiles = (int32_t*)(b + o.seg_mtiles);
+  L->chunk_counts = (int32_t*)(b + o.chunk_counts);
+  L->cap_rows = o.cap_rows;
+  L->cap_tiles = o.cap_tiles;
+  L->cap_mtiles = o.cap_mtiles;
+  return MOE_OK;
+}
+
+static bool layout_ok(const moe_layout* L) {
+  return L && L->counts && L->padded_off && L->recv_off && L->tile_owner && L->tile_expert && L->tile_valid &&
+         L->tile_order && L->seg_desc && L->row_src && L->combine_plan && L->scalars && L->status &&
+         L->mtile_desc && L->seg_mtiles && L->chunk_counts && L->cap_rows > 0;
+}
+
+int moe_layout_build(const moe_shape* s, const int32_t* topk_idx, const void* x, moe_layout* L, void* x_pad,
+                     void* stream) {
+  const std::string e = check_shape(s);
+  if (!e.empty()) return fail(MOE_EINVAL, e);
+  if (!layout_ok(L)) return fail(MOE_EINVAL, "layout not bound");
+  const int64_t T = (int64_t)s->R * s->tokens_per_owner;
+  if (T > 0 && (!topk_idx || !x || !x_pad)) return fail(MOE_EINVAL, "null pointer");
+  if (L->cap_tiles * s->tile_m != L->cap_rows) return fail(MOE_EINVAL, "layout bound for another tile_m");
+  LayoutLaunch p;
+  p.topk_idx = topk_idx;
+  p.x = x;
+  p.x_pad = x_pad;
+  p.L = L;
+  p.R = s->R;
+  p.T_o = s->tokens_per_owner;
+  p.G = s->num_global_experts;
+  p.k = s->top_k;
+  p.lo = s->self_rank * s->num_local_experts;
+  p.E = s->num_local_experts;
+  p.M = s->tile_m;
+  p.mgb = s->seg_bands;
+  p.self_rank = s->self_rank;
+  p.mt_sub = ffn_gemm_bm(s->dtype) / 16;
+  p.row_bytes = (int64_t)s->d * (s->dtype == MOE_BF16 ? 2 : 4);
+  if (launch_layout(p, (hipStream_t)stream)) return fail(MOE_EHIP, "layout launch failed");
+  return MOE_OK;
+}
+
+int moe_read_status(const moe_layout* L, void* stream) {
+  if (!L || !L->status) return fail(MOE_EINVAL, "null layout");
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return fail(MOE_EHIP, "stream sync failed");
+  int32_t v = 0;
+  if (hipMemcpy(&v, L->status, 4, hipMemcpyDeviceToHost) != hipSuccess) return fail(MOE_EHIP, "status copy failed");
+  return v;
+}
+
+int64_t moe_ffn_flags_count(const moe_shape* s) {
+  if (!check_shape(s).empty()) return -1;
+  const Offsets o = layout_offsets(s);
+  return o.cap_mtiles * (s->d / ffn_gemm2_bn(s->dtype, s->d));
+}
+
+int moe_expert_ffn_overlap(const moe_shape* s, const moe_layout* L, const void* x_pad, const void* w_gate_up,
+                           const void* w_down, void* h_ws, void* y_pad, void* const* recv, uint32_t* flags,
+                           const moe_overlap_cfg* cfg, void* stream) {
+  const std::string e = check_shape(s);
+  if (!e.empty()) return fail(MOE_EINVAL, e);
+  if (!layout_ok(L) || !cfg) return fail(MOE_EINVAL, "null layout or cfg");
+  if (!x_pad || !w_gate_up || !w_down || !h_ws || !y_pad || !recv || !flags)
+    return fail(MOE_EINVAL, "null pointer");
+  for (int r = 0; r < s->R; ++r)
+    if (!recv[r]) return fail(MOE_EINVAL, "null receive buffer");
+  if (cfg->epoch == 0) return fail(MOE_EINVAL, "epoch must be nonzero");
+  if (cfg->mode < 0 || cfg->mode > 2) return fail(MOE_EINVAL, "mode must be 0, 1 or 2");
+  if (cfg->band_window < 0) return fail(MOE_EINVAL, "band_window must be >= 0");
+  hipStream_t st = (hipStream_t)stream;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MOE_EHIP, "hipGetDevice failed");
+  const int n_cu = device_cus(dev);
+  if (n_cu <= 0) return fail(MOE_EHIP, "cannot query the CU count");
+  if (cfg->consumer_cus < 1 || cfg->consumer_cus > n_cu / 2)
+    return fail(MOE_EINVAL, "consumer_cus must be in [1, CUs/2]");
+
+  FfnLaunch p;
+  p.dtype = s->dtype;
+  p.R = s->R;
+  p.E = s->num_local_experts;
+  p.d = s->d;
+  p.f = s->f;
+  p.L = L;
+  p.x_pad = x_pad;
+  p.w_gate_up = w_gate_up;
+  p.w_down = w_down;
+  p.h = h_ws;
+  p.y_pad = y_pad;
+  p.recv = recv;
+  p.flags = flags;
+  p.epoch = cfg->epoch;
+  p.band_window = cfg->band_window;
+  p.watchdog_ticks = cfg->watchdog_ticks ? cfg->watchdog_ticks : 200000000ull;
+  p.timestamps = cfg->timestamps;
+  const int C = cfg->consumer_cus;
+
+  if (cfg->mode == 2) {  // return only
+    if (launch_ffn_gemm2(p, C, C, st)) return fail(MOE_EHIP, "consumer launch failed");
+    return MOE_OK;
+  }
+  CallEvents ce;
+  const bool timed = g_timing && timing_begin(&ce) == 0;
+  if (cfg->timestamps && launch_ts_init(cfg->timestamps, st)) return fail(MOE_EHIP, "launch failed");
+  if (timed) hipEventRecord(ce.e[0], st);
+  if (launch_ffn_gemm1(p, n_cu, st)) return fail(MOE_EHIP, "producer launch failed");
+  if (timed) hipEventRecord(ce.e[1], st);
+  // overlapped: one launch, C consumer workgroups + producers on the other CUs;
+  // sequential: producers on every CU, then the consumer alone
+  if (launch_ffn_gemm2(p, n_cu, cfg->mode == 0 ? C : 0, st)) return fail(MOE_EHIP, "producer launch failed");
+  if (timed) {
+    hipEventRecord(ce.e[2], st);
+    hipEventRecord(ce.e[3], st);
+  }
+  if (cfg->mode == 1 && launch_ffn_gemm2(p, C, C, st)) return fail(MOE_EHIP, "consumer launch failed");
+  if (timed) {
+    hipEventRecord(ce.e[4], st);
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_events.push_back(ce);
+  }
+  return MOE_OK;
+}
+
+int moe_combine(const moe_shape* s, const moe_layout* L, const float* topk_w, void* const* recv, void* out,
+                void* stream) {
+  const std::string e = check_shape(s);
+  if (!e.empty()) return fail(MOE_EINVAL, e);
+  if (!layout_ok(L)) return fail(MOE_EINVAL, "layout not bound");
+  const int64_t T = (int64_t)s->R * s->tokens_per_owner;
+  if (T > 0 && (!topk_w || !recv || !out)) return fail(MOE_EINVAL, "null pointer");
+  for (int r = 0; T > 0 && r < s->R; ++r)
+    if (!recv[r]) return fail(MOE_EINVAL, "null receive buffer");
+  CombineLaunch p;
+  p.dtype = s->dtype;
+  p.R = s->R;
+  p.T_o = s->tokens_per_owner;
+  p.k = s->top_k;
+  p.d = s->d;
+  p.L = L;
+  p.topk_w = topk_w;
+  p.recv = recv;
+  p.out = out;
+  if (launch_combine(p, (hipStream_t)stream)) return fail(MOE_EHIP, "combine launch failed");
+  return MOE_OK;
+}
+
+}  // extern "C"

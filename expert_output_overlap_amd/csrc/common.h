@@ -1,0 +1,87 @@
+// Device-side helpers shared by the gfx950 kernels of this library (never by the CPU oracle).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe_overlap.h"
+
+#define MOE_WAVE 64
+
+// GEMM row tile: up to MOE_MT_SUB sub-blocks of MOE_SUB rows of one expert.
+#define MOE_SUB 16
+#define MOE_MT_SUB 16
+#define MOE_MT_FIELDS (2 + MOE_MT_SUB)
+
+// scalars[] indices
+#define SC_MPAD 0
+#define SC_NTILES 1
+#define SC_NSEGS 2
+#define SC_NR 3
+// n_mtiles sits at 3 + R
+
+// segment descriptor fields
+#define SEG_OWNER 0
+#define SEG_EXPERT 1
+#define SEG_FIRST_BAND 2
+#define SEG_NBANDS 3
+#define SEG_SRC_ROW 4
+#define SEG_DST_ROW 5
+#define SEG_ROWS 6
+#define SEG_GROUP 7
+
+typedef uint16_t bf16_t;  // raw bf16 storage
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+
+// fp32 -> bf16, round to nearest even (inputs here are finite; NaN kept quiet)
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+// 100 MHz constant-rate device clock, comparable across CUs
+__device__ __forceinline__ uint64_t moe_clock() { return wall_clock64(); }
+
+// Status word helpers: first error wins.
+__device__ __forceinline__ void set_status(int32_t* status, int32_t code) { atomicCAS(status, 0, code); }
+
+__device__ __forceinline__ int32_t load_status(const int32_t* status) {
+  return __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// wave-level helpers
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int t = __shfl_up(v, o, 64);
+    if (l >= o) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Owner receive-buffer table passed by value in the kernel arguments.
+struct RecvPtrs {
+  void* p[MOE_MAX_OWNERS];
+};

@@ -1,0 +1,352 @@
+// Producer: persistent grouped SwiGLU expert FFN on CDNA4 MFMA (review page: "The pith" and "Core claim":
+// one rank-wide persistent GEMM over all local experts that publishes a readiness flag per output tile;
+// "What carries the argument": remote-bound tiles first).
+//
+// Two persistent launches, one workgroup per CU:
+//   GEMM1 (GLU):  h[rows, f] = bf16(silu(x Wg^T) * (x Wu^T)),  one tile = BN/2 gate + BN/2 up columns
+//   GEMM2:        y[rows, d] = h Wd^T, then flags[tile] = epoch with an agent-scope release.  The first C
+//                 workgroups of this launch are the consumer partition instead (consumer.h): round-robin
+//                 dispatch puts workgroup b on XCD b % 8, so C consumers spread over the XCDs, one per CU,
+//                 and the producer and consumer are co-resident by construction.
+// Row tiles are the layout's GEMM row tiles: up to BM/16 sub-blocks of 16 rows of one expert, walked in
+// the remote-first group order, so all-padding sub-blocks cost nothing.  Items (row tile, column tile)
+// are visited window by window (band_window row tiles, column-tile-major inside a window) for weight
+// reuse, and consecutive items go to workgroups on the same XCD.
+#include "common.h"
+#include "consumer.h"
+#include "launch.h"
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // 16-byte chunk (native vector: stays in VGPRs)
+
+template <typename T>
+struct Mfma;
+
+// v_mfma_f32_32x32x16_bf16: lane l holds row (l % 32) of A and column (l % 32) of B, 8 consecutive k at
+// 8 * (l / 32); D[i][j] with j = l % 32 and i = 8 * (reg / 4) + 4 * (l / 32) + reg % 4.
+template <>
+struct Mfma<bf16_t> {
+  static constexpr int KM = 16, EPL = 8, BK = 64;
+  typedef bf16x8_t frag;
+  static __device__ __forceinline__ frag load(const bf16_t* p) {
+    return __builtin_bit_cast(frag, *(const u32x4_t*)p);
+  }
+  static __device__ __forceinline__ f32x16_t mma(frag a, frag b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ bf16_t out(float v) { return f32_to_bf16(v); }
+};
+
+// v_mfma_f32_32x32x2_f32: one k per lane at (l / 32); same D layout.
+template <>
+struct Mfma<float> {
+  static constexpr int KM = 2, EPL = 1, BK = 32;
+  typedef float frag;
+  static __device__ __forceinline__ frag load(const float* p) { return *p; }
+  static __device__ __forceinline__ f32x16_t mma(frag a, frag b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float out(float v) { return v; }
+};
+
+struct GemmArgs {
+  const void* A;  // [rows, K]: x_pad (GEMM1) or h (GEMM2)
+  const void* W;  // [E, w_rows, K]
+  void* C;        // [rows, ldc]
+  int K, w_rows, ldc, f;
+  int n_nt;  // column tiles
+  const int32_t* mtile_desc;
+  const int32_t* scalars;
+  int sc_nmt;
+  const int32_t* status;
+  uint32_t* flags;
+  uint32_t epoch;
+  int window;
+  uint64_t* ts;
+  int n_cons;  // GEMM2 only: workgroups [0, n_cons) run the consumer role
+  ConsumerArgs cons;
+};
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+
+template <typename T, int BM, int BN, int WGM, int WGN, bool GLU, bool PUBLISH>
+__global__ __launch_bounds__(WGM* WGN * 64) void k_gemm(GemmArgs a) {
+  using Tr = Mfma<T>;
+  constexpr int BK = Tr::BK, NTHR = WGM * WGN * 64;
+  constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte chunk
+  constexpr int LDK = BK + VEC;        // padded LDS row stride (elements)
+  constexpr int WM = BM / WGM, WN = BN / WGN, MI = WM / 32, NI = WN / 32;
+  constexpr int CPR = BK / VEC;     // chunks per tile row
+  constexpr int RPP = NTHR / CPR;   // tile rows per load pass
+  constexpr int PA = BM / RPP, PB = BN / RPP;
+  constexpr int OUT_BN = GLU ? BN / 2 : BN;  // output columns per tile
+  static_assert(!GLU || NI % 2 == 0, "GLU pairs gate and up blocks");
+  static_assert(BM % RPP == 0 && BN % RPP == 0 && BM / 16 <= MOE_MT_SUB, "tile shape");
+
+  __shared__ __align__(16) T sA[2][BM * LDK];
+  __shared__ __align__(16) T sB[2][BN * LDK];
+  __shared__ int s_sub[MOE_MT_SUB];
+  __shared__ int s_hdr[2];
+
+  if (PUBLISH && (int)blockIdx.x < a.n_cons) {
+    consumer_role(a.cons, blockIdx.x, a.n_cons);
+    return;
+  }
+  if (load_status(a.status) != 0) return;
+  const int n_mt = a.scalars[a.sc_nmt];
+  const int n_items = n_mt * a.n_nt;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int n_cons = PUBLISH ? a.n_cons : 0;
+  const int G = gridDim.x - n_cons;  // producer workgroups
+  int bid = blockIdx.x - n_cons;
+  // producers of one XCD (workgroup index mod 8) take consecutive items, which share a weight tile
+  if ((G & 7) == 0 && (n_cons & 7) == 0) bid = (bid & 7) * (G >> 3) + (bid >> 3);
+  const T* __restrict__ A = (const T*)a.A;
+  const T* __restrict__ Wt = (const T*)a.W;
+  T* __restrict__ C = (T*)a.C;
+  const int K = a.K;
+  const int nk = K / BK;
+  const int cr = tid / CPR, cc = (tid % CPR) * VEC;
+  bool first = true;
+
+  for (int item = bid; item < n_items; item += G) {
+    const int per_win = a.window * a.n_nt;
+    const int w = item / per_win, j = item - w * per_win;
+    const int mt0 = w * a.window;
+    const int Wc = min(a.window, n_mt - mt0);
+    const int nt = j / Wc, mt = mt0 + (j - nt * Wc);
+
+    __syncthreads();  // previous item finished with LDS and the header
+    if (tid < MOE_MT_FIELDS) {
+      const int v = a.mtile_desc[(int64_t)mt * MOE_MT_FIELDS + tid];
+      if (tid < 2) s_hdr[tid] = v;
+      else s_sub[tid - 2] = v;
+    }
+    if (PUBLISH && a.ts != nullptr && first && tid == 0)
+      atomicMin((unsigned long long*)&a.ts[0], (unsigned long long)moe_clock());
+    first = false;
+    __syncthreads();
+    const int e = s_hdr[0], n_sub = s_hdr[1];
+
+    const T* pa[PA];
+#pragma unroll
+    for (int p = 0; p < PA; ++p) {
+      const int r = p * RPP + cr;
+      const int sub = r >> 4;
+      pa[p] = A + (int64_t)(sub < n_sub ? s_sub[sub] + (r & 15) : 0) * K + cc;
+    }
+    const T* pb[PB];
+    const T* wbase = Wt + (int64_t)e * a.w_rows * K;
+#pragma unroll
+    for (int p = 0; p < PB; ++p) {
+      const int i = p * RPP + cr;
+      int wrow;
+      if (GLU) wrow = i < BN / 2 ? nt * (BN / 2) + i : a.f + nt * (BN / 2) + (i - BN / 2);
+      else wrow = nt * BN + i;
+      pb[p] = wbase + (int64_t)wrow * K + cc;
+    }
+    bool mvalid[MI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) mvalid[mi] = ((wm * WM + mi * 32) >> 4) < n_sub;
+
+    f32x16_t acc[MI][NI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.f;
+
+    // Rows of absent sub-blocks read row 0 of the tile's source instead (always allocated); their outputs are
+    // never stored, and rows are independent in both GEMMs.
+    {
+      u32x4_t ra[PA], rb[PB];
+#pragma unroll
+      for (int p = 0; p < PA; ++p) ra[p] = *(const u32x4_t*)(pa[p]);
+#pragma unroll
+      for (int p = 0; p < PB; ++p) rb[p] = *(const u32x4_t*)(pb[p]);
+#pragma unroll
+      for (int p = 0; p < PA; ++p) *(u32x4_t*)&sA[0][(p * RPP + cr) * LDK + cc] = ra[p];
+#pragma unroll
+      for (int p = 0; p < PB; ++p) *(u32x4_t*)&sB[0][(p * RPP + cr) * LDK + cc] = rb[p];
+    }
+    __syncthreads();
+
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      const bool more = kt + 1 < nk;
+      u32x4_t ra[PA], rb[PB];
+      if (more) {
+        const int k0 = (kt + 1) * BK;
+#pragma unroll
+        for (int p = 0; p < PA; ++p) ra[p] = *(const u32x4_t*)(pa[p] + k0);
+#pragma unroll
+        for (int p = 0; p < PB; ++p) rb[p] = *(const u32x4_t*)(pb[p] + k0);
+      }
+      const T* cA = sA[cur];
+      const T* cB = sB[cur];
+#pragma unroll
+      for (int s = 0; s < BK / Tr::KM; ++s) {
+        const int kk = s * Tr::KM + (lane >> 5) * Tr::EPL;
+        typename Tr::frag fa[MI], fb[NI];
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) fa[mi] = Tr::load(&cA[(wm * WM + mi * 32 + (lane & 31)) * LDK + kk]);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          int row;
+          if (GLU) row = ni < NI / 2 ? wn * (WN / 2) + ni * 32 : BN / 2 + wn * (WN / 2) + (ni - NI / 2) * 32;
+          else row = wn * WN + ni * 32;
+          fb[ni] = Tr::load(&cB[(row + (lane & 31)) * LDK + kk]);
+        }
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+          if (!mvalid[mi]) continue;
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = Tr::mma(fa[mi], fb[ni], acc[mi][ni]);
+        }
+      }
+      if (more) {
+        const int nxt = cur ^ 1;
+#pragma unroll
+        for (int p = 0; p < PA; ++p) *(u32x4_t*)&sA[nxt][(p * RPP + cr) * LDK + cc] = ra[p];
+#pragma unroll
+        for (int p = 0; p < PB; ++p) *(u32x4_t*)&sB[nxt][(p * RPP + cr) * LDK + cc] = rb[p];
+      }
+      __syncthreads();
+    }
+
+    // epilogue: store the tile's real sub-blocks (padding rows inside a present sub-block included)
+    constexpr int NO = GLU ? NI / 2 : NI;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      if (!mvalid[mi]) continue;
+#pragma unroll
+      for (int ni = 0; ni < NO; ++ni) {
+        const int col = nt * OUT_BN + (GLU ? wn * (WN / 2) : wn * WN) + ni * 32 + (lane & 31);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int row = wm * WM + mi * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+          const int sub = row >> 4;
+          if (sub < n_sub) {
+            const int64_t grow = s_sub[sub] + (row & 15);
+            float v = acc[mi][ni][q];
+            if (GLU) v = silu_f32(v) * acc[mi][ni + NI / 2][q];
+            C[grow * a.ldc + col] = Tr::out(v);
+          }
+        }
+      }
+    }
+    if (PUBLISH) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this thread's tile stores, agent-visible
+      __syncthreads();
+      if (tid == 0) {
+        __hip_atomic_store(&a.flags[(int64_t)mt * a.n_nt + nt], a.epoch, __ATOMIC_RELEASE,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        if (a.ts != nullptr) atomicMax((unsigned long long*)&a.ts[1], (unsigned long long)moe_clock());
+      }
+    }
+  }
+}
+
+// ---- tile configurations --------------------------------------------------------------------------------
+#define BF_BM 128
+#define BF_BN 128
+#define F32_BM 64
+#define F32_BN 64
+
+// Extra dynamic LDS per bf16 workgroup: keeps the total above half of the CU's 160 KB so that a CU holds one
+// producer workgroup (or one consumer workgroup) of a launch, never two.
+#define BF_LDS_PAD (10 * 1024)
+
+int ffn_gemm_bm(int dtype) { return dtype == MOE_BF16 ? BF_BM : F32_BM; }
+
+int ffn_gemm2_bn(int dtype, int d) {
+  if (dtype == MOE_BF16) return d % BF_BN == 0 ? BF_BN : 64;
+  return F32_BN;
+}
+
+
+static GemmArgs base_args(const FfnLaunch& p) {
+  GemmArgs a;
+  a.mtile_desc = p.L->mtile_desc;
+  a.scalars = p.L->scalars;
+  a.sc_nmt = SC_NR + p.R;
+  a.status = p.L->status;
+  a.window = p.band_window > 0 ? p.band_window : 4;
+  a.ts = p.timestamps;
+  a.epoch = p.epoch;
+  a.flags = nullptr;
+  a.n_cons = 0;
+  return a;
+}
+
+int launch_ffn_gemm1(const FfnLaunch& p, int grid, hipStream_t st) {
+  GemmArgs a = base_args(p);
+  a.A = p.x_pad;
+  a.W = p.w_gate_up;
+  a.C = p.h;
+  a.K = p.d;
+  a.w_rows = 2 * p.f;
+  a.ldc = p.f;
+  a.f = p.f;
+  if (p.dtype == MOE_BF16) {
+    a.n_nt = p.f / (BF_BN / 2);
+    hipLaunchKernelGGL((k_gemm<bf16_t, BF_BM, BF_BN, 2, 2, true, false>), dim3(grid), dim3(256), BF_LDS_PAD, st,
+                       a);
+  } else {
+    a.n_nt = p.f / (F32_BN / 2);
+    hipLaunchKernelGGL((k_gemm<float, F32_BM, F32_BN, 2, 1, true, false>), dim3(grid), dim3(128), 0, st, a);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_ffn_gemm2(const FfnLaunch& p, int grid, int n_cons, hipStream_t st) {
+  GemmArgs a = base_args(p);
+  a.A = p.h;
+  a.W = p.w_down;
+  a.C = p.y_pad;
+  a.K = p.f;
+  a.w_rows = p.d;
+  a.ldc = p.d;
+  a.f = p.f;
+  a.flags = p.flags;
+  const int bn = ffn_gemm2_bn(p.dtype, p.d);
+  a.n_nt = p.d / bn;
+  a.n_cons = n_cons;
+  ConsumerArgs& c = a.cons;
+  c.y = (const uint4*)p.y_pad;
+  for (int r = 0; r < MOE_MAX_OWNERS; ++r) c.recv.p[r] = r < p.R ? p.recv[r] : nullptr;
+  c.seg_desc = p.L->seg_desc;
+  c.seg_mtiles = p.L->seg_mtiles;
+  c.scalars = p.L->scalars;
+  c.status = p.L->status;
+  c.flags = p.flags;
+  c.epoch = p.epoch;
+  c.n_nt = a.n_nt;
+  c.row_vec = p.d * (p.dtype == MOE_BF16 ? 2 : 4) / 16;
+  c.budget = p.watchdog_ticks;
+  c.ts = p.timestamps;
+  if (p.dtype == MOE_BF16) {
+    if (bn == BF_BN)
+      hipLaunchKernelGGL((k_gemm<bf16_t, BF_BM, BF_BN, 2, 2, false, true>), dim3(grid), dim3(256), BF_LDS_PAD, st,
+                         a);
+    else
+      hipLaunchKernelGGL((k_gemm<bf16_t, BF_BM, 64, 2, 2, false, true>), dim3(grid), dim3(256), 3 * BF_LDS_PAD, st,
+                         a);
+  } else {
+    hipLaunchKernelGGL((k_gemm<float, F32_BM, F32_BN, 2, 1, false, true>), dim3(grid), dim3(128), 0, st, a);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+__global__ void k_ts_init(uint64_t* ts) {
+  ts[0] = ~0ull;
+  ts[1] = 0ull;
+}
+
+int launch_ts_init(uint64_t* timestamps, hipStream_t st) {
+  hipLaunchKernelGGL(k_ts_init, dim3(1), dim3(1), 0, st, timestamps);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}

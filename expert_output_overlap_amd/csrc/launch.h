@@ -1,0 +1,57 @@
+// Internal launch interface between the C-ABI host code and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe_overlap.h"
+
+struct LayoutLaunch {
+  const int32_t* topk_idx;
+  const void* x;
+  void* x_pad;
+  moe_layout* L;
+  int R, T_o, G, k, lo, E, M, mgb, self_rank, mt_sub;
+  int64_t row_bytes;
+};
+
+// Expert FFN launch description (producer GEMMs and the consumer role of the second GEMM's launch).
+struct FfnLaunch {
+  int dtype;  // moe_dtype
+  int R, E, d, f;
+  const moe_layout* L;
+  const void* x_pad;
+  const void* w_gate_up;
+  const void* w_down;
+  void* h;
+  void* y_pad;
+  void* const* recv;
+  uint32_t* flags;
+  uint32_t epoch;
+  int band_window;
+  uint64_t watchdog_ticks;
+  uint64_t* timestamps;
+};
+
+struct CombineLaunch {
+  int dtype;
+  int R, T_o, k, d;
+  const moe_layout* L;
+  const float* topk_w;
+  void* const* recv;
+  void* out;
+};
+
+int launch_route(int T, int G, int k, const float* logits, int32_t* topk_idx, float* topk_w, hipStream_t st);
+int launch_layout(const LayoutLaunch& p, hipStream_t st);
+
+// GEMM row-tile height (rows) of the producer: the layout builds its row tiles from BM/16 sub-blocks.
+int ffn_gemm_bm(int dtype);
+// Output tile width of the second GEMM (y): flags are one per (row tile, column tile).
+int ffn_gemm2_bn(int dtype, int d);
+// One workgroup per CU for the first GEMM; the second GEMM's launch runs `n_cons` consumer workgroups
+// first (a launch with grid == n_cons is the consumer alone).
+int launch_ffn_gemm1(const FfnLaunch& p, int grid, hipStream_t st);
+int launch_ffn_gemm2(const FfnLaunch& p, int grid, int n_cons, hipStream_t st);
+int launch_ts_init(uint64_t* timestamps, hipStream_t st);
+int launch_combine(const CombineLaunch& p, hipStream_t st);

@@ -1,0 +1,400 @@
+// Remote-owner-aligned layout on the GPU (review page: "What carries the argument"; referee major
+// comment 1, section 4.5 / Algorithm 1): rows of each local expert grouped by owner rank, each
+// (expert, owner) group padded to a multiple of the tile height M, remote groups scheduled first.
+//
+//   k_layout_count   per 64-token chunk of one owner: histogram of local experts (wave ballots)
+//   k_layout_scan    one workgroup: chunk prefixes, group sizes, wavefront prefix scans of padded sizes,
+//                    band tables, remote-first order, transfer segments, GEMM row tiles
+//   k_layout_scatter per chunk: stable rank of each (token, slot) in its group -> row_src, combine plan
+//   k_gather_rows    x_pad[p] = x[row_src[p]] for real rows, 16-byte lanes
+#include "common.h"
+#include "launch.h"
+
+#define SCAN_THREADS 1024
+#define MAX_GROUPS (MOE_MAX_OWNERS * MOE_MAX_LOCAL_EXPERTS)
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+__global__ __launch_bounds__(256) void k_layout_count(const int32_t* __restrict__ topk_idx, int T_o, int G, int k,
+                                                      int lo, int E, int n_chunks, int32_t* __restrict__ chunk_counts,
+                                                      int32_t* __restrict__ status) {
+  const int wave = threadIdx.x / MOE_WAVE, lane = lane_id();
+  const int r = blockIdx.y;
+  const int c = blockIdx.x * 4 + wave;
+  if (c >= n_chunks) return;
+  const int t = c * 64 + lane;
+  uint64_t mask = 0;
+  bool bad = false;
+  if (t < T_o) {
+    const int32_t* ids = topk_idx + ((int64_t)r * T_o + t) * k;
+    for (int j = 0; j < k; ++j) {
+      const int g = ids[j];
+      bad |= (g < 0 || g >= G);
+      const int e = g - lo;
+      if (e >= 0 && e < E) {
+        bad |= ((mask >> e) & 1ull) != 0;  // the same local expert twice in one token
+        mask |= 1ull << e;
+      }
+    }
+  }
+  if (bad) set_status(status, MOE_EINVAL);
+  int mine = 0;
+  for (int e = 0; e < E; ++e) {
+    const int cnt = __popcll(__ballot((mask >> e) & 1ull));
+    if (lane == e) mine = cnt;
+  }
+  if (lane < E) chunk_counts[((int64_t)r * n_chunks + c) * E + lane] = mine;
+}
+
+// Exclusive scan of one value per thread over a 1024-thread block; *total gets the sum.
+__device__ int block_excl_scan(int v, int* s_wsum, int* total) {
+  const int wave = threadIdx.x / MOE_WAVE, lane = lane_id();
+  const int incl = wave_incl_scan(v);
+  __syncthreads();
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    const int w = lane < SCAN_THREADS / MOE_WAVE ? s_wsum[lane] : 0;
+    const int wi = wave_incl_scan(w);
+    if (lane < SCAN_THREADS / MOE_WAVE) s_wsum[lane] = wi - w;
+    if (lane == SCAN_THREADS / MOE_WAVE - 1) s_wsum[SCAN_THREADS / MOE_WAVE] = wi;
+  }
+  __syncthreads();
+  const int out = s_wsum[wave] + incl - v;
+  *total = s_wsum[SCAN_THREADS / MOE_WAVE];
+  __syncthreads();
+  return out;
+}
+
+struct ScanArgs {
+  int R, T_o, E, M, mgb, self_rank, n_chunks, mt_sub;
+  int64_t cap_rows, cap_tiles, cap_mtiles;
+  int32_t *chunk_counts, *counts, *padded_off, *recv_off, *tile_owner, *tile_expert, *tile_valid, *tile_order,
+      *seg_desc, *row_src, *scalars, *status, *mtile_desc, *seg_mtiles;
+};
+
+__global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
+  __shared__ int s_n[MAX_GROUPS];      // n_g
+  __shared__ int s_poff[MAX_GROUPS];   // padded offset of g
+  __shared__ int s_order[MAX_GROUPS];  // q -> g (non-empty groups, remote-first)
+  __shared__ int s_band_pos[MAX_GROUPS], s_seg_pos[MAX_GROUPS], s_sub_pos[MAX_GROUPS];
+  __shared__ int s_tile_base[MAX_GROUPS], s_run_off[MAX_GROUPS], s_run_subs[MAX_GROUPS];
+  __shared__ int s_wsum[SCAN_THREADS / MOE_WAVE + 1];
+  __shared__ int s_misc[4];
+
+  const int tid = threadIdx.x;
+  const int R = a.R, E = a.E, M = a.M, NG = E * R;
+  const int32_t status0 = load_status(a.status);
+
+  // (a) group sizes; per-(owner, expert) chunk counts become exclusive prefixes in place
+  for (int g = tid; g < NG; g += SCAN_THREADS) {
+    const int e = g / R, r = g % R;
+    int run = 0;
+    for (int c = 0; c < a.n_chunks; ++c) {
+      int32_t* p = a.chunk_counts + ((int64_t)r * a.n_chunks + c) * E + e;
+      const int v = *p;
+      *p = run;
+      run += v;
+    }
+    s_n[g] = run;
+    a.counts[g] = run;
+  }
+  __syncthreads();
+
+  // (b) padded offsets: exclusive scan of P = ceil(n/M)*M in (e, r) order
+  int total = 0;
+  {
+    const int n = tid < NG ? s_n[tid] : 0;
+    const int P = ((n + M - 1) / M) * M;
+    const int off = block_excl_scan(P, s_wsum, &total);
+    if (tid < NG) {
+      s_poff[tid] = off;
+      a.padded_off[tid] = off;
+    }
+  }
+  const int M_pad = total;
+  const int n_tiles = M_pad / M;
+  // (c) receive offsets per owner: sum over e' < e of n_{e', r}
+  if (tid < R) {
+    int run = 0;
+    for (int e = 0; e < E; ++e) {
+      a.recv_off[e * R + tid] = run;
+      run += s_n[e * R + tid];
+    }
+    a.scalars[SC_NR + tid] = run;
+  }
+  if ((int64_t)M_pad > a.cap_rows || status0 != 0) {
+    if (tid == 0) {
+      if (status0 == 0) set_status(a.status, MOE_ECAPACITY);
+      a.scalars[SC_MPAD] = 0;
+      a.scalars[SC_NTILES] = 0;
+      a.scalars[SC_NSEGS] = 0;
+      a.scalars[SC_NR + R] = 0;
+    }
+    return;
+  }
+  __syncthreads();
+
+  // (d) band tables and padding entries of row_src
+  for (int g = tid; g < NG; g += SCAN_THREADS) {
+    const int n = s_n[g], off = s_poff[g];
+    for (int row = 0; row < n; row += M) {
+      const int b = (off + row) / M;
+      a.tile_owner[b] = g % R;
+      a.tile_expert[b] = g / R;
+      const int valid = (n - row) < M ? (n - row) : M;
+      a.tile_valid[b] = valid;
+      for (int i = valid; i < M; ++i) a.row_src[(int64_t)b * M + i] = -1;
+    }
+  }
+
+  // (e) remote-first order of non-empty groups: key (owner == self, -P, e, r) ascending
+  {
+    int rank = 0;
+    const bool mine = tid < NG && s_n[tid] > 0;
+    if (mine) {
+      const int g = tid, e = g / R, r = g % R;
+      const int self = (r == a.self_rank), P = ((s_n[g] + M - 1) / M) * M;
+      for (int h = 0; h < NG; ++h) {
+        const int nh = s_n[h];
+        if (nh == 0 || h == g) continue;
+        const int eh = h / R, rh = h % R;
+        const int selfh = (rh == a.self_rank), Ph = ((nh + M - 1) / M) * M;
+        bool less;
+        if (selfh != self) less = selfh < self;
+        else if (Ph != P) less = Ph > P;
+        else if (eh != e) less = eh < e;
+        else less = rh < r;
+        rank += less;
+      }
+    }
+    int n_ne = 0;
+    block_excl_scan(mine ? 1 : 0, s_wsum, &n_ne);
+    if (mine) s_order[rank] = tid;
+    if (tid == 0) s_misc[0] = n_ne;
+    __syncthreads();
+  }
+  const int n_ne = s_misc[0];
+
+  // (f) per position q: band, segment and sub-block positions (exclusive scans in q order)
+  {
+    const int q = tid;
+    int nb = 0, ns = 0, nsub = 0;
+    if (q < n_ne) {
+      const int n = s_n[s_order[q]];
+      nb = (n + M - 1) / M;
+      ns = (nb + a.mgb - 1) / a.mgb;
+      nsub = (n + MOE_SUB - 1) / MOE_SUB;
+    }
+    int tb = 0, ts = 0, tsub = 0;
+    const int pb = block_excl_scan(nb, s_wsum, &tb);
+    const int ps = block_excl_scan(ns, s_wsum, &ts);
+    const int psub = block_excl_scan(nsub, s_wsum, &tsub);
+    if (q < n_ne) {
+      s_band_pos[q] = pb;
+      s_seg_pos[q] = ps;
+      s_sub_pos[q] = psub;
+    }
+    if (tid == 0) {
+      s_misc[1] = ts;
+      s_misc[2] = tsub;
+    }
+    __syncthreads();
+  }
+  const int n_segs = s_misc[1];
+
+  // (g) GEMM row tiles: runs of consecutive same-expert groups (in q order) cut into tiles of mt_sub
+  // sub-blocks; sequential over at most 1024 groups
+  if (tid == 0) {
+    int tile_base = 0, q0 = 0;
+    while (q0 < n_ne) {
+      const int e = s_order[q0] / R;
+      int q1 = q0;
+      while (q1 < n_ne && s_order[q1] / R == e) ++q1;
+      const int run_subs = (q1 < n_ne ? s_sub_pos[q1] : s_misc[2]) - s_sub_pos[q0];
+      for (int q = q0; q < q1; ++q) {
+        s_tile_base[q] = tile_base;
+        s_run_off[q] = s_sub_pos[q] - s_sub_pos[q0];
+        s_run_subs[q] = run_subs;
+      }
+      tile_base += (run_subs + a.mt_sub - 1) / a.mt_sub;
+      q0 = q1;
+    }
+    s_misc[3] = tile_base;
+  }
+  __syncthreads();
+  const int n_mtiles = s_misc[3];
+  if ((int64_t)n_mtiles > a.cap_mtiles) {  // cannot happen within the capacity bound; guard anyway
+    if (tid == 0) {
+      set_status(a.status, MOE_ECAPACITY);
+      a.scalars[SC_MPAD] = 0;
+      a.scalars[SC_NTILES] = 0;
+      a.scalars[SC_NSEGS] = 0;
+      a.scalars[SC_NR + R] = 0;
+    }
+    return;
+  }
+
+  // (h) per group: tile_order, segments, row-tile entries
+  for (int q = tid; q < n_ne; q += SCAN_THREADS) {
+    const int g = s_order[q], e = g / R, r = g % R, n = s_n[g], off = s_poff[g];
+    const int nb = (n + M - 1) / M, b0 = off / M;
+    for (int b = 0; b < nb; ++b) a.tile_order[s_band_pos[q] + b] = b0 + b;
+    const int base = s_tile_base[q], roff = s_run_off[q], rsubs = s_run_subs[q];
+    const int nsub = (n + MOE_SUB - 1) / MOE_SUB;
+    for (int j = 0; j < nsub; ++j) {
+      const int u = roff + j;
+      const int mt = base + u / a.mt_sub, slot = u % a.mt_sub;
+      int32_t* d = a.mtile_desc + (int64_t)mt * MOE_MT_FIELDS;
+      d[2 + slot] = off + MOE_SUB * j;
+      if (slot == 0) {
+        const int cnt = (rsubs - u) < a.mt_sub ? (rsubs - u) : a.mt_sub;
+        d[0] = e;
+        d[1] = cnt;
+        for (int s2 = cnt; s2 < MOE_MT_SUB; ++s2) d[2 + s2] = -1;
+      }
+    }
+    int sp = s_seg_pos[q];
+    for (int b = 0; b < nb; b += a.mgb, ++sp) {
+      const int cnt = (nb - b) < a.mgb ? (nb - b) : a.mgb;
+      int rows = n - b * M;
+      if (rows > cnt * M) rows = cnt * M;
+      int32_t* s = a.seg_desc + (int64_t)sp * MOE_SEG_FIELDS;
+      s[SEG_OWNER] = r;
+      s[SEG_EXPERT] = e;
+      s[SEG_FIRST_BAND] = b0 + b;
+      s[SEG_NBANDS] = cnt;
+      s[SEG_SRC_ROW] = off + b * M;
+      s[SEG_DST_ROW] = a.recv_off[g] + b * M;
+      s[SEG_ROWS] = rows;
+      s[SEG_GROUP] = g;
+      const int sub0 = (b * M) / MOE_SUB, sub1 = (b * M + rows - 1) / MOE_SUB;
+      const int mt0 = base + (roff + sub0) / a.mt_sub, mt1 = base + (roff + sub1) / a.mt_sub;
+      a.seg_mtiles[2 * sp] = mt0;
+      a.seg_mtiles[2 * sp + 1] = mt1 - mt0 + 1;
+    }
+  }
+  if (tid == 0) {
+    a.scalars[SC_MPAD] = M_pad;
+    a.scalars[SC_NTILES] = n_tiles;
+    a.scalars[SC_NSEGS] = n_segs;
+    a.scalars[SC_NR + R] = n_mtiles;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_layout_scatter(const int32_t* __restrict__ topk_idx, int R, int T_o, int k,
+                                                        int lo, int E, int n_chunks,
+                                                        const int32_t* __restrict__ chunk_prefix,
+                                                        const int32_t* __restrict__ padded_off,
+                                                        const int32_t* __restrict__ recv_off,
+                                                        int32_t* __restrict__ row_src, int32_t* __restrict__ plan,
+                                                        const int32_t* __restrict__ status) {
+  if (load_status(status) != 0) return;
+  const int wave = threadIdx.x / MOE_WAVE, lane = lane_id();
+  const int r = blockIdx.y;
+  const int c = blockIdx.x * 4 + wave;
+  if (c >= n_chunks) return;
+  const int t = c * 64 + lane;
+  const bool valid = t < T_o;
+  const int64_t tok = (int64_t)r * T_o + t;
+  uint64_t mask = 0;
+  int slot_of[MOE_MAX_LOCAL_EXPERTS > 16 ? 16 : 16];  // slot j -> local expert or -1 (k <= 16)
+  for (int j = 0; j < k; ++j) {
+    int e = -1;
+    if (valid) {
+      e = topk_idx[tok * k + j] - lo;
+      if (e < 0 || e >= E) e = -1;
+    }
+    slot_of[j] = e;
+    if (e >= 0) mask |= 1ull << e;
+    if (valid && e < 0) plan[tok * k + j] = -1;
+  }
+  const uint64_t lt = lanemask_lt();
+  const int32_t* pre = chunk_prefix + ((int64_t)r * n_chunks + c) * E;
+  for (int e = 0; e < E; ++e) {
+    const uint64_t b = __ballot((mask >> e) & 1ull);
+    if ((mask >> e) & 1ull) {
+      const int g = e * R + r;
+      const int rank = pre[e] + __popcll(b & lt);
+      row_src[(int64_t)padded_off[g] + rank] = (int32_t)tok;
+      for (int j = 0; j < k; ++j)
+        if (slot_of[j] == e) plan[tok * k + j] = recv_off[g] + rank;
+    }
+  }
+}
+
+// x_pad[p] = x[row_src[p]] for the real rows; one wavefront per row, 16-byte lanes.
+__global__ __launch_bounds__(256) void k_gather_rows(const uint4* __restrict__ x, uint4* __restrict__ x_pad,
+                                                     const int32_t* __restrict__ row_src,
+                                                     const int32_t* __restrict__ scalars, int row_vec,
+                                                     const int32_t* __restrict__ status) {
+  if (load_status(status) != 0) return;
+  const int M_pad = scalars[SC_MPAD];
+  const int wave = threadIdx.x / MOE_WAVE, lane = lane_id();
+  for (int p = blockIdx.x * 4 + wave; p < M_pad; p += gridDim.x * 4) {
+    const int src = row_src[p];
+    if (src < 0) continue;
+    const uint4* s = x + (int64_t)src * row_vec;
+    uint4* d = x_pad + (int64_t)p * row_vec;
+    int i = lane;
+    for (; i + 192 < row_vec; i += 256) {
+      const uint4 v0 = s[i], v1 = s[i + 64], v2 = s[i + 128], v3 = s[i + 192];
+      d[i] = v0;
+      d[i + 64] = v1;
+      d[i + 128] = v2;
+      d[i + 192] = v3;
+    }
+    for (; i < row_vec; i += 64) d[i] = s[i];
+  }
+}
+
+__global__ void k_reset_status(int32_t* status) { *status = 0; }
+
+int launch_layout(const LayoutLaunch& p, hipStream_t st) {
+  const int n_chunks = (p.T_o + 63) / 64;
+  hipLaunchKernelGGL(k_reset_status, dim3(1), dim3(1), 0, st, p.L->status);
+  if (n_chunks > 0)
+    hipLaunchKernelGGL(k_layout_count, dim3((n_chunks + 3) / 4, p.R), dim3(256), 0, st, p.topk_idx, p.T_o, p.G, p.k,
+                       p.lo, p.E, n_chunks, p.L->chunk_counts, p.L->status);
+  ScanArgs a;
+  a.R = p.R;
+  a.T_o = p.T_o;
+  a.E = p.E;
+  a.M = p.M;
+  a.mgb = p.mgb;
+  a.self_rank = p.self_rank;
+  a.n_chunks = n_chunks;
+  a.mt_sub = p.mt_sub;
+  a.cap_rows = p.L->cap_rows;
+  a.cap_tiles = p.L->cap_tiles;
+  a.cap_mtiles = p.L->cap_mtiles;
+  a.chunk_counts = p.L->chunk_counts;
+  a.counts = p.L->counts;
+  a.padded_off = p.L->padded_off;
+  a.recv_off = p.L->recv_off;
+  a.tile_owner = p.L->tile_owner;
+  a.tile_expert = p.L->tile_expert;
+  a.tile_valid = p.L->tile_valid;
+  a.tile_order = p.L->tile_order;
+  a.seg_desc = p.L->seg_desc;
+  a.row_src = p.L->row_src;
+  a.scalars = p.L->scalars;
+  a.status = p.L->status;
+  a.mtile_desc = p.L->mtile_desc;
+  a.seg_mtiles = p.L->seg_mtiles;
+  hipLaunchKernelGGL(k_layout_scan, dim3(1), dim3(SCAN_THREADS), 0, st, a);
+  if (n_chunks > 0)
+    hipLaunchKernelGGL(k_layout_scatter, dim3((n_chunks + 3) / 4, p.R), dim3(256), 0, st, p.topk_idx, p.R, p.T_o,
+                       p.k, p.lo, p.E, n_chunks, p.L->chunk_counts, p.L->padded_off, p.L->recv_off, p.L->row_src,
+                       p.L->combine_plan, p.L->status);
+  const int row_vec = (int)(p.row_bytes / 16);
+  int64_t blocks = (p.L->cap_rows + 3) / 4;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks > 0)
+    hipLaunchKernelGGL(k_gather_rows, dim3((unsigned)blocks), dim3(256), 0, st, (const uint4*)p.x, (uint4*)p.x_pad,
+                       p.L->row_src, p.L->scalars, row_vec, p.L->status);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}

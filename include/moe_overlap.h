@@ -1,0 +1,196 @@
+/*
+ * moe_overlap.h - C ABI of the MI355X (gfx950) MoE expert-compute-plus-return path.
+ *
+ * The method: "Fine-grained Computation-Communication Overlap via Tile-level Signaling and Scheduling for
+ * Mixture-of-Experts" (Cui, Wingkvist, Ericsson; arXiv 2607.19539), as described on its review page.
+ * An expert-parallel rank computes the expert FFN for every row routed to its local experts and returns
+ * each output row to the rank that owns the token.  Rows are laid out grouped by (local expert, owner rank)
+ * and padded to the tile height, so every output tile has one owner ("What carries the argument"; referee
+ * major comment 1, section 4.5 / Algorithm 1).  A persistent grouped GEMM (the producer) publishes a
+ * readiness flag per output tile while a persistent consumer on a small CU partition forwards finished
+ * row-band segments to their owners ("The pith"; "Core claim").  Here all R owner ranks are R receive
+ * buffers in the local HBM of one GPU: the consumer's transfers are device-memory copies.
+ *
+ * Conventions shared by every entry point
+ *  - Pointers marked (device) are device memory; everything else is host memory.  The caller owns every
+ *    buffer; the library allocates no device memory and creates no streams.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every call is asynchronous on it.
+ *  - Return values are moe_status codes for synchronous (host-side) checks: MOE_EINVAL for a bad shape,
+ *    a null pointer or an unsupported size, MOE_EHIP when a HIP call or launch fails.  moe_last_error()
+ *    gives a message.  Errors found on the device (capacity overflow, consumer watchdog) are written to
+ *    the layout's device status word; read it with moe_read_status().  Kernels that follow a failed one
+ *    see the nonzero status and do nothing.
+ *  - Not thread-safe for one moe_layout; calls that share a layout or flag array must be ordered.
+ *  - Matrices are row-major.  Weights follow the (out, in) convention of a linear layer.
+ *  - Element type: MOE_BF16 (activations, weights, hidden h, outputs in bf16, fp32 accumulation) or
+ *    MOE_F32 (everything fp32).  topk weights are always fp32, ids int32.
+ */
+#ifndef MOE_OVERLAP_H
+#define MOE_OVERLAP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MOE_OK = 0, MOE_EINVAL = -1, MOE_ECAPACITY = -2, MOE_EHIP = -3, MOE_ETIMEOUT = -4 } moe_status;
+typedef enum { MOE_BF16 = 0, MOE_F32 = 1 } moe_dtype;
+
+#define MOE_MAX_OWNERS 16      /* R <= 16 owner ranks */
+#define MOE_MAX_LOCAL_EXPERTS 64
+#define MOE_SEG_FIELDS 8       /* int32 fields of one segment descriptor, see moe_layout.seg_desc */
+
+/* Problem shape.  Tokens are owner-major: token row r*tokens_per_owner + t belongs to owner rank r.
+ * Local experts are global ids [self_rank*num_local_experts, (self_rank+1)*num_local_experts). */
+typedef struct {
+  int32_t R;                  /* owner ranks, 1..MOE_MAX_OWNERS */
+  int32_t tokens_per_owner;   /* T_o >= 0; T = R*T_o */
+  int32_t num_global_experts; /* G >= 1 */
+  int32_t num_local_experts;  /* E_l, 1..MOE_MAX_LOCAL_EXPERTS, G % E_l == 0 */
+  int32_t top_k;              /* k, 1..min(G, 16) */
+  int32_t self_rank;          /* this rank, 0 <= self_rank < G/E_l and < R */
+  int32_t d;                  /* hidden size, multiple of 64 */
+  int32_t f;                  /* FFN width, multiple of 64 */
+  int32_t tile_m;             /* layout tile height M (rows per band), multiple of 16, <= 256 */
+  int32_t seg_bands;          /* mgb: bands per transfer segment, >= 1 */
+  int32_t dtype;              /* moe_dtype */
+} moe_shape;
+
+/* Layout and its metadata (all device pointers into one caller workspace, see moe_layout_bind).
+ * Group g = e*R + r is the rows of owner r routed to local expert e, n_{e,r} rows, padded to
+ * P = ceil(n/M)*M.  Band (tile) b covers padded rows [b*M, (b+1)*M). */
+typedef struct {
+  int32_t* counts;       /* [E_l*R]  n_{e,r} */
+  int32_t* padded_off;   /* [E_l*R]  first padded row of group g: exclusive prefix of P in g order */
+  int32_t* recv_off;     /* [E_l*R]  first row of group g in owner r's receive buffer: sum_{e'<e} n_{e',r} */
+  int32_t* tile_owner;   /* [cap_tiles] owner of band b */
+  int32_t* tile_expert;  /* [cap_tiles] local expert of band b */
+  int32_t* tile_valid;   /* [cap_tiles] real rows in band b (1..M) */
+  int32_t* tile_order;   /* [cap_tiles] bands in remote-first order: groups by (owner == self, -P, e, r),
+                            bands ascending inside a group */
+  int32_t* seg_desc;     /* [cap_tiles][MOE_SEG_FIELDS] transfer segments in tile_order order, each up to
+                            seg_bands bands of one group: {owner, expert, first_band, n_bands, src_row,
+                            dst_row, rows, group}; rows counts real rows only */
+  int32_t* row_src;      /* [cap_rows] token row of each padded row, -1 for padding */
+  int32_t* combine_plan; /* [T*k] receive-buffer row of token slot (t, j) in its owner's buffer, -1 if the
+                            expert is not local */
+  int32_t* scalars;      /* [4+R] M_pad, n_tiles, n_segs, N_r[0..R), n_mtiles */
+  int32_t* status;       /* [1] device status word (moe_status) */
+  int32_t* mtile_desc;   /* [cap_mtiles][18] GEMM row tiles: {expert, n_sub, sub_start[16]}, 16-row
+                            sub-blocks of one expert that hold at least one real row (internal schedule) */
+  int32_t* seg_mtiles;   /* [cap_tiles][2] first GEMM row tile and count a segment depends on (internal) */
+  int32_t* chunk_counts; /* [R][ceil(T_o/64)][E_l] per-64-token histogram, then its prefix (internal) */
+  int64_t cap_rows;      /* capacity in padded rows (x_pad, h, y_pad, row_src) */
+  int64_t cap_tiles;     /* cap_rows / M */
+  int64_t cap_mtiles;    /* capacity of mtile_desc */
+} moe_layout;
+
+/* Knobs of moe_expert_ffn_overlap. */
+typedef struct {
+  int32_t consumer_cus;    /* C: consumer workgroups, one per CU, in [1, CUs/2]; the producer's persistent
+                              launch runs one workgroup on each other CU */
+  int32_t mode;            /* 0 = overlapped (the C consumer workgroups and the producers of the second GEMM in
+                                  one launch, on disjoint CUs),
+                              1 = sequential (producer on all CUs, then the consumer),
+                              2 = return only (the consumer alone, on consumer_cus workgroups, for flags
+                                  already published with this epoch; a flag never published ends in the
+                                  watchdog) */
+  uint32_t epoch;          /* flag value of this call: nonzero and different from what the flag array holds
+                              (flags start zeroed; pass 1, 2, 3, ...) */
+  int32_t band_window;     /* GEMM row tiles per weight-reuse window (0 = library default) */
+  uint64_t watchdog_ticks; /* consumer spin budget in 100 MHz ticks (0 = 2 s); on expiry the status word
+                              becomes MOE_ETIMEOUT and the consumer exits */
+  uint64_t* timestamps;    /* optional (device) [2 + 2*cap_tiles] u64, 100 MHz clock: [0] first producer
+                              item start, [1] last flag publish, [2+2s] / [3+2s] copy start / end of segment
+                              s; NULL to skip */
+} moe_overlap_cfg;
+
+/* Last host-side error message of the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Library build identifier, e.g. "moe_overlap gfx950". */
+const char* moe_version(void);
+
+/* ---- routing (input of the path) ----------------------------------------------------------------
+ * Per token: top-k of G logits, descending, equal logits to the lower expert id; weight of a chosen
+ * expert = softmax over all G logits at that id, not renormalised over the k (the router output the
+ * review page's ledger, axiom 3, takes as known before the return).
+ * logits (device) fp32 [T, G]; topk_idx (device) int32 [T, k]; topk_w (device) fp32 [T, k]. */
+int moe_route(const moe_shape* s, const float* logits, int32_t* topk_idx, float* topk_w, void* stream);
+
+/* ---- layout -------------------------------------------------------------------------------------- */
+
+/* Capacity bound of the padded row count: T*min(k, E_l) + E_l*R*(M-1), rounded up to M.
+ * Returns -1 for an invalid shape. */
+int64_t moe_layout_capacity_rows(const moe_shape* s);
+
+/* Bytes of device workspace that moe_layout_bind carves (256-byte aligned arrays); -1 if invalid. */
+int64_t moe_layout_workspace_bytes(const moe_shape* s);
+
+/* Host-only: point the arrays of *L into `workspace` (device, >= moe_layout_workspace_bytes bytes,
+ * 256-byte aligned).  No device work. */
+int moe_layout_bind(const moe_shape* s, void* workspace, int64_t workspace_bytes, moe_layout* L);
+
+/* Build the remote-owner-aligned layout (review page: "What carries the argument"; referee major comment
+ * 1 restating Algorithm 1): histogram of (expert, owner) groups, prefix scans and metadata, stable
+ * scatter (rows of a group ascend by token), and the gather of token rows into x_pad.
+ * topk_idx (device) int32 [T, k]; x (device) [T, d] in s->dtype; x_pad (device) [cap_rows, d].
+ * Padding rows of x_pad are not written.  Resets the status word to MOE_OK first; sets MOE_ECAPACITY if
+ * the padded rows exceed L->cap_rows (then all outputs are left empty: M_pad = 0). */
+int moe_layout_build(const moe_shape* s, const int32_t* topk_idx, const void* x, moe_layout* L, void* x_pad,
+                     void* stream);
+
+/* Syncs `stream` and returns the device status word. */
+int moe_read_status(const moe_layout* L, void* stream);
+
+/* ---- expert FFN + return ------------------------------------------------------------------------- */
+
+/* Number of uint32 readiness flags moe_expert_ffn_overlap needs (one per output tile of the second GEMM);
+ * -1 if the shape is invalid. */
+int64_t moe_ffn_flags_count(const moe_shape* s);
+
+/* Expert SwiGLU FFN over the padded layout with the return of each finished row-band segment to its
+ * owner (review page: "The pith", "Core claim", "What carries the argument").
+ *   h = bf16(silu(x Wg^T) * (x Wu^T)),  y = h Wd^T, per row with the row's local expert;
+ *   Wg = rows [0, f) and Wu = rows [f, 2f) of w_gate_up[e].
+ * The producer (a persistent grouped GEMM over all local experts, remote-first order) stores y tiles and
+ * publishes flags[tile] = epoch with an agent-scope release; the consumer acquires the flags of a segment
+ * and copies its real rows into recv[owner].  Launches: the first GEMM on every CU, then one launch whose
+ * first C workgroups are the consumer and whose others run the second GEMM (overlapped mode).  Owner r receives, at row recv_off_{e,r} + i, the FFN output
+ * of the i-th row of group (e, r).
+ * x_pad (device) [cap_rows, d]; w_gate_up (device) [E_l, 2f, d]; w_down (device) [E_l, d, f];
+ * h_ws (device) [cap_rows, f] workspace; y_pad (device) [cap_rows, d]; recv: host array of R device
+ * pointers, recv[r] holds >= N_r rows of d; flags (device) uint32 [moe_ffn_flags_count] (zeroed before the
+ * first call); cfg: see moe_overlap_cfg. */
+int moe_expert_ffn_overlap(const moe_shape* s, const moe_layout* L, const void* x_pad, const void* w_gate_up,
+                           const void* w_down, void* h_ws, void* y_pad, void* const* recv, uint32_t* flags,
+                           const moe_overlap_cfg* cfg, void* stream);
+
+/* ---- combine ------------------------------------------------------------------------------------- */
+
+/* Top-k weighted combine at the owners (review page ledger, axiom 3: the combine plan is known from the
+ * router output).  out[r*T_o+t] = sum over slots j ascending with plan >= 0 of
+ * topk_w[t, j] * recv[r][plan[t, j]], fp32 accumulation, rounded to the element type; tokens with no local
+ * expert get zeros.  topk_w (device) fp32 [T, k]; recv: host array of R device pointers; out (device)
+ * [T, d]. */
+int moe_combine(const moe_shape* s, const moe_layout* L, const float* topk_w, void* const* recv, void* out,
+                void* stream);
+
+/* ---- kernel timing ------------------------------------------------------------------------------- */
+
+/* While enabled (nonzero), every moe_expert_ffn_overlap call of this process records HIP timing events
+ * around its launches on the caller's stream.  Disabled by default.  Returns MOE_OK. */
+int moe_set_kernel_timing(int enable);
+
+/* Waits for the recorded events and writes the summed milliseconds since the last query:
+ * out[0] first GEMM (gate/up + SwiGLU), out[1] second GEMM launch (down projection + flag publish, with the
+ * consumer workgroups in overlapped mode), out[2] the separate consumer launch of sequential mode (0 in
+ * overlapped mode), out[3] number of calls recorded.  Clears the record. */
+int moe_kernel_times(double* out4);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_OVERLAP_H */

@@ -1,0 +1,100 @@
+"""The C-ABI library loads and exports every entry point its header declares; host-only helpers (sizes,
+workspace carving, argument checks) behave as documented.  No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from expert_output_overlap_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe_overlap.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.lib()
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(B.EXPORTS) == names
+
+
+def test_version():
+    assert "gfx950" in B.moe_version()
+
+
+def shape(**kw):
+    base = dict(R=4, tokens_per_owner=1024, num_global_experts=8, num_local_experts=2, top_k=2, self_rank=0, d=4096,
+                f=14336, tile_m=128, seg_bands=1, dtype=B.MOE_BF16)
+    base.update(kw)
+    return B.moe_shape(**base)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(R=8, tokens_per_owner=2048, num_global_experts=256, num_local_experts=32,
+                                            top_k=8, d=7168, f=2048), dict(tile_m=64, top_k=6, num_local_experts=16,
+                                                                           num_global_experts=64)])
+def test_capacity_matches_bound(kw):
+    s = shape(**kw)
+    cap = B.moe_layout_capacity_rows(s)
+    assert cap == oracle.capacity_rows(s.R, s.tokens_per_owner, s.num_local_experts, s.top_k, s.tile_m)
+
+
+@pytest.mark.parametrize("bad", [dict(R=0), dict(R=17), dict(d=96), dict(f=0), dict(tile_m=24), dict(tile_m=272),
+                                 dict(top_k=0), dict(top_k=9), dict(num_local_experts=3), dict(self_rank=4),
+                                 dict(dtype=7), dict(seg_bands=0), dict(tokens_per_owner=-1),
+                                 dict(num_local_experts=65, num_global_experts=130)])
+def test_invalid_shapes_rejected(bad):
+    s = shape(**bad)
+    assert B.moe_layout_capacity_rows(s) == -1
+    assert B.moe_layout_workspace_bytes(s) == -1
+    assert B.moe_ffn_flags_count(s) == -1
+    L = B.moe_layout()
+    buf = np.zeros(1 << 16, np.uint8)
+    assert B.lib().moe_layout_bind(ctypes.byref(s), ctypes.c_void_p(buf.ctypes.data), buf.size,
+                                   ctypes.byref(L)) == B.MOE_EINVAL
+    assert B.moe_last_error() != ""
+
+
+def test_bind_carves_disjoint_aligned_arrays():
+    s = shape(R=3, tokens_per_owner=300, num_global_experts=12, num_local_experts=4, d=256, f=512, tile_m=32)
+    nbytes = B.moe_layout_workspace_bytes(s)
+    buf = np.zeros(nbytes + 512, np.uint8)
+    base = (buf.ctypes.data + 255) // 256 * 256
+    L = B.moe_layout()
+    lib = B.lib()
+    assert lib.moe_layout_bind(ctypes.byref(s), ctypes.c_void_p(base), nbytes - 1, ctypes.byref(L)) == B.MOE_EINVAL
+    assert lib.moe_layout_bind(ctypes.byref(s), ctypes.c_void_p(base + 4), nbytes, ctypes.byref(L)) == B.MOE_EINVAL
+    assert lib.moe_layout_bind(ctypes.byref(s), ctypes.c_void_p(base), nbytes, ctypes.byref(L)) == B.MOE_OK
+    NG = s.num_local_experts * s.R
+    T = s.R * s.tokens_per_owner
+    sizes = {"counts": NG, "padded_off": NG, "recv_off": NG, "tile_owner": L.cap_tiles, "tile_expert": L.cap_tiles,
+             "tile_valid": L.cap_tiles, "tile_order": L.cap_tiles, "seg_desc": 8 * L.cap_tiles,
+             "row_src": L.cap_rows, "combine_plan": T * s.top_k, "scalars": 4 + s.R, "status": 1,
+             "mtile_desc": 18 * L.cap_mtiles, "seg_mtiles": 2 * L.cap_tiles,
+             "chunk_counts": s.R * ((s.tokens_per_owner + 63) // 64) * s.num_local_experts}
+    spans = sorted((getattr(L, n) - base, getattr(L, n) - base + 4 * sizes[n], n) for n in sizes)
+    for (a0, a1, n), (b0, b1, m) in zip(spans, spans[1:]):
+        assert a1 <= b0, (n, m)
+    assert spans[0][0] >= 0 and spans[-1][1] <= nbytes
+    assert all(a % 256 == 0 for a, _, _ in spans)
+    assert L.cap_tiles * s.tile_m == L.cap_rows
+
+
+def test_flag_count_covers_row_tiles():
+    s = shape()
+    L = B.moe_layout()
+    nbytes = B.moe_layout_workspace_bytes(s)
+    buf = np.zeros(nbytes + 256, np.uint8)
+    base = (buf.ctypes.data + 255) // 256 * 256
+    assert B.lib().moe_layout_bind(ctypes.byref(s), ctypes.c_void_p(base), nbytes, ctypes.byref(L)) == 0
+    nflags = B.moe_ffn_flags_count(s)
+    assert nflags % L.cap_mtiles == 0 and nflags // L.cap_mtiles >= 1

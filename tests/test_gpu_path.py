@@ -1,0 +1,307 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C-ABI.
+
+Layout arrays and permutations bit for bit; FFN output rows, delivered rows and the combined output within the
+tolerance of ``tolerance.py``; delivery bit-equal to the GPU's own y rows; sequential and overlapped runs bitwise
+equal.  Small shapes are compared element by element; the full-size workloads compare the complete layout and
+sampled rows and tokens, in the launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle
+import tolerance
+from expert_output_overlap_amd import binding as B
+from expert_output_overlap_amd.runtime import MoePath, to_device
+
+pytestmark = pytest.mark.gpu
+
+LAYOUT_INT = ["counts", "padded_off", "recv_off"]
+
+
+def _require_gpu():
+    assert torch.cuda.is_available(), "the gpu tests need the MI355X"
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16 if t.element_size() == 2 else torch.int32).cpu().numpy()
+
+
+class Run:
+    """Inputs of one workload on host and device, the GPU path's buffers, and the oracle's routing and layout."""
+
+    def __init__(self, s, logits=None):
+        _require_gpu()
+        print("case", s, flush=True)
+        self.s = s
+        self.inp = mi.inputs(s)
+        if logits is not None:
+            self.inp["logits"] = logits
+        self.P = MoePath.from_spec(s)
+        self.dev = {k: to_device(v, s.dtype) for k, v in self.inp.items()}
+        self.P.route(self.dev["logits"])
+        self.P.layout(self.dev["x"])
+        self.idx, self.w = oracle.route(self.inp["logits"], s.k)
+        self.lay = oracle.layout(self.idx, s.R, s.T_o, s.G, s.E_l, s.k, s.M, s.mgb, 0)
+
+    def ffn(self, **kw):
+        self.P.ffn(self.dev["w_gate_up"], self.dev["w_down"], **kw)
+
+    def check_rows(self, rows, what="y"):
+        """Check the GPU's y at padded rows ``rows`` (real rows) against the oracle, up to the oracle's own
+        alternative roundings of h; returns the oracle reference rows that matched."""
+        lay, s = self.lay, self.s
+        bf = s.dtype == "bf16"
+        ex = oracle.ffn_rows_ex(lay["row_src"][rows], lay["tile_expert"][rows // s.M], self.inp["x"],
+                                self.inp["w_gate_up"], self.inp["w_down"], bf)
+        ref, flips = tolerance.check_ffn(f64(self.P.y_pad)[rows], ex, what, bf)
+        print("%s: %d rows, %d alternative h roundings taken" % (what, len(rows), flips), flush=True)
+        return ref
+
+
+def check_route_and_layout(run):
+    s, P, lay = run.s, run.P, run.lay
+    torch.cuda.synchronize()
+    assert P.status() == B.MOE_OK
+    np.testing.assert_array_equal(P.topk_idx[: s.T].cpu().numpy(), run.idx)
+    np.testing.assert_allclose(P.topk_w[: s.T].cpu().numpy(), run.w, rtol=2e-6, atol=1e-9)
+    for n in LAYOUT_INT:
+        np.testing.assert_array_equal(P.array(n).cpu().numpy(), lay[n], err_msg=n)
+    sc = P.scalars()
+    assert (sc["M_pad"], sc["n_tiles"], sc["n_segs"]) == (lay["M_pad"], lay["n_tiles"], lay["n_segs"])
+    assert sc["N_r"] == lay["N_r"].tolist()
+    nt, ns = lay["n_tiles"], lay["n_segs"]
+    for n in ("tile_owner", "tile_expert", "tile_valid", "tile_order"):
+        np.testing.assert_array_equal(P.array(n)[:nt].cpu().numpy(), lay[n], err_msg=n)
+    np.testing.assert_array_equal(P.array("seg_desc").view(-1, 8)[:ns].cpu().numpy(), lay["seg_desc"])
+    np.testing.assert_array_equal(P.array("row_src")[: lay["M_pad"]].cpu().numpy(), lay["row_src"])
+    np.testing.assert_array_equal(P.array("combine_plan").view(-1, s.k).cpu().numpy(), lay["combine_plan"])
+    real = np.nonzero(lay["row_src"] >= 0)[0]
+    xb = bits(P.x_pad)
+    np.testing.assert_array_equal(xb[real], bits(run.dev["x"])[lay["row_src"][real]])
+    check_schedule(run)
+
+
+def check_schedule(run):
+    """GEMM row tiles cover every real row exactly once, with one expert each, and every segment's row tiles
+    contain all of its rows (host-side property check of the internal schedule)."""
+    P, lay, s = run.P, run.lay, run.s
+    n_mt = P.scalars()["n_mtiles"]
+    desc = P.array("mtile_desc").view(-1, B.MT_FIELDS)[:n_mt].cpu().numpy()
+    covered = np.zeros(lay["M_pad"], np.int32)
+    tile_of_row = np.full(lay["M_pad"], -1)
+    for mt, dsc in enumerate(desc):
+        e, nsub = dsc[0], dsc[1]
+        assert 1 <= nsub <= 16 and (dsc[2 + nsub:] == -1).all()
+        for st in dsc[2:2 + nsub]:
+            assert st % 16 == 0
+            covered[st:st + 16] += 1
+            tile_of_row[st:st + 16] = mt
+            assert (lay["tile_expert"][st // s.M] == e)
+    real = lay["row_src"] >= 0
+    assert (covered[real] == 1).all() and (covered <= 1).all()
+    segm = P.array("seg_mtiles").view(-1, 2)[: lay["n_segs"]].cpu().numpy()
+    for sd, (m0, mc) in zip(lay["seg_desc"], segm):
+        rows = np.arange(sd[4], sd[4] + sd[6])
+        assert ((tile_of_row[rows] >= m0) & (tile_of_row[rows] < m0 + mc)).all()
+
+
+def check_delivery(run):
+    """recv[r] rows are the GPU's own y rows of group (e, r), bit for bit; rows past N_r untouched (NaN canary)."""
+    P, lay, s = run.P, run.lay, run.s
+    yb = bits(P.y_pad)
+    for r in range(s.R):
+        rb = bits(P.recv[r])
+        n_r = int(lay["N_r"][r])
+        for e in range(s.E_l):
+            g = e * s.R + r
+            n, po, ro = lay["counts"][g], lay["padded_off"][g], lay["recv_off"][g]
+            np.testing.assert_array_equal(rb[ro:ro + n], yb[po:po + n], err_msg="owner %d expert %d" % (r, e))
+        tail = f64(P.recv[r][n_r:P.recv_cap])
+        assert np.isnan(tail).all(), "rows past N_r were written"
+
+
+SMALL = [
+    mi.spec("tiny"), mi.spec("tiny_f32"), mi.spec("tiny", mgb=2),
+    mi.Spec("ragged", R=4, T_o=300, G=16, E_l=4, k=2, d=256, f=512, M=32, seed=11),
+    mi.Spec("ragged_skew", R=3, T_o=500, G=12, E_l=4, k=3, d=192, f=320, M=48, seed=12, bias="zipf",
+            bias_param=1.2, mgb=2),
+    mi.Spec("one_owner", R=1, T_o=200, G=1, E_l=1, k=1, d=128, f=128, M=16, seed=13),
+    mi.Spec("k_eq_el", R=2, T_o=70, G=6, E_l=3, k=3, d=128, f=192, M=64, seed=14),
+    mi.Spec("f32_ragged", R=3, T_o=90, G=9, E_l=3, k=2, d=128, f=192, M=32, dtype="f32", seed=15),
+]
+
+
+@pytest.mark.parametrize("s", SMALL, ids=lambda s: s.name + ("_mgb%d" % s.mgb))
+def test_small_full_parity(s):
+    run = Run(s)
+    check_route_and_layout(run)
+    P, lay = run.P, run.lay
+    for r in range(s.R):
+        P.recv[r].fill_(float("nan"))
+    run.ffn(mode=0, consumer_cus=4)
+    torch.cuda.synchronize()
+    assert P.status() == B.MOE_OK
+    real = np.nonzero(lay["row_src"] >= 0)[0]
+    y_ref = run.check_rows(real)
+    check_delivery(run)
+    y_pad = np.full((lay["M_pad"], s.d), np.nan)
+    y_pad[real] = y_ref
+    recv_ref = oracle.deliver(lay, y_pad, s.R, s.E_l)
+    for r in range(s.R):
+        tolerance.check(f64(P.recv[r][: int(lay["N_r"][r])]), recv_ref[r], "recv[%d]" % r)
+    P.combine()
+    torch.cuda.synchronize()
+    out_ref = oracle.combine(lay, run.w, recv_ref, s.R, s.T_o, s.k, s.dtype == "bf16")
+    tolerance.check(f64(P.out[: s.T]), out_ref, "out")
+    # sequential mode gives the same bits
+    recv_ovl = [bits(b) for b in P.recv]
+    out_ovl = bits(P.out)
+    run.ffn(mode=1, consumer_cus=4)
+    P.combine()
+    torch.cuda.synchronize()
+    for r in range(s.R):
+        np.testing.assert_array_equal(bits(P.recv[r]), recv_ovl[r])
+    np.testing.assert_array_equal(bits(P.out), out_ovl)
+
+
+FULL = ["mixtral", "skew", "sweep1", "sweep2", "sweep4", "sweep8", "sweep16", "deepseek"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_parity(name):
+    """Full-size workload in the benchmark's launch configuration: whole layout, sampled rows and tokens."""
+    s = mi.spec(name)
+    run = Run(s)
+    check_route_and_layout(run)
+    P, lay = run.P, run.lay
+    for r in range(s.R):
+        P.recv[r].fill_(float("nan"))
+    run.ffn(mode=0, consumer_cus=16)
+    P.combine()
+    torch.cuda.synchronize()
+    assert P.status() == B.MOE_OK
+    check_delivery(run)
+    rng = np.random.default_rng(0)
+    real = np.nonzero(lay["row_src"] >= 0)[0]
+    ne = lay["counts"] > 0
+    ends = np.concatenate([lay["padded_off"][ne], (lay["padded_off"] + lay["counts"] - 1)[ne]])
+    rows = np.unique(np.concatenate([rng.choice(real, 24, replace=False), rng.choice(ends, 8, replace=False)]))
+    run.check_rows(rows, "y rows")
+    # combine for sampled tokens: the oracle's FFN rows of their local slots, the oracle's combine
+    toks = rng.choice(s.T, 16, replace=False)
+    plan = lay["combine_plan"][toks]
+    src_rows = []
+    mini_plan = np.full_like(plan, -1)
+    for i, t in enumerate(toks):
+        r = t // s.T_o
+        for j in range(s.k):
+            if plan[i, j] >= 0:
+                e = run.idx[t, j]
+                g = e * s.R + r
+                p = lay["padded_off"][g] + plan[i, j] - lay["recv_off"][g]
+                mini_plan[i, j] = len(src_rows)
+                src_rows.append(p)
+    y_rows = run.check_rows(np.array(src_rows, dtype=np.int64), "y of sampled tokens") if src_rows else \
+        np.zeros((0, s.d))
+    mini = {"combine_plan": np.ascontiguousarray(mini_plan, dtype=np.int32)}
+    out_ref = oracle.combine(mini, run.w[toks], [y_rows], 1, len(toks), s.k, s.dtype == "bf16")
+    tolerance.check(f64(P.out)[toks], out_ref, "out tokens")
+    # sequential == overlapped, bitwise
+    recv_ovl = [bits(b) for b in P.recv]
+    out_ovl = bits(P.out)
+    run.ffn(mode=1, consumer_cus=16)
+    P.combine()
+    torch.cuda.synchronize()
+    for r in range(s.R):
+        np.testing.assert_array_equal(bits(P.recv[r]), recv_ovl[r])
+    np.testing.assert_array_equal(bits(P.out), out_ovl)
+
+
+def test_overlap_ordering_stress():
+    """Many overlapped runs over consumer partitions and segment sizes; delivery must be exact every time."""
+    s = mi.Spec("stress", R=4, T_o=512, G=16, E_l=4, k=2, d=512, f=512, M=32, seed=21)
+    run = Run(s)
+    check_route_and_layout(run)
+    ref = None
+    for it, cus in enumerate([1, 2, 4, 8, 16, 32] * 4):
+        for r in range(s.R):
+            run.P.recv[r].fill_(float("nan"))
+        run.ffn(mode=0, consumer_cus=cus)
+        torch.cuda.synchronize()
+        assert run.P.status() == B.MOE_OK
+        check_delivery(run)
+        cur = [bits(b) for b in run.P.recv]
+        if ref is None:
+            ref = cur
+        for a, b in zip(cur, ref):
+            np.testing.assert_array_equal(a, b)
+
+
+def test_watchdog_ends_a_wait_that_never_ends():
+    s = mi.spec("tiny")
+    run = Run(s)
+    run.ffn(mode=0, consumer_cus=2)
+    torch.cuda.synchronize()
+    assert run.P.status() == B.MOE_OK
+    # return only, for an epoch the producer never published: the consumer must give up, not hang
+    run.P.ffn(run.dev["w_gate_up"], run.dev["w_down"], mode=2, consumer_cus=2, watchdog_ticks=100000, epoch=999)
+    torch.cuda.synchronize()
+    assert run.P.status() == B.MOE_ETIMEOUT
+    # later kernels are no-ops until the next layout resets the status
+    run.P.out.fill_(7.0)
+    run.P.combine()
+    torch.cuda.synchronize()
+    assert (f64(run.P.out) == 7.0).all()
+    run.P.layout(run.dev["x"])
+    torch.cuda.synchronize()
+    assert run.P.status() == B.MOE_OK
+
+
+def test_capacity_overflow_reported():
+    s = mi.spec("tiny")
+    run = Run(s)
+    P = run.P
+    P.L.cap_rows = s.M
+    P.L.cap_tiles = 1
+    P.layout(run.dev["x"])
+    torch.cuda.synchronize()
+    assert P.status() == B.MOE_ECAPACITY
+    assert P.scalars()["M_pad"] == 0
+
+
+def test_empty_and_degenerate_inputs():
+    # no tokens
+    s = mi.spec("tiny", T_o=0)
+    P = MoePath.from_spec(s)
+    P.route(torch.empty(0, s.G, device="cuda"))
+    P.layout(torch.empty(0, s.d, dtype=torch.bfloat16, device="cuda"))
+    w1, w2 = (to_device(a, s.dtype) for a in mi.weights(s))
+    P.ffn(w1, w2)
+    P.combine()
+    torch.cuda.synchronize()
+    assert P.status() == B.MOE_OK and P.scalars()["M_pad"] == 0
+    # no token routed to a local expert: out is zero
+    s = mi.spec("tiny")
+    lg = mi.logits(s)
+    lg[:, : s.E_l] -= 100.0
+    run = Run(s, logits=lg)
+    check_route_and_layout(run)
+    run.ffn()
+    run.P.combine()
+    torch.cuda.synchronize()
+    assert run.P.scalars()["M_pad"] == 0 and (f64(run.P.out[: s.T]) == 0).all()
+    # every token routed to local expert 0
+    lg = mi.logits(s)
+    lg[:, 0] += 100.0
+    run = Run(s, logits=lg)
+    check_route_and_layout(run)
+    run.ffn()
+    torch.cuda.synchronize()
+    real = np.nonzero(run.lay["row_src"] >= 0)[0]
+    run.check_rows(real)
