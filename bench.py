@@ -193,7 +193,7 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": s.dtype, "data": "synthetic",
-        "config": {"workload": workload_name(s), "M_real": M_real, "M_pad": M_pad, "consumer_cus": cus,
+        "config": {"workload": workload_name(s), "M_real": M_real, "M_pad": M_pad, "gemm_row_tiles": sc["n_mtiles"], "consumer_cus": cus,
                    "band_window": args.band_window or 4, "mode": "overlapped"},
         "pct_bf16_peak_step": round(100 * value / peak, 2),
         "ffn_tflops_overlapped": round(ffn_tflops, 2),

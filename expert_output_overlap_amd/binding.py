@@ -30,7 +30,7 @@ class moe_shape(ctypes.Structure):
 
 LAYOUT_ARRAYS = ["counts", "padded_off", "recv_off", "tile_owner", "tile_expert", "tile_valid", "tile_order",
                  "seg_desc", "row_src", "combine_plan", "scalars", "status", "mtile_desc", "seg_mtiles",
-                 "chunk_counts"]
+                 "seg_sched", "chunk_counts"]
 
 
 class moe_layout(ctypes.Structure):

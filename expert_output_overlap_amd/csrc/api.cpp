@@ -42,6 +42,11 @@ std::string check_shape(const moe_shape* s) {
   const int64_t cap = (T * std::min(s->top_k, s->num_local_experts) +
                        (int64_t)s->num_local_experts * s->R * (s->tile_m - 1));
   if (cap >= (1ll << 30)) return "padded row capacity too large";
+  // the GEMMs address rows of x_pad / h and of one expert's weights with 32-bit byte offsets
+  const int64_t esize = s->dtype == MOE_BF16 ? 2 : 4;
+  const int64_t kmax = s->d > s->f ? s->d : s->f;
+  if ((cap + 256) * kmax * esize >= (1ll << 32) || 2ll * s->f * s->d * esize >= (1ll << 32))
+    return "rows x width too large for 32-bit offsets";
   return "";
 }
 
@@ -63,7 +68,7 @@ struct Carve {
 
 struct Offsets {
   int64_t counts, padded_off, recv_off, tile_owner, tile_expert, tile_valid, tile_order, seg_desc, row_src,
-      combine_plan, scalars, status, mtile_desc, seg_mtiles, chunk_counts, total;
+      combine_plan, scalars, status, mtile_desc, seg_mtiles, seg_sched, chunk_counts, total;
   int64_t cap_rows, cap_tiles, cap_mtiles;
 };
 
@@ -91,6 +96,7 @@ Offsets layout_offsets(const moe_shape* s) {
   o.status = c.take(1, 4);
   o.mtile_desc = c.take(o.cap_mtiles * (2 + 16), 4);
   o.seg_mtiles = c.take(o.cap_tiles * 2, 4);
+  o.seg_sched = c.take(o.cap_tiles, 4);
   o.chunk_counts = c.take((int64_t)s->R * n_chunks * s->num_local_experts, 4);
   o.total = c.off;
   return o;
@@ -196,6 +202,7 @@ int moe_layout_bind(const moe_shape* s, void* workspace, int64_t workspace_bytes
   L->status = (int32_t*)(b + o.status);
   L->mtile_desc = (int32_t*)(b + o.mtile_desc);
   L->seg_mtiles = (int32_t*)(b + o.seg_mtiles);
+  L->seg_sched = (int32_t*)(b + o.seg_sched);
   L->chunk_counts = (int32_t*)(b + o.chunk_counts);
   L->cap_rows = o.cap_rows;
   L->cap_tiles = o.cap_tiles;
@@ -206,7 +213,7 @@ int moe_layout_bind(const moe_shape* s, void* workspace, int64_t workspace_bytes
 static bool layout_ok(const moe_layout* L) {
   return L && L->counts && L->padded_off && L->recv_off && L->tile_owner && L->tile_expert && L->tile_valid &&
          L->tile_order && L->seg_desc && L->row_src && L->combine_plan && L->scalars && L->status &&
-         L->mtile_desc && L->seg_mtiles && L->chunk_counts && L->cap_rows > 0;
+         L->mtile_desc && L->seg_mtiles && L->seg_sched && L->chunk_counts && L->cap_rows > 0;
 }
 
 int moe_layout_build(const moe_shape* s, const int32_t* topk_idx, const void* x, moe_layout* L, void* x_pad,

@@ -4,7 +4,7 @@
 // width -- to its owner as one contiguous write).  On one GPU the owner ranks are receive buffers in HBM,
 // so a transfer is a device-memory copy by the consumer's CUs.
 //
-// Consumer workgroup w of C takes segments w, w + C, ... in remote-first order.  For a segment it polls the flags of
+// Consumer workgroup w of C takes segments w, w + C, ... of the order in which their GEMM row tiles complete.  For a segment it polls the flags of
 // the GEMM row tiles the segment depends on with relaxed agent-scope loads, then issues one agent-scope
 // acquire fence (pairing with the producer's release) before reading the rows; a spin budget on the
 // 100 MHz clock bounds every wait.
@@ -16,6 +16,7 @@ struct ConsumerArgs {
   RecvPtrs recv;
   const int32_t* seg_desc;
   const int32_t* seg_mtiles;
+  const int32_t* seg_sched;
   const int32_t* scalars;
   int32_t* status;
   const uint32_t* flags;
@@ -33,7 +34,8 @@ __device__ void consumer_role(const ConsumerArgs& a, int cid, int n_cons) {
   if (load_status(a.status) != 0) return;
   const int n_segs = a.scalars[SC_NSEGS];
   const uint64_t t0 = moe_clock();
-  for (int s = cid; s < n_segs; s += n_cons) {
+  for (int si = cid; si < n_segs; si += n_cons) {
+    const int s = a.seg_sched[si];
     const int mt0 = a.seg_mtiles[2 * s], mcnt = a.seg_mtiles[2 * s + 1];
     const int nflags = mcnt * a.n_nt;
     const uint32_t* fl = a.flags + (int64_t)mt0 * a.n_nt;

@@ -12,6 +12,8 @@
 // the remote-first group order, so all-padding sub-blocks cost nothing.  Items (row tile, column tile)
 // are visited window by window (band_window row tiles, column-tile-major inside a window) for weight
 // reuse, and consecutive items go to workgroups on the same XCD.
+#include <type_traits>
+
 #include "common.h"
 #include "consumer.h"
 #include "launch.h"
@@ -250,23 +252,233 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm(GemmArgs a) {
   }
 }
 
+// ---- bf16 GEMM: 256-row tiles, direct global->LDS loads ------------------------------------------------
+//
+// Workgroup tile 256 x BN x 64 (k), 4 waves in 2 x 2, wave tile 128 x BN/2 (4 x BN/64 MFMA blocks of 32 x 32,
+// accumulators in AGPRs).  Operand tiles are staged in LDS without padding, 128 bytes per row; a 16-byte
+// k-chunk c of row r sits at slot c ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1), so the 16-byte fragment
+// reads of 16 consecutive rows hit distinct banks for 32 or 64 banks.  global_load_lds_dwordx4 moves each
+// 16-byte chunk straight from global memory into its swizzled LDS slot (one wave instruction fills 8 rows,
+// 1 KB); two LDS stages (128 KB at BN = 256) and one barrier per k-tile: loads of k-tile kt+1 fly while the
+// MFMAs of k-tile kt run.
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void load_lds16(const void* g, lds_void* l) {
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+}
+
+template <int BN, bool GLU, bool PUBLISH>
+__global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmArgs a) {
+  constexpr int BM = 256, BK = 64;
+  constexpr int WM = 128, WN = BN / 2, MI = WM / 32, NI = WN / 32;
+  constexpr int OUT_BN = GLU ? BN / 2 : BN;
+  constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, STAGE = A_BYTES + B_BYTES;
+  constexpr int A_LOADS = BM / 8 / 4, B_LOADS = BN / 8 / 4;  // 1 KB wave loads per wave per k-tile
+  static_assert(!GLU || NI % 2 == 0, "GLU pairs gate and up blocks");
+  static_assert(B_LOADS >= 1, "tile width");
+
+  __shared__ __align__(1024) unsigned char smem[2 * STAGE];
+  __shared__ int s_sub[MOE_MT_SUB];
+  __shared__ int s_hdr[2];
+
+  if (PUBLISH && (int)blockIdx.x < a.n_cons) {
+    consumer_role(a.cons, blockIdx.x, a.n_cons);
+    return;
+  }
+  if (load_status(a.status) != 0) return;
+  const int n_mt = a.scalars[a.sc_nmt];
+  const int n_items = n_mt * a.n_nt;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n_cons = PUBLISH ? a.n_cons : 0;
+  const int G = gridDim.x - n_cons;
+  int bid = blockIdx.x - n_cons;
+  if ((G & 7) == 0 && (n_cons & 7) == 0) bid = (bid & 7) * (G >> 3) + (bid >> 3);
+  const unsigned char* __restrict__ Ab = (const unsigned char*)a.A;
+  const unsigned char* __restrict__ Wb = (const unsigned char*)a.W;
+  bf16_t* __restrict__ C = (bf16_t*)a.C;
+  const int K = a.K;
+  const uint32_t row_bytes = (uint32_t)K * 2u;
+  const int nk = K / BK;
+  // load mapping: wave instruction q fills tile rows [8q, 8q+8); lane -> row 8q + lane/8, LDS slot lane & 7,
+  // which holds k-chunk (lane & 7) ^ swz(row) = (lane & 7) ^ (lane >> 3) ^ (q & 1)
+  const uint32_t chunk0 = (uint32_t)(((lane & 7) ^ (lane >> 3)) << 4);
+  // fragment mapping: row = base + (lane & 31), k-chunk c = 2 * kstep + (lane >> 5)
+  const int swz = (lane & 7) ^ ((lane >> 3) & 1);
+  bool first = true;
+
+  for (int item = bid; item < n_items; item += G) {
+    const int per_win = a.window * a.n_nt;
+    const int w = item / per_win, j = item - w * per_win;
+    const int mt0 = w * a.window;
+    const int Wc = min(a.window, n_mt - mt0);
+    const int nt = j / Wc, mt = mt0 + (j - nt * Wc);
+
+    __syncthreads();  // previous item done with LDS and the header
+    if (tid < MOE_MT_FIELDS) {
+      const int v = a.mtile_desc[(int64_t)mt * MOE_MT_FIELDS + tid];
+      if (tid < 2) s_hdr[tid] = v;
+      else s_sub[tid - 2] = v;
+    }
+    if (PUBLISH && a.ts != nullptr && first && tid == 0)
+      atomicMin((unsigned long long*)&a.ts[0], (unsigned long long)moe_clock());
+    first = false;
+    __syncthreads();
+    const int e = s_hdr[0], n_sub = s_hdr[1];
+
+    uint32_t aoff[A_LOADS], boff[B_LOADS];
+#pragma unroll
+    for (int jj = 0; jj < A_LOADS; ++jj) {
+      const int q = wave * A_LOADS + jj;
+      const int r = 8 * q + (lane >> 3);
+      const int sub = r >> 4;
+      const int row = sub < n_sub ? s_sub[sub] + (r & 15) : s_sub[0];  // absent sub-blocks read a real row
+      aoff[jj] = (uint32_t)row * row_bytes + (chunk0 ^ ((uint32_t)(q & 1) << 4));
+    }
+    const unsigned char* wbase = Wb + (int64_t)e * a.w_rows * row_bytes;
+#pragma unroll
+    for (int jj = 0; jj < B_LOADS; ++jj) {
+      const int q = wave * B_LOADS + jj;
+      const int i = 8 * q + (lane >> 3);
+      int wrow;
+      if (GLU) wrow = i < BN / 2 ? nt * (BN / 2) + i : a.f + nt * (BN / 2) + (i - BN / 2);
+      else wrow = nt * BN + i;
+      boff[jj] = (uint32_t)wrow * row_bytes + (chunk0 ^ ((uint32_t)(q & 1) << 4));
+    }
+    f32x16_t acc[MI][NI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.f;
+
+    auto issue = [&](int kt, int stage) {
+      unsigned char* sb = smem + stage * STAGE;
+      const uint32_t kb = (uint32_t)kt * (BK * 2);
+#pragma unroll
+      for (int jj = 0; jj < A_LOADS; ++jj)
+        load_lds16(Ab + aoff[jj] + kb, (lds_void*)(sb + (wave * A_LOADS + jj) * 1024));
+#pragma unroll
+      for (int jj = 0; jj < B_LOADS; ++jj)
+        load_lds16(wbase + boff[jj] + kb, (lds_void*)(sb + A_BYTES + (wave * B_LOADS + jj) * 1024));
+    };
+
+    // 32-row MFMA blocks of this wave that hold present sub-blocks: all MI except in a tile's ragged tail
+    const int mact = min(MI, max(0, (n_sub * 16 - wm * WM + 31) / 32));
+    auto kloop = [&](auto full_tag) {
+      constexpr bool FULL = decltype(full_tag)::value;
+      issue(0, 0);
+      for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of k-tile kt are in LDS
+        __syncthreads();                      // everyone's are; everyone is done reading the other stage
+        if (kt + 1 < nk) issue(kt + 1, cur ^ 1);
+        const unsigned char* sa = smem + cur * STAGE;
+        const unsigned char* sbb = sa + A_BYTES;
+        // fragments double-buffered in registers: reads of k-step ks+1 overlap the MFMAs of k-step ks
+        bf16x8_t fa[2][MI], fb[2][NI];
+        auto frags = [&](int ks, bf16x8_t* A_, bf16x8_t* B_) {
+          const int sl = (((2 * ks + (lane >> 5)) ^ swz) << 4);
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi)
+            A_[mi] = __builtin_bit_cast(bf16x8_t,
+                                        *(const u32x4_t*)(sa + (wm * WM + mi * 32 + (lane & 31)) * 128 + sl));
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) {
+            int row;
+            if (GLU) row = ni < NI / 2 ? wn * (WN / 2) + ni * 32 : BN / 2 + wn * (WN / 2) + (ni - NI / 2) * 32;
+            else row = wn * WN + ni * 32;
+            B_[ni] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(sbb + (row + (lane & 31)) * 128 + sl));
+          }
+        };
+        frags(0, fa[0], fb[0]);
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+          const int c = ks & 1;
+          if (ks + 1 < BK / 16) frags(ks + 1, fa[c ^ 1], fb[c ^ 1]);
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi) {
+            if (!FULL && mi >= mact) continue;
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni)
+              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][mi], fb[c][ni], acc[mi][ni], 0, 0, 0);
+          }
+        }
+        if (FULL) {
+          // schedule: the first k-step's reads, then per k-step its MFMAs interleaved one-for-one with the next
+          // k-step's reads (mask 0x100 = LDS reads, 0x008 = MFMA)
+          __builtin_amdgcn_sched_group_barrier(0x100, MI + NI, 0);
+#pragma unroll
+          for (int ks = 0; ks < BK / 16; ++ks) {
+            if (ks + 1 < BK / 16) {
+#pragma unroll
+              for (int i = 0; i < MI + NI; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+              }
+              __builtin_amdgcn_sched_group_barrier(0x008, MI * NI - (MI + NI), 0);
+            } else {
+              __builtin_amdgcn_sched_group_barrier(0x008, MI * NI, 0);
+            }
+          }
+        }
+      }
+    };
+    if (mact == MI) kloop(std::true_type{});
+    else kloop(std::false_type{});
+
+    // epilogue: a 32-row MFMA block is two 16-row sub-blocks (accumulator registers 0-7 and 8-15); only present
+    // sub-blocks are stored (their padding rows included, never read for a result)
+    constexpr int NO = GLU ? NI / 2 : NI;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int sub = (wm * WM + mi * 32) / 16 + half;
+        if (sub >= n_sub) continue;
+        const int64_t rbase = s_sub[sub];
+#pragma unroll
+        for (int ni = 0; ni < NO; ++ni) {
+          const int col = nt * OUT_BN + (GLU ? wn * (WN / 2) : wn * WN) + ni * 32 + (lane & 31);
+#pragma unroll
+          for (int q = 8 * half; q < 8 * half + 8; ++q) {
+            const int row = ((q >> 2) & 1) * 8 + (lane >> 5) * 4 + (q & 3);  // row inside the sub-block
+            float v = acc[mi][ni][q];
+            if (GLU) v = silu_f32(v) * acc[mi][ni + NI / 2][q];
+            C[(rbase + row) * a.ldc + col] = f32_to_bf16(v);
+          }
+        }
+      }
+    }
+    if (PUBLISH) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __syncthreads();
+      if (tid == 0) {
+        __hip_atomic_store(&a.flags[(int64_t)mt * a.n_nt + nt], a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        if (a.ts != nullptr) atomicMax((unsigned long long*)&a.ts[1], (unsigned long long)moe_clock());
+      }
+    }
+  }
+}
+
 // ---- tile configurations --------------------------------------------------------------------------------
-#define BF_BM 128
-#define BF_BN 128
+#define BF_BM 256
 #define F32_BM 64
 #define F32_BN 64
 
-// Extra dynamic LDS per bf16 workgroup: keeps the total above half of the CU's 160 KB so that a CU holds one
-// producer workgroup (or one consumer workgroup) of a launch, never two.
-#define BF_LDS_PAD (10 * 1024)
-
 int ffn_gemm_bm(int dtype) { return dtype == MOE_BF16 ? BF_BM : F32_BM; }
 
-int ffn_gemm2_bn(int dtype, int d) {
-  if (dtype == MOE_BF16) return d % BF_BN == 0 ? BF_BN : 64;
+static int gemm1_bn(int dtype, int f) {
+  if (dtype == MOE_BF16) return f % 128 == 0 ? 256 : 128;
   return F32_BN;
 }
 
+int ffn_gemm2_bn(int dtype, int d) {
+  if (dtype == MOE_BF16) return d % 256 == 0 ? 256 : (d % 128 == 0 ? 128 : 64);
+  return F32_BN;
+}
 
 static GemmArgs base_args(const FfnLaunch& p) {
   GemmArgs a;
@@ -291,12 +503,12 @@ int launch_ffn_gemm1(const FfnLaunch& p, int grid, hipStream_t st) {
   a.w_rows = 2 * p.f;
   a.ldc = p.f;
   a.f = p.f;
+  const int bn = gemm1_bn(p.dtype, p.f);
+  a.n_nt = p.f / (bn / 2);
   if (p.dtype == MOE_BF16) {
-    a.n_nt = p.f / (BF_BN / 2);
-    hipLaunchKernelGGL((k_gemm<bf16_t, BF_BM, BF_BN, 2, 2, true, false>), dim3(grid), dim3(256), BF_LDS_PAD, st,
-                       a);
+    if (bn == 256) hipLaunchKernelGGL((k_gemm_bf16<256, true, false>), dim3(grid), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_gemm_bf16<128, true, false>), dim3(grid), dim3(256), 0, st, a);
   } else {
-    a.n_nt = p.f / (F32_BN / 2);
     hipLaunchKernelGGL((k_gemm<float, F32_BM, F32_BN, 2, 1, true, false>), dim3(grid), dim3(128), 0, st, a);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
@@ -320,6 +532,7 @@ int launch_ffn_gemm2(const FfnLaunch& p, int grid, int n_cons, hipStream_t st) {
   for (int r = 0; r < MOE_MAX_OWNERS; ++r) c.recv.p[r] = r < p.R ? p.recv[r] : nullptr;
   c.seg_desc = p.L->seg_desc;
   c.seg_mtiles = p.L->seg_mtiles;
+  c.seg_sched = p.L->seg_sched;
   c.scalars = p.L->scalars;
   c.status = p.L->status;
   c.flags = p.flags;
@@ -328,13 +541,11 @@ int launch_ffn_gemm2(const FfnLaunch& p, int grid, int n_cons, hipStream_t st) {
   c.row_vec = p.d * (p.dtype == MOE_BF16 ? 2 : 4) / 16;
   c.budget = p.watchdog_ticks;
   c.ts = p.timestamps;
+  // the bf16 workgroups hold over 80 KB of LDS (one per CU); pad the narrow variants to keep that true
   if (p.dtype == MOE_BF16) {
-    if (bn == BF_BN)
-      hipLaunchKernelGGL((k_gemm<bf16_t, BF_BM, BF_BN, 2, 2, false, true>), dim3(grid), dim3(256), BF_LDS_PAD, st,
-                         a);
-    else
-      hipLaunchKernelGGL((k_gemm<bf16_t, BF_BM, 64, 2, 2, false, true>), dim3(grid), dim3(256), 3 * BF_LDS_PAD, st,
-                         a);
+    if (bn == 256) hipLaunchKernelGGL((k_gemm_bf16<256, false, true>), dim3(grid), dim3(256), 0, st, a);
+    else if (bn == 128) hipLaunchKernelGGL((k_gemm_bf16<128, false, true>), dim3(grid), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_gemm_bf16<64, false, true>), dim3(grid), dim3(256), 16384, st, a);
   } else {
     hipLaunchKernelGGL((k_gemm<float, F32_BM, F32_BN, 2, 1, false, true>), dim3(grid), dim3(128), 0, st, a);
   }

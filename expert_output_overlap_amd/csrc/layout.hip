@@ -73,15 +73,17 @@ struct ScanArgs {
   int R, T_o, E, M, mgb, self_rank, n_chunks, mt_sub;
   int64_t cap_rows, cap_tiles, cap_mtiles;
   int32_t *chunk_counts, *counts, *padded_off, *recv_off, *tile_owner, *tile_expert, *tile_valid, *tile_order,
-      *seg_desc, *row_src, *scalars, *status, *mtile_desc, *seg_mtiles;
+      *seg_desc, *row_src, *scalars, *status, *mtile_desc, *seg_mtiles, *seg_sched;
 };
 
 __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
   __shared__ int s_n[MAX_GROUPS];      // n_g
   __shared__ int s_poff[MAX_GROUPS];   // padded offset of g
   __shared__ int s_order[MAX_GROUPS];  // q -> g (non-empty groups, remote-first)
+  __shared__ int s_q2[MAX_GROUPS];     // g -> position in the row-tile packing order
   __shared__ int s_band_pos[MAX_GROUPS], s_seg_pos[MAX_GROUPS], s_sub_pos[MAX_GROUPS];
-  __shared__ int s_tile_base[MAX_GROUPS], s_run_off[MAX_GROUPS], s_run_subs[MAX_GROUPS];
+  __shared__ int s_order2[MAX_GROUPS];  // q2 -> g, row-tile packing order
+  __shared__ int s_tile_base[MAX_GROUPS], s_run_off[MAX_GROUPS], s_run_subs[MAX_GROUPS];  // by q2
   __shared__ int s_wsum[SCAN_THREADS / MOE_WAVE + 1];
   __shared__ int s_misc[4];
 
@@ -151,9 +153,11 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
     }
   }
 
-  // (e) remote-first order of non-empty groups: key (owner == self, -P, e, r) ascending
+  // (e) remote-first order of non-empty groups: key (owner == self, -P, e, r) ascending (bands, segments);
+  // row-tile packing order: key (owner == self, e, -P, r), remote groups first and each expert's groups together
+  // so that a GEMM row tile (one expert) packs as many sub-blocks as possible
   {
-    int rank = 0;
+    int rank = 0, rank2 = 0;
     const bool mine = tid < NG && s_n[tid] > 0;
     if (mine) {
       const int g = tid, e = g / R, r = g % R;
@@ -163,23 +167,32 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
         if (nh == 0 || h == g) continue;
         const int eh = h / R, rh = h % R;
         const int selfh = (rh == a.self_rank), Ph = ((nh + M - 1) / M) * M;
-        bool less;
+        bool less, less2;
         if (selfh != self) less = selfh < self;
         else if (Ph != P) less = Ph > P;
         else if (eh != e) less = eh < e;
         else less = rh < r;
+        if (selfh != self) less2 = selfh < self;
+        else if (eh != e) less2 = eh < e;
+        else if (Ph != P) less2 = Ph > P;
+        else less2 = rh < r;
         rank += less;
+        rank2 += less2;
       }
     }
     int n_ne = 0;
     block_excl_scan(mine ? 1 : 0, s_wsum, &n_ne);
-    if (mine) s_order[rank] = tid;
+    if (mine) {
+      s_order[rank] = tid;
+      s_order2[rank2] = tid;
+      s_q2[tid] = rank2;
+    }
     if (tid == 0) s_misc[0] = n_ne;
     __syncthreads();
   }
   const int n_ne = s_misc[0];
 
-  // (f) per position q: band, segment and sub-block positions (exclusive scans in q order)
+  // (f) band and segment positions in remote-first order, sub-block positions in packing order
   {
     const int q = tid;
     int nb = 0, ns = 0, nsub = 0;
@@ -187,7 +200,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
       const int n = s_n[s_order[q]];
       nb = (n + M - 1) / M;
       ns = (nb + a.mgb - 1) / a.mgb;
-      nsub = (n + MOE_SUB - 1) / MOE_SUB;
+      nsub = (s_n[s_order2[q]] + MOE_SUB - 1) / MOE_SUB;
     }
     int tb = 0, ts = 0, tsub = 0;
     const int pb = block_excl_scan(nb, s_wsum, &tb);
@@ -196,7 +209,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
     if (q < n_ne) {
       s_band_pos[q] = pb;
       s_seg_pos[q] = ps;
-      s_sub_pos[q] = psub;
+      s_sub_pos[q] = psub;  // indexed by q2
     }
     if (tid == 0) {
       s_misc[1] = ts;
@@ -206,14 +219,14 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
   }
   const int n_segs = s_misc[1];
 
-  // (g) GEMM row tiles: runs of consecutive same-expert groups (in q order) cut into tiles of mt_sub
-  // sub-blocks; sequential over at most 1024 groups
+  // (g) GEMM row tiles: runs of consecutive same-expert groups in packing order, each cut into tiles of
+  // mt_sub sub-blocks; sequential over at most 1024 groups
   if (tid == 0) {
     int tile_base = 0, q0 = 0;
     while (q0 < n_ne) {
-      const int e = s_order[q0] / R;
+      const int e = s_order2[q0] / R;
       int q1 = q0;
-      while (q1 < n_ne && s_order[q1] / R == e) ++q1;
+      while (q1 < n_ne && s_order2[q1] / R == e) ++q1;
       const int run_subs = (q1 < n_ne ? s_sub_pos[q1] : s_misc[2]) - s_sub_pos[q0];
       for (int q = q0; q < q1; ++q) {
         s_tile_base[q] = tile_base;
@@ -243,7 +256,8 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
     const int g = s_order[q], e = g / R, r = g % R, n = s_n[g], off = s_poff[g];
     const int nb = (n + M - 1) / M, b0 = off / M;
     for (int b = 0; b < nb; ++b) a.tile_order[s_band_pos[q] + b] = b0 + b;
-    const int base = s_tile_base[q], roff = s_run_off[q], rsubs = s_run_subs[q];
+    const int q2 = s_q2[g];
+    const int base = s_tile_base[q2], roff = s_run_off[q2], rsubs = s_run_subs[q2];
     const int nsub = (n + MOE_SUB - 1) / MOE_SUB;
     for (int j = 0; j < nsub; ++j) {
       const int u = roff + j;
@@ -276,6 +290,17 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
       a.seg_mtiles[2 * sp] = mt0;
       a.seg_mtiles[2 * sp + 1] = mt1 - mt0 + 1;
     }
+  }
+  __syncthreads();
+  // (i) consumer order: segments by the last GEMM row tile they wait for, ties by segment index (stable)
+  for (int sg = tid; sg < n_segs; sg += SCAN_THREADS) {
+    const int last = a.seg_mtiles[2 * sg] + a.seg_mtiles[2 * sg + 1];
+    int rank = 0;
+    for (int o = 0; o < n_segs; ++o) {
+      const int lo2 = a.seg_mtiles[2 * o] + a.seg_mtiles[2 * o + 1];
+      rank += (lo2 < last) || (lo2 == last && o < sg);
+    }
+    a.seg_sched[rank] = sg;
   }
   if (tid == 0) {
     a.scalars[SC_MPAD] = M_pad;
@@ -385,6 +410,7 @@ int launch_layout(const LayoutLaunch& p, hipStream_t st) {
   a.status = p.L->status;
   a.mtile_desc = p.L->mtile_desc;
   a.seg_mtiles = p.L->seg_mtiles;
+  a.seg_sched = p.L->seg_sched;
   hipLaunchKernelGGL(k_layout_scan, dim3(1), dim3(SCAN_THREADS), 0, st, a);
   if (n_chunks > 0)
     hipLaunchKernelGGL(k_layout_scatter, dim3((n_chunks + 3) / 4, p.R), dim3(256), 0, st, p.topk_idx, p.R, p.T_o,

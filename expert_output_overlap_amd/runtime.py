@@ -57,7 +57,7 @@ class MoePath:
             "tile_owner": L.cap_tiles, "tile_expert": L.cap_tiles, "tile_valid": L.cap_tiles,
             "tile_order": L.cap_tiles, "seg_desc": L.cap_tiles * B.MOE_SEG_FIELDS, "row_src": L.cap_rows,
             "combine_plan": self.T * self.k, "scalars": 4 + self.R, "status": 1,
-            "mtile_desc": L.cap_mtiles * B.MT_FIELDS, "seg_mtiles": L.cap_tiles * 2,
+            "mtile_desc": L.cap_mtiles * B.MT_FIELDS, "seg_mtiles": L.cap_tiles * 2, "seg_sched": L.cap_tiles,
         }
         off = (getattr(L, name) - self.ws_aligned.data_ptr()) // 4
         return self.ws_aligned.view(torch.int32)[off: off + sizes[name]]
