@@ -257,16 +257,28 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm(GemmArgs a) {
 // Workgroup tile 256 x BN x 64 (k), 4 waves in 2 x 2, wave tile 128 x BN/2 (4 x BN/64 MFMA blocks of 32 x 32,
 // accumulators in AGPRs).  Operand tiles are staged in LDS without padding, 128 bytes per row; a 16-byte
 // k-chunk c of row r sits at slot c ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1), so the 16-byte fragment
-// reads of 16 consecutive rows hit distinct banks for 32 or 64 banks.  global_load_lds_dwordx4 moves each
-// 16-byte chunk straight from global memory into its swizzled LDS slot (one wave instruction fills 8 rows,
-// 1 KB); two LDS stages (128 KB at BN = 256) and one barrier per k-tile: loads of k-tile kt+1 fly while the
-// MFMAs of k-tile kt run.
+// reads of 16 consecutive rows hit distinct banks.  global_load_lds_dwordx4 moves each 16-byte chunk straight
+// from global memory into its swizzled LDS slot (one wave instruction fills 8 rows, 1 KB).  Two LDS stages
+// (128 KB at BN = 256) and one barrier per k-tile: the loads of k-tile kt+1 are issued a quarter per k-step
+// in between the MFMAs of k-tile kt.
+//
+// The loads are issued from inline assembly and the per-k-tile wait is an explicit "vmcnt(0); s_barrier":
+// the compiler's own waitcnt insertion cannot tell an LDS-DMA store from the fragment reads of the other stage
+// and would drain every load in flight before each LDS read, serialising loads and MFMAs.  The stage
+// discipline makes that unnecessary: a stage is written only after the barrier that ends every read of it.
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void load_lds16(const void* g, lds_void* l) {
-  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+// global_load_lds_dwordx4 in its scalar-base form: lane i moves 16 bytes from base + off into LDS at
+// m0 + 16 * i (m0 is set in the same statement, so no other code depends on it)
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(lds_addr)),
+               "v"(off), "s"(base) : "memory");
 }
+
+// this wave's loads have landed in LDS, then the workgroup barrier: after it every wave's have
+__device__ __forceinline__ void wait_loads_barrier() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// SiLU with the hardware reciprocal (about 1 ulp), rounded to bf16 right after
+__device__ __forceinline__ float silu_fast(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 template <int BN, bool GLU, bool PUBLISH>
 __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmArgs a) {
@@ -274,9 +286,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmArgs a) {
   constexpr int WM = 128, WN = BN / 2, MI = WM / 32, NI = WN / 32;
   constexpr int OUT_BN = GLU ? BN / 2 : BN;
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, STAGE = A_BYTES + B_BYTES;
-  constexpr int A_LOADS = BM / 8 / 4, B_LOADS = BN / 8 / 4;  // 1 KB wave loads per wave per k-tile
+  constexpr int A_LOADS = BM / 8 / 4, B_LOADS = BN / 8 / 4;  // 1 KB wave loads (8 rows) per wave per k-tile
+  constexpr int N_LOADS = A_LOADS + B_LOADS, PER = (N_LOADS + 3) / 4;  // loads issued per k-step
   static_assert(!GLU || NI % 2 == 0, "GLU pairs gate and up blocks");
   static_assert(B_LOADS >= 1, "tile width");
+  static_assert(BM * OUT_BN * 2 <= 2 * STAGE, "output staging fits the operand stages");
 
   __shared__ __align__(1024) unsigned char smem[2 * STAGE];
   __shared__ int s_sub[MOE_MT_SUB];
@@ -297,10 +311,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmArgs a) {
   if ((G & 7) == 0 && (n_cons & 7) == 0) bid = (bid & 7) * (G >> 3) + (bid >> 3);
   const unsigned char* __restrict__ Ab = (const unsigned char*)a.A;
   const unsigned char* __restrict__ Wb = (const unsigned char*)a.W;
-  bf16_t* __restrict__ C = (bf16_t*)a.C;
+  unsigned char* __restrict__ Cb = (unsigned char*)a.C;
   const int K = a.K;
   const uint32_t row_bytes = (uint32_t)K * 2u;
   const int nk = K / BK;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;  // LDS byte address of the stages
   // load mapping: wave instruction q fills tile rows [8q, 8q+8); lane -> row 8q + lane/8, LDS slot lane & 7,
   // which holds k-chunk (lane & 7) ^ swz(row) = (lane & 7) ^ (lane >> 3) ^ (q & 1)
   const uint32_t chunk0 = (uint32_t)(((lane & 7) ^ (lane >> 3)) << 4);
@@ -354,29 +369,30 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmArgs a) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.f;
 
-    auto issue = [&](int kt, int stage) {
-      unsigned char* sb = smem + stage * STAGE;
-      const uint32_t kb = (uint32_t)kt * (BK * 2);
+    // this wave's loads [part * PER, part * PER + PER) of k-tile kt into the stage at LDS address sb
+    auto issue = [&](int kt, uint32_t sb, int part) {
+      const unsigned char* ak = Ab + (uint32_t)kt * (BK * 2);
+      const unsigned char* bk = wbase + (uint32_t)kt * (BK * 2);
 #pragma unroll
-      for (int jj = 0; jj < A_LOADS; ++jj)
-        load_lds16(Ab + aoff[jj] + kb, (lds_void*)(sb + (wave * A_LOADS + jj) * 1024));
-#pragma unroll
-      for (int jj = 0; jj < B_LOADS; ++jj)
-        load_lds16(wbase + boff[jj] + kb, (lds_void*)(sb + A_BYTES + (wave * B_LOADS + jj) * 1024));
+      for (int i = 0; i < PER; ++i) {
+        const int u = part * PER + i;
+        if (u < A_LOADS) dma16(ak, aoff[u], sb + (wave * A_LOADS + u) * 1024);
+        else if (u < N_LOADS) dma16(bk, boff[u - A_LOADS], sb + A_BYTES + (wave * B_LOADS + u - A_LOADS) * 1024);
+      }
     };
 
     // 32-row MFMA blocks of this wave that hold present sub-blocks: all MI except in a tile's ragged tail
     const int mact = min(MI, max(0, (n_sub * 16 - wm * WM + 31) / 32));
     auto kloop = [&](auto full_tag) {
       constexpr bool FULL = decltype(full_tag)::value;
-      issue(0, 0);
+#pragma unroll
+      for (int part = 0; part < 4; ++part) issue(0, lds0, part);
       for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of k-tile kt are in LDS
-        __syncthreads();                      // everyone's are; everyone is done reading the other stage
-        if (kt + 1 < nk) issue(kt + 1, cur ^ 1);
-        const unsigned char* sa = smem + cur * STAGE;
+        wait_loads_barrier();  // k-tile kt is in LDS for every wave; nobody reads the other stage any more
+        const bool more = kt + 1 < nk;
+        const unsigned char* sa = smem + (kt & 1) * STAGE;
         const unsigned char* sbb = sa + A_BYTES;
+        const uint32_t nsb = lds0 + ((kt + 1) & 1) * STAGE;
         // fragments double-buffered in registers: reads of k-step ks+1 overlap the MFMAs of k-step ks
         bf16x8_t fa[2][MI], fb[2][NI];
         auto frags = [&](int ks, bf16x8_t* A_, bf16x8_t* B_) {
@@ -397,6 +413,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmArgs a) {
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
           const int c = ks & 1;
+          if (more) issue(kt + 1, nsb, ks);
           if (ks + 1 < BK / 16) frags(ks + 1, fa[c ^ 1], fb[c ^ 1]);
 #pragma unroll
           for (int mi = 0; mi < MI; ++mi) {
@@ -405,20 +422,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmArgs a) {
             for (int ni = 0; ni < NI; ++ni)
               acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][mi], fb[c][ni], acc[mi][ni], 0, 0, 0);
           }
-        }
-        if (FULL) {
-          // schedule: the first k-step's reads, then per k-step its MFMAs interleaved one-for-one with the next
-          // k-step's reads (mask 0x100 = LDS reads, 0x008 = MFMA)
-          __builtin_amdgcn_sched_group_barrier(0x100, MI + NI, 0);
-#pragma unroll
-          for (int ks = 0; ks < BK / 16; ++ks) {
-            if (ks + 1 < BK / 16) {
+          if (FULL) {
+            // this k-step's MFMAs interleaved one-for-one with the next k-step's LDS reads, so each read has
+            // several MFMAs to land in (mask 0x008 = MFMA, 0x100 = LDS read)
+            if (ks + 1 < BK / 16 && MI * NI >= MI + NI) {
 #pragma unroll
               for (int i = 0; i < MI + NI; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
               }
-              __builtin_amdgcn_sched_group_barrier(0x008, MI * NI - (MI + NI), 0);
+              if (MI * NI > MI + NI) __builtin_amdgcn_sched_group_barrier(0x008, MI * NI - (MI + NI), 0);
             } else {
               __builtin_amdgcn_sched_group_barrier(0x008, MI * NI, 0);
             }
@@ -429,31 +442,38 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmArgs a) {
     if (mact == MI) kloop(std::true_type{});
     else kloop(std::false_type{});
 
-    // epilogue: a 32-row MFMA block is two 16-row sub-blocks (accumulator registers 0-7 and 8-15); only present
-    // sub-blocks are stored (their padding rows included, never read for a result)
+    // epilogue: every wave writes its bf16 outputs into LDS as a 256 x OUT_BN tile (16-byte chunk ch of row r at
+    // chunk ch ^ (r & 7), so neither the column writes nor the row reads collide), then 16-byte stores of the rows
+    // of present sub-blocks (padding rows inside them included, never read for a result)
     constexpr int NO = GLU ? NI / 2 : NI;
+    constexpr int OUT_ROW = OUT_BN * 2, CPR = OUT_ROW / 16;
+    __syncthreads();  // every wave is done with the operand stages
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int sub = (wm * WM + mi * 32) / 16 + half;
-        if (sub >= n_sub) continue;
-        const int64_t rbase = s_sub[sub];
+      for (int ni = 0; ni < NO; ++ni) {
+        const int col = (GLU ? wn * (WN / 2) : wn * WN) + ni * 32 + (lane & 31);
 #pragma unroll
-        for (int ni = 0; ni < NO; ++ni) {
-          const int col = nt * OUT_BN + (GLU ? wn * (WN / 2) : wn * WN) + ni * 32 + (lane & 31);
-#pragma unroll
-          for (int q = 8 * half; q < 8 * half + 8; ++q) {
-            const int row = ((q >> 2) & 1) * 8 + (lane >> 5) * 4 + (q & 3);  // row inside the sub-block
-            float v = acc[mi][ni][q];
-            if (GLU) v = silu_f32(v) * acc[mi][ni + NI / 2][q];
-            C[(rbase + row) * a.ldc + col] = f32_to_bf16(v);
-          }
+        for (int q = 0; q < 16; ++q) {
+          const int row = wm * WM + mi * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+          float v = acc[mi][ni][q];
+          if (GLU) v = silu_fast(v) * acc[mi][ni + NI / 2][q];
+          const int chunk = (col >> 3) ^ (row & 7);
+          *(__bf16*)(smem + row * OUT_ROW + chunk * 16 + (col & 7) * 2) = (__bf16)v;  // round to nearest even
         }
       }
     }
+    __syncthreads();
+    for (int idx = tid; idx < BM * CPR; idx += 256) {
+      const int row = idx / CPR, ch = idx - row * CPR;
+      const int sub = row >> 4;
+      if (sub >= n_sub) continue;
+      const u32x4_t v = *(const u32x4_t*)(smem + row * OUT_ROW + ((ch ^ (row & 7)) << 4));
+      const int64_t grow = s_sub[sub] + (row & 15);
+      *(u32x4_t*)(Cb + (grow * a.ldc + (int64_t)nt * OUT_BN) * 2 + ch * 16) = v;
+    }
     if (PUBLISH) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this thread's tile stores, agent-visible
       __syncthreads();
       if (tid == 0) {
         __hip_atomic_store(&a.flags[(int64_t)mt * a.n_nt + nt], a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
