@@ -258,9 +258,15 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm(GemmArgs a) {
 // accumulators in AGPRs).  Operand tiles are staged in LDS without padding, 128 bytes per row; a 16-byte
 // k-chunk c of row r sits at slot c ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1), so the 16-byte fragment
 // reads of 16 consecutive rows hit distinct banks.  global_load_lds_dwordx4 moves each 16-byte chunk straight
-// from global memory into its swizzled LDS slot (one wave instruction fills 8 rows, 1 KB).  Two LDS stages
-// (128 KB at BN = 256) and one barrier per k-tile: the loads of k-tile kt+1 are issued a quarter per k-step
-// in between the MFMAs of k-tile kt.
+// from global memory into its swizzled LDS slot (one wave instruction fills 8 rows, 1 KB).
+//
+// Pipeline, two LDS stages, one barrier per k-tile.  A k-tile is four k-steps of 16 MFMAs per wave; the
+// fragments of k-step s+1 are read while the MFMAs of k-step s run.  The barrier sits between k-steps 2 and
+// 3 of k-tile kt: past it, k-tile kt+1 is in LDS for every wave (its first fragments are read during
+// k-step 3) and no wave reads the stage of kt any more, so the loads of k-tile kt+2 go into that stage, half
+// in k-step 3 of kt and half in k-step 0 of kt+1.  Every load thus has about three k-steps to land, and the
+// address unit sees an even trickle of 1 KB requests rather than one burst.  MFMAs, LDS reads and loads are
+// placed one group at a time (sched_barrier between groups), so the schedule is the one written here.
 //
 // The loads are issued from inline assembly and the per-k-tile wait is an explicit "vmcnt(0); s_barrier":
 // the compiler's own waitcnt insertion cannot tell an LDS-DMA store from the fragment reads of the other stage
@@ -287,7 +293,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmArgs a) {
   constexpr int OUT_BN = GLU ? BN / 2 : BN;
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, STAGE = A_BYTES + B_BYTES;
   constexpr int A_LOADS = BM / 8 / 4, B_LOADS = BN / 8 / 4;  // 1 KB wave loads (8 rows) per wave per k-tile
-  constexpr int N_LOADS = A_LOADS + B_LOADS, PER = (N_LOADS + 3) / 4;  // loads issued per k-step
+  constexpr int N_LOADS = A_LOADS + B_LOADS;
   static_assert(!GLU || NI % 2 == 0, "GLU pairs gate and up blocks");
   static_assert(B_LOADS >= 1, "tile width");
   static_assert(BM * OUT_BN * 2 <= 2 * STAGE, "output staging fits the operand stages");
@@ -369,75 +375,95 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmArgs a) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.f;
 
-    // this wave's loads [part * PER, part * PER + PER) of k-tile kt into the stage at LDS address sb
-    auto issue = [&](int kt, uint32_t sb, int part) {
-      const unsigned char* ak = Ab + (uint32_t)kt * (BK * 2);
-      const unsigned char* bk = wbase + (uint32_t)kt * (BK * 2);
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int u = part * PER + i;
-        if (u < A_LOADS) dma16(ak, aoff[u], sb + (wave * A_LOADS + u) * 1024);
-        else if (u < N_LOADS) dma16(bk, boff[u - A_LOADS], sb + A_BYTES + (wave * B_LOADS + u - A_LOADS) * 1024);
-      }
-    };
-
     // 32-row MFMA blocks of this wave that hold present sub-blocks: all MI except in a tile's ragged tail
     const int mact = min(MI, max(0, (n_sub * 16 - wm * WM + 31) / 32));
     auto kloop = [&](auto full_tag) {
       constexpr bool FULL = decltype(full_tag)::value;
-#pragma unroll
-      for (int part = 0; part < 4; ++part) issue(0, lds0, part);
-      for (int kt = 0; kt < nk; ++kt) {
-        wait_loads_barrier();  // k-tile kt is in LDS for every wave; nobody reads the other stage any more
-        const bool more = kt + 1 < nk;
+      // slots of a k-step: MFMA i (if i < MI*NI), then fragment read i (if i < MI+NI), then loads; the loads go
+      // after the slots with a read where there are such slots, else spread over all of them
+      constexpr int NSLOT = MI * NI > MI + NI ? MI * NI : MI + NI;
+      constexpr int FIRST = MI * NI > MI + NI ? MI + NI : 0;
+      constexpr int HALF = (N_LOADS + 1) / 2;  // loads per half k-tile
+      constexpr int DPS = (HALF + (NSLOT - FIRST) - 1) / (NSLOT - FIRST);
+      // fragment i of k-step ks (i < MI: A block i, else B block i - MI) from the stage at sa
+      auto frag1 = [&](const unsigned char* sa, int ks, int i, bf16x8_t* A_, bf16x8_t* B_) {
+        const int sl = (((2 * ks + (lane >> 5)) ^ swz) << 4);
+        if (i < MI) {
+          A_[i] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(sa + (wm * WM + i * 32 + (lane & 31)) * 128 + sl));
+        } else {
+          const int ni = i - MI;
+          int row;
+          if (GLU) row = ni < NI / 2 ? wn * (WN / 2) + ni * 32 : BN / 2 + wn * (WN / 2) + (ni - NI / 2) * 32;
+          else row = wn * WN + ni * 32;
+          B_[ni] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(sa + A_BYTES + (row + (lane & 31)) * 128 + sl));
+        }
+      };
+      // this wave's load u of k-tile kt into the stage at LDS address sb
+      auto dma1 = [&](int kt, uint32_t sb, int u) {
+        const unsigned char* ak = Ab + (uint32_t)kt * (BK * 2);
+        const unsigned char* bk = wbase + (uint32_t)kt * (BK * 2);
+        if (u < A_LOADS) dma16(ak, aoff[u], sb + (wave * A_LOADS + u) * 1024);
+        else dma16(bk, boff[u - A_LOADS], sb + A_BYTES + (wave * B_LOADS + u - A_LOADS) * 1024);
+      };
+      bf16x8_t fa[2][MI], fb[2][NI];
+      // one k-step of k-tile kt; M1: k-tile kt+1 exists, M2: k-tile kt+2 exists
+      auto step = [&](auto ks_tag, auto m1_tag, auto m2_tag, int kt) {
+        constexpr int ks = decltype(ks_tag)::value;
+        constexpr bool M1 = decltype(m1_tag)::value, M2 = decltype(m2_tag)::value;
+        constexpr int c = ks & 1;
         const unsigned char* sa = smem + (kt & 1) * STAGE;
-        const unsigned char* sbb = sa + A_BYTES;
-        const uint32_t nsb = lds0 + ((kt + 1) & 1) * STAGE;
-        // fragments double-buffered in registers: reads of k-step ks+1 overlap the MFMAs of k-step ks
-        bf16x8_t fa[2][MI], fb[2][NI];
-        auto frags = [&](int ks, bf16x8_t* A_, bf16x8_t* B_) {
-          const int sl = (((2 * ks + (lane >> 5)) ^ swz) << 4);
+        const unsigned char* nsa = smem + ((kt + 1) & 1) * STAGE;
 #pragma unroll
-          for (int mi = 0; mi < MI; ++mi)
-            A_[mi] = __builtin_bit_cast(bf16x8_t,
-                                        *(const u32x4_t*)(sa + (wm * WM + mi * 32 + (lane & 31)) * 128 + sl));
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni) {
-            int row;
-            if (GLU) row = ni < NI / 2 ? wn * (WN / 2) + ni * 32 : BN / 2 + wn * (WN / 2) + (ni - NI / 2) * 32;
-            else row = wn * WN + ni * 32;
-            B_[ni] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(sbb + (row + (lane & 31)) * 128 + sl));
+        for (int i = 0; i < NSLOT; ++i) {
+          const int mi = i / NI, ni = i % NI;
+          if (i < MI * NI && (FULL || mi < mact))
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][mi], fb[c][ni], acc[mi][ni], 0, 0, 0);
+          if (i < MI + NI) {
+            if (ks < 3) frag1(sa, ks + 1, i, fa[c ^ 1], fb[c ^ 1]);
+            else if (M1) frag1(nsa, 0, i, fa[c ^ 1], fb[c ^ 1]);
           }
-        };
-        frags(0, fa[0], fb[0]);
+          if (i >= FIRST && ((ks == 3 && M2) || (ks == 0 && M1))) {
+            // first half of k-tile kt+2 after this tile's barrier; second half of k-tile kt+1 in k-step 0
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-          const int c = ks & 1;
-          if (more) issue(kt + 1, nsb, ks);
-          if (ks + 1 < BK / 16) frags(ks + 1, fa[c ^ 1], fb[c ^ 1]);
-#pragma unroll
-          for (int mi = 0; mi < MI; ++mi) {
-            if (!FULL && mi >= mact) continue;
-#pragma unroll
-            for (int ni = 0; ni < NI; ++ni)
-              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][mi], fb[c][ni], acc[mi][ni], 0, 0, 0);
-          }
-          if (FULL) {
-            // this k-step's MFMAs interleaved one-for-one with the next k-step's LDS reads, so each read has
-            // several MFMAs to land in (mask 0x008 = MFMA, 0x100 = LDS read)
-            if (ks + 1 < BK / 16 && MI * NI >= MI + NI) {
-#pragma unroll
-              for (int i = 0; i < MI + NI; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            for (int t = 0; t < DPS; ++t) {
+              const int v = (i - FIRST) * DPS + t;
+              if (v < HALF) {
+                if (ks == 3) dma1(kt + 2, lds0 + (kt & 1) * STAGE, v);
+                else if (HALF + v < N_LOADS) dma1(kt + 1, lds0 + ((kt + 1) & 1) * STAGE, HALF + v);
               }
-              if (MI * NI > MI + NI) __builtin_amdgcn_sched_group_barrier(0x008, MI * NI - (MI + NI), 0);
-            } else {
-              __builtin_amdgcn_sched_group_barrier(0x008, MI * NI, 0);
             }
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
+        if (ks == 2) {
+          // this wave's fragment reads of k-tile kt and loads of k-tile kt+1 are done; then everyone's are
+          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      auto tile = [&](auto m1, auto m2, int kt) {
+        step(std::integral_constant<int, 0>{}, m1, m2, kt);
+        step(std::integral_constant<int, 1>{}, m1, m2, kt);
+        step(std::integral_constant<int, 2>{}, m1, m2, kt);
+        step(std::integral_constant<int, 3>{}, m1, m2, kt);
+      };
+      // prologue: k-tile 0 whole, first half of k-tile 1 (its second half goes out in k-step 0 of k-tile 0)
+#pragma unroll
+      for (int u = 0; u < N_LOADS; ++u) dma1(0, lds0, u);
+      wait_loads_barrier();
+#pragma unroll
+      for (int i = 0; i < MI + NI; ++i) frag1(smem, 0, i, fa[0], fb[0]);
+      if (nk > 1) {
+#pragma unroll
+        for (int u = 0; u < HALF; ++u) dma1(1, lds0 + STAGE, u);
       }
+      int kt = 0;
+      for (; kt + 2 < nk; ++kt) tile(std::true_type{}, std::true_type{}, kt);
+      if (kt + 1 < nk) {
+        tile(std::true_type{}, std::false_type{}, kt);
+        ++kt;
+      }
+      tile(std::false_type{}, std::false_type{}, kt);
     };
     if (mact == MI) kloop(std::true_type{});
     else kloop(std::false_type{});
@@ -447,15 +473,20 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmArgs a) {
     // of present sub-blocks (padding rows inside them included, never read for a result)
     constexpr int NO = GLU ? NI / 2 : NI;
     constexpr int OUT_ROW = OUT_BN * 2, CPR = OUT_ROW / 16;
+    // the thread index, made opaque here, so that the many epilogue addresses are computed per item instead of
+    // being hoisted out of the item loop, where they would hold (and spill) registers through the k-loop
+    int tid_e = tid;
+    asm volatile("" : "+v"(tid_e));
+    const int lane_e = tid_e & 63;
     __syncthreads();  // every wave is done with the operand stages
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
       for (int ni = 0; ni < NO; ++ni) {
-        const int col = (GLU ? wn * (WN / 2) : wn * WN) + ni * 32 + (lane & 31);
+        const int col = (GLU ? wn * (WN / 2) : wn * WN) + ni * 32 + (lane_e & 31);
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-          const int row = wm * WM + mi * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+          const int row = wm * WM + mi * 32 + (q >> 2) * 8 + (lane_e >> 5) * 4 + (q & 3);
           float v = acc[mi][ni][q];
           if (GLU) v = silu_fast(v) * acc[mi][ni + NI / 2][q];
           const int chunk = (col >> 3) ^ (row & 7);
@@ -464,7 +495,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmArgs a) {
       }
     }
     __syncthreads();
-    for (int idx = tid; idx < BM * CPR; idx += 256) {
+    for (int idx = tid_e; idx < BM * CPR; idx += 256) {
       const int row = idx / CPR, ch = idx - row * CPR;
       const int sub = row >> 4;
       if (sub >= n_sub) continue;
