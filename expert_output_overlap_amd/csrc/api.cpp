@@ -112,7 +112,7 @@ int device_cus(int dev) {
 
 // Optional kernel timing: per call, events around GEMM1, GEMM2 (producer stream) and the consumer.
 struct CallEvents {
-  hipEvent_t e[5];  // gemm1 start, gemm1 end / gemm2 start, gemm2 end, consumer start, consumer end
+  hipEvent_t e[5];  // producer launch start, its end / second launch start, its end, consumer start, end
 };
 bool g_timing = false;
 std::vector<CallEvents> g_events;
@@ -255,7 +255,7 @@ int moe_read_status(const moe_layout* L, void* stream) {
 int64_t moe_ffn_flags_count(const moe_shape* s) {
   if (!check_shape(s).empty()) return -1;
   const Offsets o = layout_offsets(s);
-  return o.cap_mtiles * (s->d / ffn_gemm2_bn(s->dtype, s->d));
+  return ffn_flag_words(s->dtype, s->d, s->f, o.cap_mtiles);
 }
 
 int moe_expert_ffn_overlap(const moe_shape* s, const moe_layout* L, const void* x_pad, const void* w_gate_up,
@@ -297,26 +297,29 @@ int moe_expert_ffn_overlap(const moe_shape* s, const moe_layout* L, const void* 
   p.band_window = cfg->band_window;
   p.watchdog_ticks = cfg->watchdog_ticks ? cfg->watchdog_ticks : 200000000ull;
   p.timestamps = cfg->timestamps;
+  p.cap_mtiles = layout_offsets(s).cap_mtiles;
   const int C = cfg->consumer_cus;
 
   if (cfg->mode == 2) {  // return only
-    if (launch_ffn_gemm2(p, C, C, st)) return fail(MOE_EHIP, "consumer launch failed");
+    if (launch_ffn_consumer(p, C, st)) return fail(MOE_EHIP, "consumer launch failed");
     return MOE_OK;
   }
   CallEvents ce;
   const bool timed = g_timing && timing_begin(&ce) == 0;
-  if (cfg->timestamps && launch_ts_init(cfg->timestamps, st)) return fail(MOE_EHIP, "launch failed");
+  if (cfg->timestamps && launch_ts_init(cfg->timestamps, 2 + 2 * layout_offsets(s).cap_tiles, st))
+    return fail(MOE_EHIP, "launch failed");
+  // overlapped: C consumer workgroups in the producer launch (bf16: the whole FFN; fp32: its second GEMM),
+  // producers on the other CUs; sequential: producers on every CU, then the consumer alone
+  const int n_cons = cfg->mode == 0 ? C : 0;
   if (timed) hipEventRecord(ce.e[0], st);
-  if (launch_ffn_gemm1(p, n_cu, st)) return fail(MOE_EHIP, "producer launch failed");
+  if (launch_ffn_producer(p, n_cu, p.dtype == MOE_BF16 ? n_cons : 0, st)) return fail(MOE_EHIP, "producer launch failed");
   if (timed) hipEventRecord(ce.e[1], st);
-  // overlapped: one launch, C consumer workgroups + producers on the other CUs;
-  // sequential: producers on every CU, then the consumer alone
-  if (launch_ffn_gemm2(p, n_cu, cfg->mode == 0 ? C : 0, st)) return fail(MOE_EHIP, "producer launch failed");
+  if (launch_ffn_producer2(p, n_cu, n_cons, st)) return fail(MOE_EHIP, "producer launch failed");
   if (timed) {
     hipEventRecord(ce.e[2], st);
     hipEventRecord(ce.e[3], st);
   }
-  if (cfg->mode == 1 && launch_ffn_gemm2(p, C, C, st)) return fail(MOE_EHIP, "consumer launch failed");
+  if (cfg->mode == 1 && launch_ffn_consumer(p, C, st)) return fail(MOE_EHIP, "consumer launch failed");
   if (timed) {
     hipEventRecord(ce.e[4], st);
     std::lock_guard<std::mutex> lk(g_mu);

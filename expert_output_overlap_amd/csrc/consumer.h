@@ -4,10 +4,12 @@
 // width -- to its owner as one contiguous write).  On one GPU the owner ranks are receive buffers in HBM,
 // so a transfer is a device-memory copy by the consumer's CUs.
 //
-// Consumer workgroup w of C takes segments w, w + C, ... of the order in which their GEMM row tiles complete.  For a segment it polls the flags of
-// the GEMM row tiles the segment depends on with relaxed agent-scope loads, then issues one agent-scope
-// acquire fence (pairing with the producer's release) before reading the rows; a spin budget on the
-// 100 MHz clock bounds every wait.
+// Every consumer workgroup walks all segments in the order in which their GEMM row tiles complete and copies
+// its 1/C share of each (16-byte chunks w*B + t, then every C*B chunks for B threads): all C CUs work on the
+// segment that became ready last, so the copy that remains after the producer's final tile is short.  For a
+// segment it polls the flags of the GEMM row tiles the segment depends on with relaxed agent-scope loads,
+// then issues one agent-scope acquire fence (pairing with the producer's publish) before reading the rows;
+// a spin budget on the 100 MHz clock bounds every wait.
 #pragma once
 #include "common.h"
 
@@ -34,7 +36,7 @@ __device__ void consumer_role(const ConsumerArgs& a, int cid, int n_cons) {
   if (load_status(a.status) != 0) return;
   const int n_segs = a.scalars[SC_NSEGS];
   const uint64_t t0 = moe_clock();
-  for (int si = cid; si < n_segs; si += n_cons) {
+  for (int si = 0; si < n_segs; ++si) {
     const int s = a.seg_sched[si];
     const int mt0 = a.seg_mtiles[2 * s], mcnt = a.seg_mtiles[2 * s + 1];
     const int nflags = mcnt * a.n_nt;
@@ -56,12 +58,12 @@ __device__ void consumer_role(const ConsumerArgs& a, int cid, int n_cons) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const int32_t* sd = a.seg_desc + (int64_t)s * MOE_SEG_FIELDS;
     const int owner = sd[SEG_OWNER], src = sd[SEG_SRC_ROW], dst = sd[SEG_DST_ROW], rows = sd[SEG_ROWS];
-    if (a.ts != nullptr && tid == 0) a.ts[2 + 2 * s] = moe_clock();
+    if (a.ts != nullptr && tid == 0) atomicMin((unsigned long long*)&a.ts[2 + 2 * s], (unsigned long long)moe_clock());
     const uint4* __restrict__ from = a.y + (int64_t)src * a.row_vec;
     uint4* __restrict__ to = (uint4*)a.recv.p[owner] + (int64_t)dst * a.row_vec;
     const int64_t n = (int64_t)rows * a.row_vec;
-    int64_t i = tid;
-    const int64_t stride = blockDim.x;
+    const int64_t stride = (int64_t)n_cons * blockDim.x;
+    int64_t i = (int64_t)cid * blockDim.x + tid;
     for (; i + 3 * stride < n; i += 4 * stride) {
       const uint4 v0 = from[i], v1 = from[i + stride], v2 = from[i + 2 * stride], v3 = from[i + 3 * stride];
       to[i] = v0;
@@ -72,8 +74,7 @@ __device__ void consumer_role(const ConsumerArgs& a, int cid, int n_cons) {
     for (; i < n; i += stride) to[i] = from[i];
     if (a.ts != nullptr) {
       __syncthreads();
-      if (tid == 0) a.ts[3 + 2 * s] = moe_clock();
+      if (tid == 0) atomicMax((unsigned long long*)&a.ts[3 + 2 * s], (unsigned long long)moe_clock());
     }
   }
 }
-

@@ -286,8 +286,138 @@ __device__ __forceinline__ void wait_loads_barrier() { asm volatile("s_waitcnt v
 // SiLU with the hardware reciprocal (about 1 ulp), rounded to bf16 right after
 __device__ __forceinline__ float silu_fast(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
-template <int BN, bool GLU, bool PUBLISH>
-__global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmArgs a) {
+
+// The expert FFN as one persistent launch.  Work items:
+//   GEMM1 item (row tile mt, column tile nt): h[rows, nt*BN1/2 ...] = bf16(silu(x Wg^T) * (x Wu^T)), then
+//     flags1[mt][nt] = epoch (release);
+//   GEMM2 item (mt, nt, split s): the k-tiles of split s of y[rows, nt*BN2 ...] = h Wd^T, after acquiring the
+//     flags1 of the h columns that split reads.  With S > 1 splits, splits s < S-1 store fp32 partial sums and
+//     release sflags; split S-1 acquires them, adds them in split order (sum of splits 0..S-2, then its own),
+//     and stores the bf16 y tile and releases flags2[mt][nt], which the consumer waits on.
+// Items are listed window by window (band_window row tiles, remote-first order): GEMM1 of window 0, then
+// GEMM1 of window w+1 before GEMM2 of window w, so each GEMM2 item's inputs are finished well before it starts,
+// and row tiles complete (and are returned) one window after another instead of all at the end.  Producer
+// workgroup b takes items b, b + G, ... (XCD-aware: a run of consecutive items goes to the workgroups of one
+// XCD, which share the operands in their L2).  Every wait is on an item earlier in the list, so the lowest
+// unfinished item can always run: the waits end while every workgroup is resident, and a spin budget bounds
+// them otherwise.
+
+struct FusedArgs {
+  const unsigned char* x;   // x_pad [cap_rows, d]
+  const unsigned char* w1;  // [E_l, 2f, d]
+  const unsigned char* w2;  // [E_l, d, f]
+  unsigned char* h;         // [cap_rows, f]
+  unsigned char* y;         // y_pad [cap_rows, d]
+  int d, f;
+  int n_nt1, n_nt2, S, window;
+  const int32_t* mtile_desc;
+  const int32_t* scalars;
+  int sc_nmt;
+  int32_t* status;
+  uint32_t* flags2;  // [cap_mtiles][n_nt2]: y tile published (the consumer's flags)
+  uint32_t* flags1;  // [cap_mtiles][n_nt1]: h tile finished
+  uint32_t* sflags;  // [cap_mtiles][n_nt2][S-1]: partial sums of a split stored
+  float* partial;    // [cap_mtiles][n_nt2][S-1][256 * BN2]
+  uint32_t epoch;
+  uint64_t budget;
+  uint64_t* ts;
+  int n_cons;
+  ConsumerArgs cons;
+};
+
+struct FfnItem {
+  int kind;  // 1: GEMM1 tile, 2: GEMM2 split
+  int mt, nt, s;
+};
+
+// Item i of the list G1(0), G1(1), G2(0), G1(2), G2(1), ..., G1(nw-1), G2(nw-2), G2(nw-1) over nw windows of
+// W row tiles (the last one Wl <= W); inside a window, GEMM1 items are column-tile major (consecutive items share
+// a column tile of weights) and GEMM2 items split-major, then column-tile major.
+__device__ __forceinline__ FfnItem ffn_item(int i, int n_mt, int W, int n1, int n2, int S) {
+  const int n2S = n2 * S;
+  const int nw = (n_mt + W - 1) / W;
+  const int Wl = n_mt - (nw - 1) * W;
+  auto g1 = [&](int w, int j, int Wc) {
+    FfnItem it;
+    it.kind = 1;
+    it.nt = j / Wc;
+    it.mt = w * W + (j - it.nt * Wc);
+    it.s = 0;
+    return it;
+  };
+  auto g2 = [&](int w, int j, int Wc) {
+    FfnItem it;
+    it.kind = 2;
+    const int per = Wc * n2;
+    it.s = j / per;
+    const int r = j - it.s * per;
+    it.nt = r / Wc;
+    it.mt = w * W + (r - it.nt * Wc);
+    return it;
+  };
+  const int W0 = nw == 1 ? Wl : W;
+  if (i < W0 * n1) return g1(0, i, W0);
+  i -= W0 * n1;
+  if (nw == 1) return g2(0, i, Wl);
+  const int pz = W * (n1 + n2S);  // a pair (G1(p), G2(p-1)) of two full windows, p = 1 .. nw-2
+  if (i < (nw - 2) * pz) {
+    const int p = 1 + i / pz, j = i - (p - 1) * pz;
+    return j < W * n1 ? g1(p, j, W) : g2(p - 1, j - W * n1, W);
+  }
+  i -= (nw - 2) * pz;
+  if (i < Wl * n1) return g1(nw - 1, i, Wl);
+  i -= Wl * n1;
+  if (i < W * n2S) return g2(nw - 2, i, W);
+  return g2(nw - 1, i - W * n2S, Wl);
+}
+
+// All threads of the workgroup: wait until the n flags equal epoch, then acquire.  False if the spin budget ran
+// out (status set to MOE_ETIMEOUT) or another workgroup reported an error.
+__device__ bool wait_flags(const uint32_t* fl, int n, uint32_t epoch, uint64_t budget, int32_t* status, int* s_stop) {
+  const uint64_t t0 = moe_clock();
+  for (;;) {
+    int ok = 1;
+    for (int i = threadIdx.x; i < n; i += blockDim.x)
+      ok &= __hip_atomic_load(&fl[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
+    if (__syncthreads_and(ok)) break;
+    if (threadIdx.x == 0) *s_stop = (moe_clock() - t0 > budget) ? 1 : (load_status(status) != 0 ? 2 : 0);
+    __syncthreads();
+    if (*s_stop) {
+      if (*s_stop == 1 && threadIdx.x == 0) set_status(status, MOE_ETIMEOUT);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return true;
+}
+
+// Results that other workgroups read inside this launch (h tiles, split partial sums, y tiles) are written with
+// agent-scope atomic stores: on this chip those are coherent across the XCDs' separate L2 caches (they carry the
+// device-scope cache policy), and a store's completion, which s_waitcnt vmcnt waits for, means it is visible
+// device-wide.  Publishing is then: every thread's stores completed (the barrier's vmcnt(0)), then the flag.
+// An agent-scope release fence would write back the whole L2 of the XCD instead, once per published tile, which
+// stalls every workgroup on that XCD; the reader still acquires at agent scope before it reads.
+__device__ __forceinline__ void store16_coherent(void* p, u32x4_t v) {
+  uint64_t* q = (uint64_t*)p;
+  __hip_atomic_store(q, ((uint64_t)v.y << 32) | v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, ((uint64_t)v.w << 32) | v.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void publish(uint32_t* flag, uint32_t epoch) {
+  __syncthreads();  // waits for this wave's stores (vmcnt(0)), then for every wave's
+  if (threadIdx.x == 0) __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x8_t __attribute__((ext_vector_type(8)));
+
+// One item: output tile (row tile with sub-block rows s_sub[0, n_sub) of expert e, column tile nt), k-tiles of
+// split s.  GLU: the first GEMM (A = x_pad rows, B = gate rows nt*BN/2.. and up rows f + nt*BN/2..); else the
+// second (A = h rows, B = down-projection rows nt*BN..).  False if a wait gave up (the workgroup must exit).
+template <int BN, bool GLU>
+__device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem, const int* s_sub, int e, int n_sub,
+                                         int mt, int nt, int s, int* s_stop) {
   constexpr int BM = 256, BK = 64;
   constexpr int WM = 128, WN = BN / 2, MI = WM / 32, NI = WN / 32;
   constexpr int OUT_BN = GLU ? BN / 2 : BN;
@@ -296,223 +426,280 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16(GemmArgs a) {
   constexpr int N_LOADS = A_LOADS + B_LOADS;
   static_assert(!GLU || NI % 2 == 0, "GLU pairs gate and up blocks");
   static_assert(B_LOADS >= 1, "tile width");
-  static_assert(BM * OUT_BN * 2 <= 2 * STAGE, "output staging fits the operand stages");
 
-  __shared__ __align__(1024) unsigned char smem[2 * STAGE];
-  __shared__ int s_sub[MOE_MT_SUB];
-  __shared__ int s_hdr[2];
-
-  if (PUBLISH && (int)blockIdx.x < a.n_cons) {
-    consumer_role(a.cons, blockIdx.x, a.n_cons);
-    return;
-  }
-  if (load_status(a.status) != 0) return;
-  const int n_mt = a.scalars[a.sc_nmt];
-  const int n_items = n_mt * a.n_nt;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the thread index, made opaque per item, so that lane-derived addresses are computed here instead of being
+  // hoisted out of the item loop for both GEMMs at once (that would hold, and spill, their registers throughout)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int n_cons = PUBLISH ? a.n_cons : 0;
-  const int G = gridDim.x - n_cons;
-  int bid = blockIdx.x - n_cons;
-  if ((G & 7) == 0 && (n_cons & 7) == 0) bid = (bid & 7) * (G >> 3) + (bid >> 3);
-  const unsigned char* __restrict__ Ab = (const unsigned char*)a.A;
-  const unsigned char* __restrict__ Wb = (const unsigned char*)a.W;
-  unsigned char* __restrict__ Cb = (unsigned char*)a.C;
-  const int K = a.K;
+  const int K = GLU ? a.d : a.f;
+  const int nk = GLU ? K / BK : K / BK / a.S;
+  const int kt0 = GLU ? 0 : s * nk;
   const uint32_t row_bytes = (uint32_t)K * 2u;
-  const int nk = K / BK;
+  const unsigned char* __restrict__ Ab = (GLU ? a.x : a.h) + (uint32_t)kt0 * (BK * 2);
+  const unsigned char* __restrict__ Wb = GLU ? a.w1 : a.w2;
+  const int w_rows = GLU ? 2 * a.f : a.d;
+  unsigned char* __restrict__ Cb = GLU ? a.h : a.y;
+  const int64_t ldc = GLU ? a.f : a.d;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;  // LDS byte address of the stages
   // load mapping: wave instruction q fills tile rows [8q, 8q+8); lane -> row 8q + lane/8, LDS slot lane & 7,
   // which holds k-chunk (lane & 7) ^ swz(row) = (lane & 7) ^ (lane >> 3) ^ (q & 1)
   const uint32_t chunk0 = (uint32_t)(((lane & 7) ^ (lane >> 3)) << 4);
   // fragment mapping: row = base + (lane & 31), k-chunk c = 2 * kstep + (lane >> 5)
   const int swz = (lane & 7) ^ ((lane >> 3) & 1);
-  bool first = true;
 
-  for (int item = bid; item < n_items; item += G) {
-    const int per_win = a.window * a.n_nt;
-    const int w = item / per_win, j = item - w * per_win;
-    const int mt0 = w * a.window;
-    const int Wc = min(a.window, n_mt - mt0);
-    const int nt = j / Wc, mt = mt0 + (j - nt * Wc);
-
-    __syncthreads();  // previous item done with LDS and the header
-    if (tid < MOE_MT_FIELDS) {
-      const int v = a.mtile_desc[(int64_t)mt * MOE_MT_FIELDS + tid];
-      if (tid < 2) s_hdr[tid] = v;
-      else s_sub[tid - 2] = v;
-    }
-    if (PUBLISH && a.ts != nullptr && first && tid == 0)
-      atomicMin((unsigned long long*)&a.ts[0], (unsigned long long)moe_clock());
-    first = false;
-    __syncthreads();
-    const int e = s_hdr[0], n_sub = s_hdr[1];
-
-    uint32_t aoff[A_LOADS], boff[B_LOADS];
+  uint32_t aoff[A_LOADS], boff[B_LOADS];
 #pragma unroll
-    for (int jj = 0; jj < A_LOADS; ++jj) {
-      const int q = wave * A_LOADS + jj;
-      const int r = 8 * q + (lane >> 3);
-      const int sub = r >> 4;
-      const int row = sub < n_sub ? s_sub[sub] + (r & 15) : s_sub[0];  // absent sub-blocks read a real row
-      aoff[jj] = (uint32_t)row * row_bytes + (chunk0 ^ ((uint32_t)(q & 1) << 4));
-    }
-    const unsigned char* wbase = Wb + (int64_t)e * a.w_rows * row_bytes;
+  for (int jj = 0; jj < A_LOADS; ++jj) {
+    const int q = wave * A_LOADS + jj;
+    const int r = 8 * q + (lane >> 3);
+    const int sub = r >> 4;
+    const int row = sub < n_sub ? s_sub[sub] + (r & 15) : s_sub[0];  // absent sub-blocks read a real row
+    aoff[jj] = (uint32_t)row * row_bytes + (chunk0 ^ ((uint32_t)(q & 1) << 4));
+  }
+  const unsigned char* wbase = Wb + (int64_t)e * w_rows * row_bytes + (uint32_t)kt0 * (BK * 2);
 #pragma unroll
-    for (int jj = 0; jj < B_LOADS; ++jj) {
-      const int q = wave * B_LOADS + jj;
-      const int i = 8 * q + (lane >> 3);
-      int wrow;
-      if (GLU) wrow = i < BN / 2 ? nt * (BN / 2) + i : a.f + nt * (BN / 2) + (i - BN / 2);
-      else wrow = nt * BN + i;
-      boff[jj] = (uint32_t)wrow * row_bytes + (chunk0 ^ ((uint32_t)(q & 1) << 4));
+  for (int jj = 0; jj < B_LOADS; ++jj) {
+    const int q = wave * B_LOADS + jj;
+    const int i = 8 * q + (lane >> 3);
+    int wrow;
+    if (GLU) wrow = i < BN / 2 ? nt * (BN / 2) + i : a.f + nt * (BN / 2) + (i - BN / 2);
+    else wrow = nt * BN + i;
+    boff[jj] = (uint32_t)wrow * row_bytes + (chunk0 ^ ((uint32_t)(q & 1) << 4));
+  }
+  f32x16_t acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.f;
+
+  // 32-row MFMA blocks of this wave that hold present sub-blocks: all MI except in a tile's ragged tail
+  const int mact = min(MI, max(0, (n_sub * 16 - wm * WM + 31) / 32));
+  auto kloop = [&](auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    // slots of a k-step: MFMA i (if i < MI*NI), then fragment read i (if i < MI+NI), then loads; the loads go
+    // after the slots with a read where there are such slots, else spread over all of them
+    constexpr int NSLOT = MI * NI > MI + NI ? MI * NI : MI + NI;
+    constexpr int FIRST = MI * NI > MI + NI ? MI + NI : 0;
+    constexpr int HALF = (N_LOADS + 1) / 2;  // loads per half k-tile
+    constexpr int DPS = (HALF + (NSLOT - FIRST) - 1) / (NSLOT - FIRST);
+    // fragment i of k-step ks (i < MI: A block i, else B block i - MI) from the stage at sa
+    auto frag1 = [&](const unsigned char* sa, int ks, int i, bf16x8_t* A_, bf16x8_t* B_) {
+      const int sl = (((2 * ks + (lane >> 5)) ^ swz) << 4);
+      if (i < MI) {
+        A_[i] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(sa + (wm * WM + i * 32 + (lane & 31)) * 128 + sl));
+      } else {
+        const int ni = i - MI;
+        int row;
+        if (GLU) row = ni < NI / 2 ? wn * (WN / 2) + ni * 32 : BN / 2 + wn * (WN / 2) + (ni - NI / 2) * 32;
+        else row = wn * WN + ni * 32;
+        B_[ni] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(sa + A_BYTES + (row + (lane & 31)) * 128 + sl));
+      }
+    };
+    // this wave's load u of k-tile kt into the stage at LDS address sb
+    auto dma1 = [&](int kt, uint32_t sb, int u) {
+      const unsigned char* ak = Ab + (uint32_t)kt * (BK * 2);
+      const unsigned char* bk = wbase + (uint32_t)kt * (BK * 2);
+      if (u < A_LOADS) dma16(ak, aoff[u], sb + (wave * A_LOADS + u) * 1024);
+      else dma16(bk, boff[u - A_LOADS], sb + A_BYTES + (wave * B_LOADS + u - A_LOADS) * 1024);
+    };
+    bf16x8_t fa[2][MI], fb[2][NI];
+    // one k-step of k-tile kt; M1: k-tile kt+1 exists, M2: k-tile kt+2 exists
+    auto step = [&](auto ks_tag, auto m1_tag, auto m2_tag, int kt) {
+      constexpr int ks = decltype(ks_tag)::value;
+      constexpr bool M1 = decltype(m1_tag)::value, M2 = decltype(m2_tag)::value;
+      constexpr int c = ks & 1;
+      const unsigned char* sa = smem + (kt & 1) * STAGE;
+      const unsigned char* nsa = smem + ((kt + 1) & 1) * STAGE;
+#pragma unroll
+      for (int i = 0; i < NSLOT; ++i) {
+        const int mi = i / NI, ni = i % NI;
+        if (i < MI * NI && (FULL || mi < mact))
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][mi], fb[c][ni], acc[mi][ni], 0, 0, 0);
+        if (i < MI + NI) {
+          if (ks < 3) frag1(sa, ks + 1, i, fa[c ^ 1], fb[c ^ 1]);
+          else if (M1) frag1(nsa, 0, i, fa[c ^ 1], fb[c ^ 1]);
+        }
+        if (i >= FIRST && ((ks == 3 && M2) || (ks == 0 && M1))) {
+          // first half of k-tile kt+2 after this tile's barrier; second half of k-tile kt+1 in k-step 0
+#pragma unroll
+          for (int t = 0; t < DPS; ++t) {
+            const int v = (i - FIRST) * DPS + t;
+            if (v < HALF) {
+              if (ks == 3) dma1(kt + 2, lds0 + (kt & 1) * STAGE, v);
+              else if (HALF + v < N_LOADS) dma1(kt + 1, lds0 + ((kt + 1) & 1) * STAGE, HALF + v);
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (ks == 2) {
+        // this wave's fragment reads of k-tile kt and loads of k-tile kt+1 are done; then everyone's are
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    auto tile = [&](auto m1, auto m2, int kt) {
+      step(std::integral_constant<int, 0>{}, m1, m2, kt);
+      step(std::integral_constant<int, 1>{}, m1, m2, kt);
+      step(std::integral_constant<int, 2>{}, m1, m2, kt);
+      step(std::integral_constant<int, 3>{}, m1, m2, kt);
+    };
+    // prologue: k-tile 0 whole, first half of k-tile 1 (its second half goes out in k-step 0 of k-tile 0)
+#pragma unroll
+    for (int u = 0; u < N_LOADS; ++u) dma1(0, lds0, u);
+    wait_loads_barrier();
+#pragma unroll
+    for (int i = 0; i < MI + NI; ++i) frag1(smem, 0, i, fa[0], fb[0]);
+    if (nk > 1) {
+#pragma unroll
+      for (int u = 0; u < HALF; ++u) dma1(1, lds0 + STAGE, u);
     }
-    f32x16_t acc[MI][NI];
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) tile(std::true_type{}, std::true_type{}, kt);
+    if (kt + 1 < nk) {
+      tile(std::true_type{}, std::false_type{}, kt);
+      ++kt;
+    }
+    tile(std::false_type{}, std::false_type{}, kt);
+  };
+  if (mact == MI) kloop(std::true_type{});
+  else kloop(std::false_type{});
+  if (!GLU && a.S > 1) {
+    // split-K: thread tid keeps its accumulators at float4 chunk ((mi * NI + ni) * 4 + q4) * 256 + tid of a slot
+    const int64_t tile = (int64_t)mt * a.n_nt2 + nt;
+    f32x4_t* slots = (f32x4_t*)(a.partial + tile * (a.S - 1) * (BM * BN));
+    constexpr int SLOT4 = BM * BN / 4;
+    if (s < a.S - 1) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          f32x4_t* dst = slots + (int64_t)s * SLOT4 + (mi * NI + ni) * 4 * 256 + tid;
+          const f32x16_t v = acc[mi][ni];
+          store16_coherent(dst, __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v, v, 0, 1, 2, 3)));
+          store16_coherent(dst + 256, __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v, v, 4, 5, 6, 7)));
+          store16_coherent(dst + 512, __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v, v, 8, 9, 10, 11)));
+          store16_coherent(dst + 768, __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v, v, 12, 13, 14, 15)));
+        }
+      publish(&a.sflags[tile * (a.S - 1) + s], a.epoch);
+      return true;
+    }
+    if (!wait_flags(a.sflags + tile * (a.S - 1), a.S - 1, a.epoch, a.budget, a.status, s_stop)) return false;
+    // y = (p_0 + p_1 + ... + p_{S-2}) + own, the same association on every call; one 32 x 32 block at a time
+    auto ld16 = [&](const f32x4_t* src) {
+      const f32x4_t q0 = __builtin_nontemporal_load(src), q1 = __builtin_nontemporal_load(src + 256);
+      const f32x4_t q2 = __builtin_nontemporal_load(src + 512), q3 = __builtin_nontemporal_load(src + 768);
+      const f32x8_t h0 = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
+      const f32x8_t h1 = __builtin_shufflevector(q2, q3, 0, 1, 2, 3, 4, 5, 6, 7);
+      return (f32x16_t)__builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+    };
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.f;
+      for (int ni = 0; ni < NI; ++ni) {
+        const f32x4_t* src = slots + (mi * NI + ni) * 4 * 256 + tid;
+        f32x16_t t = ld16(src);
+        for (int sp = 1; sp < a.S - 1; ++sp) t += ld16(src + (int64_t)sp * SLOT4);
+        acc[mi][ni] = t + acc[mi][ni];
+      }
+  }
 
-    // 32-row MFMA blocks of this wave that hold present sub-blocks: all MI except in a tile's ragged tail
-    const int mact = min(MI, max(0, (n_sub * 16 - wm * WM + 31) / 32));
-    auto kloop = [&](auto full_tag) {
-      constexpr bool FULL = decltype(full_tag)::value;
-      // slots of a k-step: MFMA i (if i < MI*NI), then fragment read i (if i < MI+NI), then loads; the loads go
-      // after the slots with a read where there are such slots, else spread over all of them
-      constexpr int NSLOT = MI * NI > MI + NI ? MI * NI : MI + NI;
-      constexpr int FIRST = MI * NI > MI + NI ? MI + NI : 0;
-      constexpr int HALF = (N_LOADS + 1) / 2;  // loads per half k-tile
-      constexpr int DPS = (HALF + (NSLOT - FIRST) - 1) / (NSLOT - FIRST);
-      // fragment i of k-step ks (i < MI: A block i, else B block i - MI) from the stage at sa
-      auto frag1 = [&](const unsigned char* sa, int ks, int i, bf16x8_t* A_, bf16x8_t* B_) {
-        const int sl = (((2 * ks + (lane >> 5)) ^ swz) << 4);
-        if (i < MI) {
-          A_[i] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(sa + (wm * WM + i * 32 + (lane & 31)) * 128 + sl));
-        } else {
-          const int ni = i - MI;
-          int row;
-          if (GLU) row = ni < NI / 2 ? wn * (WN / 2) + ni * 32 : BN / 2 + wn * (WN / 2) + (ni - NI / 2) * 32;
-          else row = wn * WN + ni * 32;
-          B_[ni] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(sa + A_BYTES + (row + (lane & 31)) * 128 + sl));
-        }
-      };
-      // this wave's load u of k-tile kt into the stage at LDS address sb
-      auto dma1 = [&](int kt, uint32_t sb, int u) {
-        const unsigned char* ak = Ab + (uint32_t)kt * (BK * 2);
-        const unsigned char* bk = wbase + (uint32_t)kt * (BK * 2);
-        if (u < A_LOADS) dma16(ak, aoff[u], sb + (wave * A_LOADS + u) * 1024);
-        else dma16(bk, boff[u - A_LOADS], sb + A_BYTES + (wave * B_LOADS + u - A_LOADS) * 1024);
-      };
-      bf16x8_t fa[2][MI], fb[2][NI];
-      // one k-step of k-tile kt; M1: k-tile kt+1 exists, M2: k-tile kt+2 exists
-      auto step = [&](auto ks_tag, auto m1_tag, auto m2_tag, int kt) {
-        constexpr int ks = decltype(ks_tag)::value;
-        constexpr bool M1 = decltype(m1_tag)::value, M2 = decltype(m2_tag)::value;
-        constexpr int c = ks & 1;
-        const unsigned char* sa = smem + (kt & 1) * STAGE;
-        const unsigned char* nsa = smem + ((kt + 1) & 1) * STAGE;
+  // epilogue: every wave writes its bf16 outputs into LDS as a 256 x OUT_BN tile (16-byte chunk ch of row r at
+  // chunk ch ^ (r & 7), so neither the column writes nor the row reads collide), then 16-byte stores of the rows
+  // of present sub-blocks (padding rows inside them included, never read for a result)
+  constexpr int NO = GLU ? NI / 2 : NI;
+  constexpr int OUT_ROW = OUT_BN * 2, CPR = OUT_ROW / 16;
+  // the thread index, made opaque here, so that the many epilogue addresses are computed per item instead of
+  // being hoisted out of the item loop, where they would hold (and spill) registers through the k-loop
+  int tid_e = tid;
+  asm volatile("" : "+v"(tid_e));
+  const int lane_e = tid_e & 63;
+  __syncthreads();  // every wave is done with the operand stages
 #pragma unroll
-        for (int i = 0; i < NSLOT; ++i) {
-          const int mi = i / NI, ni = i % NI;
-          if (i < MI * NI && (FULL || mi < mact))
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][mi], fb[c][ni], acc[mi][ni], 0, 0, 0);
-          if (i < MI + NI) {
-            if (ks < 3) frag1(sa, ks + 1, i, fa[c ^ 1], fb[c ^ 1]);
-            else if (M1) frag1(nsa, 0, i, fa[c ^ 1], fb[c ^ 1]);
-          }
-          if (i >= FIRST && ((ks == 3 && M2) || (ks == 0 && M1))) {
-            // first half of k-tile kt+2 after this tile's barrier; second half of k-tile kt+1 in k-step 0
+  for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
-            for (int t = 0; t < DPS; ++t) {
-              const int v = (i - FIRST) * DPS + t;
-              if (v < HALF) {
-                if (ks == 3) dma1(kt + 2, lds0 + (kt & 1) * STAGE, v);
-                else if (HALF + v < N_LOADS) dma1(kt + 1, lds0 + ((kt + 1) & 1) * STAGE, HALF + v);
-              }
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if (ks == 2) {
-          // this wave's fragment reads of k-tile kt and loads of k-tile kt+1 are done; then everyone's are
-          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      };
-      auto tile = [&](auto m1, auto m2, int kt) {
-        step(std::integral_constant<int, 0>{}, m1, m2, kt);
-        step(std::integral_constant<int, 1>{}, m1, m2, kt);
-        step(std::integral_constant<int, 2>{}, m1, m2, kt);
-        step(std::integral_constant<int, 3>{}, m1, m2, kt);
-      };
-      // prologue: k-tile 0 whole, first half of k-tile 1 (its second half goes out in k-step 0 of k-tile 0)
+    for (int ni = 0; ni < NO; ++ni) {
+      const int col = (GLU ? wn * (WN / 2) : wn * WN) + ni * 32 + (lane_e & 31);
 #pragma unroll
-      for (int u = 0; u < N_LOADS; ++u) dma1(0, lds0, u);
-      wait_loads_barrier();
-#pragma unroll
-      for (int i = 0; i < MI + NI; ++i) frag1(smem, 0, i, fa[0], fb[0]);
-      if (nk > 1) {
-#pragma unroll
-        for (int u = 0; u < HALF; ++u) dma1(1, lds0 + STAGE, u);
-      }
-      int kt = 0;
-      for (; kt + 2 < nk; ++kt) tile(std::true_type{}, std::true_type{}, kt);
-      if (kt + 1 < nk) {
-        tile(std::true_type{}, std::false_type{}, kt);
-        ++kt;
-      }
-      tile(std::false_type{}, std::false_type{}, kt);
-    };
-    if (mact == MI) kloop(std::true_type{});
-    else kloop(std::false_type{});
-
-    // epilogue: every wave writes its bf16 outputs into LDS as a 256 x OUT_BN tile (16-byte chunk ch of row r at
-    // chunk ch ^ (r & 7), so neither the column writes nor the row reads collide), then 16-byte stores of the rows
-    // of present sub-blocks (padding rows inside them included, never read for a result)
-    constexpr int NO = GLU ? NI / 2 : NI;
-    constexpr int OUT_ROW = OUT_BN * 2, CPR = OUT_ROW / 16;
-    // the thread index, made opaque here, so that the many epilogue addresses are computed per item instead of
-    // being hoisted out of the item loop, where they would hold (and spill) registers through the k-loop
-    int tid_e = tid;
-    asm volatile("" : "+v"(tid_e));
-    const int lane_e = tid_e & 63;
-    __syncthreads();  // every wave is done with the operand stages
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-#pragma unroll
-      for (int ni = 0; ni < NO; ++ni) {
-        const int col = (GLU ? wn * (WN / 2) : wn * WN) + ni * 32 + (lane_e & 31);
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int row = wm * WM + mi * 32 + (q >> 2) * 8 + (lane_e >> 5) * 4 + (q & 3);
-          float v = acc[mi][ni][q];
-          if (GLU) v = silu_fast(v) * acc[mi][ni + NI / 2][q];
-          const int chunk = (col >> 3) ^ (row & 7);
-          *(__bf16*)(smem + row * OUT_ROW + chunk * 16 + (col & 7) * 2) = (__bf16)v;  // round to nearest even
-        }
-      }
-    }
-    __syncthreads();
-    for (int idx = tid_e; idx < BM * CPR; idx += 256) {
-      const int row = idx / CPR, ch = idx - row * CPR;
-      const int sub = row >> 4;
-      if (sub >= n_sub) continue;
-      const u32x4_t v = *(const u32x4_t*)(smem + row * OUT_ROW + ((ch ^ (row & 7)) << 4));
-      const int64_t grow = s_sub[sub] + (row & 15);
-      *(u32x4_t*)(Cb + (grow * a.ldc + (int64_t)nt * OUT_BN) * 2 + ch * 16) = v;
-    }
-    if (PUBLISH) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this thread's tile stores, agent-visible
-      __syncthreads();
-      if (tid == 0) {
-        __hip_atomic_store(&a.flags[(int64_t)mt * a.n_nt + nt], a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        if (a.ts != nullptr) atomicMax((unsigned long long*)&a.ts[1], (unsigned long long)moe_clock());
+      for (int q = 0; q < 16; ++q) {
+        const int row = wm * WM + mi * 32 + (q >> 2) * 8 + (lane_e >> 5) * 4 + (q & 3);
+        float v = acc[mi][ni][q];
+        if (GLU) v = silu_fast(v) * acc[mi][ni + NI / 2][q];
+        const int chunk = (col >> 3) ^ (row & 7);
+        *(__bf16*)(smem + row * OUT_ROW + chunk * 16 + (col & 7) * 2) = (__bf16)v;  // round to nearest even
       }
     }
   }
+  __syncthreads();
+  for (int idx = tid_e; idx < BM * CPR; idx += 256) {
+    const int row = idx / CPR, ch = idx - row * CPR;
+    const int sub = row >> 4;
+    if (sub >= n_sub) continue;
+    const u32x4_t v = *(const u32x4_t*)(smem + row * OUT_ROW + ((ch ^ (row & 7)) << 4));
+    const int64_t grow = s_sub[sub] + (row & 15);
+    store16_coherent(Cb + (grow * ldc + (int64_t)nt * OUT_BN) * 2 + ch * 16, v);
+  }
+  if (GLU) {
+    publish(&a.flags1[(int64_t)mt * a.n_nt1 + nt], a.epoch);
+  } else {
+    publish(&a.flags2[(int64_t)mt * a.n_nt2 + nt], a.epoch);
+    if (a.ts != nullptr && tid == 0) atomicMax((unsigned long long*)&a.ts[1], (unsigned long long)moe_clock());
+  }
+  return true;
 }
+
+template <int BN1, int BN2>
+__global__ __launch_bounds__(256, 1) void k_ffn_bf16(FusedArgs a) {
+  constexpr int BM = 256, BK = 64, BNX = BN1 > BN2 ? BN1 : BN2;
+  constexpr int STAGE = (BM + BNX) * BK * 2;
+  static_assert(BM * BN2 * 2 <= 2 * STAGE && BM * BN1 <= 2 * STAGE, "output staging fits the operand stages");
+  __shared__ __align__(1024) unsigned char smem[2 * STAGE];
+  __shared__ int s_sub[MOE_MT_SUB];
+  __shared__ int s_hdr[2];
+  __shared__ int s_stop;
+
+  if ((int)blockIdx.x < a.n_cons) {
+    consumer_role(a.cons, blockIdx.x, a.n_cons);
+    return;
+  }
+  if (load_status(a.status) != 0) return;
+  const int n_mt = a.scalars[a.sc_nmt];
+  const int n_items = n_mt * (a.n_nt1 + a.n_nt2 * a.S);
+  const int tid = threadIdx.x;
+  const int G = gridDim.x - a.n_cons;
+  int bid = blockIdx.x - a.n_cons;
+  if ((G & 7) == 0 && (a.n_cons & 7) == 0) bid = (bid & 7) * (G >> 3) + (bid >> 3);
+  bool first = true;
+  for (int item = bid; item < n_items; item += G) {
+    const FfnItem it = ffn_item(item, n_mt, a.window, a.n_nt1, a.n_nt2, a.S);
+    __syncthreads();  // previous item done with LDS and the header
+    if (tid < MOE_MT_FIELDS) {
+      const int v = a.mtile_desc[(int64_t)it.mt * MOE_MT_FIELDS + tid];
+      if (tid < 2) s_hdr[tid] = v;
+      else s_sub[tid - 2] = v;
+    }
+    if (a.ts != nullptr && first && tid == 0) atomicMin((unsigned long long*)&a.ts[0], (unsigned long long)moe_clock());
+    first = false;
+    __syncthreads();
+    const int e = s_hdr[0], n_sub = s_hdr[1];
+    bool ok;
+    if (it.kind == 1) {
+      ok = ffn_tile<BN1, true>(a, smem, s_sub, e, n_sub, it.mt, it.nt, 0, &s_stop);
+    } else {
+      // the h columns this split reads: column tiles [s, s+1) * n_nt1 / S of the first GEMM
+      const int per = a.n_nt1 / a.S;
+      ok = wait_flags(a.flags1 + (int64_t)it.mt * a.n_nt1 + it.s * per, per, a.epoch, a.budget, a.status, &s_stop) &&
+           ffn_tile<BN2, false>(a, smem, s_sub, e, n_sub, it.mt, it.nt, it.s, &s_stop);
+    }
+    if (!ok) return;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_consumer(ConsumerArgs c) { consumer_role(c, blockIdx.x, gridDim.x); }
 
 // ---- tile configurations --------------------------------------------------------------------------------
 #define BF_BM 256
@@ -531,7 +718,56 @@ int ffn_gemm2_bn(int dtype, int d) {
   return F32_BN;
 }
 
-static GemmArgs base_args(const FfnLaunch& p) {
+// k-splits of a second-GEMM tile: about as many as make its k-loop as long as a first-GEMM tile's
+// (f / d rounded, at most 8), restricted so that each split reads whole first-GEMM column tiles of h
+int ffn_splits(int dtype, int d, int f) {
+  if (dtype != MOE_BF16) return 1;
+  const int n_nt1 = f / (gemm1_bn(dtype, f) / 2), nk2 = f / 64;
+  int want = (2 * f + d) / (2 * d);
+  want = want < 1 ? 1 : (want > 8 ? 8 : want);
+  for (int S = want; S > 1; --S)
+    if (n_nt1 % S == 0 && nk2 % S == 0) return S;
+  return 1;
+}
+
+namespace {
+struct FlagCarve {
+  int64_t flags2, flags1, sflags, partial, total;  // offsets and size in 4-byte words
+};
+FlagCarve flag_carve(int dtype, int d, int f, int64_t cap_mtiles) {
+  FlagCarve c;
+  const int64_t n2 = d / ffn_gemm2_bn(dtype, d);
+  c.flags2 = 0;
+  if (dtype != MOE_BF16) {
+    c.flags1 = c.sflags = c.partial = c.total = cap_mtiles * n2;
+    return c;
+  }
+  const int64_t n1 = f / (gemm1_bn(dtype, f) / 2), S = ffn_splits(dtype, d, f);
+  auto up = [](int64_t v) { return (v + 63) / 64 * 64; };
+  c.flags1 = up(cap_mtiles * n2);
+  c.sflags = c.flags1 + up(cap_mtiles * n1);
+  c.partial = c.sflags + up(cap_mtiles * n2 * (S - 1));
+  c.total = c.partial + cap_mtiles * n2 * (S - 1) * (int64_t)BF_BM * ffn_gemm2_bn(dtype, d);
+  return c;
+}
+
+void fill_consumer(ConsumerArgs& c, const FfnLaunch& p, int n_nt2) {
+  c.y = (const uint4*)p.y_pad;
+  for (int r = 0; r < MOE_MAX_OWNERS; ++r) c.recv.p[r] = r < p.R ? p.recv[r] : nullptr;
+  c.seg_desc = p.L->seg_desc;
+  c.seg_mtiles = p.L->seg_mtiles;
+  c.seg_sched = p.L->seg_sched;
+  c.scalars = p.L->scalars;
+  c.status = p.L->status;
+  c.flags = p.flags;
+  c.epoch = p.epoch;
+  c.n_nt = n_nt2;
+  c.row_vec = p.d * (p.dtype == MOE_BF16 ? 2 : 4) / 16;
+  c.budget = p.watchdog_ticks;
+  c.ts = p.timestamps;
+}
+
+GemmArgs base_args(const FfnLaunch& p) {
   GemmArgs a;
   a.mtile_desc = p.L->mtile_desc;
   a.scalars = p.L->scalars;
@@ -545,7 +781,50 @@ static GemmArgs base_args(const FfnLaunch& p) {
   return a;
 }
 
-int launch_ffn_gemm1(const FfnLaunch& p, int grid, hipStream_t st) {
+int launch_bf16(const FfnLaunch& p, int grid, int n_cons, hipStream_t st) {
+  FusedArgs a;
+  const FlagCarve fc = flag_carve(p.dtype, p.d, p.f, p.cap_mtiles);
+  a.x = (const unsigned char*)p.x_pad;
+  a.w1 = (const unsigned char*)p.w_gate_up;
+  a.w2 = (const unsigned char*)p.w_down;
+  a.h = (unsigned char*)p.h;
+  a.y = (unsigned char*)p.y_pad;
+  a.d = p.d;
+  a.f = p.f;
+  const int bn1 = gemm1_bn(p.dtype, p.f), bn2 = ffn_gemm2_bn(p.dtype, p.d);
+  a.n_nt1 = p.f / (bn1 / 2);
+  a.n_nt2 = p.d / bn2;
+  a.S = ffn_splits(p.dtype, p.d, p.f);
+  a.window = p.band_window > 0 ? p.band_window : 4;
+  a.mtile_desc = p.L->mtile_desc;
+  a.scalars = p.L->scalars;
+  a.sc_nmt = SC_NR + p.R;
+  a.status = p.L->status;
+  a.flags2 = p.flags + fc.flags2;
+  a.flags1 = p.flags + fc.flags1;
+  a.sflags = p.flags + fc.sflags;
+  a.partial = (float*)(p.flags + fc.partial);
+  a.epoch = p.epoch;
+  a.budget = p.watchdog_ticks;
+  a.ts = p.timestamps;
+  a.n_cons = n_cons;
+  fill_consumer(a.cons, p, a.n_nt2);
+  const dim3 g(grid), b(256);
+  if (bn1 == 256 && bn2 == 256) hipLaunchKernelGGL((k_ffn_bf16<256, 256>), g, b, 0, st, a);
+  else if (bn1 == 256 && bn2 == 128) hipLaunchKernelGGL((k_ffn_bf16<256, 128>), g, b, 0, st, a);
+  else if (bn1 == 256) hipLaunchKernelGGL((k_ffn_bf16<256, 64>), g, b, 0, st, a);
+  else if (bn2 == 256) hipLaunchKernelGGL((k_ffn_bf16<128, 256>), g, b, 0, st, a);
+  // narrower tiles hold under 80 KB of LDS; pad them so that one workgroup still fills a CU
+  else if (bn2 == 128) hipLaunchKernelGGL((k_ffn_bf16<128, 128>), g, b, 16384, st, a);
+  else hipLaunchKernelGGL((k_ffn_bf16<128, 64>), g, b, 16384, st, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+}  // namespace
+
+int64_t ffn_flag_words(int dtype, int d, int f, int64_t cap_mtiles) { return flag_carve(dtype, d, f, cap_mtiles).total; }
+
+int launch_ffn_producer(const FfnLaunch& p, int grid, int n_cons, hipStream_t st) {
+  if (p.dtype == MOE_BF16) return launch_bf16(p, grid, n_cons, st);
   GemmArgs a = base_args(p);
   a.A = p.x_pad;
   a.W = p.w_gate_up;
@@ -554,18 +833,13 @@ int launch_ffn_gemm1(const FfnLaunch& p, int grid, hipStream_t st) {
   a.w_rows = 2 * p.f;
   a.ldc = p.f;
   a.f = p.f;
-  const int bn = gemm1_bn(p.dtype, p.f);
-  a.n_nt = p.f / (bn / 2);
-  if (p.dtype == MOE_BF16) {
-    if (bn == 256) hipLaunchKernelGGL((k_gemm_bf16<256, true, false>), dim3(grid), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((k_gemm_bf16<128, true, false>), dim3(grid), dim3(256), 0, st, a);
-  } else {
-    hipLaunchKernelGGL((k_gemm<float, F32_BM, F32_BN, 2, 1, true, false>), dim3(grid), dim3(128), 0, st, a);
-  }
+  a.n_nt = p.f / (F32_BN / 2);
+  hipLaunchKernelGGL((k_gemm<float, F32_BM, F32_BN, 2, 1, true, false>), dim3(grid), dim3(128), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int launch_ffn_gemm2(const FfnLaunch& p, int grid, int n_cons, hipStream_t st) {
+int launch_ffn_producer2(const FfnLaunch& p, int grid, int n_cons, hipStream_t st) {
+  if (p.dtype == MOE_BF16) return 0;  // one launch does both GEMMs
   GemmArgs a = base_args(p);
   a.A = p.h;
   a.W = p.w_down;
@@ -575,40 +849,27 @@ int launch_ffn_gemm2(const FfnLaunch& p, int grid, int n_cons, hipStream_t st) {
   a.ldc = p.d;
   a.f = p.f;
   a.flags = p.flags;
-  const int bn = ffn_gemm2_bn(p.dtype, p.d);
-  a.n_nt = p.d / bn;
+  a.n_nt = p.d / F32_BN;
   a.n_cons = n_cons;
-  ConsumerArgs& c = a.cons;
-  c.y = (const uint4*)p.y_pad;
-  for (int r = 0; r < MOE_MAX_OWNERS; ++r) c.recv.p[r] = r < p.R ? p.recv[r] : nullptr;
-  c.seg_desc = p.L->seg_desc;
-  c.seg_mtiles = p.L->seg_mtiles;
-  c.seg_sched = p.L->seg_sched;
-  c.scalars = p.L->scalars;
-  c.status = p.L->status;
-  c.flags = p.flags;
-  c.epoch = p.epoch;
-  c.n_nt = a.n_nt;
-  c.row_vec = p.d * (p.dtype == MOE_BF16 ? 2 : 4) / 16;
-  c.budget = p.watchdog_ticks;
-  c.ts = p.timestamps;
-  // the bf16 workgroups hold over 80 KB of LDS (one per CU); pad the narrow variants to keep that true
-  if (p.dtype == MOE_BF16) {
-    if (bn == 256) hipLaunchKernelGGL((k_gemm_bf16<256, false, true>), dim3(grid), dim3(256), 0, st, a);
-    else if (bn == 128) hipLaunchKernelGGL((k_gemm_bf16<128, false, true>), dim3(grid), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((k_gemm_bf16<64, false, true>), dim3(grid), dim3(256), 16384, st, a);
-  } else {
-    hipLaunchKernelGGL((k_gemm<float, F32_BM, F32_BN, 2, 1, false, true>), dim3(grid), dim3(128), 0, st, a);
-  }
+  fill_consumer(a.cons, p, a.n_nt);
+  hipLaunchKernelGGL((k_gemm<float, F32_BM, F32_BN, 2, 1, false, true>), dim3(grid), dim3(128), 0, st, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-__global__ void k_ts_init(uint64_t* ts) {
-  ts[0] = ~0ull;
-  ts[1] = 0ull;
+int launch_ffn_consumer(const FfnLaunch& p, int n_cons, hipStream_t st) {
+  ConsumerArgs c;
+  fill_consumer(c, p, p.d / ffn_gemm2_bn(p.dtype, p.d));
+  hipLaunchKernelGGL(k_consumer, dim3(n_cons), dim3(256), 0, st, c);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int launch_ts_init(uint64_t* timestamps, hipStream_t st) {
-  hipLaunchKernelGGL(k_ts_init, dim3(1), dim3(1), 0, st, timestamps);
+// even entries (starts, taken with atomicMin) to the largest value, odd ones (ends, atomicMax) to zero
+__global__ void k_ts_init(uint64_t* ts, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    ts[i] = (i & 1) ? 0ull : ~0ull;
+}
+
+int launch_ts_init(uint64_t* timestamps, int64_t n, hipStream_t st) {
+  hipLaunchKernelGGL(k_ts_init, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, timestamps, n);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

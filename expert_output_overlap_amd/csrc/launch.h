@@ -31,6 +31,7 @@ struct FfnLaunch {
   int band_window;
   uint64_t watchdog_ticks;
   uint64_t* timestamps;
+  int64_t cap_mtiles;
 };
 
 struct CombineLaunch {
@@ -49,9 +50,18 @@ int launch_layout(const LayoutLaunch& p, hipStream_t st);
 int ffn_gemm_bm(int dtype);
 // Output tile width of the second GEMM (y): flags are one per (row tile, column tile).
 int ffn_gemm2_bn(int dtype, int d);
-// One workgroup per CU for the first GEMM; the second GEMM's launch runs `n_cons` consumer workgroups
-// first (a launch with grid == n_cons is the consumer alone).
-int launch_ffn_gemm1(const FfnLaunch& p, int grid, hipStream_t st);
-int launch_ffn_gemm2(const FfnLaunch& p, int grid, int n_cons, hipStream_t st);
-int launch_ts_init(uint64_t* timestamps, hipStream_t st);
+// k-splits of a second-GEMM tile (bf16; 1 for fp32).
+int ffn_splits(int dtype, int d, int f);
+// 4-byte words of the FFN flag buffer: y-tile flags first, then (bf16) h-tile flags, split flags and the
+// fp32 partial sums of the k-splits.
+int64_t ffn_flag_words(int dtype, int d, int f, int64_t cap_mtiles);
+// Producer launch, one workgroup per CU, whose first `n_cons` workgroups run the consumer role.  bf16: the
+// whole FFN in one launch (launch_ffn_producer2 is a no-op); fp32: the first GEMM, then the second GEMM with the
+// consumer workgroups.
+int launch_ffn_producer(const FfnLaunch& p, int grid, int n_cons, hipStream_t st);
+int launch_ffn_producer2(const FfnLaunch& p, int grid, int n_cons, hipStream_t st);
+// The consumer alone (`n_cons` workgroups).
+int launch_ffn_consumer(const FfnLaunch& p, int n_cons, hipStream_t st);
+// Resets the n timestamp entries of a call (starts to the largest value, ends to zero).
+int launch_ts_init(uint64_t* timestamps, int64_t n, hipStream_t st);
 int launch_combine(const CombineLaunch& p, hipStream_t st);

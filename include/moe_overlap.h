@@ -104,8 +104,9 @@ typedef struct {
   uint64_t watchdog_ticks; /* consumer spin budget in 100 MHz ticks (0 = 2 s); on expiry the status word
                               becomes MOE_ETIMEOUT and the consumer exits */
   uint64_t* timestamps;    /* optional (device) [2 + 2*cap_tiles] u64, 100 MHz clock: [0] first producer
-                              item start, [1] last flag publish, [2+2s] / [3+2s] copy start / end of segment
-                              s; NULL to skip */
+                              item start, [1] last flag publish, [2+2s] / [3+2s] first copy start / last copy
+                              end of segment s over the consumer workgroups; reset by the call; NULL to
+                              skip */
 } moe_overlap_cfg;
 
 /* Last host-side error message of the calling thread ("" if none). */

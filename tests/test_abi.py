@@ -97,4 +97,16 @@ def test_flag_count_covers_row_tiles():
     base = (buf.ctypes.data + 255) // 256 * 256
     assert B.lib().moe_layout_bind(ctypes.byref(s), ctypes.c_void_p(base), nbytes, ctypes.byref(L)) == 0
     nflags = B.moe_ffn_flags_count(s)
-    assert nflags % L.cap_mtiles == 0 and nflags // L.cap_mtiles >= 1
+    n_nt2 = s.d // 256  # 256-wide output tiles of the second GEMM
+    assert nflags >= L.cap_mtiles * n_nt2
+    # f = 3.5 d: the second GEMM's tiles are split 4 ways over k, and three fp32 partial 256 x 256 tiles per
+    # output tile live in the same buffer
+    assert nflags >= L.cap_mtiles * n_nt2 * (1 + 3 * 256 * 256)
+    # an fp32 shape has one flag per output tile of the second GEMM (64 wide) and nothing else
+    sf = shape(dtype=B.MOE_F32, d=256, f=512)
+    Lf = B.moe_layout()
+    nb = B.moe_layout_workspace_bytes(sf)
+    buf2 = np.zeros(nb + 256, np.uint8)
+    base2 = (buf2.ctypes.data + 255) // 256 * 256
+    assert B.lib().moe_layout_bind(ctypes.byref(sf), ctypes.c_void_p(base2), nb, ctypes.byref(Lf)) == 0
+    assert B.moe_ffn_flags_count(sf) == Lf.cap_mtiles * (256 // 64)

@@ -134,6 +134,8 @@ SMALL = [
     mi.Spec("one_owner", R=1, T_o=200, G=1, E_l=1, k=1, d=128, f=128, M=16, seed=13),
     mi.Spec("k_eq_el", R=2, T_o=70, G=6, E_l=3, k=3, d=128, f=192, M=64, seed=14),
     mi.Spec("f32_ragged", R=3, T_o=90, G=9, E_l=3, k=2, d=128, f=192, M=32, dtype="f32", seed=15),
+    # f = 4 d: the second GEMM's output tiles are summed from 4 k-splits (ragged row tiles, two windows)
+    mi.Spec("splitk", R=4, T_o=600, G=8, E_l=2, k=2, d=256, f=1024, M=32, seed=16),
 ]
 
 
@@ -241,6 +243,34 @@ def test_overlap_ordering_stress():
             ref = cur
         for a, b in zip(cur, ref):
             np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["splitk", "mixtral"])
+def test_no_stale_reads_across_calls(name):
+    """Results handed between workgroups inside the FFN launch (h tiles, split-K partial sums, y tiles) are read
+    only once they are complete and visible: a call on new data after a call on old data, with h and y_pad
+    poisoned in between, gives bit for bit what a fresh run on the new data gives."""
+    s = [c for c in SMALL if c.name == name][0] if name != "mixtral" else mi.spec("mixtral")
+    run = Run(s)
+    run.ffn(mode=0)
+    torch.cuda.synchronize()
+    assert run.P.status() == B.MOE_OK
+    neg = -run.dev["x"]  # same routing, different h, partial sums and y everywhere
+    run.P.h.fill_(float("nan"))
+    run.P.y_pad.fill_(float("nan"))
+    run.P.layout(neg)
+    run.ffn(mode=0)
+    fresh = MoePath.from_spec(s)
+    fresh.route(run.dev["logits"])
+    fresh.layout(neg)
+    fresh.ffn(run.dev["w_gate_up"], run.dev["w_down"], mode=1)
+    torch.cuda.synchronize()
+    assert run.P.status() == B.MOE_OK and fresh.status() == B.MOE_OK
+    real = np.nonzero(run.lay["row_src"] >= 0)[0]
+    np.testing.assert_array_equal(bits(run.P.y_pad)[real], bits(fresh.y_pad)[real])
+    for r in range(s.R):
+        n_r = int(run.lay["N_r"][r])
+        np.testing.assert_array_equal(bits(run.P.recv[r])[:n_r], bits(fresh.recv[r])[:n_r])
 
 
 def test_watchdog_ends_a_wait_that_never_ends():
