@@ -50,6 +50,22 @@ def overlap_stats(ts: np.ndarray, n_segs: int, tick_ns: float = 10.0) -> dict:
     }
 
 
+def hbm_traffic(s, cus: int, band_window: int):
+    """HBM bytes per launch of the FFN kernel from the committed counter summary (FETCH_SIZE and WRITE_SIZE, each
+    scaled by the same counter's reading for a plain copy of known size), if it covers this workload and
+    configuration and the kernel sources are the ones it was taken on; else None."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "k_ffn_bf16_mixtral_hbm_bytes.json")
+    if s.name != "mixtral" or s.mgb != 1 or cus != 8 or band_window not in (0, 4) or not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for p in rec["sources"]:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return rec["hbm_bytes_per_launch"] if h.hexdigest() == rec["source_sha256"] else None
+
+
 def cpu_baseline(s, inp, lay_rows, target_s: float):
     """The CPU oracle's FFN rate on a bounded sample of real rows of the same workload (useful TFLOP/s)."""
     import oracle
@@ -215,7 +231,8 @@ def main():
                                 "down projection with split-K, flag publish; consumer workgroups inside)"
                                 if s.dtype == "bf16" else "k_gemm<float> first GEMM"),
                      "achieved": round(roof_flops / (g1_avg * 1e-3) / 1e12, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(roof_flops / (g1_avg * 1e-3) / 1e12 / peak, 4), "traffic": None},
+                     "frac": round(roof_flops / (g1_avg * 1e-3) / 1e12 / peak, 4),
+                     "traffic": hbm_traffic(s, cus, args.band_window), "traffic_unit": "HBM bytes per launch"},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(s, inp, M_real, args.cpu_seconds)
