@@ -92,17 +92,20 @@ typedef struct {
 typedef struct {
   int32_t consumer_cus;    /* C: consumer workgroups, one per CU, in [1, CUs/2]; the producer's persistent
                               launch runs one workgroup on each other CU */
-  int32_t mode;            /* 0 = overlapped (the C consumer workgroups and the producers of the second GEMM in
-                                  one launch, on disjoint CUs),
+  int32_t mode;            /* 0 = overlapped (the C consumer workgroups and the producer workgroups in one
+                                  launch, on disjoint CUs),
                               1 = sequential (producer on all CUs, then the consumer),
                               2 = return only (the consumer alone, on consumer_cus workgroups, for flags
                                   already published with this epoch; a flag never published ends in the
                                   watchdog) */
   uint32_t epoch;          /* flag value of this call: nonzero and different from what the flag array holds
                               (flags start zeroed; pass 1, 2, 3, ...) */
-  int32_t band_window;     /* GEMM row tiles per weight-reuse window (0 = library default) */
-  uint64_t watchdog_ticks; /* consumer spin budget in 100 MHz ticks (0 = 2 s); on expiry the status word
-                              becomes MOE_ETIMEOUT and the consumer exits */
+  int32_t band_window;     /* GEMM row tiles per window of the producer's item list (0 = library default, 4):
+                              the items of a window share weight tiles, and a window's second-GEMM items
+                              follow the next window's first-GEMM items */
+  uint64_t watchdog_ticks; /* spin budget of every wait in the launch (consumer and producer), 100 MHz ticks
+                              (0 = 2 s); on expiry the status word becomes MOE_ETIMEOUT and the waiting
+                              workgroup exits */
   uint64_t* timestamps;    /* optional (device) [2 + 2*cap_tiles] u64, 100 MHz clock: [0] first producer
                               item start, [1] last flag publish, [2+2s] / [3+2s] first copy start / last copy
                               end of segment s over the consumer workgroups; reset by the call; NULL to
@@ -149,23 +152,31 @@ int moe_read_status(const moe_layout* L, void* stream);
 
 /* ---- expert FFN + return ------------------------------------------------------------------------- */
 
-/* Number of uint32 readiness flags moe_expert_ffn_overlap needs (one per output tile of the second GEMM);
- * -1 if the shape is invalid. */
+/* Size, in 4-byte words, of the flag buffer moe_expert_ffn_overlap needs; -1 if the shape is invalid.  It
+ * holds the readiness flags of the second GEMM's output tiles (what the consumer waits on), and for bf16 the
+ * flags of the first GEMM's h tiles and of the second GEMM's k-splits, followed by the fp32 partial sums of
+ * those splits (256 x 256 floats per output tile and split after the first; f/d rounded gives the number of
+ * splits, up to 8).  Zero the buffer once before the first call; afterwards it is epoch-valued. */
 int64_t moe_ffn_flags_count(const moe_shape* s);
 
 /* Expert SwiGLU FFN over the padded layout with the return of each finished row-band segment to its
  * owner (review page: "The pith", "Core claim", "What carries the argument").
  *   h = bf16(silu(x Wg^T) * (x Wu^T)),  y = h Wd^T, per row with the row's local expert;
  *   Wg = rows [0, f) and Wu = rows [f, 2f) of w_gate_up[e].
- * The producer (a persistent grouped GEMM over all local experts, remote-first order) stores y tiles and
- * publishes flags[tile] = epoch with an agent-scope release; the consumer acquires the flags of a segment
- * and copies its real rows into recv[owner].  Launches: the first GEMM on every CU, then one launch whose
- * first C workgroups are the consumer and whose others run the second GEMM (overlapped mode).  Owner r receives, at row recv_off_{e,r} + i, the FFN output
- * of the i-th row of group (e, r).
+ * The producer is one persistent launch over all local experts (bf16): tiles of h, then k-splits of y tiles,
+ * window by window in remote-first row-tile order; a tile other workgroups read is published with an
+ * epoch-valued flag once its stores are complete and visible device-wide.  The consumer waits for the flags
+ * of a segment's row tiles, acquires, and copies the segment's real rows into recv[owner].
+ *   mode 0 (overlapped): the consumer is the first consumer_cus workgroups of the producer launch;
+ *   mode 1 (sequential): producer on every CU, then the consumer alone;
+ *   mode 2: the consumer alone (return only; for tests of the wait).
+ * fp32 runs the two GEMMs as two launches (consumer inside the second).  Owner r receives, at row
+ * recv_off_{e,r} + i, the FFN output of the i-th row of group (e, r); results are identical in every mode.
  * x_pad (device) [cap_rows, d]; w_gate_up (device) [E_l, 2f, d]; w_down (device) [E_l, d, f];
  * h_ws (device) [cap_rows, f] workspace; y_pad (device) [cap_rows, d]; recv: host array of R device
- * pointers, recv[r] holds >= N_r rows of d; flags (device) uint32 [moe_ffn_flags_count] (zeroed before the
- * first call); cfg: see moe_overlap_cfg. */
+ * pointers, recv[r] holds >= N_r rows of d; flags (device) [moe_ffn_flags_count] 4-byte words (zeroed before
+ * the first call); cfg: see moe_overlap_cfg.  Waits inside the launch are bounded by cfg->watchdog_ticks;
+ * on expiry the status word becomes MOE_ETIMEOUT. */
 int moe_expert_ffn_overlap(const moe_shape* s, const moe_layout* L, const void* x_pad, const void* w_gate_up,
                            const void* w_down, void* h_ws, void* y_pad, void* const* recv, uint32_t* flags,
                            const moe_overlap_cfg* cfg, void* stream);
@@ -187,9 +198,10 @@ int moe_combine(const moe_shape* s, const moe_layout* L, const float* topk_w, vo
 int moe_set_kernel_timing(int enable);
 
 /* Waits for the recorded events and writes the summed milliseconds since the last query:
- * out[0] first GEMM (gate/up + SwiGLU), out[1] second GEMM launch (down projection + flag publish, with the
- * consumer workgroups in overlapped mode), out[2] the separate consumer launch of sequential mode (0 in
- * overlapped mode), out[3] number of calls recorded.  Clears the record. */
+ * out[0] the producer launch (bf16: the whole FFN, with the consumer workgroups in overlapped mode; fp32: the
+ * first GEMM), out[1] the second launch (fp32: the second GEMM with the consumer workgroups; bf16: 0),
+ * out[2] the separate consumer launch of sequential mode (0 in overlapped mode), out[3] number of calls
+ * recorded.  Clears the record. */
 int moe_kernel_times(double* out4);
 
 #ifdef __cplusplus
