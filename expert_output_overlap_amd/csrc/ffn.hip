@@ -289,18 +289,17 @@ __device__ __forceinline__ float silu_fast(float g) { return g * __builtin_amdgc
 
 // The expert FFN as one persistent launch.  Work items:
 //   GEMM1 item (row tile mt, column tile nt): h[rows, nt*BN1/2 ...] = bf16(silu(x Wg^T) * (x Wu^T)), then
-//     flags1[mt][nt] = epoch (release);
+//     flags1[mt][nt] = epoch;
 //   GEMM2 item (mt, nt, split s): the k-tiles of split s of y[rows, nt*BN2 ...] = h Wd^T, after acquiring the
 //     flags1 of the h columns that split reads.  With S > 1 splits, splits s < S-1 store fp32 partial sums and
-//     release sflags; split S-1 acquires them, adds them in split order (sum of splits 0..S-2, then its own),
-//     and stores the bf16 y tile and releases flags2[mt][nt], which the consumer waits on.
-// Items are listed window by window (band_window row tiles, remote-first order): GEMM1 of window 0, then
-// GEMM1 of window w+1 before GEMM2 of window w, so each GEMM2 item's inputs are finished well before it starts,
-// and row tiles complete (and are returned) one window after another instead of all at the end.  Producer
-// workgroup b takes items b, b + G, ... (XCD-aware: a run of consecutive items goes to the workgroups of one
-// XCD, which share the operands in their L2).  Every wait is on an item earlier in the list, so the lowest
-// unfinished item can always run: the waits end while every workgroup is resident, and a spin budget bounds
-// them otherwise.
+//     publish sflags; split S-1 acquires them, adds them in split order (sum of splits 0..S-2, then its own),
+//     stores the bf16 y tile and publishes flags2[mt][nt], which the consumer waits on.
+// Items are listed as all GEMM1 items, then the GEMM2 items window by window (band_window row tiles,
+// remote-first order), so row tiles complete (and are returned) one window after another during the second
+// part of the launch.  Producer workgroup b takes items b, b + G, ... (XCD-aware: a run of consecutive items
+// goes to the workgroups of one XCD, which share the operands in their L2).  Every wait is on an item earlier in
+// the list, so the lowest unfinished item can always run: the waits end while every workgroup is resident, and
+// a spin budget bounds them otherwise.
 
 struct FusedArgs {
   const unsigned char* x;   // x_pad [cap_rows, d]
@@ -330,45 +329,40 @@ struct FfnItem {
   int mt, nt, s;
 };
 
-// Item i of the list G1(0), G1(1), G2(0), G1(2), G2(1), ..., G1(nw-1), G2(nw-2), G2(nw-1) over nw windows of
-// W row tiles (the last one Wl <= W); inside a window, GEMM1 items are column-tile major (consecutive items share
-// a column tile of weights) and GEMM2 items split-major, then column-tile major.
+// Item i of the list: all GEMM1 items, column-tile major over every row tile (each gate/up weight tile is
+// streamed once, by consecutive items), then the GEMM2 items in windows of W row tiles (remote-first order),
+// split-major and column-tile major inside a window.  A GEMM2 split reads only its own share of h's columns,
+// which the first part of the GEMM1 list produced, so the splits find their inputs finished; the last split of
+// a tile follows its other splits; and the row tiles of a window complete together, window after window, while
+// the later windows are still computed, so the return of the early windows overlaps them.
 __device__ __forceinline__ FfnItem ffn_item(int i, int n_mt, int W, int n1, int n2, int S) {
-  const int n2S = n2 * S;
-  const int nw = (n_mt + W - 1) / W;
-  const int Wl = n_mt - (nw - 1) * W;
-  auto g1 = [&](int w, int j, int Wc) {
-    FfnItem it;
+  FfnItem it;
+  if (i < n_mt * n1) {
     it.kind = 1;
-    it.nt = j / Wc;
-    it.mt = w * W + (j - it.nt * Wc);
+    it.nt = i / n_mt;
+    it.mt = i - it.nt * n_mt;
     it.s = 0;
     return it;
-  };
-  auto g2 = [&](int w, int j, int Wc) {
-    FfnItem it;
-    it.kind = 2;
-    const int per = Wc * n2;
-    it.s = j / per;
-    const int r = j - it.s * per;
-    it.nt = r / Wc;
-    it.mt = w * W + (r - it.nt * Wc);
-    return it;
-  };
-  const int W0 = nw == 1 ? Wl : W;
-  if (i < W0 * n1) return g1(0, i, W0);
-  i -= W0 * n1;
-  if (nw == 1) return g2(0, i, Wl);
-  const int pz = W * (n1 + n2S);  // a pair (G1(p), G2(p-1)) of two full windows, p = 1 .. nw-2
-  if (i < (nw - 2) * pz) {
-    const int p = 1 + i / pz, j = i - (p - 1) * pz;
-    return j < W * n1 ? g1(p, j, W) : g2(p - 1, j - W * n1, W);
   }
-  i -= (nw - 2) * pz;
-  if (i < Wl * n1) return g1(nw - 1, i, Wl);
-  i -= Wl * n1;
-  if (i < W * n2S) return g2(nw - 2, i, W);
-  return g2(nw - 1, i - W * n2S, Wl);
+  int j = i - n_mt * n1;
+  const int per = n2 * S;        // GEMM2 items per row tile
+  const int full = n_mt / W;     // windows of W row tiles, then one of n_mt % W
+  int w, Wc;
+  if (j < full * W * per) {
+    w = j / (W * per);
+    j -= w * W * per;
+    Wc = W;
+  } else {
+    w = full;
+    j -= full * W * per;
+    Wc = n_mt - full * W;
+  }
+  it.kind = 2;
+  it.s = j / (Wc * n2);
+  const int r = j - it.s * Wc * n2;
+  it.nt = r / Wc;
+  it.mt = w * W + (r - it.nt * Wc);
+  return it;
 }
 
 // All threads of the workgroup: wait until the n flags equal epoch, then acquire.  False if the spin budget ran
@@ -671,12 +665,16 @@ __global__ __launch_bounds__(256, 1) void k_ffn_bf16(FusedArgs a) {
   const int n_items = n_mt * (a.n_nt1 + a.n_nt2 * a.S);
   const int tid = threadIdx.x;
   const int G = gridDim.x - a.n_cons;
+  // workgroup b takes items b', b' + G, ..., b' remapped so that a run of consecutive items goes to the
+  // workgroups of one XCD (workgroup b sits on XCD b % 8), which share operand tiles in its L2; all workgroups
+  // move through the list in step.  (Claiming items from a counter instead balances the end better but loses
+  // that locality, and the clock drops with the extra off-XCD traffic: measured slower.)
   int bid = blockIdx.x - a.n_cons;
   if ((G & 7) == 0 && (a.n_cons & 7) == 0) bid = (bid & 7) * (G >> 3) + (bid >> 3);
   bool first = true;
   for (int item = bid; item < n_items; item += G) {
-    const FfnItem it = ffn_item(item, n_mt, a.window, a.n_nt1, a.n_nt2, a.S);
     __syncthreads();  // previous item done with LDS and the header
+    const FfnItem it = ffn_item(item, n_mt, a.window, a.n_nt1, a.n_nt2, a.S);
     if (tid < MOE_MT_FIELDS) {
       const int v = a.mtile_desc[(int64_t)it.mt * MOE_MT_FIELDS + tid];
       if (tid < 2) s_hdr[tid] = v;
