@@ -291,9 +291,9 @@ __device__ __forceinline__ float silu_fast(float g) { return g * __builtin_amdgc
 //   GEMM1 item (row tile mt, column tile nt): h[rows, nt*BN1/2 ...] = bf16(silu(x Wg^T) * (x Wu^T)), then
 //     flags1[mt][nt] = epoch;
 //   GEMM2 item (mt, nt, split s): the k-tiles of split s of y[rows, nt*BN2 ...] = h Wd^T, after acquiring the
-//     flags1 of the h columns that split reads.  With S > 1 splits, splits s < S-1 store fp32 partial sums and
-//     publish sflags; split S-1 acquires them, adds them in split order (sum of splits 0..S-2, then its own),
-//     stores the bf16 y tile and publishes flags2[mt][nt], which the consumer waits on.
+//     flags1 of the h columns that split reads.  With S > 1 splits, each split stores fp32 partial sums and
+//     counts itself in; the last to arrive adds the partial sums in split order, stores the bf16 y tile and
+//     publishes flags2[mt][nt], which the consumer waits on.
 // Items are listed as all GEMM1 items, then the GEMM2 items window by window (band_window row tiles,
 // remote-first order), so row tiles complete (and are returned) one window after another during the second
 // part of the launch.  Producer workgroup b takes items b, b + G, ... (XCD-aware: a run of consecutive items
@@ -315,8 +315,8 @@ struct FusedArgs {
   int32_t* status;
   uint32_t* flags2;  // [cap_mtiles][n_nt2]: y tile published (the consumer's flags)
   uint32_t* flags1;  // [cap_mtiles][n_nt1]: h tile finished
-  uint32_t* sflags;  // [cap_mtiles][n_nt2][S-1]: partial sums of a split stored
-  float* partial;    // [cap_mtiles][n_nt2][S-1][256 * BN2]
+  uint64_t* scount;  // [cap_mtiles][n_nt2]: splits of a y tile that have stored their partial sums
+  float* partial;    // [cap_mtiles][n_nt2][S][256 * BN2]
   uint32_t epoch;
   uint64_t budget;
   uint64_t* ts;
@@ -401,6 +401,19 @@ __device__ __forceinline__ void store16_coherent(void* p, u32x4_t v) {
 __device__ __forceinline__ void publish(uint32_t* flag, uint32_t epoch) {
   __syncthreads();  // waits for this wave's stores (vmcnt(0)), then for every wave's
   if (threadIdx.x == 0) __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Arrival count of this call at a counter that holds (epoch << 32) | count: returns how many arrived before.  A
+// counter that still carries another call's epoch counts from zero, so no reset between calls is needed.
+__device__ __forceinline__ uint32_t arrive(uint64_t* ctr, uint32_t epoch) {
+  uint64_t old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (;;) {
+    const bool cur = (uint32_t)(old >> 32) == epoch;
+    const uint64_t nw = cur ? old + 1 : (((uint64_t)epoch << 32) | 1u);
+    if (__hip_atomic_compare_exchange_strong(ctr, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      return cur ? (uint32_t)old : 0u;
+  }
 }
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -563,27 +576,29 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
   if (mact == MI) kloop(std::true_type{});
   else kloop(std::false_type{});
   if (!GLU && a.S > 1) {
-    // split-K: thread tid keeps its accumulators at float4 chunk ((mi * NI + ni) * 4 + q4) * 256 + tid of a slot
+    // split-K: every split stores its fp32 partial sums (thread tid keeps its accumulators at float4 chunk
+    // ((mi * NI + ni) * 4 + q4) * 256 + tid of its slot), waits for the stores to complete, and counts itself in;
+    // the split that arrives last adds the slots in split order, its own from registers: y = ((p_0 + p_1) + ...)
+    // + p_{S-1}, the same association whichever split is last, so the result is the same on every call.
     const int64_t tile = (int64_t)mt * a.n_nt2 + nt;
-    f32x4_t* slots = (f32x4_t*)(a.partial + tile * (a.S - 1) * (BM * BN));
+    f32x4_t* slots = (f32x4_t*)(a.partial + tile * a.S * (BM * BN));
     constexpr int SLOT4 = BM * BN / 4;
-    if (s < a.S - 1) {
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          f32x4_t* dst = slots + (int64_t)s * SLOT4 + (mi * NI + ni) * 4 * 256 + tid;
-          const f32x16_t v = acc[mi][ni];
-          store16_coherent(dst, __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v, v, 0, 1, 2, 3)));
-          store16_coherent(dst + 256, __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v, v, 4, 5, 6, 7)));
-          store16_coherent(dst + 512, __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v, v, 8, 9, 10, 11)));
-          store16_coherent(dst + 768, __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v, v, 12, 13, 14, 15)));
-        }
-      publish(&a.sflags[tile * (a.S - 1) + s], a.epoch);
-      return true;
-    }
-    if (!wait_flags(a.sflags + tile * (a.S - 1), a.S - 1, a.epoch, a.budget, a.status, s_stop)) return false;
-    // y = (p_0 + p_1 + ... + p_{S-2}) + own, the same association on every call; one 32 x 32 block at a time
+      for (int ni = 0; ni < NI; ++ni) {
+        f32x4_t* dst = slots + (int64_t)s * SLOT4 + (mi * NI + ni) * 4 * 256 + tid;
+        const f32x16_t v = acc[mi][ni];
+        store16_coherent(dst, __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v, v, 0, 1, 2, 3)));
+        store16_coherent(dst + 256, __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v, v, 4, 5, 6, 7)));
+        store16_coherent(dst + 512, __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v, v, 8, 9, 10, 11)));
+        store16_coherent(dst + 768, __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v, v, 12, 13, 14, 15)));
+      }
+    __syncthreads();  // every thread's partial stores completed (vmcnt(0))
+    if (tid == 0) *s_stop = (int)arrive(&a.scount[tile], a.epoch);
+    __syncthreads();
+    if (*s_stop != a.S - 1) return true;  // not the last split of this tile
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     auto ld16 = [&](const f32x4_t* src) {
       const f32x4_t q0 = __builtin_nontemporal_load(src), q1 = __builtin_nontemporal_load(src + 256);
       const f32x4_t q2 = __builtin_nontemporal_load(src + 512), q3 = __builtin_nontemporal_load(src + 768);
@@ -596,9 +611,9 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
         const f32x4_t* src = slots + (mi * NI + ni) * 4 * 256 + tid;
-        f32x16_t t = ld16(src);
-        for (int sp = 1; sp < a.S - 1; ++sp) t += ld16(src + (int64_t)sp * SLOT4);
-        acc[mi][ni] = t + acc[mi][ni];
+        f32x16_t t = s == 0 ? acc[mi][ni] : ld16(src);
+        for (int sp = 1; sp < a.S; ++sp) t += sp == s ? acc[mi][ni] : ld16(src + (int64_t)sp * SLOT4);
+        acc[mi][ni] = t;
       }
   }
 
@@ -730,22 +745,22 @@ int ffn_splits(int dtype, int d, int f) {
 
 namespace {
 struct FlagCarve {
-  int64_t flags2, flags1, sflags, partial, total;  // offsets and size in 4-byte words
+  int64_t flags2, flags1, scount, partial, total;  // offsets and size in 4-byte words
 };
 FlagCarve flag_carve(int dtype, int d, int f, int64_t cap_mtiles) {
   FlagCarve c;
   const int64_t n2 = d / ffn_gemm2_bn(dtype, d);
   c.flags2 = 0;
   if (dtype != MOE_BF16) {
-    c.flags1 = c.sflags = c.partial = c.total = cap_mtiles * n2;
+    c.flags1 = c.scount = c.partial = c.total = cap_mtiles * n2;
     return c;
   }
   const int64_t n1 = f / (gemm1_bn(dtype, f) / 2), S = ffn_splits(dtype, d, f);
   auto up = [](int64_t v) { return (v + 63) / 64 * 64; };
   c.flags1 = up(cap_mtiles * n2);
-  c.sflags = c.flags1 + up(cap_mtiles * n1);
-  c.partial = c.sflags + up(cap_mtiles * n2 * (S - 1));
-  c.total = c.partial + cap_mtiles * n2 * (S - 1) * (int64_t)BF_BM * ffn_gemm2_bn(dtype, d);
+  c.scount = c.flags1 + up(cap_mtiles * n1);
+  c.partial = c.scount + up(S > 1 ? 2 * cap_mtiles * n2 : 0);
+  c.total = c.partial + (S > 1 ? cap_mtiles * n2 * S * (int64_t)BF_BM * ffn_gemm2_bn(dtype, d) : 0);
   return c;
 }
 
@@ -800,7 +815,7 @@ int launch_bf16(const FfnLaunch& p, int grid, int n_cons, hipStream_t st) {
   a.status = p.L->status;
   a.flags2 = p.flags + fc.flags2;
   a.flags1 = p.flags + fc.flags1;
-  a.sflags = p.flags + fc.sflags;
+  a.scount = (uint64_t*)(p.flags + fc.scount);
   a.partial = (float*)(p.flags + fc.partial);
   a.epoch = p.epoch;
   a.budget = p.watchdog_ticks;

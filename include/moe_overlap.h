@@ -154,9 +154,9 @@ int moe_read_status(const moe_layout* L, void* stream);
 
 /* Size, in 4-byte words, of the flag buffer moe_expert_ffn_overlap needs; -1 if the shape is invalid.  It
  * holds the readiness flags of the second GEMM's output tiles (what the consumer waits on), and for bf16 the
- * flags of the first GEMM's h tiles and of the second GEMM's k-splits, followed by the fp32 partial sums of
- * those splits (256 x 256 floats per output tile and split after the first; f/d rounded gives the number of
- * splits, up to 8).  Zero the buffer once before the first call; afterwards it is epoch-valued. */
+ * flags of the first GEMM's h tiles, an arrival counter per output tile of the second GEMM and the fp32 partial
+ * sums of its k-splits (256 x 256 floats per output tile and split; f/d rounded gives the number of splits, up
+ * to 8).  Zero the buffer once before the first call; afterwards it is epoch-valued. */
 int64_t moe_ffn_flags_count(const moe_shape* s);
 
 /* Expert SwiGLU FFN over the padded layout with the return of each finished row-band segment to its

@@ -99,9 +99,9 @@ def test_flag_count_covers_row_tiles():
     nflags = B.moe_ffn_flags_count(s)
     n_nt2 = s.d // 256  # 256-wide output tiles of the second GEMM
     assert nflags >= L.cap_mtiles * n_nt2
-    # f = 3.5 d: the second GEMM's tiles are split 4 ways over k, and three fp32 partial 256 x 256 tiles per
-    # output tile live in the same buffer
-    assert nflags >= L.cap_mtiles * n_nt2 * (1 + 3 * 256 * 256)
+    # f = 3.5 d: the second GEMM's tiles are split 4 ways over k, and the four splits' fp32 partial 256 x 256
+    # tiles per output tile live in the same buffer
+    assert nflags >= L.cap_mtiles * n_nt2 * (1 + 4 * 256 * 256)
     # an fp32 shape has one flag per output tile of the second GEMM (64 wide) and nothing else
     sf = shape(dtype=B.MOE_F32, d=256, f=512)
     Lf = B.moe_layout()
