@@ -1,7 +1,7 @@
 // Top-k weighted combine at the owners (review page ledger, axiom 3: the router output, hence the combine
 // plan, is known before the return): out[r*T_o+t] = sum_j w[t,j] * recv[r][plan[t,j]] over the slots with a
 // local expert, fp32 accumulation in ascending j, rounded once to the element type.
-// One wavefront per token, 16-byte lanes along the hidden dimension.
+// One wavefront per token, 16-byte lanes along the hidden dimension, four 16-byte chunks per lane in flight.
 #include "common.h"
 #include "launch.h"
 
@@ -37,39 +37,56 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   }
   const uint4* src = (const uint4*)a.recv.p[r];
   uint4* dst = (uint4*)a.out + (int64_t)tok * a.row_vec;
-  for (int c = lane; c < a.row_vec; c += MOE_WAVE) {
-    float acc[VEC];
+  // U chunks of the row per lane at a time, all their loads issued before any is used
+  constexpr int U = 4;
+  for (int c0 = lane; c0 < a.row_vec; c0 += U * MOE_WAVE) {
+    float acc[U][VEC];
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[u][i] = 0.f;
     for (int j = 0; j < nloc; ++j) {
-      const uint4 v = src[(int64_t)p[j] * a.row_vec + c];
-      if (sizeof(T) == 2) {
-        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+      uint4 v[U];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] += w[j] * bf16_to_f32((bf16_t)(u[i] & 0xffffu));
-          acc[2 * i + 1] += w[j] * bf16_to_f32((bf16_t)(u[i] >> 16));
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * MOE_WAVE;
+        v[u] = c < a.row_vec ? src[(int64_t)p[j] * a.row_vec + c] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (sizeof(T) == 2) {
+          const uint32_t q[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[u][2 * i] += w[j] * bf16_to_f32((bf16_t)(q[i] & 0xffffu));
+            acc[u][2 * i + 1] += w[j] * bf16_to_f32((bf16_t)(q[i] >> 16));
+          }
+        } else {
+          acc[u][0] += w[j] * __uint_as_float(v[u].x);
+          acc[u][1] += w[j] * __uint_as_float(v[u].y);
+          acc[u][2] += w[j] * __uint_as_float(v[u].z);
+          acc[u][3] += w[j] * __uint_as_float(v[u].w);
         }
-      } else {
-        acc[0] += w[j] * __uint_as_float(v.x);
-        acc[1] += w[j] * __uint_as_float(v.y);
-        acc[2] += w[j] * __uint_as_float(v.z);
-        acc[3] += w[j] * __uint_as_float(v.w);
       }
     }
-    uint4 o;
-    if (sizeof(T) == 2) {
-      o.x = pack_bf16x2(acc[0], acc[1]);
-      o.y = pack_bf16x2(acc[2], acc[3]);
-      o.z = pack_bf16x2(acc[4], acc[5]);
-      o.w = pack_bf16x2(acc[6], acc[7]);
-    } else {
-      o.x = __float_as_uint(acc[0]);
-      o.y = __float_as_uint(acc[1]);
-      o.z = __float_as_uint(acc[2]);
-      o.w = __float_as_uint(acc[3]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * MOE_WAVE;
+      if (c >= a.row_vec) break;
+      uint4 o;
+      if (sizeof(T) == 2) {
+        o.x = pack_bf16x2(acc[u][0], acc[u][1]);
+        o.y = pack_bf16x2(acc[u][2], acc[u][3]);
+        o.z = pack_bf16x2(acc[u][4], acc[u][5]);
+        o.w = pack_bf16x2(acc[u][6], acc[u][7]);
+      } else {
+        o.x = __float_as_uint(acc[u][0]);
+        o.y = __float_as_uint(acc[u][1]);
+        o.z = __float_as_uint(acc[u][2]);
+        o.w = __float_as_uint(acc[u][3]);
+      }
+      dst[c] = o;
     }
-    dst[c] = o;
   }
 }
 

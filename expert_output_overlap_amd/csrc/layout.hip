@@ -12,6 +12,7 @@
 
 #define SCAN_THREADS 1024
 #define MAX_GROUPS (MOE_MAX_OWNERS * MOE_MAX_LOCAL_EXPERTS)
+#define SCAN_KEYS 4096  // segments whose consumer-order keys are staged in LDS
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int l = lane_id();
@@ -19,8 +20,7 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 }
 
 __global__ __launch_bounds__(256) void k_layout_count(const int32_t* __restrict__ topk_idx, int T_o, int G, int k,
-                                                      int lo, int E, int n_chunks, int32_t* __restrict__ chunk_counts,
-                                                      int32_t* __restrict__ status) {
+                                                      int lo, int E, int n_chunks, int32_t* __restrict__ chunk_counts) {
   const int wave = threadIdx.x / MOE_WAVE, lane = lane_id();
   const int r = blockIdx.y;
   const int c = blockIdx.x * 4 + wave;
@@ -40,13 +40,14 @@ __global__ __launch_bounds__(256) void k_layout_count(const int32_t* __restrict_
       }
     }
   }
-  if (bad) set_status(status, MOE_EINVAL);
+  // a chunk with an invalid token records -1 counts; the scan turns that into MOE_EINVAL
+  const bool chunk_bad = __ballot(bad) != 0ull;
   int mine = 0;
   for (int e = 0; e < E; ++e) {
     const int cnt = __popcll(__ballot((mask >> e) & 1ull));
     if (lane == e) mine = cnt;
   }
-  if (lane < E) chunk_counts[((int64_t)r * n_chunks + c) * E + lane] = mine;
+  if (lane < E) chunk_counts[((int64_t)r * n_chunks + c) * E + lane] = chunk_bad ? -1 : mine;
 }
 
 // Exclusive scan of one value per thread over a 1024-thread block; *total gets the sum.
@@ -86,25 +87,39 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
   __shared__ int s_tile_base[MAX_GROUPS], s_run_off[MAX_GROUPS], s_run_subs[MAX_GROUPS];  // by q2
   __shared__ int s_wsum[SCAN_THREADS / MOE_WAVE + 1];
   __shared__ int s_misc[4];
+  // scratch reused by steps that never overlap: 64-bit sort keys of the groups (e), run tables (g), segment
+  // keys (i)
+  __shared__ uint64_t s_scratch[SCAN_KEYS / 2];
 
   const int tid = threadIdx.x;
   const int R = a.R, E = a.E, M = a.M, NG = E * R;
-  const int32_t status0 = load_status(a.status);
 
-  // (a) group sizes; per-(owner, expert) chunk counts become exclusive prefixes in place
+  // (a) group sizes; per-(owner, expert) chunk counts become exclusive prefixes in place (loads in batches of 8
+  // independent ones); a chunk that saw an invalid token holds -1 counts
+  int bad = 0;
   for (int g = tid; g < NG; g += SCAN_THREADS) {
     const int e = g / R, r = g % R;
+    int32_t* base = a.chunk_counts + (int64_t)r * a.n_chunks * E + e;
     int run = 0;
-    for (int c = 0; c < a.n_chunks; ++c) {
-      int32_t* p = a.chunk_counts + ((int64_t)r * a.n_chunks + c) * E + e;
-      const int v = *p;
-      *p = run;
-      run += v;
+    for (int c0 = 0; c0 < a.n_chunks; c0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = c0 + u < a.n_chunks ? base[(int64_t)(c0 + u) * E] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (c0 + u < a.n_chunks) {
+          base[(int64_t)(c0 + u) * E] = run;
+          bad |= v[u] < 0;
+          run += v[u];
+        }
     }
     s_n[g] = run;
     a.counts[g] = run;
   }
-  __syncthreads();
+  // the layout build sets the status word: MOE_EINVAL for an invalid token, then MOE_ECAPACITY, else MOE_OK
+  const int any_bad = __syncthreads_or(bad);
+  const int32_t status0 = any_bad ? MOE_EINVAL : MOE_OK;
+  if (tid == 0) *a.status = status0;
 
   // (b) padded offsets: exclusive scan of P = ceil(n/M)*M in (e, r) order
   int total = 0;
@@ -140,44 +155,44 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
   }
   __syncthreads();
 
-  // (d) band tables and padding entries of row_src
+  // (d) band tables; every padded row of row_src starts as padding (-1), the scatter then writes the real rows
+  for (int p = tid; p < M_pad; p += SCAN_THREADS) a.row_src[p] = -1;
   for (int g = tid; g < NG; g += SCAN_THREADS) {
-    const int n = s_n[g], off = s_poff[g];
-    for (int row = 0; row < n; row += M) {
-      const int b = (off + row) / M;
-      a.tile_owner[b] = g % R;
-      a.tile_expert[b] = g / R;
-      const int valid = (n - row) < M ? (n - row) : M;
-      a.tile_valid[b] = valid;
-      for (int i = valid; i < M; ++i) a.row_src[(int64_t)b * M + i] = -1;
+    const int n = s_n[g], off = s_poff[g], e = g / R, r = g - e * R;
+    for (int row = 0, b = off / M; row < n; row += M, ++b) {
+      a.tile_owner[b] = r;
+      a.tile_expert[b] = e;
+      a.tile_valid[b] = (n - row) < M ? (n - row) : M;
     }
   }
 
   // (e) remote-first order of non-empty groups: key (owner == self, -P, e, r) ascending (bands, segments);
   // row-tile packing order: key (owner == self, e, -P, r), remote groups first and each expert's groups together
-  // so that a GEMM row tile (one expert) packs as many sub-blocks as possible
+  // so that a GEMM row tile (one expert) packs as many sub-blocks as possible.  Both keys are packed into one
+  // unsigned 64-bit value per group (unique, since (e, r) is), so a group's rank is the count of smaller keys.
   {
-    int rank = 0, rank2 = 0;
+    uint64_t* key1 = s_scratch;
+    uint64_t* key2 = s_scratch + MAX_GROUPS;
     const bool mine = tid < NG && s_n[tid] > 0;
+    const uint64_t none = ~0ull;
+    uint64_t k1 = none, k2 = none;
     if (mine) {
-      const int g = tid, e = g / R, r = g % R;
-      const int self = (r == a.self_rank), P = ((s_n[g] + M - 1) / M) * M;
+      const int g = tid, e = g / R, r = g - e * R;
+      const uint64_t self = r == a.self_rank, nP = (uint64_t)((1 << 30) - ((s_n[g] + M - 1) / M) * M);
+      k1 = (self << 63) | (nP << 32) | ((uint64_t)e << 16) | (uint64_t)r;
+      k2 = (self << 63) | ((uint64_t)e << 50) | (nP << 16) | (uint64_t)r;
+    }
+    if (tid < NG) {
+      key1[tid] = k1;
+      key2[tid] = k2;
+    }
+    __syncthreads();
+    int rank = 0, rank2 = 0;
+    if (mine) {
+#pragma unroll 8
       for (int h = 0; h < NG; ++h) {
-        const int nh = s_n[h];
-        if (nh == 0 || h == g) continue;
-        const int eh = h / R, rh = h % R;
-        const int selfh = (rh == a.self_rank), Ph = ((nh + M - 1) / M) * M;
-        bool less, less2;
-        if (selfh != self) less = selfh < self;
-        else if (Ph != P) less = Ph > P;
-        else if (eh != e) less = eh < e;
-        else less = rh < r;
-        if (selfh != self) less2 = selfh < self;
-        else if (eh != e) less2 = eh < e;
-        else if (Ph != P) less2 = Ph > P;
-        else less2 = rh < r;
-        rank += less;
-        rank2 += less2;
+        rank += key1[h] < k1;
+        rank2 += key2[h] < k2;
       }
     }
     int n_ne = 0;
@@ -220,25 +235,42 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
   const int n_segs = s_misc[1];
 
   // (g) GEMM row tiles: runs of consecutive same-expert groups in packing order, each cut into tiles of
-  // mt_sub sub-blocks; sequential over at most 1024 groups
-  if (tid == 0) {
-    int tile_base = 0, q0 = 0;
-    while (q0 < n_ne) {
-      const int e = s_order2[q0] / R;
-      int q1 = q0;
-      while (q1 < n_ne && s_order2[q1] / R == e) ++q1;
-      const int run_subs = (q1 < n_ne ? s_sub_pos[q1] : s_misc[2]) - s_sub_pos[q0];
-      for (int q = q0; q < q1; ++q) {
-        s_tile_base[q] = tile_base;
-        s_run_off[q] = s_sub_pos[q] - s_sub_pos[q0];
-        s_run_subs[q] = run_subs;
-      }
-      tile_base += (run_subs + a.mt_sub - 1) / a.mt_sub;
-      q0 = q1;
+  // mt_sub sub-blocks (run starts, then two block scans: runs' tile counts, positions inside a run)
+  {
+    int* s_e2 = (int*)s_scratch;               // expert of packing position q
+    int* s_first = s_e2 + MAX_GROUPS;          // first packing position of run j
+    int* s_tbase = s_first + MAX_GROUPS;       // first row tile of run j
+    int* s_rsubs = s_tbase + MAX_GROUPS;       // sub-blocks of run j
+    const int q = tid;
+    const bool in = q < n_ne;
+    if (in) s_e2[q] = s_order2[q] / R;
+    __syncthreads();
+    const int start = in && (q == 0 || s_e2[q - 1] != s_e2[q]);
+    int n_runs = 0;
+    const int run = block_excl_scan(start, s_wsum, &n_runs) + start - 1;  // run of q
+    if (start) s_first[run] = q;
+    __syncthreads();
+    int tiles = 0, rsubs = 0;
+    if (tid < n_runs) {
+      const int q0 = s_first[tid], q1 = tid + 1 < n_runs ? s_first[tid + 1] : n_ne;
+      rsubs = (q1 < n_ne ? s_sub_pos[q1] : s_misc[2]) - s_sub_pos[q0];
+      tiles = (rsubs + a.mt_sub - 1) / a.mt_sub;
     }
-    s_misc[3] = tile_base;
+    int n_mt = 0;
+    const int tb = block_excl_scan(tiles, s_wsum, &n_mt);
+    if (tid < n_runs) {
+      s_tbase[tid] = tb;
+      s_rsubs[tid] = rsubs;
+    }
+    __syncthreads();
+    if (in) {
+      s_tile_base[q] = s_tbase[run];
+      s_run_off[q] = s_sub_pos[q] - s_sub_pos[s_first[run]];
+      s_run_subs[q] = s_rsubs[run];
+    }
+    if (tid == 0) s_misc[3] = n_mt;
+    __syncthreads();
   }
-  __syncthreads();
   const int n_mtiles = s_misc[3];
   if ((int64_t)n_mtiles > a.cap_mtiles) {  // cannot happen within the capacity bound; guard anyway
     if (tid == 0) {
@@ -251,56 +283,81 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
     return;
   }
 
-  // (h) per group: tile_order, segments, row-tile entries
-  for (int q = tid; q < n_ne; q += SCAN_THREADS) {
-    const int g = s_order[q], e = g / R, r = g % R, n = s_n[g], off = s_poff[g];
-    const int nb = (n + M - 1) / M, b0 = off / M;
-    for (int b = 0; b < nb; ++b) a.tile_order[s_band_pos[q] + b] = b0 + b;
-    const int q2 = s_q2[g];
-    const int base = s_tile_base[q2], roff = s_run_off[q2], rsubs = s_run_subs[q2];
-    const int nsub = (n + MOE_SUB - 1) / MOE_SUB;
-    for (int j = 0; j < nsub; ++j) {
-      const int u = roff + j;
-      const int mt = base + u / a.mt_sub, slot = u % a.mt_sub;
-      int32_t* d = a.mtile_desc + (int64_t)mt * MOE_MT_FIELDS;
-      d[2 + slot] = off + MOE_SUB * j;
-      if (slot == 0) {
-        const int cnt = (rsubs - u) < a.mt_sub ? (rsubs - u) : a.mt_sub;
-        d[0] = e;
-        d[1] = cnt;
-        for (int s2 = cnt; s2 < MOE_MT_SUB; ++s2) d[2 + s2] = -1;
-      }
+  // (h) tile_order, row-tile entries and segments, one thread per band, sub-block and segment; the group of an
+  // entry is the last one whose first position (prefix over non-empty groups) is not after it
+  auto find = [&](const int* first, int pos) {
+    int lo = 0, hi = n_ne - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (first[mid] <= pos) lo = mid;
+      else hi = mid - 1;
     }
-    int sp = s_seg_pos[q];
-    for (int b = 0; b < nb; b += a.mgb, ++sp) {
-      const int cnt = (nb - b) < a.mgb ? (nb - b) : a.mgb;
-      int rows = n - b * M;
-      if (rows > cnt * M) rows = cnt * M;
-      int32_t* s = a.seg_desc + (int64_t)sp * MOE_SEG_FIELDS;
-      s[SEG_OWNER] = r;
-      s[SEG_EXPERT] = e;
-      s[SEG_FIRST_BAND] = b0 + b;
-      s[SEG_NBANDS] = cnt;
-      s[SEG_SRC_ROW] = off + b * M;
-      s[SEG_DST_ROW] = a.recv_off[g] + b * M;
-      s[SEG_ROWS] = rows;
-      s[SEG_GROUP] = g;
-      const int sub0 = (b * M) / MOE_SUB, sub1 = (b * M + rows - 1) / MOE_SUB;
-      const int mt0 = base + (roff + sub0) / a.mt_sub, mt1 = base + (roff + sub1) / a.mt_sub;
-      a.seg_mtiles[2 * sp] = mt0;
-      a.seg_mtiles[2 * sp + 1] = mt1 - mt0 + 1;
+    return lo;
+  };
+  for (int pos = tid; pos < n_tiles; pos += SCAN_THREADS) {
+    const int q = find(s_band_pos, pos);
+    a.tile_order[pos] = s_poff[s_order[q]] / M + (pos - s_band_pos[q]);
+  }
+  const int mt_mask = a.mt_sub - 1, mt_shift = __builtin_ctz(a.mt_sub);  // mt_sub is a power of two
+  for (int pos = tid; pos < s_misc[2]; pos += SCAN_THREADS) {
+    const int q2 = find(s_sub_pos, pos);
+    const int g = s_order2[q2], j = pos - s_sub_pos[q2], u = s_run_off[q2] + j;
+    int32_t* d = a.mtile_desc + (int64_t)(s_tile_base[q2] + (u >> mt_shift)) * MOE_MT_FIELDS;
+    const int slot = u & mt_mask;
+    d[2 + slot] = s_poff[g] + MOE_SUB * j;
+    if (slot == 0) {
+      const int left = s_run_subs[q2] - u, cnt = left < a.mt_sub ? left : a.mt_sub;
+      d[0] = g / R;
+      d[1] = cnt;
+      for (int s2 = cnt; s2 < MOE_MT_SUB; ++s2) d[2 + s2] = -1;
     }
   }
+  for (int sp = tid; sp < n_segs; sp += SCAN_THREADS) {
+    const int q = find(s_seg_pos, sp);
+    const int g = s_order[q], e = g / R, r = g - e * R, n = s_n[g], off = s_poff[g];
+    const int nb = (n + M - 1) / M, b = (sp - s_seg_pos[q]) * a.mgb;
+    const int cnt = (nb - b) < a.mgb ? (nb - b) : a.mgb;
+    int rows = n - b * M;
+    if (rows > cnt * M) rows = cnt * M;
+    int32_t* sd = a.seg_desc + (int64_t)sp * MOE_SEG_FIELDS;
+    sd[SEG_OWNER] = r;
+    sd[SEG_EXPERT] = e;
+    sd[SEG_FIRST_BAND] = off / M + b;
+    sd[SEG_NBANDS] = cnt;
+    sd[SEG_SRC_ROW] = off + b * M;
+    sd[SEG_DST_ROW] = a.recv_off[g] + b * M;
+    sd[SEG_ROWS] = rows;
+    sd[SEG_GROUP] = g;
+    const int q2 = s_q2[g], base = s_tile_base[q2], roff = s_run_off[q2];
+    const int sub0 = (b * M) / MOE_SUB, sub1 = (b * M + rows - 1) / MOE_SUB;
+    const int mt0 = base + ((roff + sub0) >> mt_shift), mt1 = base + ((roff + sub1) >> mt_shift);
+    a.seg_mtiles[2 * sp] = mt0;
+    a.seg_mtiles[2 * sp + 1] = mt1 - mt0 + 1;
+  }
   __syncthreads();
-  // (i) consumer order: segments by the last GEMM row tile they wait for, ties by segment index (stable)
-  for (int sg = tid; sg < n_segs; sg += SCAN_THREADS) {
-    const int last = a.seg_mtiles[2 * sg] + a.seg_mtiles[2 * sg + 1];
-    int rank = 0;
-    for (int o = 0; o < n_segs; ++o) {
-      const int lo2 = a.seg_mtiles[2 * o] + a.seg_mtiles[2 * o + 1];
-      rank += (lo2 < last) || (lo2 == last && o < sg);
+  // (i) consumer order: segments by the last GEMM row tile they wait for, ties by segment index (stable); the
+  // keys are staged in LDS when they fit
+  int* s_key = (int*)s_scratch;
+  if (n_segs <= SCAN_KEYS) {
+    for (int sg = tid; sg < n_segs; sg += SCAN_THREADS) s_key[sg] = a.seg_mtiles[2 * sg] + a.seg_mtiles[2 * sg + 1];
+    __syncthreads();
+    for (int sg = tid; sg < n_segs; sg += SCAN_THREADS) {
+      const int last = s_key[sg];
+      int rank = 0;
+#pragma unroll 8
+      for (int o = 0; o < n_segs; ++o) rank += (s_key[o] < last) || (s_key[o] == last && o < sg);
+      a.seg_sched[rank] = sg;
     }
-    a.seg_sched[rank] = sg;
+  } else {
+    for (int sg = tid; sg < n_segs; sg += SCAN_THREADS) {
+      const int last = a.seg_mtiles[2 * sg] + a.seg_mtiles[2 * sg + 1];
+      int rank = 0;
+      for (int o = 0; o < n_segs; ++o) {
+        const int lo2 = a.seg_mtiles[2 * o] + a.seg_mtiles[2 * o + 1];
+        rank += (lo2 < last) || (lo2 == last && o < sg);
+      }
+      a.seg_sched[rank] = sg;
+    }
   }
   if (tid == 0) {
     a.scalars[SC_MPAD] = M_pad;
@@ -376,14 +433,11 @@ __global__ __launch_bounds__(256) void k_gather_rows(const uint4* __restrict__ x
   }
 }
 
-__global__ void k_reset_status(int32_t* status) { *status = 0; }
-
 int launch_layout(const LayoutLaunch& p, hipStream_t st) {
   const int n_chunks = (p.T_o + 63) / 64;
-  hipLaunchKernelGGL(k_reset_status, dim3(1), dim3(1), 0, st, p.L->status);
   if (n_chunks > 0)
     hipLaunchKernelGGL(k_layout_count, dim3((n_chunks + 3) / 4, p.R), dim3(256), 0, st, p.topk_idx, p.T_o, p.G, p.k,
-                       p.lo, p.E, n_chunks, p.L->chunk_counts, p.L->status);
+                       p.lo, p.E, n_chunks, p.L->chunk_counts);
   ScanArgs a;
   a.R = p.R;
   a.T_o = p.T_o;
