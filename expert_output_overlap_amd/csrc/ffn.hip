@@ -276,8 +276,12 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm(GemmArgs a) {
 // global_load_lds_dwordx4 in its scalar-base form: lane i moves 16 bytes from base + off into LDS at
 // m0 + 16 * i (m0 is set in the same statement, so no other code depends on it)
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_addr) {
+  // base and lds_addr are the same in every lane; readfirstlane puts them in scalar registers
+  const uint64_t b = (uint64_t)base;
+  const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(lds_addr)),
-               "v"(off), "s"(base) : "memory");
+               "v"(off), "s"((const void*)sb) : "memory");
 }
 
 // this wave's loads have landed in LDS, then the workgroup barrier: after it every wave's have
@@ -392,14 +396,18 @@ __device__ bool wait_flags(const uint32_t* fl, int n, uint32_t epoch, uint64_t b
 // device-wide.  Publishing is then: every thread's stores completed (the barrier's vmcnt(0)), then the flag.
 // An agent-scope release fence would write back the whole L2 of the XCD instead, once per published tile, which
 // stalls every workgroup on that XCD; the reader still acquires at agent scope before it reads.
+// 16 bytes with the device-scope cache policy (the one agent-scope atomic stores use), as one dwordx4 store:
+// two 8-byte atomic stores per 16 bytes measured 2-3 times slower.  The compiler does not count this store, so
+// whoever needs it complete waits with an explicit vmcnt(0) (wait_stores).
 __device__ __forceinline__ void store16_coherent(void* p, u32x4_t v) {
-  uint64_t* q = (uint64_t*)p;
-  __hip_atomic_store(q, ((uint64_t)v.y << 32) | v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(q + 1, ((uint64_t)v.w << 32) | v.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
 }
 
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ void publish(uint32_t* flag, uint32_t epoch) {
-  __syncthreads();  // waits for this wave's stores (vmcnt(0)), then for every wave's
+  wait_stores();    // this wave's stores are complete
+  __syncthreads();  // and every wave's
   if (threadIdx.x == 0) __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -594,7 +602,8 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
         store16_coherent(dst + 512, __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v, v, 8, 9, 10, 11)));
         store16_coherent(dst + 768, __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v, v, 12, 13, 14, 15)));
       }
-    __syncthreads();  // every thread's partial stores completed (vmcnt(0))
+    wait_stores();
+    __syncthreads();  // every thread's partial stores completed
     if (tid == 0) *s_stop = (int)arrive(&a.scount[tile], a.epoch);
     __syncthreads();
     if (*s_stop != a.S - 1) return true;  // not the last split of this tile
@@ -606,6 +615,7 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
       const f32x8_t h1 = __builtin_shufflevector(q2, q3, 0, 1, 2, 3, 4, 5, 6, 7);
       return (f32x16_t)__builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
     };
+    // one 32 x 32 block at a time (loading several splits' blocks ahead spills the accumulators: slower)
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -644,13 +654,23 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
     }
   }
   __syncthreads();
-  for (int idx = tid_e; idx < BM * CPR; idx += 256) {
-    const int row = idx / CPR, ch = idx - row * CPR;
-    const int sub = row >> 4;
-    if (sub >= n_sub) continue;
-    const u32x4_t v = *(const u32x4_t*)(smem + row * OUT_ROW + ((ch ^ (row & 7)) << 4));
-    const int64_t grow = s_sub[sub] + (row & 15);
-    store16_coherent(Cb + (grow * ldc + (int64_t)nt * OUT_BN) * 2 + ch * 16, v);
+  // 8 chunks per thread at a time: their LDS reads first, then their stores, so neither latency is paid per chunk
+  constexpr int ITER = BM * CPR / 256, UN = ITER < 8 ? ITER : 8;
+  static_assert(ITER % UN == 0, "store loop unroll");
+#pragma unroll 1
+  for (int i0 = 0; i0 < ITER; i0 += UN) {
+    u32x4_t v[UN];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int idx = tid_e + (i0 + u) * 256, row = idx / CPR, ch = idx - row * CPR;
+      v[u] = *(const u32x4_t*)(smem + row * OUT_ROW + ((ch ^ (row & 7)) << 4));
+    }
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int idx = tid_e + (i0 + u) * 256, row = idx / CPR, ch = idx - row * CPR, sub = row >> 4;
+      if (sub < n_sub)
+        store16_coherent(Cb + ((s_sub[sub] + (row & 15)) * ldc + (int64_t)nt * OUT_BN) * 2 + ch * 16, v[u]);
+    }
   }
   if (GLU) {
     publish(&a.flags1[(int64_t)mt * a.n_nt1 + nt], a.epoch);
@@ -698,7 +718,7 @@ __global__ __launch_bounds__(256, 1) void k_ffn_bf16(FusedArgs a) {
     if (a.ts != nullptr && first && tid == 0) atomicMin((unsigned long long*)&a.ts[0], (unsigned long long)moe_clock());
     first = false;
     __syncthreads();
-    const int e = s_hdr[0], n_sub = s_hdr[1];
+    const int e = __builtin_amdgcn_readfirstlane(s_hdr[0]), n_sub = __builtin_amdgcn_readfirstlane(s_hdr[1]);
     bool ok;
     if (it.kind == 1) {
       ok = ffn_tile<BN1, true>(a, smem, s_sub, e, n_sub, it.mt, it.nt, 0, &s_stop);
