@@ -4,14 +4,20 @@
 // width -- to its owner as one contiguous write).  On one GPU the owner ranks are receive buffers in HBM,
 // so a transfer is a device-memory copy by the consumer's CUs.
 //
-// Every consumer workgroup walks all segments in the order in which their GEMM row tiles complete and copies
-// its 1/C share of each (16-byte chunks w*B + t, then every C*B chunks for B threads): all C CUs work on the
-// segment that became ready last, so the copy that remains after the producer's final tile is short.  For a
-// segment it polls the flags of the GEMM row tiles the segment depends on with relaxed agent-scope loads,
-// then issues one agent-scope acquire fence (pairing with the producer's publish) before reading the rows;
-// a spin budget on the 100 MHz clock bounds every wait.
+// The copy work is cut into units of at most CONSUMER_UNIT bytes: a segment of n bytes is ceil(n / unit) units
+// of whole 16-byte chunks.  Units are numbered in the order in which their segments' GEMM row tiles complete,
+// and consumer workgroup w of C takes units w, w + C, ...: a small segment goes to one workgroup whole, a large
+// one is spread over several, so the copy that remains after the producer's final tile is short and no
+// workgroup pays a wait per segment for segments it has no part of.  For a unit it polls the flags of the GEMM
+// row tiles its segment depends on with relaxed agent-scope loads, then issues one agent-scope acquire fence
+// (pairing with the producer's publish) before reading the rows; a spin budget on the 100 MHz clock bounds
+// every wait.
 #pragma once
 #include "common.h"
+
+#define CONSUMER_UNIT_CHUNKS 8192  // 16-byte chunks per copy unit (128 KB)
+
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
 
 struct ConsumerArgs {
   const uint4* y;  // y_pad rows, row_vec 16-byte chunks per row
@@ -36,8 +42,16 @@ __device__ void consumer_role(const ConsumerArgs& a, int cid, int n_cons) {
   if (load_status(a.status) != 0) return;
   const int n_segs = a.scalars[SC_NSEGS];
   const uint64_t t0 = moe_clock();
+  int64_t u0 = 0;  // first unit of the current segment
   for (int si = 0; si < n_segs; ++si) {
     const int s = a.seg_sched[si];
+    const int32_t* sd = a.seg_desc + (int64_t)s * MOE_SEG_FIELDS;
+    const int64_t n = (int64_t)sd[SEG_ROWS] * a.row_vec;  // 16-byte chunks of the segment
+    const int64_t units = (n + CONSUMER_UNIT_CHUNKS - 1) / CONSUMER_UNIT_CHUNKS;
+    // this workgroup's first unit of the segment: the smallest u >= u0 with u % n_cons == cid
+    int64_t u = u0 + ((cid - u0 % n_cons) % n_cons + n_cons) % n_cons;
+    u0 += units;
+    if (u >= u0) continue;  // no part of this segment
     const int mt0 = a.seg_mtiles[2 * s], mcnt = a.seg_mtiles[2 * s + 1];
     const int nflags = mcnt * a.n_nt;
     const uint32_t* fl = a.flags + (int64_t)mt0 * a.n_nt;
@@ -56,22 +70,26 @@ __device__ void consumer_role(const ConsumerArgs& a, int cid, int n_cons) {
       __builtin_amdgcn_s_sleep(1);
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    const int32_t* sd = a.seg_desc + (int64_t)s * MOE_SEG_FIELDS;
-    const int owner = sd[SEG_OWNER], src = sd[SEG_SRC_ROW], dst = sd[SEG_DST_ROW], rows = sd[SEG_ROWS];
+    const int owner = sd[SEG_OWNER], src = sd[SEG_SRC_ROW], dst = sd[SEG_DST_ROW];
     if (a.ts != nullptr && tid == 0) atomicMin((unsigned long long*)&a.ts[2 + 2 * s], (unsigned long long)moe_clock());
     const uint4* __restrict__ from = a.y + (int64_t)src * a.row_vec;
     uint4* __restrict__ to = (uint4*)a.recv.p[owner] + (int64_t)dst * a.row_vec;
-    const int64_t n = (int64_t)rows * a.row_vec;
-    const int64_t stride = (int64_t)n_cons * blockDim.x;
-    int64_t i = (int64_t)cid * blockDim.x + tid;
-    for (; i + 3 * stride < n; i += 4 * stride) {
-      const uint4 v0 = from[i], v1 = from[i + stride], v2 = from[i + 2 * stride], v3 = from[i + 3 * stride];
-      to[i] = v0;
-      to[i + stride] = v1;
-      to[i + 2 * stride] = v2;
-      to[i + 3 * stride] = v3;
+    const int64_t B = blockDim.x;
+    for (; u < u0; u += n_cons) {
+      const int64_t c0 = (u - (u0 - units)) * CONSUMER_UNIT_CHUNKS;
+      const int64_t c1 = c0 + CONSUMER_UNIT_CHUNKS < n ? c0 + CONSUMER_UNIT_CHUNKS : n;
+      int64_t i = c0 + tid;
+      const v4u32* __restrict__ f4 = (const v4u32*)from;
+      v4u32* __restrict__ t4 = (v4u32*)to;
+      for (; i + 7 * B < c1; i += 8 * B) {  // 8 loads in flight per thread (32 KB per workgroup)
+        v4u32 v[8];  // a native vector type: an array of it stays in registers
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = f4[i + k * B];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) t4[i + k * B] = v[k];
+      }
+      for (; i < c1; i += B) t4[i] = f4[i];
     }
-    for (; i < n; i += stride) to[i] = from[i];
     if (a.ts != nullptr) {
       __syncthreads();
       if (tid == 0) atomicMax((unsigned long long*)&a.ts[3 + 2 * s], (unsigned long long)moe_clock());

@@ -313,6 +313,7 @@ struct FusedArgs {
   unsigned char* y;         // y_pad [cap_rows, d]
   int d, f;
   int n_nt1, n_nt2, S, window;
+  int interleave;  // item order: 0 = GEMM1 first, 1 = interleaved windows
   const int32_t* mtile_desc;
   const int32_t* scalars;
   int sc_nmt;
@@ -333,40 +334,63 @@ struct FfnItem {
   int mt, nt, s;
 };
 
-// Item i of the list: all GEMM1 items, column-tile major over every row tile (each gate/up weight tile is
-// streamed once, by consecutive items), then the GEMM2 items in windows of W row tiles (remote-first order),
-// split-major and column-tile major inside a window.  A GEMM2 split reads only its own share of h's columns,
-// which the first part of the GEMM1 list produced, so the splits find their inputs finished; the last split of
-// a tile follows its other splits; and the row tiles of a window complete together, window after window, while
-// the later windows are still computed, so the return of the early windows overlaps them.
-__device__ __forceinline__ FfnItem ffn_item(int i, int n_mt, int W, int n1, int n2, int S) {
-  FfnItem it;
-  if (i < n_mt * n1) {
+// Item i of the list, in one of two orders over windows of W row tiles (remote-first row-tile order); inside a
+// window, GEMM1 items are column-tile major (consecutive items share a weight tile) and GEMM2 items split-major,
+// then column-tile major.
+//  - GEMM1 first: every GEMM1 item (one window over all row tiles: each gate/up weight tile streamed once), then
+//    the GEMM2 windows.  A GEMM2 split reads only its own share of h's columns, which the first part of the GEMM1
+//    list produced; row tiles complete window after window during the last part of the launch.
+//  - interleaved: G1(0), G1(1), G2(0), G1(2), G2(1), ..., G1(nw-1), G2(nw-2), G2(nw-1): row tiles complete
+//    window after window over the whole launch, so a return that is large next to the FFN starts early.
+// In both, every GEMM2 item follows the GEMM1 items it reads and the last split of a tile follows its others.
+__device__ __forceinline__ FfnItem ffn_item(int i, int n_mt, int W, int n1, int n2, int S, bool interleave) {
+  const int n2S = n2 * S;
+  auto g1 = [&](int w, int j, int Wc) {  // GEMM1 item j of a window of Wc row tiles starting at row tile w*W
+    FfnItem it;
     it.kind = 1;
-    it.nt = i / n_mt;
-    it.mt = i - it.nt * n_mt;
+    it.nt = j / Wc;
+    it.mt = w * W + (j - it.nt * Wc);
     it.s = 0;
     return it;
+  };
+  auto g2 = [&](int w, int j, int Wc) {
+    FfnItem it;
+    it.kind = 2;
+    const int per = Wc * n2;
+    it.s = j / per;
+    const int r = j - it.s * per;
+    it.nt = r / Wc;
+    it.mt = w * W + (r - it.nt * Wc);
+    return it;
+  };
+  const int nw = (n_mt + W - 1) / W;
+  const int Wl = n_mt - (nw - 1) * W;
+  if (!interleave) {
+    if (i < n_mt * n1) {
+      FfnItem it;
+      it.kind = 1;
+      it.nt = i / n_mt;
+      it.mt = i - it.nt * n_mt;
+      it.s = 0;
+      return it;
+    }
+    const int j = i - n_mt * n1, w = j / (W * n2S);
+    return w < nw - 1 ? g2(w, j - w * W * n2S, W) : g2(nw - 1, j - (nw - 1) * W * n2S, Wl);
   }
-  int j = i - n_mt * n1;
-  const int per = n2 * S;        // GEMM2 items per row tile
-  const int full = n_mt / W;     // windows of W row tiles, then one of n_mt % W
-  int w, Wc;
-  if (j < full * W * per) {
-    w = j / (W * per);
-    j -= w * W * per;
-    Wc = W;
-  } else {
-    w = full;
-    j -= full * W * per;
-    Wc = n_mt - full * W;
+  const int W0 = nw == 1 ? Wl : W;
+  if (i < W0 * n1) return g1(0, i, W0);
+  i -= W0 * n1;
+  if (nw == 1) return g2(0, i, Wl);
+  const int pz = W * (n1 + n2S);  // a pair (G1(p), G2(p-1)) of two full windows, p = 1 .. nw-2
+  if (i < (nw - 2) * pz) {
+    const int p = 1 + i / pz, j = i - (p - 1) * pz;
+    return j < W * n1 ? g1(p, j, W) : g2(p - 1, j - W * n1, W);
   }
-  it.kind = 2;
-  it.s = j / (Wc * n2);
-  const int r = j - it.s * Wc * n2;
-  it.nt = r / Wc;
-  it.mt = w * W + (r - it.nt * Wc);
-  return it;
+  i -= (nw - 2) * pz;
+  if (i < Wl * n1) return g1(nw - 1, i, Wl);
+  i -= Wl * n1;
+  if (i < W * n2S) return g2(nw - 2, i, W);
+  return g2(nw - 1, i - W * n2S, Wl);
 }
 
 // All threads of the workgroup: wait until the n flags equal epoch, then acquire.  False if the spin budget ran
@@ -709,7 +733,7 @@ __global__ __launch_bounds__(256, 1) void k_ffn_bf16(FusedArgs a) {
   bool first = true;
   for (int item = bid; item < n_items; item += G) {
     __syncthreads();  // previous item done with LDS and the header
-    const FfnItem it = ffn_item(item, n_mt, a.window, a.n_nt1, a.n_nt2, a.S);
+    const FfnItem it = ffn_item(item, n_mt, a.window, a.n_nt1, a.n_nt2, a.S, a.interleave != 0);
     if (tid < MOE_MT_FIELDS) {
       const int v = a.mtile_desc[(int64_t)it.mt * MOE_MT_FIELDS + tid];
       if (tid < 2) s_hdr[tid] = v;
@@ -829,6 +853,11 @@ int launch_bf16(const FfnLaunch& p, int grid, int n_cons, hipStream_t st) {
   a.n_nt2 = p.d / bn2;
   a.S = ffn_splits(p.dtype, p.d, p.f);
   a.window = p.band_window > 0 ? p.band_window : 4;
+  // Interleave when the return is large next to the FFN.  At about 45 GB/s of copy per consumer CU and 0.8
+  // PFLOP/s of FFN, copy time / FFN time = 4 M d / (45e9 C) / (6 M d f / 0.8e15) ~= 11850 / (C f), whatever M
+  // and d are; GEMM1 first (faster, weights streamed once) leaves the last third of the launch for the copies,
+  // so it is used while that ratio stays under about 1/4.
+  a.interleave = n_cons > 0 && (int64_t)n_cons * p.f < 48000;
   a.mtile_desc = p.L->mtile_desc;
   a.scalars = p.L->scalars;
   a.sc_nmt = SC_NR + p.R;
