@@ -106,6 +106,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--kernels-only", action="store_true", help="timed loop only (for profiler runs)")
+    ap.add_argument("--mode", type=int, default=0, choices=(0, 1),
+                    help="FFN mode of the timed steps: 0 overlapped, 1 sequential (the consumer alone after the "
+                         "producer, for profiling the copy)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this path runs on a single MI355X (the owner ranks are receive buffers in "
@@ -137,7 +140,7 @@ def main():
         P.combine()
 
     for _ in range(args.warmup):
-        step()
+        step(mode=args.mode)
     torch.cuda.synchronize()
     assert P.status() == B.MOE_OK, "device status %d" % P.status()
     sc = P.scalars()
@@ -151,7 +154,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        step(mode=args.mode)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     g1_ms, g2_ms, cons_ms, ncalls = B.moe_kernel_times()
@@ -211,7 +214,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": s.dtype, "data": "synthetic",
         "config": {"workload": workload_name(s), "M_real": M_real, "M_pad": M_pad, "gemm_row_tiles": sc["n_mtiles"], "consumer_cus": cus,
-                   "band_window": args.band_window or 4, "mode": "overlapped"},
+                   "band_window": args.band_window or 4, "mode": "overlapped" if args.mode == 0 else "sequential"},
         "pct_bf16_peak_step": round(100 * value / peak, 2),
         "ffn_tflops_overlapped": round(ffn_tflops, 2),
         "pct_bf16_peak_ffn": round(100 * ffn_tflops / peak, 2),
