@@ -268,6 +268,7 @@ int moe_expert_ffn_overlap(const moe_shape* s, const moe_layout* L, const void* 
     return fail(MOE_EINVAL, "null pointer");
   for (int r = 0; r < s->R; ++r)
     if (!recv[r]) return fail(MOE_EINVAL, "null receive buffer");
+  if ((uintptr_t)flags % 8 != 0) return fail(MOE_EINVAL, "flags must be 8-byte aligned");
   if (cfg->epoch == 0) return fail(MOE_EINVAL, "epoch must be nonzero");
   if (cfg->mode < 0 || cfg->mode > 2) return fail(MOE_EINVAL, "mode must be 0, 1 or 2");
   if (cfg->band_window < 0) return fail(MOE_EINVAL, "band_window must be >= 0");
@@ -309,7 +310,8 @@ int moe_expert_ffn_overlap(const moe_shape* s, const moe_layout* L, const void* 
   if (cfg->timestamps && launch_ts_init(cfg->timestamps, 2 + 2 * layout_offsets(s).cap_tiles, st))
     return fail(MOE_EHIP, "launch failed");
   // overlapped: C consumer workgroups in the producer launch (bf16: the whole FFN; fp32: its second GEMM),
-  // producers on the other CUs; sequential: producers on every CU, then the consumer alone
+  // producers on the other CUs, each joining the return once its items are done; sequential: producers on
+  // every CU, then the return on every CU
   const int n_cons = cfg->mode == 0 ? C : 0;
   if (timed) hipEventRecord(ce.e[0], st);
   if (launch_ffn_producer(p, n_cu, p.dtype == MOE_BF16 ? n_cons : 0, st)) return fail(MOE_EHIP, "producer launch failed");
@@ -319,7 +321,7 @@ int moe_expert_ffn_overlap(const moe_shape* s, const moe_layout* L, const void* 
     hipEventRecord(ce.e[2], st);
     hipEventRecord(ce.e[3], st);
   }
-  if (cfg->mode == 1 && launch_ffn_consumer(p, C, st)) return fail(MOE_EHIP, "consumer launch failed");
+  if (cfg->mode == 1 && launch_ffn_consumer(p, n_cu, st)) return fail(MOE_EHIP, "consumer launch failed");
   if (timed) {
     hipEventRecord(ce.e[4], st);
     std::lock_guard<std::mutex> lk(g_mu);

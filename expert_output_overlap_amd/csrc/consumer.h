@@ -6,12 +6,17 @@
 //
 // The copy work is cut into units of at most CONSUMER_UNIT bytes: a segment of n bytes is ceil(n / unit) units
 // of whole 16-byte chunks.  Units are numbered in the order in which their segments' GEMM row tiles complete,
-// and consumer workgroup w of C takes units w, w + C, ...: a small segment goes to one workgroup whole, a large
-// one is spread over several, so the copy that remains after the producer's final tile is short and no
-// workgroup pays a wait per segment for segments it has no part of.  For a unit it polls the flags of the GEMM
-// row tiles its segment depends on with relaxed agent-scope loads, then issues one agent-scope acquire fence
-// (pairing with the producer's publish) before reading the rows; a spin budget on the 100 MHz clock bounds
-// every wait.
+// and every workgroup in the role takes the next unit from a counter, one at a time: the consumer partition
+// during the FFN, and every producer workgroup as soon as its own items are done, so the copies still pending
+// when the last tile is published are spread over the whole chip.  For a unit whose segment it has not seen
+// complete yet, a workgroup polls the flags of the segment's GEMM row tiles with relaxed agent-scope loads, then
+// issues one agent-scope acquire fence (pairing with the producer's publish) before reading the rows; a spin
+// budget on the 100 MHz clock bounds every wait.
+//
+// The counter is one 64-bit word: the launch's stamp (nonzero, distinct for every launch) in the high half and
+// the units handed out in the low half.  One workgroup writes the stamp with a zero count at the start of the
+// launch; a workgroup takes its first unit only once it sees the stamp, so no count of an earlier launch is
+// ever used.
 #pragma once
 #include "common.h"
 
@@ -28,68 +33,126 @@ struct ConsumerArgs {
   const int32_t* scalars;
   int32_t* status;
   const uint32_t* flags;
+  uint64_t* claim;  // unit counter: stamp << 32 | units handed out
   uint32_t epoch;
+  uint32_t stamp;
   int n_nt;
   int row_vec;
   uint64_t budget;
   uint64_t* ts;
 };
 
-// Runs in consumer workgroup `cid` of `n_cons`, blockDim.x threads.
-__device__ void consumer_role(const ConsumerArgs& a, int cid, int n_cons) {
-  __shared__ int s_stop;
-  const int tid = threadIdx.x;
+// Opens the counter for this launch; called by one workgroup at its start, before it claims.
+__device__ __forceinline__ void consumer_stamp(const ConsumerArgs& a) {
+  if (threadIdx.x == 0)
+    __hip_atomic_store(a.claim, (uint64_t)a.stamp << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Runs in a workgroup of up to 256 threads (whole waves) until every unit has been handed out.
+__device__ void consumer_role(const ConsumerArgs& a) {
+  // a window of up to blockDim.x scheduled segments: their ids and, relative to the window, the units before them
+  __shared__ int s_seg[256];
+  __shared__ uint32_t s_pre[257];
+  __shared__ int s_wsum[4];
+  __shared__ uint32_t s_cur;
+  __shared__ int s_hit, s_stop;
+  const int tid = threadIdx.x, nthr = blockDim.x;
   if (load_status(a.status) != 0) return;
   const int n_segs = a.scalars[SC_NSEGS];
   const uint64_t t0 = moe_clock();
-  int64_t u0 = 0;  // first unit of the current segment
-  for (int si = 0; si < n_segs; ++si) {
-    const int s = a.seg_sched[si];
-    const int32_t* sd = a.seg_desc + (int64_t)s * MOE_SEG_FIELDS;
-    const int64_t n = (int64_t)sd[SEG_ROWS] * a.row_vec;  // 16-byte chunks of the segment
-    const int64_t units = (n + CONSUMER_UNIT_CHUNKS - 1) / CONSUMER_UNIT_CHUNKS;
-    // this workgroup's first unit of the segment: the smallest u >= u0 with u % n_cons == cid
-    int64_t u = u0 + ((cid - u0 % n_cons) % n_cons + n_cons) % n_cons;
-    u0 += units;
-    if (u >= u0) continue;  // no part of this segment
-    const int mt0 = a.seg_mtiles[2 * s], mcnt = a.seg_mtiles[2 * s + 1];
-    const int nflags = mcnt * a.n_nt;
-    const uint32_t* fl = a.flags + (int64_t)mt0 * a.n_nt;
-    // wait for every tile of the segment
-    for (;;) {
-      int ok = 1;
-      for (int i = tid; i < nflags; i += blockDim.x)
-        ok &= __hip_atomic_load(&fl[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch;
-      if (__syncthreads_and(ok)) break;
-      if (tid == 0) s_stop = (moe_clock() - t0 > a.budget) ? 1 : (load_status(a.status) != 0 ? 2 : 0);
-      __syncthreads();
-      if (s_stop) {
-        if (s_stop == 1 && tid == 0) set_status(a.status, MOE_ETIMEOUT);
-        return;
+  uint32_t next = 0;  // thread 0: the unit claimed for the next round
+  if (tid == 0) {
+    int stop = 0;
+    while ((uint32_t)(__hip_atomic_load(a.claim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 32) != a.stamp) {
+      if (moe_clock() - t0 > a.budget) {
+        stop = 1;
+        break;
       }
       __builtin_amdgcn_s_sleep(1);
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (stop) set_status(a.status, MOE_ETIMEOUT);
+    else next = (uint32_t)__hip_atomic_fetch_add(a.claim, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_stop = stop;
+  }
+  __syncthreads();
+  if (s_stop) return;
+  int base = 0, span = 0;  // scheduled segments [base, base + span) are in the window
+  uint32_t ubase = 0;      // units before segment base
+  int seen = -1;           // the last segment whose flags this workgroup found complete
+  for (;;) {
+    __syncthreads();  // the previous unit's s_cur and s_hit have been read
+    if (tid == 0) s_cur = next;
+    __syncthreads();
+    const uint32_t cur = s_cur;
+    // move the window forward to the one holding unit cur (claims only grow)
+    while (span == 0 || cur - ubase >= s_pre[span]) {
+      if (span > 0) {
+        ubase += s_pre[span];
+        base += span;
+      }
+      if (base >= n_segs) return;  // every unit has been handed out
+      span = min(nthr, n_segs - base);
+      __syncthreads();  // the old window is no longer read
+      uint32_t u = 0;
+      if (tid < span) {
+        const int s = a.seg_sched[base + tid];
+        s_seg[tid] = s;
+        const int64_t n = (int64_t)a.seg_desc[(int64_t)s * MOE_SEG_FIELDS + SEG_ROWS] * a.row_vec;
+        u = (uint32_t)((n + CONSUMER_UNIT_CHUNKS - 1) / CONSUMER_UNIT_CHUNKS);
+      }
+      int v = wave_incl_scan((int)u);
+      if ((tid & 63) == 63) s_wsum[tid >> 6] = v;
+      __syncthreads();
+      for (int w = 0; w < (tid >> 6); ++w) v += s_wsum[w];
+      if (tid < span) s_pre[tid + 1] = (uint32_t)v;
+      if (tid == 0) s_pre[0] = 0;
+      __syncthreads();
+    }
+    const uint32_t r = cur - ubase;
+    if (tid < span && s_pre[tid] <= r && r < s_pre[tid + 1]) s_hit = tid;
+    __syncthreads();
+    const int t = s_hit;
+    const int s = s_seg[t];
+    const int64_t c0 = (int64_t)(r - s_pre[t]) * CONSUMER_UNIT_CHUNKS;
+    // the next claim goes out now; its reply is needed only at the top of the next round
+    if (tid == 0) next = (uint32_t)__hip_atomic_fetch_add(a.claim, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int32_t* sd = a.seg_desc + (int64_t)s * MOE_SEG_FIELDS;
+    if (s != seen) {
+      const int mt0 = a.seg_mtiles[2 * s], mcnt = a.seg_mtiles[2 * s + 1];
+      const int nflags = mcnt * a.n_nt;
+      const uint32_t* fl = a.flags + (int64_t)mt0 * a.n_nt;
+      for (;;) {
+        int ok = 1;
+        for (int i = tid; i < nflags; i += nthr)
+          ok &= __hip_atomic_load(&fl[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch;
+        if (__syncthreads_and(ok)) break;
+        if (tid == 0) s_stop = (moe_clock() - t0 > a.budget) ? 1 : (load_status(a.status) != 0 ? 2 : 0);
+        __syncthreads();
+        if (s_stop) {
+          if (s_stop == 1 && tid == 0) set_status(a.status, MOE_ETIMEOUT);
+          return;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      seen = s;
+    }
+    const int64_t n = (int64_t)sd[SEG_ROWS] * a.row_vec;
+    const int64_t c1 = c0 + CONSUMER_UNIT_CHUNKS < n ? c0 + CONSUMER_UNIT_CHUNKS : n;
     const int owner = sd[SEG_OWNER], src = sd[SEG_SRC_ROW], dst = sd[SEG_DST_ROW];
     if (a.ts != nullptr && tid == 0) atomicMin((unsigned long long*)&a.ts[2 + 2 * s], (unsigned long long)moe_clock());
-    const uint4* __restrict__ from = a.y + (int64_t)src * a.row_vec;
-    uint4* __restrict__ to = (uint4*)a.recv.p[owner] + (int64_t)dst * a.row_vec;
-    const int64_t B = blockDim.x;
-    for (; u < u0; u += n_cons) {
-      const int64_t c0 = (u - (u0 - units)) * CONSUMER_UNIT_CHUNKS;
-      const int64_t c1 = c0 + CONSUMER_UNIT_CHUNKS < n ? c0 + CONSUMER_UNIT_CHUNKS : n;
-      int64_t i = c0 + tid;
-      const v4u32* __restrict__ f4 = (const v4u32*)from;
-      v4u32* __restrict__ t4 = (v4u32*)to;
-      for (; i + 7 * B < c1; i += 8 * B) {  // 8 loads in flight per thread (32 KB per workgroup)
-        v4u32 v[8];  // a native vector type: an array of it stays in registers
+    const v4u32* __restrict__ f4 = (const v4u32*)(a.y + (int64_t)src * a.row_vec);
+    v4u32* __restrict__ t4 = (v4u32*)((uint4*)a.recv.p[owner] + (int64_t)dst * a.row_vec);
+    const int64_t B = nthr;
+    int64_t i = c0 + tid;
+    for (; i + 7 * B < c1; i += 8 * B) {  // 8 loads in flight per thread (32 KB per workgroup of 256)
+      v4u32 v[8];  // a native vector type: an array of it stays in registers
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = f4[i + k * B];
+      for (int k = 0; k < 8; ++k) v[k] = f4[i + k * B];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) t4[i + k * B] = v[k];
-      }
-      for (; i < c1; i += B) t4[i] = f4[i];
+      for (int k = 0; k < 8; ++k) t4[i + k * B] = v[k];
     }
+    for (; i < c1; i += B) t4[i] = f4[i];
     if (a.ts != nullptr) {
       __syncthreads();
       if (tid == 0) atomicMax((unsigned long long*)&a.ts[3 + 2 * s], (unsigned long long)moe_clock());

@@ -12,6 +12,7 @@
 // the remote-first group order, so all-padding sub-blocks cost nothing.  Items (row tile, column tile)
 // are visited window by window (band_window row tiles, column-tile-major inside a window) for weight
 // reuse, and consecutive items go to workgroups on the same XCD.
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -91,8 +92,9 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm(GemmArgs a) {
   __shared__ int s_sub[MOE_MT_SUB];
   __shared__ int s_hdr[2];
 
+  if (PUBLISH && a.n_cons > 0 && blockIdx.x == 0) consumer_stamp(a.cons);
   if (PUBLISH && (int)blockIdx.x < a.n_cons) {
-    consumer_role(a.cons, blockIdx.x, a.n_cons);
+    consumer_role(a.cons);
     return;
   }
   if (load_status(a.status) != 0) return;
@@ -250,6 +252,8 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm(GemmArgs a) {
       }
     }
   }
+  // then every producer returns segments until no copy unit is left
+  if (PUBLISH && n_cons > 0) consumer_role(a.cons);
 }
 
 // ---- bf16 GEMM: 256-row tiles, direct global->LDS loads ------------------------------------------------
@@ -607,11 +611,32 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
   };
   if (mact == MI) kloop(std::true_type{});
   else kloop(std::false_type{});
+  // epilogue: every wave writes its bf16 outputs into LDS as a 256 x OUT_BN tile (16-byte chunk ch of row r at
+  // chunk ch ^ (r & 7), so neither the column writes nor the row reads collide), then 16-byte stores of the rows
+  // of present sub-blocks (padding rows inside them included, never read for a result)
+  constexpr int NO = GLU ? NI / 2 : NI;
+  constexpr int OUT_ROW = OUT_BN * 2, CPR = OUT_ROW / 16;
+  // the thread index, made opaque here, so that the many epilogue addresses are computed per item instead of
+  // being hoisted out of the item loop, where they would hold (and spill) registers through the k-loop
+  int tid_e = tid;
+  asm volatile("" : "+v"(tid_e));
+  const int lane_e = tid_e & 63;
+  auto stage = [&](int mi, int ni, const f32x16_t& v, const f32x16_t& up) {  // one 32 x 32 block into LDS
+    const int col = (GLU ? wn * (WN / 2) : wn * WN) + ni * 32 + (lane_e & 31);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int row = wm * WM + mi * 32 + (q >> 2) * 8 + (lane_e >> 5) * 4 + (q & 3);
+      const float o = GLU ? silu_fast(v[q]) * up[q] : v[q];
+      const int chunk = (col >> 3) ^ (row & 7);
+      *(__bf16*)(smem + row * OUT_ROW + chunk * 16 + (col & 7) * 2) = (__bf16)o;  // round to nearest even
+    }
+  };
+  bool staged = false;
   if (!GLU && a.S > 1) {
     // split-K: every split stores its fp32 partial sums (thread tid keeps its accumulators at float4 chunk
     // ((mi * NI + ni) * 4 + q4) * 256 + tid of its slot), waits for the stores to complete, and counts itself in;
-    // the split that arrives last adds the slots in split order, its own from registers: y = ((p_0 + p_1) + ...)
-    // + p_{S-1}, the same association whichever split is last, so the result is the same on every call.
+    // the split that arrives last adds the slots in split order: y = ((p_0 + p_1) + ...) + p_{S-1}, the same
+    // association whichever split is last, so the result is the same on every call.
     const int64_t tile = (int64_t)mt * a.n_nt2 + nt;
     f32x4_t* slots = (f32x4_t*)(a.partial + tile * a.S * (BM * BN));
     constexpr int SLOT4 = BM * BN / 4;
@@ -627,7 +652,7 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
         store16_coherent(dst + 768, __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v, v, 12, 13, 14, 15)));
       }
     wait_stores();
-    __syncthreads();  // every thread's partial stores completed
+    __syncthreads();  // every thread's partial stores completed; every wave is done with the operand stages
     if (tid == 0) *s_stop = (int)arrive(&a.scount[tile], a.epoch);
     __syncthreads();
     if (*s_stop != a.S - 1) return true;  // not the last split of this tile
@@ -639,43 +664,54 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
       const f32x8_t h1 = __builtin_shufflevector(q2, q3, 0, 1, 2, 3, 4, 5, 6, 7);
       return (f32x16_t)__builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
     };
-    // one 32 x 32 block at a time (loading several splits' blocks ahead spills the accumulators: slower)
+    // With the split count fixed at compile time, every slot of a 32 x 32 block (this split's own too) is loaded
+    // in one go, D blocks ahead of the one being summed, so about D round trips of the reads are in flight
+    // instead of one, and each sum goes straight to the LDS tile (the accumulators are dead by then).  The loads
+    // and sums of consecutive blocks are kept in order so that the register ring is all that is live.  Other
+    // split counts sum one block and split at a time into the accumulators.
+    auto ring_sum = [&](auto S_) {
+      constexpr int SC = decltype(S_)::value, NB = MI * NI, D = SC <= 2 ? 3 : 2;
+      f32x16_t ring[D + 1][SC];
+      auto load = [&](int b) {
+#pragma unroll
+        for (int sp = 0; sp < SC; ++sp) ring[b % (D + 1)][sp] = ld16(slots + (int64_t)sp * SLOT4 + b * 4 * 256 + tid);
+      };
+#pragma unroll
+      for (int b = 0; b < D; ++b) load(b);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        if (b + D < NB) load(b + D);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16_t t = ring[b % (D + 1)][0];
+#pragma unroll
+        for (int sp = 1; sp < SC; ++sp) t += ring[b % (D + 1)][sp];
+        stage(b / NI, b % NI, t, t);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    staged = true;
+    if (a.S == 2) ring_sum(std::integral_constant<int, 2>{});
+    else if (a.S == 3) ring_sum(std::integral_constant<int, 3>{});
+    else if (a.S == 4) ring_sum(std::integral_constant<int, 4>{});
+    else {
+      staged = false;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const f32x4_t* src = slots + (mi * NI + ni) * 4 * 256 + tid;
+          f32x16_t t = s == 0 ? acc[mi][ni] : ld16(src);
+          for (int sp = 1; sp < a.S; ++sp) t += sp == s ? acc[mi][ni] : ld16(src + (int64_t)sp * SLOT4);
+          acc[mi][ni] = t;
+        }
+    }
+  }
+  if (!staged) {
+    __syncthreads();  // every wave is done with the operand stages
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        const f32x4_t* src = slots + (mi * NI + ni) * 4 * 256 + tid;
-        f32x16_t t = s == 0 ? acc[mi][ni] : ld16(src);
-        for (int sp = 1; sp < a.S; ++sp) t += sp == s ? acc[mi][ni] : ld16(src + (int64_t)sp * SLOT4);
-        acc[mi][ni] = t;
-      }
-  }
-
-  // epilogue: every wave writes its bf16 outputs into LDS as a 256 x OUT_BN tile (16-byte chunk ch of row r at
-  // chunk ch ^ (r & 7), so neither the column writes nor the row reads collide), then 16-byte stores of the rows
-  // of present sub-blocks (padding rows inside them included, never read for a result)
-  constexpr int NO = GLU ? NI / 2 : NI;
-  constexpr int OUT_ROW = OUT_BN * 2, CPR = OUT_ROW / 16;
-  // the thread index, made opaque here, so that the many epilogue addresses are computed per item instead of
-  // being hoisted out of the item loop, where they would hold (and spill) registers through the k-loop
-  int tid_e = tid;
-  asm volatile("" : "+v"(tid_e));
-  const int lane_e = tid_e & 63;
-  __syncthreads();  // every wave is done with the operand stages
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
-#pragma unroll
-    for (int ni = 0; ni < NO; ++ni) {
-      const int col = (GLU ? wn * (WN / 2) : wn * WN) + ni * 32 + (lane_e & 31);
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int row = wm * WM + mi * 32 + (q >> 2) * 8 + (lane_e >> 5) * 4 + (q & 3);
-        float v = acc[mi][ni][q];
-        if (GLU) v = silu_fast(v) * acc[mi][ni + NI / 2][q];
-        const int chunk = (col >> 3) ^ (row & 7);
-        *(__bf16*)(smem + row * OUT_ROW + chunk * 16 + (col & 7) * 2) = (__bf16)v;  // round to nearest even
-      }
-    }
+      for (int ni = 0; ni < NO; ++ni) stage(mi, ni, acc[mi][ni], acc[mi][GLU ? ni + NI / 2 : ni]);
   }
   __syncthreads();
   // 8 chunks per thread at a time: their LDS reads first, then their stores, so neither latency is paid per chunk
@@ -715,23 +751,14 @@ __global__ __launch_bounds__(256, 1) void k_ffn_bf16(FusedArgs a) {
   __shared__ int s_hdr[2];
   __shared__ int s_stop;
 
-  if ((int)blockIdx.x < a.n_cons) {
-    consumer_role(a.cons, blockIdx.x, a.n_cons);
-    return;
-  }
   if (load_status(a.status) != 0) return;
+  if (a.n_cons > 0 && blockIdx.x == 0) consumer_stamp(a.cons);
   const int n_mt = a.scalars[a.sc_nmt];
   const int n_items = n_mt * (a.n_nt1 + a.n_nt2 * a.S);
   const int tid = threadIdx.x;
-  const int G = gridDim.x - a.n_cons;
-  // workgroup b takes items b', b' + G, ..., b' remapped so that a run of consecutive items goes to the
-  // workgroups of one XCD (workgroup b sits on XCD b % 8), which share operand tiles in its L2; all workgroups
-  // move through the list in step.  (Claiming items from a counter instead balances the end better but loses
-  // that locality, and the clock drops with the extra off-XCD traffic: measured slower.)
-  int bid = blockIdx.x - a.n_cons;
-  if ((G & 7) == 0 && (a.n_cons & 7) == 0) bid = (bid & 7) * (G >> 3) + (bid >> 3);
+  const int C = a.n_cons, G = gridDim.x - C;
   bool first = true;
-  for (int item = bid; item < n_items; item += G) {
+  auto run = [&](int item) {  // one item of the list; false once the launch has failed
     __syncthreads();  // previous item done with LDS and the header
     const FfnItem it = ffn_item(item, n_mt, a.window, a.n_nt1, a.n_nt2, a.S, a.interleave != 0);
     if (tid < MOE_MT_FIELDS) {
@@ -743,20 +770,49 @@ __global__ __launch_bounds__(256, 1) void k_ffn_bf16(FusedArgs a) {
     first = false;
     __syncthreads();
     const int e = __builtin_amdgcn_readfirstlane(s_hdr[0]), n_sub = __builtin_amdgcn_readfirstlane(s_hdr[1]);
-    bool ok;
-    if (it.kind == 1) {
-      ok = ffn_tile<BN1, true>(a, smem, s_sub, e, n_sub, it.mt, it.nt, 0, &s_stop);
-    } else {
-      // the h columns this split reads: column tiles [s, s+1) * n_nt1 / S of the first GEMM
-      const int per = a.n_nt1 / a.S;
-      ok = wait_flags(a.flags1 + (int64_t)it.mt * a.n_nt1 + it.s * per, per, a.epoch, a.budget, a.status, &s_stop) &&
+    if (it.kind == 1) return ffn_tile<BN1, true>(a, smem, s_sub, e, n_sub, it.mt, it.nt, 0, &s_stop);
+    // the h columns this split reads: column tiles [s, s+1) * n_nt1 / S of the first GEMM
+    const int per = a.n_nt1 / a.S;
+    return wait_flags(a.flags1 + (int64_t)it.mt * a.n_nt1 + it.s * per, per, a.epoch, a.budget, a.status, &s_stop) &&
            ffn_tile<BN2, false>(a, smem, s_sub, e, n_sub, it.mt, it.nt, it.s, &s_stop);
-    }
-    if (!ok) return;
+  };
+  // With every GEMM1 item first, no row tile is returned before the GEMM1 part of the list is done, so the
+  // consumer workgroups first take kc GEMM1 items each from the head of the list: just enough that the producers'
+  // share fits in as few rounds as the whole list would on all workgroups, and no more than the consumers finish
+  // before the GEMM1 part ends.  GEMM1 items wait on nothing, so the consumer's later waits still end.
+  int kc = 0;
+  if (C > 0 && a.interleave == 0) {
+    const int rounds = (n_items + G + C - 1) / (G + C), over = n_items - rounds * G;
+    kc = over > 0 ? (over + C - 1) / C : 0;
+    kc = min(kc, n_mt * a.n_nt1 / (G + C));
   }
+  // A producer workgroup b takes items b', b' + G, ... after the consumers' share, b' remapped so that a run of
+  // consecutive items goes to the workgroups of one XCD (workgroup b sits on XCD b % 8), which share operand tiles
+  // in its L2; all workgroups move through the list in step.  (Claiming items from a counter instead balances the
+  // end better but loses that locality, and the clock drops with the extra off-XCD traffic: measured slower.)
+  const bool cons = (int)blockIdx.x < C;
+  int i0, i1, step;
+  if (cons) {
+    i0 = (int)blockIdx.x * kc;
+    i1 = i0 + kc;
+    step = 1;
+  } else {
+    int bid = blockIdx.x - C;
+    if ((G & 7) == 0 && (C & 7) == 0) bid = (bid & 7) * (G >> 3) + (bid >> 3);
+    i0 = C * kc + bid;
+    i1 = n_items;
+    step = G;
+  }
+  for (int item = i0; item < i1; item += step)
+    if (!run(item)) return;
+  // then every workgroup returns segments until no copy unit is left
+  if (C > 0) consumer_role(a.cons);
 }
 
-__global__ __launch_bounds__(256) void k_consumer(ConsumerArgs c) { consumer_role(c, blockIdx.x, gridDim.x); }
+__global__ __launch_bounds__(256) void k_consumer(ConsumerArgs c) {
+  if (blockIdx.x == 0) consumer_stamp(c);
+  consumer_role(c);
+}
 
 // ---- tile configurations --------------------------------------------------------------------------------
 #define BF_BM 256
@@ -789,23 +845,34 @@ int ffn_splits(int dtype, int d, int f) {
 
 namespace {
 struct FlagCarve {
-  int64_t flags2, flags1, scount, partial, total;  // offsets and size in 4-byte words
+  int64_t flags2, flags1, scount, partial, claim, total;  // offsets and size in 4-byte words
 };
 FlagCarve flag_carve(int dtype, int d, int f, int64_t cap_mtiles) {
   FlagCarve c;
   const int64_t n2 = d / ffn_gemm2_bn(dtype, d);
+  auto up = [](int64_t v) { return (v + 63) / 64 * 64; };
   c.flags2 = 0;
   if (dtype != MOE_BF16) {
-    c.flags1 = c.scount = c.partial = c.total = cap_mtiles * n2;
-    return c;
+    c.flags1 = c.scount = c.partial = cap_mtiles * n2;
+    c.claim = up(c.partial);
+  } else {
+    const int64_t n1 = f / (gemm1_bn(dtype, f) / 2), S = ffn_splits(dtype, d, f);
+    c.flags1 = up(cap_mtiles * n2);
+    c.scount = c.flags1 + up(cap_mtiles * n1);
+    c.partial = c.scount + up(S > 1 ? 2 * cap_mtiles * n2 : 0);
+    c.claim = c.partial + (S > 1 ? cap_mtiles * n2 * S * (int64_t)BF_BM * ffn_gemm2_bn(dtype, d) : 0);
   }
-  const int64_t n1 = f / (gemm1_bn(dtype, f) / 2), S = ffn_splits(dtype, d, f);
-  auto up = [](int64_t v) { return (v + 63) / 64 * 64; };
-  c.flags1 = up(cap_mtiles * n2);
-  c.scount = c.flags1 + up(cap_mtiles * n1);
-  c.partial = c.scount + up(S > 1 ? 2 * cap_mtiles * n2 : 0);
-  c.total = c.partial + (S > 1 ? cap_mtiles * n2 * S * (int64_t)BF_BM * ffn_gemm2_bn(dtype, d) : 0);
+  c.total = c.claim + 2;  // the consumer's 64-bit unit counter
   return c;
+}
+
+// A nonzero value distinct for every launch that runs the consumer role (the unit counter's stamp).
+uint32_t next_stamp() {
+  static std::atomic<uint32_t> seq{0};
+  uint32_t v;
+  do v = ++seq;
+  while (v == 0);
+  return v;
 }
 
 void fill_consumer(ConsumerArgs& c, const FfnLaunch& p, int n_nt2) {
@@ -817,6 +884,8 @@ void fill_consumer(ConsumerArgs& c, const FfnLaunch& p, int n_nt2) {
   c.scalars = p.L->scalars;
   c.status = p.L->status;
   c.flags = p.flags;
+  c.claim = (uint64_t*)(p.flags + flag_carve(p.dtype, p.d, p.f, p.cap_mtiles).claim);
+  c.stamp = next_stamp();
   c.epoch = p.epoch;
   c.n_nt = n_nt2;
   c.row_vec = p.d * (p.dtype == MOE_BF16 ? 2 : 4) / 16;

@@ -93,8 +93,9 @@ typedef struct {
   int32_t consumer_cus;    /* C: consumer workgroups, one per CU, in [1, CUs/2]; the producer's persistent
                               launch runs one workgroup on each other CU */
   int32_t mode;            /* 0 = overlapped (the C consumer workgroups and the producer workgroups in one
-                                  launch, on disjoint CUs),
-                              1 = sequential (producer on all CUs, then the consumer),
+                                  launch, on disjoint CUs; a producer workgroup joins the return once its
+                                  own items are done),
+                              1 = sequential (producer on all CUs, then the return on all CUs),
                               2 = return only (the consumer alone, on consumer_cus workgroups, for flags
                                   already published with this epoch; a flag never published ends in the
                                   watchdog) */
@@ -108,7 +109,7 @@ typedef struct {
                               workgroup exits */
   uint64_t* timestamps;    /* optional (device) [2 + 2*cap_tiles] u64, 100 MHz clock: [0] first producer
                               item start, [1] last flag publish, [2+2s] / [3+2s] first copy start / last copy
-                              end of segment s over the consumer workgroups; reset by the call; NULL to
+                              end of segment s over the workgroups that copy it; reset by the call; NULL to
                               skip */
 } moe_overlap_cfg;
 
@@ -156,7 +157,8 @@ int moe_read_status(const moe_layout* L, void* stream);
  * holds the readiness flags of the second GEMM's output tiles (what the consumer waits on), and for bf16 the
  * flags of the first GEMM's h tiles, an arrival counter per output tile of the second GEMM and the fp32 partial
  * sums of its k-splits (256 x 256 floats per output tile and split; f/d rounded gives the number of splits, up
- * to 8).  Zero the buffer once before the first call; afterwards it is epoch-valued. */
+ * to 8); last, one 64-bit counter of the return's copy units.  Zero the buffer once before the first call;
+ * afterwards it is epoch-valued. */
 int64_t moe_ffn_flags_count(const moe_shape* s);
 
 /* Expert SwiGLU FFN over the padded layout with the return of each finished row-band segment to its
@@ -165,17 +167,20 @@ int64_t moe_ffn_flags_count(const moe_shape* s);
  *   Wg = rows [0, f) and Wu = rows [f, 2f) of w_gate_up[e].
  * The producer is one persistent launch over all local experts (bf16): tiles of h, then k-splits of y tiles,
  * window by window in remote-first row-tile order; a tile other workgroups read is published with an
- * epoch-valued flag once its stores are complete and visible device-wide.  The consumer waits for the flags
- * of a segment's row tiles, acquires, and copies the segment's real rows into recv[owner].
- *   mode 0 (overlapped): the consumer is the first consumer_cus workgroups of the producer launch;
- *   mode 1 (sequential): producer on every CU, then the consumer alone;
+ * epoch-valued flag once its stores are complete and visible device-wide.  The return is cut into copy units
+ * of up to 128 KB of a segment, handed out in the order the segments complete: a workgroup in the consumer
+ * role takes the next unit, waits for the flags of its segment's row tiles, acquires, and copies the unit's
+ * rows into recv[owner].
+ *   mode 0 (overlapped): the consumer is the first consumer_cus workgroups of the producer launch, and every
+ *     producer workgroup joins it once its own items are done;
+ *   mode 1 (sequential): producer on every CU, then the return alone on every CU;
  *   mode 2: the consumer alone (return only; for tests of the wait).
  * fp32 runs the two GEMMs as two launches (consumer inside the second).  Owner r receives, at row
  * recv_off_{e,r} + i, the FFN output of the i-th row of group (e, r); results are identical in every mode.
  * x_pad (device) [cap_rows, d]; w_gate_up (device) [E_l, 2f, d]; w_down (device) [E_l, d, f];
  * h_ws (device) [cap_rows, f] workspace; y_pad (device) [cap_rows, d]; recv: host array of R device
- * pointers, recv[r] holds >= N_r rows of d; flags (device) [moe_ffn_flags_count] 4-byte words (zeroed before
- * the first call); cfg: see moe_overlap_cfg.  Waits inside the launch are bounded by cfg->watchdog_ticks;
+ * pointers, recv[r] holds >= N_r rows of d; flags (device, 8-byte aligned) [moe_ffn_flags_count] 4-byte
+ * words (zeroed before the first call); cfg: see moe_overlap_cfg.  Waits inside the launch are bounded by cfg->watchdog_ticks;
  * on expiry the status word becomes MOE_ETIMEOUT. */
 int moe_expert_ffn_overlap(const moe_shape* s, const moe_layout* L, const void* x_pad, const void* w_gate_up,
                            const void* w_down, void* h_ws, void* y_pad, void* const* recv, uint32_t* flags,

@@ -136,6 +136,10 @@ SMALL = [
     mi.Spec("f32_ragged", R=3, T_o=90, G=9, E_l=3, k=2, d=128, f=192, M=32, dtype="f32", seed=15),
     # f = 4 d: the second GEMM's output tiles are summed from 4 k-splits (ragged row tiles, two windows)
     mi.Spec("splitk", R=4, T_o=600, G=8, E_l=2, k=2, d=256, f=1024, M=32, seed=16),
+    # f = 2 d, 3 d and 6 d: 2, 3 and 6 k-splits (the last summed by the general loop)
+    mi.Spec("splitk2", R=4, T_o=300, G=8, E_l=2, k=2, d=256, f=512, M=32, seed=17),
+    mi.Spec("splitk3", R=2, T_o=500, G=8, E_l=2, k=2, d=256, f=768, M=64, seed=18),
+    mi.Spec("splitk6", R=3, T_o=200, G=6, E_l=2, k=1, d=256, f=1536, M=16, seed=19),
 ]
 
 
