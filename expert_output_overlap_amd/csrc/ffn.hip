@@ -922,11 +922,15 @@ int launch_bf16(const FfnLaunch& p, int grid, int n_cons, hipStream_t st) {
   a.n_nt2 = p.d / bn2;
   a.S = ffn_splits(p.dtype, p.d, p.f);
   a.window = p.band_window > 0 ? p.band_window : 4;
-  // Interleave when the return is large next to the FFN.  At about 45 GB/s of copy per consumer CU and 0.8
-  // PFLOP/s of FFN, copy time / FFN time = 4 M d / (45e9 C) / (6 M d f / 0.8e15) ~= 11850 / (C f), whatever M
-  // and d are; GEMM1 first (faster, weights streamed once) leaves the last third of the launch for the copies,
-  // so it is used while that ratio stays under about 1/4.
-  a.interleave = n_cons > 0 && (int64_t)n_cons * p.f < 48000;
+  // Interleave when the return is large next to the FFN and re-streaming weights is cheap.  At about 45 GB/s of
+  // copy per consumer CU and 0.8 PFLOP/s of FFN, copy time / FFN time = 4 M d / (45e9 C) / (6 M d f / 0.8e15)
+  // ~= 11850 / (C f), whatever M and d are; GEMM1 first leaves the last part of the launch for the copies, and
+  // the workgroups that finish early help with what is left, so it is used while that ratio stays under about
+  // 1/4.  Interleaved windows stream an expert's weight tiles once per window holding its rows, and consecutive
+  // items share fewer of them, which pays only while the local experts' weights (3 d f per expert) fit in the
+  // 256 MB last-level cache; measured: 1 and 2 experts of d = f = 4096 gain, 4 or more lose.
+  const double w_bytes = 3.0 * p.d * p.f * 2.0 * p.E;
+  a.interleave = n_cons > 0 && (int64_t)n_cons * p.f < 48000 && w_bytes <= 256.0 * 1024 * 1024;
   a.mtile_desc = p.L->mtile_desc;
   a.scalars = p.L->scalars;
   a.sc_nmt = SC_NR + p.R;

@@ -59,7 +59,8 @@ class Run:
         bf = s.dtype == "bf16"
         ex = oracle.ffn_rows_ex(lay["row_src"][rows], lay["tile_expert"][rows // s.M], self.inp["x"],
                                 self.inp["w_gate_up"], self.inp["w_down"], bf)
-        ref, flips = tolerance.check_ffn(f64(self.P.y_pad)[rows], ex, what, bf)
+        got = f64(self.P.y_pad[torch.as_tensor(np.asarray(rows), dtype=torch.long, device=self.P.y_pad.device)])
+        ref, flips = tolerance.check_ffn(got, ex, what, bf)
         print("%s: %d rows, %d alternative h roundings taken" % (what, len(rows), flips), flush=True)
         return ref
 
