@@ -167,8 +167,10 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
   }
 
   // (e) remote-first order of non-empty groups: key (owner == self, -P, e, r) ascending (bands, segments);
-  // row-tile packing order: key (owner == self, e, -P, r), remote groups first and each expert's groups together
-  // so that a GEMM row tile (one expert) packs as many sub-blocks as possible.  Both keys are packed into one
+  // row-tile packing order: key (e, owner == self, -P, r): each expert's groups together, so that a GEMM row tile
+  // (one expert) packs as many sub-blocks as possible, and inside an expert the self-owned group last.  (Keeping
+  // every self-owned group behind all remote ones instead gives each expert a second, mostly empty tile when R is
+  // large: 142 row tiles instead of about 100 for 32 experts and 8 owners.)  Both keys are packed into one
   // unsigned 64-bit value per group (unique, since (e, r) is), so a group's rank is the count of smaller keys.
   {
     uint64_t* key1 = s_scratch;
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
       const int g = tid, e = g / R, r = g - e * R;
       const uint64_t self = r == a.self_rank, nP = (uint64_t)((1 << 30) - ((s_n[g] + M - 1) / M) * M);
       k1 = (self << 63) | (nP << 32) | ((uint64_t)e << 16) | (uint64_t)r;
-      k2 = (self << 63) | ((uint64_t)e << 50) | (nP << 16) | (uint64_t)r;
+      k2 = ((uint64_t)e << 50) | (self << 49) | (nP << 16) | (uint64_t)r;
     }
     if (tid < NG) {
       key1[tid] = k1;
