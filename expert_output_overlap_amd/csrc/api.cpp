@@ -94,7 +94,7 @@ Offsets layout_offsets(const moe_shape* s) {
   o.combine_plan = c.take(T * s->top_k, 4);
   o.scalars = c.take(4 + s->R, 4);
   o.status = c.take(1, 4);
-  o.mtile_desc = c.take(o.cap_mtiles * (2 + 16), 4);
+  o.mtile_desc = c.take(o.cap_mtiles * (4 + 16), 4);
   o.seg_mtiles = c.take(o.cap_tiles * 2, 4);
   o.seg_sched = c.take(o.cap_tiles, 4);
   o.chunk_counts = c.take((int64_t)s->R * n_chunks * s->num_local_experts, 4);

@@ -90,7 +90,7 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm(GemmArgs a) {
   __shared__ __align__(16) T sA[2][BM * LDK];
   __shared__ __align__(16) T sB[2][BN * LDK];
   __shared__ int s_sub[MOE_MT_SUB];
-  __shared__ int s_hdr[2];
+  __shared__ int s_hdr[MOE_MT_HDR];
 
   if (PUBLISH && a.n_cons > 0 && blockIdx.x == 0) consumer_stamp(a.cons);
   if (PUBLISH && (int)blockIdx.x < a.n_cons) {
@@ -125,8 +125,8 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm(GemmArgs a) {
     __syncthreads();  // previous item finished with LDS and the header
     if (tid < MOE_MT_FIELDS) {
       const int v = a.mtile_desc[(int64_t)mt * MOE_MT_FIELDS + tid];
-      if (tid < 2) s_hdr[tid] = v;
-      else s_sub[tid - 2] = v;
+      if (tid < MOE_MT_HDR) s_hdr[tid] = v;
+      else s_sub[tid - MOE_MT_HDR] = v;
     }
     if (PUBLISH && a.ts != nullptr && first && tid == 0)
       atomicMin((unsigned long long*)&a.ts[0], (unsigned long long)moe_clock());
@@ -338,12 +338,13 @@ struct FfnItem {
   int mt, nt, s;
 };
 
-// Item i of the list, in one of two orders over windows of W row tiles (remote-first row-tile order); inside a
+// Item i of the list, in one of two orders over windows of W row tiles (row tiles expert by expert); inside a
 // window, GEMM1 items are column-tile major (consecutive items share a weight tile) and GEMM2 items split-major,
 // then column-tile major.
-//  - GEMM1 first: every GEMM1 item (one window over all row tiles: each gate/up weight tile streamed once), then
-//    the GEMM2 windows.  A GEMM2 split reads only its own share of h's columns, which the first part of the GEMM1
-//    list produced; row tiles complete window after window during the last part of the launch.
+//  - GEMM1 first: every GEMM1 item (each gate/up weight tile streamed once; the kernel lists them expert by
+//    expert itself, from the row tiles' run fields, and uses this function for the rest), then the GEMM2
+//    windows.  A GEMM2 split reads only its own share of h's columns, which the first part of the GEMM1 list
+//    produced; row tiles complete window after window during the last part of the launch.
 //  - interleaved: G1(0), G1(1), G2(0), G1(2), G2(1), ..., G1(nw-1), G2(nw-2), G2(nw-1): row tiles complete
 //    window after window over the whole launch, so a return that is large next to the FFN starts early.
 // In both, every GEMM2 item follows the GEMM1 items it reads and the last split of a tile follows its others.
@@ -748,7 +749,7 @@ __global__ __launch_bounds__(256, 1) void k_ffn_bf16(FusedArgs a) {
   static_assert(BM * BN2 * 2 <= 2 * STAGE && BM * BN1 <= 2 * STAGE, "output staging fits the operand stages");
   __shared__ __align__(1024) unsigned char smem[2 * STAGE];
   __shared__ int s_sub[MOE_MT_SUB];
-  __shared__ int s_hdr[2];
+  __shared__ int s_hdr[MOE_MT_HDR];
   __shared__ int s_stop;
 
   if (load_status(a.status) != 0) return;
@@ -760,11 +761,25 @@ __global__ __launch_bounds__(256, 1) void k_ffn_bf16(FusedArgs a) {
   bool first = true;
   auto run = [&](int item) {  // one item of the list; false once the launch has failed
     __syncthreads();  // previous item done with LDS and the header
-    const FfnItem it = ffn_item(item, n_mt, a.window, a.n_nt1, a.n_nt2, a.S, a.interleave != 0);
+    FfnItem it;
+    if (a.interleave == 0 && item < n_mt * a.n_nt1) {
+      // GEMM1 part of the list with every GEMM1 item first: expert by expert (each expert's row tiles are one run
+      // of consecutive tiles), column-tile major inside an expert, so that a run of consecutive items -- one
+      // XCD's share of a round -- reads few distinct weight and row tiles.  Item i lies in the run of row tile
+      // i / n_nt1, since a run of c tiles holds c * n_nt1 items.
+      const int32_t* d = a.mtile_desc + (int64_t)(item / a.n_nt1) * MOE_MT_FIELDS;
+      const int r0 = d[2], rc = d[3], j = item - r0 * a.n_nt1;
+      it.kind = 1;
+      it.nt = j / rc;
+      it.mt = r0 + (j - it.nt * rc);
+      it.s = 0;
+    } else {
+      it = ffn_item(item, n_mt, a.window, a.n_nt1, a.n_nt2, a.S, a.interleave != 0);
+    }
     if (tid < MOE_MT_FIELDS) {
       const int v = a.mtile_desc[(int64_t)it.mt * MOE_MT_FIELDS + tid];
-      if (tid < 2) s_hdr[tid] = v;
-      else s_sub[tid - 2] = v;
+      if (tid < MOE_MT_HDR) s_hdr[tid] = v;
+      else s_sub[tid - MOE_MT_HDR] = v;
     }
     if (a.ts != nullptr && first && tid == 0) atomicMin((unsigned long long*)&a.ts[0], (unsigned long long)moe_clock());
     first = false;

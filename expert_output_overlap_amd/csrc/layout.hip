@@ -306,12 +306,14 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
     const int g = s_order2[q2], j = pos - s_sub_pos[q2], u = s_run_off[q2] + j;
     int32_t* d = a.mtile_desc + (int64_t)(s_tile_base[q2] + (u >> mt_shift)) * MOE_MT_FIELDS;
     const int slot = u & mt_mask;
-    d[2 + slot] = s_poff[g] + MOE_SUB * j;
+    d[MOE_MT_HDR + slot] = s_poff[g] + MOE_SUB * j;
     if (slot == 0) {
       const int left = s_run_subs[q2] - u, cnt = left < a.mt_sub ? left : a.mt_sub;
       d[0] = g / R;
       d[1] = cnt;
-      for (int s2 = cnt; s2 < MOE_MT_SUB; ++s2) d[2 + s2] = -1;
+      d[2] = s_tile_base[q2];
+      d[3] = (s_run_subs[q2] + a.mt_sub - 1) >> mt_shift;
+      for (int s2 = cnt; s2 < MOE_MT_SUB; ++s2) d[MOE_MT_HDR + s2] = -1;
     }
   }
   for (int sp = tid; sp < n_segs; sp += SCAN_THREADS) {
