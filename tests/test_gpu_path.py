@@ -50,7 +50,7 @@ class Run:
         self.lay = oracle.layout(self.idx, s.R, s.T_o, s.G, s.E_l, s.k, s.M, s.mgb, 0)
 
     def ffn(self, **kw):
-        self.P.ffn(self.dev["w_gate_up"], self.dev["w_down"], **kw)
+        return self.P.ffn(self.dev["w_gate_up"], self.dev["w_down"], **kw)
 
     def check_rows(self, rows, what="y"):
         """Check the GPU's y at padded rows ``rows`` (real rows) against the oracle, up to the oracle's own
@@ -146,6 +146,8 @@ SMALL = [
     mi.Spec("splitk2", R=4, T_o=300, G=8, E_l=2, k=2, d=256, f=512, M=32, seed=17),
     mi.Spec("splitk3", R=2, T_o=500, G=8, E_l=2, k=2, d=256, f=768, M=64, seed=18),
     mi.Spec("splitk6", R=3, T_o=200, G=6, E_l=2, k=1, d=256, f=1536, M=16, seed=19),
+    # fp32 with more transfer segments than a 128-thread consumer workgroup holds in its window at once
+    mi.Spec("f32_many_segs", R=8, T_o=400, G=32, E_l=16, k=2, d=128, f=128, M=16, dtype="f32", seed=20),
 ]
 
 
@@ -281,6 +283,30 @@ def test_no_stale_reads_across_calls(name):
     for r in range(s.R):
         n_r = int(run.lay["N_r"][r])
         np.testing.assert_array_equal(bits(run.P.recv[r])[:n_r], bits(fresh.recv[r])[:n_r])
+
+
+@pytest.mark.parametrize("name", ["tiny", "splitk"])
+def test_return_only_repeats(name):
+    """The return alone, for flags an overlapped call already published, delivers the same rows again, call after
+    call and whatever the partition: every launch hands out its copy units afresh (a new stamp on the counter)."""
+    s = [c for c in SMALL if c.name == name][0]
+    run = Run(s)
+    for r in range(s.R):
+        run.P.recv[r].fill_(float("nan"))
+    epoch = run.ffn(mode=0, consumer_cus=4)
+    torch.cuda.synchronize()
+    assert run.P.status() == B.MOE_OK
+    check_delivery(run)
+    ref = [bits(b) for b in run.P.recv]
+    for cus in (3, 16, 1):
+        for r in range(s.R):
+            run.P.recv[r].fill_(float("nan"))
+        run.P.ffn(run.dev["w_gate_up"], run.dev["w_down"], mode=2, consumer_cus=cus, epoch=epoch)
+        torch.cuda.synchronize()
+        assert run.P.status() == B.MOE_OK
+        check_delivery(run)
+        for a, b in zip(ref, run.P.recv):
+            np.testing.assert_array_equal(a, bits(b))
 
 
 def test_watchdog_ends_a_wait_that_never_ends():
