@@ -78,8 +78,8 @@ Offsets layout_offsets(const moe_shape* s) {
   const int64_t T = (int64_t)s->R * s->tokens_per_owner;
   o.cap_rows = capacity_rows(s);
   o.cap_tiles = o.cap_rows / s->tile_m;
-  const int mt_sub = ffn_gemm_bm(s->dtype) / 16;
-  o.cap_mtiles = (o.cap_rows / 16 + mt_sub - 1) / mt_sub + NG + 1;
+  const int mt_rows = ffn_gemm_bm(s->dtype);
+  o.cap_mtiles = (o.cap_rows + mt_rows - 1) / mt_rows + NG + 1;
   const int64_t n_chunks = (s->tokens_per_owner + 63) / 64;
   Carve c;
   o.counts = c.take(NG, 4);
@@ -94,7 +94,7 @@ Offsets layout_offsets(const moe_shape* s) {
   o.combine_plan = c.take(T * s->top_k, 4);
   o.scalars = c.take(4 + s->R, 4);
   o.status = c.take(1, 4);
-  o.mtile_desc = c.take(o.cap_mtiles * (4 + 16), 4);
+  o.mtile_desc = c.take(o.cap_mtiles * (4 + 256), 4);
   o.seg_mtiles = c.take(o.cap_tiles * 2, 4);
   o.seg_sched = c.take(o.cap_tiles, 4);
   o.chunk_counts = c.take((int64_t)s->R * n_chunks * s->num_local_experts, 4);
@@ -238,7 +238,7 @@ int moe_layout_build(const moe_shape* s, const int32_t* topk_idx, const void* x,
   p.M = s->tile_m;
   p.mgb = s->seg_bands;
   p.self_rank = s->self_rank;
-  p.mt_sub = ffn_gemm_bm(s->dtype) / 16;
+  p.mt_rows = ffn_gemm_bm(s->dtype);
   p.row_bytes = (int64_t)s->d * (s->dtype == MOE_BF16 ? 2 : 4);
   if (launch_layout(p, (hipStream_t)stream)) return fail(MOE_EHIP, "layout launch failed");
   return MOE_OK;

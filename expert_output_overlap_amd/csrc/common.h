@@ -8,13 +8,12 @@
 
 #define MOE_WAVE 64
 
-// GEMM row tile: up to MOE_MT_SUB sub-blocks of MOE_SUB rows of one expert.  Descriptor fields: expert,
-// sub-block count, first row tile and row-tile count of the expert's run (its row tiles are consecutive), then
-// the sub-block starts.
-#define MOE_SUB 16
-#define MOE_MT_SUB 16
+// GEMM row tile: up to MOE_MT_ROWS real rows of one expert (the kernel's tile height: 256 bf16, 64 fp32).
+// Descriptor fields: expert, row count, first row tile and row-tile count of the expert's run (its row tiles are
+// consecutive), then the rows' positions in the padded layout (-1 past the row count).
+#define MOE_MT_ROWS 256
 #define MOE_MT_HDR 4
-#define MOE_MT_FIELDS (MOE_MT_HDR + MOE_MT_SUB)
+#define MOE_MT_FIELDS (MOE_MT_HDR + MOE_MT_ROWS)
 
 // scalars[] indices
 #define SC_MPAD 0

@@ -8,8 +8,8 @@
 //                 workgroups of this launch are the consumer partition instead (consumer.h): round-robin
 //                 dispatch puts workgroup b on XCD b % 8, so C consumers spread over the XCDs, one per CU,
 //                 and the producer and consumer are co-resident by construction.
-// Row tiles are the layout's GEMM row tiles: up to BM/16 sub-blocks of 16 rows of one expert, walked in
-// the remote-first group order, so all-padding sub-blocks cost nothing.  Items (row tile, column tile)
+// Row tiles are the layout's GEMM row tiles: up to BM real rows of one expert, each expert's rows packed into
+// consecutive tiles, so padding rows cost nothing.  Items (row tile, column tile)
 // are visited window by window (band_window row tiles, column-tile-major inside a window) for weight
 // reuse, and consecutive items go to workgroups on the same XCD.
 #include <atomic>
@@ -85,11 +85,11 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm(GemmArgs a) {
   constexpr int PA = BM / RPP, PB = BN / RPP;
   constexpr int OUT_BN = GLU ? BN / 2 : BN;  // output columns per tile
   static_assert(!GLU || NI % 2 == 0, "GLU pairs gate and up blocks");
-  static_assert(BM % RPP == 0 && BN % RPP == 0 && BM / 16 <= MOE_MT_SUB, "tile shape");
+  static_assert(BM % RPP == 0 && BN % RPP == 0 && BM <= MOE_MT_ROWS, "tile shape");
 
   __shared__ __align__(16) T sA[2][BM * LDK];
   __shared__ __align__(16) T sB[2][BN * LDK];
-  __shared__ int s_sub[MOE_MT_SUB];
+  __shared__ int s_rows[BM];
   __shared__ int s_hdr[MOE_MT_HDR];
 
   if (PUBLISH && a.n_cons > 0 && blockIdx.x == 0) consumer_stamp(a.cons);
@@ -123,23 +123,22 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm(GemmArgs a) {
     const int nt = j / Wc, mt = mt0 + (j - nt * Wc);
 
     __syncthreads();  // previous item finished with LDS and the header
-    if (tid < MOE_MT_FIELDS) {
-      const int v = a.mtile_desc[(int64_t)mt * MOE_MT_FIELDS + tid];
-      if (tid < MOE_MT_HDR) s_hdr[tid] = v;
-      else s_sub[tid - MOE_MT_HDR] = v;
+    {
+      const int32_t* dsc = a.mtile_desc + (int64_t)mt * MOE_MT_FIELDS;
+      if (tid < MOE_MT_HDR) s_hdr[tid] = dsc[tid];
+      for (int i = tid; i < BM; i += NTHR) s_rows[i] = dsc[MOE_MT_HDR + i];
     }
     if (PUBLISH && a.ts != nullptr && first && tid == 0)
       atomicMin((unsigned long long*)&a.ts[0], (unsigned long long)moe_clock());
     first = false;
     __syncthreads();
-    const int e = s_hdr[0], n_sub = s_hdr[1];
+    const int e = s_hdr[0], n_rows = s_hdr[1];
 
     const T* pa[PA];
 #pragma unroll
     for (int p = 0; p < PA; ++p) {
       const int r = p * RPP + cr;
-      const int sub = r >> 4;
-      pa[p] = A + (int64_t)(sub < n_sub ? s_sub[sub] + (r & 15) : 0) * K + cc;
+      pa[p] = A + (int64_t)(r < n_rows ? s_rows[r] : s_rows[0]) * K + cc;  // absent rows read a real row
     }
     const T* pb[PB];
     const T* wbase = Wt + (int64_t)e * a.w_rows * K;
@@ -153,7 +152,7 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm(GemmArgs a) {
     }
     bool mvalid[MI];
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) mvalid[mi] = ((wm * WM + mi * 32) >> 4) < n_sub;
+    for (int mi = 0; mi < MI; ++mi) mvalid[mi] = wm * WM + mi * 32 < n_rows;
 
     f32x16_t acc[MI][NI];
 #pragma unroll
@@ -163,8 +162,8 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm(GemmArgs a) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.f;
 
-    // Rows of absent sub-blocks read row 0 of the tile's source instead (always allocated); their outputs are
-    // never stored, and rows are independent in both GEMMs.
+    // Absent rows (past the tile's row count) read the tile's first row instead; their outputs are never
+    // stored, and rows are independent in both GEMMs.
     {
       u32x4_t ra[PA], rb[PB];
 #pragma unroll
@@ -221,7 +220,7 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm(GemmArgs a) {
       __syncthreads();
     }
 
-    // epilogue: store the tile's real sub-blocks (padding rows inside a present sub-block included)
+    // epilogue: store the tile's real rows
     constexpr int NO = GLU ? NI / 2 : NI;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
@@ -232,9 +231,8 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm(GemmArgs a) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           const int row = wm * WM + mi * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
-          const int sub = row >> 4;
-          if (sub < n_sub) {
-            const int64_t grow = s_sub[sub] + (row & 15);
+          if (row < n_rows) {
+            const int64_t grow = s_rows[row];
             float v = acc[mi][ni][q];
             if (GLU) v = silu_f32(v) * acc[mi][ni + NI / 2][q];
             C[grow * a.ldc + col] = Tr::out(v);
@@ -456,11 +454,11 @@ __device__ __forceinline__ uint32_t arrive(uint64_t* ctr, uint32_t epoch) {
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x8_t __attribute__((ext_vector_type(8)));
 
-// One item: output tile (row tile with sub-block rows s_sub[0, n_sub) of expert e, column tile nt), k-tiles of
+// One item: output tile (row tile with rows s_rows[0, n_rows) of expert e, column tile nt), k-tiles of
 // split s.  GLU: the first GEMM (A = x_pad rows, B = gate rows nt*BN/2.. and up rows f + nt*BN/2..); else the
 // second (A = h rows, B = down-projection rows nt*BN..).  False if a wait gave up (the workgroup must exit).
 template <int BN, bool GLU>
-__device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem, const int* s_sub, int e, int n_sub,
+__device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem, const int* s_rows, int e, int n_rows,
                                          int mt, int nt, int s, int* s_stop) {
   constexpr int BM = 256, BK = 64;
   constexpr int WM = 128, WN = BN / 2, MI = WM / 32, NI = WN / 32;
@@ -498,8 +496,7 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
   for (int jj = 0; jj < A_LOADS; ++jj) {
     const int q = wave * A_LOADS + jj;
     const int r = 8 * q + (lane >> 3);
-    const int sub = r >> 4;
-    const int row = sub < n_sub ? s_sub[sub] + (r & 15) : s_sub[0];  // absent sub-blocks read a real row
+    const int row = r < n_rows ? s_rows[r] : s_rows[0];  // absent rows read a real row
     aoff[jj] = (uint32_t)row * row_bytes + (chunk0 ^ ((uint32_t)(q & 1) << 4));
   }
   const unsigned char* wbase = Wb + (int64_t)e * w_rows * row_bytes + (uint32_t)kt0 * (BK * 2);
@@ -520,8 +517,8 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.f;
 
-  // 32-row MFMA blocks of this wave that hold present sub-blocks: all MI except in a tile's ragged tail
-  const int mact = min(MI, max(0, (n_sub * 16 - wm * WM + 31) / 32));
+  // 32-row MFMA blocks of this wave that hold real rows: all MI except in the last tile of an expert's run
+  const int mact = min(MI, max(0, (n_rows - wm * WM + 31) / 32));
   auto kloop = [&](auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
     // slots of a k-step: MFMA i (if i < MI*NI), then fragment read i (if i < MI+NI), then loads; the loads go
@@ -613,8 +610,8 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
   if (mact == MI) kloop(std::true_type{});
   else kloop(std::false_type{});
   // epilogue: every wave writes its bf16 outputs into LDS as a 256 x OUT_BN tile (16-byte chunk ch of row r at
-  // chunk ch ^ (r & 7), so neither the column writes nor the row reads collide), then 16-byte stores of the rows
-  // of present sub-blocks (padding rows inside them included, never read for a result)
+  // chunk ch ^ (r & 7), so neither the column writes nor the row reads collide), then 16-byte stores of the
+  // tile's real rows
   constexpr int NO = GLU ? NI / 2 : NI;
   constexpr int OUT_ROW = OUT_BN * 2, CPR = OUT_ROW / 16;
   // the thread index, made opaque here, so that the many epilogue addresses are computed per item instead of
@@ -728,9 +725,8 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
     }
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
-      const int idx = tid_e + (i0 + u) * 256, row = idx / CPR, ch = idx - row * CPR, sub = row >> 4;
-      if (sub < n_sub)
-        store16_coherent(Cb + ((s_sub[sub] + (row & 15)) * ldc + (int64_t)nt * OUT_BN) * 2 + ch * 16, v[u]);
+      const int idx = tid_e + (i0 + u) * 256, row = idx / CPR, ch = idx - row * CPR;
+      if (row < n_rows) store16_coherent(Cb + ((int64_t)s_rows[row] * ldc + (int64_t)nt * OUT_BN) * 2 + ch * 16, v[u]);
     }
   }
   if (GLU) {
@@ -748,7 +744,7 @@ __global__ __launch_bounds__(256, 1) void k_ffn_bf16(FusedArgs a) {
   constexpr int STAGE = (BM + BNX) * BK * 2;
   static_assert(BM * BN2 * 2 <= 2 * STAGE && BM * BN1 <= 2 * STAGE, "output staging fits the operand stages");
   __shared__ __align__(1024) unsigned char smem[2 * STAGE];
-  __shared__ int s_sub[MOE_MT_SUB];
+  __shared__ int s_rows[MOE_MT_ROWS];
   __shared__ int s_hdr[MOE_MT_HDR];
   __shared__ int s_stop;
 
@@ -776,20 +772,20 @@ __global__ __launch_bounds__(256, 1) void k_ffn_bf16(FusedArgs a) {
     } else {
       it = ffn_item(item, n_mt, a.window, a.n_nt1, a.n_nt2, a.S, a.interleave != 0);
     }
-    if (tid < MOE_MT_FIELDS) {
-      const int v = a.mtile_desc[(int64_t)it.mt * MOE_MT_FIELDS + tid];
-      if (tid < MOE_MT_HDR) s_hdr[tid] = v;
-      else s_sub[tid - MOE_MT_HDR] = v;
+    {
+      const int32_t* dsc = a.mtile_desc + (int64_t)it.mt * MOE_MT_FIELDS;
+      if (tid < MOE_MT_HDR) s_hdr[tid] = dsc[tid];
+      s_rows[tid] = dsc[MOE_MT_HDR + tid];  // 256 threads, 256 rows
     }
     if (a.ts != nullptr && first && tid == 0) atomicMin((unsigned long long*)&a.ts[0], (unsigned long long)moe_clock());
     first = false;
     __syncthreads();
-    const int e = __builtin_amdgcn_readfirstlane(s_hdr[0]), n_sub = __builtin_amdgcn_readfirstlane(s_hdr[1]);
-    if (it.kind == 1) return ffn_tile<BN1, true>(a, smem, s_sub, e, n_sub, it.mt, it.nt, 0, &s_stop);
+    const int e = __builtin_amdgcn_readfirstlane(s_hdr[0]), n_rows = __builtin_amdgcn_readfirstlane(s_hdr[1]);
+    if (it.kind == 1) return ffn_tile<BN1, true>(a, smem, s_rows, e, n_rows, it.mt, it.nt, 0, &s_stop);
     // the h columns this split reads: column tiles [s, s+1) * n_nt1 / S of the first GEMM
     const int per = a.n_nt1 / a.S;
     return wait_flags(a.flags1 + (int64_t)it.mt * a.n_nt1 + it.s * per, per, a.epoch, a.budget, a.status, &s_stop) &&
-           ffn_tile<BN2, false>(a, smem, s_sub, e, n_sub, it.mt, it.nt, it.s, &s_stop);
+           ffn_tile<BN2, false>(a, smem, s_rows, e, n_rows, it.mt, it.nt, it.s, &s_stop);
   };
   // With every GEMM1 item first, no row tile is returned before the GEMM1 part of the list is done, so the
   // consumer workgroups first take kc GEMM1 items each from the head of the list: just enough that the producers'

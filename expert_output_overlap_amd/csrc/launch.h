@@ -11,7 +11,7 @@ struct LayoutLaunch {
   const void* x;
   void* x_pad;
   moe_layout* L;
-  int R, T_o, G, k, lo, E, M, mgb, self_rank, mt_sub;
+  int R, T_o, G, k, lo, E, M, mgb, self_rank, mt_rows;
   int64_t row_bytes;
 };
 

@@ -71,7 +71,7 @@ __device__ int block_excl_scan(int v, int* s_wsum, int* total) {
 }
 
 struct ScanArgs {
-  int R, T_o, E, M, mgb, self_rank, n_chunks, mt_sub;
+  int R, T_o, E, M, mgb, self_rank, n_chunks, mt_rows;
   int64_t cap_rows, cap_tiles, cap_mtiles;
   int32_t *chunk_counts, *counts, *padded_off, *recv_off, *tile_owner, *tile_expert, *tile_valid, *tile_order,
       *seg_desc, *row_src, *scalars, *status, *mtile_desc, *seg_mtiles, *seg_sched;
@@ -82,9 +82,9 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
   __shared__ int s_poff[MAX_GROUPS];   // padded offset of g
   __shared__ int s_order[MAX_GROUPS];  // q -> g (non-empty groups, remote-first)
   __shared__ int s_q2[MAX_GROUPS];     // g -> position in the row-tile packing order
-  __shared__ int s_band_pos[MAX_GROUPS], s_seg_pos[MAX_GROUPS], s_sub_pos[MAX_GROUPS];
+  __shared__ int s_band_pos[MAX_GROUPS], s_seg_pos[MAX_GROUPS], s_row_pos[MAX_GROUPS];
   __shared__ int s_order2[MAX_GROUPS];  // q2 -> g, row-tile packing order
-  __shared__ int s_tile_base[MAX_GROUPS], s_run_off[MAX_GROUPS], s_run_subs[MAX_GROUPS];  // by q2
+  __shared__ int s_tile_base[MAX_GROUPS], s_run_off[MAX_GROUPS], s_run_rows[MAX_GROUPS];  // by q2
   __shared__ int s_wsum[SCAN_THREADS / MOE_WAVE + 1];
   __shared__ int s_misc[4];
   // scratch reused by steps that never overlap: 64-bit sort keys of the groups (e), run tables (g), segment
@@ -209,40 +209,41 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
   }
   const int n_ne = s_misc[0];
 
-  // (f) band and segment positions in remote-first order, sub-block positions in packing order
+  // (f) band and segment positions in remote-first order, real-row positions in packing order
   {
     const int q = tid;
-    int nb = 0, ns = 0, nsub = 0;
+    int nb = 0, ns = 0, nrow = 0;
     if (q < n_ne) {
       const int n = s_n[s_order[q]];
       nb = (n + M - 1) / M;
       ns = (nb + a.mgb - 1) / a.mgb;
-      nsub = (s_n[s_order2[q]] + MOE_SUB - 1) / MOE_SUB;
+      nrow = s_n[s_order2[q]];
     }
-    int tb = 0, ts = 0, tsub = 0;
+    int tb = 0, ts = 0, trow = 0;
     const int pb = block_excl_scan(nb, s_wsum, &tb);
     const int ps = block_excl_scan(ns, s_wsum, &ts);
-    const int psub = block_excl_scan(nsub, s_wsum, &tsub);
+    const int prow = block_excl_scan(nrow, s_wsum, &trow);
     if (q < n_ne) {
       s_band_pos[q] = pb;
       s_seg_pos[q] = ps;
-      s_sub_pos[q] = psub;  // indexed by q2
+      s_row_pos[q] = prow;  // indexed by q2
     }
     if (tid == 0) {
       s_misc[1] = ts;
-      s_misc[2] = tsub;
+      s_misc[2] = trow;
     }
     __syncthreads();
   }
   const int n_segs = s_misc[1];
 
-  // (g) GEMM row tiles: runs of consecutive same-expert groups in packing order, each cut into tiles of
-  // mt_sub sub-blocks (run starts, then two block scans: runs' tile counts, positions inside a run)
+  // (g) GEMM row tiles: runs of consecutive same-expert groups in packing order (one per expert), each run's real
+  // rows cut into tiles of mt_rows rows (run starts, then two block scans: runs' tile counts, positions inside a
+  // run)
   {
     int* s_e2 = (int*)s_scratch;               // expert of packing position q
     int* s_first = s_e2 + MAX_GROUPS;          // first packing position of run j
     int* s_tbase = s_first + MAX_GROUPS;       // first row tile of run j
-    int* s_rsubs = s_tbase + MAX_GROUPS;       // sub-blocks of run j
+    int* s_rrows = s_tbase + MAX_GROUPS;       // real rows of run j
     const int q = tid;
     const bool in = q < n_ne;
     if (in) s_e2[q] = s_order2[q] / R;
@@ -252,23 +253,23 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
     const int run = block_excl_scan(start, s_wsum, &n_runs) + start - 1;  // run of q
     if (start) s_first[run] = q;
     __syncthreads();
-    int tiles = 0, rsubs = 0;
+    int tiles = 0, rrows = 0;
     if (tid < n_runs) {
       const int q0 = s_first[tid], q1 = tid + 1 < n_runs ? s_first[tid + 1] : n_ne;
-      rsubs = (q1 < n_ne ? s_sub_pos[q1] : s_misc[2]) - s_sub_pos[q0];
-      tiles = (rsubs + a.mt_sub - 1) / a.mt_sub;
+      rrows = (q1 < n_ne ? s_row_pos[q1] : s_misc[2]) - s_row_pos[q0];
+      tiles = (rrows + a.mt_rows - 1) / a.mt_rows;
     }
     int n_mt = 0;
     const int tb = block_excl_scan(tiles, s_wsum, &n_mt);
     if (tid < n_runs) {
       s_tbase[tid] = tb;
-      s_rsubs[tid] = rsubs;
+      s_rrows[tid] = rrows;
     }
     __syncthreads();
     if (in) {
       s_tile_base[q] = s_tbase[run];
-      s_run_off[q] = s_sub_pos[q] - s_sub_pos[s_first[run]];
-      s_run_subs[q] = s_rsubs[run];
+      s_run_off[q] = s_row_pos[q] - s_row_pos[s_first[run]];
+      s_run_rows[q] = s_rrows[run];
     }
     if (tid == 0) s_misc[3] = n_mt;
     __syncthreads();
@@ -300,20 +301,31 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
     const int q = find(s_band_pos, pos);
     a.tile_order[pos] = s_poff[s_order[q]] / M + (pos - s_band_pos[q]);
   }
-  const int mt_mask = a.mt_sub - 1, mt_shift = __builtin_ctz(a.mt_sub);  // mt_sub is a power of two
-  for (int pos = tid; pos < s_misc[2]; pos += SCAN_THREADS) {
-    const int q2 = find(s_sub_pos, pos);
-    const int g = s_order2[q2], j = pos - s_sub_pos[q2], u = s_run_off[q2] + j;
-    int32_t* d = a.mtile_desc + (int64_t)(s_tile_base[q2] + (u >> mt_shift)) * MOE_MT_FIELDS;
-    const int slot = u & mt_mask;
-    d[MOE_MT_HDR + slot] = s_poff[g] + MOE_SUB * j;
-    if (slot == 0) {
-      const int left = s_run_subs[q2] - u, cnt = left < a.mt_sub ? left : a.mt_sub;
-      d[0] = g / R;
-      d[1] = cnt;
-      d[2] = s_tile_base[q2];
-      d[3] = (s_run_subs[q2] + a.mt_sub - 1) >> mt_shift;
-      for (int s2 = cnt; s2 < MOE_MT_SUB; ++s2) d[MOE_MT_HDR + s2] = -1;
+  const int mt_mask = a.mt_rows - 1, mt_shift = __builtin_ctz(a.mt_rows);  // mt_rows is a power of two
+  // row-tile entries: one wave per group of the packing order, 64 of its rows at a time; row j of group g is
+  // row u = run offset + j of its expert's run, slot u % mt_rows of tile (run base + u / mt_rows).  The group that
+  // ends a run marks the slots of its last tile past the run's rows with -1.
+  {
+    const int wave = tid / MOE_WAVE, lane = tid % MOE_WAVE;
+    for (int q2 = wave; q2 < n_ne; q2 += SCAN_THREADS / MOE_WAVE) {
+      const int g = s_order2[q2], n = s_n[g], base = s_tile_base[q2], roff = s_run_off[q2], rrows = s_run_rows[q2];
+      for (int j = lane; j < n; j += MOE_WAVE) {
+        const int u = roff + j, slot = u & mt_mask;
+        int32_t* d = a.mtile_desc + (int64_t)(base + (u >> mt_shift)) * MOE_MT_FIELDS;
+        d[MOE_MT_HDR + slot] = s_poff[g] + j;
+        if (slot == 0) {
+          const int left = rrows - u;
+          d[0] = g / R;
+          d[1] = left < a.mt_rows ? left : a.mt_rows;
+          d[2] = base;
+          d[3] = (rrows + a.mt_rows - 1) >> mt_shift;
+        }
+      }
+      const int used = rrows & mt_mask;
+      if (roff + n == rrows && used != 0) {
+        int32_t* d = a.mtile_desc + (int64_t)(base + (rrows >> mt_shift)) * MOE_MT_FIELDS;
+        for (int sl = used + lane; sl < a.mt_rows; sl += MOE_WAVE) d[MOE_MT_HDR + sl] = -1;
+      }
     }
   }
   for (int sp = tid; sp < n_segs; sp += SCAN_THREADS) {
@@ -333,8 +345,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
     sd[SEG_ROWS] = rows;
     sd[SEG_GROUP] = g;
     const int q2 = s_q2[g], base = s_tile_base[q2], roff = s_run_off[q2];
-    const int sub0 = (b * M) / MOE_SUB, sub1 = (b * M + rows - 1) / MOE_SUB;
-    const int mt0 = base + ((roff + sub0) >> mt_shift), mt1 = base + ((roff + sub1) >> mt_shift);
+    const int mt0 = base + ((roff + b * M) >> mt_shift), mt1 = base + ((roff + b * M + rows - 1) >> mt_shift);
     a.seg_mtiles[2 * sp] = mt0;
     a.seg_mtiles[2 * sp + 1] = mt1 - mt0 + 1;
   }
@@ -450,7 +461,7 @@ int launch_layout(const LayoutLaunch& p, hipStream_t st) {
   a.mgb = p.mgb;
   a.self_rank = p.self_rank;
   a.n_chunks = n_chunks;
-  a.mt_sub = p.mt_sub;
+  a.mt_rows = p.mt_rows;
   a.cap_rows = p.L->cap_rows;
   a.cap_tiles = p.L->cap_tiles;
   a.cap_mtiles = p.L->cap_mtiles;

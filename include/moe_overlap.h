@@ -77,11 +77,11 @@ typedef struct {
                             expert is not local */
   int32_t* scalars;      /* [4+R] M_pad, n_tiles, n_segs, N_r[0..R), n_mtiles */
   int32_t* status;       /* [1] device status word (moe_status) */
-  int32_t* mtile_desc;   /* [cap_mtiles][20] GEMM row tiles: {expert, n_sub, run_first, run_count,
-                            sub_start[16]}, 16-row sub-blocks of one expert that hold at least one real
-                            row; each expert's groups are packed together (self-owned group last) into
-                            the consecutive row tiles [run_first, run_first + run_count) (internal
-                            schedule) */
+  int32_t* mtile_desc;   /* [cap_mtiles][260] GEMM row tiles: {expert, n_rows, run_first, run_count,
+                            row[256]}, up to 256 (fp32: 64) real rows of one expert given by their
+                            padded-layout positions, -1 past n_rows; each expert's groups are packed
+                            together (self-owned group last) into the consecutive row tiles
+                            [run_first, run_first + run_count) (internal schedule) */
   int32_t* seg_mtiles;   /* [cap_tiles][2] first GEMM row tile and count a segment depends on (internal) */
   int32_t* seg_sched;    /* [cap_tiles] segments in the order their row tiles complete (internal) */
   int32_t* chunk_counts; /* [R][ceil(T_o/64)][E_l] per-64-token histogram, then its prefix (internal) */

@@ -89,28 +89,29 @@ def check_route_and_layout(run):
 
 
 def check_schedule(run):
-    """GEMM row tiles cover every real row exactly once, with one expert each; each expert's row tiles form one
-    run of consecutive tiles that every tile of it names; every segment's row tiles contain all of its rows
-    (host-side property check of the internal schedule)."""
+    """GEMM row tiles hold every real row exactly once and no padding row, with one expert each; each expert's
+    row tiles form one run of consecutive tiles that every tile of it names, all full but the last; every
+    segment's row tiles contain all of its rows (host-side property check of the internal schedule)."""
     P, lay, s = run.P, run.lay, run.s
+    TR = 256 if s.dtype == "bf16" else 64
     n_mt = P.scalars()["n_mtiles"]
     desc = P.array("mtile_desc").view(-1, B.MT_FIELDS)[:n_mt].cpu().numpy()
     covered = np.zeros(lay["M_pad"], np.int32)
     tile_of_row = np.full(lay["M_pad"], -1)
     runs = {}
     for mt, dsc in enumerate(desc):
-        e, nsub, r0, rc = dsc[0], dsc[1], dsc[2], dsc[3]
-        assert 1 <= nsub <= 16 and (dsc[4 + nsub:] == -1).all()
+        e, nrow, r0, rc = dsc[0], dsc[1], dsc[2], dsc[3]
+        assert 1 <= nrow <= TR and (dsc[4 + nrow:4 + TR] == -1).all()
         assert r0 <= mt < r0 + rc <= n_mt and runs.setdefault(e, (r0, rc)) == (r0, rc)
-        for st in dsc[4:4 + nsub]:
-            assert st % 16 == 0
-            covered[st:st + 16] += 1
-            tile_of_row[st:st + 16] = mt
-            assert (lay["tile_expert"][st // s.M] == e)
+        assert nrow == TR or mt == r0 + rc - 1
+        rows = dsc[4:4 + nrow]
+        covered[rows] += 1
+        tile_of_row[rows] = mt
+        assert (lay["tile_expert"][rows // s.M] == e).all()
     for e, (r0, rc) in runs.items():
         assert (desc[r0:r0 + rc, 0] == e).all()
     real = lay["row_src"] >= 0
-    assert (covered[real] == 1).all() and (covered <= 1).all()
+    assert (covered[real] == 1).all() and (covered[~real] == 0).all()
     segm = P.array("seg_mtiles").view(-1, 2)[: lay["n_segs"]].cpu().numpy()
     for sd, (m0, mc) in zip(lay["seg_desc"], segm):
         rows = np.arange(sd[4], sd[4] + sd[6])
