@@ -338,11 +338,13 @@ struct FfnItem {
 
 // Item i of the list, in one of two orders over windows of W row tiles (row tiles expert by expert); inside a
 // window, GEMM1 items are column-tile major (consecutive items share a weight tile) and GEMM2 items split-major,
-// then column-tile major.
+// then column-tile major, so consecutive GEMM2 items share a down-projection weight tile too.
 //  - GEMM1 first: every GEMM1 item (each gate/up weight tile streamed once; the kernel lists them expert by
 //    expert itself, from the row tiles' run fields, and uses this function for the rest), then the GEMM2
 //    windows.  A GEMM2 split reads only its own share of h's columns, which the first part of the GEMM1 list
-//    produced; row tiles complete window after window during the last part of the launch.
+//    produced; row tiles complete window after window during the last part of the launch.  With at most four
+//    windows that leaves most of the return to the launch's last round, so there a window's GEMM2 items go row
+//    tile by row tile instead (split-major inside a row tile), and its row tiles complete one after another.
 //  - interleaved: G1(0), G1(1), G2(0), G1(2), G2(1), ..., G1(nw-1), G2(nw-2), G2(nw-1): row tiles complete
 //    window after window over the whole launch, so a return that is large next to the FFN starts early.
 // In both, every GEMM2 item follows the GEMM1 items it reads and the last split of a tile follows its others.
@@ -356,9 +358,18 @@ __device__ __forceinline__ FfnItem ffn_item(int i, int n_mt, int W, int n1, int 
     it.s = 0;
     return it;
   };
+  const int nw = (n_mt + W - 1) / W;
+  const bool by_tile = !interleave && nw <= 4;
   auto g2 = [&](int w, int j, int Wc) {
     FfnItem it;
     it.kind = 2;
+    if (by_tile) {
+      const int ml = j / n2S, r = j - ml * n2S;
+      it.s = r / n2;
+      it.nt = r - it.s * n2;
+      it.mt = w * W + ml;
+      return it;
+    }
     const int per = Wc * n2;
     it.s = j / per;
     const int r = j - it.s * per;
@@ -366,7 +377,6 @@ __device__ __forceinline__ FfnItem ffn_item(int i, int n_mt, int W, int n1, int 
     it.mt = w * W + (r - it.nt * Wc);
     return it;
   };
-  const int nw = (n_mt + W - 1) / W;
   const int Wl = n_mt - (nw - 1) * W;
   if (!interleave) {
     if (i < n_mt * n1) {
