@@ -110,15 +110,21 @@ int device_cus(int dev) {
   return n;
 }
 
-// Optional kernel timing: per call, events around GEMM1, GEMM2 (producer stream) and the consumer.
+// Optional kernel timing: per call, events on the caller's stream at the boundaries of the launches the call
+// makes, and no others: a timing event waits for the work before it to drain, so each extra one would stretch
+// the stream.  e[0] before the producer launch, e[1] after it, then one after each further launch (fp32 second
+// GEMM, sequential-mode consumer).
 struct CallEvents {
-  hipEvent_t e[5];  // producer launch start, its end / second launch start, its end, consumer start, end
+  hipEvent_t e[4];
+  int n = 0;            // events recorded
+  bool second = false;  // e[1] -> e[2] is the fp32 second GEMM
+  bool cons = false;    // e[n-2] -> e[n-1] is the sequential-mode consumer
 };
 bool g_timing = false;
 std::vector<CallEvents> g_events;
 
 int timing_begin(CallEvents* ce) {
-  for (int i = 0; i < 5; ++i)
+  for (int i = 0; i < 4; ++i)
     if (hipEventCreate(&ce->e[i]) != hipSuccess) return -1;
   return 0;
 }
@@ -140,12 +146,16 @@ int moe_kernel_times(double* out4) {
   int rc = MOE_OK;
   for (auto& ce : g_events) {
     float ms = 0;
-    for (int i = 0; i < 5; ++i)
+    for (int i = 0; i < ce.n; ++i)
       if (hipEventSynchronize(ce.e[i]) != hipSuccess) rc = MOE_EHIP;
     if (hipEventElapsedTime(&ms, ce.e[0], ce.e[1]) == hipSuccess) t[0] += ms; else rc = MOE_EHIP;
-    if (hipEventElapsedTime(&ms, ce.e[1], ce.e[2]) == hipSuccess) t[1] += ms; else rc = MOE_EHIP;
-    if (hipEventElapsedTime(&ms, ce.e[3], ce.e[4]) == hipSuccess) t[2] += ms; else rc = MOE_EHIP;
-    for (int i = 0; i < 5; ++i) hipEventDestroy(ce.e[i]);
+    if (ce.second) {
+      if (hipEventElapsedTime(&ms, ce.e[1], ce.e[2]) == hipSuccess) t[1] += ms; else rc = MOE_EHIP;
+    }
+    if (ce.cons) {
+      if (hipEventElapsedTime(&ms, ce.e[ce.n - 2], ce.e[ce.n - 1]) == hipSuccess) t[2] += ms; else rc = MOE_EHIP;
+    }
+    for (int i = 0; i < 4; ++i) hipEventDestroy(ce.e[i]);
   }
   out4[0] = t[0];
   out4[1] = t[1];
@@ -313,17 +323,24 @@ int moe_expert_ffn_overlap(const moe_shape* s, const moe_layout* L, const void* 
   // producers on the other CUs, each joining the return once its items are done; sequential: producers on
   // every CU, then the return on every CU
   const int n_cons = cfg->mode == 0 ? C : 0;
-  if (timed) hipEventRecord(ce.e[0], st);
+  if (timed) hipEventRecord(ce.e[ce.n++], st);
   if (launch_ffn_producer(p, n_cu, p.dtype == MOE_BF16 ? n_cons : 0, st)) return fail(MOE_EHIP, "producer launch failed");
-  if (timed) hipEventRecord(ce.e[1], st);
-  if (launch_ffn_producer2(p, n_cu, n_cons, st)) return fail(MOE_EHIP, "producer launch failed");
-  if (timed) {
-    hipEventRecord(ce.e[2], st);
-    hipEventRecord(ce.e[3], st);
+  if (timed) hipEventRecord(ce.e[ce.n++], st);
+  if (p.dtype != MOE_BF16) {
+    if (launch_ffn_producer2(p, n_cu, n_cons, st)) return fail(MOE_EHIP, "producer launch failed");
+    if (timed) {
+      hipEventRecord(ce.e[ce.n++], st);
+      ce.second = true;
+    }
   }
-  if (cfg->mode == 1 && launch_ffn_consumer(p, n_cu, st)) return fail(MOE_EHIP, "consumer launch failed");
+  if (cfg->mode == 1) {
+    if (launch_ffn_consumer(p, n_cu, st)) return fail(MOE_EHIP, "consumer launch failed");
+    if (timed) {
+      hipEventRecord(ce.e[ce.n++], st);
+      ce.cons = true;
+    }
+  }
   if (timed) {
-    hipEventRecord(ce.e[4], st);
     std::lock_guard<std::mutex> lk(g_mu);
     g_events.push_back(ce);
   }
