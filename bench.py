@@ -234,7 +234,7 @@ def main():
         "executed_pad_pct": round(100.0 * (M_pad - M_real) / max(M_real, 1), 2),
         "roofline": {"bound": "mfma",
                      "kernel": ("k_ffn_bf16: whole expert FFN in one persistent launch (gate/up + SwiGLU, "
-                                "down projection with split-K, flag publish; consumer workgroups inside)"
+                                "down projection with split-K, flag publish; the return inside)"
                                 if s.dtype == "bf16" else "k_gemm<float> first GEMM"),
                      "achieved": round(roof_flops / (g1_avg * 1e-3) / 1e12, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(roof_flops / (g1_avg * 1e-3) / 1e12 / peak, 4),

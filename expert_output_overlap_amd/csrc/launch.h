@@ -46,7 +46,7 @@ struct CombineLaunch {
 int launch_route(int T, int G, int k, const float* logits, int32_t* topk_idx, float* topk_w, hipStream_t st);
 int launch_layout(const LayoutLaunch& p, hipStream_t st);
 
-// GEMM row-tile height (rows) of the producer: the layout builds its row tiles from BM/16 sub-blocks.
+// GEMM row-tile height (rows) of the producer: the layout packs up to this many real rows into a row tile.
 int ffn_gemm_bm(int dtype);
 // Output tile width of the second GEMM (y): flags are one per (row tile, column tile).
 int ffn_gemm2_bn(int dtype, int d);

@@ -168,7 +168,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
 
   // (e) remote-first order of non-empty groups: key (owner == self, -P, e, r) ascending (bands, segments);
   // row-tile packing order: key (e, owner == self, -P, r): each expert's groups together, so that a GEMM row tile
-  // (one expert) packs as many sub-blocks as possible, and inside an expert the self-owned group last.  (Keeping
+  // (one expert) is as full as possible, and inside an expert the self-owned group last.  (Keeping
   // every self-owned group behind all remote ones instead gives each expert a second, mostly empty tile when R is
   // large: 142 row tiles instead of about 100 for 32 experts and 8 owners.)  Both keys are packed into one
   // unsigned 64-bit value per group (unique, since (e, r) is), so a group's rank is the count of smaller keys.
@@ -286,7 +286,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
     return;
   }
 
-  // (h) tile_order, row-tile entries and segments, one thread per band, sub-block and segment; the group of an
+  // (h) tile_order, row-tile entries and segments, one thread per band and segment; the group of an
   // entry is the last one whose first position (prefix over non-empty groups) is not after it
   auto find = [&](const int* first, int pos) {
     int lo = 0, hi = n_ne - 1;
