@@ -147,6 +147,9 @@ SMALL = [
     mi.Spec("splitk2", R=4, T_o=300, G=8, E_l=2, k=2, d=256, f=512, M=32, seed=17),
     mi.Spec("splitk3", R=2, T_o=500, G=8, E_l=2, k=2, d=256, f=768, M=64, seed=18),
     mi.Spec("splitk6", R=3, T_o=200, G=6, E_l=2, k=1, d=256, f=1536, M=16, seed=19),
+    # 4 k-splits over more than four windows of row tiles: split-major second-GEMM windows (sequential call) and
+    # interleaved windows (overlapped call)
+    mi.Spec("splitk_windows", R=4, T_o=2400, G=8, E_l=2, k=2, d=256, f=1024, M=32, seed=22),
     # fp32 with more transfer segments than a 128-thread consumer workgroup holds in its window at once
     mi.Spec("f32_many_segs", R=8, T_o=400, G=32, E_l=16, k=2, d=128, f=128, M=16, dtype="f32", seed=20),
 ]
