@@ -2,16 +2,16 @@
 // one rank-wide persistent GEMM over all local experts that publishes a readiness flag per output tile;
 // "What carries the argument": remote-bound tiles first).
 //
-// Two persistent launches, one workgroup per CU:
 //   GEMM1 (GLU):  h[rows, f] = bf16(silu(x Wg^T) * (x Wu^T)),  one tile = BN/2 gate + BN/2 up columns
-//   GEMM2:        y[rows, d] = h Wd^T, then flags[tile] = epoch with an agent-scope release.  The first C
-//                 workgroups of this launch are the consumer partition instead (consumer.h): round-robin
-//                 dispatch puts workgroup b on XCD b % 8, so C consumers spread over the XCDs, one per CU,
-//                 and the producer and consumer are co-resident by construction.
+//   GEMM2:        y[rows, d] = h Wd^T, then the y tile's flag = epoch once its stores are visible device-wide
+// bf16: both GEMMs are one persistent launch (k_ffn_bf16) over a list of GEMM1 tiles and GEMM2 k-splits, each
+// GEMM2 item waiting for the flags of the h tiles it reads; fp32: two launches (k_gemm), the second publishing.
+// The first C workgroups of the publishing launch are the consumer partition (consumer.h): round-robin dispatch
+// puts workgroup b on XCD b % 8, so C consumers spread over the XCDs, one per CU, co-resident with the producers
+// by construction; every producer workgroup joins the return once its own items are done.
 // Row tiles are the layout's GEMM row tiles: up to BM real rows of one expert, each expert's rows packed into
-// consecutive tiles, so padding rows cost nothing.  Items (row tile, column tile)
-// are visited window by window (band_window row tiles, column-tile-major inside a window) for weight
-// reuse, and consecutive items go to workgroups on the same XCD.
+// consecutive tiles, so padding rows cost nothing.  Items (row tile, column tile) are visited window by window
+// (band_window row tiles) for weight reuse, and consecutive items go to workgroups on the same XCD.
 #include <atomic>
 #include <type_traits>
 
@@ -378,15 +378,7 @@ __device__ __forceinline__ FfnItem ffn_item(int i, int n_mt, int W, int n1, int 
     return it;
   };
   const int Wl = n_mt - (nw - 1) * W;
-  if (!interleave) {
-    if (i < n_mt * n1) {
-      FfnItem it;
-      it.kind = 1;
-      it.nt = i / n_mt;
-      it.mt = i - it.nt * n_mt;
-      it.s = 0;
-      return it;
-    }
+  if (!interleave) {  // i >= n_mt * n1: the kernel maps the GEMM1 part of this order itself
     const int j = i - n_mt * n1, w = j / (W * n2S);
     return w < nw - 1 ? g2(w, j - w * W * n2S, W) : g2(nw - 1, j - (nw - 1) * W * n2S, Wl);
   }
