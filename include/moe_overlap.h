@@ -17,9 +17,9 @@
  *  - `stream` is a hipStream_t (NULL = the null stream).  Every call is asynchronous on it.
  *  - Return values are moe_status codes for synchronous (host-side) checks: MOE_EINVAL for a bad shape,
  *    a null pointer or an unsupported size, MOE_EHIP when a HIP call or launch fails.  moe_last_error()
- *    gives a message.  Errors found on the device (capacity overflow, consumer watchdog) are written to
- *    the layout's device status word; read it with moe_read_status().  Kernels that follow a failed one
- *    see the nonzero status and do nothing.
+ *    gives a message.  Errors found on the device (an invalid token id, capacity overflow, a wait in the
+ *    FFN launch that ran out of its spin budget) are written to the layout's device status word; read it
+ *    with moe_read_status().  Kernels that follow a failed one see the nonzero status and do nothing.
  *  - Not thread-safe for one moe_layout; calls that share a layout or flag array must be ordered.
  *  - Matrices are row-major.  Weights follow the (out, in) convention of a linear layer.
  *  - Element type: MOE_BF16 (activations, weights, hidden h, outputs in bf16, fp32 accumulation) or
