@@ -333,6 +333,32 @@ def test_watchdog_ends_a_wait_that_never_ends():
     assert run.P.status() == B.MOE_OK
 
 
+@pytest.mark.parametrize("name", ["splitk", "splitk_windows"])
+def test_tiny_spin_budget_ends_every_wait(name):
+    """With a one-tick spin budget the producer's waits for h tiles, the consumer's waits and the workgroups that
+    join the return give up instead of waiting: the launch ends with MOE_OK (nothing had to wait) or
+    MOE_ETIMEOUT, and the next call, on a fresh layout, delivers exactly what a fresh run delivers."""
+    s = [c for c in SMALL if c.name == name][0]
+    run = Run(s)
+    run.ffn(mode=0, consumer_cus=4, watchdog_ticks=1)
+    torch.cuda.synchronize()
+    assert run.P.status() in (B.MOE_OK, B.MOE_ETIMEOUT)
+    run.P.layout(run.dev["x"])
+    for r in range(s.R):
+        run.P.recv[r].fill_(float("nan"))
+    run.ffn(mode=0, consumer_cus=4)
+    fresh = MoePath.from_spec(s)
+    fresh.route(run.dev["logits"])
+    fresh.layout(run.dev["x"])
+    fresh.ffn(run.dev["w_gate_up"], run.dev["w_down"], mode=1)
+    torch.cuda.synchronize()
+    assert run.P.status() == B.MOE_OK and fresh.status() == B.MOE_OK
+    check_delivery(run)
+    for r in range(s.R):
+        n_r = int(run.lay["N_r"][r])
+        np.testing.assert_array_equal(bits(run.P.recv[r])[:n_r], bits(fresh.recv[r])[:n_r])
+
+
 def test_capacity_overflow_reported():
     s = mi.spec("tiny")
     run = Run(s)
