@@ -110,22 +110,27 @@ int device_cus(int dev) {
   return n;
 }
 
-// Optional kernel timing: per call, events on the caller's stream at the boundaries of the launches the call
-// makes, and no others: a timing event waits for the work before it to drain, so each extra one would stretch
-// the stream.  e[0] before the producer launch, e[1] after it, then one after each further launch (fp32 second
-// GEMM, sequential-mode consumer).
+// Optional kernel timing: per call, a start and an end event for each launch the call makes, taken by the
+// launch itself (hipExtLaunchKernel), so timing puts no marker in the stream.  Pair 0 is the producer launch,
+// then the fp32 second GEMM if there is one, then the sequential-mode consumer if there is one.
 struct CallEvents {
-  hipEvent_t e[4];
-  int n = 0;            // events recorded
-  bool second = false;  // e[1] -> e[2] is the fp32 second GEMM
-  bool cons = false;    // e[n-2] -> e[n-1] is the sequential-mode consumer
+  hipEvent_t e[6];
+  int n = 0;            // launches timed (pairs used)
+  bool second = false;  // pair 1 is the fp32 second GEMM
+  bool cons = false;    // the last pair is the sequential-mode consumer
+  void destroy() {
+    for (int i = 0; i < 6; ++i) hipEventDestroy(e[i]);
+  }
 };
 bool g_timing = false;
 std::vector<CallEvents> g_events;
 
 int timing_begin(CallEvents* ce) {
-  for (int i = 0; i < 4; ++i)
-    if (hipEventCreate(&ce->e[i]) != hipSuccess) return -1;
+  for (int i = 0; i < 6; ++i)
+    if (hipEventCreate(&ce->e[i]) != hipSuccess) {
+      for (int j = 0; j < i; ++j) hipEventDestroy(ce->e[j]);
+      return -1;
+    }
   return 0;
 }
 
@@ -146,16 +151,16 @@ int moe_kernel_times(double* out4) {
   int rc = MOE_OK;
   for (auto& ce : g_events) {
     float ms = 0;
-    for (int i = 0; i < ce.n; ++i)
+    for (int i = 0; i < 2 * ce.n; ++i)
       if (hipEventSynchronize(ce.e[i]) != hipSuccess) rc = MOE_EHIP;
-    if (hipEventElapsedTime(&ms, ce.e[0], ce.e[1]) == hipSuccess) t[0] += ms; else rc = MOE_EHIP;
-    if (ce.second) {
-      if (hipEventElapsedTime(&ms, ce.e[1], ce.e[2]) == hipSuccess) t[1] += ms; else rc = MOE_EHIP;
-    }
-    if (ce.cons) {
-      if (hipEventElapsedTime(&ms, ce.e[ce.n - 2], ce.e[ce.n - 1]) == hipSuccess) t[2] += ms; else rc = MOE_EHIP;
-    }
-    for (int i = 0; i < 4; ++i) hipEventDestroy(ce.e[i]);
+    auto pair = [&](int j, double* acc) {
+      if (hipEventElapsedTime(&ms, ce.e[2 * j], ce.e[2 * j + 1]) == hipSuccess) *acc += ms;
+      else rc = MOE_EHIP;
+    };
+    if (ce.n > 0) pair(0, &t[0]);
+    if (ce.second) pair(1, &t[1]);
+    if (ce.cons) pair(ce.n - 1, &t[2]);
+    ce.destroy();
   }
   out4[0] = t[0];
   out4[1] = t[1];
@@ -317,28 +322,36 @@ int moe_expert_ffn_overlap(const moe_shape* s, const moe_layout* L, const void* 
   }
   CallEvents ce;
   const bool timed = g_timing && timing_begin(&ce) == 0;
+  auto failed = [&](const char* m) {
+    if (timed) ce.destroy();
+    return fail(MOE_EHIP, m);
+  };
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;  // the next launch's pair
+  auto next_pair = [&]() {
+    if (timed) {
+      ev0 = ce.e[2 * ce.n];
+      ev1 = ce.e[2 * ce.n + 1];
+      ++ce.n;
+    }
+  };
   if (cfg->timestamps && launch_ts_init(cfg->timestamps, 2 + 2 * layout_offsets(s).cap_tiles, st))
-    return fail(MOE_EHIP, "launch failed");
+    return failed("launch failed");
   // overlapped: C consumer workgroups in the producer launch (bf16: the whole FFN; fp32: its second GEMM),
   // producers on the other CUs, each joining the return once its items are done; sequential: producers on
   // every CU, then the return on every CU
   const int n_cons = cfg->mode == 0 ? C : 0;
-  if (timed) hipEventRecord(ce.e[ce.n++], st);
-  if (launch_ffn_producer(p, n_cu, p.dtype == MOE_BF16 ? n_cons : 0, st)) return fail(MOE_EHIP, "producer launch failed");
-  if (timed) hipEventRecord(ce.e[ce.n++], st);
+  next_pair();
+  if (launch_ffn_producer(p, n_cu, p.dtype == MOE_BF16 ? n_cons : 0, st, ev0, ev1))
+    return failed("producer launch failed");
   if (p.dtype != MOE_BF16) {
-    if (launch_ffn_producer2(p, n_cu, n_cons, st)) return fail(MOE_EHIP, "producer launch failed");
-    if (timed) {
-      hipEventRecord(ce.e[ce.n++], st);
-      ce.second = true;
-    }
+    ce.second = timed;
+    next_pair();
+    if (launch_ffn_producer2(p, n_cu, n_cons, st, ev0, ev1)) return failed("producer launch failed");
   }
   if (cfg->mode == 1) {
-    if (launch_ffn_consumer(p, n_cu, st)) return fail(MOE_EHIP, "consumer launch failed");
-    if (timed) {
-      hipEventRecord(ce.e[ce.n++], st);
-      ce.cons = true;
-    }
+    ce.cons = timed;
+    next_pair();
+    if (launch_ffn_consumer(p, n_cu, st, ev0, ev1)) return failed("consumer launch failed");
   }
   if (timed) {
     std::lock_guard<std::mutex> lk(g_mu);

@@ -61,13 +61,16 @@ __device__ __forceinline__ int32_t load_status(const int32_t* status) {
 // wave-level helpers
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by 1, 2, 4 and 8 lanes inside each
+// 16-lane row (lanes with no source add the zero `old`), then lane 15 into row 1 and lane 47 into row 3
+// (row_bcast:15), then lane 31 into rows 2 and 3 (row_bcast:31).  Every lane of the wave must be active.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int t = __shfl_up(v, o, 64);
-    if (l >= o) v += t;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2 and 3
   return v;
 }
 

@@ -12,6 +12,8 @@
 // Row tiles are the layout's GEMM row tiles: up to BM real rows of one expert, each expert's rows packed into
 // consecutive tiles, so padding rows cost nothing.  Items (row tile, column tile) are visited window by window
 // (band_window row tiles) for weight reuse, and consecutive items go to workgroups on the same XCD.
+#include <hip/hip_ext.h>
+
 #include <atomic>
 #include <type_traits>
 
@@ -922,7 +924,7 @@ GemmArgs base_args(const FfnLaunch& p) {
   return a;
 }
 
-int launch_bf16(const FfnLaunch& p, int grid, int n_cons, hipStream_t st) {
+int launch_bf16(const FfnLaunch& p, int grid, int n_cons, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   FusedArgs a;
   const FlagCarve fc = flag_carve(p.dtype, p.d, p.f, p.cap_mtiles);
   a.x = (const unsigned char*)p.x_pad;
@@ -960,21 +962,21 @@ int launch_bf16(const FfnLaunch& p, int grid, int n_cons, hipStream_t st) {
   a.n_cons = n_cons;
   fill_consumer(a.cons, p, a.n_nt2);
   const dim3 g(grid), b(256);
-  if (bn1 == 256 && bn2 == 256) hipLaunchKernelGGL((k_ffn_bf16<256, 256>), g, b, 0, st, a);
-  else if (bn1 == 256 && bn2 == 128) hipLaunchKernelGGL((k_ffn_bf16<256, 128>), g, b, 0, st, a);
-  else if (bn1 == 256) hipLaunchKernelGGL((k_ffn_bf16<256, 64>), g, b, 0, st, a);
-  else if (bn2 == 256) hipLaunchKernelGGL((k_ffn_bf16<128, 256>), g, b, 0, st, a);
+  if (bn1 == 256 && bn2 == 256) hipExtLaunchKernelGGL((k_ffn_bf16<256, 256>), g, b, 0, st, ev0, ev1, 0, a);
+  else if (bn1 == 256 && bn2 == 128) hipExtLaunchKernelGGL((k_ffn_bf16<256, 128>), g, b, 0, st, ev0, ev1, 0, a);
+  else if (bn1 == 256) hipExtLaunchKernelGGL((k_ffn_bf16<256, 64>), g, b, 0, st, ev0, ev1, 0, a);
+  else if (bn2 == 256) hipExtLaunchKernelGGL((k_ffn_bf16<128, 256>), g, b, 0, st, ev0, ev1, 0, a);
   // narrower tiles hold under 80 KB of LDS; pad them so that one workgroup still fills a CU
-  else if (bn2 == 128) hipLaunchKernelGGL((k_ffn_bf16<128, 128>), g, b, 16384, st, a);
-  else hipLaunchKernelGGL((k_ffn_bf16<128, 64>), g, b, 16384, st, a);
+  else if (bn2 == 128) hipExtLaunchKernelGGL((k_ffn_bf16<128, 128>), g, b, 16384, st, ev0, ev1, 0, a);
+  else hipExtLaunchKernelGGL((k_ffn_bf16<128, 64>), g, b, 16384, st, ev0, ev1, 0, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 }  // namespace
 
 int64_t ffn_flag_words(int dtype, int d, int f, int64_t cap_mtiles) { return flag_carve(dtype, d, f, cap_mtiles).total; }
 
-int launch_ffn_producer(const FfnLaunch& p, int grid, int n_cons, hipStream_t st) {
-  if (p.dtype == MOE_BF16) return launch_bf16(p, grid, n_cons, st);
+int launch_ffn_producer(const FfnLaunch& p, int grid, int n_cons, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  if (p.dtype == MOE_BF16) return launch_bf16(p, grid, n_cons, st, ev0, ev1);
   GemmArgs a = base_args(p);
   a.A = p.x_pad;
   a.W = p.w_gate_up;
@@ -984,11 +986,12 @@ int launch_ffn_producer(const FfnLaunch& p, int grid, int n_cons, hipStream_t st
   a.ldc = p.f;
   a.f = p.f;
   a.n_nt = p.f / (F32_BN / 2);
-  hipLaunchKernelGGL((k_gemm<float, F32_BM, F32_BN, 2, 1, true, false>), dim3(grid), dim3(128), 0, st, a);
+  hipExtLaunchKernelGGL((k_gemm<float, F32_BM, F32_BN, 2, 1, true, false>), dim3(grid), dim3(128), 0, st, ev0, ev1, 0,
+                        a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int launch_ffn_producer2(const FfnLaunch& p, int grid, int n_cons, hipStream_t st) {
+int launch_ffn_producer2(const FfnLaunch& p, int grid, int n_cons, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   if (p.dtype == MOE_BF16) return 0;  // one launch does both GEMMs
   GemmArgs a = base_args(p);
   a.A = p.h;
@@ -1002,14 +1005,15 @@ int launch_ffn_producer2(const FfnLaunch& p, int grid, int n_cons, hipStream_t s
   a.n_nt = p.d / F32_BN;
   a.n_cons = n_cons;
   fill_consumer(a.cons, p, a.n_nt);
-  hipLaunchKernelGGL((k_gemm<float, F32_BM, F32_BN, 2, 1, false, true>), dim3(grid), dim3(128), 0, st, a);
+  hipExtLaunchKernelGGL((k_gemm<float, F32_BM, F32_BN, 2, 1, false, true>), dim3(grid), dim3(128), 0, st, ev0, ev1, 0,
+                        a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int launch_ffn_consumer(const FfnLaunch& p, int n_cons, hipStream_t st) {
+int launch_ffn_consumer(const FfnLaunch& p, int n_cons, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   ConsumerArgs c;
   fill_consumer(c, p, p.d / ffn_gemm2_bn(p.dtype, p.d));
-  hipLaunchKernelGGL(k_consumer, dim3(n_cons), dim3(256), 0, st, c);
+  hipExtLaunchKernelGGL(k_consumer, dim3(n_cons), dim3(256), 0, st, ev0, ev1, 0, c);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -57,11 +57,15 @@ int ffn_splits(int dtype, int d, int f);
 int64_t ffn_flag_words(int dtype, int d, int f, int64_t cap_mtiles);
 // Producer launch, one workgroup per CU, whose first `n_cons` workgroups run the consumer role.  bf16: the
 // whole FFN in one launch (launch_ffn_producer2 is a no-op); fp32: the first GEMM, then the second GEMM with the
-// consumer workgroups.
-int launch_ffn_producer(const FfnLaunch& p, int grid, int n_cons, hipStream_t st);
-int launch_ffn_producer2(const FfnLaunch& p, int grid, int n_cons, hipStream_t st);
+// consumer workgroups.  Non-null ev0 / ev1 take the launch's own start and end times (hipExtLaunchKernel), with
+// no marker in the stream.
+int launch_ffn_producer(const FfnLaunch& p, int grid, int n_cons, hipStream_t st, hipEvent_t ev0 = nullptr,
+                        hipEvent_t ev1 = nullptr);
+int launch_ffn_producer2(const FfnLaunch& p, int grid, int n_cons, hipStream_t st, hipEvent_t ev0 = nullptr,
+                         hipEvent_t ev1 = nullptr);
 // The consumer alone (`n_cons` workgroups).
-int launch_ffn_consumer(const FfnLaunch& p, int n_cons, hipStream_t st);
+int launch_ffn_consumer(const FfnLaunch& p, int n_cons, hipStream_t st, hipEvent_t ev0 = nullptr,
+                        hipEvent_t ev1 = nullptr);
 // Resets the n timestamp entries of a call (starts to the largest value, ends to zero).
 int launch_ts_init(uint64_t* timestamps, int64_t n, hipStream_t st);
 int launch_combine(const CombineLaunch& p, hipStream_t st);

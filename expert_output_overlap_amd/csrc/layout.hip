@@ -50,24 +50,36 @@ __global__ __launch_bounds__(256) void k_layout_count(const int32_t* __restrict_
   if (lane < E) chunk_counts[((int64_t)r * n_chunks + c) * E + lane] = chunk_bad ? -1 : mine;
 }
 
-// Exclusive scan of one value per thread over a 1024-thread block; *total gets the sum.
-__device__ int block_excl_scan(int v, int* s_wsum, int* total) {
+// Exclusive scans of N values per thread over the 1024-thread block, with two barriers: the waves' sums go to LDS,
+// then every wave scans the 16 sums itself.  out[i] gets the thread's exclusive prefix, total[i] the block's sum.
+// s_wsum holds N * 16 ints; every thread of the block calls this.
+template <int N>
+__device__ void block_excl_scan_n(const int (&v)[N], int (&out)[N], int (&total)[N], int* s_wsum) {
+  constexpr int W = SCAN_THREADS / MOE_WAVE;
   const int wave = threadIdx.x / MOE_WAVE, lane = lane_id();
-  const int incl = wave_incl_scan(v);
-  __syncthreads();
-  if (lane == 63) s_wsum[wave] = incl;
-  __syncthreads();
-  if (wave == 0) {
-    const int w = lane < SCAN_THREADS / MOE_WAVE ? s_wsum[lane] : 0;
-    const int wi = wave_incl_scan(w);
-    if (lane < SCAN_THREADS / MOE_WAVE) s_wsum[lane] = wi - w;
-    if (lane == SCAN_THREADS / MOE_WAVE - 1) s_wsum[SCAN_THREADS / MOE_WAVE] = wi;
+  int incl[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    incl[i] = wave_incl_scan(v[i]);
+    if (lane == MOE_WAVE - 1) s_wsum[i * W + wave] = incl[i];
   }
   __syncthreads();
-  const int out = s_wsum[wave] + incl - v;
-  *total = s_wsum[SCAN_THREADS / MOE_WAVE];
-  __syncthreads();
-  return out;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int w = lane < W ? s_wsum[i * W + lane] : 0;
+    const int wi = wave_incl_scan(w);
+    out[i] = __builtin_amdgcn_readlane(wi - w, wave) + incl[i] - v[i];
+    total[i] = __builtin_amdgcn_readlane(wi, W - 1);
+  }
+  __syncthreads();  // the sums are read before the next call writes them
+}
+
+__device__ __forceinline__ int block_excl_scan(int v, int* s_wsum, int* total) {
+  const int in[1] = {v};
+  int out[1], tot[1];
+  block_excl_scan_n<1>(in, out, tot, s_wsum);
+  *total = tot[0];
+  return out[0];
 }
 
 struct ScanArgs {
@@ -85,7 +97,8 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
   __shared__ int s_band_pos[MAX_GROUPS], s_seg_pos[MAX_GROUPS], s_row_pos[MAX_GROUPS];
   __shared__ int s_order2[MAX_GROUPS];  // q2 -> g, row-tile packing order
   __shared__ int s_tile_base[MAX_GROUPS], s_run_off[MAX_GROUPS], s_run_rows[MAX_GROUPS];  // by q2
-  __shared__ int s_wsum[SCAN_THREADS / MOE_WAVE + 1];
+  __shared__ int s_roff[MAX_GROUPS];    // receive offset of g
+  __shared__ int s_wsum[3 * SCAN_THREADS / MOE_WAVE];
   __shared__ int s_misc[4];
   // scratch reused by steps that never overlap: 64-bit sort keys of the groups (e), run tables (g), segment
   // keys (i)
@@ -94,27 +107,60 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
   const int tid = threadIdx.x;
   const int R = a.R, E = a.E, M = a.M, NG = E * R;
 
-  // (a) group sizes; per-(owner, expert) chunk counts become exclusive prefixes in place (loads in batches of 8
-  // independent ones); a chunk that saw an invalid token holds -1 counts
+  // (a) group sizes; per-(owner, expert) chunk counts become exclusive prefixes in place.  A group's chunks are
+  // cut into P parts of at most 8 consecutive chunks (P <= 1024 / groups), one thread per (group, part): it loads
+  // its part's counts at once, the part sums meet in LDS, then it writes its part's prefixes.  A chunk that saw
+  // an invalid token holds -1 counts.
   int bad = 0;
-  for (int g = tid; g < NG; g += SCAN_THREADS) {
+  {
+    int* s_part = (int*)s_scratch;  // [P][NG] part sums
+    int P = SCAN_THREADS / NG;
+    if (P > (a.n_chunks + 7) / 8) P = (a.n_chunks + 7) / 8;
+    if (P < 1) P = 1;
+    const int L = (a.n_chunks + P - 1) / P;  // chunks per part
+    const int g = tid % NG, p = tid / NG;
+    const bool act = p < P;
     const int e = g / R, r = g % R;
     int32_t* base = a.chunk_counts + (int64_t)r * a.n_chunks * E + e;
-    int run = 0;
-    for (int c0 = 0; c0 < a.n_chunks; c0 += 8) {
-      int v[8];
+    const int c0 = p * L, c1 = min(c0 + L, a.n_chunks);
+    int v[8];
+    int sum = 0;
+    if (act) {
+      if (L <= 8) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = c0 + u < a.n_chunks ? base[(int64_t)(c0 + u) * E] : 0;
+        for (int u = 0; u < 8; ++u) v[u] = c0 + u < c1 ? base[(int64_t)(c0 + u) * E] : 0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (c0 + u < a.n_chunks) {
-          base[(int64_t)(c0 + u) * E] = run;
-          bad |= v[u] < 0;
-          run += v[u];
-        }
+        for (int u = 0; u < 8; ++u) sum += v[u];
+      } else {
+        for (int c = c0; c < c1; ++c) sum += base[(int64_t)c * E];
+      }
+      s_part[p * NG + g] = sum;
     }
-    s_n[g] = run;
-    a.counts[g] = run;
+    __syncthreads();
+    if (act) {
+      int run = 0;
+      for (int q = 0; q < p; ++q) run += s_part[q * NG + g];
+      if (L <= 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (c0 + u < c1) {
+            base[(int64_t)(c0 + u) * E] = run;
+            bad |= v[u] < 0;
+            run += v[u];
+          }
+      } else {
+        for (int c = c0; c < c1; ++c) {
+          const int x = base[(int64_t)c * E];
+          base[(int64_t)c * E] = run;
+          bad |= x < 0;
+          run += x;
+        }
+      }
+      if (p == P - 1) {
+        s_n[g] = run;
+        a.counts[g] = run;
+      }
+    }
   }
   // the layout build sets the status word: MOE_EINVAL for an invalid token, then MOE_ECAPACITY, else MOE_OK
   const int any_bad = __syncthreads_or(bad);
@@ -139,6 +185,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
     int run = 0;
     for (int e = 0; e < E; ++e) {
       a.recv_off[e * R + tid] = run;
+      s_roff[e * R + tid] = run;
       run += s_n[e * R + tid];
     }
     a.scalars[SC_NR + tid] = run;
@@ -191,7 +238,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
     __syncthreads();
     int rank = 0, rank2 = 0;
     if (mine) {
-#pragma unroll 8
+#pragma unroll 16
       for (int h = 0; h < NG; ++h) {
         rank += key1[h] < k1;
         rank2 += key2[h] < k2;
@@ -219,10 +266,10 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
       ns = (nb + a.mgb - 1) / a.mgb;
       nrow = s_n[s_order2[q]];
     }
-    int tb = 0, ts = 0, trow = 0;
-    const int pb = block_excl_scan(nb, s_wsum, &tb);
-    const int ps = block_excl_scan(ns, s_wsum, &ts);
-    const int prow = block_excl_scan(nrow, s_wsum, &trow);
+    const int in3[3] = {nb, ns, nrow};
+    int pre3[3], tot3[3];
+    block_excl_scan_n<3>(in3, pre3, tot3, s_wsum);
+    const int pb = pre3[0], ps = pre3[1], prow = pre3[2], ts = tot3[1], trow = tot3[2];
     if (q < n_ne) {
       s_band_pos[q] = pb;
       s_seg_pos[q] = ps;
@@ -304,15 +351,29 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
   const int mt_mask = a.mt_rows - 1, mt_shift = __builtin_ctz(a.mt_rows);  // mt_rows is a power of two
   // row-tile entries: one wave per group of the packing order, 64 of its rows at a time; row j of group g is
   // row u = run offset + j of its expert's run, slot u % mt_rows of tile (run base + u / mt_rows).  The group that
-  // ends a run marks the slots of its last tile past the run's rows with -1.
+  // ends a run marks the slots of its last tile past the run's rows with -1.  Lane l of wave w first loads the
+  // tables of packing position w + 16 l, and the wave takes them from there one group at a time.
   {
+    constexpr int W = SCAN_THREADS / MOE_WAVE;
     const int wave = tid / MOE_WAVE, lane = tid % MOE_WAVE;
-    for (int q2 = wave; q2 < n_ne; q2 += SCAN_THREADS / MOE_WAVE) {
-      const int g = s_order2[q2], n = s_n[g], base = s_tile_base[q2], roff = s_run_off[q2], rrows = s_run_rows[q2];
+    const int ql = wave + W * lane;  // < 64 W = MAX_GROUPS
+    int g_l = 0, n_l = 0, base_l = 0, roff_l = 0, rrows_l = 0, poff_l = 0;
+    if (ql < n_ne) {
+      g_l = s_order2[ql];
+      n_l = s_n[g_l];
+      base_l = s_tile_base[ql];
+      roff_l = s_run_off[ql];
+      rrows_l = s_run_rows[ql];
+      poff_l = s_poff[g_l];
+    }
+    for (int i = 0; wave + W * i < n_ne; ++i) {
+      const int g = __builtin_amdgcn_readlane(g_l, i), n = __builtin_amdgcn_readlane(n_l, i);
+      const int base = __builtin_amdgcn_readlane(base_l, i), roff = __builtin_amdgcn_readlane(roff_l, i);
+      const int rrows = __builtin_amdgcn_readlane(rrows_l, i), poff = __builtin_amdgcn_readlane(poff_l, i);
       for (int j = lane; j < n; j += MOE_WAVE) {
         const int u = roff + j, slot = u & mt_mask;
         int32_t* d = a.mtile_desc + (int64_t)(base + (u >> mt_shift)) * MOE_MT_FIELDS;
-        d[MOE_MT_HDR + slot] = s_poff[g] + j;
+        d[MOE_MT_HDR + slot] = poff + j;
         if (slot == 0) {
           const int left = rrows - u;
           d[0] = g / R;
@@ -341,7 +402,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
     sd[SEG_FIRST_BAND] = off / M + b;
     sd[SEG_NBANDS] = cnt;
     sd[SEG_SRC_ROW] = off + b * M;
-    sd[SEG_DST_ROW] = a.recv_off[g] + b * M;
+    sd[SEG_DST_ROW] = s_roff[g] + b * M;
     sd[SEG_ROWS] = rows;
     sd[SEG_GROUP] = g;
     const int q2 = s_q2[g], base = s_tile_base[q2], roff = s_run_off[q2];
@@ -350,18 +411,62 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
     a.seg_mtiles[2 * sp + 1] = mt1 - mt0 + 1;
   }
   __syncthreads();
-  // (i) consumer order: segments by the last GEMM row tile they wait for, ties by segment index (stable); the
-  // keys are staged in LDS when they fit
-  int* s_key = (int*)s_scratch;
-  if (n_segs <= SCAN_KEYS) {
-    for (int sg = tid; sg < n_segs; sg += SCAN_THREADS) s_key[sg] = a.seg_mtiles[2 * sg] + a.seg_mtiles[2 * sg + 1];
+  // (i) consumer order: segments by the last GEMM row tile they wait for, ties by segment index (stable).  In LDS a
+  // counting sort over the row tiles: per-tile counts (LDS atomics), their exclusive scan, each segment dropped
+  // into its tile's bucket, then placed inside the bucket by the segments of the bucket with a smaller index (at
+  // most mt_rows segments end in one row tile, since each has a row in it).  Larger layouts rank every segment
+  // against all others in global memory.
+  if (n_mtiles + 1 + n_segs <= SCAN_KEYS) {
+    int* s_start = (int*)s_scratch;          // [n_mtiles + 1]: counts per last tile, then bucket starts
+    int* s_list = s_start + n_mtiles + 1;    // [n_segs]: bucket members
+    constexpr int PER = SCAN_KEYS / SCAN_THREADS;
+    for (int t = tid; t <= n_mtiles; t += SCAN_THREADS) s_start[t] = 0;
     __syncthreads();
-    for (int sg = tid; sg < n_segs; sg += SCAN_THREADS) {
-      const int last = s_key[sg];
-      int rank = 0;
-#pragma unroll 8
-      for (int o = 0; o < n_segs; ++o) rank += (s_key[o] < last) || (s_key[o] == last && o < sg);
-      a.seg_sched[rank] = sg;
+    int key[PER], slot[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int sg = tid + j * SCAN_THREADS;
+      key[j] = 0;
+      slot[j] = 0;
+      if (sg < n_segs) {
+        key[j] = a.seg_mtiles[2 * sg] + a.seg_mtiles[2 * sg + 1] - 1;
+        slot[j] = atomicAdd(&s_start[key[j]], 1);
+      }
+    }
+    __syncthreads();
+    {  // buckets [PER tid, PER tid + PER) of this thread; bucket n_mtiles (empty) gets start n_segs
+      int c[PER], sum = 0;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int t = PER * tid + j;
+        c[j] = t <= n_mtiles ? s_start[t] : 0;
+        sum += c[j];
+      }
+      int tot = 0;
+      int run = block_excl_scan(sum, s_wsum, &tot);
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int t = PER * tid + j;
+        if (t <= n_mtiles) s_start[t] = run;
+        run += c[j];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int sg = tid + j * SCAN_THREADS;
+      if (sg < n_segs) s_list[s_start[key[j]] + slot[j]] = sg;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int sg = tid + j * SCAN_THREADS;
+      if (sg < n_segs) {
+        const int b0 = s_start[key[j]], b1 = s_start[key[j] + 1];
+        int rank = b0;
+        for (int o = b0; o < b1; ++o) rank += s_list[o] < sg;
+        a.seg_sched[rank] = sg;
+      }
     }
   } else {
     for (int sg = tid; sg < n_segs; sg += SCAN_THREADS) {

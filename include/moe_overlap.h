@@ -200,8 +200,9 @@ int moe_combine(const moe_shape* s, const moe_layout* L, const float* topk_w, vo
 
 /* ---- kernel timing ------------------------------------------------------------------------------- */
 
-/* While enabled (nonzero), every moe_expert_ffn_overlap call of this process records HIP timing events
- * around its launches on the caller's stream.  Disabled by default.  Returns MOE_OK. */
+/* While enabled (nonzero), every moe_expert_ffn_overlap call of this process times each of its launches with
+ * a pair of HIP events that the launch itself records (hipExtLaunchKernel: the kernel's start and end, no marker
+ * in the caller's stream).  Disabled by default.  Returns MOE_OK. */
 int moe_set_kernel_timing(int enable);
 
 /* Waits for the recorded events and writes the summed milliseconds since the last query:
