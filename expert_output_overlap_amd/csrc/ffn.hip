@@ -431,9 +431,12 @@ __device__ bool wait_flags(const uint32_t* fl, int n, uint32_t epoch, uint64_t b
 // stalls every workgroup on that XCD; the reader still acquires at agent scope before it reads.
 // 16 bytes with the device-scope cache policy (the one agent-scope atomic stores use), as one dwordx4 store:
 // two 8-byte atomic stores per 16 bytes measured 2-3 times slower.  The compiler does not count this store, so
-// whoever needs it complete waits with an explicit vmcnt(0) (wait_stores).
+// whoever needs it complete waits with an explicit vmcnt(0) (wait_stores).  Nor does it see that the registers of
+// v are store data: on this chip a VALU write to the data registers of a store wider than 8 bytes needs two wait
+// states after the store (else the store can send the new value), which the compiler inserts only for stores it
+// recognises, so the s_nop is part of the statement.
 __device__ __forceinline__ void store16_coherent(void* p, u32x4_t v) {
-  asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+  asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(p), "v"(v) : "memory");
 }
 
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
