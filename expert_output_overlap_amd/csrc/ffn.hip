@@ -336,6 +336,7 @@ struct FusedArgs {
 struct FfnItem {
   int kind;  // 1: GEMM1 tile, 2: GEMM2 split
   int mt, nt, s;
+  int stride;  // GEMM2: list distance between consecutive splits of the tile
 };
 
 // Item i of the list, in one of two orders over windows of W row tiles (row tiles expert by expert); inside a
@@ -360,6 +361,7 @@ __device__ __forceinline__ FfnItem ffn_item(int i, int n_mt, int W, int n1, int 
     it.nt = j / Wc;
     it.mt = w * W + (j - it.nt * Wc);
     it.s = 0;
+    it.stride = 0;
     return it;
   };
   const int nw = (n_mt + W - 1) / W;
@@ -372,6 +374,7 @@ __device__ __forceinline__ FfnItem ffn_item(int i, int n_mt, int W, int n1, int 
       it.s = r / n2;
       it.nt = r - it.s * n2;
       it.mt = w * W + ml;
+      it.stride = n2;
       return it;
     }
     const int per = Wc * n2;
@@ -379,6 +382,7 @@ __device__ __forceinline__ FfnItem ffn_item(int i, int n_mt, int W, int n1, int 
     const int r = j - it.s * per;
     it.nt = r / Wc;
     it.mt = w * W + (r - it.nt * Wc);
+    it.stride = per;
     return it;
   };
   const int Wl = n_mt - (nw - 1) * W;
@@ -463,12 +467,113 @@ __device__ __forceinline__ uint32_t arrive(uint64_t* ctr, uint32_t epoch) {
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x8_t __attribute__((ext_vector_type(8)));
 
+// 16 fp32 partial sums of one thread in one 32 x 32 accumulator block (the layout the splits store them in)
+__device__ __forceinline__ f32x16_t load_block16(const f32x4_t* src) {
+  const f32x4_t q0 = __builtin_nontemporal_load(src), q1 = __builtin_nontemporal_load(src + 256);
+  const f32x4_t q2 = __builtin_nontemporal_load(src + 512), q3 = __builtin_nontemporal_load(src + 768);
+  const f32x8_t h0 = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
+  const f32x8_t h1 = __builtin_shufflevector(q2, q3, 0, 1, 2, 3, 4, 5, 6, 7);
+  return (f32x16_t)__builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+}
+
+// Stores the real rows of a 256 x OUT_BN bf16 tile staged in LDS (16-byte chunk ch of row r at chunk ch ^ (r & 7)):
+// row r goes to base + s_rows[r] * ldc elements, 8 chunks per thread at a time (their LDS reads first, then their
+// stores, so neither latency is paid per chunk).
+template <int OUT_BN>
+__device__ __forceinline__ void store_rows(const unsigned char* smem, unsigned char* base, int64_t ldc,
+                                           const int* s_rows, int n_rows, int tid) {
+  constexpr int BM = 256, OUT_ROW = OUT_BN * 2, CPR = OUT_ROW / 16;
+  constexpr int ITER = BM * CPR / 256, UN = ITER < 8 ? ITER : 8;
+  static_assert(ITER % UN == 0, "store loop unroll");
+#pragma unroll 1
+  for (int i0 = 0; i0 < ITER; i0 += UN) {
+    u32x4_t v[UN];
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int idx = tid + (i0 + u) * 256, row = idx / CPR, ch = idx - row * CPR;
+      v[u] = *(const u32x4_t*)(smem + row * OUT_ROW + ((ch ^ (row & 7)) << 4));
+    }
+#pragma unroll
+    for (int u = 0; u < UN; ++u) {
+      const int idx = tid + (i0 + u) * 256, row = idx / CPR, ch = idx - row * CPR;
+      if (row < n_rows) store16_coherent(base + (int64_t)s_rows[row] * ldc * 2 + ch * 16, v[u]);
+    }
+  }
+}
+
+// The sum of split-K y tile (mt, nt), BN columns wide, by the item that completed it: the splits' fp32 partial
+// sums added in split order, y = ((p_0 + p_1) + ...) + p_{S-1} (the same association whichever item completes the
+// tile, so the result is the same on every call and in every mode), rounded to bf16 into LDS, then the tile's real
+// rows stored and its flag published.  Every thread's own partial sums were stored like the others', so all slots
+// are read back.  With the split count fixed at compile time, every slot of a 32 x 32 block is loaded in one go, D
+// blocks ahead of the one being summed, so about D round trips of the reads are in flight instead of one; other
+// split counts sum one block and split at a time.
+template <int BN>
+__device__ __forceinline__ void reduce_tile(const FusedArgs& a, unsigned char* smem, const int* s_rows, int n_rows,
+                                            int mt, int nt) {
+  constexpr int BM = 256, WM = 128, WN = BN / 2, MI = WM / 32, NI = WN / 32, NB = MI * NI;
+  constexpr int OUT_ROW = BN * 2, SLOT4 = BM * BN / 4;
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int64_t tile = (int64_t)mt * a.n_nt2 + nt;
+  const f32x4_t* slots = (const f32x4_t*)(a.partial + tile * a.S * (BM * BN));
+  auto stage = [&](int b, const f32x16_t& v) {  // block b of this thread's accumulators, as bf16, into LDS
+    const int mi = b / NI, ni = b - mi * NI, col = wn * WN + ni * 32 + (lane & 31);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int row = wm * WM + mi * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+      const int chunk = (col >> 3) ^ (row & 7);
+      *(__bf16*)(smem + row * OUT_ROW + chunk * 16 + (col & 7) * 2) = (__bf16)v[q];  // round to nearest even
+    }
+  };
+  auto ring_sum = [&](auto S_) {
+    constexpr int SC = decltype(S_)::value, D = SC <= 2 ? 3 : 2;
+    f32x16_t ring[D + 1][SC];
+    auto load = [&](int b) {
+#pragma unroll
+      for (int sp = 0; sp < SC; ++sp) ring[b % (D + 1)][sp] = load_block16(slots + (int64_t)sp * SLOT4 + b * 4 * 256 + tid);
+    };
+#pragma unroll
+    for (int b = 0; b < D; ++b) load(b);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b + D < NB) load(b + D);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16_t t = ring[b % (D + 1)][0];
+#pragma unroll
+      for (int sp = 1; sp < SC; ++sp) t += ring[b % (D + 1)][sp];
+      stage(b, t);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  if (a.S == 2) ring_sum(std::integral_constant<int, 2>{});
+  else if (a.S == 3) ring_sum(std::integral_constant<int, 3>{});
+  else if (a.S == 4) ring_sum(std::integral_constant<int, 4>{});
+  else {
+#pragma unroll 1
+    for (int b = 0; b < NB; ++b) {
+      const f32x4_t* src = slots + b * 4 * 256 + tid;
+      f32x16_t t = load_block16(src);
+      for (int sp = 1; sp < a.S; ++sp) t += load_block16(src + (int64_t)sp * SLOT4);
+      stage(b, t);
+    }
+  }
+  __syncthreads();
+  store_rows<BN>(smem, a.y + (int64_t)nt * BN * 2, a.d, s_rows, n_rows, tid);
+  publish(&a.flags2[tile], a.epoch);
+  if (a.ts != nullptr && tid == 0) atomicMax((unsigned long long*)&a.ts[1], (unsigned long long)moe_clock());
+}
+
 // One item: output tile (row tile with rows s_rows[0, n_rows) of expert e, column tile nt), k-tiles of
 // split s.  GLU: the first GEMM (A = x_pad rows, B = gate rows nt*BN/2.. and up rows f + nt*BN/2..); else the
-// second (A = h rows, B = down-projection rows nt*BN..).  False if a wait gave up (the workgroup must exit).
-template <int BN, bool GLU>
+// second (A = h rows, B = down-projection rows col0.., output columns col0..), whose y tile (mt, nt) is complete
+// after `target` items have counted themselves in (1: this item alone).  HALF_TILE: this item computes half (`half`,
+// 0 or 1) of a y tile twice as wide; its partial sums go to their places in that tile's layout.  False if a wait
+// gave up (the workgroup must exit).
+template <int BN, bool GLU, bool HALF_TILE = false>
 __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem, const int* s_rows, int e, int n_rows,
-                                         int mt, int nt, int s, int* s_stop) {
+                                         int mt, int nt, int s, int col0, int target, int half, int* s_stop) {
   constexpr int BM = 256, BK = 64;
   constexpr int WM = 128, WN = BN / 2, MI = WM / 32, NI = WN / 32;
   constexpr int OUT_BN = GLU ? BN / 2 : BN;
@@ -515,7 +620,7 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
     const int i = 8 * q + (lane >> 3);
     int wrow;
     if (GLU) wrow = i < BN / 2 ? nt * (BN / 2) + i : a.f + nt * (BN / 2) + (i - BN / 2);
-    else wrow = nt * BN + i;
+    else wrow = col0 + i;
     boff[jj] = (uint32_t)wrow * row_bytes + (chunk0 ^ ((uint32_t)(q & 1) << 4));
   }
   f32x16_t acc[MI][NI];
@@ -638,20 +743,21 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
       *(__bf16*)(smem + row * OUT_ROW + chunk * 16 + (col & 7) * 2) = (__bf16)o;  // round to nearest even
     }
   };
-  bool staged = false;
   if (!GLU && a.S > 1) {
     // split-K: every split stores its fp32 partial sums (thread tid keeps its accumulators at float4 chunk
-    // ((mi * NI + ni) * 4 + q4) * 256 + tid of its slot), waits for the stores to complete, and counts itself in;
-    // the split that arrives last adds the slots in split order: y = ((p_0 + p_1) + ...) + p_{S-1}, the same
-    // association whichever split is last, so the result is the same on every call.
+    // ((mi * NI + ni) * 4 + q4) * 256 + tid of its slot; a half item writes the chunks that the full tile's
+    // threads of its columns would), waits for the stores to complete, and counts itself in; the item that
+    // completes the tile sums it (reduce_tile)
+    constexpr int BNF = HALF_TILE ? 2 * BN : BN, NIF = BNF / 2 / 32, SLOT4 = BM * BNF / 4;
     const int64_t tile = (int64_t)mt * a.n_nt2 + nt;
-    f32x4_t* slots = (f32x4_t*)(a.partial + tile * a.S * (BM * BN));
-    constexpr int SLOT4 = BM * BN / 4;
+    f32x4_t* slot = (f32x4_t*)(a.partial + tile * a.S * (BM * BNF)) + (int64_t)s * SLOT4;
+    const int tid_f = HALF_TILE ? (wm * 2 + half) * 64 + lane : tid;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
-        f32x4_t* dst = slots + (int64_t)s * SLOT4 + (mi * NI + ni) * 4 * 256 + tid;
+        const int b = HALF_TILE ? mi * NIF + wn * NI + ni : mi * NI + ni;
+        f32x4_t* dst = slot + b * 4 * 256 + tid_f;
         const f32x16_t v = acc[mi][ni];
         store16_coherent(dst, __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v, v, 0, 1, 2, 3)));
         store16_coherent(dst + 256, __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v, v, 4, 5, 6, 7)));
@@ -662,87 +768,31 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
     __syncthreads();  // every thread's partial stores completed; every wave is done with the operand stages
     if (tid == 0) *s_stop = (int)arrive(&a.scount[tile], a.epoch);
     __syncthreads();
-    if (*s_stop != a.S - 1) return true;  // not the last split of this tile
+    if (*s_stop != target - 1) return true;  // the tile is not complete yet
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    auto ld16 = [&](const f32x4_t* src) {
-      const f32x4_t q0 = __builtin_nontemporal_load(src), q1 = __builtin_nontemporal_load(src + 256);
-      const f32x4_t q2 = __builtin_nontemporal_load(src + 512), q3 = __builtin_nontemporal_load(src + 768);
-      const f32x8_t h0 = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
-      const f32x8_t h1 = __builtin_shufflevector(q2, q3, 0, 1, 2, 3, 4, 5, 6, 7);
-      return (f32x16_t)__builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
-    };
-    // With the split count fixed at compile time, every slot of a 32 x 32 block (this split's own too) is loaded
-    // in one go, D blocks ahead of the one being summed, so about D round trips of the reads are in flight
-    // instead of one, and each sum goes straight to the LDS tile (the accumulators are dead by then).  The loads
-    // and sums of consecutive blocks are kept in order so that the register ring is all that is live.  Other
-    // split counts sum one block and split at a time into the accumulators.
-    auto ring_sum = [&](auto S_) {
-      constexpr int SC = decltype(S_)::value, NB = MI * NI, D = SC <= 2 ? 3 : 2;
-      f32x16_t ring[D + 1][SC];
-      auto load = [&](int b) {
-#pragma unroll
-        for (int sp = 0; sp < SC; ++sp) ring[b % (D + 1)][sp] = ld16(slots + (int64_t)sp * SLOT4 + b * 4 * 256 + tid);
-      };
-#pragma unroll
-      for (int b = 0; b < D; ++b) load(b);
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        if (b + D < NB) load(b + D);
-        __builtin_amdgcn_sched_barrier(0);
-        f32x16_t t = ring[b % (D + 1)][0];
-#pragma unroll
-        for (int sp = 1; sp < SC; ++sp) t += ring[b % (D + 1)][sp];
-        stage(b / NI, b % NI, t, t);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    staged = true;
-    if (a.S == 2) ring_sum(std::integral_constant<int, 2>{});
-    else if (a.S == 3) ring_sum(std::integral_constant<int, 3>{});
-    else if (a.S == 4) ring_sum(std::integral_constant<int, 4>{});
-    else {
-      staged = false;
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          const f32x4_t* src = slots + (mi * NI + ni) * 4 * 256 + tid;
-          f32x16_t t = s == 0 ? acc[mi][ni] : ld16(src);
-          for (int sp = 1; sp < a.S; ++sp) t += sp == s ? acc[mi][ni] : ld16(src + (int64_t)sp * SLOT4);
-          acc[mi][ni] = t;
-        }
-    }
+    reduce_tile<BNF>(a, smem, s_rows, n_rows, mt, nt);
+    return true;
   }
-  if (!staged) {
-    __syncthreads();  // every wave is done with the operand stages
+  __syncthreads();  // every wave is done with the operand stages
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < NO; ++ni) stage(mi, ni, acc[mi][ni], acc[mi][GLU ? ni + NI / 2 : ni]);
-  }
+    for (int ni = 0; ni < NO; ++ni) stage(mi, ni, acc[mi][ni], acc[mi][GLU ? ni + NI / 2 : ni]);
   __syncthreads();
-  // 8 chunks per thread at a time: their LDS reads first, then their stores, so neither latency is paid per chunk
-  constexpr int ITER = BM * CPR / 256, UN = ITER < 8 ? ITER : 8;
-  static_assert(ITER % UN == 0, "store loop unroll");
-#pragma unroll 1
-  for (int i0 = 0; i0 < ITER; i0 += UN) {
-    u32x4_t v[UN];
-#pragma unroll
-    for (int u = 0; u < UN; ++u) {
-      const int idx = tid_e + (i0 + u) * 256, row = idx / CPR, ch = idx - row * CPR;
-      v[u] = *(const u32x4_t*)(smem + row * OUT_ROW + ((ch ^ (row & 7)) << 4));
-    }
-#pragma unroll
-    for (int u = 0; u < UN; ++u) {
-      const int idx = tid_e + (i0 + u) * 256, row = idx / CPR, ch = idx - row * CPR;
-      if (row < n_rows) store16_coherent(Cb + ((int64_t)s_rows[row] * ldc + (int64_t)nt * OUT_BN) * 2 + ch * 16, v[u]);
-    }
-  }
+  store_rows<OUT_BN>(smem, Cb + (GLU ? (int64_t)nt * OUT_BN : (int64_t)col0) * 2, ldc, s_rows, n_rows, tid_e);
   if (GLU) {
     publish(&a.flags1[(int64_t)mt * a.n_nt1 + nt], a.epoch);
-  } else {
+  } else if (target == 1) {
     publish(&a.flags2[(int64_t)mt * a.n_nt2 + nt], a.epoch);
     if (a.ts != nullptr && tid == 0) atomicMax((unsigned long long*)&a.ts[1], (unsigned long long)moe_clock());
+  } else {  // a half of an unsplit tile: the second half to finish publishes
+    wait_stores();
+    __syncthreads();
+    const int64_t tile = (int64_t)mt * a.n_nt2 + nt;
+    if (tid == 0 && (int)arrive(&a.scount[tile], a.epoch) == target - 1) {
+      __hip_atomic_store(&a.flags2[tile], a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (a.ts != nullptr) atomicMax((unsigned long long*)&a.ts[1], (unsigned long long)moe_clock());
+    }
   }
   return true;
 }
@@ -763,9 +813,39 @@ __global__ __launch_bounds__(256, 1) void k_ffn_bf16(FusedArgs a) {
   const int n_items = n_mt * (a.n_nt1 + a.n_nt2 * a.S);
   const int tid = threadIdx.x;
   const int C = a.n_cons, G = gridDim.x - C;
+  // With every GEMM1 item first, no row tile is returned before the GEMM1 part of the list is done, so the
+  // consumer workgroups first take kc GEMM1 items each from the head of the list: just enough that the producers'
+  // share fits in as few rounds as the whole list would on all workgroups, and no more than the consumers finish
+  // before the GEMM1 part ends.  GEMM1 items wait on nothing, so the consumer's later waits still end.
+  int kc = 0;
+  if (C > 0 && a.interleave == 0) {
+    const int rounds = (n_items + G + C - 1) / (G + C), over = n_items - rounds * G;
+    kc = over > 0 ? (over + C - 1) / C : 0;
+    kc = min(kc, n_mt * a.n_nt1 / (G + C));
+  }
+  // The producers' last round holds q items.  When they are GEMM2 items and at most half a round, each becomes
+  // two items of half the tile width (columns [0, BN2/2) and [BN2/2, BN2) of its y tile), so that the round
+  // keeps twice as many CUs busy: a half-width tile takes ~0.7 of a full one's time.  Every output element is
+  // accumulated as before, so results do not change.  List items i >= i_tail are then the halves, two per item.
+  int i_tail = n_items, n_list = n_items;
+  if (BN2 >= 128 && n_items > C * kc) {
+    const int np = n_items - C * kc, q = np - (np - 1) / G * G;
+    const int nw = (n_mt + a.window - 1) / a.window, Wl = n_mt - (nw - 1) * a.window;
+    const int g2_tail = a.interleave == 0 ? n_mt * a.n_nt2 * a.S
+                                          : (Wl + (nw > 1 ? a.window : 0)) * a.n_nt2 * a.S;  // trailing GEMM2 items
+    if (2 * q <= G && q <= g2_tail) {
+      i_tail = n_items - q;
+      n_list = n_items + q;
+    }
+  }
   bool first = true;
   auto run = [&](int item) {  // one item of the list; false once the launch has failed
     __syncthreads();  // previous item done with LDS and the header
+    int half = -1;
+    if (item >= i_tail) {
+      half = (item - i_tail) & 1;
+      item = i_tail + ((item - i_tail) >> 1);
+    }
     FfnItem it;
     if (a.interleave == 0 && item < n_mt * a.n_nt1) {
       // GEMM1 part of the list with every GEMM1 item first: expert by expert (each expert's row tiles are one run
@@ -790,22 +870,22 @@ __global__ __launch_bounds__(256, 1) void k_ffn_bf16(FusedArgs a) {
     first = false;
     __syncthreads();
     const int e = __builtin_amdgcn_readfirstlane(s_hdr[0]), n_rows = __builtin_amdgcn_readfirstlane(s_hdr[1]);
-    if (it.kind == 1) return ffn_tile<BN1, true>(a, smem, s_rows, e, n_rows, it.mt, it.nt, 0, &s_stop);
+    if (it.kind == 1) return ffn_tile<BN1, true>(a, smem, s_rows, e, n_rows, it.mt, it.nt, 0, 0, 1, -1, &s_stop);
     // the h columns this split reads: column tiles [s, s+1) * n_nt1 / S of the first GEMM
     const int per = a.n_nt1 / a.S;
-    return wait_flags(a.flags1 + (int64_t)it.mt * a.n_nt1 + it.s * per, per, a.epoch, a.budget, a.status, &s_stop) &&
-           ffn_tile<BN2, false>(a, smem, s_rows, e, n_rows, it.mt, it.nt, it.s, &s_stop);
+    if (!wait_flags(a.flags1 + (int64_t)it.mt * a.n_nt1 + it.s * per, per, a.epoch, a.budget, a.status, &s_stop))
+      return false;
+    // items that complete the y tile: its S splits, one more for each split that is halved
+    const int last = item + (a.S - 1 - it.s) * it.stride;
+    int target = a.S;
+    for (int sp = 0; sp < a.S; ++sp) target += last - (a.S - 1 - sp) * it.stride >= i_tail;
+    if (half < 0)
+      return ffn_tile<BN2, false>(a, smem, s_rows, e, n_rows, it.mt, it.nt, it.s, it.nt * BN2, target, -1, &s_stop);
+    if constexpr (BN2 >= 128)
+      return ffn_tile<BN2 / 2, false, true>(a, smem, s_rows, e, n_rows, it.mt, it.nt, it.s,
+                                            it.nt * BN2 + half * (BN2 / 2), target, half, &s_stop);
+    return false;
   };
-  // With every GEMM1 item first, no row tile is returned before the GEMM1 part of the list is done, so the
-  // consumer workgroups first take kc GEMM1 items each from the head of the list: just enough that the producers'
-  // share fits in as few rounds as the whole list would on all workgroups, and no more than the consumers finish
-  // before the GEMM1 part ends.  GEMM1 items wait on nothing, so the consumer's later waits still end.
-  int kc = 0;
-  if (C > 0 && a.interleave == 0) {
-    const int rounds = (n_items + G + C - 1) / (G + C), over = n_items - rounds * G;
-    kc = over > 0 ? (over + C - 1) / C : 0;
-    kc = min(kc, n_mt * a.n_nt1 / (G + C));
-  }
   // A producer workgroup b takes items b', b' + G, ... after the consumers' share, b' remapped so that a run of
   // consecutive items goes to the workgroups of one XCD (workgroup b sits on XCD b % 8), which share operand tiles
   // in its L2; all workgroups move through the list in step.  (Claiming items from a counter instead balances the
@@ -820,7 +900,7 @@ __global__ __launch_bounds__(256, 1) void k_ffn_bf16(FusedArgs a) {
     int bid = blockIdx.x - C;
     if ((G & 7) == 0 && (C & 7) == 0) bid = (bid & 7) * (G >> 3) + (bid >> 3);
     i0 = C * kc + bid;
-    i1 = n_items;
+    i1 = n_list;
     step = G;
   }
   for (int item = i0; item < i1; item += step)
@@ -879,7 +959,7 @@ FlagCarve flag_carve(int dtype, int d, int f, int64_t cap_mtiles) {
     const int64_t n1 = f / (gemm1_bn(dtype, f) / 2), S = ffn_splits(dtype, d, f);
     c.flags1 = up(cap_mtiles * n2);
     c.scount = c.flags1 + up(cap_mtiles * n1);
-    c.partial = c.scount + up(S > 1 ? 2 * cap_mtiles * n2 : 0);
+    c.partial = c.scount + up(2 * cap_mtiles * n2);  // split counts; also the halves of unsplit tiles
     c.claim = c.partial + (S > 1 ? cap_mtiles * n2 * S * (int64_t)BF_BM * ffn_gemm2_bn(dtype, d) : 0);
   }
   c.total = c.claim + 2;  // the consumer's 64-bit unit counter

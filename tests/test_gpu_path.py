@@ -150,6 +150,11 @@ SMALL = [
     # 4 k-splits over more than four windows of row tiles: split-major second-GEMM windows (sequential call) and
     # interleaved windows (overlapped call)
     mi.Spec("splitk_windows", R=4, T_o=2400, G=8, E_l=2, k=2, d=256, f=1024, M=32, seed=22),
+    # more items than one round of the producers, the last round at most half full (on 256 CUs: 300 items, 48 and
+    # 44 in the last round of the overlapped and sequential calls): that round's second-GEMM items run as two
+    # half-width items each; with 4 k-splits (halves of splits) and with none (halves counted in by the tile)
+    mi.Spec("splitk_halves", R=4, T_o=3150, G=4, E_l=1, k=2, d=256, f=1024, M=32, seed=23),
+    mi.Spec("halves", R=4, T_o=12800, G=4, E_l=1, k=2, d=256, f=256, M=32, seed=24),
     # fp32 with more transfer segments than a 128-thread consumer workgroup holds in its window at once
     mi.Spec("f32_many_segs", R=8, T_o=400, G=32, E_l=16, k=2, d=128, f=128, M=16, dtype="f32", seed=20),
 ]
