@@ -280,12 +280,14 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm(GemmArgs a) {
 // global_load_lds_dwordx4 in its scalar-base form: lane i moves 16 bytes from base + off into LDS at
 // m0 + 16 * i (m0 is set in the same statement, so no other code depends on it)
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_addr) {
-  // base and lds_addr are the same in every lane; readfirstlane puts them in scalar registers
+  // base and lds_addr are the same in every lane; readfirstlane puts them in scalar registers.  The load takes its
+  // LDS address from M0, which needs one wait state after an SALU write (the s_nop; the compiler adds it only for
+  // loads it emits itself)
   const uint64_t b = (uint64_t)base;
   const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(lds_addr)),
-               "v"(off), "s"((const void*)sb) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(lds_addr)),
+               "v"(off), "s"((const void*)sb) : "memory", "m0");
 }
 
 // this wave's loads have landed in LDS, then the workgroup barrier: after it every wave's have
