@@ -1029,10 +1029,11 @@ int launch_bf16(const FfnLaunch& p, int grid, int n_cons, hipStream_t st, hipEve
   // ~= 11850 / (C f), whatever M and d are; GEMM1 first leaves the last part of the launch for the copies, and
   // the workgroups that finish early help with what is left, so it is used while that ratio stays under about
   // 1/4.  Interleaved windows stream an expert's weight tiles once per window holding its rows, and consecutive
-  // items share fewer of them, which pays only while the local experts' weights (3 d f per expert) fit in the
-  // 256 MB last-level cache; measured: 1 and 2 experts of d = f = 4096 gain, 4 or more lose.
+  // items share fewer of them, which pays only while the local experts' weights (3 d f per expert) take at most
+  // half of the 256 MB last-level cache; measured with d = f = 4096: one expert (100 MB) gains 4%, two (201 MB)
+  // lose 3%, four or more lose more.
   const double w_bytes = 3.0 * p.d * p.f * 2.0 * p.E;
-  a.interleave = n_cons > 0 && (int64_t)n_cons * p.f < 48000 && w_bytes <= 256.0 * 1024 * 1024;
+  a.interleave = n_cons > 0 && (int64_t)n_cons * p.f < 48000 && w_bytes <= 128.0 * 1024 * 1024;
   a.mtile_desc = p.L->mtile_desc;
   a.scalars = p.L->scalars;
   a.sc_nmt = SC_NR + p.R;
