@@ -111,3 +111,29 @@ def test_flag_count_covers_row_tiles():
     base2 = (buf2.ctypes.data + 255) // 256 * 256
     assert B.lib().moe_layout_bind(ctypes.byref(sf), ctypes.c_void_p(base2), nb, ctypes.byref(Lf)) == 0
     assert B.moe_ffn_flags_count(sf) == (Lf.cap_mtiles * (256 // 64) + 63) // 64 * 64 + 2
+
+
+CSRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "expert_output_overlap_amd", "csrc")
+
+
+def test_inline_asm_carries_its_wait_states():
+    """The compiler inserts hazard wait states only around instructions it emits itself, so every inline-assembly
+    statement that needs them carries its own: a store wider than 8 bytes is followed by two wait states before
+    its data registers may be rewritten (s_nop 1), and an SALU write of M0 by one before the LDS-DMA load that
+    reads it (s_nop 0)."""
+    found = {"store": 0, "m0": 0}
+    for fn in sorted(os.listdir(CSRC)):
+        if not fn.endswith((".hip", ".h", ".cpp")):
+            continue
+        src = open(os.path.join(CSRC, fn)).read()
+        for stmt in re.findall(r'asm\s+volatile\s*\(\s*((?:"[^"]*"\s*)+)', src):
+            text = "".join(re.findall(r'"([^"]*)"', stmt)).replace("\\n", "\n").replace("\\t", " ")
+            ins = [l.strip() for l in text.split("\n") if l.strip()]
+            for i, op in enumerate(ins):
+                if re.match(r"(global|buffer|flat)_store_dwordx(3|4)\b", op):
+                    found["store"] += 1
+                    assert i + 1 < len(ins) and re.match(r"s_nop\s+[1-9]", ins[i + 1]), (fn, text)
+                if op.startswith("s_mov_b32 m0"):
+                    found["m0"] += 1
+                    assert i + 2 < len(ins) and ins[i + 1].startswith("s_nop") and "lds" in ins[i + 2], (fn, text)
+    assert found["store"] >= 1 and found["m0"] >= 1, found
