@@ -502,28 +502,40 @@ __global__ __launch_bounds__(256) void k_layout_scatter(const int32_t* __restric
   const int t = c * 64 + lane;
   const bool valid = t < T_o;
   const int64_t tok = (int64_t)r * T_o + t;
+  constexpr int KMAX = 16;  // top-k <= 16
   uint64_t mask = 0;
-  int slot_of[MOE_MAX_LOCAL_EXPERTS > 16 ? 16 : 16];  // slot j -> local expert or -1 (k <= 16)
-  for (int j = 0; j < k; ++j) {
+  int e_of[KMAX];  // slot j -> local expert or -1 (compile-time indices: registers)
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
     int e = -1;
-    if (valid) {
+    if (j < k && valid) {
       e = topk_idx[tok * k + j] - lo;
       if (e < 0 || e >= E) e = -1;
+      if (e < 0) plan[tok * k + j] = -1;
     }
-    slot_of[j] = e;
+    e_of[j] = e;
     if (e >= 0) mask |= 1ull << e;
-    if (valid && e < 0) plan[tok * k + j] = -1;
+  }
+  // lane e holds local expert e's chunk prefix and group offsets (E <= 64), read below with readlane
+  const int32_t* pre = chunk_prefix + ((int64_t)r * n_chunks + c) * E;
+  int pre_l = 0, poff_l = 0, roff_l = 0;
+  if (lane < E) {
+    pre_l = pre[lane];
+    poff_l = padded_off[lane * R + r];
+    roff_l = recv_off[lane * R + r];
   }
   const uint64_t lt = lanemask_lt();
-  const int32_t* pre = chunk_prefix + ((int64_t)r * n_chunks + c) * E;
   for (int e = 0; e < E; ++e) {
     const uint64_t b = __ballot((mask >> e) & 1ull);
+    if (b == 0) continue;
+    const int pe = __builtin_amdgcn_readlane(pre_l, e), po = __builtin_amdgcn_readlane(poff_l, e);
+    const int ro = __builtin_amdgcn_readlane(roff_l, e);
     if ((mask >> e) & 1ull) {
-      const int g = e * R + r;
-      const int rank = pre[e] + __popcll(b & lt);
-      row_src[(int64_t)padded_off[g] + rank] = (int32_t)tok;
-      for (int j = 0; j < k; ++j)
-        if (slot_of[j] == e) plan[tok * k + j] = recv_off[g] + rank;
+      const int rank = pe + __popcll(b & lt);
+      row_src[(int64_t)po + rank] = (int32_t)tok;
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j)
+        if (e_of[j] == e) plan[tok * k + j] = ro + rank;
     }
   }
 }
