@@ -118,9 +118,10 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
     if (P > (a.n_chunks + 7) / 8) P = (a.n_chunks + 7) / 8;
     if (P < 1) P = 1;
     const int L = (a.n_chunks + P - 1) / P;  // chunks per part
-    const int g = tid % NG, p = tid / NG;
+    // consecutive threads take consecutive experts of one owner, whose counts are adjacent in memory
+    const int gi = tid % NG, p = tid / NG;
     const bool act = p < P;
-    const int e = g / R, r = g % R;
+    const int r = gi / E, e = gi - r * E, g = e * R + r;
     int32_t* base = a.chunk_counts + (int64_t)r * a.n_chunks * E + e;
     const int c0 = p * L, c1 = min(c0 + L, a.n_chunks);
     int v[8];
@@ -134,12 +135,12 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
       } else {
         for (int c = c0; c < c1; ++c) sum += base[(int64_t)c * E];
       }
-      s_part[p * NG + g] = sum;
+      s_part[p * NG + gi] = sum;
     }
     __syncthreads();
     if (act) {
       int run = 0;
-      for (int q = 0; q < p; ++q) run += s_part[q * NG + g];
+      for (int q = 0; q < p; ++q) run += s_part[q * NG + gi];
       if (L <= 8) {
 #pragma unroll
         for (int u = 0; u < 8; ++u)
@@ -235,15 +236,36 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
       key1[tid] = k1;
       key2[tid] = k2;
     }
+    int* s_rank = s_order;  // [NG] ranks by key1, then [NG] by key2 (s_order2), before either order is written
+    if (tid < NG) {
+      s_rank[tid] = 0;
+      s_order2[tid] = 0;
+    }
+    __syncthreads();
+    // the ranks of a group's keys are counted by NP threads, each over a slice of the groups
+    {
+      const int NP = SCAN_THREADS / NG >= 4 ? 4 : SCAN_THREADS / NG;
+      const int gi = tid % NG, part = tid / NG;
+      if (part < NP && gi < NG && s_n[gi] > 0) {
+        const uint64_t c1 = key1[gi], c2 = key2[gi];
+        const int h0 = part * NG / NP, h1 = (part + 1) * NG / NP;
+        int r1 = 0, r2 = 0;
+#pragma unroll 8
+        for (int h = h0; h < h1; ++h) {
+          r1 += key1[h] < c1;
+          r2 += key2[h] < c2;
+        }
+        atomicAdd(&s_rank[gi], r1);
+        atomicAdd(&s_order2[gi], r2);
+      }
+    }
     __syncthreads();
     int rank = 0, rank2 = 0;
     if (mine) {
-#pragma unroll 16
-      for (int h = 0; h < NG; ++h) {
-        rank += key1[h] < k1;
-        rank2 += key2[h] < k2;
-      }
+      rank = s_rank[tid];
+      rank2 = s_order2[tid];
     }
+    __syncthreads();  // the ranks are read before the orders are written over them
     int n_ne = 0;
     block_excl_scan(mine ? 1 : 0, s_wsum, &n_ne);
     if (mine) {
