@@ -2,7 +2,7 @@
 // comment 1, section 4.5 / Algorithm 1): rows of each local expert grouped by owner rank, each
 // (expert, owner) group padded to a multiple of the tile height M, remote groups scheduled first.
 //
-//   k_layout_count   per 64-token chunk of one owner: histogram of local experts (wave ballots)
+//   k_layout_count   per 64-token chunk of one owner: histogram of local experts (wave ballots); row_src to -1
 //   k_layout_scan    one workgroup: chunk prefixes, group sizes, wavefront prefix scans of padded sizes,
 //                    band tables, remote-first order, transfer segments, GEMM row tiles
 //   k_layout_scatter per chunk: stable rank of each (token, slot) in its group -> row_src, combine plan
@@ -20,7 +20,12 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 }
 
 __global__ __launch_bounds__(256) void k_layout_count(const int32_t* __restrict__ topk_idx, int T_o, int G, int k,
-                                                      int lo, int E, int n_chunks, int32_t* __restrict__ chunk_counts) {
+                                                      int lo, int E, int n_chunks, int32_t* __restrict__ chunk_counts,
+                                                      int32_t* __restrict__ row_src, int64_t cap_rows) {
+  // every padded row starts as padding (-1); the scatter writes the real rows after the scan
+  const int64_t nthr = (int64_t)gridDim.x * gridDim.y * blockDim.x;
+  for (int64_t p = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x; p < cap_rows; p += nthr)
+    row_src[p] = -1;
   const int wave = threadIdx.x / MOE_WAVE, lane = lane_id();
   const int r = blockIdx.y;
   const int c = blockIdx.x * 4 + wave;
@@ -203,8 +208,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
   }
   __syncthreads();
 
-  // (d) band tables; every padded row of row_src starts as padding (-1), the scatter then writes the real rows
-  for (int p = tid; p < M_pad; p += SCAN_THREADS) a.row_src[p] = -1;
+  // (d) band tables (row_src holds -1 everywhere from the count kernel; the scatter writes the real rows)
   for (int g = tid; g < NG; g += SCAN_THREADS) {
     const int n = s_n[g], off = s_poff[g], e = g / R, r = g - e * R;
     for (int row = 0, b = off / M; row < n; row += M, ++b) {
@@ -591,7 +595,7 @@ int launch_layout(const LayoutLaunch& p, hipStream_t st) {
   const int n_chunks = (p.T_o + 63) / 64;
   if (n_chunks > 0)
     hipLaunchKernelGGL(k_layout_count, dim3((n_chunks + 3) / 4, p.R), dim3(256), 0, st, p.topk_idx, p.T_o, p.G, p.k,
-                       p.lo, p.E, n_chunks, p.L->chunk_counts);
+                       p.lo, p.E, n_chunks, p.L->chunk_counts, p.L->row_src, p.L->cap_rows);
   ScanArgs a;
   a.R = p.R;
   a.T_o = p.T_o;
