@@ -571,11 +571,15 @@ __device__ __forceinline__ void reduce_tile(const FusedArgs& a, unsigned char* s
 // split s.  GLU: the first GEMM (A = x_pad rows, B = gate rows nt*BN/2.. and up rows f + nt*BN/2..); else the
 // second (A = h rows, B = down-projection rows col0.., output columns col0..), whose y tile (mt, nt) is complete
 // after `target` items have counted themselves in (1: this item alone).  HALF_TILE: this item computes half (`half`,
-// 0 or 1) of a y tile twice as wide; its partial sums go to their places in that tile's layout.  False if a wait
-// gave up (the workgroup must exit).
+// 0 or 1) of a y tile twice as wide; its partial sums go to their places in that tile's layout.  A tile that this
+// item completes alone (an h tile, an unsplit y tile) is not published here: its flag goes to *s_pend (*s_pend_y:
+// a y tile), and the workgroup publishes it once the stores have completed, at the start of its next item or after
+// its last, so that the stores drain while the next item's row list loads.  False if a wait gave up (the
+// workgroup must exit).
 template <int BN, bool GLU, bool HALF_TILE = false>
 __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem, const int* s_rows, int e, int n_rows,
-                                         int mt, int nt, int s, int col0, int target, int half, int* s_stop) {
+                                         int mt, int nt, int s, int col0, int target, int half, int* s_stop,
+                                         uint32_t** s_pend, int* s_pend_y) {
   constexpr int BM = 256, BK = 64;
   constexpr int WM = 128, WN = BN / 2, MI = WM / 32, NI = WN / 32;
   constexpr int OUT_BN = GLU ? BN / 2 : BN;
@@ -782,11 +786,11 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
     for (int ni = 0; ni < NO; ++ni) stage(mi, ni, acc[mi][ni], acc[mi][GLU ? ni + NI / 2 : ni]);
   __syncthreads();
   store_rows<OUT_BN>(smem, Cb + (GLU ? (int64_t)nt * OUT_BN : (int64_t)col0) * 2, ldc, s_rows, n_rows, tid_e);
-  if (GLU) {
-    publish(&a.flags1[(int64_t)mt * a.n_nt1 + nt], a.epoch);
-  } else if (target == 1) {
-    publish(&a.flags2[(int64_t)mt * a.n_nt2 + nt], a.epoch);
-    if (a.ts != nullptr && tid == 0) atomicMax((unsigned long long*)&a.ts[1], (unsigned long long)moe_clock());
+  if (GLU || target == 1) {
+    if (tid == 0) {
+      *s_pend = GLU ? &a.flags1[(int64_t)mt * a.n_nt1 + nt] : &a.flags2[(int64_t)mt * a.n_nt2 + nt];
+      *s_pend_y = GLU ? 0 : 1;
+    }
   } else {  // a half of an unsplit tile: the second half to finish publishes
     wait_stores();
     __syncthreads();
@@ -808,12 +812,28 @@ __global__ __launch_bounds__(256, 1) void k_ffn_bf16(FusedArgs a) {
   __shared__ int s_rows[MOE_MT_ROWS];
   __shared__ int s_hdr[MOE_MT_HDR];
   __shared__ int s_stop;
+  __shared__ uint32_t* s_pend;  // flag of the previous item, published once its stores have completed
+  __shared__ int s_pend_y;
 
   if (load_status(a.status) != 0) return;
   if (a.n_cons > 0 && blockIdx.x == 0) consumer_stamp(a.cons);
   const int n_mt = a.scalars[a.sc_nmt];
   const int n_items = n_mt * (a.n_nt1 + a.n_nt2 * a.S);
   const int tid = threadIdx.x;
+  if (tid == 0) s_pend = nullptr;
+  // every wave's stores of the previous item have completed, then its flag (a wait on it may come next)
+  auto flush = [&]() {
+    uint32_t* f = s_pend;
+    if (f == nullptr) return;
+    const int y = s_pend_y;
+    wait_stores();
+    __syncthreads();
+    if (tid == 0) {
+      __hip_atomic_store(f, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (y && a.ts != nullptr) atomicMax((unsigned long long*)&a.ts[1], (unsigned long long)moe_clock());
+      s_pend = nullptr;
+    }
+  };
   const int C = a.n_cons, G = gridDim.x - C;
   // With every GEMM1 item first, no row tile is returned before the GEMM1 part of the list is done, so the
   // consumer workgroups first take kc GEMM1 items each from the head of the list: just enough that the producers'
@@ -871,8 +891,10 @@ __global__ __launch_bounds__(256, 1) void k_ffn_bf16(FusedArgs a) {
     if (a.ts != nullptr && first && tid == 0) atomicMin((unsigned long long*)&a.ts[0], (unsigned long long)moe_clock());
     first = false;
     __syncthreads();
+    flush();
     const int e = __builtin_amdgcn_readfirstlane(s_hdr[0]), n_rows = __builtin_amdgcn_readfirstlane(s_hdr[1]);
-    if (it.kind == 1) return ffn_tile<BN1, true>(a, smem, s_rows, e, n_rows, it.mt, it.nt, 0, 0, 1, -1, &s_stop);
+    if (it.kind == 1)
+      return ffn_tile<BN1, true>(a, smem, s_rows, e, n_rows, it.mt, it.nt, 0, 0, 1, -1, &s_stop, &s_pend, &s_pend_y);
     // the h columns this split reads: column tiles [s, s+1) * n_nt1 / S of the first GEMM
     const int per = a.n_nt1 / a.S;
     if (!wait_flags(a.flags1 + (int64_t)it.mt * a.n_nt1 + it.s * per, per, a.epoch, a.budget, a.status, &s_stop))
@@ -882,10 +904,11 @@ __global__ __launch_bounds__(256, 1) void k_ffn_bf16(FusedArgs a) {
     int target = a.S;
     for (int sp = 0; sp < a.S; ++sp) target += last - (a.S - 1 - sp) * it.stride >= i_tail;
     if (half < 0)
-      return ffn_tile<BN2, false>(a, smem, s_rows, e, n_rows, it.mt, it.nt, it.s, it.nt * BN2, target, -1, &s_stop);
+      return ffn_tile<BN2, false>(a, smem, s_rows, e, n_rows, it.mt, it.nt, it.s, it.nt * BN2, target, -1, &s_stop,
+                                  &s_pend, &s_pend_y);
     if constexpr (BN2 >= 128)
       return ffn_tile<BN2 / 2, false, true>(a, smem, s_rows, e, n_rows, it.mt, it.nt, it.s,
-                                            it.nt * BN2 + half * (BN2 / 2), target, half, &s_stop);
+                                            it.nt * BN2 + half * (BN2 / 2), target, half, &s_stop, &s_pend, &s_pend_y);
     return false;
   };
   // A producer workgroup b takes items b', b' + G, ... after the consumers' share, b' remapped so that a run of
@@ -907,6 +930,8 @@ __global__ __launch_bounds__(256, 1) void k_ffn_bf16(FusedArgs a) {
   }
   for (int item = i0; item < i1; item += step)
     if (!run(item)) return;
+  __syncthreads();
+  flush();
   // then every workgroup returns segments until no copy unit is left
   if (C > 0) consumer_role(a.cons);
 }
