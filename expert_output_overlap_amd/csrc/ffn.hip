@@ -11,7 +11,10 @@
 // by construction; every producer workgroup joins the return once its own items are done.
 // Row tiles are the layout's GEMM row tiles: up to BM real rows of one expert, each expert's rows packed into
 // consecutive tiles, so padding rows cost nothing.  Items (row tile, column tile) are visited window by window
-// (band_window row tiles) for weight reuse, and consecutive items go to workgroups on the same XCD.
+// (band_window row tiles) for weight reuse, and consecutive items go to workgroups on the same XCD.  When the
+// producers' last round is at most half full, its GEMM2 items run as two half-width items each.  A tile that one
+// item completes is published at the start of the workgroup's next item (before any of its waits), so that the
+// stores drain under that item's first loads.
 #include <hip/hip_ext.h>
 
 #include <atomic>

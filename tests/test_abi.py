@@ -137,3 +137,13 @@ def test_inline_asm_carries_its_wait_states():
                     found["m0"] += 1
                     assert i + 2 < len(ins) and ins[i + 1].startswith("s_nop") and "lds" in ins[i + 2], (fn, text)
     assert found["store"] >= 1 and found["m0"] >= 1, found
+
+
+def test_full_size_parity_runs_in_the_bench_configuration():
+    """The full-size GPU parity tests use the consumer partition that bench.py times by default."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    bench = open(os.path.join(root, "bench.py")).read()
+    m = re.search(r'"--consumer-cus", type=int, default=(\d+)', bench)
+    tests = open(os.path.join(root, "tests", "test_gpu_path.py")).read()
+    t = re.search(r"^BENCH_CONSUMER_CUS = (\d+)", tests, re.M)
+    assert m and t and int(m.group(1)) == int(t.group(1))

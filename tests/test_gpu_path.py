@@ -194,6 +194,7 @@ def test_small_full_parity(s):
 
 
 FULL = ["mixtral", "skew", "sweep1", "sweep2", "sweep4", "sweep8", "sweep16", "deepseek"]
+BENCH_CONSUMER_CUS = 8  # bench.py's default partition (and its default band window)
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -205,7 +206,7 @@ def test_full_size_parity(name):
     P, lay = run.P, run.lay
     for r in range(s.R):
         P.recv[r].fill_(float("nan"))
-    run.ffn(mode=0, consumer_cus=16)
+    run.ffn(mode=0, consumer_cus=BENCH_CONSUMER_CUS)
     P.combine()
     torch.cuda.synchronize()
     assert P.status() == B.MOE_OK
@@ -238,7 +239,7 @@ def test_full_size_parity(name):
     # sequential == overlapped, bitwise
     recv_ovl = [bits(b) for b in P.recv]
     out_ovl = bits(P.out)
-    run.ffn(mode=1, consumer_cus=16)
+    run.ffn(mode=1, consumer_cus=BENCH_CONSUMER_CUS)
     P.combine()
     torch.cuda.synchronize()
     for r in range(s.R):
