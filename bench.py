@@ -100,7 +100,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="mixtral")
-    ap.add_argument("--consumer-cus", type=int, default=8)
+    ap.add_argument("--consumer-cus", type=int, default=0,
+                    help="consumer CUs of the overlapped launch (0 = the library's pick for the shape)")
     ap.add_argument("--mgb", type=int, default=1)
     ap.add_argument("--band-window", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -132,7 +133,9 @@ def main():
     P.route(dev["logits"])
     torch.cuda.synchronize()
     w1, w2 = dev["w_gate_up"], dev["w_down"]
-    cus = args.consumer_cus
+    # the partition the library uses for consumer_cus = 0, resolved here so the line reports it
+    cus = args.consumer_cus or B.moe_pick_consumer_cus(P.shape, torch.cuda.get_device_properties(0).multi_processor_count)
+    assert cus > 0, B.moe_last_error()
 
     def step(mode=0, timestamps=False):
         P.layout(dev["x"])
@@ -214,6 +217,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": s.dtype, "data": "synthetic",
         "config": {"workload": workload_name(s), "M_real": M_real, "M_pad": M_pad, "gemm_row_tiles": sc["n_mtiles"], "consumer_cus": cus,
+                   "consumer_cus_chosen_by": "option" if args.consumer_cus else "library pick",
                    "band_window": args.band_window or 4, "mode": "overlapped" if args.mode == 0 else "sequential"},
         "pct_bf16_peak_step": round(100 * value / peak, 2),
         "ffn_tflops_overlapped": round(ffn_tflops, 2),

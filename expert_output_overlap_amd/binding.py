@@ -19,7 +19,8 @@ MOE_BF16, MOE_F32 = 0, 1
 MOE_SEG_FIELDS = 8
 MT_FIELDS = 260
 EXPORTS = ["moe_last_error", "moe_version", "moe_route", "moe_layout_capacity_rows", "moe_layout_workspace_bytes",
-           "moe_layout_bind", "moe_layout_build", "moe_read_status", "moe_ffn_flags_count", "moe_expert_ffn_overlap",
+           "moe_layout_bind", "moe_layout_build", "moe_read_status", "moe_ffn_flags_count", "moe_pick_consumer_cus",
+           "moe_expert_ffn_overlap",
            "moe_combine", "moe_set_kernel_timing", "moe_kernel_times"]
 
 
@@ -69,6 +70,7 @@ def lib():
             "moe_layout_bind": ([ps, vp, i64, pl], i32),
             "moe_layout_build": ([ps, vp, vp, pl, vp, vp], i32),
             "moe_read_status": ([pl, vp], i32), "moe_ffn_flags_count": ([ps], i64),
+            "moe_pick_consumer_cus": ([ps, i32], i32),
             "moe_expert_ffn_overlap": ([ps, pl, vp, vp, vp, vp, vp, vp, vp, pc, vp], i32),
             "moe_combine": ([ps, pl, vp, vp, vp, vp], i32),
             "moe_set_kernel_timing": ([i32], i32), "moe_kernel_times": ([ctypes.POINTER(ctypes.c_double)], i32),
@@ -144,6 +146,10 @@ def moe_read_status(layout: moe_layout, stream=None) -> int:
 
 def moe_ffn_flags_count(shape: moe_shape) -> int:
     return lib().moe_ffn_flags_count(ctypes.byref(shape))
+
+
+def moe_pick_consumer_cus(shape: moe_shape, n_cu: int) -> int:
+    return lib().moe_pick_consumer_cus(ctypes.byref(shape), n_cu)
 
 
 def moe_expert_ffn_overlap(shape: moe_shape, layout: moe_layout, x_pad, w_gate_up, w_down, h_ws, y_pad, recv,

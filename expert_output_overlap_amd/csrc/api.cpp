@@ -2,6 +2,8 @@
 // Host side only: argument checks, workspace carving, launches on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <cmath>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -273,6 +275,20 @@ int64_t moe_ffn_flags_count(const moe_shape* s) {
   return ffn_flag_words(s->dtype, s->d, s->f, o.cap_mtiles);
 }
 
+int32_t moe_pick_consumer_cus(const moe_shape* s, int32_t n_cu) {
+  if (!check_shape(s).empty() || n_cu < 2) return -1;
+  // Returning 4 M_real d bytes (bf16 rows read and written) at ~45 GB/s per consumer CU, next to 6 M_real d f
+  // FFN flops at ~0.8 PFLOP/s, takes 11850 / (C f) of the FFN's time on C consumer CUs, whatever M_real and d
+  // are.  Take the smallest multiple of 8 (the same count on each of the 8 XCDs) at which the consumers alone
+  // would finish the return in half the FFN's time, so tiles published late still have time to go: at least
+  // 8, at most 32 (the range measured) and a quarter of the CUs.
+  const int cap = std::max(1, std::min(32, n_cu / 4));
+  if (s->dtype != MOE_BF16) return std::min(8, cap);
+  const int need = (int)std::ceil(2.0 * 11850.0 / s->f);
+  const int c = std::max(8, (need + 7) / 8 * 8);
+  return std::min(c, cap);
+}
+
 int moe_expert_ffn_overlap(const moe_shape* s, const moe_layout* L, const void* x_pad, const void* w_gate_up,
                            const void* w_down, void* h_ws, void* y_pad, void* const* recv, uint32_t* flags,
                            const moe_overlap_cfg* cfg, void* stream) {
@@ -292,8 +308,10 @@ int moe_expert_ffn_overlap(const moe_shape* s, const moe_layout* L, const void* 
   if (hipGetDevice(&dev) != hipSuccess) return fail(MOE_EHIP, "hipGetDevice failed");
   const int n_cu = device_cus(dev);
   if (n_cu <= 0) return fail(MOE_EHIP, "cannot query the CU count");
-  if (cfg->consumer_cus < 1 || cfg->consumer_cus > n_cu / 2)
-    return fail(MOE_EINVAL, "consumer_cus must be in [1, CUs/2]");
+  if (cfg->consumer_cus < 0 || cfg->consumer_cus > n_cu / 2)
+    return fail(MOE_EINVAL, "consumer_cus must be 0 (library pick) or in [1, CUs/2]");
+  const int C = cfg->consumer_cus ? cfg->consumer_cus : moe_pick_consumer_cus(s, n_cu);
+  if (C < 1) return fail(MOE_EINVAL, "no consumer partition fits this device");
 
   FfnLaunch p;
   p.dtype = s->dtype;
@@ -314,7 +332,6 @@ int moe_expert_ffn_overlap(const moe_shape* s, const moe_layout* L, const void* 
   p.watchdog_ticks = cfg->watchdog_ticks ? cfg->watchdog_ticks : 200000000ull;
   p.timestamps = cfg->timestamps;
   p.cap_mtiles = layout_offsets(s).cap_mtiles;
-  const int C = cfg->consumer_cus;
 
   if (cfg->mode == 2) {  // return only
     if (launch_ffn_consumer(p, C, st)) return fail(MOE_EHIP, "consumer launch failed");

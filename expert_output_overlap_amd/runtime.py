@@ -69,7 +69,7 @@ class MoePath:
     def layout(self, x: torch.Tensor, topk_idx: torch.Tensor | None = None, stream=None):
         B.moe_layout_build(self.shape, self.topk_idx if topk_idx is None else topk_idx, x, self.L, self.x_pad, stream)
 
-    def ffn(self, w_gate_up, w_down, mode=0, consumer_cus=16, band_window=0, timestamps=False, watchdog_ticks=0,
+    def ffn(self, w_gate_up, w_down, mode=0, consumer_cus=0, band_window=0, timestamps=False, watchdog_ticks=0,
             epoch=None, stream=None):
         if epoch is None:
             self.epoch += 1

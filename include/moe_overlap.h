@@ -93,7 +93,8 @@ typedef struct {
 /* Knobs of moe_expert_ffn_overlap. */
 typedef struct {
   int32_t consumer_cus;    /* C: consumer workgroups, one per CU, in [1, CUs/2]; the producer's persistent
-                              launch runs one workgroup on each other CU */
+                              launch runs one workgroup on each other CU.  0 = the library picks C for the
+                              shape (moe_pick_consumer_cus) */
   int32_t mode;            /* 0 = overlapped (the C consumer workgroups and the producer workgroups in one
                                   launch, on disjoint CUs; a producer workgroup joins the return once its
                                   own items are done),
@@ -162,6 +163,15 @@ int moe_read_status(const moe_layout* L, void* stream);
  * to 8); last, one 64-bit counter of the return's copy units.  Zero the buffer once before the first call;
  * afterwards it is epoch-valued. */
 int64_t moe_ffn_flags_count(const moe_shape* s);
+
+/* Consumer partition the library uses when cfg->consumer_cus is 0, for a device of n_cu CUs; -1 if the shape
+ * is invalid or n_cu < 2.  Host only (no device call).  Sized from the ratio of the return's time to the FFN's
+ * (review page: "If this is right" reports the overlap collapsing with too few consumer SMs; "Where Pith is
+ * reading between the lines" proposes sizing the partition at run time): the return moves
+ * 4 bytes per routed row and hidden unit (bf16, read and written), the FFN 6 f flops, so the ratio depends on f
+ * alone; the pick is the smallest multiple of 8 at which the consumers alone would return everything in half
+ * the FFN's time at the measured per-CU copy rate and FFN rate, in [8, min(32, n_cu/4)] (fp32: 8). */
+int32_t moe_pick_consumer_cus(const moe_shape* s, int32_t n_cu);
 
 /* Expert SwiGLU FFN over the padded layout with the return of each finished row-band segment to its
  * owner (review page: "The pith", "Core claim", "What carries the argument").

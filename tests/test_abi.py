@@ -48,6 +48,29 @@ def test_capacity_matches_bound(kw):
     assert cap == oracle.capacity_rows(s.R, s.tokens_per_owner, s.num_local_experts, s.top_k, s.tile_m)
 
 
+@pytest.mark.parametrize("kw,want", [
+    (dict(), 8),                                                       # f = 14336
+    (dict(tokens_per_owner=4096, num_global_experts=8, num_local_experts=2, f=4096), 8),
+    (dict(R=8, tokens_per_owner=2048, num_global_experts=256, num_local_experts=32, top_k=8, d=7168, f=2048), 16),
+    (dict(tokens_per_owner=2048, num_global_experts=64, num_local_experts=16, top_k=6, d=2048, f=1408,
+          tile_m=64), 24),
+    (dict(d=64, f=128, tile_m=16), 32),                                # capped at 32
+    (dict(d=64, f=128, tile_m=16, dtype=B.MOE_F32), 8),
+])
+def test_consumer_partition_pick(kw, want):
+    """The library's partition: the smallest multiple of 8 at which the consumers alone return the rows in half the
+    FFN's time, by the rate model (11850 / (C f) of the FFN's time), within [8, min(32, CUs/4)]."""
+    s = shape(**kw)
+    c = B.moe_pick_consumer_cus(s, 256)
+    assert c == want
+    if s.dtype == B.MOE_BF16 and 8 < c < 32:
+        assert 11850.0 / (c * s.f) <= 0.5 < 11850.0 / ((c - 8) * s.f)
+    assert B.moe_pick_consumer_cus(s, 16) == min(want, 4)   # a quarter of a small device's CUs
+    assert B.moe_pick_consumer_cus(s, 4) == 1
+    assert B.moe_pick_consumer_cus(s, 1) == -1
+    assert B.moe_pick_consumer_cus(shape(f=0), 256) == -1
+
+
 @pytest.mark.parametrize("bad", [dict(R=0), dict(R=17), dict(d=96), dict(f=0), dict(tile_m=24), dict(tile_m=272),
                                  dict(top_k=0), dict(top_k=9), dict(num_local_experts=3), dict(self_rank=4),
                                  dict(dtype=7), dict(seg_bands=0), dict(tokens_per_owner=-1),
