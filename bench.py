@@ -34,10 +34,14 @@ def workload_name(s) -> str:
 
 
 def overlap_stats(ts: np.ndarray, n_segs: int, tick_ns: float = 10.0) -> dict:
-    """Fraction of consumer copy time inside [first producer item start, last flag publish]."""
+    """Fraction of consumer copy time inside [first producer item start, last flag publish], over the segments the
+    consumer copied (the self owner's segments have no copy: the producer stores those rows itself)."""
     p0, p1 = int(ts[0]), int(ts[1])
-    s = ts[2:2 + 2 * n_segs:2].astype(np.int64)
-    e = ts[3:3 + 2 * n_segs:2].astype(np.int64)
+    s = ts[2:2 + 2 * n_segs:2]
+    e = ts[3:3 + 2 * n_segs:2]
+    copied = e != 0
+    s, e = s[copied].astype(np.int64), e[copied].astype(np.int64)
+    n_segs = int(copied.sum())
     dur = np.maximum(e - s, 0)
     inter = np.maximum(np.minimum(e, p1) - np.maximum(s, p0), 0)
     tot = dur.sum()
@@ -209,14 +213,16 @@ def main():
     ffn_tflops = useful / (t_ovl[0] * 1e-3) / 1e12
     # the dominant launch: for bf16 the whole FFN (6 M_real d f flops), for fp32 the first GEMM (4 M_real d f)
     roof_flops = useful if s.dtype == "bf16" else 4.0 * M_real * s.d * s.f
-    copy_bytes = 2.0 * M_real * s.d * (2 if s.dtype == "bf16" else 4)
+    # the return moves the other owners' rows (the producer stores the self owner's rows into its buffer itself)
+    M_ret = M_real - int(sc["N_r"][P.shape.self_rank])
+    copy_bytes = 2.0 * M_ret * s.d * (2 if s.dtype == "bf16" else 4)
     peak = MFMA_BF16_PEAK_TFLOPS if s.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     value = useful / (ms_step * 1e-3) / 1e12
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": s.dtype, "data": "synthetic",
-        "config": {"workload": workload_name(s), "M_real": M_real, "M_pad": M_pad, "gemm_row_tiles": sc["n_mtiles"], "consumer_cus": cus,
+        "config": {"workload": workload_name(s), "M_real": M_real, "M_returned": M_ret, "M_pad": M_pad, "gemm_row_tiles": sc["n_mtiles"], "consumer_cus": cus,
                    "consumer_cus_chosen_by": "option" if args.consumer_cus else "library pick",
                    "band_window": args.band_window or 4, "mode": "overlapped" if args.mode == 0 else "sequential"},
         "pct_bf16_peak_step": round(100 * value / peak, 2),

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(HERE, "libmoe_overlap.so")
 MOE_OK, MOE_EINVAL, MOE_ECAPACITY, MOE_EHIP, MOE_ETIMEOUT = 0, -1, -2, -3, -4
 MOE_BF16, MOE_F32 = 0, 1
 MOE_SEG_FIELDS = 8
-MT_FIELDS = 260
+MT_HDR = 8
+MT_FIELDS = MT_HDR + 256
 EXPORTS = ["moe_last_error", "moe_version", "moe_route", "moe_layout_capacity_rows", "moe_layout_workspace_bytes",
            "moe_layout_bind", "moe_layout_build", "moe_read_status", "moe_ffn_flags_count", "moe_pick_consumer_cus",
            "moe_expert_ffn_overlap",

@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "../../include/moe_overlap.h"
+#include "common.h"
 #include "launch.h"
 
 namespace {
@@ -96,7 +97,7 @@ Offsets layout_offsets(const moe_shape* s) {
   o.combine_plan = c.take(T * s->top_k, 4);
   o.scalars = c.take(4 + s->R, 4);
   o.status = c.take(1, 4);
-  o.mtile_desc = c.take(o.cap_mtiles * (4 + 256), 4);
+  o.mtile_desc = c.take(o.cap_mtiles * MOE_MT_FIELDS, 4);
   o.seg_mtiles = c.take(o.cap_tiles * 2, 4);
   o.seg_sched = c.take(o.cap_tiles, 4);
   o.chunk_counts = c.take((int64_t)s->R * n_chunks * s->num_local_experts, 4);
@@ -316,6 +317,7 @@ int moe_expert_ffn_overlap(const moe_shape* s, const moe_layout* L, const void* 
   FfnLaunch p;
   p.dtype = s->dtype;
   p.R = s->R;
+  p.self_rank = s->self_rank;
   p.E = s->num_local_experts;
   p.d = s->d;
   p.f = s->f;

@@ -9,10 +9,16 @@
 #define MOE_WAVE 64
 
 // GEMM row tile: up to MOE_MT_ROWS real rows of one expert (the kernel's tile height: 256 bf16, 64 fp32).
-// Descriptor fields: expert, row count, first row tile and row-tile count of the expert's run (its row tiles are
-// consecutive), then the rows' positions in the padded layout (-1 past the row count).
+// Descriptor: MOE_MT_HDR header fields (expert, row count, first row tile and row-tile count of the expert's run,
+// whose row tiles are consecutive, and the expert's self-owned group), then the rows' positions in the padded
+// layout (-1 past the row count).
 #define MOE_MT_ROWS 256
-#define MOE_MT_HDR 4
+#define MOE_MT_HDR 8
+// header fields of a row tile: expert, real rows, first row tile and row-tile count of the expert's run, then the
+// self-owned group of the expert: first padded row, rows, and receive row minus padded row
+#define MT_SELF_LO 4
+#define MT_SELF_N 5
+#define MT_SELF_DELTA 6
 #define MOE_MT_FIELDS (MOE_MT_HDR + MOE_MT_ROWS)
 
 // scalars[] indices
@@ -90,3 +96,22 @@ __device__ __forceinline__ float wave_sum_f(float v) {
 struct RecvPtrs {
   void* p[MOE_MAX_OWNERS];
 };
+
+// Store destinations of an output tile whose first column is col_bytes into the row: padded rows [lo, lo + n) (the
+// self-owned group of the tile's expert) go to alt + (p + delta) rows, every other row p to the padded layout.  The
+// self owner's rows need no transfer, so the producer stores them straight into the self owner's receive buffer
+// and the consumer returns only the other owners' groups.
+struct RowDst {
+  unsigned char* alt;
+  int lo, n, delta;
+};
+
+// from the row-tile header (in LDS)
+__device__ __forceinline__ RowDst self_dst(unsigned char* self_recv, const int* s_hdr, int64_t col_bytes) {
+  RowDst d;
+  d.lo = s_hdr[MT_SELF_LO];
+  d.n = s_hdr[MT_SELF_N];
+  d.delta = s_hdr[MT_SELF_DELTA];
+  d.alt = self_recv + col_bytes;
+  return d;
+}

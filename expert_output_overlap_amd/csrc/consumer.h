@@ -5,7 +5,8 @@
 // so a transfer is a device-memory copy by the consumer's CUs.
 //
 // The copy work is cut into units of at most CONSUMER_UNIT bytes: a segment of n bytes is ceil(n / unit) units
-// of whole 16-byte chunks.  Units are numbered in the order in which their segments' GEMM row tiles complete,
+// of whole 16-byte chunks.  Segments of the self owner have none: their rows need no transfer, and the producer
+// stores them into the self owner's buffer itself.  Units are numbered in the order in which their segments' GEMM row tiles complete,
 // and every workgroup in the role takes the next unit from a counter, one at a time: the consumer partition
 // during the FFN, and every producer workgroup as soon as its own items are done, so the copies still pending
 // when the last tile is published are spread over the whole chip.  For a unit whose segment it has not seen
@@ -36,6 +37,7 @@ struct ConsumerArgs {
   uint64_t* claim;  // unit counter: stamp << 32 | units handed out
   uint32_t epoch;
   uint32_t stamp;
+  int self_rank;  // segments of this owner are stored by the producer itself: no copy units
   int n_nt;
   int row_vec;
   uint64_t budget;
@@ -97,7 +99,8 @@ __device__ void consumer_role(const ConsumerArgs& a) {
       if (tid < span) {
         const int s = a.seg_sched[base + tid];
         s_seg[tid] = s;
-        const int64_t n = (int64_t)a.seg_desc[(int64_t)s * MOE_SEG_FIELDS + SEG_ROWS] * a.row_vec;
+        const int32_t* sd = a.seg_desc + (int64_t)s * MOE_SEG_FIELDS;
+        const int64_t n = sd[SEG_OWNER] == a.self_rank ? 0 : (int64_t)sd[SEG_ROWS] * a.row_vec;
         u = (uint32_t)((n + CONSUMER_UNIT_CHUNKS - 1) / CONSUMER_UNIT_CHUNKS);
       }
       int v = wave_incl_scan((int)u);

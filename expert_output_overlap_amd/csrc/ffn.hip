@@ -74,6 +74,7 @@ struct GemmArgs {
   uint64_t* ts;
   int n_cons;  // GEMM2 only: workgroups [0, n_cons) run the consumer role
   ConsumerArgs cons;
+  void* self_recv;  // GEMM2 only: its rows of the self-owned groups go straight to the self owner's buffer
 };
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
@@ -225,8 +226,10 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm(GemmArgs a) {
       __syncthreads();
     }
 
-    // epilogue: store the tile's real rows
+    // epilogue: store the tile's real rows (the second GEMM's self-owned rows into the self owner's buffer)
     constexpr int NO = GLU ? NI / 2 : NI;
+    const int self_lo = s_hdr[MT_SELF_LO], self_n = PUBLISH ? s_hdr[MT_SELF_N] : 0, self_delta = s_hdr[MT_SELF_DELTA];
+    T* __restrict__ Cs = (T*)a.self_recv;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
       if (!mvalid[mi]) continue;
@@ -240,7 +243,8 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm(GemmArgs a) {
             const int64_t grow = s_rows[row];
             float v = acc[mi][ni][q];
             if (GLU) v = silu_f32(v) * acc[mi][ni + NI / 2][q];
-            C[grow * a.ldc + col] = Tr::out(v);
+            if (PUBLISH && (uint32_t)(grow - self_lo) < (uint32_t)self_n) Cs[(grow + self_delta) * a.ldc + col] = Tr::out(v);
+            else C[grow * a.ldc + col] = Tr::out(v);
           }
         }
       }
@@ -336,6 +340,7 @@ struct FusedArgs {
   uint64_t* ts;
   int n_cons;
   ConsumerArgs cons;
+  unsigned char* self_recv;  // the self owner's buffer: y rows of the self-owned groups go straight there
 };
 
 struct FfnItem {
@@ -482,13 +487,14 @@ __device__ __forceinline__ f32x16_t load_block16(const f32x4_t* src) {
 }
 
 // Stores the real rows of a 256 x OUT_BN bf16 tile staged in LDS (16-byte chunk ch of row r at chunk ch ^ (r & 7)):
-// row r goes to base + s_rows[r] * ldc elements, 8 chunks per thread at a time (their LDS reads first, then their
-// stores, so neither latency is paid per chunk).
+// row r, at padded row p = s_rows[r], goes to base + p * ldc elements, or to dst.alt + (p + dst.delta) * ldc if p
+// is in the self-owned range of dst; 4 chunks per thread at a time (their LDS reads first, then their stores, so
+// neither latency is paid per chunk; 8 at a time held more registers and ran 1-2% slower).
 template <int OUT_BN>
 __device__ __forceinline__ void store_rows(const unsigned char* smem, unsigned char* base, int64_t ldc,
-                                           const int* s_rows, int n_rows, int tid) {
+                                           const int* s_rows, int n_rows, int tid, const RowDst& dst) {
   constexpr int BM = 256, OUT_ROW = OUT_BN * 2, CPR = OUT_ROW / 16;
-  constexpr int ITER = BM * CPR / 256, UN = ITER < 8 ? ITER : 8;
+  constexpr int ITER = BM * CPR / 256, UN = ITER < 4 ? ITER : 4;
   static_assert(ITER % UN == 0, "store loop unroll");
 #pragma unroll 1
   for (int i0 = 0; i0 < ITER; i0 += UN) {
@@ -501,7 +507,12 @@ __device__ __forceinline__ void store_rows(const unsigned char* smem, unsigned c
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
       const int idx = tid + (i0 + u) * 256, row = idx / CPR, ch = idx - row * CPR;
-      if (row < n_rows) store16_coherent(base + (int64_t)s_rows[row] * ldc * 2 + ch * 16, v[u]);
+      if (row < n_rows) {
+        const int p = s_rows[row];
+        const bool self = (unsigned)(p - dst.lo) < (unsigned)dst.n;
+        unsigned char* b = self ? dst.alt : base;
+        store16_coherent(b + (int64_t)(self ? p + dst.delta : p) * ldc * 2 + ch * 16, v[u]);
+      }
     }
   }
 }
@@ -514,8 +525,8 @@ __device__ __forceinline__ void store_rows(const unsigned char* smem, unsigned c
 // blocks ahead of the one being summed, so about D round trips of the reads are in flight instead of one; other
 // split counts sum one block and split at a time.
 template <int BN>
-__device__ __forceinline__ void reduce_tile(const FusedArgs& a, unsigned char* smem, const int* s_rows, int n_rows,
-                                            int mt, int nt) {
+__device__ __forceinline__ void reduce_tile(const FusedArgs& a, unsigned char* smem, const int* s_rows,
+                                            const int* s_hdr, int n_rows, int mt, int nt) {
   constexpr int BM = 256, WM = 128, WN = BN / 2, MI = WM / 32, NI = WN / 32, NB = MI * NI;
   constexpr int OUT_ROW = BN * 2, SLOT4 = BM * BN / 4;
   int tid = threadIdx.x;
@@ -565,7 +576,7 @@ __device__ __forceinline__ void reduce_tile(const FusedArgs& a, unsigned char* s
     }
   }
   __syncthreads();
-  store_rows<BN>(smem, a.y + (int64_t)nt * BN * 2, a.d, s_rows, n_rows, tid);
+  store_rows<BN>(smem, a.y + (int64_t)nt * BN * 2, a.d, s_rows, n_rows, tid, self_dst(a.self_recv, s_hdr, (int64_t)nt * BN * 2));
   publish(&a.flags2[tile], a.epoch);
   if (a.ts != nullptr && tid == 0) atomicMax((unsigned long long*)&a.ts[1], (unsigned long long)moe_clock());
 }
@@ -580,7 +591,8 @@ __device__ __forceinline__ void reduce_tile(const FusedArgs& a, unsigned char* s
 // its last, so that the stores drain while the next item's row list loads.  False if a wait gave up (the
 // workgroup must exit).
 template <int BN, bool GLU, bool HALF_TILE = false>
-__device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem, const int* s_rows, int e, int n_rows,
+__device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem, const int* s_rows, const int* s_hdr,
+                                         int e, int n_rows,
                                          int mt, int nt, int s, int col0, int target, int half, int* s_stop,
                                          uint32_t** s_pend, int* s_pend_y) {
   constexpr int BM = 256, BK = 64;
@@ -779,7 +791,7 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
     __syncthreads();
     if (*s_stop != target - 1) return true;  // the tile is not complete yet
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    reduce_tile<BNF>(a, smem, s_rows, n_rows, mt, nt);
+    reduce_tile<BNF>(a, smem, s_rows, s_hdr, n_rows, mt, nt);
     return true;
   }
   __syncthreads();  // every wave is done with the operand stages
@@ -788,7 +800,8 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
 #pragma unroll
     for (int ni = 0; ni < NO; ++ni) stage(mi, ni, acc[mi][ni], acc[mi][GLU ? ni + NI / 2 : ni]);
   __syncthreads();
-  store_rows<OUT_BN>(smem, Cb + (GLU ? (int64_t)nt * OUT_BN : (int64_t)col0) * 2, ldc, s_rows, n_rows, tid_e);
+  const RowDst dst = GLU ? RowDst{nullptr, 0, 0, 0} : self_dst(a.self_recv, s_hdr, (int64_t)col0 * 2);
+  store_rows<OUT_BN>(smem, Cb + (GLU ? (int64_t)nt * OUT_BN : (int64_t)col0) * 2, ldc, s_rows, n_rows, tid_e, dst);
   if (GLU || target == 1) {
     if (tid == 0) {
       *s_pend = GLU ? &a.flags1[(int64_t)mt * a.n_nt1 + nt] : &a.flags2[(int64_t)mt * a.n_nt2 + nt];
@@ -897,7 +910,7 @@ __global__ __launch_bounds__(256, 1) void k_ffn_bf16(FusedArgs a) {
     flush();
     const int e = __builtin_amdgcn_readfirstlane(s_hdr[0]), n_rows = __builtin_amdgcn_readfirstlane(s_hdr[1]);
     if (it.kind == 1)
-      return ffn_tile<BN1, true>(a, smem, s_rows, e, n_rows, it.mt, it.nt, 0, 0, 1, -1, &s_stop, &s_pend, &s_pend_y);
+      return ffn_tile<BN1, true>(a, smem, s_rows, s_hdr, e, n_rows, it.mt, it.nt, 0, 0, 1, -1, &s_stop, &s_pend, &s_pend_y);
     // the h columns this split reads: column tiles [s, s+1) * n_nt1 / S of the first GEMM
     const int per = a.n_nt1 / a.S;
     if (!wait_flags(a.flags1 + (int64_t)it.mt * a.n_nt1 + it.s * per, per, a.epoch, a.budget, a.status, &s_stop))
@@ -907,10 +920,10 @@ __global__ __launch_bounds__(256, 1) void k_ffn_bf16(FusedArgs a) {
     int target = a.S;
     for (int sp = 0; sp < a.S; ++sp) target += last - (a.S - 1 - sp) * it.stride >= i_tail;
     if (half < 0)
-      return ffn_tile<BN2, false>(a, smem, s_rows, e, n_rows, it.mt, it.nt, it.s, it.nt * BN2, target, -1, &s_stop,
+      return ffn_tile<BN2, false>(a, smem, s_rows, s_hdr, e, n_rows, it.mt, it.nt, it.s, it.nt * BN2, target, -1, &s_stop,
                                   &s_pend, &s_pend_y);
     if constexpr (BN2 >= 128)
-      return ffn_tile<BN2 / 2, false, true>(a, smem, s_rows, e, n_rows, it.mt, it.nt, it.s,
+      return ffn_tile<BN2 / 2, false, true>(a, smem, s_rows, s_hdr, e, n_rows, it.mt, it.nt, it.s,
                                             it.nt * BN2 + half * (BN2 / 2), target, half, &s_stop, &s_pend, &s_pend_y);
     return false;
   };
@@ -1021,7 +1034,9 @@ void fill_consumer(ConsumerArgs& c, const FfnLaunch& p, int n_nt2) {
   c.row_vec = p.d * (p.dtype == MOE_BF16 ? 2 : 4) / 16;
   c.budget = p.watchdog_ticks;
   c.ts = p.timestamps;
+  c.self_rank = p.self_rank;
 }
+
 
 GemmArgs base_args(const FfnLaunch& p) {
   GemmArgs a;
@@ -1034,6 +1049,7 @@ GemmArgs base_args(const FfnLaunch& p) {
   a.epoch = p.epoch;
   a.flags = nullptr;
   a.n_cons = 0;
+  a.self_recv = p.recv[p.self_rank];
   return a;
 }
 
@@ -1075,6 +1091,7 @@ int launch_bf16(const FfnLaunch& p, int grid, int n_cons, hipStream_t st, hipEve
   a.ts = p.timestamps;
   a.n_cons = n_cons;
   fill_consumer(a.cons, p, a.n_nt2);
+  a.self_recv = (unsigned char*)p.recv[p.self_rank];
   const dim3 g(grid), b(256);
   if (bn1 == 256 && bn2 == 256) hipExtLaunchKernelGGL((k_ffn_bf16<256, 256>), g, b, 0, st, ev0, ev1, 0, a);
   else if (bn1 == 256 && bn2 == 128) hipExtLaunchKernelGGL((k_ffn_bf16<256, 128>), g, b, 0, st, ev0, ev1, 0, a);

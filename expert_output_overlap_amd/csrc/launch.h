@@ -19,6 +19,7 @@ struct LayoutLaunch {
 struct FfnLaunch {
   int dtype;  // moe_dtype
   int R, E, d, f;
+  int self_rank;  // owner whose rows the producer stores into its receive buffer itself
   const moe_layout* L;
   const void* x_pad;
   const void* w_gate_up;

@@ -406,6 +406,11 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
           d[1] = left < a.mt_rows ? left : a.mt_rows;
           d[2] = base;
           d[3] = (rrows + a.mt_rows - 1) >> mt_shift;
+          const int gs = (g / R) * R + a.self_rank;
+          d[MT_SELF_LO] = s_poff[gs];
+          d[MT_SELF_N] = s_n[gs];
+          d[MT_SELF_DELTA] = s_roff[gs] - s_poff[gs];
+          d[7] = 0;
         }
       }
       const int used = rrows & mt_mask;

@@ -77,8 +77,10 @@ typedef struct {
                             expert is not local */
   int32_t* scalars;      /* [4+R] M_pad, n_tiles, n_segs, N_r[0..R), n_mtiles */
   int32_t* status;       /* [1] device status word (moe_status) */
-  int32_t* mtile_desc;   /* [cap_mtiles][260] GEMM row tiles: {expert, n_rows, run_first, run_count,
-                            row[256]}, up to 256 (fp32: 64) real rows of one expert given by their
+  int32_t* mtile_desc;   /* [cap_mtiles][264] GEMM row tiles: {expert, n_rows, run_first, run_count,
+                            self_lo, self_n, self_delta, 0, row[256]} (self_*: the expert's self-owned
+                            group, first padded row, rows, receive row minus padded row), up to
+                            256 (fp32: 64) real rows of one expert given by their
                             padded-layout positions, -1 past n_rows; each expert's groups are packed
                             together (self-owned group last) into the consecutive row tiles
                             [run_first, run_first + run_count) (internal schedule) */

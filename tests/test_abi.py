@@ -102,7 +102,7 @@ def test_bind_carves_disjoint_aligned_arrays():
     sizes = {"counts": NG, "padded_off": NG, "recv_off": NG, "tile_owner": L.cap_tiles, "tile_expert": L.cap_tiles,
              "tile_valid": L.cap_tiles, "tile_order": L.cap_tiles, "seg_desc": 8 * L.cap_tiles,
              "row_src": L.cap_rows, "combine_plan": T * s.top_k, "scalars": 4 + s.R, "status": 1,
-             "mtile_desc": 260 * L.cap_mtiles, "seg_mtiles": 2 * L.cap_tiles, "seg_sched": L.cap_tiles,
+             "mtile_desc": 264 * L.cap_mtiles, "seg_mtiles": 2 * L.cap_tiles, "seg_sched": L.cap_tiles,
              "chunk_counts": s.R * ((s.tokens_per_owner + 63) // 64) * s.num_local_experts}
     spans = sorted((getattr(L, n) - base, getattr(L, n) - base + 4 * sizes[n], n) for n in sizes)
     for (a0, a1, n), (b0, b1, m) in zip(spans, spans[1:]):

@@ -15,6 +15,8 @@ import tolerance
 from expert_output_overlap_amd import binding as B
 from expert_output_overlap_amd.runtime import MoePath, to_device
 
+SELF = 0  # the GPU's own rank among the owners (self_rank) in every workload here
+
 pytestmark = pytest.mark.gpu
 
 LAYOUT_INT = ["counts", "padded_off", "recv_off"]
@@ -52,6 +54,20 @@ class Run:
     def ffn(self, **kw):
         return self.P.ffn(self.dev["w_gate_up"], self.dev["w_down"], **kw)
 
+    def y_at(self, rows) -> torch.Tensor:
+        """The GPU's y at padded rows ``rows`` (real rows): from y_pad, except the self-owned groups' rows, which the
+        producer stores straight into the self owner's receive buffer."""
+        lay, s = self.lay, self.s
+        rows = np.asarray(rows, dtype=np.int64)
+        g = lay["tile_expert"][rows // s.M] * s.R + lay["tile_owner"][rows // s.M]
+        own = lay["tile_owner"][rows // s.M] == SELF
+        dev = self.P.y_pad.device
+        out = self.P.y_pad[torch.as_tensor(rows, device=dev)].clone()
+        if own.any():
+            dst = lay["recv_off"][g[own]] + rows[own] - lay["padded_off"][g[own]]
+            out[torch.as_tensor(np.nonzero(own)[0], device=dev)] = self.P.recv[SELF][torch.as_tensor(dst, device=dev)]
+        return out
+
     def check_rows(self, rows, what="y"):
         """Check the GPU's y at padded rows ``rows`` (real rows) against the oracle, up to the oracle's own
         alternative roundings of h; returns the oracle reference rows that matched."""
@@ -59,7 +75,7 @@ class Run:
         bf = s.dtype == "bf16"
         ex = oracle.ffn_rows_ex(lay["row_src"][rows], lay["tile_expert"][rows // s.M], self.inp["x"],
                                 self.inp["w_gate_up"], self.inp["w_down"], bf)
-        got = f64(self.P.y_pad[torch.as_tensor(np.asarray(rows), dtype=torch.long, device=self.P.y_pad.device)])
+        got = f64(self.y_at(rows))
         ref, flips = tolerance.check_ffn(got, ex, what, bf)
         print("%s: %d rows, %d alternative h roundings taken" % (what, len(rows), flips), flush=True)
         return ref
@@ -101,6 +117,11 @@ def check_schedule(run):
     runs = {}
     for mt, dsc in enumerate(desc):
         e, nrow, r0, rc = dsc[0], dsc[1], dsc[2], dsc[3]
+        gs = e * s.R + SELF
+        assert dsc[4:8].tolist() == [lay["padded_off"][gs], lay["counts"][gs],
+                                     lay["recv_off"][gs] - lay["padded_off"][gs], 0]
+        H = B.MT_HDR
+        dsc = np.concatenate([dsc[:4], dsc[H:]])
         assert 1 <= nrow <= TR and (dsc[4 + nrow:4 + TR] == -1).all()
         assert r0 <= mt < r0 + rc <= n_mt and runs.setdefault(e, (r0, rc)) == (r0, rc)
         assert nrow == TR or mt == r0 + rc - 1
@@ -119,13 +140,16 @@ def check_schedule(run):
 
 
 def check_delivery(run):
-    """recv[r] rows are the GPU's own y rows of group (e, r), bit for bit; rows past N_r untouched (NaN canary)."""
+    """recv[r] rows of another owner are the GPU's own y rows of group (e, r), bit for bit; the self owner's rows,
+    which the producer stores there itself, are all written; rows past N_r untouched (NaN canary)."""
     P, lay, s = run.P, run.lay, run.s
     yb = bits(P.y_pad)
     for r in range(s.R):
         rb = bits(P.recv[r])
         n_r = int(lay["N_r"][r])
-        for e in range(s.E_l):
+        if r == SELF:
+            assert not np.isnan(f64(P.recv[r][:n_r])).any(), "a self-owned row was not written"
+        for e in range(s.E_l if r != SELF else 0):
             g = e * s.R + r
             n, po, ro = lay["counts"][g], lay["padded_off"][g], lay["recv_off"][g]
             np.testing.assert_array_equal(rb[ro:ro + n], yb[po:po + n], err_msg="owner %d expert %d" % (r, e))
@@ -280,6 +304,7 @@ def test_no_stale_reads_across_calls(name):
     neg = -run.dev["x"]  # same routing, different h, partial sums and y everywhere
     run.P.h.fill_(float("nan"))
     run.P.y_pad.fill_(float("nan"))
+    run.P.recv[SELF].fill_(float("nan"))
     run.P.layout(neg)
     run.ffn(mode=0)
     fresh = MoePath.from_spec(s)
@@ -288,7 +313,8 @@ def test_no_stale_reads_across_calls(name):
     fresh.ffn(run.dev["w_gate_up"], run.dev["w_down"], mode=1)
     torch.cuda.synchronize()
     assert run.P.status() == B.MOE_OK and fresh.status() == B.MOE_OK
-    real = np.nonzero(run.lay["row_src"] >= 0)[0]
+    lay = run.lay
+    real = np.nonzero((lay["row_src"] >= 0) & (lay["tile_owner"][np.arange(lay["M_pad"]) // s.M] != SELF))[0]
     np.testing.assert_array_equal(bits(run.P.y_pad)[real], bits(fresh.y_pad)[real])
     for r in range(s.R):
         n_r = int(run.lay["N_r"][r])
@@ -309,8 +335,9 @@ def test_return_only_repeats(name):
     check_delivery(run)
     ref = [bits(b) for b in run.P.recv]
     for cus in (3, 16, 1):
-        for r in range(s.R):
-            run.P.recv[r].fill_(float("nan"))
+        for r in range(s.R):  # the return delivers the other owners' rows (the producer stored the self owner's)
+            if r != SELF:
+                run.P.recv[r].fill_(float("nan"))
         run.P.ffn(run.dev["w_gate_up"], run.dev["w_down"], mode=2, consumer_cus=cus, epoch=epoch)
         torch.cuda.synchronize()
         assert run.P.status() == B.MOE_OK
