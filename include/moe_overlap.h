@@ -103,7 +103,7 @@ typedef struct {
                               1 = sequential (producer on all CUs, then the return on all CUs),
                               2 = return only (the consumer alone, on consumer_cus workgroups, for flags
                                   already published with this epoch; a flag never published ends in the
-                                  watchdog) */
+                                  watchdog; it delivers the other owners' rows, not the self owner's) */
   uint32_t epoch;          /* flag value of this call: nonzero and different from what the flag array holds
                               (flags start zeroed; pass 1, 2, 3, ...) */
   int32_t band_window;     /* GEMM row tiles per window of the producer's item list (0 = library default, 4):
@@ -114,8 +114,8 @@ typedef struct {
                               workgroup exits */
   uint64_t* timestamps;    /* optional (device) [2 + 2*cap_tiles] u64, 100 MHz clock: [0] first producer
                               item start, [1] last flag publish, [2+2s] / [3+2s] first copy start / last copy
-                              end of segment s over the workgroups that copy it; reset by the call; NULL to
-                              skip */
+                              end of segment s over the workgroups that copy it (a self-owned segment,
+                              never copied, keeps ~0 / 0); reset by the call; NULL to skip */
 } moe_overlap_cfg;
 
 /* Last host-side error message of the calling thread ("" if none). */
@@ -184,13 +184,16 @@ int32_t moe_pick_consumer_cus(const moe_shape* s, int32_t n_cu);
  * epoch-valued flag once its stores are complete and visible device-wide.  The return is cut into copy units
  * of up to 128 KB of a segment, handed out in the order the segments complete: a workgroup in the consumer
  * role takes the next unit, waits for the flags of its segment's row tiles, acquires, and copies the unit's
- * rows into recv[owner].
+ * rows into recv[owner].  The self owner's rows need no transfer (review page: the producer schedules the
+ * remote-bound tiles first and the consumer moves those): the second GEMM stores them straight into
+ * recv[self_rank], and its segments have no copy units.
  *   mode 0 (overlapped): the consumer is the first consumer_cus workgroups of the producer launch, and every
  *     producer workgroup joins it once its own items are done;
  *   mode 1 (sequential): producer on every CU, then the return alone on every CU;
  *   mode 2: the consumer alone (return only; for tests of the wait).
  * fp32 runs the two GEMMs as two launches (consumer inside the second).  Owner r receives, at row
  * recv_off_{e,r} + i, the FFN output of the i-th row of group (e, r); results are identical in every mode.
+ * y_pad holds the other owners' rows only (scratch of the return).
  * x_pad (device) [cap_rows, d]; w_gate_up (device) [E_l, 2f, d]; w_down (device) [E_l, d, f];
  * h_ws (device) [cap_rows, f] workspace; y_pad (device) [cap_rows, d]; recv: host array of R device
  * pointers, recv[r] holds >= N_r rows of d; flags (device, 8-byte aligned) [moe_ffn_flags_count] 4-byte
