@@ -15,7 +15,7 @@ import tolerance
 from expert_output_overlap_amd import binding as B
 from expert_output_overlap_amd.runtime import MoePath, to_device
 
-SELF = 0  # the GPU's own rank among the owners (self_rank) in every workload here
+SELF = 0  # the GPU's own rank among the owners (self_rank) unless a test says otherwise
 
 pytestmark = pytest.mark.gpu
 
@@ -37,19 +37,20 @@ def bits(t: torch.Tensor) -> np.ndarray:
 class Run:
     """Inputs of one workload on host and device, the GPU path's buffers, and the oracle's routing and layout."""
 
-    def __init__(self, s, logits=None):
+    def __init__(self, s, logits=None, self_rank=SELF):
         _require_gpu()
-        print("case", s, flush=True)
+        print("case", s, "self_rank", self_rank, flush=True)
         self.s = s
+        self.sr = self_rank
         self.inp = mi.inputs(s)
         if logits is not None:
             self.inp["logits"] = logits
-        self.P = MoePath.from_spec(s)
+        self.P = MoePath(s.R, s.T_o, s.G, s.E_l, s.k, s.d, s.f, s.M, s.mgb, s.dtype, self_rank)
         self.dev = {k: to_device(v, s.dtype) for k, v in self.inp.items()}
         self.P.route(self.dev["logits"])
         self.P.layout(self.dev["x"])
         self.idx, self.w = oracle.route(self.inp["logits"], s.k)
-        self.lay = oracle.layout(self.idx, s.R, s.T_o, s.G, s.E_l, s.k, s.M, s.mgb, 0)
+        self.lay = oracle.layout(self.idx, s.R, s.T_o, s.G, s.E_l, s.k, s.M, s.mgb, self_rank)
 
     def ffn(self, **kw):
         return self.P.ffn(self.dev["w_gate_up"], self.dev["w_down"], **kw)
@@ -60,12 +61,12 @@ class Run:
         lay, s = self.lay, self.s
         rows = np.asarray(rows, dtype=np.int64)
         g = lay["tile_expert"][rows // s.M] * s.R + lay["tile_owner"][rows // s.M]
-        own = lay["tile_owner"][rows // s.M] == SELF
+        own = lay["tile_owner"][rows // s.M] == self.sr
         dev = self.P.y_pad.device
         out = self.P.y_pad[torch.as_tensor(rows, device=dev)].clone()
         if own.any():
             dst = lay["recv_off"][g[own]] + rows[own] - lay["padded_off"][g[own]]
-            out[torch.as_tensor(np.nonzero(own)[0], device=dev)] = self.P.recv[SELF][torch.as_tensor(dst, device=dev)]
+            out[torch.as_tensor(np.nonzero(own)[0], device=dev)] = self.P.recv[self.sr][torch.as_tensor(dst, device=dev)]
         return out
 
     def check_rows(self, rows, what="y"):
@@ -117,7 +118,7 @@ def check_schedule(run):
     runs = {}
     for mt, dsc in enumerate(desc):
         e, nrow, r0, rc = dsc[0], dsc[1], dsc[2], dsc[3]
-        gs = e * s.R + SELF
+        gs = e * s.R + run.sr
         assert dsc[4:8].tolist() == [lay["padded_off"][gs], lay["counts"][gs],
                                      lay["recv_off"][gs] - lay["padded_off"][gs], 0]
         H = B.MT_HDR
@@ -147,9 +148,9 @@ def check_delivery(run):
     for r in range(s.R):
         rb = bits(P.recv[r])
         n_r = int(lay["N_r"][r])
-        if r == SELF:
+        if r == run.sr:
             assert not np.isnan(f64(P.recv[r][:n_r])).any(), "a self-owned row was not written"
-        for e in range(s.E_l if r != SELF else 0):
+        for e in range(s.E_l if r != run.sr else 0):
             g = e * s.R + r
             n, po, ro = lay["counts"][g], lay["padded_off"][g], lay["recv_off"][g]
             np.testing.assert_array_equal(rb[ro:ro + n], yb[po:po + n], err_msg="owner %d expert %d" % (r, e))
@@ -184,9 +185,11 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("s", SMALL, ids=lambda s: s.name + ("_mgb%d" % s.mgb))
-def test_small_full_parity(s):
-    run = Run(s)
+@pytest.mark.parametrize("s,self_rank", [(s, SELF) for s in SMALL] + [(SMALL[3], 2), (SMALL[4], 1), (SMALL[1], 1)],
+                         ids=lambda v: v.name + ("_mgb%d" % v.mgb) if isinstance(v, mi.Spec) else "rank%d" % v)
+def test_small_full_parity(s, self_rank):
+    """Whole path against the oracle; ranks other than 0 own other experts, and the producer stores their rows."""
+    run = Run(s, self_rank=self_rank)
     check_route_and_layout(run)
     P, lay = run.P, run.lay
     for r in range(s.R):
@@ -314,8 +317,12 @@ def test_no_stale_reads_across_calls(name):
     torch.cuda.synchronize()
     assert run.P.status() == B.MOE_OK and fresh.status() == B.MOE_OK
     lay = run.lay
-    real = np.nonzero((lay["row_src"] >= 0) & (lay["tile_owner"][np.arange(lay["M_pad"]) // s.M] != SELF))[0]
+    own = lay["tile_owner"][np.arange(lay["M_pad"]) // s.M] == SELF
+    real = np.nonzero((lay["row_src"] >= 0) & ~own)[0]
     np.testing.assert_array_equal(bits(run.P.y_pad)[real], bits(fresh.y_pad)[real])
+    # the self owner's rows went straight to its buffer: y_pad keeps the poison there
+    mine = np.nonzero((lay["row_src"] >= 0) & own)[0]
+    assert np.isnan(f64(run.P.y_pad[torch.as_tensor(mine, device=run.P.y_pad.device)])).all()
     for r in range(s.R):
         n_r = int(run.lay["N_r"][r])
         np.testing.assert_array_equal(bits(run.P.recv[r])[:n_r], bits(fresh.recv[r])[:n_r])
