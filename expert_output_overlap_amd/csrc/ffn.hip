@@ -356,8 +356,10 @@ struct FfnItem {
 //    expert itself, from the row tiles' run fields, and uses this function for the rest), then the GEMM2
 //    windows.  A GEMM2 split reads only its own share of h's columns, which the first part of the GEMM1 list
 //    produced; row tiles complete window after window during the last part of the launch.  With at most four
-//    windows that leaves most of the return to the launch's last round, so there a window's GEMM2 items go row
-//    tile by row tile instead (split-major inside a row tile), and its row tiles complete one after another.
+//    windows that leaves most of the return to the launch's last round, so there every window but the first goes
+//    row tile by row tile instead (split-major inside a row tile), and its row tiles complete one after another;
+//    the first keeps the weight sharing (its row tiles publish together, early enough to be returned under the
+//    later windows).
 //    The window(s) whose GEMM2 items end the list (the last one; with interleaving the last two) go row tile by
 //    row tile in every order, so that what is left to return after the last publish is one row tile's rows.
 //  - interleaved: G1(0), G1(1), G2(0), G1(2), G2(1), ..., G1(nw-1), G2(nw-2), G2(nw-1): row tiles complete
@@ -379,7 +381,7 @@ __device__ __forceinline__ FfnItem ffn_item(int i, int n_mt, int W, int n1, int 
   auto g2 = [&](int w, int j, int Wc) {
     FfnItem it;
     it.kind = 2;
-    if (by_tile || w >= nw - (interleave ? 2 : 1)) {
+    if ((by_tile && w >= 1) || w >= nw - (interleave ? 2 : 1)) {
       const int ml = j / n2S, r = j - ml * n2S;
       it.s = r / n2;
       it.nt = r - it.s * n2;
