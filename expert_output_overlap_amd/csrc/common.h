@@ -64,6 +64,21 @@ __device__ __forceinline__ int32_t load_status(const int32_t* status) {
   return __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---- the in-launch publish protocol ----------------------------------------------------------------------
+// Results one workgroup hands to another inside a launch (h tiles, split-K partial sums, y tiles) go out with
+// device-scope stores, which write through to the level shared by the XCDs; the producer waits for their
+// completion (s_waitcnt vmcnt(0), ordered by a release fence at workgroup scope) and then stores the flag with an
+// agent-scope atomic.  A reader polls the flag with agent-scope atomic loads.  What it reads next cannot be stale in
+// its own caches: every line that is read after a flag wait is read only after this launch wrote it (each such
+// result is read only once its flag is set, and no two results share a cache line), so the only stale copies a
+// CU's L1 or an XCD's L2 can hold are from before the launch, and every workgroup drops those with one
+// agent-scope acquire when it starts (launch_acquire).  After a flag wait the reader then needs only compiler
+// ordering (flag_acquire), not the agent-scope acquire that invalidates the XCD's whole L2 on every wait, which
+// made every second-GEMM k-loop on the XCD refetch its operands (measured ~3200 against ~2450 shader cycles per
+// 256 x 256 x 64 k-tile).
+__device__ __forceinline__ void launch_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+__device__ __forceinline__ void flag_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup"); }
+
 // wave-level helpers
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 

@@ -11,8 +11,9 @@
 // during the FFN, and every producer workgroup as soon as its own items are done, so the copies still pending
 // when the last tile is published are spread over the whole chip.  For a unit whose segment it has not seen
 // complete yet, a workgroup polls the flags of the segment's GEMM row tiles with relaxed agent-scope loads, then
-// issues one agent-scope acquire fence (pairing with the producer's publish) before reading the rows; a spin
-// budget on the 100 MHz clock bounds every wait.
+// reads the rows (the publish protocol in common.h: every workgroup of the launch dropped stale cache lines at its
+// start, and rows are read only after this launch wrote them); a spin budget on the 100 MHz clock bounds every
+// wait.
 //
 // The counter is one 64-bit word: the launch's stamp (nonzero, distinct for every launch) in the high half and
 // the units handed out in the low half.  One workgroup writes the stamp with a zero count at the start of the
@@ -50,12 +51,14 @@ __device__ __forceinline__ void consumer_stamp(const ConsumerArgs& a) {
     __hip_atomic_store(a.claim, (uint64_t)a.stamp << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Runs in a workgroup of up to 256 threads (whole waves) until every unit has been handed out.
+#define CONSUMER_MAX_THREADS 512
+
+// Runs in a workgroup of up to CONSUMER_MAX_THREADS threads (whole waves) until every unit has been handed out.
 __device__ void consumer_role(const ConsumerArgs& a) {
   // a window of up to blockDim.x scheduled segments: their ids and, relative to the window, the units before them
-  __shared__ int s_seg[256];
-  __shared__ uint32_t s_pre[257];
-  __shared__ int s_wsum[4];
+  __shared__ int s_seg[CONSUMER_MAX_THREADS];
+  __shared__ uint32_t s_pre[CONSUMER_MAX_THREADS + 1];
+  __shared__ int s_wsum[CONSUMER_MAX_THREADS / 64];
   __shared__ uint32_t s_cur;
   __shared__ int s_hit, s_stop;
   const int tid = threadIdx.x, nthr = blockDim.x;
@@ -137,7 +140,7 @@ __device__ void consumer_role(const ConsumerArgs& a) {
         }
         __builtin_amdgcn_s_sleep(1);
       }
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      flag_acquire();  // the launch_acquire of this launch left no stale copy of these rows (common.h)
       seen = s;
     }
     const int64_t n = (int64_t)sd[SEG_ROWS] * a.row_vec;
@@ -148,7 +151,7 @@ __device__ void consumer_role(const ConsumerArgs& a) {
     v4u32* __restrict__ t4 = (v4u32*)((uint4*)a.recv.p[owner] + (int64_t)dst * a.row_vec);
     const int64_t B = nthr;
     int64_t i = c0 + tid;
-    for (; i + 7 * B < c1; i += 8 * B) {  // 8 loads in flight per thread (32 KB per workgroup of 256)
+    for (; i + 7 * B < c1; i += 8 * B) {  // 8 loads in flight per thread (128 B per thread)
       v4u32 v[8];  // a native vector type: an array of it stays in registers
 #pragma unroll
       for (int k = 0; k < 8; ++k) v[k] = f4[i + k * B];

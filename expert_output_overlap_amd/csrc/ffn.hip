@@ -98,6 +98,7 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm(GemmArgs a) {
   __shared__ int s_rows[BM];
   __shared__ int s_hdr[MOE_MT_HDR];
 
+  if (PUBLISH) launch_acquire();
   if (PUBLISH && a.n_cons > 0 && blockIdx.x == 0) consumer_stamp(a.cons);
   if (PUBLISH && (int)blockIdx.x < a.n_cons) {
     consumer_role(a.cons);
@@ -265,13 +266,17 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm(GemmArgs a) {
 
 // ---- bf16 GEMM: 256-row tiles, direct global->LDS loads ------------------------------------------------
 //
-// Workgroup tile 256 x BN x 64 (k), 4 waves in 2 x 2, wave tile 128 x BN/2 (4 x BN/64 MFMA blocks of 32 x 32,
-// accumulators in AGPRs).  Operand tiles are staged in LDS without padding, 128 bytes per row; a 16-byte
-// k-chunk c of row r sits at slot c ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1), so the 16-byte fragment
-// reads of 16 consecutive rows hit distinct banks.  global_load_lds_dwordx4 moves each 16-byte chunk straight
-// from global memory into its swizzled LDS slot (one wave instruction fills 8 rows, 1 KB).
+// Workgroup tile 256 x BN x 64 (k), 8 waves (two per SIMD) in (8 / (BN / 64)) x (BN / 64), wave tile
+// (64 * BN / 256 ... 128) x 64: MI x 2 MFMA blocks of 32 x 32, accumulators in AGPRs.  Two waves per SIMD, not
+// one: a wave's global->LDS loads go out at a bounded rate (about 30 GB/s per CU from four waves whatever the
+// number in flight, 75 GB/s from eight, measured from L2-resident data), and a 256 x 256 tile at the MFMA rate
+// needs about 45 GB/s per CU at the clock this chip holds under a dense bf16 load.  Operand tiles are staged in
+// LDS without padding, 128 bytes per row; a 16-byte k-chunk c of row r sits at slot c ^ swz(r),
+// swz(r) = (r & 7) ^ ((r >> 3) & 1), so the 16-byte fragment reads of 16 consecutive rows hit distinct banks.
+// global_load_lds_dwordx4 moves each 16-byte chunk straight from global memory into its swizzled LDS slot (one
+// wave instruction fills 8 rows, 1 KB).
 //
-// Pipeline, two LDS stages, one barrier per k-tile.  A k-tile is four k-steps of 16 MFMAs per wave; the
+// Pipeline, two LDS stages, one barrier per k-tile.  A k-tile is four k-steps of MI x 2 MFMAs per wave; the
 // fragments of k-step s+1 are read while the MFMAs of k-step s run.  The barrier sits between k-steps 2 and
 // 3 of k-tile kt: past it, k-tile kt+1 is in LDS for every wave (its first fragments are read during
 // k-step 3) and no wave reads the stage of kt any more, so the loads of k-tile kt+2 go into that stage, half
@@ -284,17 +289,26 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm(GemmArgs a) {
 // and would drain every load in flight before each LDS read, serialising loads and MFMAs.  The stage
 // discipline makes that unnecessary: a stage is written only after the barrier that ends every read of it.
 
+#define FFN_THREADS 512  // 8 waves, two per SIMD
+#define FFN_WAVES (FFN_THREADS / 64)
+
 // global_load_lds_dwordx4 in its scalar-base form: lane i moves 16 bytes from base + off into LDS at
-// m0 + 16 * i (m0 is set in the same statement, so no other code depends on it)
+// m0 + 16 * i.  The statement leaves M0 as it found it: it saves M0 in a scratch SGPR, sets it, issues the load
+// (which reads M0 when it issues) and restores it, so no code outside depends on the compiler honouring an M0
+// clobber (M0 is a reserved register, which an inline-asm clobber list may not name).
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_addr) {
   // base and lds_addr are the same in every lane; readfirstlane puts them in scalar registers.  The load takes its
-  // LDS address from M0, which needs one wait state after an SALU write (the s_nop; the compiler adds it only for
-  // loads it emits itself)
+  // LDS address from M0, which needs one wait state after an SALU write (the first s_nop); the second covers a
+  // read of M0 right after the statement (the compiler inserts such wait states only around its own M0 writes)
   const uint64_t b = (uint64_t)base;
   const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(lds_addr)),
-               "v"(off), "s"((const void*)sb) : "memory", "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0\n\ts_nop 0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(off), "s"((const void*)sb)
+      : "memory");
 }
 
 // this wave's loads have landed in LDS, then the workgroup barrier: after it every wave's have
@@ -418,7 +432,8 @@ __device__ __forceinline__ FfnItem ffn_item(int i, int n_mt, int W, int n1, int 
   return g2(nw - 1, i - W * n2S, Wl);
 }
 
-// All threads of the workgroup: wait until the n flags equal epoch, then acquire.  False if the spin budget ran
+// All threads of the workgroup: wait until the n flags equal epoch, then acquire (compiler ordering; see the
+// publish protocol in common.h).  False if the spin budget ran
 // out (status set to MOE_ETIMEOUT) or another workgroup reported an error.
 __device__ bool wait_flags(const uint32_t* fl, int n, uint32_t epoch, uint64_t budget, int32_t* status, int* s_stop) {
   const uint64_t t0 = moe_clock();
@@ -435,16 +450,18 @@ __device__ bool wait_flags(const uint32_t* fl, int n, uint32_t epoch, uint64_t b
     }
     __builtin_amdgcn_s_sleep(2);
   }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  flag_acquire();  // no stale copies to drop: the publish protocol in common.h
   return true;
 }
 
 // Results that other workgroups read inside this launch (h tiles, split partial sums, y tiles) are written with
 // agent-scope atomic stores: on this chip those are coherent across the XCDs' separate L2 caches (they carry the
 // device-scope cache policy), and a store's completion, which s_waitcnt vmcnt waits for, means it is visible
-// device-wide.  Publishing is then: every thread's stores completed (the barrier's vmcnt(0)), then the flag.
-// An agent-scope release fence would write back the whole L2 of the XCD instead, once per published tile, which
-// stalls every workgroup on that XCD; the reader still acquires at agent scope before it reads.
+// device-wide.  Publishing is then: every thread's stores completed (a release fence at workgroup scope, which is
+// that vmcnt(0), and the barrier), then the flag, an agent-scope atomic store.  An agent-scope release fence would
+// write back the whole L2 of the XCD instead, once per published tile, which stalls every workgroup on that XCD
+// (nothing the tile needs is dirty in L2: its data went out with device-scope stores).  The reader's side is in
+// common.h.
 // 16 bytes with the device-scope cache policy (the one agent-scope atomic stores use), as one dwordx4 store:
 // two 8-byte atomic stores per 16 bytes measured 2-3 times slower.  The compiler does not count this store, so
 // whoever needs it complete waits with an explicit vmcnt(0) (wait_stores).  Nor does it see that the registers of
@@ -458,7 +475,8 @@ __device__ __forceinline__ void store16_coherent(void* p, u32x4_t v) {
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ void publish(uint32_t* flag, uint32_t epoch) {
-  wait_stores();    // this wave's stores are complete
+  wait_stores();  // this wave's stores are complete
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();  // and every wave's
   if (threadIdx.x == 0) __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -479,10 +497,12 @@ __device__ __forceinline__ uint32_t arrive(uint64_t* ctr, uint32_t epoch) {
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x8_t __attribute__((ext_vector_type(8)));
 
-// 16 fp32 partial sums of one thread in one 32 x 32 accumulator block (the layout the splits store them in)
+// 16 fp32 partial sums of one thread in one 32 x 32 accumulator block (the layout the splits store them in:
+// float4 chunk q4 of block b of thread t at (b * 4 + q4) * FFN_THREADS + t)
 __device__ __forceinline__ f32x16_t load_block16(const f32x4_t* src) {
-  const f32x4_t q0 = __builtin_nontemporal_load(src), q1 = __builtin_nontemporal_load(src + 256);
-  const f32x4_t q2 = __builtin_nontemporal_load(src + 512), q3 = __builtin_nontemporal_load(src + 768);
+  constexpr int T = FFN_THREADS;
+  const f32x4_t q0 = __builtin_nontemporal_load(src), q1 = __builtin_nontemporal_load(src + T);
+  const f32x4_t q2 = __builtin_nontemporal_load(src + 2 * T), q3 = __builtin_nontemporal_load(src + 3 * T);
   const f32x8_t h0 = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
   const f32x8_t h1 = __builtin_shufflevector(q2, q3, 0, 1, 2, 3, 4, 5, 6, 7);
   return (f32x16_t)__builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
@@ -495,20 +515,20 @@ __device__ __forceinline__ f32x16_t load_block16(const f32x4_t* src) {
 template <int OUT_BN>
 __device__ __forceinline__ void store_rows(const unsigned char* smem, unsigned char* base, int64_t ldc,
                                            const int* s_rows, int n_rows, int tid, const RowDst& dst) {
-  constexpr int BM = 256, OUT_ROW = OUT_BN * 2, CPR = OUT_ROW / 16;
-  constexpr int ITER = BM * CPR / 256, UN = ITER < 4 ? ITER : 4;
-  static_assert(ITER % UN == 0, "store loop unroll");
+  constexpr int BM = 256, OUT_ROW = OUT_BN * 2, CPR = OUT_ROW / 16, NT = FFN_THREADS;
+  constexpr int ITER = BM * CPR / NT, UN = ITER < 4 ? ITER : 4;
+  static_assert(ITER >= 1 && ITER % UN == 0, "store loop unroll");
 #pragma unroll 1
   for (int i0 = 0; i0 < ITER; i0 += UN) {
     u32x4_t v[UN];
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
-      const int idx = tid + (i0 + u) * 256, row = idx / CPR, ch = idx - row * CPR;
+      const int idx = tid + (i0 + u) * NT, row = idx / CPR, ch = idx - row * CPR;
       v[u] = *(const u32x4_t*)(smem + row * OUT_ROW + ((ch ^ (row & 7)) << 4));
     }
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
-      const int idx = tid + (i0 + u) * 256, row = idx / CPR, ch = idx - row * CPR;
+      const int idx = tid + (i0 + u) * NT, row = idx / CPR, ch = idx - row * CPR;
       if (row < n_rows) {
         const int p = s_rows[row];
         const bool self = (unsigned)(p - dst.lo) < (unsigned)dst.n;
@@ -529,15 +549,15 @@ __device__ __forceinline__ void store_rows(const unsigned char* smem, unsigned c
 template <int BN>
 __device__ __forceinline__ void reduce_tile(const FusedArgs& a, unsigned char* smem, const int* s_rows,
                                             const int* s_hdr, int n_rows, int mt, int nt) {
-  constexpr int BM = 256, WM = 128, WN = BN / 2, MI = WM / 32, NI = WN / 32, NB = MI * NI;
+  constexpr int BM = 256, WGN = BN / 64, WGM = FFN_WAVES / WGN, WM = BM / WGM, MI = WM / 32, NI = 2, NB = MI * NI;
   constexpr int OUT_ROW = BN * 2, SLOT4 = BM * BN / 4;
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
-  const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int lane = tid & 63, wave = tid >> 6, wm = wave / WGN, wn = wave % WGN;
   const int64_t tile = (int64_t)mt * a.n_nt2 + nt;
   const f32x4_t* slots = (const f32x4_t*)(a.partial + tile * a.S * (BM * BN));
   auto stage = [&](int b, const f32x16_t& v) {  // block b of this thread's accumulators, as bf16, into LDS
-    const int mi = b / NI, ni = b - mi * NI, col = wn * WN + ni * 32 + (lane & 31);
+    const int mi = b / NI, ni = b - mi * NI, col = wn * 64 + ni * 32 + (lane & 31);
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int row = wm * WM + mi * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
@@ -546,11 +566,12 @@ __device__ __forceinline__ void reduce_tile(const FusedArgs& a, unsigned char* s
     }
   };
   auto ring_sum = [&](auto S_) {
-    constexpr int SC = decltype(S_)::value, D = SC <= 2 ? 3 : 2;
+    constexpr int SC = decltype(S_)::value, D = SC <= 2 ? 2 : 1;
     f32x16_t ring[D + 1][SC];
     auto load = [&](int b) {
 #pragma unroll
-      for (int sp = 0; sp < SC; ++sp) ring[b % (D + 1)][sp] = load_block16(slots + (int64_t)sp * SLOT4 + b * 4 * 256 + tid);
+      for (int sp = 0; sp < SC; ++sp)
+        ring[b % (D + 1)][sp] = load_block16(slots + (int64_t)sp * SLOT4 + b * 4 * FFN_THREADS + tid);
     };
 #pragma unroll
     for (int b = 0; b < D; ++b) load(b);
@@ -571,7 +592,7 @@ __device__ __forceinline__ void reduce_tile(const FusedArgs& a, unsigned char* s
   else {
 #pragma unroll 1
     for (int b = 0; b < NB; ++b) {
-      const f32x4_t* src = slots + b * 4 * 256 + tid;
+      const f32x4_t* src = slots + b * 4 * FFN_THREADS + tid;
       f32x16_t t = load_block16(src);
       for (int sp = 1; sp < a.S; ++sp) t += load_block16(src + (int64_t)sp * SLOT4);
       stage(b, t);
@@ -597,13 +618,15 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
                                          int e, int n_rows,
                                          int mt, int nt, int s, int col0, int target, int half, int* s_stop,
                                          uint32_t** s_pend, int* s_pend_y) {
+  // waves: WGM x WGN, each a WM x 64 wave tile of MI x 2 MFMA blocks (GLU: one block of gate columns and the
+  // block of up columns that pairs with it)
   constexpr int BM = 256, BK = 64;
-  constexpr int WM = 128, WN = BN / 2, MI = WM / 32, NI = WN / 32;
+  constexpr int WGN = BN / 64, WGM = FFN_WAVES / WGN, WM = BM / WGM, MI = WM / 32, NI = 2;
   constexpr int OUT_BN = GLU ? BN / 2 : BN;
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, STAGE = A_BYTES + B_BYTES;
-  constexpr int A_LOADS = BM / 8 / 4, B_LOADS = BN / 8 / 4;  // 1 KB wave loads (8 rows) per wave per k-tile
+  constexpr int A_LOADS = BM / 8 / FFN_WAVES, B_LOADS = BN / 8 / FFN_WAVES;  // 1 KB wave loads (8 rows) per k-tile
   constexpr int N_LOADS = A_LOADS + B_LOADS;
-  static_assert(!GLU || NI % 2 == 0, "GLU pairs gate and up blocks");
+  static_assert(WGN >= 1 && WGM * WGN == FFN_WAVES && MI >= 1, "wave grid");
   static_assert(B_LOADS >= 1, "tile width");
 
   // the thread index, made opaque per item, so that lane-derived addresses are computed here instead of being
@@ -611,7 +634,7 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int K = GLU ? a.d : a.f;
   const int nk = GLU ? K / BK : K / BK / a.S;
   const int kt0 = GLU ? 0 : s * nk;
@@ -658,10 +681,12 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
   const int mact = min(MI, max(0, (n_rows - wm * WM + 31) / 32));
   auto kloop = [&](auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
-    // slots of a k-step: MFMA i (if i < MI*NI), then fragment read i (if i < MI+NI), then loads; the loads go
-    // after the slots with a read where there are such slots, else spread over all of them
+    // slots of a k-step: MFMA i (if i < MI*NI); the next k-step's fragment reads all go out in the first RS
+    // slots, so that each has most of the k-step's MFMAs to land in (spread one per slot, the last ones arrived
+    // two MFMAs before they were needed: ~8% slower first-GEMM k-loops); the loads go in the slots after those
     constexpr int NSLOT = MI * NI > MI + NI ? MI * NI : MI + NI;
-    constexpr int FIRST = MI * NI > MI + NI ? MI + NI : 0;
+    constexpr int RS = NSLOT >= 4 ? 2 : 1, RPS = (MI + NI + RS - 1) / RS;  // read slots, reads per slot
+    constexpr int FIRST = NSLOT > RS ? RS : 0;
     constexpr int HALF = (N_LOADS + 1) / 2;  // loads per half k-tile
     constexpr int DPS = (HALF + (NSLOT - FIRST) - 1) / (NSLOT - FIRST);
     // fragment i of k-step ks (i < MI: A block i, else B block i - MI) from the stage at sa
@@ -672,8 +697,8 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
       } else {
         const int ni = i - MI;
         int row;
-        if (GLU) row = ni < NI / 2 ? wn * (WN / 2) + ni * 32 : BN / 2 + wn * (WN / 2) + (ni - NI / 2) * 32;
-        else row = wn * WN + ni * 32;
+        if (GLU) row = ni == 0 ? wn * 32 : BN / 2 + wn * 32;
+        else row = wn * 64 + ni * 32;
         B_[ni] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(sa + A_BYTES + (row + (lane & 31)) * 128 + sl));
       }
     };
@@ -697,9 +722,12 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
         const int mi = i / NI, ni = i % NI;
         if (i < MI * NI && (FULL || mi < mact))
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][mi], fb[c][ni], acc[mi][ni], 0, 0, 0);
-        if (i < MI + NI) {
-          if (ks < 3) frag1(sa, ks + 1, i, fa[c ^ 1], fb[c ^ 1]);
-          else if (M1) frag1(nsa, 0, i, fa[c ^ 1], fb[c ^ 1]);
+        if (i < RS) {
+#pragma unroll
+          for (int r = i * RPS; r < (i + 1) * RPS && r < MI + NI; ++r) {
+            if (ks < 3) frag1(sa, ks + 1, r, fa[c ^ 1], fb[c ^ 1]);
+            else if (M1) frag1(nsa, 0, r, fa[c ^ 1], fb[c ^ 1]);
+          }
         }
         if (i >= FIRST && ((ks == 3 && M2) || (ks == 0 && M1))) {
           // first half of k-tile kt+2 after this tile's barrier; second half of k-tile kt+1 in k-step 0
@@ -749,15 +777,15 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
   // epilogue: every wave writes its bf16 outputs into LDS as a 256 x OUT_BN tile (16-byte chunk ch of row r at
   // chunk ch ^ (r & 7), so neither the column writes nor the row reads collide), then 16-byte stores of the
   // tile's real rows
-  constexpr int NO = GLU ? NI / 2 : NI;
-  constexpr int OUT_ROW = OUT_BN * 2, CPR = OUT_ROW / 16;
+  constexpr int NO = GLU ? 1 : NI;
+  constexpr int OUT_ROW = OUT_BN * 2;
   // the thread index, made opaque here, so that the many epilogue addresses are computed per item instead of
   // being hoisted out of the item loop, where they would hold (and spill) registers through the k-loop
   int tid_e = tid;
   asm volatile("" : "+v"(tid_e));
   const int lane_e = tid_e & 63;
   auto stage = [&](int mi, int ni, const f32x16_t& v, const f32x16_t& up) {  // one 32 x 32 block into LDS
-    const int col = (GLU ? wn * (WN / 2) : wn * WN) + ni * 32 + (lane_e & 31);
+    const int col = (GLU ? wn * 32 : wn * 64 + ni * 32) + (lane_e & 31);
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int row = wm * WM + mi * 32 + (q >> 2) * 8 + (lane_e >> 5) * 4 + (q & 3);
@@ -771,28 +799,32 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
     // ((mi * NI + ni) * 4 + q4) * 256 + tid of its slot; a half item writes the chunks that the full tile's
     // threads of its columns would), waits for the stores to complete, and counts itself in; the item that
     // completes the tile sums it (reduce_tile)
-    constexpr int BNF = HALF_TILE ? 2 * BN : BN, NIF = BNF / 2 / 32, SLOT4 = BM * BNF / 4;
+    // the full tile's wave grid (a half item's blocks go where the full tile's thread for those rows and columns
+    // keeps them)
+    constexpr int BNF = HALF_TILE ? 2 * BN : BN, SLOT4 = BM * BNF / 4, NT = FFN_THREADS;
+    constexpr int WGN_F = BNF / 64, WM_F = BM / (FFN_WAVES / WGN_F);
     const int64_t tile = (int64_t)mt * a.n_nt2 + nt;
     f32x4_t* slot = (f32x4_t*)(a.partial + tile * a.S * (BM * BNF)) + (int64_t)s * SLOT4;
-    const int tid_f = HALF_TILE ? (wm * 2 + half) * 64 + lane : tid;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
-        const int b = HALF_TILE ? mi * NIF + wn * NI + ni : mi * NI + ni;
-        f32x4_t* dst = slot + b * 4 * 256 + tid_f;
+        const int row0 = wm * WM + mi * 32, col0 = (HALF_TILE ? half * BN : 0) + wn * 64 + ni * 32;
+        const int tid_f = ((row0 / WM_F) * WGN_F + col0 / 64) * 64 + lane;
+        const int b = ((row0 % WM_F) / 32) * NI + ni;
+        f32x4_t* dst = slot + b * 4 * NT + tid_f;
         const f32x16_t v = acc[mi][ni];
         store16_coherent(dst, __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v, v, 0, 1, 2, 3)));
-        store16_coherent(dst + 256, __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v, v, 4, 5, 6, 7)));
-        store16_coherent(dst + 512, __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v, v, 8, 9, 10, 11)));
-        store16_coherent(dst + 768, __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v, v, 12, 13, 14, 15)));
+        store16_coherent(dst + NT, __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v, v, 4, 5, 6, 7)));
+        store16_coherent(dst + 2 * NT, __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v, v, 8, 9, 10, 11)));
+        store16_coherent(dst + 3 * NT, __builtin_bit_cast(u32x4_t, __builtin_shufflevector(v, v, 12, 13, 14, 15)));
       }
     wait_stores();
     __syncthreads();  // every thread's partial stores completed; every wave is done with the operand stages
     if (tid == 0) *s_stop = (int)arrive(&a.scount[tile], a.epoch);
     __syncthreads();
     if (*s_stop != target - 1) return true;  // the tile is not complete yet
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    flag_acquire();  // the other splits' partial sums completed before they counted themselves in
     reduce_tile<BNF>(a, smem, s_rows, s_hdr, n_rows, mt, nt);
     return true;
   }
@@ -800,7 +832,7 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < NO; ++ni) stage(mi, ni, acc[mi][ni], acc[mi][GLU ? ni + NI / 2 : ni]);
+    for (int ni = 0; ni < NO; ++ni) stage(mi, ni, acc[mi][ni], acc[mi][GLU ? 1 : ni]);
   __syncthreads();
   const RowDst dst = GLU ? RowDst{nullptr, 0, 0, 0} : self_dst(a.self_recv, s_hdr, (int64_t)col0 * 2);
   store_rows<OUT_BN>(smem, Cb + (GLU ? (int64_t)nt * OUT_BN : (int64_t)col0) * 2, ldc, s_rows, n_rows, tid_e, dst);
@@ -822,7 +854,7 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
 }
 
 template <int BN1, int BN2>
-__global__ __launch_bounds__(256, 1) void k_ffn_bf16(FusedArgs a) {
+__global__ __launch_bounds__(FFN_THREADS, 1) void k_ffn_bf16(FusedArgs a) {
   constexpr int BM = 256, BK = 64, BNX = BN1 > BN2 ? BN1 : BN2;
   constexpr int STAGE = (BM + BNX) * BK * 2;
   static_assert(BM * BN2 * 2 <= 2 * STAGE && BM * BN1 <= 2 * STAGE, "output staging fits the operand stages");
@@ -833,6 +865,7 @@ __global__ __launch_bounds__(256, 1) void k_ffn_bf16(FusedArgs a) {
   __shared__ uint32_t* s_pend;  // flag of the previous item, published once its stores have completed
   __shared__ int s_pend_y;
 
+  launch_acquire();  // drop cache lines older than this launch (the publish protocol in common.h)
   if (load_status(a.status) != 0) return;
   if (a.n_cons > 0 && blockIdx.x == 0) consumer_stamp(a.cons);
   const int n_mt = a.scalars[a.sc_nmt];
@@ -845,6 +878,7 @@ __global__ __launch_bounds__(256, 1) void k_ffn_bf16(FusedArgs a) {
     if (f == nullptr) return;
     const int y = s_pend_y;
     wait_stores();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
     if (tid == 0) {
       __hip_atomic_store(f, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -904,7 +938,7 @@ __global__ __launch_bounds__(256, 1) void k_ffn_bf16(FusedArgs a) {
     {
       const int32_t* dsc = a.mtile_desc + (int64_t)it.mt * MOE_MT_FIELDS;
       if (tid < MOE_MT_HDR) s_hdr[tid] = dsc[tid];
-      s_rows[tid] = dsc[MOE_MT_HDR + tid];  // 256 threads, 256 rows
+      if (tid < MOE_MT_ROWS) s_rows[tid] = dsc[MOE_MT_HDR + tid];
     }
     if (a.ts != nullptr && first && tid == 0) atomicMin((unsigned long long*)&a.ts[0], (unsigned long long)moe_clock());
     first = false;
@@ -955,6 +989,7 @@ __global__ __launch_bounds__(256, 1) void k_ffn_bf16(FusedArgs a) {
 }
 
 __global__ __launch_bounds__(256) void k_consumer(ConsumerArgs c) {
+  launch_acquire();
   if (blockIdx.x == 0) consumer_stamp(c);
   consumer_role(c);
 }
@@ -1094,7 +1129,7 @@ int launch_bf16(const FfnLaunch& p, int grid, int n_cons, hipStream_t st, hipEve
   a.n_cons = n_cons;
   fill_consumer(a.cons, p, a.n_nt2);
   a.self_recv = (unsigned char*)p.recv[p.self_rank];
-  const dim3 g(grid), b(256);
+  const dim3 g(grid), b(FFN_THREADS);
   if (bn1 == 256 && bn2 == 256) hipExtLaunchKernelGGL((k_ffn_bf16<256, 256>), g, b, 0, st, ev0, ev1, 0, a);
   else if (bn1 == 256 && bn2 == 128) hipExtLaunchKernelGGL((k_ffn_bf16<256, 128>), g, b, 0, st, ev0, ev1, 0, a);
   else if (bn1 == 256) hipExtLaunchKernelGGL((k_ffn_bf16<256, 64>), g, b, 0, st, ev0, ev1, 0, a);

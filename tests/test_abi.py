@@ -142,8 +142,9 @@ CSRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
 def test_inline_asm_carries_its_wait_states():
     """The compiler inserts hazard wait states only around instructions it emits itself, so every inline-assembly
     statement that needs them carries its own: a store wider than 8 bytes is followed by two wait states before
-    its data registers may be rewritten (s_nop 1), and an SALU write of M0 by one before the LDS-DMA load that
-    reads it (s_nop 0)."""
+    its data registers may be rewritten (s_nop 1), and every SALU write of M0 by one (s_nop), which the LDS-DMA
+    load that reads M0 needs.  M0 is a reserved register that a clobber list may not name, so a statement that
+    writes M0 first saves it in an output register and writes the saved value back as its last M0 write."""
     found = {"store": 0, "m0": 0}
     for fn in sorted(os.listdir(CSRC)):
         if not fn.endswith((".hip", ".h", ".cpp")):
@@ -152,13 +153,24 @@ def test_inline_asm_carries_its_wait_states():
         for stmt in re.findall(r'asm\s+volatile\s*\(\s*((?:"[^"]*"\s*)+)', src):
             text = "".join(re.findall(r'"([^"]*)"', stmt)).replace("\\n", "\n").replace("\\t", " ")
             ins = [l.strip() for l in text.split("\n") if l.strip()]
+            assert not re.search(r'"m0"', src[src.index(stmt):src.index(stmt) + len(stmt) + 400].split(";")[0]), \
+                (fn, "M0 named in a clobber list")
+            m0_writes = [i for i, op in enumerate(ins) if re.match(r"s_mov_b32\s+m0\s*,", op)]
             for i, op in enumerate(ins):
                 if re.match(r"(global|buffer|flat)_store_dwordx(3|4)\b", op):
                     found["store"] += 1
                     assert i + 1 < len(ins) and re.match(r"s_nop\s+[1-9]", ins[i + 1]), (fn, text)
-                if op.startswith("s_mov_b32 m0"):
-                    found["m0"] += 1
-                    assert i + 2 < len(ins) and ins[i + 1].startswith("s_nop") and "lds" in ins[i + 2], (fn, text)
+                if "_lds_" in op or op.endswith(" lds"):
+                    # the LDS-DMA load reads the M0 set before it, one wait state after that write
+                    assert any(w + 1 < i and ins[w + 1].startswith("s_nop") for w in m0_writes), (fn, text)
+            if m0_writes:
+                found["m0"] += 1
+                save = re.match(r"s_mov_b32\s+(%\d+)\s*,\s*m0$", ins[0])
+                assert save, (fn, "M0 not saved first", text)
+                last = ins[m0_writes[-1]]
+                assert re.match(r"s_mov_b32\s+m0\s*,\s*" + re.escape(save.group(1)) + r"$", last), (fn, text)
+                for w in m0_writes:
+                    assert w + 1 < len(ins) and ins[w + 1].startswith("s_nop"), (fn, text)
     assert found["store"] >= 1 and found["m0"] >= 1, found
 
 

@@ -5,6 +5,8 @@ tolerance of ``tolerance.py``; delivery bit-equal to the GPU's own y rows; seque
 equal.  Small shapes are compared element by element; the full-size workloads compare the complete layout and
 sampled rows and tokens, in the launch configuration the benchmark times.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -274,24 +276,51 @@ def test_full_size_parity(name):
     np.testing.assert_array_equal(bits(P.out), out_ovl)
 
 
-def test_overlap_ordering_stress():
-    """Many overlapped runs over consumer partitions and segment sizes; delivery must be exact every time."""
-    s = mi.Spec("stress", R=4, T_o=512, G=16, E_l=4, k=2, d=512, f=512, M=32, seed=21)
+STRESS_SHAPES = [
+    # 4 k-splits (partial sums handed between workgroups, last-arriver reductions), ragged row tiles
+    mi.Spec("stress_splitk", R=4, T_o=600, G=8, E_l=2, k=2, d=256, f=1024, M=32, seed=21),
+    # no split, many small segments (16 experts x 4 owners), many flags per segment wait
+    mi.Spec("stress_segs", R=4, T_o=512, G=16, E_l=4, k=2, d=512, f=512, M=32, seed=25),
+]
+
+
+@pytest.mark.parametrize("mgb", [1, 2])
+@pytest.mark.parametrize("s", STRESS_SHAPES, ids=lambda v: v.name)
+def test_overlap_ordering_stress(s, mgb):
+    """Publish/acquire ordering under stress (the page's falsifier: "What would settle it"): 500 overlapped calls per
+    shape and segment size (2,000 in all) over consumer partitions {1, 2, 4, 8, 16, 32}, band windows {2, 4, 16} and
+    shuffled epochs; every call's delivered rows, and the self owner's rows the producer stores, must equal the
+    sequential call's bit for bit.  Stops at the first mismatch (and names the call)."""
+    s = dataclasses.replace(s, mgb=mgb)
     run = Run(s)
     check_route_and_layout(run)
-    ref = None
-    for it, cus in enumerate([1, 2, 4, 8, 16, 32] * 4):
+    P = run.P
+    run.ffn(mode=1)
+    torch.cuda.synchronize()
+    assert P.status() == B.MOE_OK
+    ref = [P.recv[r][: int(run.lay["N_r"][r])].clone() for r in range(s.R)]
+    rng = np.random.default_rng(1000 + mgb)
+    last = P.epoch
+    for it in range(500):
+        cus = int(rng.choice([1, 2, 4, 8, 16, 32]))
+        win = int(rng.choice([2, 4, 16]))
+        ep = last
+        while ep == last:  # shuffled, but never the value the flags hold from the previous call
+            ep = int(rng.integers(1, 1 << 31))
+        last = ep
         for r in range(s.R):
-            run.P.recv[r].fill_(float("nan"))
-        run.ffn(mode=0, consumer_cus=cus)
+            P.recv[r].fill_(float("nan"))
+        run.ffn(mode=0, consumer_cus=cus, band_window=win, epoch=ep)
         torch.cuda.synchronize()
-        assert run.P.status() == B.MOE_OK
-        check_delivery(run)
-        cur = [bits(b) for b in run.P.recv]
-        if ref is None:
-            ref = cur
-        for a, b in zip(cur, ref):
-            np.testing.assert_array_equal(a, b)
+        st = P.status()
+        assert st == B.MOE_OK, "call %d (consumer_cus %d, band_window %d): status %d" % (it, cus, win, st)
+        for r in range(s.R):
+            got = P.recv[r][: ref[r].shape[0]]
+            if not torch.equal(got.view(torch.int16), ref[r].view(torch.int16)):
+                bad = (got.view(torch.int16) != ref[r].view(torch.int16)).any(dim=1).nonzero().flatten()[:8].tolist()
+                raise AssertionError("call %d (consumer_cus %d, band_window %d, epoch %d): owner %d rows %s differ"
+                                     % (it, cus, win, ep, r, bad))
+    check_delivery(run)
 
 
 @pytest.mark.parametrize("name", ["splitk", "mixtral"])
