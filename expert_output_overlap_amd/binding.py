@@ -21,7 +21,7 @@ MT_HDR = 8
 MT_FIELDS = MT_HDR + 256
 EXPORTS = ["moe_last_error", "moe_version", "moe_route", "moe_layout_capacity_rows", "moe_layout_workspace_bytes",
            "moe_layout_bind", "moe_layout_build", "moe_read_status", "moe_ffn_flags_count", "moe_pick_consumer_cus",
-           "moe_expert_ffn_overlap",
+           "moe_expert_ffn_overlap", "moe_ffn_schedule",
            "moe_combine", "moe_set_kernel_timing", "moe_kernel_times"]
 
 
@@ -32,7 +32,7 @@ class moe_shape(ctypes.Structure):
 
 LAYOUT_ARRAYS = ["counts", "padded_off", "recv_off", "tile_owner", "tile_expert", "tile_valid", "tile_order",
                  "seg_desc", "row_src", "combine_plan", "scalars", "status", "mtile_desc", "seg_mtiles",
-                 "seg_sched", "chunk_counts"]
+                 "seg_sched", "chunk_counts", "mt_order"]
 
 
 class moe_layout(ctypes.Structure):
@@ -43,7 +43,7 @@ class moe_layout(ctypes.Structure):
 class moe_overlap_cfg(ctypes.Structure):
     _fields_ = [("consumer_cus", ctypes.c_int32), ("mode", ctypes.c_int32), ("epoch", ctypes.c_uint32),
                 ("band_window", ctypes.c_int32), ("watchdog_ticks", ctypes.c_uint64),
-                ("timestamps", ctypes.c_void_p)]
+                ("timestamps", ctypes.c_void_p), ("tile_order", ctypes.c_int32)]
 
 
 class MoeError(RuntimeError):
@@ -74,6 +74,7 @@ def lib():
             "moe_pick_consumer_cus": ([ps, i32], i32),
             "moe_expert_ffn_overlap": ([ps, pl, vp, vp, vp, vp, vp, vp, vp, pc, vp], i32),
             "moe_combine": ([ps, pl, vp, vp, vp, vp], i32),
+            "moe_ffn_schedule": ([ps, i32, pc, i32, i32, vp, vp, vp, i64, ctypes.POINTER(ctypes.c_int64)], i32),
             "moe_set_kernel_timing": ([i32], i32), "moe_kernel_times": ([ctypes.POINTER(ctypes.c_double)], i32),
         }
         for name, (args, res) in sig.items():
@@ -158,6 +159,22 @@ def moe_expert_ffn_overlap(shape: moe_shape, layout: moe_layout, x_pad, w_gate_u
     return _check("moe_expert_ffn_overlap", lib().moe_expert_ffn_overlap(
         ctypes.byref(shape), ctypes.byref(layout), _ptr(x_pad), _ptr(w_gate_up), _ptr(w_down), _ptr(h_ws),
         _ptr(y_pad), _ptr_array(recv), _ptr(flags), ctypes.byref(cfg), _stream(stream)))
+
+
+def moe_ffn_schedule(shape: moe_shape, n_cu: int, cfg: moe_overlap_cfg, mt_hdr, mt_order, n_remote: int):
+    """The bf16 FFN launch's item list (host only): int32 numpy array [n, 8] of {workgroup, sequence, kind, row tile,
+    column tile, split, half, target} by list index.  mt_hdr: int32 [n_mtiles, 4]; mt_order: int32 [n_mtiles]."""
+    import numpy as np
+
+    mt_hdr = np.ascontiguousarray(mt_hdr, dtype=np.int32).reshape(-1, 4)
+    mt_order = np.ascontiguousarray(mt_order, dtype=np.int32).reshape(-1)
+    n = ctypes.c_int64(0)
+    args = (ctypes.byref(shape), n_cu, ctypes.byref(cfg), mt_hdr.shape[0], n_remote, mt_hdr.ctypes.data,
+            mt_order.ctypes.data)
+    _check("moe_ffn_schedule", lib().moe_ffn_schedule(*args, None, 0, ctypes.byref(n)))
+    out = np.zeros((max(n.value, 1), 8), dtype=np.int32)
+    _check("moe_ffn_schedule", lib().moe_ffn_schedule(*args, out.ctypes.data, n.value, ctypes.byref(n)))
+    return out[: n.value]
 
 
 def moe_combine(shape: moe_shape, layout: moe_layout, topk_w, recv, out, stream=None) -> int:

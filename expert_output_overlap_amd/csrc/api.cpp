@@ -71,7 +71,7 @@ struct Carve {
 
 struct Offsets {
   int64_t counts, padded_off, recv_off, tile_owner, tile_expert, tile_valid, tile_order, seg_desc, row_src,
-      combine_plan, scalars, status, mtile_desc, seg_mtiles, seg_sched, chunk_counts, total;
+      combine_plan, scalars, status, mtile_desc, seg_mtiles, seg_sched, chunk_counts, mt_order, total;
   int64_t cap_rows, cap_tiles, cap_mtiles;
 };
 
@@ -95,12 +95,13 @@ Offsets layout_offsets(const moe_shape* s) {
   o.seg_desc = c.take(o.cap_tiles * MOE_SEG_FIELDS, 4);
   o.row_src = c.take(o.cap_rows, 4);
   o.combine_plan = c.take(T * s->top_k, 4);
-  o.scalars = c.take(4 + s->R, 4);
+  o.scalars = c.take(5 + s->R, 4);
   o.status = c.take(1, 4);
   o.mtile_desc = c.take(o.cap_mtiles * MOE_MT_FIELDS, 4);
   o.seg_mtiles = c.take(o.cap_tiles * 2, 4);
   o.seg_sched = c.take(o.cap_tiles, 4);
   o.chunk_counts = c.take((int64_t)s->R * n_chunks * s->num_local_experts, 4);
+  o.mt_order = c.take(o.cap_mtiles, 4);
   o.total = c.off;
   return o;
 }
@@ -222,6 +223,7 @@ int moe_layout_bind(const moe_shape* s, void* workspace, int64_t workspace_bytes
   L->seg_mtiles = (int32_t*)(b + o.seg_mtiles);
   L->seg_sched = (int32_t*)(b + o.seg_sched);
   L->chunk_counts = (int32_t*)(b + o.chunk_counts);
+  L->mt_order = (int32_t*)(b + o.mt_order);
   L->cap_rows = o.cap_rows;
   L->cap_tiles = o.cap_tiles;
   L->cap_mtiles = o.cap_mtiles;
@@ -231,7 +233,7 @@ int moe_layout_bind(const moe_shape* s, void* workspace, int64_t workspace_bytes
 static bool layout_ok(const moe_layout* L) {
   return L && L->counts && L->padded_off && L->recv_off && L->tile_owner && L->tile_expert && L->tile_valid &&
          L->tile_order && L->seg_desc && L->row_src && L->combine_plan && L->scalars && L->status &&
-         L->mtile_desc && L->seg_mtiles && L->seg_sched && L->chunk_counts && L->cap_rows > 0;
+         L->mtile_desc && L->seg_mtiles && L->seg_sched && L->chunk_counts && L->mt_order && L->cap_rows > 0;
 }
 
 int moe_layout_build(const moe_shape* s, const int32_t* topk_idx, const void* x, moe_layout* L, void* x_pad,
@@ -304,6 +306,7 @@ int moe_expert_ffn_overlap(const moe_shape* s, const moe_layout* L, const void* 
   if (cfg->epoch == 0) return fail(MOE_EINVAL, "epoch must be nonzero");
   if (cfg->mode < 0 || cfg->mode > 2) return fail(MOE_EINVAL, "mode must be 0, 1 or 2");
   if (cfg->band_window < 0) return fail(MOE_EINVAL, "band_window must be >= 0");
+  if (cfg->tile_order != 0 && cfg->tile_order != 1) return fail(MOE_EINVAL, "tile_order must be 0 or 1");
   hipStream_t st = (hipStream_t)stream;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(MOE_EHIP, "hipGetDevice failed");
@@ -331,6 +334,7 @@ int moe_expert_ffn_overlap(const moe_shape* s, const moe_layout* L, const void* 
   p.flags = flags;
   p.epoch = cfg->epoch;
   p.band_window = cfg->band_window;
+  p.tile_order = cfg->tile_order;
   p.watchdog_ticks = cfg->watchdog_ticks ? cfg->watchdog_ticks : 200000000ull;
   p.timestamps = cfg->timestamps;
   p.cap_mtiles = layout_offsets(s).cap_mtiles;
@@ -376,6 +380,39 @@ int moe_expert_ffn_overlap(const moe_shape* s, const moe_layout* L, const void* 
     std::lock_guard<std::mutex> lk(g_mu);
     g_events.push_back(ce);
   }
+  return MOE_OK;
+}
+
+int moe_ffn_schedule(const moe_shape* s, int32_t n_cu, const moe_overlap_cfg* cfg, int32_t n_mtiles,
+                     int32_t n_remote_mtiles, const int32_t* mt_hdr, const int32_t* mt_order, int32_t* items,
+                     int64_t cap, int64_t* n_items) {
+  const std::string e = check_shape(s);
+  if (!e.empty()) return fail(MOE_EINVAL, e);
+  if (s->dtype != MOE_BF16) return fail(MOE_EINVAL, "the fp32 path runs two plain launches, not an item list");
+  if (!cfg || !n_items || n_cu < 2 || n_mtiles < 0 || n_remote_mtiles < 0 || n_remote_mtiles > n_mtiles)
+    return fail(MOE_EINVAL, "bad arguments");
+  if (n_mtiles > 0 && (!mt_hdr || !mt_order)) return fail(MOE_EINVAL, "null pointer");
+  if (cfg->mode != 0 && cfg->mode != 1) return fail(MOE_EINVAL, "mode must be 0 or 1");
+  if (cfg->consumer_cus < 0 || cfg->consumer_cus > n_cu / 2 || cfg->band_window < 0 ||
+      (cfg->tile_order != 0 && cfg->tile_order != 1))
+    return fail(MOE_EINVAL, "consumer_cus, band_window or tile_order out of range");
+  std::vector<int32_t> ident;
+  if (cfg->tile_order == 1) {  // row-tile numbering: no boundary
+    ident.resize(n_mtiles);
+    for (int i = 0; i < n_mtiles; ++i) ident[i] = i;
+    mt_order = ident.data();
+    n_remote_mtiles = n_mtiles;
+  }
+  for (int i = 0; i < n_mtiles; ++i) {
+    const int32_t* h = mt_hdr + 4 * (int64_t)i;
+    if (h[2] < 0 || h[3] < 1 || h[2] + h[3] > n_mtiles || i < h[2] || i >= h[2] + h[3] || mt_order[i] < 0 ||
+        mt_order[i] >= n_mtiles)
+      return fail(MOE_EINVAL, "row-tile headers or order out of range");
+  }
+  const int C = cfg->mode == 0 ? (cfg->consumer_cus ? cfg->consumer_cus : moe_pick_consumer_cus(s, n_cu)) : 0;
+  if (ffn_schedule_host(s->d, s->f, s->num_local_experts, C, n_cu - C, cfg->band_window, n_mtiles, n_remote_mtiles,
+                        mt_hdr, mt_order, items, cap, n_items))
+    return items == nullptr && cap == 0 ? MOE_OK : fail(MOE_EINVAL, "cap is below the list length");
   return MOE_OK;
 }
 

@@ -22,6 +22,7 @@
 
 #include "common.h"
 #include "consumer.h"
+#include "item_list.h"
 #include "launch.h"
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -325,12 +326,11 @@ __device__ __forceinline__ float silu_fast(float g) { return g * __builtin_amdgc
 //     flags1 of the h columns that split reads.  With S > 1 splits, each split stores fp32 partial sums and
 //     counts itself in; the last to arrive adds the partial sums in split order, stores the bf16 y tile and
 //     publishes flags2[mt][nt], which the consumer waits on.
-// Items are listed as all GEMM1 items, then the GEMM2 items window by window (band_window row tiles,
-// remote-first order), so row tiles complete (and are returned) one window after another during the second
-// part of the launch.  Producer workgroup b takes items b, b + G, ... (XCD-aware: a run of consecutive items
-// goes to the workgroups of one XCD, which share the operands in their L2).  Every wait is on an item earlier in
-// the list, so the lowest unfinished item can always run: the waits end while every workgroup is resident, and
-// a spin budget bounds them otherwise.
+// The list and who runs which item are in item_list.h: GEMM2 items go window by window over the row tiles in
+// remote-first order (every row tile holding a row bound for another owner before every row tile of self-owned
+// rows only), so row tiles complete (and are returned) one window after another during the second part of the
+// launch.  Every wait is on an item earlier in the list, so the lowest unfinished item can always run: the waits
+// end while every workgroup is resident, and a spin budget bounds them otherwise.
 
 struct FusedArgs {
   const unsigned char* x;   // x_pad [cap_rows, d]
@@ -342,6 +342,8 @@ struct FusedArgs {
   int n_nt1, n_nt2, S, window;
   int interleave;  // item order: 0 = GEMM1 first, 1 = interleaved windows
   const int32_t* mtile_desc;
+  const int32_t* mt_order;  // [n_mt] row tile at each position of the list (remote-bound row tiles first), or
+                            // null: row-tile numbering
   const int32_t* scalars;
   int sc_nmt;
   int32_t* status;
@@ -356,81 +358,6 @@ struct FusedArgs {
   ConsumerArgs cons;
   unsigned char* self_recv;  // the self owner's buffer: y rows of the self-owned groups go straight there
 };
-
-struct FfnItem {
-  int kind;  // 1: GEMM1 tile, 2: GEMM2 split
-  int mt, nt, s;
-  int stride;  // GEMM2: list distance between consecutive splits of the tile
-};
-
-// Item i of the list, in one of two orders over windows of W row tiles (row tiles expert by expert); inside a
-// window, GEMM1 items are column-tile major (consecutive items share a weight tile) and GEMM2 items split-major,
-// then column-tile major, so consecutive GEMM2 items share a down-projection weight tile too.
-//  - GEMM1 first: every GEMM1 item (each gate/up weight tile streamed once; the kernel lists them expert by
-//    expert itself, from the row tiles' run fields, and uses this function for the rest), then the GEMM2
-//    windows.  A GEMM2 split reads only its own share of h's columns, which the first part of the GEMM1 list
-//    produced; row tiles complete window after window during the last part of the launch.  With at most four
-//    windows that leaves most of the return to the launch's last round, so there every window but the first goes
-//    row tile by row tile instead (split-major inside a row tile), and its row tiles complete one after another;
-//    the first keeps the weight sharing (its row tiles publish together, early enough to be returned under the
-//    later windows).
-//    The window(s) whose GEMM2 items end the list (the last one; with interleaving the last two) go row tile by
-//    row tile in every order, so that what is left to return after the last publish is one row tile's rows.
-//  - interleaved: G1(0), G1(1), G2(0), G1(2), G2(1), ..., G1(nw-1), G2(nw-2), G2(nw-1): row tiles complete
-//    window after window over the whole launch, so a return that is large next to the FFN starts early.
-// In both, every GEMM2 item follows the GEMM1 items it reads and the last split of a tile follows its others.
-__device__ __forceinline__ FfnItem ffn_item(int i, int n_mt, int W, int n1, int n2, int S, bool interleave) {
-  const int n2S = n2 * S;
-  auto g1 = [&](int w, int j, int Wc) {  // GEMM1 item j of a window of Wc row tiles starting at row tile w*W
-    FfnItem it;
-    it.kind = 1;
-    it.nt = j / Wc;
-    it.mt = w * W + (j - it.nt * Wc);
-    it.s = 0;
-    it.stride = 0;
-    return it;
-  };
-  const int nw = (n_mt + W - 1) / W;
-  const bool by_tile = !interleave && nw <= 4;
-  auto g2 = [&](int w, int j, int Wc) {
-    FfnItem it;
-    it.kind = 2;
-    if ((by_tile && w >= 1) || w >= nw - (interleave ? 2 : 1)) {
-      const int ml = j / n2S, r = j - ml * n2S;
-      it.s = r / n2;
-      it.nt = r - it.s * n2;
-      it.mt = w * W + ml;
-      it.stride = n2;
-      return it;
-    }
-    const int per = Wc * n2;
-    it.s = j / per;
-    const int r = j - it.s * per;
-    it.nt = r / Wc;
-    it.mt = w * W + (r - it.nt * Wc);
-    it.stride = per;
-    return it;
-  };
-  const int Wl = n_mt - (nw - 1) * W;
-  if (!interleave) {  // i >= n_mt * n1: the kernel maps the GEMM1 part of this order itself
-    const int j = i - n_mt * n1, w = j / (W * n2S);
-    return w < nw - 1 ? g2(w, j - w * W * n2S, W) : g2(nw - 1, j - (nw - 1) * W * n2S, Wl);
-  }
-  const int W0 = nw == 1 ? Wl : W;
-  if (i < W0 * n1) return g1(0, i, W0);
-  i -= W0 * n1;
-  if (nw == 1) return g2(0, i, Wl);
-  const int pz = W * (n1 + n2S);  // a pair (G1(p), G2(p-1)) of two full windows, p = 1 .. nw-2
-  if (i < (nw - 2) * pz) {
-    const int p = 1 + i / pz, j = i - (p - 1) * pz;
-    return j < W * n1 ? g1(p, j, W) : g2(p - 1, j - W * n1, W);
-  }
-  i -= (nw - 2) * pz;
-  if (i < Wl * n1) return g1(nw - 1, i, Wl);
-  i -= Wl * n1;
-  if (i < W * n2S) return g2(nw - 2, i, W);
-  return g2(nw - 1, i - W * n2S, Wl);
-}
 
 // All threads of the workgroup: wait until the n flags equal epoch, then acquire (compiler ordering; see the
 // publish protocol in common.h).  False if the spin budget ran
@@ -869,7 +796,6 @@ __global__ __launch_bounds__(FFN_THREADS, 1) void k_ffn_bf16(FusedArgs a) {
   if (load_status(a.status) != 0) return;
   if (a.n_cons > 0 && blockIdx.x == 0) consumer_stamp(a.cons);
   const int n_mt = a.scalars[a.sc_nmt];
-  const int n_items = n_mt * (a.n_nt1 + a.n_nt2 * a.S);
   const int tid = threadIdx.x;
   if (tid == 0) s_pend = nullptr;
   // every wave's stores of the previous item have completed, then its flag (a wait on it may come next)
@@ -887,54 +813,20 @@ __global__ __launch_bounds__(FFN_THREADS, 1) void k_ffn_bf16(FusedArgs a) {
     }
   };
   const int C = a.n_cons, G = gridDim.x - C;
-  // With every GEMM1 item first, no row tile is returned before the GEMM1 part of the list is done, so the
-  // consumer workgroups first take kc GEMM1 items each from the head of the list: just enough that the producers'
-  // share fits in as few rounds as the whole list would on all workgroups, and no more than the consumers finish
-  // before the GEMM1 part ends.  GEMM1 items wait on nothing, so the consumer's later waits still end.
-  int kc = 0;
-  if (C > 0 && a.interleave == 0) {
-    const int rounds = (n_items + G + C - 1) / (G + C), over = n_items - rounds * G;
-    kc = over > 0 ? (over + C - 1) / C : 0;
-    kc = min(kc, n_mt * a.n_nt1 / (G + C));
-  }
-  // The producers' last round holds q items.  When they are GEMM2 items and at most half a round, each becomes
-  // two items of half the tile width (columns [0, BN2/2) and [BN2/2, BN2) of its y tile), so that the round
-  // keeps twice as many CUs busy: a half-width tile takes ~0.7 of a full one's time.  Every output element is
-  // accumulated as before, so results do not change.  List items i >= i_tail are then the halves, two per item.
-  int i_tail = n_items, n_list = n_items;
-  if (BN2 >= 128 && n_items > C * kc) {
-    const int np = n_items - C * kc, q = np - (np - 1) / G * G;
-    const int nw = (n_mt + a.window - 1) / a.window, Wl = n_mt - (nw - 1) * a.window;
-    const int g2_tail = a.interleave == 0 ? n_mt * a.n_nt2 * a.S
-                                          : (Wl + (nw > 1 ? a.window : 0)) * a.n_nt2 * a.S;  // trailing GEMM2 items
-    if (2 * q <= G && q <= g2_tail) {
-      i_tail = n_items - q;
-      n_list = n_items + q;
-    }
-  }
+  // the item list (item_list.h): the consumers' share of GEMM1 items, the producers' round-robin share, and the
+  // half-width items of a last round at most half full
+  const FfnList L = ffn_list_make(n_mt, a.mt_order ? a.scalars[a.sc_nmt + 1] : n_mt, a.n_nt1, a.n_nt2, a.S, a.window,
+                                  a.interleave, C, G, BN2 >= 128);
+  auto run_of = [&](int mt, int* r0, int* rc) {
+    const int32_t* d = a.mtile_desc + (int64_t)mt * MOE_MT_FIELDS;
+    *r0 = d[2];
+    *rc = d[3];
+  };
+  auto order = [&](int p) { return a.mt_order ? (int)a.mt_order[p] : p; };
   bool first = true;
-  auto run = [&](int item) {  // one item of the list; false once the launch has failed
+  auto run = [&](int idx) {  // one item of the list; false once the launch has failed
     __syncthreads();  // previous item done with LDS and the header
-    int half = -1;
-    if (item >= i_tail) {
-      half = (item - i_tail) & 1;
-      item = i_tail + ((item - i_tail) >> 1);
-    }
-    FfnItem it;
-    if (a.interleave == 0 && item < n_mt * a.n_nt1) {
-      // GEMM1 part of the list with every GEMM1 item first: expert by expert (each expert's row tiles are one run
-      // of consecutive tiles), column-tile major inside an expert, so that a run of consecutive items -- one
-      // XCD's share of a round -- reads few distinct weight and row tiles.  Item i lies in the run of row tile
-      // i / n_nt1, since a run of c tiles holds c * n_nt1 items.
-      const int32_t* d = a.mtile_desc + (int64_t)(item / a.n_nt1) * MOE_MT_FIELDS;
-      const int r0 = d[2], rc = d[3], j = item - r0 * a.n_nt1;
-      it.kind = 1;
-      it.nt = j / rc;
-      it.mt = r0 + (j - it.nt * rc);
-      it.s = 0;
-    } else {
-      it = ffn_item(item, n_mt, a.window, a.n_nt1, a.n_nt2, a.S, a.interleave != 0);
-    }
+    const FfnItem it = ffn_list_item(L, idx, run_of, order);
     {
       const int32_t* dsc = a.mtile_desc + (int64_t)it.mt * MOE_MT_FIELDS;
       if (tid < MOE_MT_HDR) s_hdr[tid] = dsc[tid];
@@ -951,35 +843,20 @@ __global__ __launch_bounds__(FFN_THREADS, 1) void k_ffn_bf16(FusedArgs a) {
     const int per = a.n_nt1 / a.S;
     if (!wait_flags(a.flags1 + (int64_t)it.mt * a.n_nt1 + it.s * per, per, a.epoch, a.budget, a.status, &s_stop))
       return false;
-    // items that complete the y tile: its S splits, one more for each split that is halved
-    const int last = item + (a.S - 1 - it.s) * it.stride;
-    int target = a.S;
-    for (int sp = 0; sp < a.S; ++sp) target += last - (a.S - 1 - sp) * it.stride >= i_tail;
-    if (half < 0)
-      return ffn_tile<BN2, false>(a, smem, s_rows, s_hdr, e, n_rows, it.mt, it.nt, it.s, it.nt * BN2, target, -1, &s_stop,
-                                  &s_pend, &s_pend_y);
+    if (it.half < 0)
+      return ffn_tile<BN2, false>(a, smem, s_rows, s_hdr, e, n_rows, it.mt, it.nt, it.s, it.nt * BN2, it.target, -1,
+                                  &s_stop, &s_pend, &s_pend_y);
     if constexpr (BN2 >= 128)
       return ffn_tile<BN2 / 2, false, true>(a, smem, s_rows, s_hdr, e, n_rows, it.mt, it.nt, it.s,
-                                            it.nt * BN2 + half * (BN2 / 2), target, half, &s_stop, &s_pend, &s_pend_y);
+                                            it.nt * BN2 + it.half * (BN2 / 2), it.target, it.half, &s_stop, &s_pend,
+                                            &s_pend_y);
     return false;
   };
-  // A producer workgroup b takes items b', b' + G, ... after the consumers' share, b' remapped so that a run of
-  // consecutive items goes to the workgroups of one XCD (workgroup b sits on XCD b % 8), which share operand tiles
-  // in its L2; all workgroups move through the list in step.  (Claiming items from a counter instead balances the
-  // end better but loses that locality, and the clock drops with the extra off-XCD traffic: measured slower.)
-  const bool cons = (int)blockIdx.x < C;
+  // Producer workgroups move through the list in step, a run of consecutive items on one XCD, whose workgroups share
+  // operand tiles in its L2.  (Claiming items from a counter instead balances the end better but loses that
+  // locality, and the clock drops with the extra off-XCD traffic: measured slower.)
   int i0, i1, step;
-  if (cons) {
-    i0 = (int)blockIdx.x * kc;
-    i1 = i0 + kc;
-    step = 1;
-  } else {
-    int bid = blockIdx.x - C;
-    if ((G & 7) == 0 && (C & 7) == 0) bid = (bid & 7) * (G >> 3) + (bid >> 3);
-    i0 = C * kc + bid;
-    i1 = n_list;
-    step = G;
-  }
+  ffn_list_range(L, (int)blockIdx.x, &i0, &i1, &step);
   for (int item = i0; item < i1; item += step)
     if (!run(item)) return;
   __syncthreads();
@@ -1105,17 +982,10 @@ int launch_bf16(const FfnLaunch& p, int grid, int n_cons, hipStream_t st, hipEve
   a.n_nt2 = p.d / bn2;
   a.S = ffn_splits(p.dtype, p.d, p.f);
   a.window = p.band_window > 0 ? p.band_window : 4;
-  // Interleave when the return is large next to the FFN and re-streaming weights is cheap.  At about 45 GB/s of
-  // copy per consumer CU and 0.8 PFLOP/s of FFN, copy time / FFN time = 4 M d / (45e9 C) / (6 M d f / 0.8e15)
-  // ~= 11850 / (C f), whatever M and d are; GEMM1 first leaves the last part of the launch for the copies, and
-  // the workgroups that finish early help with what is left, so it is used while that ratio stays under about
-  // 1/4.  Interleaved windows stream an expert's weight tiles once per window holding its rows, and consecutive
-  // items share fewer of them, which pays only while the local experts' weights (3 d f per expert) take at most
-  // half of the 256 MB last-level cache; measured with d = f = 4096: one expert (100 MB) gains 4%, two (201 MB)
-  // lose 3%, four or more lose more.
-  const double w_bytes = 3.0 * p.d * p.f * 2.0 * p.E;
-  a.interleave = n_cons > 0 && (int64_t)n_cons * p.f < 48000 && w_bytes <= 128.0 * 1024 * 1024;
+  // item order: GEMM1 first or interleaved windows (the rule is in item_list.h)
+  a.interleave = ffn_interleave(n_cons, p.d, p.f, p.E);
   a.mtile_desc = p.L->mtile_desc;
+  a.mt_order = p.tile_order == 0 ? p.L->mt_order : nullptr;
   a.scalars = p.L->scalars;
   a.sc_nmt = SC_NR + p.R;
   a.status = p.L->status;
@@ -1142,6 +1012,40 @@ int launch_bf16(const FfnLaunch& p, int grid, int n_cons, hipStream_t st, hipEve
 }  // namespace
 
 int64_t ffn_flag_words(int dtype, int d, int f, int64_t cap_mtiles) { return flag_carve(dtype, d, f, cap_mtiles).total; }
+
+int ffn_schedule_host(int d, int f, int E, int n_cons, int n_producers, int band_window, int n_mt, int n_rem,
+                      const int32_t* mt_hdr, const int32_t* mt_order, int32_t* items, int64_t cap, int64_t* n_out) {
+  const int bn1 = gemm1_bn(MOE_BF16, f), bn2 = ffn_gemm2_bn(MOE_BF16, d);
+  const int n_nt1 = f / (bn1 / 2), n_nt2 = d / bn2, S = ffn_splits(MOE_BF16, d, f);
+  const int W = band_window > 0 ? band_window : 4;
+  const FfnList L = ffn_list_make(n_mt, n_rem, n_nt1, n_nt2, S, W, ffn_interleave(n_cons, d, f, E), n_cons,
+                                  n_producers, bn2 >= 128);
+  *n_out = L.n_list;
+  if (cap < L.n_list) return -1;
+  auto run_of = [&](int mt, int* r0, int* rc) {
+    *r0 = mt_hdr[4 * mt + 2];
+    *rc = mt_hdr[4 * mt + 3];
+  };
+  auto order = [&](int p) { return (int)mt_order[p]; };
+  for (int b = 0; b < n_cons + n_producers; ++b) {
+    int i0, i1, step;
+    ffn_list_range(L, b, &i0, &i1, &step);
+    int seq = 0;
+    for (int idx = i0; idx < i1; idx += step, ++seq) {
+      const FfnItem it = ffn_list_item(L, idx, run_of, order);
+      int32_t* o = items + 8 * (int64_t)idx;
+      o[0] = b;
+      o[1] = seq;
+      o[2] = it.kind;
+      o[3] = it.mt;
+      o[4] = it.nt;
+      o[5] = it.s;
+      o[6] = it.half;
+      o[7] = it.target;
+    }
+  }
+  return 0;
+}
 
 int launch_ffn_producer(const FfnLaunch& p, int grid, int n_cons, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   if (p.dtype == MOE_BF16) return launch_bf16(p, grid, n_cons, st, ev0, ev1);

@@ -30,6 +30,7 @@ struct FfnLaunch {
   uint32_t* flags;
   uint32_t epoch;
   int band_window;
+  int tile_order;  // 0: remote first (the layout's mt_order), 1: row-tile numbering
   uint64_t watchdog_ticks;
   uint64_t* timestamps;
   int64_t cap_mtiles;
@@ -67,6 +68,12 @@ int launch_ffn_producer2(const FfnLaunch& p, int grid, int n_cons, hipStream_t s
 // The consumer alone (`n_cons` workgroups).
 int launch_ffn_consumer(const FfnLaunch& p, int n_cons, hipStream_t st, hipEvent_t ev0 = nullptr,
                         hipEvent_t ev1 = nullptr);
+// The fused bf16 launch's item list on the host (item_list.h), as moe_ffn_schedule reports it: for list index i,
+// items[8 i ..] = {workgroup, its sequence number there, kind, row tile, column tile, split, half, target}.  -1 if
+// cap < the list length (*n_out holds it either way).
+int ffn_schedule_host(int d, int f, int E, int n_cons, int n_producers, int band_window, int n_mt, int n_rem,
+                      const int32_t* mt_hdr, const int32_t* mt_order, int32_t* items, int64_t cap, int64_t* n_out);
+// n_rem and mt_order of a launch: the layout's (remote first), or every tile in number order (tile_order = 1)
 // Resets the n timestamp entries of a call (starts to the largest value, ends to zero).
 int launch_ts_init(uint64_t* timestamps, int64_t n, hipStream_t st);
 int launch_combine(const CombineLaunch& p, hipStream_t st);

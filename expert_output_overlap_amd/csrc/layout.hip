@@ -91,7 +91,7 @@ struct ScanArgs {
   int R, T_o, E, M, mgb, self_rank, n_chunks, mt_rows;
   int64_t cap_rows, cap_tiles, cap_mtiles;
   int32_t *chunk_counts, *counts, *padded_off, *recv_off, *tile_owner, *tile_expert, *tile_valid, *tile_order,
-      *seg_desc, *row_src, *scalars, *status, *mtile_desc, *seg_mtiles, *seg_sched;
+      *seg_desc, *row_src, *scalars, *status, *mtile_desc, *seg_mtiles, *seg_sched, *mt_order;
 };
 
 __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
@@ -203,6 +203,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
       a.scalars[SC_NTILES] = 0;
       a.scalars[SC_NSEGS] = 0;
       a.scalars[SC_NR + R] = 0;
+      a.scalars[SC_NR + R + 1] = 0;
     }
     return;
   }
@@ -326,17 +327,24 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
     const int run = block_excl_scan(start, s_wsum, &n_runs) + start - 1;  // run of q
     if (start) s_first[run] = q;
     __syncthreads();
-    int tiles = 0, rrows = 0;
+    int tiles = 0, rrows = 0, fp = 0;
     if (tid < n_runs) {
       const int q0 = s_first[tid], q1 = tid + 1 < n_runs ? s_first[tid + 1] : n_ne;
       rrows = (q1 < n_ne ? s_row_pos[q1] : s_misc[2]) - s_row_pos[q0];
       tiles = (rrows + a.mt_rows - 1) / a.mt_rows;
+      // the run's self-owned rows come last: its tiles from fp on hold self-owned rows only
+      const int nself = s_n[s_e2[q0] * R + a.self_rank];
+      fp = (rrows - nself + a.mt_rows - 1) / a.mt_rows;
     }
-    int n_mt = 0;
+    int n_mt = 0, n_pure = 0;
     const int tb = block_excl_scan(tiles, s_wsum, &n_mt);
+    const int pre = block_excl_scan(tiles - fp, s_wsum, &n_pure);
     if (tid < n_runs) {
       s_tbase[tid] = tb;
       s_rrows[tid] = rrows;
+      // the producer's order: tiles holding another owner's rows by number, then the self-owned-only tiles
+      for (int t = 0; t < tiles; ++t)
+        a.mt_order[t < fp ? tb - pre + t : n_mt - n_pure + pre + (t - fp)] = tb + t;
     }
     __syncthreads();
     if (in) {
@@ -344,7 +352,10 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_layout_scan(ScanArgs a) {
       s_run_off[q] = s_row_pos[q] - s_row_pos[s_first[run]];
       s_run_rows[q] = s_rrows[run];
     }
-    if (tid == 0) s_misc[3] = n_mt;
+    if (tid == 0) {
+      s_misc[3] = n_mt;
+      a.scalars[SC_NR + R + 1] = n_mt - n_pure;
+    }
     __syncthreads();
   }
   const int n_mtiles = s_misc[3];
@@ -628,6 +639,7 @@ int launch_layout(const LayoutLaunch& p, hipStream_t st) {
   a.mtile_desc = p.L->mtile_desc;
   a.seg_mtiles = p.L->seg_mtiles;
   a.seg_sched = p.L->seg_sched;
+  a.mt_order = p.L->mt_order;
   hipLaunchKernelGGL(k_layout_scan, dim3(1), dim3(SCAN_THREADS), 0, st, a);
   if (n_chunks > 0)
     hipLaunchKernelGGL(k_layout_scatter, dim3((n_chunks + 3) / 4, p.R), dim3(256), 0, st, p.topk_idx, p.R, p.T_o,

@@ -56,8 +56,9 @@ class MoePath:
             "counts": self.E_l * self.R, "padded_off": self.E_l * self.R, "recv_off": self.E_l * self.R,
             "tile_owner": L.cap_tiles, "tile_expert": L.cap_tiles, "tile_valid": L.cap_tiles,
             "tile_order": L.cap_tiles, "seg_desc": L.cap_tiles * B.MOE_SEG_FIELDS, "row_src": L.cap_rows,
-            "combine_plan": self.T * self.k, "scalars": 4 + self.R, "status": 1,
+            "combine_plan": self.T * self.k, "scalars": 5 + self.R, "status": 1,
             "mtile_desc": L.cap_mtiles * B.MT_FIELDS, "seg_mtiles": L.cap_tiles * 2, "seg_sched": L.cap_tiles,
+            "mt_order": L.cap_mtiles,
         }
         off = (getattr(L, name) - self.ws_aligned.data_ptr()) // 4
         return self.ws_aligned.view(torch.int32)[off: off + sizes[name]]
@@ -70,12 +71,12 @@ class MoePath:
         B.moe_layout_build(self.shape, self.topk_idx if topk_idx is None else topk_idx, x, self.L, self.x_pad, stream)
 
     def ffn(self, w_gate_up, w_down, mode=0, consumer_cus=0, band_window=0, timestamps=False, watchdog_ticks=0,
-            epoch=None, stream=None):
+            epoch=None, tile_order=0, stream=None):
         if epoch is None:
             self.epoch += 1
             epoch = self.epoch
         cfg = B.moe_overlap_cfg(consumer_cus, mode, epoch, band_window, watchdog_ticks,
-                                self.timestamps.data_ptr() if timestamps else None)
+                                self.timestamps.data_ptr() if timestamps else None, tile_order)
         B.moe_expert_ffn_overlap(self.shape, self.L, self.x_pad, w_gate_up, w_down, self.h, self.y_pad, self.recv,
                                  self.flags, cfg, stream)
         return epoch
@@ -88,7 +89,8 @@ class MoePath:
 
     def scalars(self):
         sc = self.array("scalars").cpu().tolist()
-        return {"M_pad": sc[0], "n_tiles": sc[1], "n_segs": sc[2], "N_r": sc[3:3 + self.R], "n_mtiles": sc[3 + self.R]}
+        return {"M_pad": sc[0], "n_tiles": sc[1], "n_segs": sc[2], "N_r": sc[3:3 + self.R], "n_mtiles": sc[3 + self.R],
+                "n_remote_mtiles": sc[4 + self.R]}
 
 
 def to_device(a, dtype: str, device="cuda") -> torch.Tensor:

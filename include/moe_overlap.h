@@ -75,7 +75,8 @@ typedef struct {
   int32_t* row_src;      /* [cap_rows] token row of each padded row, -1 for padding */
   int32_t* combine_plan; /* [T*k] receive-buffer row of token slot (t, j) in its owner's buffer, -1 if the
                             expert is not local */
-  int32_t* scalars;      /* [4+R] M_pad, n_tiles, n_segs, N_r[0..R), n_mtiles */
+  int32_t* scalars;      /* [5+R] M_pad, n_tiles, n_segs, N_r[0..R), n_mtiles, then the number of row tiles
+                            that hold a row of another owner (they come first in mt_order) */
   int32_t* status;       /* [1] device status word (moe_status) */
   int32_t* mtile_desc;   /* [cap_mtiles][264] GEMM row tiles: {expert, n_rows, run_first, run_count,
                             self_lo, self_n, self_delta, 0, row[256]} (self_*: the expert's self-owned
@@ -87,6 +88,9 @@ typedef struct {
   int32_t* seg_mtiles;   /* [cap_tiles][2] first GEMM row tile and count a segment depends on (internal) */
   int32_t* seg_sched;    /* [cap_tiles] segments in the order their row tiles complete (internal) */
   int32_t* chunk_counts; /* [R][ceil(T_o/64)][E_l] per-64-token histogram, then its prefix (internal) */
+  int32_t* mt_order;     /* [cap_mtiles] the producer's row-tile order (remote first): every GEMM row tile that holds
+                            a row of another owner, by number, then every row tile of self-owned rows only, by
+                            number (internal schedule) */
   int64_t cap_rows;      /* capacity in padded rows (x_pad, h, y_pad, row_src) */
   int64_t cap_tiles;     /* cap_rows / M */
   int64_t cap_mtiles;    /* capacity of mtile_desc */
@@ -116,6 +120,10 @@ typedef struct {
                               item start, [1] last flag publish, [2+2s] / [3+2s] first copy start / last copy
                               end of segment s over the workgroups that copy it (a self-owned segment,
                               never copied, keeps ~0 / 0); reset by the call; NULL to skip */
+  int32_t tile_order;      /* the producer's row-tile order (bf16): 0 = remote first (moe_layout.mt_order: every row
+                              tile holding another owner's row before every row tile of self-owned rows only; the
+                              review page's "Core claim"), 1 = row-tile numbering (each expert's rows together,
+                              its self-owned rows last) */
 } moe_overlap_cfg;
 
 /* Last host-side error message of the calling thread ("" if none). */
@@ -202,6 +210,21 @@ int32_t moe_pick_consumer_cus(const moe_shape* s, int32_t n_cu);
 int moe_expert_ffn_overlap(const moe_shape* s, const moe_layout* L, const void* x_pad, const void* w_gate_up,
                            const void* w_down, void* h_ws, void* y_pad, void* const* recv, uint32_t* flags,
                            const moe_overlap_cfg* cfg, void* stream);
+
+/* The work-item list of the bf16 FFN launch (host only, no device call; for inspection and tests): which
+ * workgroup runs which item, in what order, for a launch on n_cu CUs with cfg's mode, consumer_cus, band_window and
+ * tile_order (the library's pick when consumer_cus is 0).  The review page ("Core claim", "What carries the argument")
+ * describes one persistent GEMM over all local experts whose remote-bound tiles are scheduled first; the list is
+ * the kernel's own (a header both compile).  Inputs are the layout's row tiles as the device built them:
+ * mt_hdr [n_mtiles][4] = the first four fields of each mtile_desc entry {expert, rows, run_first, run_count},
+ * mt_order [n_mtiles] = moe_layout.mt_order, n_remote_mtiles = the layout scalar after n_mtiles.  Output: items [n][8] int32, list index i = {workgroup, sequence
+ * number in that workgroup, kind (1 = GEMM1 tile, 2 = GEMM2 k-split), row tile, column tile, split, half (-1 or
+ * 0/1 for a half-width item), target (GEMM2: items that complete the y tile)}.  *n_items receives the list length;
+ * items == NULL with cap == 0 only queries it.  MOE_EINVAL for fp32 (two plain launches, no list), an invalid
+ * shape or configuration, row-tile headers out of range, or cap below the length. */
+int moe_ffn_schedule(const moe_shape* s, int32_t n_cu, const moe_overlap_cfg* cfg, int32_t n_mtiles,
+                     int32_t n_remote_mtiles, const int32_t* mt_hdr, const int32_t* mt_order, int32_t* items,
+                     int64_t cap, int64_t* n_items);
 
 /* ---- combine ------------------------------------------------------------------------------------- */
 

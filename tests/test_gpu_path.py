@@ -13,6 +13,7 @@ import torch
 
 import moe_inputs as mi
 import oracle
+import schedule_model
 import tolerance
 from expert_output_overlap_amd import binding as B
 from expert_output_overlap_amd.runtime import MoePath, to_device
@@ -140,6 +141,23 @@ def check_schedule(run):
     for sd, (m0, mc) in zip(lay["seg_desc"], segm):
         rows = np.arange(sd[4], sd[4] + sd[6])
         assert ((tile_of_row[rows] >= m0) & (tile_of_row[rows] < m0 + mc)).all()
+    if s.dtype != "bf16":
+        return
+    # the row-tile model of the CPU schedule tests is the device's packing, and the device's producer order is its
+    # remote-first order; the list the launch runs over these tables passes the CPU checks
+    hdr_m, rows_m, pure_m, order_m = schedule_model.packing(lay["counts"], lay["padded_off"], s.R, s.E_l, run.sr, s.M)
+    np.testing.assert_array_equal(desc[:, :4], hdr_m)
+    for mt in range(n_mt):
+        np.testing.assert_array_equal(desc[mt, B.MT_HDR:B.MT_HDR + desc[mt, 1]], rows_m[mt])
+    order = P.array("mt_order")[:n_mt].cpu().numpy()
+    np.testing.assert_array_equal(order, order_m)
+    n_rem = P.scalars()["n_remote_mtiles"]
+    assert n_rem == int((~pure_m).sum())
+    for mode in (0, 1):
+        cfg = B.moe_overlap_cfg(0, mode, 1, 0, 0, None)
+        items = B.moe_ffn_schedule(P.shape, torch.cuda.get_device_properties(0).multi_processor_count, cfg,
+                                   desc[:, :4], order, n_rem)
+        schedule_model.check_list(items, n_mt, s.d, s.f, pure_m)
 
 
 def check_delivery(run):
@@ -211,15 +229,17 @@ def test_small_full_parity(s, self_rank):
     torch.cuda.synchronize()
     out_ref = oracle.combine(lay, run.w, recv_ref, s.R, s.T_o, s.k, s.dtype == "bf16")
     tolerance.check(f64(P.out[: s.T]), out_ref, "out")
-    # sequential mode gives the same bits
+    # sequential mode, and the producer's other row-tile order, give the same bits
     recv_ovl = [bits(b) for b in P.recv]
     out_ovl = bits(P.out)
-    run.ffn(mode=1, consumer_cus=4)
-    P.combine()
-    torch.cuda.synchronize()
-    for r in range(s.R):
-        np.testing.assert_array_equal(bits(P.recv[r]), recv_ovl[r])
-    np.testing.assert_array_equal(bits(P.out), out_ovl)
+    for kw in (dict(mode=1), dict(mode=0, tile_order=1)):
+        run.ffn(consumer_cus=4, **kw)
+        P.combine()
+        torch.cuda.synchronize()
+        assert P.status() == B.MOE_OK
+        for r in range(s.R):
+            np.testing.assert_array_equal(bits(P.recv[r]), recv_ovl[r], err_msg=str(kw))
+        np.testing.assert_array_equal(bits(P.out), out_ovl, err_msg=str(kw))
 
 
 FULL = ["mixtral", "skew", "sweep1", "sweep2", "sweep4", "sweep8", "sweep16", "deepseek"]
