@@ -21,7 +21,7 @@ MT_HDR = 8
 MT_FIELDS = MT_HDR + 256
 EXPORTS = ["moe_last_error", "moe_version", "moe_route", "moe_layout_capacity_rows", "moe_layout_workspace_bytes",
            "moe_layout_bind", "moe_layout_build", "moe_read_status", "moe_ffn_flags_count", "moe_pick_consumer_cus",
-           "moe_expert_ffn_overlap", "moe_ffn_schedule",
+           "moe_expert_ffn_overlap", "moe_expert_ffn_overlap_noalloc", "moe_ffn_schedule",
            "moe_combine", "moe_set_kernel_timing", "moe_kernel_times"]
 
 
@@ -73,6 +73,7 @@ def lib():
             "moe_read_status": ([pl, vp], i32), "moe_ffn_flags_count": ([ps], i64),
             "moe_pick_consumer_cus": ([ps, i32], i32),
             "moe_expert_ffn_overlap": ([ps, pl, vp, vp, vp, vp, vp, vp, vp, pc, vp], i32),
+            "moe_expert_ffn_overlap_noalloc": ([ps, pl, vp, vp, vp, vp, vp, vp, pc, vp], i32),
             "moe_combine": ([ps, pl, vp, vp, vp, vp], i32),
             "moe_ffn_schedule": ([ps, i32, pc, i32, i32, vp, vp, vp, i64, ctypes.POINTER(ctypes.c_int64)], i32),
             "moe_set_kernel_timing": ([i32], i32), "moe_kernel_times": ([ctypes.POINTER(ctypes.c_double)], i32),
@@ -159,6 +160,13 @@ def moe_expert_ffn_overlap(shape: moe_shape, layout: moe_layout, x_pad, w_gate_u
     return _check("moe_expert_ffn_overlap", lib().moe_expert_ffn_overlap(
         ctypes.byref(shape), ctypes.byref(layout), _ptr(x_pad), _ptr(w_gate_up), _ptr(w_down), _ptr(h_ws),
         _ptr(y_pad), _ptr_array(recv), _ptr(flags), ctypes.byref(cfg), _stream(stream)))
+
+
+def moe_expert_ffn_overlap_noalloc(shape: moe_shape, layout: moe_layout, x_pad, w_gate_up, w_down, h_ws, y_pad, recv,
+                                   cfg: moe_overlap_cfg, stream=None) -> int:
+    return _check("moe_expert_ffn_overlap_noalloc", lib().moe_expert_ffn_overlap_noalloc(
+        ctypes.byref(shape), ctypes.byref(layout), _ptr(x_pad), _ptr(w_gate_up), _ptr(w_down), _ptr(h_ws),
+        _ptr(y_pad), _ptr_array(recv), ctypes.byref(cfg), _stream(stream)))
 
 
 def moe_ffn_schedule(shape: moe_shape, n_cu: int, cfg: moe_overlap_cfg, mt_hdr, mt_order, n_remote: int):

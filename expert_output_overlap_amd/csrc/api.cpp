@@ -292,18 +292,24 @@ int32_t moe_pick_consumer_cus(const moe_shape* s, int32_t n_cu) {
   return std::min(c, cap);
 }
 
-int moe_expert_ffn_overlap(const moe_shape* s, const moe_layout* L, const void* x_pad, const void* w_gate_up,
-                           const void* w_down, void* h_ws, void* y_pad, void* const* recv, uint32_t* flags,
-                           const moe_overlap_cfg* cfg, void* stream) {
+}  // extern "C"
+
+namespace {
+// The body of moe_expert_ffn_overlap; flags == nullptr selects the allocation-free variant's own flag buffer.
+int ffn_overlap(const moe_shape* s, const moe_layout* L, const void* x_pad, const void* w_gate_up, const void* w_down,
+                void* h_ws, void* y_pad, void* const* recv, uint32_t* flags, const moe_overlap_cfg* cfg_in,
+                void* stream) {
   const std::string e = check_shape(s);
   if (!e.empty()) return fail(MOE_EINVAL, e);
-  if (!layout_ok(L) || !cfg) return fail(MOE_EINVAL, "null layout or cfg");
-  if (!x_pad || !w_gate_up || !w_down || !h_ws || !y_pad || !recv || !flags)
+  if (!layout_ok(L) || !cfg_in) return fail(MOE_EINVAL, "null layout or cfg");
+  if (!x_pad || !w_gate_up || !w_down || !h_ws || !y_pad || !recv)
     return fail(MOE_EINVAL, "null pointer");
+  moe_overlap_cfg cfg_v = *cfg_in;
+  const moe_overlap_cfg* cfg = &cfg_v;
   for (int r = 0; r < s->R; ++r)
     if (!recv[r]) return fail(MOE_EINVAL, "null receive buffer");
   if ((uintptr_t)flags % 8 != 0) return fail(MOE_EINVAL, "flags must be 8-byte aligned");
-  if (cfg->epoch == 0) return fail(MOE_EINVAL, "epoch must be nonzero");
+  if (cfg->epoch == 0 && flags != nullptr) return fail(MOE_EINVAL, "epoch must be nonzero");
   if (cfg->mode < 0 || cfg->mode > 2) return fail(MOE_EINVAL, "mode must be 0, 1 or 2");
   if (cfg->band_window < 0) return fail(MOE_EINVAL, "band_window must be >= 0");
   if (cfg->tile_order != 0 && cfg->tile_order != 1) return fail(MOE_EINVAL, "tile_order must be 0 or 1");
@@ -316,6 +322,19 @@ int moe_expert_ffn_overlap(const moe_shape* s, const moe_layout* L, const void* 
     return fail(MOE_EINVAL, "consumer_cus must be 0 (library pick) or in [1, CUs/2]");
   const int C = cfg->consumer_cus ? cfg->consumer_cus : moe_pick_consumer_cus(s, n_cu);
   if (C < 1) return fail(MOE_EINVAL, "no consumer partition fits this device");
+  if (flags == nullptr) {  // the allocation-free variant: flags in the library's scratch array, cleared per call
+    if (cfg->mode == 2) return fail(MOE_EINVAL, "mode 2 (return only) needs the flags of an earlier call");
+    const int64_t words = ffn_flag_words(s->dtype, s->d, s->f, layout_offsets(s).cap_mtiles);
+    if (words > ffn_noalloc_scratch_words())
+      return fail(MOE_EINVAL, "this shape's flag buffer needs " + std::to_string(words * 4) +
+                                  " bytes, over the allocation-free variant's " +
+                                  std::to_string(ffn_noalloc_scratch_words() * 4) + "-byte maximum");
+    flags = ffn_noalloc_scratch(dev);
+    if (flags == nullptr) return fail(MOE_EHIP, "hipGetSymbolAddress of the scratch array failed");
+    if (launch_flags_clear(s->dtype, s->d, s->f, layout_offsets(s).cap_mtiles, flags, (hipStream_t)stream))
+      return fail(MOE_EHIP, "flag clear launch failed");
+    cfg_v.epoch = 1;  // the flags were just cleared
+  }
 
   FfnLaunch p;
   p.dtype = s->dtype;
@@ -381,6 +400,22 @@ int moe_expert_ffn_overlap(const moe_shape* s, const moe_layout* L, const void* 
     g_events.push_back(ce);
   }
   return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int moe_expert_ffn_overlap(const moe_shape* s, const moe_layout* L, const void* x_pad, const void* w_gate_up,
+                           const void* w_down, void* h_ws, void* y_pad, void* const* recv, uint32_t* flags,
+                           const moe_overlap_cfg* cfg, void* stream) {
+  if (!flags) return fail(MOE_EINVAL, "null pointer");
+  return ffn_overlap(s, L, x_pad, w_gate_up, w_down, h_ws, y_pad, recv, flags, cfg, stream);
+}
+
+int moe_expert_ffn_overlap_noalloc(const moe_shape* s, const moe_layout* L, const void* x_pad, const void* w_gate_up,
+                                   const void* w_down, void* h_ws, void* y_pad, void* const* recv,
+                                   const moe_overlap_cfg* cfg, void* stream) {
+  return ffn_overlap(s, L, x_pad, w_gate_up, w_down, h_ws, y_pad, recv, nullptr, cfg, stream);
 }
 
 int moe_ffn_schedule(const moe_shape* s, int32_t n_cu, const moe_overlap_cfg* cfg, int32_t n_mtiles,

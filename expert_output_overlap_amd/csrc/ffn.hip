@@ -17,8 +17,11 @@
 // stores drain under that item's first loads.
 #include <hip/hip_ext.h>
 
+#include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <type_traits>
+#include <vector>
 
 #include "common.h"
 #include "consumer.h"
@@ -1086,6 +1089,48 @@ int launch_ffn_consumer(const FfnLaunch& p, int n_cons, hipStream_t st, hipEvent
   ConsumerArgs c;
   fill_consumer(c, p, p.d / ffn_gemm2_bn(p.dtype, p.d));
   hipExtLaunchKernelGGL(k_consumer, dim3(n_cons), dim3(256), 0, st, ev0, ev1, 0, c);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// ---- the allocation-free variant's flag buffer --------------------------------------------------------------
+// moe_expert_ffn_overlap_noalloc keeps the FFN launch's flag buffer (tile flags, split arrival counters, split-K
+// partial sums, the copy-unit counter) in this file-scope array instead of a caller's workspace.  Every device the
+// library runs on holds its own copy until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: only the address hipGetSymbolAddress returns, taken once per device with that device current,
+// is ever passed to a kernel or a copy.
+#define MOE_NOALLOC_SCRATCH_BYTES (64ll << 20)
+static __device__ __align__(256) uint32_t scratch[MOE_NOALLOC_SCRATCH_BYTES / 4];
+
+namespace {
+std::mutex g_scratch_mu;
+std::vector<uint32_t*> g_scratch_ptr;  // per device: the device address of `scratch`, null until looked up
+}  // namespace
+
+int64_t ffn_noalloc_scratch_words() { return MOE_NOALLOC_SCRATCH_BYTES / 4; }
+
+uint32_t* ffn_noalloc_scratch(int dev) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (dev < 0) return nullptr;
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    g_scratch_ptr[dev] = (uint32_t*)p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+__global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+int launch_flags_clear(int dtype, int d, int f, int64_t cap_mtiles, uint32_t* flags, hipStream_t st) {
+  // everything that is read before this call writes it: tile flags, arrival counters, the copy-unit counter (the
+  // split-K partial sums are always written before they are read)
+  const FlagCarve c = flag_carve(dtype, d, f, cap_mtiles);
+  const int64_t blocks = std::min<int64_t>((c.partial + 255) / 256, 1024);
+  if (c.partial > 0) hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(256), 0, st, flags, c.partial);
+  hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(64), 0, st, flags + c.claim, (int64_t)2);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

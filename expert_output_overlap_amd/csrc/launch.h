@@ -74,6 +74,12 @@ int launch_ffn_consumer(const FfnLaunch& p, int n_cons, hipStream_t st, hipEvent
 int ffn_schedule_host(int d, int f, int E, int n_cons, int n_producers, int band_window, int n_mt, int n_rem,
                       const int32_t* mt_hdr, const int32_t* mt_order, int32_t* items, int64_t cap, int64_t* n_out);
 // n_rem and mt_order of a launch: the layout's (remote first), or every tile in number order (tile_order = 1)
+// The allocation-free variant's flag buffer: its size in 4-byte words, and its device address on device `dev` (the
+// current device; looked up once per device), null if the lookup fails.
+int64_t ffn_noalloc_scratch_words();
+uint32_t* ffn_noalloc_scratch(int dev);
+// Zeroes the words of a flag buffer that a call reads before writing (flags, counters), on stream st.
+int launch_flags_clear(int dtype, int d, int f, int64_t cap_mtiles, uint32_t* flags, hipStream_t st);
 // Resets the n timestamp entries of a call (starts to the largest value, ends to zero).
 int launch_ts_init(uint64_t* timestamps, int64_t n, hipStream_t st);
 int launch_combine(const CombineLaunch& p, hipStream_t st);

@@ -211,6 +211,22 @@ int moe_expert_ffn_overlap(const moe_shape* s, const moe_layout* L, const void* 
                            const void* w_down, void* h_ws, void* y_pad, void* const* recv, uint32_t* flags,
                            const moe_overlap_cfg* cfg, void* stream);
 
+/* For callers that cannot allocate device memory or pass a workspace of their own (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): moe_expert_ffn_overlap without the `flags`
+ * workspace.  The flag buffer (tile flags, split arrival counters, split-K partial sums, the copy-unit counter)
+ * lives in a file-scope device array of the library, at most 64 MiB, which every device the library runs on
+ * holds until the process ends; the call allocates nothing and calls no allocating routine.  Each call first
+ * clears the flags and counters of that array with a fill kernel on `stream` and then runs with epoch 1
+ * (cfg->epoch is ignored), so calls need no epoch sequence of their own.  All calls on one device share the
+ * array: calls that overlap on one device (different streams, or host threads) race and give wrong results;
+ * order them.  Inputs, outputs and the other workspaces (h_ws, y_pad) are the caller's, as for
+ * moe_expert_ffn_overlap, whose arguments and results this call has.  MOE_EINVAL when the shape's flag buffer
+ * (moe_ffn_flags_count words) exceeds the 64 MiB maximum, or for mode 2 (it needs an earlier call's flags);
+ * MOE_EHIP if the array's device address cannot be obtained. */
+int moe_expert_ffn_overlap_noalloc(const moe_shape* s, const moe_layout* L, const void* x_pad, const void* w_gate_up,
+                                   const void* w_down, void* h_ws, void* y_pad, void* const* recv,
+                                   const moe_overlap_cfg* cfg, void* stream);
+
 /* The work-item list of the bf16 FFN launch (host only, no device call; for inspection and tests): which
  * workgroup runs which item, in what order, for a launch on n_cu CUs with cfg's mode, consumer_cus, band_window and
  * tile_order (the library's pick when consumer_cus is 0).  The review page ("Core claim", "What carries the argument")
