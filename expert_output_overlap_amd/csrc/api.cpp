@@ -10,6 +10,7 @@
 
 #include "../../include/moe_overlap.h"
 #include "common.h"
+#include "item_list.h"
 #include "launch.h"
 
 namespace {
@@ -295,6 +296,131 @@ int32_t moe_pick_consumer_cus(const moe_shape* s, int32_t n_cu) {
 }  // extern "C"
 
 namespace {
+// Mode 3: the return on the DMA engines (review page of FiCCO, "If this is right": DMA-offloaded transfers contend
+// less with the GEMMs than copies on the compute units).  The FFN's item list runs as a few launches, cut at GEMM2
+// window boundaries (a y tile's k-splits never straddle two launches); after each launch an event gates the copy
+// streams that move the segments the launch completed with hipMemcpyDeviceToDeviceNoCU copies (DMA engines, no
+// CUs) while the next launch computes.  One DMA engine copies HBM to HBM at ~50 GB/s (measured), so the copies
+// are spread over DMA_STREAMS streams, each to the one with the fewest bytes queued.  The host needs the segment table for the copies: it reads it back after
+// synchronising the caller's stream (the layout build), once per call.
+#define DMA_STREAMS 3  // copy streams: with the caller's stream, the four hardware queues of a process
+struct DmaCtx {
+  hipStream_t copy[DMA_STREAMS] = {};
+  hipEvent_t ev[4] = {};            // end of each launch chunk, on the caller's stream
+  hipEvent_t done[DMA_STREAMS] = {};  // end of each copy stream's work
+};
+std::vector<DmaCtx> g_dma;  // per device, guarded by g_mu
+
+int ffn_dma(const moe_shape* s, const moe_layout* L, FfnLaunch& p, int n_cu, int dev, hipStream_t st, CallEvents* ce,
+            bool timed) {
+  DmaCtx* ctx;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if ((int)g_dma.size() <= dev) g_dma.resize(dev + 1);
+    ctx = &g_dma[dev];
+    if (ctx->copy[DMA_STREAMS - 1] == nullptr) {
+      for (auto& c : ctx->copy)
+        if (c == nullptr && hipStreamCreateWithFlags(&c, hipStreamNonBlocking) != hipSuccess) {
+          c = nullptr;
+          return fail(MOE_EHIP, "copy stream creation failed");
+        }
+      for (auto& e : ctx->ev)
+        if (e == nullptr && hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+          e = nullptr;
+          return fail(MOE_EHIP, "event creation failed");
+        }
+      for (auto& e : ctx->done)
+        if (e == nullptr && hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+          e = nullptr;
+          return fail(MOE_EHIP, "event creation failed");
+        }
+    }
+  }
+  // the segment table and the producer's row-tile order, on the host
+  const int R = s->R;
+  if (hipStreamSynchronize(st) != hipSuccess) return fail(MOE_EHIP, "stream sync failed");
+  std::vector<int32_t> sc(5 + R);
+  int32_t status = 0;
+  if (hipMemcpy(&status, L->status, 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(sc.data(), L->scalars, sc.size() * 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(MOE_EHIP, "layout readback failed");
+  if (status != MOE_OK) return MOE_OK;  // the device status already reports the failure; nothing runs after it
+  const int n_segs = sc[SC_NSEGS], n_mt = sc[SC_NR + R], n_rem = sc[SC_NR + R + 1];
+  if (n_mt == 0) return MOE_OK;
+  std::vector<int32_t> seg(8 * (size_t)n_segs), segm(2 * (size_t)n_segs), order(n_mt);
+  if ((n_segs > 0 && (hipMemcpy(seg.data(), L->seg_desc, seg.size() * 4, hipMemcpyDeviceToHost) != hipSuccess ||
+                      hipMemcpy(segm.data(), L->seg_mtiles, segm.size() * 4, hipMemcpyDeviceToHost) != hipSuccess)) ||
+      hipMemcpy(order.data(), L->mt_order, order.size() * 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(MOE_EHIP, "layout readback failed");
+  // the list (GEMM1 first, no half-width round, no consumer workgroups) and its chunks: windows of the GEMM2 part
+  int n1, n2, S;
+  ffn_list_dims(s->d, s->f, &n1, &n2, &S);
+  const int W = p.band_window > 0 ? p.band_window : 4;
+  const FfnList Lst = ffn_list_make(n_mt, p.tile_order == 0 ? n_rem : n_mt, n1, n2, S, W, 0, 0, n_cu, false);
+  const int64_t g1 = (int64_t)n_mt * n1;
+  const int nw = (n_mt + W - 1) / W, K = std::min(4, nw);
+  auto wstart = [&](int w) { return g1 + (int64_t)std::min(w * W, n_mt) * n2 * S; };
+  std::vector<int64_t> cb(K + 1);
+  cb[0] = 0;
+  for (int c = 1; c <= K; ++c) cb[c] = wstart((int)((int64_t)c * nw / K));
+  // the chunk that completes each row tile (its last second-GEMM item), then each segment
+  std::vector<int> done(n_mt, 0);
+  for (int c = 0; c < K; ++c)
+    for (int64_t i = std::max(cb[c], g1); i < cb[c + 1]; ++i) {
+      const FfnSlot sl = ffn_slot((int)i, Lst);
+      const int mt = p.tile_order == 0 ? order[sl.pos] : sl.pos;
+      done[mt] = std::max(done[mt], c);
+    }
+  const int64_t row_bytes = (int64_t)s->d * 2;
+  const char* y = (const char*)p.y_pad;
+  int64_t queued[DMA_STREAMS] = {};  // bytes given to each copy stream: each copy goes to the least loaded
+  for (int c = 0; c < K; ++c) {
+    p.item_begin = (int)cb[c];
+    p.item_end = (int)cb[c + 1];
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (timed && c == 0) e0 = ce->e[0];
+    if (timed && c == K - 1) e1 = ce->e[1];
+    if (launch_ffn_producer(p, n_cu, 0, st, e0, e1)) return fail(MOE_EHIP, "producer launch failed");
+    if (hipEventRecord(ctx->ev[c], st) != hipSuccess) return fail(MOE_EHIP, "event failed");
+    for (auto cs : ctx->copy)
+      if (hipStreamWaitEvent(cs, ctx->ev[c], 0) != hipSuccess) return fail(MOE_EHIP, "event failed");
+    // the segments this chunk completed, other owners only, contiguous runs of one owner merged into one copy
+    std::vector<int> mine;
+    for (int i = 0; i < n_segs; ++i) {
+      const int32_t* sd = &seg[8 * (size_t)i];
+      if (sd[SEG_OWNER] == s->self_rank || sd[SEG_ROWS] == 0) continue;
+      int c_seg = 0;
+      for (int m = segm[2 * i]; m < segm[2 * i] + segm[2 * i + 1]; ++m) c_seg = std::max(c_seg, done[m]);
+      if (c_seg == c) mine.push_back(i);
+    }
+    std::sort(mine.begin(), mine.end(), [&](int a, int b) {
+      const int32_t *x = &seg[8 * (size_t)a], *z = &seg[8 * (size_t)b];
+      return x[SEG_OWNER] != z[SEG_OWNER] ? x[SEG_OWNER] < z[SEG_OWNER] : x[SEG_DST_ROW] < z[SEG_DST_ROW];
+    });
+    for (size_t k = 0; k < mine.size();) {
+      const int32_t* sd = &seg[8 * (size_t)mine[k]];
+      const int owner = sd[SEG_OWNER];
+      int64_t src = sd[SEG_SRC_ROW], dst = sd[SEG_DST_ROW], rows = sd[SEG_ROWS];
+      size_t j = k + 1;
+      for (; j < mine.size(); ++j) {
+        const int32_t* nx = &seg[8 * (size_t)mine[j]];
+        if (nx[SEG_OWNER] != owner || nx[SEG_SRC_ROW] != src + rows || nx[SEG_DST_ROW] != dst + rows) break;
+        rows += nx[SEG_ROWS];
+      }
+      const int q = (int)(std::min_element(queued, queued + DMA_STREAMS) - queued);
+      queued[q] += rows * row_bytes;
+      if (hipMemcpyAsync((char*)p.recv[owner] + dst * row_bytes, y + src * row_bytes, rows * row_bytes,
+                         hipMemcpyDeviceToDeviceNoCU, ctx->copy[q]) != hipSuccess)
+        return fail(MOE_EHIP, "DMA copy failed");
+      k = j;
+    }
+  }
+  for (int q = 0; q < DMA_STREAMS; ++q)
+    if (hipEventRecord(ctx->done[q], ctx->copy[q]) != hipSuccess || hipStreamWaitEvent(st, ctx->done[q], 0) != hipSuccess)
+      return fail(MOE_EHIP, "event failed");
+  return MOE_OK;
+}
+
 // The body of moe_expert_ffn_overlap; flags == nullptr selects the allocation-free variant's own flag buffer.
 int ffn_overlap(const moe_shape* s, const moe_layout* L, const void* x_pad, const void* w_gate_up, const void* w_down,
                 void* h_ws, void* y_pad, void* const* recv, uint32_t* flags, const moe_overlap_cfg* cfg_in,
@@ -310,7 +436,9 @@ int ffn_overlap(const moe_shape* s, const moe_layout* L, const void* x_pad, cons
     if (!recv[r]) return fail(MOE_EINVAL, "null receive buffer");
   if ((uintptr_t)flags % 8 != 0) return fail(MOE_EINVAL, "flags must be 8-byte aligned");
   if (cfg->epoch == 0 && flags != nullptr) return fail(MOE_EINVAL, "epoch must be nonzero");
-  if (cfg->mode < 0 || cfg->mode > 2) return fail(MOE_EINVAL, "mode must be 0, 1 or 2");
+  if (cfg->mode < 0 || cfg->mode > 3) return fail(MOE_EINVAL, "mode must be 0, 1, 2 or 3");
+  if (cfg->mode == 3 && (s->dtype != MOE_BF16 || flags == nullptr))
+    return fail(MOE_EINVAL, "mode 3 (return on the DMA engines) is for bf16 with a flag workspace");
   if (cfg->band_window < 0) return fail(MOE_EINVAL, "band_window must be >= 0");
   if (cfg->tile_order != 0 && cfg->tile_order != 1) return fail(MOE_EINVAL, "tile_order must be 0 or 1");
   hipStream_t st = (hipStream_t)stream;
@@ -361,6 +489,25 @@ int ffn_overlap(const moe_shape* s, const moe_layout* L, const void* x_pad, cons
   if (cfg->mode == 2) {  // return only
     if (launch_ffn_consumer(p, C, st)) return fail(MOE_EHIP, "consumer launch failed");
     return MOE_OK;
+  }
+  if (cfg->mode == 3) {
+    CallEvents ce3;
+    const bool timed3 = g_timing && timing_begin(&ce3) == 0;
+    if (timed3) ce3.n = 1;
+    if (cfg->timestamps && launch_ts_init(cfg->timestamps, 2 + 2 * layout_offsets(s).cap_tiles, st)) {
+      if (timed3) ce3.destroy();
+      return fail(MOE_EHIP, "launch failed");
+    }
+    const int rc = ffn_dma(s, L, p, n_cu, dev, st, &ce3, timed3);
+    if (timed3) {
+      if (rc != MOE_OK) {
+        ce3.destroy();
+      } else {
+        std::lock_guard<std::mutex> lk(g_mu);
+        g_events.push_back(ce3);
+      }
+    }
+    return rc;
   }
   CallEvents ce;
   const bool timed = g_timing && timing_begin(&ce) == 0;

@@ -344,6 +344,8 @@ struct FusedArgs {
   int d, f;
   int n_nt1, n_nt2, S, window;
   int interleave;  // item order: 0 = GEMM1 first, 1 = interleaved windows
+  int halves;      // the half-width final round is allowed
+  int item_begin, item_end;  // this launch runs the list indices in [item_begin, item_end) (one chunk of the list)
   const int32_t* mtile_desc;
   const int32_t* mt_order;  // [n_mt] row tile at each position of the list (remote-bound row tiles first), or
                             // null: row-tile numbering
@@ -819,7 +821,7 @@ __global__ __launch_bounds__(FFN_THREADS, 1) void k_ffn_bf16(FusedArgs a) {
   // the item list (item_list.h): the consumers' share of GEMM1 items, the producers' round-robin share, and the
   // half-width items of a last round at most half full
   const FfnList L = ffn_list_make(n_mt, a.mt_order ? a.scalars[a.sc_nmt + 1] : n_mt, a.n_nt1, a.n_nt2, a.S, a.window,
-                                  a.interleave, C, G, BN2 >= 128);
+                                  a.interleave, C, G, BN2 >= 128 && a.halves);
   auto run_of = [&](int mt, int* r0, int* rc) {
     const int32_t* d = a.mtile_desc + (int64_t)mt * MOE_MT_FIELDS;
     *r0 = d[2];
@@ -860,6 +862,8 @@ __global__ __launch_bounds__(FFN_THREADS, 1) void k_ffn_bf16(FusedArgs a) {
   // locality, and the clock drops with the extra off-XCD traffic: measured slower.)
   int i0, i1, step;
   ffn_list_range(L, (int)blockIdx.x, &i0, &i1, &step);
+  if (a.item_begin > i0) i0 += (a.item_begin - i0 + step - 1) / step * step;  // this launch's chunk of the list
+  i1 = min(i1, a.item_end);
   for (int item = i0; item < i1; item += step)
     if (!run(item)) return;
   __syncthreads();
@@ -986,7 +990,10 @@ int launch_bf16(const FfnLaunch& p, int grid, int n_cons, hipStream_t st, hipEve
   a.S = ffn_splits(p.dtype, p.d, p.f);
   a.window = p.band_window > 0 ? p.band_window : 4;
   // item order: GEMM1 first or interleaved windows (the rule is in item_list.h)
-  a.interleave = ffn_interleave(n_cons, p.d, p.f, p.E);
+  a.interleave = p.item_end >= 0 ? 0 : ffn_interleave(n_cons, p.d, p.f, p.E);  // chunks: GEMM1 first
+  a.halves = p.item_end >= 0 ? 0 : 1;  // a chunked list has no single last round
+  a.item_begin = p.item_end >= 0 ? p.item_begin : 0;
+  a.item_end = p.item_end >= 0 ? p.item_end : INT32_MAX;
   a.mtile_desc = p.L->mtile_desc;
   a.mt_order = p.tile_order == 0 ? p.L->mt_order : nullptr;
   a.scalars = p.L->scalars;
@@ -1015,6 +1022,12 @@ int launch_bf16(const FfnLaunch& p, int grid, int n_cons, hipStream_t st, hipEve
 }  // namespace
 
 int64_t ffn_flag_words(int dtype, int d, int f, int64_t cap_mtiles) { return flag_carve(dtype, d, f, cap_mtiles).total; }
+
+void ffn_list_dims(int d, int f, int* n_nt1, int* n_nt2, int* S) {
+  *n_nt1 = f / (gemm1_bn(MOE_BF16, f) / 2);
+  *n_nt2 = d / ffn_gemm2_bn(MOE_BF16, d);
+  *S = ffn_splits(MOE_BF16, d, f);
+}
 
 int ffn_schedule_host(int d, int f, int E, int n_cons, int n_producers, int band_window, int n_mt, int n_rem,
                       const int32_t* mt_hdr, const int32_t* mt_order, int32_t* items, int64_t cap, int64_t* n_out) {

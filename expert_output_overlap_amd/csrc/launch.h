@@ -31,6 +31,8 @@ struct FfnLaunch {
   uint32_t epoch;
   int band_window;
   int tile_order;  // 0: remote first (the layout's mt_order), 1: row-tile numbering
+  int item_begin = 0, item_end = -1;  // bf16: run list indices [item_begin, item_end) only (GEMM1 first, no
+                                      // half-width round); item_end < 0: the whole list
   uint64_t watchdog_ticks;
   uint64_t* timestamps;
   int64_t cap_mtiles;
@@ -74,6 +76,8 @@ int launch_ffn_consumer(const FfnLaunch& p, int n_cons, hipStream_t st, hipEvent
 int ffn_schedule_host(int d, int f, int E, int n_cons, int n_producers, int band_window, int n_mt, int n_rem,
                       const int32_t* mt_hdr, const int32_t* mt_order, int32_t* items, int64_t cap, int64_t* n_out);
 // n_rem and mt_order of a launch: the layout's (remote first), or every tile in number order (tile_order = 1)
+// Column tiles of the two GEMMs and k-splits of the bf16 launch for hidden d and FFN width f.
+void ffn_list_dims(int d, int f, int* n_nt1, int* n_nt2, int* S);
 // The allocation-free variant's flag buffer: its size in 4-byte words, and its device address on device `dev` (the
 // current device; looked up once per device), null if the lookup fails.
 int64_t ffn_noalloc_scratch_words();

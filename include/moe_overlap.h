@@ -13,7 +13,8 @@
  *
  * Conventions shared by every entry point
  *  - Pointers marked (device) are device memory; everything else is host memory.  The caller owns every
- *    buffer; the library allocates no device memory and creates no streams.
+ *    buffer; the library allocates no device memory and creates no streams, except three copy streams (default
+ *    priority) per device that the DMA return mode of moe_expert_ffn_overlap creates on first use.
  *  - `stream` is a hipStream_t (NULL = the null stream).  Every call is asynchronous on it.
  *  - Return values are moe_status codes for synchronous (host-side) checks: MOE_EINVAL for a bad shape,
  *    a null pointer or an unsupported size, MOE_EHIP when a HIP call or launch fails.  moe_last_error()
@@ -107,7 +108,12 @@ typedef struct {
                               1 = sequential (producer on all CUs, then the return on all CUs),
                               2 = return only (the consumer alone, on consumer_cus workgroups, for flags
                                   already published with this epoch; a flag never published ends in the
-                                  watchdog; it delivers the other owners' rows, not the self owner's) */
+                                  watchdog; it delivers the other owners' rows, not the self owner's),
+                              3 = return on the DMA engines (bf16): the producer's item list as a few launches
+                                  on every CU, cut at window boundaries; after each, the segments it completed
+                                  are copied with hipMemcpyDeviceToDeviceNoCU on a copy streams of the library
+                                  while the next launch computes.  Reads the layout's segment table back first
+                                  (synchronises `stream`); consumer_cus is not used */
   uint32_t epoch;          /* flag value of this call: nonzero and different from what the flag array holds
                               (flags start zeroed; pass 1, 2, 3, ...) */
   int32_t band_window;     /* GEMM row tiles per window of the producer's item list (0 = library default, 4):
@@ -198,7 +204,9 @@ int32_t moe_pick_consumer_cus(const moe_shape* s, int32_t n_cu);
  *   mode 0 (overlapped): the consumer is the first consumer_cus workgroups of the producer launch, and every
  *     producer workgroup joins it once its own items are done;
  *   mode 1 (sequential): producer on every CU, then the return alone on every CU;
- *   mode 2: the consumer alone (return only; for tests of the wait).
+ *   mode 2: the consumer alone (return only; for tests of the wait);
+ *   mode 3: the return on the DMA engines instead of consumer CUs (the FiCCO review page's DMA offload), gated per
+ *     launch chunk by events (see moe_overlap_cfg.mode).
  * fp32 runs the two GEMMs as two launches (consumer inside the second).  Owner r receives, at row
  * recv_off_{e,r} + i, the FFN output of the i-th row of group (e, r); results are identical in every mode.
  * y_pad holds the other owners' rows only (scratch of the return).
