@@ -70,17 +70,34 @@ def hbm_traffic(s, cus: int, band_window: int):
     return rec["hbm_bytes_per_launch"] if h.hexdigest() == rec["source_sha256"] else None
 
 
-def cpu_baseline(s, inp, lay_rows, target_s: float):
-    """The CPU oracle's FFN rate on a bounded sample of real rows of the same workload (useful TFLOP/s)."""
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _omp_threads(n: int) -> None:
+    """Set the OpenMP thread count of this process (the oracle's parallel FFN)."""
+    import ctypes
+
+    for name in ("libgomp.so.1", "libgomp.so"):
+        try:
+            ctypes.CDLL(name).omp_set_num_threads(int(n))
+            return
+        except OSError:
+            continue
+
+
+def _oracle_ffn_sample(s, inp, lay, target_s: float, seed: int = 1):
+    """The oracle's FFN on a random sample of real rows grown until it takes about target_s; (rows, seconds)."""
     import oracle
 
-    oracle.load()
-    idx, _ = oracle.route(inp["logits"], s.k)
-    t0 = time.perf_counter()
-    lay = oracle.layout(idx, s.R, s.T_o, s.G, s.E_l, s.k, s.M, s.mgb, 0)
-    t_layout = time.perf_counter() - t0
     real = np.nonzero(lay["row_src"] >= 0)[0]
-    rng = np.random.default_rng(1)
+    rng = np.random.default_rng(seed)
     n = 8
     while True:
         rows = rng.choice(real, min(n, real.size), replace=False)
@@ -89,13 +106,59 @@ def cpu_baseline(s, inp, lay_rows, target_s: float):
                         inp["w_down"], s.dtype == "bf16")
         dt = time.perf_counter() - t0
         if dt >= target_s or n >= real.size:
-            break
+            return rows.size, real.size, dt
         n = min(real.size, int(n * max(2.0, 1.2 * target_s / max(dt, 1e-3))))
-    flops = 6.0 * rows.size * s.d * s.f
+
+
+def cpu_baseline(s, inp, target_s: float):
+    """The CPU oracle on the same workload: routing, layout, delivery and combine on the full batch, the FFN on a
+    bounded random sample of real rows (useful TFLOP/s), every stage timed, all host threads; plus the whole oracle
+    on Tiny and the FFN of Skewed on one thread."""
+    import oracle
+    import moe_inputs as mi
+
+    oracle.load()
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    _omp_threads(cores)
+    st = {}
+    t0 = time.perf_counter()
+    idx, w = oracle.route(inp["logits"], s.k)
+    st["route_s"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    lay = oracle.layout(idx, s.R, s.T_o, s.G, s.E_l, s.k, s.M, s.mgb, 0)
+    st["layout_s"] = time.perf_counter() - t0
+    n_rows, n_real, dt = _oracle_ffn_sample(s, inp, lay, target_s)
+    st["ffn_sample_s"] = dt
+    flops = 6.0 * n_rows * s.d * s.f
+    # delivery and combine of the full batch (their cost does not depend on the values)
+    y_pad = np.zeros((lay["M_pad"], s.d))
+    t0 = time.perf_counter()
+    recv = oracle.deliver(lay, y_pad, s.R, s.E_l)
+    st["deliver_s"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.combine(lay, w, recv, s.R, s.T_o, s.k, s.dtype == "bf16")
+    st["combine_s"] = time.perf_counter() - t0
+    st["ffn_full_batch_s_extrapolated"] = dt * n_real / n_rows
+    # one thread: the whole oracle on Tiny, and the FFN of Skewed on a sample
+    _omp_threads(1)
+    ts = mi.spec("tiny")
+    tin = mi.inputs(ts)
+    t0 = time.perf_counter()
+    oracle.run(ts, tin)
+    one = {"tiny_whole_path_s": time.perf_counter() - t0}
+    sk = mi.spec("skew")
+    skin = mi.inputs(sk)
+    skidx, _ = oracle.route(skin["logits"], sk.k)
+    sklay = oracle.layout(skidx, sk.R, sk.T_o, sk.G, sk.E_l, sk.k, sk.M, sk.mgb, 0)
+    r1, n1, d1 = _oracle_ffn_sample(sk, skin, sklay, min(3.0, target_s / 3), seed=2)
+    one["skew_ffn_tflops"] = 6.0 * r1 * sk.d * sk.f / d1 / 1e12
+    one["skew_ffn_sample"] = "%d of %d real rows, %.1f s" % (r1, n1, d1)
+    _omp_threads(cores)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": "oracle FFN (fp64, h and y rounded to bf16) on %d of %d real rows, %.1f s; oracle layout of "
-                      "the full batch %.3f s" % (rows.size, real.size, dt, t_layout)}
+            "sample": "oracle FFN (fp64, h and y rounded to bf16) on %d of %d real rows, %.1f s; routing, layout, "
+                      "delivery and combine of the full batch" % (n_rows, n_real, dt),
+            "cpu_model": _cpu_model(), "stages_s": {k: round(v, 4) for k, v in st.items()},
+            "one_thread": one}
 
 
 def main():
@@ -103,17 +166,18 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="mixtral")
+    ap.add_argument("--config", default="deepseek")
     ap.add_argument("--consumer-cus", type=int, default=0,
-                    help="consumer CUs of the overlapped launch (0 = the library's pick for the shape)")
+                    help="consumer CUs of the overlapped launch (0 = the launch picks them from the batch's routing "
+                         "and the rates it observed)")
     ap.add_argument("--mgb", type=int, default=1)
     ap.add_argument("--band-window", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--kernels-only", action="store_true", help="timed loop only (for profiler runs)")
-    ap.add_argument("--mode", type=int, default=0, choices=(0, 1),
+    ap.add_argument("--mode", type=int, default=0, choices=(0, 1, 3),
                     help="FFN mode of the timed steps: 0 overlapped, 1 sequential (the consumer alone after the "
-                         "producer, for profiling the copy)")
+                         "producer, for profiling the copy), 3 the return on the DMA engines")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this path runs on a single MI355X (the owner ranks are receive buffers in "
@@ -137,9 +201,8 @@ def main():
     P.route(dev["logits"])
     torch.cuda.synchronize()
     w1, w2 = dev["w_gate_up"], dev["w_down"]
-    # the partition the library uses for consumer_cus = 0, resolved here so the line reports it
-    cus = args.consumer_cus or B.moe_pick_consumer_cus(P.shape, torch.cuda.get_device_properties(0).multi_processor_count)
-    assert cus > 0, B.moe_last_error()
+    # consumer_cus = 0: every overlapped launch picks its partition from the batch's routing and observed rates
+    cus = args.consumer_cus
 
     def step(mode=0, timestamps=False):
         P.layout(dev["x"])
@@ -154,6 +217,10 @@ def main():
     M_real = int(sum(sc["N_r"]))
     M_pad = sc["M_pad"]
     useful = 6.0 * M_real * s.d * s.f
+    # executed MFMA work: the GEMMs skip the 32-row MFMA blocks of a row tile that hold no real row
+    n_mt = sc["n_mtiles"]
+    mt_rows = P.array("mtile_desc").view(-1, B.MT_FIELDS)[:n_mt, 1].cpu().numpy().astype(np.int64)
+    executed = 6.0 * float(((mt_rows + 31) // 32 * 32).sum()) * s.d * s.f if s.dtype == "bf16" else useful
 
     # timed region: K whole steps, kernel events recorded on the streams the kernels run on
     B.moe_set_kernel_timing(True)
@@ -188,7 +255,9 @@ def main():
 
     reps = max(5, args.steps)
     t_ovl = time_ffn(0, reps)
+    part = P.partition_record() if s.dtype == "bf16" else (cus, 0.0, 0.0, False)
     t_seq = time_ffn(1, reps)
+    t_dma = time_ffn(3, max(3, reps // 4)) if s.dtype == "bf16" else None
     B.moe_set_kernel_timing(True)
     B.moe_kernel_times()
     for _ in range(reps):
@@ -222,9 +291,11 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": s.dtype, "data": "synthetic",
-        "config": {"workload": workload_name(s), "M_real": M_real, "M_returned": M_ret, "M_pad": M_pad, "gemm_row_tiles": sc["n_mtiles"], "consumer_cus": cus,
-                   "consumer_cus_chosen_by": "option" if args.consumer_cus else "library pick",
-                   "band_window": args.band_window or 4, "mode": "overlapped" if args.mode == 0 else "sequential"},
+        "config": {"workload": workload_name(s), "M_real": M_real, "M_returned": M_ret, "M_pad": M_pad,
+                   "gemm_row_tiles": sc["n_mtiles"], "consumer_cus": args.consumer_cus or part[0],
+                   "consumer_cus_chosen_by": "option" if args.consumer_cus else "the launch (routing + observed rates)",
+                   "band_window": args.band_window or 4, "producer_order": "remote first",
+                   "mode": {0: "overlapped", 1: "sequential", 3: "DMA return"}[args.mode]},
         "pct_bf16_peak_step": round(100 * value / peak, 2),
         "ffn_tflops_overlapped": round(ffn_tflops, 2),
         "pct_bf16_peak_ffn": round(100 * ffn_tflops / peak, 2),
@@ -241,7 +312,12 @@ def main():
         "timestamps_us": {k: round(v, 2) for k, v in o_med.items()},
         "kernel_ms_avg": {"ffn_producer_launch": round(g1_avg, 4), "second_launch": round(g2_avg, 4),
                           "consumer_alone_seq": round(s1 and sc_ms / sn, 4)},
-        "executed_pad_pct": round(100.0 * (M_pad - M_real) / max(M_real, 1), 2),
+        "executed_mfma_tflop": round(executed / 1e12, 4),
+        "executed_over_useful_pct": round(100.0 * (executed - useful) / useful, 2),
+        "layout_padding_pct": round(100.0 * (M_pad - M_real) / max(M_real, 1), 2),
+        "observed_rates": {"producer_tflops_per_cu": round(part[1] * 1e8 / 1e12, 4),
+                           "consumer_copy_gbs_per_cu": round(part[2] * 1e8 / 1e9, 2), "valid": part[3]},
+        "ffn_ms_dma_return": [round(v, 4) for v in t_dma] if t_dma else None,
         "roofline": {"bound": "mfma",
                      "kernel": ("k_ffn_bf16: whole expert FFN in one persistent launch (gate/up + SwiGLU, "
                                 "down projection with split-K, flag publish; the return inside)"
@@ -251,7 +327,7 @@ def main():
                      "traffic": hbm_traffic(s, cus, args.band_window), "traffic_unit": "HBM bytes per launch"},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(s, inp, M_real, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(s, inp, args.cpu_seconds)
     print(json.dumps(res))
 
 

@@ -17,10 +17,12 @@ LIB_PATH = os.path.join(HERE, "libmoe_overlap.so")
 MOE_OK, MOE_EINVAL, MOE_ECAPACITY, MOE_EHIP, MOE_ETIMEOUT = 0, -1, -2, -3, -4
 MOE_BF16, MOE_F32 = 0, 1
 MOE_SEG_FIELDS = 8
+MOE_OBS_WORDS = 16
 MT_HDR = 8
 MT_FIELDS = MT_HDR + 256
 EXPORTS = ["moe_last_error", "moe_version", "moe_route", "moe_layout_capacity_rows", "moe_layout_workspace_bytes",
            "moe_layout_bind", "moe_layout_build", "moe_read_status", "moe_ffn_flags_count", "moe_pick_consumer_cus",
+           "moe_pick_consumer_cus_observed",
            "moe_expert_ffn_overlap", "moe_expert_ffn_overlap_noalloc", "moe_ffn_schedule",
            "moe_combine", "moe_set_kernel_timing", "moe_kernel_times"]
 
@@ -72,6 +74,7 @@ def lib():
             "moe_layout_build": ([ps, vp, vp, pl, vp, vp], i32),
             "moe_read_status": ([pl, vp], i32), "moe_ffn_flags_count": ([ps], i64),
             "moe_pick_consumer_cus": ([ps, i32], i32),
+            "moe_pick_consumer_cus_observed": ([ps, i32, i64, i64, ctypes.c_float, ctypes.c_float], i32),
             "moe_expert_ffn_overlap": ([ps, pl, vp, vp, vp, vp, vp, vp, vp, pc, vp], i32),
             "moe_expert_ffn_overlap_noalloc": ([ps, pl, vp, vp, vp, vp, vp, vp, pc, vp], i32),
             "moe_combine": ([ps, pl, vp, vp, vp, vp], i32),
@@ -153,6 +156,12 @@ def moe_ffn_flags_count(shape: moe_shape) -> int:
 
 def moe_pick_consumer_cus(shape: moe_shape, n_cu: int) -> int:
     return lib().moe_pick_consumer_cus(ctypes.byref(shape), n_cu)
+
+
+def moe_pick_consumer_cus_observed(shape: moe_shape, n_cu: int, rows_routed: int, rows_returned: int, ffn_rate: float,
+                                   copy_rate: float) -> int:
+    return lib().moe_pick_consumer_cus_observed(ctypes.byref(shape), n_cu, rows_routed, rows_returned, ffn_rate,
+                                                copy_rate)
 
 
 def moe_expert_ffn_overlap(shape: moe_shape, layout: moe_layout, x_pad, w_gate_up, w_down, h_ws, y_pad, recv,

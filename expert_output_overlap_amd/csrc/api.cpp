@@ -281,16 +281,19 @@ int64_t moe_ffn_flags_count(const moe_shape* s) {
 
 int32_t moe_pick_consumer_cus(const moe_shape* s, int32_t n_cu) {
   if (!check_shape(s).empty() || n_cu < 2) return -1;
-  // Returning 4 M_real d bytes (bf16 rows read and written) at ~45 GB/s per consumer CU, next to 6 M_real d f
-  // FFN flops at ~0.8 PFLOP/s, takes 11850 / (C f) of the FFN's time on C consumer CUs, whatever M_real and d
-  // are.  Take the smallest multiple of 8 (the same count on each of the 8 XCDs) at which the consumers alone
-  // would finish the return in half the FFN's time, so tiles published late still have time to go: at least
-  // 8, at most 32 (the range measured) and a quarter of the CUs.
-  const int cap = std::max(1, std::min(32, n_cu / 4));
-  if (s->dtype != MOE_BF16) return std::min(8, cap);
-  const int need = (int)std::ceil(2.0 * 11850.0 / s->f);
-  const int c = std::max(8, (need + 7) / 8 * 8);
-  return std::min(c, cap);
+  if (s->dtype != MOE_BF16) return std::min(8, std::max(1, std::min(32, n_cu / 4)));
+  // the launch's own rule (ffn_adaptive_consumers) before any observation, with the rows of R - 1 of the R owners
+  // returned (uniform routing)
+  const int64_t m = 1000000;
+  return ffn_adaptive_consumers(n_cu, m, m * (s->R - 1) / s->R, s->d, s->f, 0.f, 0.f);
+}
+
+int32_t moe_pick_consumer_cus_observed(const moe_shape* s, int32_t n_cu, int64_t rows_routed, int64_t rows_returned,
+                                       float ffn_rate, float copy_rate) {
+  if (!check_shape(s).empty() || n_cu < 2 || rows_routed < 0 || rows_returned < 0 || rows_returned > rows_routed)
+    return -1;
+  if (s->dtype != MOE_BF16) return moe_pick_consumer_cus(s, n_cu);
+  return ffn_adaptive_consumers(n_cu, rows_routed, rows_returned, s->d, s->f, ffn_rate, copy_rate);
 }
 
 }  // extern "C"
@@ -528,7 +531,8 @@ int ffn_overlap(const moe_shape* s, const moe_layout* L, const void* x_pad, cons
   // overlapped: C consumer workgroups in the producer launch (bf16: the whole FFN; fp32: its second GEMM),
   // producers on the other CUs, each joining the return once its items are done; sequential: producers on
   // every CU, then the return on every CU
-  const int n_cons = cfg->mode == 0 ? C : 0;
+  // overlapped bf16 with consumer_cus = 0: the launch picks its own partition (ffn_adaptive_consumers)
+  const int n_cons = cfg->mode != 0 ? 0 : (cfg->consumer_cus == 0 && p.dtype == MOE_BF16 ? -1 : C);
   next_pair();
   if (launch_ffn_producer(p, n_cu, p.dtype == MOE_BF16 ? n_cons : 0, st, ev0, ev1))
     return failed("producer launch failed");

@@ -43,6 +43,7 @@ struct ConsumerArgs {
   int row_vec;
   uint64_t budget;
   uint64_t* ts;
+  uint32_t* obs;  // the launch's partition record: copied bytes (64-bit word 6) and copy ticks (word 8), or null
 };
 
 // Opens the counter for this launch; called by one workgroup at its start, before it claims.
@@ -146,7 +147,8 @@ __device__ void consumer_role(const ConsumerArgs& a) {
     const int64_t n = (int64_t)sd[SEG_ROWS] * a.row_vec;
     const int64_t c1 = c0 + CONSUMER_UNIT_CHUNKS < n ? c0 + CONSUMER_UNIT_CHUNKS : n;
     const int owner = sd[SEG_OWNER], src = sd[SEG_SRC_ROW], dst = sd[SEG_DST_ROW];
-    if (a.ts != nullptr && tid == 0) atomicMin((unsigned long long*)&a.ts[2 + 2 * s], (unsigned long long)moe_clock());
+    const uint64_t tc0 = moe_clock();
+    if (a.ts != nullptr && tid == 0) atomicMin((unsigned long long*)&a.ts[2 + 2 * s], (unsigned long long)tc0);
     const v4u32* __restrict__ f4 = (const v4u32*)(a.y + (int64_t)src * a.row_vec);
     v4u32* __restrict__ t4 = (v4u32*)((uint4*)a.recv.p[owner] + (int64_t)dst * a.row_vec);
     const int64_t B = nthr;
@@ -160,8 +162,12 @@ __device__ void consumer_role(const ConsumerArgs& a) {
     }
     for (; i < c1; i += B) t4[i] = f4[i];
     if (a.ts != nullptr) {
-      __syncthreads();
+      __syncthreads();  // the unit is copied (loads returned; the stores need not have landed)
       if (tid == 0) atomicMax((unsigned long long*)&a.ts[3 + 2 * s], (unsigned long long)moe_clock());
+    }
+    if (a.obs != nullptr && tid == 0) {  // thread 0's share of the unit stands for the workgroup's (no barrier)
+      atomicAdd((unsigned long long*)(a.obs + 6), (unsigned long long)((c1 - c0) * 16));
+      atomicAdd((unsigned long long*)(a.obs + 8), (unsigned long long)(moe_clock() - tc0));
     }
   }
 }

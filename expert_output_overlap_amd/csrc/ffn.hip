@@ -359,10 +359,19 @@ struct FusedArgs {
   uint32_t epoch;
   uint64_t budget;
   uint64_t* ts;
-  int n_cons;
+  int n_cons;      // consumer workgroups; -1: picked by the launch (ffn_adaptive_consumers)
+  int E;           // local experts (the interleave rule, when the launch picks the partition)
+  uint32_t* obs;   // the partition record (MOE_OBS_WORDS words, see obs_*), or null
   ConsumerArgs cons;
   unsigned char* self_recv;  // the self owner's buffer: y rows of the self-owned groups go straight there
 };
+
+// The partition record in the flag buffer (64-bit fields at even words): [0] arrival counter of this call's
+// workgroups (the last one resets it; a call that fails leaves a count the next calls absorb), [2] ~(first producer item start), [4] last producer item end, [6] bytes the
+// consumer role copied, [8] its copy ticks summed over workgroups; [10] producers' flops per CU-tick and [11]
+// consumers' bytes per CU-tick (fp32, running estimates from earlier calls), [12] the partition of the last call,
+// [13] nonzero once [10] and [11] hold observations.
+__device__ __forceinline__ unsigned long long* obs64(uint32_t* obs, int w) { return (unsigned long long*)(obs + w); }
 
 // All threads of the workgroup: wait until the n flags equal epoch, then acquire (compiler ordering; see the
 // publish protocol in common.h).  False if the spin budget ran
@@ -799,8 +808,22 @@ __global__ __launch_bounds__(FFN_THREADS, 1) void k_ffn_bf16(FusedArgs a) {
 
   launch_acquire();  // drop cache lines older than this launch (the publish protocol in common.h)
   if (load_status(a.status) != 0) return;
-  if (a.n_cons > 0 && blockIdx.x == 0) consumer_stamp(a.cons);
   const int n_mt = a.scalars[a.sc_nmt];
+  // this batch's routed and returned rows (the layout's per-owner counts)
+  int64_t m_real = 0, m_self = 0;
+  for (int r = 0; r < a.sc_nmt - SC_NR; ++r) {
+    const int n = a.scalars[SC_NR + r];
+    m_real += n;
+    if (r == a.cons.self_rank) m_self = n;
+  }
+  int C = a.n_cons, interleave = a.interleave;
+  if (C < 0) {  // the launch picks its consumer partition: every workgroup computes the same value
+    const float fr = a.obs[13] ? __uint_as_float(a.obs[10]) : 0.f, cr = a.obs[13] ? __uint_as_float(a.obs[11]) : 0.f;
+    C = ffn_adaptive_consumers(gridDim.x, m_real, m_real - m_self, a.d, a.f, fr, cr);
+    interleave = ffn_interleave(C, a.d, a.f, a.E);
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.obs[12] = (uint32_t)C;
+  }
+  if (C > 0 && blockIdx.x == 0) consumer_stamp(a.cons);
   const int tid = threadIdx.x;
   if (tid == 0) s_pend = nullptr;
   // every wave's stores of the previous item have completed, then its flag (a wait on it may come next)
@@ -817,11 +840,11 @@ __global__ __launch_bounds__(FFN_THREADS, 1) void k_ffn_bf16(FusedArgs a) {
       s_pend = nullptr;
     }
   };
-  const int C = a.n_cons, G = gridDim.x - C;
+  const int G = gridDim.x - C;
   // the item list (item_list.h): the consumers' share of GEMM1 items, the producers' round-robin share, and the
   // half-width items of a last round at most half full
   const FfnList L = ffn_list_make(n_mt, a.mt_order ? a.scalars[a.sc_nmt + 1] : n_mt, a.n_nt1, a.n_nt2, a.S, a.window,
-                                  a.interleave, C, G, BN2 >= 128 && a.halves);
+                                  interleave, C, G, BN2 >= 128 && a.halves);
   auto run_of = [&](int mt, int* r0, int* rc) {
     const int32_t* d = a.mtile_desc + (int64_t)mt * MOE_MT_FIELDS;
     *r0 = d[2];
@@ -837,7 +860,11 @@ __global__ __launch_bounds__(FFN_THREADS, 1) void k_ffn_bf16(FusedArgs a) {
       if (tid < MOE_MT_HDR) s_hdr[tid] = dsc[tid];
       if (tid < MOE_MT_ROWS) s_rows[tid] = dsc[MOE_MT_HDR + tid];
     }
-    if (a.ts != nullptr && first && tid == 0) atomicMin((unsigned long long*)&a.ts[0], (unsigned long long)moe_clock());
+    if (first && tid == 0) {
+      const unsigned long long t = moe_clock();
+      if (a.ts != nullptr) atomicMin((unsigned long long*)&a.ts[0], t);
+      if (a.obs != nullptr) atomicMax(obs64(a.obs, 2), ~t);
+    }
     first = false;
     __syncthreads();
     flush();
@@ -868,8 +895,33 @@ __global__ __launch_bounds__(FFN_THREADS, 1) void k_ffn_bf16(FusedArgs a) {
     if (!run(item)) return;
   __syncthreads();
   flush();
+  if (a.obs != nullptr && tid == 0 && !first) atomicMax(obs64(a.obs, 4), (unsigned long long)moe_clock());
   // then every workgroup returns segments until no copy unit is left
   if (C > 0) consumer_role(a.cons);
+  // the last workgroup to finish folds this call's rates into the record (an error on the way leaves it as it was)
+  if (a.obs != nullptr) {
+    __syncthreads();
+    // a plain counter (fetch-and-add, reset by the last arrival): 256 compare-and-swap loops on one word at the
+    // end of the launch serialised for ~0.2 ms
+    if (tid == 0 && atomicAdd(obs64(a.obs, 0), 1ull) == (unsigned long long)gridDim.x - 1) {
+      auto ld = [&](int w) { return __hip_atomic_load(obs64(a.obs, w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+      const unsigned long long s_inv = ld(2), e = ld(4), bytes = ld(6), ticks = ld(8);
+      const bool valid = a.obs[13] != 0;
+      float fr = __uint_as_float(a.obs[10]), cr = __uint_as_float(a.obs[11]);
+      if (s_inv != 0 && e > ~s_inv && G > 0) {
+        const float nf = (float)(6.0 * (double)m_real * a.d * (double)a.f / ((double)(e - ~s_inv) * G));
+        fr = valid && fr > 0.f ? 0.5f * (fr + nf) : nf;
+      }
+      if (ticks > 0 && bytes > 0) {
+        const float nc = (float)((double)bytes / (double)ticks);
+        cr = valid && cr > 0.f ? 0.5f * (cr + nc) : nc;
+      }
+      a.obs[10] = __float_as_uint(fr);
+      a.obs[11] = __float_as_uint(cr);
+      a.obs[13] = (fr > 0.f && cr > 0.f) ? 1u : 0u;
+      for (int w = 0; w < 10; w += 2) __hip_atomic_store(obs64(a.obs, w), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void k_consumer(ConsumerArgs c) {
@@ -909,7 +961,7 @@ int ffn_splits(int dtype, int d, int f) {
 
 namespace {
 struct FlagCarve {
-  int64_t flags2, flags1, scount, partial, claim, total;  // offsets and size in 4-byte words
+  int64_t flags2, flags1, scount, partial, claim, obs, total;  // offsets and size in 4-byte words
 };
 FlagCarve flag_carve(int dtype, int d, int f, int64_t cap_mtiles) {
   FlagCarve c;
@@ -926,7 +978,8 @@ FlagCarve flag_carve(int dtype, int d, int f, int64_t cap_mtiles) {
     c.partial = c.scount + up(2 * cap_mtiles * n2);  // split counts; also the halves of unsplit tiles
     c.claim = c.partial + (S > 1 ? cap_mtiles * n2 * S * (int64_t)BF_BM * ffn_gemm2_bn(dtype, d) : 0);
   }
-  c.total = c.claim + 2;  // the consumer's 64-bit unit counter
+  c.obs = c.claim + 2;  // after the consumer's 64-bit unit counter (bf16: the partition record)
+  c.total = c.obs + (dtype == MOE_BF16 ? MOE_OBS_WORDS : 0);
   return c;
 }
 
@@ -956,6 +1009,7 @@ void fill_consumer(ConsumerArgs& c, const FfnLaunch& p, int n_nt2) {
   c.budget = p.watchdog_ticks;
   c.ts = p.timestamps;
   c.self_rank = p.self_rank;
+  c.obs = nullptr;
 }
 
 
@@ -990,7 +1044,8 @@ int launch_bf16(const FfnLaunch& p, int grid, int n_cons, hipStream_t st, hipEve
   a.S = ffn_splits(p.dtype, p.d, p.f);
   a.window = p.band_window > 0 ? p.band_window : 4;
   // item order: GEMM1 first or interleaved windows (the rule is in item_list.h)
-  a.interleave = p.item_end >= 0 ? 0 : ffn_interleave(n_cons, p.d, p.f, p.E);  // chunks: GEMM1 first
+  // chunks: GEMM1 first; a launch that picks its partition decides the order itself
+  a.interleave = p.item_end >= 0 ? 0 : (n_cons < 0 ? -1 : ffn_interleave(n_cons, p.d, p.f, p.E));
   a.halves = p.item_end >= 0 ? 0 : 1;  // a chunked list has no single last round
   a.item_begin = p.item_end >= 0 ? p.item_begin : 0;
   a.item_end = p.item_end >= 0 ? p.item_end : INT32_MAX;
@@ -1007,7 +1062,10 @@ int launch_bf16(const FfnLaunch& p, int grid, int n_cons, hipStream_t st, hipEve
   a.budget = p.watchdog_ticks;
   a.ts = p.timestamps;
   a.n_cons = n_cons;
+  a.E = p.E;
+  a.obs = p.item_end >= 0 ? nullptr : p.flags + fc.obs;  // a chunk of the list observes no whole-call rate
   fill_consumer(a.cons, p, a.n_nt2);
+  a.cons.obs = a.obs;
   a.self_recv = (unsigned char*)p.recv[p.self_rank];
   const dim3 g(grid), b(FFN_THREADS);
   if (bn1 == 256 && bn2 == 256) hipExtLaunchKernelGGL((k_ffn_bf16<256, 256>), g, b, 0, st, ev0, ev1, 0, a);
@@ -1143,7 +1201,9 @@ int launch_flags_clear(int dtype, int d, int f, int64_t cap_mtiles, uint32_t* fl
   const FlagCarve c = flag_carve(dtype, d, f, cap_mtiles);
   const int64_t blocks = std::min<int64_t>((c.partial + 255) / 256, 1024);
   if (c.partial > 0) hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(256), 0, st, flags, c.partial);
-  hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(64), 0, st, flags + c.claim, (int64_t)2);
+  // the copy-unit counter, and the partition record's arrival counter and per-call sums (its running rate estimates
+  // stay)
+  hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(64), 0, st, flags + c.claim, (int64_t)(dtype == MOE_BF16 ? 12 : 2));
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

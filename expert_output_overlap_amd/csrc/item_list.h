@@ -213,3 +213,34 @@ MOE_HD FfnItem ffn_list_item(const FfnList& L, int idx, RunOf run_of, OrderOf or
   }
   return it;
 }
+
+// ---- the consumer partition, picked at run time -------------------------------------------------------------
+// The review page ("If this is right": the overlap collapses with too few consumer SMs; "Where Pith is reading between
+// the lines": size the partition at run time) leaves the size open.  The launch picks it itself, every workgroup
+// identically, from this batch's routing (rows routed to the local experts and rows to return to other owners, from
+// the layout) and from rates observed in earlier calls: the producers' flops per CU-tick and the consumers' copied
+// bytes per CU-tick (100 MHz ticks).  The consumers have to return 4 d bytes per returned row (read and write, bf16)
+// while the producers run 6 d f flops per routed row; copies can start only once row tiles complete, in about the
+// second half of the launch, so the pick is the smallest multiple of 8 (the same count on each XCD) in [8, cmax] at
+// which the consumers alone would finish the return in half the FFN's time; cmax = min(32, n_cu / 4) (a device with
+// under 32 CUs: a quarter of them).
+#ifndef MOE_OBS_WORDS
+#define MOE_OBS_WORDS 16  // words of the partition record (also in moe_overlap.h)
+#endif
+// defaults before any observation: ~45 GB/s of copy per CU, ~0.8 PFLOP/s of FFN over 256 CUs
+#define MOE_COPY_RATE0 450.0f    // bytes per tick per consumer CU
+#define MOE_FFN_RATE0 31250.0f   // flops per tick per producer CU
+
+MOE_HD int ffn_adaptive_consumers(int n_cu, int64_t m_real, int64_t m_ret, int d, int f, float ffn_rate,
+                                  float copy_rate) {
+  const int cmax = li_min(32, n_cu / 4) / 8 * 8;
+  if (cmax < 8) return n_cu / 4 > 1 ? n_cu / 4 : 1;  // a small device: a quarter of its CUs
+  if (!(ffn_rate > 0.f)) ffn_rate = MOE_FFN_RATE0;
+  if (!(copy_rate > 0.f)) copy_rate = MOE_COPY_RATE0;
+  for (int c = 8; c <= cmax; c += 8) {
+    const double copy_t = 4.0 * (double)m_ret * d / ((double)c * copy_rate);
+    const double ffn_t = 6.0 * (double)m_real * d * (double)f / ((double)(n_cu - c) * ffn_rate);
+    if (copy_t <= 0.5 * ffn_t) return c;
+  }
+  return cmax;
+}

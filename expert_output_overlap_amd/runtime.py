@@ -84,6 +84,15 @@ class MoePath:
     def combine(self, topk_w: torch.Tensor | None = None, stream=None):
         B.moe_combine(self.shape, self.L, self.topk_w if topk_w is None else topk_w, self.recv, self.out, stream)
 
+    def partition_record(self):
+        """The launch's consumer-partition record (bf16): (consumer CUs of the last overlapped call, observed producer
+        flops per CU-tick, observed consumer bytes per CU-tick, whether the rates hold observations)."""
+        import struct
+
+        w = self.flags[-B.MOE_OBS_WORDS:].cpu().numpy().astype("<i4").view("<u4")
+        f = lambda v: struct.unpack("<f", struct.pack("<I", int(v)))[0]
+        return int(w[12]), f(w[10]), f(w[11]), bool(w[13])
+
     def status(self, stream=None) -> int:
         return B.moe_read_status(self.L, stream)
 

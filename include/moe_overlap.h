@@ -100,8 +100,8 @@ typedef struct {
 /* Knobs of moe_expert_ffn_overlap. */
 typedef struct {
   int32_t consumer_cus;    /* C: consumer workgroups, one per CU, in [1, CUs/2]; the producer's persistent
-                              launch runs one workgroup on each other CU.  0 = the library picks C for the
-                              shape (moe_pick_consumer_cus) */
+                              launch runs one workgroup on each other CU.  0 = the launch picks C from the
+                              batch's routing and observed rates (see moe_pick_consumer_cus) */
   int32_t mode;            /* 0 = overlapped (the C consumer workgroups and the producer workgroups in one
                                   launch, on disjoint CUs; a producer workgroup joins the return once its
                                   own items are done),
@@ -176,18 +176,27 @@ int moe_read_status(const moe_layout* L, void* stream);
  * holds the readiness flags of the second GEMM's output tiles (what the consumer waits on), and for bf16 the
  * flags of the first GEMM's h tiles, an arrival counter per output tile of the second GEMM and the fp32 partial
  * sums of its k-splits (256 x 256 floats per output tile and split; f/d rounded gives the number of splits, up
- * to 8); last, one 64-bit counter of the return's copy units.  Zero the buffer once before the first call;
- * afterwards it is epoch-valued. */
+ * to 8); then one 64-bit counter of the return's copy units; last (bf16), the MOE_OBS_WORDS words of the consumer
+ * partition record (see moe_pick_consumer_cus).  Zero the buffer once before the first call; afterwards it is
+ * epoch-valued. */
 int64_t moe_ffn_flags_count(const moe_shape* s);
 
-/* Consumer partition the library uses when cfg->consumer_cus is 0, for a device of n_cu CUs; -1 if the shape
- * is invalid or n_cu < 2.  Host only (no device call).  Sized from the ratio of the return's time to the FFN's
- * (review page: "If this is right" reports the overlap collapsing with too few consumer SMs; "Where Pith is
- * reading between the lines" proposes sizing the partition at run time): the return moves
- * 4 bytes per routed row and hidden unit (bf16, read and written), the FFN 6 f flops, so the ratio depends on f
- * alone; the pick is the smallest multiple of 8 at which the consumers alone would return everything in half
- * the FFN's time at the measured per-CU copy rate and FFN rate, in [8, min(32, n_cu/4)] (fp32: 8). */
+/* The consumer partition (review page: "If this is right" reports the overlap collapsing with too few consumer
+ * SMs; "Where Pith is reading between the lines" proposes sizing the partition at run time).  With
+ * cfg->consumer_cus = 0, an overlapped bf16 launch picks it itself, on the device, from this batch's routing (rows
+ * routed to the local experts, rows to return to other owners: the layout's per-owner counts) and from rates it
+ * observed in earlier calls on the same flag buffer: the producers' flops per CU and the consumers' copied bytes per
+ * CU, per 100 MHz tick.  The rule: the smallest multiple of 8 in [8, min(32, n_cu/4)] at which the consumers alone
+ * would return 4 d bytes per returned row in half the time the other CUs take for 6 d f flops per routed row.
+ * The choice of the last overlapped call is word MOE_OBS_WORDS - 4 counted from the end of the flag buffer.
+ * moe_pick_consumer_cus_observed evaluates the rule for given rows and rates (a rate <= 0 takes its default:
+ * 450 bytes and 31250 flops per CU-tick, ~45 GB/s and ~0.8 PFLOP/s over 256 CUs); moe_pick_consumer_cus for the
+ * defaults with R - 1 of every R rows returned.  fp32: 8 (at most a quarter of the CUs).  Host only; -1 for an
+ * invalid shape or arguments, or n_cu < 2. */
 int32_t moe_pick_consumer_cus(const moe_shape* s, int32_t n_cu);
+int32_t moe_pick_consumer_cus_observed(const moe_shape* s, int32_t n_cu, int64_t rows_routed, int64_t rows_returned,
+                                       float ffn_rate, float copy_rate);
+#define MOE_OBS_WORDS 16
 
 /* Expert SwiGLU FFN over the padded layout with the return of each finished row-band segment to its
  * owner (review page: "The pith", "Core claim", "What carries the argument").

@@ -53,18 +53,20 @@ def test_capacity_matches_bound(kw):
     (dict(tokens_per_owner=4096, num_global_experts=8, num_local_experts=2, f=4096), 8),
     (dict(R=8, tokens_per_owner=2048, num_global_experts=256, num_local_experts=32, top_k=8, d=7168, f=2048), 16),
     (dict(tokens_per_owner=2048, num_global_experts=64, num_local_experts=16, top_k=6, d=2048, f=1408,
-          tile_m=64), 24),
+          tile_m=64), 16),
     (dict(d=64, f=128, tile_m=16), 32),                                # capped at 32
     (dict(d=64, f=128, tile_m=16, dtype=B.MOE_F32), 8),
 ])
 def test_consumer_partition_pick(kw, want):
-    """The library's partition: the smallest multiple of 8 at which the consumers alone return the rows in half the
-    FFN's time, by the rate model (11850 / (C f) of the FFN's time), within [8, min(32, CUs/4)]."""
+    """The shape-only partition estimate: the launch's rule with default rates and R - 1 of every R rows returned
+    (the smallest multiple of 8 at which the consumers alone return the rows in half the FFN's time), within
+    [8, min(32, CUs/4)]; a device with under 32 CUs takes a quarter of them."""
     s = shape(**kw)
     c = B.moe_pick_consumer_cus(s, 256)
     assert c == want
     if s.dtype == B.MOE_BF16 and 8 < c < 32:
-        assert 11850.0 / (c * s.f) <= 0.5 < 11850.0 / ((c - 8) * s.f)
+        ratio = lambda c: 4.0 * (s.R - 1) / s.R * 31250.0 * (256 - c) / (6.0 * 450.0 * c * s.f)
+        assert ratio(c) <= 0.5 < ratio(c - 8)
     assert B.moe_pick_consumer_cus(s, 16) == min(want, 4)   # a quarter of a small device's CUs
     assert B.moe_pick_consumer_cus(s, 4) == 1
     assert B.moe_pick_consumer_cus(s, 1) == -1
@@ -182,3 +184,22 @@ def test_full_size_parity_runs_in_the_bench_configuration():
     tests = open(os.path.join(root, "tests", "test_gpu_path.py")).read()
     t = re.search(r"^BENCH_CONSUMER_CUS = (\d+)", tests, re.M)
     assert m and t and int(m.group(1)) == int(t.group(1))
+
+
+def test_partition_rule():
+    """The consumer-partition rule (the launch's own code, compiled for the host): more returned rows or slower copies
+    take more consumer CUs, a faster FFN too; nothing to return takes the minimum; multiples of 8 within
+    [8, min(32, CUs / 4)]; defaults for rates <= 0."""
+    s = shape(d=2048, f=1408, R=4)
+    pick = lambda routed, ret, fr=0.0, cr=0.0, n=256: B.moe_pick_consumer_cus_observed(s, n, routed, ret, fr, cr)
+    assert pick(15000, 0) == 8
+    vals = [pick(15000, r) for r in (0, 3000, 6000, 9000, 12000, 15000)]
+    assert vals == sorted(vals) and vals[-1] > vals[0]
+    assert all(v % 8 == 0 and 8 <= v <= 32 for v in vals)
+    assert pick(15000, 12000, cr=100.0) >= pick(15000, 12000, cr=450.0) >= pick(15000, 12000, cr=2000.0)
+    assert pick(15000, 12000, fr=60000.0) >= pick(15000, 12000, fr=31250.0)
+    assert pick(15000, 12000, 0.0, 0.0) == pick(15000, 12000, 31250.0, 450.0)
+    assert pick(15000, 15000, cr=1.0, n=64) == 16  # capped at a quarter of the CUs
+    # the shape-only estimate is the rule with 3 of 4 owners' rows returned and default rates
+    assert B.moe_pick_consumer_cus(s, 256) == pick(4000, 3000)
+    assert pick(100, 200) == -1
