@@ -176,13 +176,14 @@ def ffn_rows(src_row, expert, x, w_gate_up, w_down, is_bf16: bool, lib=None) -> 
 
 
 def ffn_rows_ex(src_row, expert, x, w_gate_up, w_down, is_bf16: bool, max_cand: int = 64, want_h: bool = False,
-                lib=None) -> dict:
+                want_vec: bool = True, lib=None) -> dict:
     """FFN rows plus, in bf16 mode, the roundings of h that an fp32 evaluation does not decide.
 
     Returns y (float64 [n, d], rounded as the path rounds), y_unr (y before its final rounding), y_delta (bound
     of an fp32 evaluation's error in y_unr), optionally h (the rounded hidden rows [n, f]), and per row
-    up to ``max_cand`` alternative roundings: cand_count [n], cand_n [n, max_cand] (hidden index),
-    cand_vec [n, max_cand, d] (exact change of y_unr when h takes the other bf16 candidate).
+    up to ``max_cand`` alternative roundings, largest step first: cand_count [n], cand_n [n, max_cand] (hidden index),
+    cand_vec [n, max_cand, d] (exact change of y_unr when h takes the other bf16 candidate; omitted with
+    want_vec=False).
     """
     lib = lib or load()
     src_row = np.ascontiguousarray(src_row, dtype=np.int32)
@@ -194,13 +195,15 @@ def ffn_rows_ex(src_row, expert, x, w_gate_up, w_down, is_bf16: bool, max_cand: 
     f = w_down.shape[2]
     n = src_row.size
     out = {"y": np.empty((n, d)), "y_unr": np.empty((n, d)), "cand_count": np.zeros(n, np.int32),
-           "cand_n": np.zeros((n, max_cand), np.int32), "cand_vec": np.zeros((n, max_cand, d)),
-           "y_delta": np.empty((n, d))}
+           "cand_n": np.zeros((n, max_cand), np.int32), "y_delta": np.empty((n, d))}
+    if want_vec:
+        out["cand_vec"] = np.zeros((n, max_cand, d))
     if want_h:
         out["h"] = np.empty((n, f))
     rc = lib.orc_ffn_rows_ex(n, _p(src_row), _p(expert), d, f, int(is_bf16), _p(x), _p(w_gate_up), _p(w_down),
                              _p(out["y"]), _p(out["y_unr"]), max_cand, _p(out["cand_count"]), _p(out["cand_n"]),
-                             _p(out["cand_vec"]), _p(out["h"]) if want_h else None, _p(out["y_delta"]))
+                             _p(out["cand_vec"]) if want_vec else None, _p(out["h"]) if want_h else None,
+                             _p(out["y_delta"]))
     if rc != 0:
         raise ValueError("orc_ffn_rows_ex failed")
     return out

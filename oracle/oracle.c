@@ -301,7 +301,8 @@ static int orc_cand_cmp(const void* a, const void* b) {
  * When the exact h_n is within delta_n of the midpoint between its bf16 rounding and the neighbouring bf16
  * value, either rounding is a correct result; the row then lists n, the step dh to the other candidate
  * and the resulting change of y, dh * Wd[e][:, n], exactly.  Up to max_cand candidates per row are kept,
- * largest |dh| first.  y_unr receives y before its final rounding; h_out (optional, [nrows][f]) the
+ * largest |dh| first (cand_vec may be NULL: the list without the vectors).  y_unr receives y before its final
+ * rounding; h_out (optional, [nrows][f]) the
  * rounded hidden row; y_delta (optional, [nrows][d]) the same kind of bound for the fp32 evaluation of y
  * itself, 2^-21 sqrt(f) Qy_m + 2^-22 |y_m| with Qy_m = sqrt(sum_n (h_n Wd[e][m][n])^2): where y_unr lies
  * within y_delta of a bf16 rounding midpoint, both neighbouring bf16 values are correct results for y.
@@ -374,6 +375,7 @@ int orc_ffn_rows_ex(int64_t nrows, const int32_t* src_row, const int32_t* expert
         cand_count[i] = nc;
         for (int q = 0; q < nc; ++q) {
           cand_n[i * max_cand + q] = cands[q].n;
+          if (cand_vec == NULL) continue; /* the list only */
           double* v = cand_vec + ((int64_t)i * max_cand + q) * d;
           for (int m = 0; m < d; ++m) v[m] = cands[q].dh * orc_ld(w_down, wd0 + (int64_t)m * f + cands[q].n, is_bf16);
         }

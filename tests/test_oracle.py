@@ -534,3 +534,105 @@ def test_ffn_ex_flip_resolution_recovers_planted_roundings(orc):
     bad[3, 7] += 0.05
     with pytest.raises(AssertionError):
         tolerance.check_ffn(bad, ex)
+
+
+# ---- pins of the comparator parts: the bf16 neighbour, the fp32 bound of y, the candidate list at full width ------
+
+def test_bf16_toward_matches_torch_nextafter(orc):
+    """orc_bf16_toward_n (the bf16 value next to a bf16 value, toward a target) against torch.nextafter on bfloat16:
+    both signs, zero, subnormals, binade edges, and a target equal to the value (itself)."""
+    rng = np.random.default_rng(7)
+    v = np.concatenate([rng.normal(0, 1, 4000), rng.normal(0, 1e-3, 1000), rng.normal(0, 1e4, 1000),
+                        np.ldexp(1.0, np.arange(-130, 20)), -np.ldexp(1.0, np.arange(-130, 20)),
+                        [0.0, -0.0, 1e-40, -1e-40, 3.0e38]])
+    h = oracle.round_bf16_array(v, orc)
+    # targets on both sides of h (the oracle steps toward v; v == h returns h)
+    for tgt in (v, h + np.where(h >= 0, 1.0, -1.0) * np.abs(h) * 0.5 + 1e-45, h - np.abs(h) * 0.5 - 1e-45, h):
+        got = oracle.bf16_toward(h, tgt, orc)
+        th = torch.from_numpy(h).to(torch.bfloat16)
+        assert (th.double().numpy() == h).all()  # h is exactly representable
+        tt = torch.from_numpy(np.where(tgt > h, np.inf, np.where(tgt < h, -np.inf, h))).to(torch.bfloat16)
+        want = torch.nextafter(th, tt).double().numpy()
+        want = np.where(tgt == h, h, want)
+        np.testing.assert_array_equal(got, want)
+
+
+def _fp32_seq_matvec(h32: np.ndarray, w32: np.ndarray) -> np.ndarray:
+    """y = w h in fp32 with a plain sequential sum over the reduction index (another summation order than torch's)."""
+    terms = (w32 * h32[None, :]).astype(np.float32)       # each product rounded to fp32
+    return np.add.accumulate(terms, axis=1, dtype=np.float32)[:, -1]
+
+
+@pytest.mark.parametrize("shape", ["ragged", "wide"])
+def test_y_delta_covers_fp32_evaluations(orc, shape):
+    """The oracle's y_delta bounds how far an fp32 evaluation of y = h Wd^T can be from the exact value: two independent
+    fp32 evaluations (torch's blocked matmul and a sequential fp32 sum) of every element stay within it, and the bound
+    is far below half a bf16 step (it lets only near-midpoint roundings go either way)."""
+    if shape == "ragged":
+        s, inp, src, ex_ = _ragged_rows()
+    else:  # full width: d = 4096, f = 14336, a few rows
+        s = mi.spec("mixtral")
+        inp = mi.inputs(s)
+        src, ex_ = np.arange(0, 2048, 512).astype(np.int32), np.array([0, 1, 0, 1], np.int32)
+    ex = oracle.ffn_rows_ex(src, ex_, inp["x"], inp["w_gate_up"], inp["w_down"], True, want_h=True, lib=orc)
+    W2 = mi.bf16_bits_to_f32(inp["w_down"])
+    h32 = ex["h"].astype(np.float32)  # bf16 values, exact in fp32
+    for i in range(len(src)):
+        w = W2[ex_[i]]
+        y_t = (torch.from_numpy(w) @ torch.from_numpy(h32[i])).double().numpy()
+        y_s = _fp32_seq_matvec(h32[i], w).astype(np.float64)
+        for y32 in (y_t, y_s):
+            assert (np.abs(y32 - ex["y_unr"][i]) <= ex["y_delta"][i]).all()
+    half_step = np.ldexp(np.abs(ex["y_unr"]), -9)
+    # about 1-5% of half a step at these widths; a dropped scale or f in place of sqrt(f) would exceed 10%
+    assert np.median(ex["y_delta"] / np.maximum(half_step, 1e-30)) < 0.1
+
+
+def _silu_coarse(g: np.ndarray, rng) -> np.ndarray:
+    """silu(g) in fp32 as coarsely as the kernel may take it: exp as exp2(g * log2 e) (the product rounded to fp32),
+    and the reciprocal of 1 + e^-g off by up to one fp32 ulp either way."""
+    g = g.astype(np.float32)
+    e = np.exp2((-g * np.float32(1.4426950408889634)).astype(np.float32)).astype(np.float32)
+    den = (np.float32(1.0) + e).astype(np.float32)
+    r = (np.float32(1.0) / den).astype(np.float32)
+    nudge = rng.integers(-1, 2, size=r.shape)
+    r = np.where(nudge > 0, np.nextafter(r, np.float32(np.inf)), np.where(nudge < 0, np.nextafter(r, np.float32(0)), r))
+    return (g * r).astype(np.float32)
+
+
+@pytest.mark.parametrize("name", ["mixtral", "deepseek"])
+def test_ffn_ex_candidates_cover_coarse_fp32_at_full_width(orc, name):
+    """At the full widths (d = 4096, f = 14336; d = 7168, f = 2048): every h that an fp32 evaluation with a coarse
+    silu (exp2-based exp, reciprocal off by one ulp; the kernel's evaluation is no coarser) rounds to the other bf16
+    neighbour is in the oracle's complete list of alternatives; the capped list the comparison uses (64 per row) holds
+    the largest steps, so an alternative it leaves out moves h by no more than every one it keeps."""
+    s = mi.spec(name)
+    inp = mi.inputs(s)
+    src = np.arange(0, s.T, s.T // 6).astype(np.int32)[:6]
+    ex_ = (np.arange(len(src)) % s.E_l).astype(np.int32)
+    full = oracle.ffn_rows_ex(src, ex_, inp["x"], inp["w_gate_up"], inp["w_down"], True, max_cand=s.f, want_h=True,
+                              want_vec=False, lib=orc)
+    capped = oracle.ffn_rows_ex(src, ex_, inp["x"], inp["w_gate_up"], inp["w_down"], True, want_vec=False, lib=orc)
+    X = torch.from_numpy(mi.bf16_bits_to_f32(inp["x"])[src])
+    W1 = mi.bf16_bits_to_f32(inp["w_gate_up"])
+    rng = np.random.default_rng(3)
+    flips = 0
+    for i in range(len(src)):
+        w = torch.from_numpy(W1[ex_[i]])
+        g = (w[: s.f] @ X[i]).numpy()
+        u = (w[s.f:] @ X[i]).numpy()
+        cand = set(full["cand_n"][i, : full["cand_count"][i]].tolist())
+        for trial in range(2):
+            h32 = (_silu_coarse(g, rng) * u.astype(np.float32)).astype(np.float32)
+            hb = torch.from_numpy(h32).to(torch.bfloat16).double().numpy()
+            for n in np.nonzero(hb != full["h"][i])[0]:
+                flips += 1
+                assert n in cand, (i, n, h32[n], full["h"][i, n])
+        # the capped list: the first min(64, count) of the complete one by step size
+        step = lambda n: abs(oracle.bf16_toward(full["h"][i, n:n + 1], np.array([np.inf]), orc)[0] - full["h"][i, n])
+        kept = capped["cand_n"][i, : capped["cand_count"][i]].tolist()
+        assert capped["cand_count"][i] == min(64, full["cand_count"][i]) and set(kept) <= cand
+        if full["cand_count"][i] > 64:
+            left = cand - set(kept)
+            assert max(step(n) for n in left) <= min(step(n) for n in kept)
+    assert flips > 0
