@@ -636,3 +636,41 @@ def test_ffn_ex_candidates_cover_coarse_fp32_at_full_width(orc, name):
             left = cand - set(kept)
             assert max(step(n) for n in left) <= min(step(n) for n in kept)
     assert flips > 0
+
+
+
+def test_combine_allowance_admits_one_step_of_each_row_and_no_more(orc):
+    """The combined output's allowance (tolerance.combine_slack): an output combined from delivered rows whose elements
+    took the other neighbour of their final rounding (one bf16 step; a quarter of them here) passes the check, also
+    where the weighted sum cancels to a small value; an output off by three steps of its contributing rows, or by
+    2e-3 at a small element, fails."""
+    import tolerance
+
+    s, inp, src, ex_ = _ragged_rows()
+    idx, w = oracle.route(inp["logits"], s.k)
+    lay = oracle.layout(idx, s.R, s.T_o, s.G, s.E_l, s.k, s.M)
+    y_pad = oracle.ffn_layout(lay, inp["x"], inp["w_gate_up"], inp["w_down"], True, s.M, orc)
+    recv = oracle.deliver(lay, y_pad, s.R, s.E_l, orc)
+    out = oracle.combine(lay, w, recv, s.R, s.T_o, s.k, True, orc)
+    base = np.concatenate([[0], np.cumsum([r.shape[0] for r in recv])])
+    y_all = np.concatenate(recv)
+    plan = lay["combine_plan"].reshape(s.T, s.k)
+    slack = tolerance.combine_slack(plan, w, y_all, lambda i, j: base[i // s.T_o] + plan[i, j])
+    rng = np.random.default_rng(5)
+    # a quarter of the delivered elements one bf16 step up or down
+    moved = [r + rng.choice([-1.0, 1.0], size=r.shape) * (rng.random(r.shape) < 0.25) * tolerance.bf16_ulp(r)
+             for r in recv]
+    out_moved = oracle.combine(lay, w, moved, s.R, s.T_o, s.k, True, orc)
+    assert np.abs(out_moved - out).max() > 1e-3  # the stated bound alone would not hold everywhere
+    tolerance.check(out_moved, out, "one step per row", slack=slack)
+    moved3 = [r + 3.0 * tolerance.bf16_ulp(r) for r in recv]
+    with pytest.raises(AssertionError):
+        tolerance.check(oracle.combine(lay, w, moved3, s.R, s.T_o, s.k, True, orc), out, "three steps", slack=slack)
+    small = np.argwhere((np.abs(out) < 0.02) & (slack < 5e-4))
+    bad = out.copy()
+    bad[tuple(small[0])] += 2e-3
+    with pytest.raises(AssertionError):
+        tolerance.check(bad, out, "planted", slack=slack)
+    # the ulp helper: bf16 spacing at binade edges and below the normal range
+    np.testing.assert_array_equal(tolerance.bf16_ulp(np.array([1.0, 1.5, 2.0, -0.75, 0.0, 1e-40])),
+                                  [2.0 ** -7, 2.0 ** -7, 2.0 ** -6, 2.0 ** -8, 2.0 ** -133, 2.0 ** -133])

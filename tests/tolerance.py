@@ -7,13 +7,17 @@ ATOL = 1e-3
 NORM_RTOL = 5e-3
 
 
-def check(got, ref, what=""):
+def check(got, ref, what="", slack=None):
+    """Per element |got - ref| <= max(RTOL |ref|, ATOL) (+ slack, an allowance derived from the inputs' own admitted
+    roundings; see combine_slack), and the normwise bound."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
     assert np.isfinite(got).all(), "%s: non-finite values" % what
     err = np.abs(got - ref)
     lim = np.maximum(RTOL * np.abs(ref), ATOL)
+    if slack is not None:
+        lim = lim + slack
     bad = err > lim
     if bad.any():
         i = np.unravel_index(np.argmax(err - lim), err.shape)
@@ -79,3 +83,25 @@ def check_ffn(got, ex, what="y", is_bf16=True):
     ref, flips = resolve_flips(got, ex, is_bf16)
     check(got, ref, what + " (%d alternative h roundings)" % flips)
     return ref, flips
+
+
+def bf16_ulp(v):
+    """The spacing of bf16 values at |v| (the step of v's binade; 2^-133 below the normal range)."""
+    v = np.abs(np.asarray(v, dtype=np.float64))
+    e = np.floor(np.log2(np.where(v > 0, v, 1.0)))
+    return np.where(v > 0, np.ldexp(1.0, np.maximum(e - 7, -133).astype(int)), np.ldexp(1.0, -133))
+
+
+def combine_slack(plan, w, y_rows, row_of):
+    """The combined output's allowance beyond the stated tolerance: each delivered y element is a correct result up to
+    one step of its own final bf16 rounding (near a rounding midpoint either neighbour is, as for h; and the
+    alternatives the comparison of y does not list can carry y across such a midpoint), so the weighted sum may differ
+    by sum_j |w_j| ulp(y_j).  plan [n, k] (>= 0 for local slots), w [n, k], y_rows [m, d] the reference rows,
+    row_of(i, j) the index into y_rows of token i's slot j."""
+    n, k = plan.shape
+    out = np.zeros((n, y_rows.shape[1]))
+    for i in range(n):
+        for j in range(k):
+            if plan[i, j] >= 0:
+                out[i] += abs(float(w[i, j])) * bf16_ulp(y_rows[row_of(i, j)])
+    return out
