@@ -169,7 +169,7 @@ def main():
     ap.add_argument("--config", default="deepseek")
     ap.add_argument("--consumer-cus", type=int, default=0,
                     help="consumer CUs of the overlapped launch (0 = the launch picks them from the batch's routing "
-                         "and the rates it observed)")
+                         "and the rates it observed, 0 included; -1 = none: the return at the launch's tail)")
     ap.add_argument("--mgb", type=int, default=1)
     ap.add_argument("--band-window", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -178,6 +178,9 @@ def main():
     ap.add_argument("--mode", type=int, default=0, choices=(0, 1, 3),
                     help="FFN mode of the timed steps: 0 overlapped, 1 sequential (the consumer alone after the "
                          "producer, for profiling the copy), 3 the return on the DMA engines")
+    ap.add_argument("--land", type=int, default=1, choices=(0, 1),
+                    help="where x_pad's token rows come from: 1 (default) the FFN launch lands them itself, row tile "
+                         "by row tile, while its first GEMM starts; 0 the layout's gather kernel")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this path runs on a single MI355X (the owner ranks are receive buffers in "
@@ -204,9 +207,12 @@ def main():
     # consumer_cus = 0: every overlapped launch picks its partition from the batch's routing and observed rates
     cus = args.consumer_cus
 
+    land = args.land == 1 and s.dtype == "bf16" and args.mode in (0, 1)
+
     def step(mode=0, timestamps=False):
-        P.layout(dev["x"])
-        P.ffn(w1, w2, mode=mode, consumer_cus=cus, band_window=args.band_window, timestamps=timestamps)
+        P.layout(None if land else dev["x"])
+        P.ffn(w1, w2, mode=mode, consumer_cus=cus, band_window=args.band_window, timestamps=timestamps,
+              x_tokens=dev["x"] if land else None)
         P.combine()
 
     for _ in range(args.warmup):
@@ -241,13 +247,13 @@ def main():
         return
 
     # FFN call alone, overlapped and sequential (events on the caller stream around the call)
-    def time_ffn(mode, reps):
+    def time_ffn(mode, reps, xt=None):
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        P.ffn(w1, w2, mode=mode, consumer_cus=cus, band_window=args.band_window)
+        P.ffn(w1, w2, mode=mode, consumer_cus=cus, band_window=args.band_window, x_tokens=xt)
         ts = []
         for _ in range(reps):
             ev0.record()
-            P.ffn(w1, w2, mode=mode, consumer_cus=cus, band_window=args.band_window)
+            P.ffn(w1, w2, mode=mode, consumer_cus=cus, band_window=args.band_window, x_tokens=xt)
             ev1.record()
             ev1.synchronize()
             ts.append(ev0.elapsed_time(ev1))
@@ -255,6 +261,7 @@ def main():
 
     reps = max(5, args.steps)
     t_ovl = time_ffn(0, reps)
+    t_land = time_ffn(0, reps, dev["x"]) if land else None
     part = P.partition_record() if s.dtype == "bf16" else (cus, 0.0, 0.0, False)
     t_seq = time_ffn(1, reps)
     t_dma = time_ffn(3, max(3, reps // 4)) if s.dtype == "bf16" else None
@@ -292,15 +299,20 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": s.dtype, "data": "synthetic",
         "config": {"workload": workload_name(s), "M_real": M_real, "M_returned": M_ret, "M_pad": M_pad,
-                   "gemm_row_tiles": sc["n_mtiles"], "consumer_cus": args.consumer_cus or part[0],
+                   "gemm_row_tiles": sc["n_mtiles"],
+                   # 0: no consumer partition (every workgroup takes copy units once its items are done)
+                   "consumer_cus": max(args.consumer_cus, 0) if args.consumer_cus else part[0],
                    "consumer_cus_chosen_by": "option" if args.consumer_cus else "the launch (routing + observed rates)",
                    "band_window": args.band_window or 4, "producer_order": "remote first",
+                   "token_rows_landed_by": "the FFN launch" if land else "the layout's gather kernel",
                    "mode": {0: "overlapped", 1: "sequential", 3: "DMA return"}[args.mode]},
         "pct_bf16_peak_step": round(100 * value / peak, 2),
         "ffn_tflops_overlapped": round(ffn_tflops, 2),
         "pct_bf16_peak_ffn": round(100 * ffn_tflops / peak, 2),
         "overlap_ratio_pct": round(100 * ratio, 2),
         "ffn_ms_overlapped": [round(v, 4) for v in t_ovl],
+        # the FFN call that also lands the token rows (the timed steps' form when the launch lands them)
+        "ffn_ms_overlapped_landing": [round(v, 4) for v in t_land] if t_land else None,
         "ffn_ms_sequential": [round(v, 4) for v in t_seq],
         "speedup_seq_over_ovl": round(t_seq[0] / t_ovl[0], 4),
         "copy_ms_sequential": round(copy_seq_ms, 4),

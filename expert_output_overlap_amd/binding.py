@@ -45,7 +45,7 @@ class moe_layout(ctypes.Structure):
 class moe_overlap_cfg(ctypes.Structure):
     _fields_ = [("consumer_cus", ctypes.c_int32), ("mode", ctypes.c_int32), ("epoch", ctypes.c_uint32),
                 ("band_window", ctypes.c_int32), ("watchdog_ticks", ctypes.c_uint64),
-                ("timestamps", ctypes.c_void_p), ("tile_order", ctypes.c_int32)]
+                ("timestamps", ctypes.c_void_p), ("tile_order", ctypes.c_int32), ("x_tokens", ctypes.c_void_p)]
 
 
 class MoeError(RuntimeError):

@@ -243,7 +243,7 @@ int moe_layout_build(const moe_shape* s, const int32_t* topk_idx, const void* x,
   if (!e.empty()) return fail(MOE_EINVAL, e);
   if (!layout_ok(L)) return fail(MOE_EINVAL, "layout not bound");
   const int64_t T = (int64_t)s->R * s->tokens_per_owner;
-  if (T > 0 && (!topk_idx || !x || !x_pad)) return fail(MOE_EINVAL, "null pointer");
+  if (T > 0 && (!topk_idx || (x && !x_pad))) return fail(MOE_EINVAL, "null pointer");
   if (L->cap_tiles * s->tile_m != L->cap_rows) return fail(MOE_EINVAL, "layout bound for another tile_m");
   LayoutLaunch p;
   p.topk_idx = topk_idx;
@@ -444,14 +444,19 @@ int ffn_overlap(const moe_shape* s, const moe_layout* L, const void* x_pad, cons
     return fail(MOE_EINVAL, "mode 3 (return on the DMA engines) is for bf16 with a flag workspace");
   if (cfg->band_window < 0) return fail(MOE_EINVAL, "band_window must be >= 0");
   if (cfg->tile_order != 0 && cfg->tile_order != 1) return fail(MOE_EINVAL, "tile_order must be 0 or 1");
+  if (cfg->x_tokens && (s->dtype != MOE_BF16 || (cfg->mode != 0 && cfg->mode != 1)))
+    return fail(MOE_EINVAL, "x_tokens (rows landed by the launch) is for bf16 in mode 0 or 1");
   hipStream_t st = (hipStream_t)stream;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(MOE_EHIP, "hipGetDevice failed");
   const int n_cu = device_cus(dev);
   if (n_cu <= 0) return fail(MOE_EHIP, "cannot query the CU count");
-  if (cfg->consumer_cus < 0 || cfg->consumer_cus > n_cu / 2)
-    return fail(MOE_EINVAL, "consumer_cus must be 0 (library pick) or in [1, CUs/2]");
-  const int C = cfg->consumer_cus ? cfg->consumer_cus : moe_pick_consumer_cus(s, n_cu);
+  if (cfg->consumer_cus < -1 || cfg->consumer_cus > n_cu / 2)
+    return fail(MOE_EINVAL, "consumer_cus must be -1 (none), 0 (library pick) or in [1, CUs/2]");
+  if (cfg->consumer_cus == -1 && (s->dtype != MOE_BF16 || (cfg->mode != 0 && cfg->mode != 1)))
+    return fail(MOE_EINVAL, "consumer_cus = -1 (no consumer partition) is for bf16 in mode 0 or 1");
+  // a partition for the launches that need one: the return alone (mode 2), fp32, a fixed bf16 choice
+  const int C = cfg->consumer_cus > 0 ? cfg->consumer_cus : std::max(1, moe_pick_consumer_cus(s, n_cu));
   if (C < 1) return fail(MOE_EINVAL, "no consumer partition fits this device");
   if (flags == nullptr) {  // the allocation-free variant: flags in the library's scratch array, cleared per call
     if (cfg->mode == 2) return fail(MOE_EINVAL, "mode 2 (return only) needs the flags of an earlier call");
@@ -485,6 +490,8 @@ int ffn_overlap(const moe_shape* s, const moe_layout* L, const void* x_pad, cons
   p.epoch = cfg->epoch;
   p.band_window = cfg->band_window;
   p.tile_order = cfg->tile_order;
+  p.x_tokens = cfg->x_tokens;
+  p.join = cfg->mode == 0 && s->dtype == MOE_BF16;
   p.watchdog_ticks = cfg->watchdog_ticks ? cfg->watchdog_ticks : 200000000ull;
   p.timestamps = cfg->timestamps;
   p.cap_mtiles = layout_offsets(s).cap_mtiles;
@@ -532,7 +539,11 @@ int ffn_overlap(const moe_shape* s, const moe_layout* L, const void* x_pad, cons
   // producers on the other CUs, each joining the return once its items are done; sequential: producers on
   // every CU, then the return on every CU
   // overlapped bf16 with consumer_cus = 0: the launch picks its own partition (ffn_adaptive_consumers)
-  const int n_cons = cfg->mode != 0 ? 0 : (cfg->consumer_cus == 0 && p.dtype == MOE_BF16 ? -1 : C);
+  // bf16 with consumer_cus = -1: no partition, the return runs at the launch's tail
+  const int n_cons = cfg->mode != 0 ? 0
+                     : p.dtype != MOE_BF16 ? C
+                     : cfg->consumer_cus == 0 ? -1
+                     : cfg->consumer_cus < 0 ? 0 : C;
   next_pair();
   if (launch_ffn_producer(p, n_cu, p.dtype == MOE_BF16 ? n_cons : 0, st, ev0, ev1))
     return failed("producer launch failed");
@@ -579,7 +590,7 @@ int moe_ffn_schedule(const moe_shape* s, int32_t n_cu, const moe_overlap_cfg* cf
     return fail(MOE_EINVAL, "bad arguments");
   if (n_mtiles > 0 && (!mt_hdr || !mt_order)) return fail(MOE_EINVAL, "null pointer");
   if (cfg->mode != 0 && cfg->mode != 1) return fail(MOE_EINVAL, "mode must be 0 or 1");
-  if (cfg->consumer_cus < 0 || cfg->consumer_cus > n_cu / 2 || cfg->band_window < 0 ||
+  if (cfg->consumer_cus < -1 || cfg->consumer_cus > n_cu / 2 || cfg->band_window < 0 ||
       (cfg->tile_order != 0 && cfg->tile_order != 1))
     return fail(MOE_EINVAL, "consumer_cus, band_window or tile_order out of range");
   std::vector<int32_t> ident;
@@ -595,7 +606,8 @@ int moe_ffn_schedule(const moe_shape* s, int32_t n_cu, const moe_overlap_cfg* cf
         mt_order[i] >= n_mtiles)
       return fail(MOE_EINVAL, "row-tile headers or order out of range");
   }
-  const int C = cfg->mode == 0 ? (cfg->consumer_cus ? cfg->consumer_cus : moe_pick_consumer_cus(s, n_cu)) : 0;
+  const int C = cfg->mode != 0 || cfg->consumer_cus < 0 ? 0
+                : cfg->consumer_cus > 0 ? cfg->consumer_cus : moe_pick_consumer_cus(s, n_cu);
   if (ffn_schedule_host(s->d, s->f, s->num_local_experts, C, n_cu - C, cfg->band_window, n_mtiles, n_remote_mtiles,
                         mt_hdr, mt_order, items, cap, n_items))
     return items == nullptr && cap == 0 ? MOE_OK : fail(MOE_EINVAL, "cap is below the list length");

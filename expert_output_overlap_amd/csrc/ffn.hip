@@ -360,8 +360,16 @@ struct FusedArgs {
   uint64_t budget;
   uint64_t* ts;
   int n_cons;      // consumer workgroups; -1: picked by the launch (ffn_adaptive_consumers)
+  int join;        // the launch runs the return: every workgroup takes copy units once its own items are done
   int E;           // local experts (the interleave rule, when the launch picks the partition)
   uint32_t* obs;   // the partition record (MOE_OBS_WORDS words, see obs_*), or null
+  // dispatch landing inside the launch (xtok non-null): the token rows of x_pad are copied here, row tile by row tile
+  const unsigned char* xtok;  // token rows X [T, d]
+  const int32_t* row_src;     // padded row -> token row
+  uint32_t* flags0;           // [cap_mtiles]: the row tile's input rows have landed
+  uint64_t* gcount;           // [cap_mtiles]: landed units of the row tile (epoch << 32 | count)
+  uint64_t* gclaim;           // landing units handed out: stamp << 32 | count
+  uint32_t gstamp;
   ConsumerArgs cons;
   unsigned char* self_recv;  // the self owner's buffer: y rows of the self-owned groups go straight there
 };
@@ -370,7 +378,7 @@ struct FusedArgs {
 // workgroups (the last one resets it; a call that fails leaves a count the next calls absorb), [2] ~(first producer item start), [4] last producer item end, [6] bytes the
 // consumer role copied, [8] its copy ticks summed over workgroups; [10] producers' flops per CU-tick and [11]
 // consumers' bytes per CU-tick (fp32, running estimates from earlier calls), [12] the partition of the last call,
-// [13] nonzero once [10] and [11] hold observations.
+// [13] bit 0 / bit 1 set once [10] / [11] hold observations.
 __device__ __forceinline__ unsigned long long* obs64(uint32_t* obs, int w) { return (unsigned long long*)(obs + w); }
 
 // All threads of the workgroup: wait until the n flags equal epoch, then acquire (compiler ordering; see the
@@ -794,6 +802,112 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
   return true;
 }
 
+// ---- dispatch landing inside the launch ---------------------------------------------------------------------
+// The first all-to-all lands token rows in x_pad (review page, "Where Pith is reading between the lines": the same
+// tile signalling applied to the dispatch).  With x_tokens given, the launch copies them itself: units of LAND_ROWS
+// rows of one row tile, numbered in the order the first GEMM needs its row tiles, handed out from a stamped counter
+// like the return's copy units.  A unit's rows go out with device-coherent stores; once they have completed the
+// unit counts itself in at its row tile, and the unit that completes the tile publishes the tile's input flag.  A
+// first-GEMM item waits for its row tile's flag and takes landing units itself while it waits; the consumer
+// workgroups, once done with their own first-GEMM items, land what is left, so the copy runs ahead of the producers
+// while the consumers would otherwise wait for the first finished segment.  (The consumers landing everything before
+// their own first-GEMM items held up the second GEMM of the first row tiles: 0.4 ms more on a 2.3 ms launch.)
+#define LAND_ROWS 32
+#define LAND_DEPTH 8  // 16-byte loads in flight per thread
+#define LAND_UNITS_PER_TILE (MOE_MT_ROWS / LAND_ROWS)
+
+// One landing unit u (row tile mt_of(u / LAND_UNITS_PER_TILE), its rows [sub * LAND_ROWS, ...)).  All threads.
+__device__ void land_unit(const FusedArgs& a, int mt, int sub, int* s_p, int* s_t) {
+  const int tid = threadIdx.x;
+  const int32_t* dsc = a.mtile_desc + (int64_t)mt * MOE_MT_FIELDS;
+  const int n_rows = dsc[1], r0 = sub * LAND_ROWS, nr = min(LAND_ROWS, n_rows - r0);
+  __syncthreads();  // s_p / s_t of the previous unit are no longer read
+  if (tid < nr) {
+    const int p = dsc[MOE_MT_HDR + r0 + tid];
+    s_p[tid] = p;
+    s_t[tid] = a.row_src[p];
+  }
+  __syncthreads();
+  const int row_vec = a.d * 2 / 16;
+  const int64_t row_bytes = (int64_t)a.d * 2;
+  unsigned char* xp = (unsigned char*)a.x;
+  const int n = nr > 0 ? nr * row_vec : 0;
+  int i = tid;
+  for (; i + (LAND_DEPTH - 1) * FFN_THREADS < n; i += LAND_DEPTH * FFN_THREADS) {  // LAND_DEPTH loads in flight
+    u32x4_t v[LAND_DEPTH];
+#pragma unroll
+    for (int k = 0; k < LAND_DEPTH; ++k) {
+      const int j = i + k * FFN_THREADS, r = j / row_vec, c = j - r * row_vec;
+      v[k] = *(const u32x4_t*)(a.xtok + (int64_t)s_t[r] * row_bytes + c * 16);
+    }
+#pragma unroll
+    for (int k = 0; k < LAND_DEPTH; ++k) {
+      const int j = i + k * FFN_THREADS, r = j / row_vec, c = j - r * row_vec;
+      store16_coherent(xp + (int64_t)s_p[r] * row_bytes + c * 16, v[k]);
+    }
+  }
+  for (; i < n; i += FFN_THREADS) {
+    const int r = i / row_vec, c = i - r * row_vec;
+    store16_coherent(xp + (int64_t)s_p[r] * row_bytes + c * 16,
+                     *(const u32x4_t*)(a.xtok + (int64_t)s_t[r] * row_bytes + c * 16));
+  }
+  wait_stores();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();  // every thread's stores of the unit have completed
+  if (tid == 0 && (int)arrive(&a.gcount[mt], a.epoch) == LAND_UNITS_PER_TILE - 1)
+    __hip_atomic_store(&a.flags0[mt], a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Takes the next landing unit and lands it; false once every unit has been handed out (or the stamp never came).
+// All threads; s_u is workgroup-shared.
+template <typename OrderOf>
+__device__ bool land_next(const FusedArgs& a, int n_mt, OrderOf mt_of, int* s_u, int* s_p, int* s_t) {
+  __syncthreads();  // s_u of the previous call has been read
+  if (threadIdx.x == 0) {
+    const uint64_t t0 = moe_clock();
+    int u = -1;
+    while ((uint32_t)(__hip_atomic_load(a.gclaim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 32) != a.gstamp) {
+      if (moe_clock() - t0 > a.budget) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if ((uint32_t)(__hip_atomic_load(a.gclaim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 32) == a.gstamp)
+      u = (int)(uint32_t)__hip_atomic_fetch_add(a.gclaim, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_u = u;
+  }
+  __syncthreads();
+  const int u = *s_u;
+  if (u < 0 || u >= n_mt * LAND_UNITS_PER_TILE) return false;
+  land_unit(a, mt_of(u / LAND_UNITS_PER_TILE), u % LAND_UNITS_PER_TILE, s_p, s_t);
+  return true;
+}
+
+// A first-GEMM item's wait for its row tile's input rows: lands units while they last, else spins (spin budget).
+template <typename OrderOf>
+__device__ bool wait_landed(const FusedArgs& a, int mt, int n_mt, OrderOf mt_of, int* s_u, int* s_p, int* s_t,
+                            int* s_stop) {
+  const uint64_t t0 = moe_clock();
+  bool more = true;
+  for (;;) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const bool ok = __hip_atomic_load(&a.flags0[mt], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch;
+      *s_stop = ok ? 3 : ((moe_clock() - t0 > a.budget) ? 1 : (load_status(a.status) != 0 ? 2 : 0));
+    }
+    __syncthreads();
+    const int st = *s_stop;
+    if (st == 3) break;
+    if (st != 0) {
+      if (st == 1 && threadIdx.x == 0) set_status(a.status, MOE_ETIMEOUT);
+      return false;
+    }
+    if (more) more = land_next(a, n_mt, mt_of, s_u, s_p, s_t);
+    else __builtin_amdgcn_s_sleep(2);
+  }
+  flag_acquire();  // the rows were written by this launch (the publish protocol in common.h)
+  __syncthreads();  // every thread has read s_stop before the item's own waits write it
+  return true;
+}
+
 template <int BN1, int BN2>
 __global__ __launch_bounds__(FFN_THREADS, 1) void k_ffn_bf16(FusedArgs a) {
   constexpr int BM = 256, BK = 64, BNX = BN1 > BN2 ? BN1 : BN2;
@@ -805,6 +919,7 @@ __global__ __launch_bounds__(FFN_THREADS, 1) void k_ffn_bf16(FusedArgs a) {
   __shared__ int s_stop;
   __shared__ uint32_t* s_pend;  // flag of the previous item, published once its stores have completed
   __shared__ int s_pend_y;
+  __shared__ int s_land_u, s_land_p[LAND_ROWS], s_land_t[LAND_ROWS];
 
   launch_acquire();  // drop cache lines older than this launch (the publish protocol in common.h)
   if (load_status(a.status) != 0) return;
@@ -818,12 +933,15 @@ __global__ __launch_bounds__(FFN_THREADS, 1) void k_ffn_bf16(FusedArgs a) {
   }
   int C = a.n_cons, interleave = a.interleave;
   if (C < 0) {  // the launch picks its consumer partition: every workgroup computes the same value
-    const float fr = a.obs[13] ? __uint_as_float(a.obs[10]) : 0.f, cr = a.obs[13] ? __uint_as_float(a.obs[11]) : 0.f;
+    // a rate never observed reads 0 (the buffer starts zeroed) and the rule takes its default
+    const float fr = (a.obs[13] & 1) ? __uint_as_float(a.obs[10]) : 0.f, cr = (a.obs[13] & 2) ? __uint_as_float(a.obs[11]) : 0.f;
     C = ffn_adaptive_consumers(gridDim.x, m_real, m_real - m_self, a.d, a.f, fr, cr);
     interleave = ffn_interleave(C, a.d, a.f, a.E);
     if (blockIdx.x == 0 && threadIdx.x == 0) a.obs[12] = (uint32_t)C;
   }
-  if (C > 0 && blockIdx.x == 0) consumer_stamp(a.cons);
+  if (a.join && blockIdx.x == 0) consumer_stamp(a.cons);
+  if (a.xtok != nullptr && blockIdx.x == 0 && threadIdx.x == 0)  // open the landing counter for this launch
+    __hip_atomic_store(a.gclaim, (uint64_t)a.gstamp << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int tid = threadIdx.x;
   if (tid == 0) s_pend = nullptr;
   // every wave's stores of the previous item have completed, then its flag (a wait on it may come next)
@@ -851,6 +969,8 @@ __global__ __launch_bounds__(FFN_THREADS, 1) void k_ffn_bf16(FusedArgs a) {
     *rc = d[3];
   };
   auto order = [&](int p) { return a.mt_order ? (int)a.mt_order[p] : p; };
+  // the order in which the first GEMM needs its row tiles: by number (GEMM1 first), by position (interleaved)
+  auto land_of = [&](int k) { return interleave ? order(k) : k; };
   bool first = true;
   auto run = [&](int idx) {  // one item of the list; false once the launch has failed
     __syncthreads();  // previous item done with LDS and the header
@@ -869,8 +989,11 @@ __global__ __launch_bounds__(FFN_THREADS, 1) void k_ffn_bf16(FusedArgs a) {
     __syncthreads();
     flush();
     const int e = __builtin_amdgcn_readfirstlane(s_hdr[0]), n_rows = __builtin_amdgcn_readfirstlane(s_hdr[1]);
-    if (it.kind == 1)
+    if (it.kind == 1) {
+      if (a.xtok != nullptr && !wait_landed(a, it.mt, n_mt, land_of, &s_land_u, s_land_p, s_land_t, &s_stop))
+        return false;
       return ffn_tile<BN1, true>(a, smem, s_rows, s_hdr, e, n_rows, it.mt, it.nt, 0, 0, 1, -1, &s_stop, &s_pend, &s_pend_y);
+    }
     // the h columns this split reads: column tiles [s, s+1) * n_nt1 / S of the first GEMM
     const int per = a.n_nt1 / a.S;
     if (!wait_flags(a.flags1 + (int64_t)it.mt * a.n_nt1 + it.s * per, per, a.epoch, a.budget, a.status, &s_stop))
@@ -895,9 +1018,15 @@ __global__ __launch_bounds__(FFN_THREADS, 1) void k_ffn_bf16(FusedArgs a) {
     if (!run(item)) return;
   __syncthreads();
   flush();
+  // the consumer workgroups, done with their share of first-GEMM items (none when interleaved), land the token
+  // rows that are left, ahead of the producers, until every unit is handed out; then they return segments
+  if (a.xtok != nullptr && (int)blockIdx.x < C)
+    while (land_next(a, n_mt, land_of, &s_land_u, s_land_p, s_land_t)) {
+    }
   if (a.obs != nullptr && tid == 0 && !first) atomicMax(obs64(a.obs, 4), (unsigned long long)moe_clock());
-  // then every workgroup returns segments until no copy unit is left
-  if (C > 0) consumer_role(a.cons);
+  // then every workgroup returns segments until no copy unit is left (with no consumer partition, the return is
+  // the tail of the launch: workgroups take copy units as they run out of items)
+  if (a.join) consumer_role(a.cons);
   // the last workgroup to finish folds this call's rates into the record (an error on the way leaves it as it was)
   if (a.obs != nullptr) {
     __syncthreads();
@@ -906,19 +1035,18 @@ __global__ __launch_bounds__(FFN_THREADS, 1) void k_ffn_bf16(FusedArgs a) {
     if (tid == 0 && atomicAdd(obs64(a.obs, 0), 1ull) == (unsigned long long)gridDim.x - 1) {
       auto ld = [&](int w) { return __hip_atomic_load(obs64(a.obs, w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
       const unsigned long long s_inv = ld(2), e = ld(4), bytes = ld(6), ticks = ld(8);
-      const bool valid = a.obs[13] != 0;
-      float fr = __uint_as_float(a.obs[10]), cr = __uint_as_float(a.obs[11]);
+      float fr = (a.obs[13] & 1) ? __uint_as_float(a.obs[10]) : 0.f, cr = (a.obs[13] & 2) ? __uint_as_float(a.obs[11]) : 0.f;
       if (s_inv != 0 && e > ~s_inv && G > 0) {
         const float nf = (float)(6.0 * (double)m_real * a.d * (double)a.f / ((double)(e - ~s_inv) * G));
-        fr = valid && fr > 0.f ? 0.5f * (fr + nf) : nf;
+        fr = fr > 0.f ? 0.5f * (fr + nf) : nf;
       }
-      if (ticks > 0 && bytes > 0) {
+      if (ticks > 0 && bytes > 0 && C > 0) {  // a consumer CU's rate (a tail return shares the chip's bandwidth)
         const float nc = (float)((double)bytes / (double)ticks);
-        cr = valid && cr > 0.f ? 0.5f * (cr + nc) : nc;
+        cr = cr > 0.f ? 0.5f * (cr + nc) : nc;
       }
       a.obs[10] = __float_as_uint(fr);
       a.obs[11] = __float_as_uint(cr);
-      a.obs[13] = (fr > 0.f && cr > 0.f) ? 1u : 0u;
+      a.obs[13] = (fr > 0.f ? 1u : 0u) | (cr > 0.f ? 2u : 0u);  // which rates hold observations
       for (int w = 0; w < 10; w += 2) __hip_atomic_store(obs64(a.obs, w), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -961,7 +1089,7 @@ int ffn_splits(int dtype, int d, int f) {
 
 namespace {
 struct FlagCarve {
-  int64_t flags2, flags1, scount, partial, claim, obs, total;  // offsets and size in 4-byte words
+  int64_t flags2, flags1, scount, partial, claim, flags0, gcount, gclaim, obs, total;  // 4-byte words
 };
 FlagCarve flag_carve(int dtype, int d, int f, int64_t cap_mtiles) {
   FlagCarve c;
@@ -978,7 +1106,14 @@ FlagCarve flag_carve(int dtype, int d, int f, int64_t cap_mtiles) {
     c.partial = c.scount + up(2 * cap_mtiles * n2);  // split counts; also the halves of unsplit tiles
     c.claim = c.partial + (S > 1 ? cap_mtiles * n2 * S * (int64_t)BF_BM * ffn_gemm2_bn(dtype, d) : 0);
   }
-  c.obs = c.claim + 2;  // after the consumer's 64-bit unit counter (bf16: the partition record)
+  if (dtype == MOE_BF16) {  // the dispatch landing: tile flags, per-tile unit counts, the unit counter
+    c.flags0 = c.claim + 2;
+    c.gcount = c.flags0 + up(cap_mtiles);
+    c.gclaim = c.gcount + up(2 * cap_mtiles);
+    c.obs = c.gclaim + 2;  // the partition record, last
+  } else {
+    c.flags0 = c.gcount = c.gclaim = c.obs = c.claim + 2;
+  }
   c.total = c.obs + (dtype == MOE_BF16 ? MOE_OBS_WORDS : 0);
   return c;
 }
@@ -1062,8 +1197,15 @@ int launch_bf16(const FfnLaunch& p, int grid, int n_cons, hipStream_t st, hipEve
   a.budget = p.watchdog_ticks;
   a.ts = p.timestamps;
   a.n_cons = n_cons;
+  a.join = p.join;
   a.E = p.E;
   a.obs = p.item_end >= 0 ? nullptr : p.flags + fc.obs;  // a chunk of the list observes no whole-call rate
+  a.xtok = (const unsigned char*)p.x_tokens;
+  a.row_src = p.L->row_src;
+  a.flags0 = p.flags + fc.flags0;
+  a.gcount = (uint64_t*)(p.flags + fc.gcount);
+  a.gclaim = (uint64_t*)(p.flags + fc.gclaim);
+  a.gstamp = next_stamp();
   fill_consumer(a.cons, p, a.n_nt2);
   a.cons.obs = a.obs;
   a.self_recv = (unsigned char*)p.recv[p.self_rank];
@@ -1201,9 +1343,11 @@ int launch_flags_clear(int dtype, int d, int f, int64_t cap_mtiles, uint32_t* fl
   const FlagCarve c = flag_carve(dtype, d, f, cap_mtiles);
   const int64_t blocks = std::min<int64_t>((c.partial + 255) / 256, 1024);
   if (c.partial > 0) hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(256), 0, st, flags, c.partial);
-  // the copy-unit counter, and the partition record's arrival counter and per-call sums (its running rate estimates
-  // stay)
-  hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(64), 0, st, flags + c.claim, (int64_t)(dtype == MOE_BF16 ? 12 : 2));
+  // the copy-unit counter, the dispatch landing's flags and counters, and the partition record's arrival counter
+  // and per-call sums (its running rate estimates stay)
+  const int64_t tail = (dtype == MOE_BF16 ? c.obs + 10 : c.claim + 2) - c.claim;  // up to the record's estimates
+  hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)std::min<int64_t>((tail + 255) / 256, 1024)), dim3(256), 0, st,
+                     flags + c.claim, tail);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -31,6 +31,8 @@ struct FfnLaunch {
   uint32_t epoch;
   int band_window;
   int tile_order;  // 0: remote first (the layout's mt_order), 1: row-tile numbering
+  int join = 0;  // bf16: the producer launch runs the return too (overlapped mode)
+  const void* x_tokens = nullptr;  // bf16: token rows; non-null: the launch lands x_pad's rows itself
   int item_begin = 0, item_end = -1;  // bf16: run list indices [item_begin, item_end) only (GEMM1 first, no
                                       // half-width round); item_end < 0: the whole list
   uint64_t watchdog_ticks;

@@ -648,7 +648,7 @@ int launch_layout(const LayoutLaunch& p, hipStream_t st) {
   const int row_vec = (int)(p.row_bytes / 16);
   int64_t blocks = (p.L->cap_rows + 3) / 4;
   if (blocks > 4096) blocks = 4096;
-  if (blocks > 0)
+  if (blocks > 0 && p.x != nullptr)  // no x: the FFN launch lands the rows itself
     hipLaunchKernelGGL(k_gather_rows, dim3((unsigned)blocks), dim3(256), 0, st, (const uint4*)p.x, (uint4*)p.x_pad,
                        p.L->row_src, p.L->scalars, row_vec, p.L->status);
   return hipGetLastError() == hipSuccess ? 0 : -1;

@@ -67,16 +67,18 @@ class MoePath:
     def route(self, logits: torch.Tensor, stream=None):
         B.moe_route(self.shape, logits, self.topk_idx, self.topk_w, stream)
 
-    def layout(self, x: torch.Tensor, topk_idx: torch.Tensor | None = None, stream=None):
+    def layout(self, x: torch.Tensor | None, topk_idx: torch.Tensor | None = None, stream=None):
+        """x None: no gather into x_pad (the FFN call lands the rows, ``ffn(x_tokens=...)``)."""
         B.moe_layout_build(self.shape, self.topk_idx if topk_idx is None else topk_idx, x, self.L, self.x_pad, stream)
 
     def ffn(self, w_gate_up, w_down, mode=0, consumer_cus=0, band_window=0, timestamps=False, watchdog_ticks=0,
-            epoch=None, tile_order=0, stream=None):
+            epoch=None, tile_order=0, x_tokens: torch.Tensor | None = None, stream=None):
         if epoch is None:
             self.epoch += 1
             epoch = self.epoch
         cfg = B.moe_overlap_cfg(consumer_cus, mode, epoch, band_window, watchdog_ticks,
-                                self.timestamps.data_ptr() if timestamps else None, tile_order)
+                                self.timestamps.data_ptr() if timestamps else None, tile_order,
+                                None if x_tokens is None else x_tokens.data_ptr())
         B.moe_expert_ffn_overlap(self.shape, self.L, self.x_pad, w_gate_up, w_down, self.h, self.y_pad, self.recv,
                                  self.flags, cfg, stream)
         return epoch
@@ -86,12 +88,12 @@ class MoePath:
 
     def partition_record(self):
         """The launch's consumer-partition record (bf16): (consumer CUs of the last overlapped call, observed producer
-        flops per CU-tick, observed consumer bytes per CU-tick, whether the rates hold observations)."""
+        flops per CU-tick, observed consumer bytes per CU-tick, whether both rates hold observations)."""
         import struct
 
         w = self.flags[-B.MOE_OBS_WORDS:].cpu().numpy().astype("<i4").view("<u4")
         f = lambda v: struct.unpack("<f", struct.pack("<I", int(v)))[0]
-        return int(w[12]), f(w[10]), f(w[11]), bool(w[13])
+        return int(w[12]), f(w[10]), f(w[11]), int(w[13]) == 3
 
     def status(self, stream=None) -> int:
         return B.moe_read_status(self.L, stream)

@@ -100,8 +100,10 @@ typedef struct {
 /* Knobs of moe_expert_ffn_overlap. */
 typedef struct {
   int32_t consumer_cus;    /* C: consumer workgroups, one per CU, in [1, CUs/2]; the producer's persistent
-                              launch runs one workgroup on each other CU.  0 = the launch picks C from the
-                              batch's routing and observed rates (see moe_pick_consumer_cus) */
+                              launch runs one workgroup on each other CU.  0 = the launch picks C (0 included)
+                              from the batch's routing and observed rates (see moe_pick_consumer_cus); -1 (bf16,
+                              mode 0) = none: every workgroup produces, and takes copy units once its items are
+                              done, so the return runs at the launch's tail */
   int32_t mode;            /* 0 = overlapped (the C consumer workgroups and the producer workgroups in one
                                   launch, on disjoint CUs; a producer workgroup joins the return once its
                                   own items are done),
@@ -130,6 +132,11 @@ typedef struct {
                               tile holding another owner's row before every row tile of self-owned rows only; the
                               review page's "Core claim"), 1 = row-tile numbering (each expert's rows together,
                               its self-owned rows last) */
+  const void* x_tokens;    /* optional (device) [T, d] bf16 token rows, modes 0 and 1: the launch lands x_pad's real
+                              rows itself (x_pad[p] = x_tokens[row_src[p]]), row tile by row tile in the order its
+                              first GEMM needs them, each row tile's first-GEMM items waiting for that tile's rows
+                              (review page, "Where Pith is reading between the lines": the dispatch side of the same
+                              tile signalling).  For a layout built with x == NULL; NULL: x_pad already holds them */
 } moe_overlap_cfg;
 
 /* Last host-side error message of the calling thread ("" if none). */
@@ -162,7 +169,8 @@ int moe_layout_bind(const moe_shape* s, void* workspace, int64_t workspace_bytes
  * 1 restating Algorithm 1): histogram of (expert, owner) groups, prefix scans and metadata, stable
  * scatter (rows of a group ascend by token), and the gather of token rows into x_pad.
  * topk_idx (device) int32 [T, k]; x (device) [T, d] in s->dtype; x_pad (device) [cap_rows, d].
- * Padding rows of x_pad are not written.  Resets the status word to MOE_OK first; sets MOE_ECAPACITY if
+ * Padding rows of x_pad are not written.  x == NULL skips the gather (x_pad is then not used and may be NULL):
+ * for a bf16 FFN call that lands the rows itself (moe_overlap_cfg.x_tokens).  Resets the status word to MOE_OK first; sets MOE_ECAPACITY if
  * the padded rows exceed L->cap_rows (then all outputs are left empty: M_pad = 0). */
 int moe_layout_build(const moe_shape* s, const int32_t* topk_idx, const void* x, moe_layout* L, void* x_pad,
                      void* stream);
@@ -176,7 +184,8 @@ int moe_read_status(const moe_layout* L, void* stream);
  * holds the readiness flags of the second GEMM's output tiles (what the consumer waits on), and for bf16 the
  * flags of the first GEMM's h tiles, an arrival counter per output tile of the second GEMM and the fp32 partial
  * sums of its k-splits (256 x 256 floats per output tile and split; f/d rounded gives the number of splits, up
- * to 8); then one 64-bit counter of the return's copy units; last (bf16), the MOE_OBS_WORDS words of the consumer
+ * to 8); then one 64-bit counter of the return's copy units; for bf16 the landing's input flag and unit count per
+ * row tile and its unit counter (moe_overlap_cfg.x_tokens); last (bf16), the MOE_OBS_WORDS words of the consumer
  * partition record (see moe_pick_consumer_cus).  Zero the buffer once before the first call; afterwards it is
  * epoch-valued. */
 int64_t moe_ffn_flags_count(const moe_shape* s);
@@ -186,8 +195,11 @@ int64_t moe_ffn_flags_count(const moe_shape* s);
  * cfg->consumer_cus = 0, an overlapped bf16 launch picks it itself, on the device, from this batch's routing (rows
  * routed to the local experts, rows to return to other owners: the layout's per-owner counts) and from rates it
  * observed in earlier calls on the same flag buffer: the producers' flops per CU and the consumers' copied bytes per
- * CU, per 100 MHz tick.  The rule: the smallest multiple of 8 in [8, min(32, n_cu/4)] at which the consumers alone
- * would return 4 d bytes per returned row in half the time the other CUs take for 6 d f flops per routed row.
+ * CU, per 100 MHz tick.  The rule: c = the smallest multiple of 8 in [8, min(32, n_cu/4)] at which the consumers
+ * alone would return 4 d bytes per returned row in half the time the other CUs take for 6 d f flops per routed row;
+ * then 0 (no partition: every workgroup takes copy units once its own items are done, the return at the launch's
+ * tail) if the whole chip copies those bytes (at 50000 bytes per tick, or n_cu times the consumer rate if lower) in
+ * no more time than the c CUs would add to the FFN.
  * The choice of the last overlapped call is word MOE_OBS_WORDS - 4 counted from the end of the flag buffer.
  * moe_pick_consumer_cus_observed evaluates the rule for given rows and rates (a rate <= 0 takes its default:
  * 450 bytes and 31250 flops per CU-tick, ~45 GB/s and ~0.8 PFLOP/s over 256 CUs); moe_pick_consumer_cus for the

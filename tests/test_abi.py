@@ -48,26 +48,33 @@ def test_capacity_matches_bound(kw):
     assert cap == oracle.capacity_rows(s.R, s.tokens_per_owner, s.num_local_experts, s.top_k, s.tile_m)
 
 
-@pytest.mark.parametrize("kw,want", [
-    (dict(), 8),                                                       # f = 14336
-    (dict(tokens_per_owner=4096, num_global_experts=8, num_local_experts=2, f=4096), 8),
-    (dict(R=8, tokens_per_owner=2048, num_global_experts=256, num_local_experts=32, top_k=8, d=7168, f=2048), 16),
+@pytest.mark.parametrize("kw,c_copy,want", [
+    # (kw, the partition the consumers' copy rate asks for, the pick)
+    (dict(), 8, 0),                                                    # f = 14336
+    (dict(tokens_per_owner=4096, num_global_experts=8, num_local_experts=2, f=4096), 8, 0),
+    (dict(R=8, tokens_per_owner=2048, num_global_experts=256, num_local_experts=32, top_k=8, d=7168, f=2048), 16, 0),
     (dict(tokens_per_owner=2048, num_global_experts=64, num_local_experts=16, top_k=6, d=2048, f=1408,
-          tile_m=64), 16),
-    (dict(d=64, f=128, tile_m=16), 32),                                # capped at 32
-    (dict(d=64, f=128, tile_m=16, dtype=B.MOE_F32), 8),
+          tile_m=64), 16, 0),
+    (dict(d=64, f=128, tile_m=16), 32, 32),                            # capped at 32; the tail return costs more
+    (dict(d=64, f=128, tile_m=16, dtype=B.MOE_F32), 8, 8),
 ])
-def test_consumer_partition_pick(kw, want):
-    """The shape-only partition estimate: the launch's rule with default rates and R - 1 of every R rows returned
-    (the smallest multiple of 8 at which the consumers alone return the rows in half the FFN's time), within
-    [8, min(32, CUs/4)]; a device with under 32 CUs takes a quarter of them."""
+def test_consumer_partition_pick(kw, c_copy, want):
+    """The shape-only partition estimate: the launch's rule with default rates and R - 1 of every R rows returned.
+    The partition size is the smallest multiple of 8 at which the consumers alone return the rows in half the FFN's
+    time, within [8, min(32, CUs/4)]; the pick is 0 (no partition, the return at the launch's tail) when the chip
+    copies the rows in less time than those CUs add to the FFN; a device with under 32 CUs takes a quarter of them."""
     s = shape(**kw)
     c = B.moe_pick_consumer_cus(s, 256)
     assert c == want
-    if s.dtype == B.MOE_BF16 and 8 < c < 32:
+    if s.dtype == B.MOE_BF16:
         ratio = lambda c: 4.0 * (s.R - 1) / s.R * 31250.0 * (256 - c) / (6.0 * 450.0 * c * s.f)
-        assert ratio(c) <= 0.5 < ratio(c - 8)
-    assert B.moe_pick_consumer_cus(s, 16) == min(want, 4)   # a quarter of a small device's CUs
+        assert ratio(c_copy) <= 0.5 or c_copy == 32
+        assert c_copy == 8 or ratio(c_copy - 8) > 0.5
+        m = 1e6  # the rule's nominal rows
+        tail = 4.0 * m * (s.R - 1) / s.R * s.d / 50000.0
+        ffn0 = 6.0 * m * s.d * s.f / (256 * 31250.0)
+        assert (tail <= ffn0 * c_copy / (256 - c_copy)) == (want == 0)
+    assert B.moe_pick_consumer_cus(s, 16) == 4   # a quarter of a small device's CUs
     assert B.moe_pick_consumer_cus(s, 4) == 1
     assert B.moe_pick_consumer_cus(s, 1) == -1
     assert B.moe_pick_consumer_cus(shape(f=0), 256) == -1
@@ -187,19 +194,52 @@ def test_full_size_parity_runs_in_the_bench_configuration():
 
 
 def test_partition_rule():
-    """The consumer-partition rule (the launch's own code, compiled for the host): more returned rows or slower copies
-    take more consumer CUs, a faster FFN too; nothing to return takes the minimum; multiples of 8 within
-    [8, min(32, CUs / 4)]; defaults for rates <= 0."""
+    """The consumer-partition rule (the launch's own code, compiled for the host): more returned rows take more
+    consumer CUs, a faster FFN too; nothing to return, or a return cheaper at the launch's tail than the CUs
+    a partition takes, takes none (0); otherwise multiples of 8 within [8, min(32, CUs / 4)]; defaults for rates <= 0."""
     s = shape(d=2048, f=1408, R=4)
     pick = lambda routed, ret, fr=0.0, cr=0.0, n=256: B.moe_pick_consumer_cus_observed(s, n, routed, ret, fr, cr)
-    assert pick(15000, 0) == 8
+    assert pick(15000, 0) == 0
     vals = [pick(15000, r) for r in (0, 3000, 6000, 9000, 12000, 15000)]
-    assert vals == sorted(vals) and vals[-1] > vals[0]
-    assert all(v % 8 == 0 and 8 <= v <= 32 for v in vals)
-    assert pick(15000, 12000, cr=100.0) >= pick(15000, 12000, cr=450.0) >= pick(15000, 12000, cr=2000.0)
+    assert vals == sorted(vals) and vals[0] == 0 and vals[-1] >= 16
+    assert all(v == 0 or (v % 8 == 0 and 8 <= v <= 32) for v in vals)
+    # the tail return against the partition, by the rule's own terms: 4 d bytes per returned row over the chip at
+    # 50000 bytes per tick, against the c CUs' share of 6 d f flops per routed row at the default rate
+    tail = lambda ret: 4.0 * ret * 2048 / 50000.0
+    ffn0 = 6.0 * 15000 * 2048 * 1408 / (256 * 31250.0)
+    assert pick(15000, 15000) == 16 and tail(15000) > ffn0 * 16 / 240
+    assert pick(15000, 3000) == 0 and tail(3000) <= ffn0 * 8 / 248
+    # the Mixtral-like and DeepSeek-V3-like shards return less than that costs: no partition
+    mix = shape()
+    assert B.moe_pick_consumer_cus_observed(mix, 256, 2048, 1536, 0.0, 0.0) == 0
+    ds = shape(R=8, tokens_per_owner=2048, num_global_experts=256, num_local_experts=32, top_k=8, d=7168, f=2048)
+    assert B.moe_pick_consumer_cus_observed(ds, 256, 24232, 21203, 0.0, 0.0) == 0
+    # slower copies take more consumers (where the return stays with a partition: faster copies also make a small
+    # partition cheaper than the tail return, so they can turn a pick of 0 into 8)
+    assert pick(15000, 15000, cr=100.0) > pick(15000, 15000, cr=450.0) > pick(15000, 15000, cr=2000.0) == 8
+    assert pick(15000, 12000, cr=450.0) == 0 and pick(15000, 12000, cr=2000.0) == 8
     assert pick(15000, 12000, fr=60000.0) >= pick(15000, 12000, fr=31250.0)
     assert pick(15000, 12000, 0.0, 0.0) == pick(15000, 12000, 31250.0, 450.0)
     assert pick(15000, 15000, cr=1.0, n=64) == 16  # capped at a quarter of the CUs
     # the shape-only estimate is the rule with 3 of 4 owners' rows returned and default rates
     assert B.moe_pick_consumer_cus(s, 256) == pick(4000, 3000)
     assert pick(100, 200) == -1
+
+
+def test_landing_rejected_where_it_does_not_apply():
+    """The launch lands token rows (cfg.x_tokens) for bf16 in modes 0 and 1 only; the call rejects the rest before
+    any device work."""
+    for dtype, mode in ((B.MOE_F32, 0), (B.MOE_BF16, 2), (B.MOE_BF16, 3)):
+        s = shape(dtype=dtype, d=256, f=512)
+        nbytes = B.moe_layout_workspace_bytes(s)
+        buf = np.zeros(nbytes + 256, np.uint8)
+        base = (buf.ctypes.data + 255) // 256 * 256
+        L = B.moe_layout()
+        assert B.lib().moe_layout_bind(ctypes.byref(s), ctypes.c_void_p(base), nbytes, ctypes.byref(L)) == 0
+        fake = np.zeros(64, np.uint64)  # never dereferenced: the call fails its checks first
+        p = ctypes.c_void_p(fake.ctypes.data)
+        recv = (ctypes.c_void_p * s.R)(*([fake.ctypes.data] * s.R))
+        cfg = B.moe_overlap_cfg(4, mode, 1, 0, 0, None, 0, fake.ctypes.data)
+        rc = B.lib().moe_expert_ffn_overlap(ctypes.byref(s), ctypes.byref(L), p, p, p, p, p, recv, p,
+                                            ctypes.byref(cfg), None)
+        assert rc == B.MOE_EINVAL and "x_tokens" in B.moe_last_error(), (dtype, mode, B.moe_last_error())

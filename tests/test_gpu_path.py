@@ -190,6 +190,27 @@ def check_delivery(run):
         assert np.isnan(tail).all(), "rows past N_r were written"
 
 
+def check_landing(run, recv_bits, out_bits, **kw):
+    """The FFN call landing the token rows itself (layout built without the gather, x_pad poisoned first): the
+    rows it lands are x's rows bit for bit, and every delivered row and the combined output are the bits of the call
+    that read the gathered x_pad."""
+    P, s, lay = run.P, run.s, run.lay
+    P.x_pad.fill_(float("nan"))
+    P.layout(None)
+    run.ffn(x_tokens=run.dev["x"], **kw)
+    P.combine()
+    torch.cuda.synchronize()
+    assert P.status() == B.MOE_OK
+    real = np.nonzero(lay["row_src"] >= 0)[0]
+    dev = P.x_pad.device
+    np.testing.assert_array_equal(bits(P.x_pad[torch.as_tensor(real, device=dev)]),
+                                  bits(run.dev["x"][torch.as_tensor(lay["row_src"][real], device=dev)]),
+                                  err_msg="landed rows " + str(kw))
+    for r in range(s.R):
+        np.testing.assert_array_equal(bits(P.recv[r]), recv_bits[r], err_msg="landing " + str(kw))
+    np.testing.assert_array_equal(bits(P.out), out_bits, err_msg="landing " + str(kw))
+
+
 SMALL = [
     mi.spec("tiny"), mi.spec("tiny_f32"), mi.spec("tiny", mgb=2),
     mi.Spec("ragged", R=4, T_o=300, G=16, E_l=4, k=2, d=256, f=512, M=32, seed=11),
@@ -244,14 +265,19 @@ def test_small_full_parity(s, self_rank):
     # sequential mode, and the producer's other row-tile order, give the same bits
     recv_ovl = [bits(b) for b in P.recv]
     out_ovl = bits(P.out)
-    for kw in (dict(mode=1), dict(mode=0, tile_order=1)) + ((dict(mode=3),) if s.dtype == "bf16" else ()):
-        run.ffn(consumer_cus=4, **kw)
+    bf = s.dtype == "bf16"
+    # bf16 also: the return on the DMA engines, and no consumer partition (the return at the launch's tail)
+    for kw in (dict(mode=1), dict(mode=0, tile_order=1)) + ((dict(mode=3), dict(mode=0, consumer_cus=-1)) if bf else ()):
+        run.ffn(**{"consumer_cus": 4, **kw})
         P.combine()
         torch.cuda.synchronize()
         assert P.status() == B.MOE_OK
         for r in range(s.R):
             np.testing.assert_array_equal(bits(P.recv[r]), recv_ovl[r], err_msg=str(kw))
         np.testing.assert_array_equal(bits(P.out), out_ovl, err_msg=str(kw))
+    if bf:  # the launch landing the token rows itself, overlapped and sequential
+        for kw in (dict(mode=0), dict(mode=1), dict(mode=0, tile_order=1), dict(mode=0, consumer_cus=-1)):
+            check_landing(run, recv_ovl, out_ovl, **{"consumer_cus": 4, **kw})
 
 
 FULL = ["mixtral", "skew", "sweep1", "sweep2", "sweep4", "sweep8", "sweep16", "deepseek"]
@@ -263,7 +289,7 @@ def test_full_size_parity(name):
     """Full-size workload in the benchmark's launch configuration: the whole layout bit for bit; y on the first, the
     last and four random real rows of every GEMM row tile (every split-K and half-width tile included), on every real
     row for the Mixtral-shaped shard; the combine of every token there, of sampled tokens elsewhere; sequential ==
-    overlapped bit for bit."""
+    overlapped bit for bit, and so is the launch that lands the token rows itself."""
     s = mi.spec(name)
     run = Run(s)
     check_route_and_layout(run)
@@ -325,6 +351,8 @@ def test_full_size_parity(name):
     for r in range(s.R):
         np.testing.assert_array_equal(bits(P.recv[r]), recv_ovl[r])
     np.testing.assert_array_equal(bits(P.out), out_ovl)
+    # the launch landing the token rows itself, in the benchmark's configuration
+    check_landing(run, recv_ovl, out_ovl, mode=0, consumer_cus=BENCH_CONSUMER_CUS)
 
 
 STRESS_SHAPES = [

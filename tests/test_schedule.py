@@ -53,16 +53,17 @@ def schedule(s, mode, cus=0, window=0, self_rank=0, tile_order=0):
     return items, hdr, pure if tile_order == 0 else np.zeros_like(pure)
 
 
-@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("mode,cus", [(0, 0), (1, 0), (0, 16)])
 @pytest.mark.parametrize("name", FULL)
-def test_full_workload_lists(name, mode):
-    """The bench's launch configuration (the library's consumer partition, default band window) on every workload."""
+def test_full_workload_lists(name, mode, cus):
+    """The bench's launch configuration (the library's consumer partition, default band window) on every workload,
+    and a 16-CU partition."""
     s = mi.spec(name)
-    items, hdr, pure = schedule(s, mode)
+    items, hdr, pure = schedule(s, mode, cus)
     waits = sm.check_list(items, len(hdr), s.d, s.f, pure)
     sm.simulate(items, waits, seed=1)
     if mode == 0:  # the consumer workgroups' own share is GEMM1 items only (they wait on nothing)
-        cons = items[:, 0] < B.moe_pick_consumer_cus(shape_of(s), N_CU)
+        cons = items[:, 0] < (cus or B.moe_pick_consumer_cus(shape_of(s), N_CU))
         assert (items[cons, 2] == 1).all()
 
 
@@ -84,8 +85,8 @@ def test_lists_at_other_ranks(s, self_rank):
     sm.check_list(items, len(hdr), s.d, s.f, pure)
 
 
-@pytest.mark.parametrize("name,mode,cus", [("splitk_halves", 1, 0), ("halves", 1, 0), ("mixtral", 0, 0),
-                                           ("mixtral", 1, 0), ("deepseek", 0, 0), ("skew", 1, 0), ("sweep1", 0, 0)])
+@pytest.mark.parametrize("name,mode,cus", [("splitk_halves", 1, 0), ("halves", 1, 0), ("mixtral", 0, 8),
+                                           ("mixtral", 1, 0), ("deepseek", 0, 16), ("skew", 1, 0), ("sweep1", 0, 8)])
 def test_half_width_items_handed_out_from_a_counter(name, mode, cus):
     """The half-width final round with its halves taken from a counter by whichever workgroup is free first (the
     variant whose GPU test once hung, and was dropped): in any such order every half runs once, its waits (GEMM1

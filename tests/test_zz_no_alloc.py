@@ -1,6 +1,7 @@
 """The allocation-free FFN entry point (flag buffer in the library's own device array) against the entry point that
 takes a flag workspace, through the C ABI: two calls in a row, the second on a smaller input, each bit for bit the
-same as the workspace entry point on the same inputs (the same kernels and item list, so the same arithmetic)."""
+same as the workspace entry point on the same inputs (the same kernels and item list, so the same arithmetic); also
+with the launch landing the token rows itself, whose per-tile flags live in the same array."""
 import numpy as np
 import pytest
 import torch
@@ -20,8 +21,8 @@ def bits(t):
     return t.contiguous().view(torch.int16).cpu().numpy()
 
 
-def run_both(s, mode):
-    print("case", s.name, "mode", mode, flush=True)
+def run_both(s, mode, land=False):
+    print("case", s.name, "mode", mode, "land", land, flush=True)
     inp = mi.inputs(s)
     P = MoePath.from_spec(s)
     dev = {k: to_device(v, s.dtype) for k, v in inp.items()}
@@ -42,7 +43,10 @@ def run_both(s, mode):
     P.h.fill_(float("nan"))
     P.y_pad.fill_(float("nan"))
     P.out.fill_(float("nan"))
-    cfg = B.moe_overlap_cfg(4, mode, 0, 0, 0, None, 0)  # epoch ignored by this entry point
+    if land:  # the launch lands the token rows itself: its landing flags must start cleared on every call
+        P.x_pad.fill_(float("nan"))
+        P.layout(None)
+    cfg = B.moe_overlap_cfg(4, mode, 0, 0, 0, None, 0, dev["x"].data_ptr() if land else None)  # epoch ignored
     B.moe_expert_ffn_overlap_noalloc(P.shape, P.L, P.x_pad, dev["w_gate_up"], dev["w_down"], P.h, P.y_pad, P.recv, cfg)
     P.combine()
     torch.cuda.synchronize()
@@ -58,6 +62,8 @@ def test_noalloc_matches_workspace_entry_point_twice():
     run_both(FIRST, 0)
     run_both(SECOND, 0)  # the second call, on a smaller input, reuses the array the first one left behind
     run_both(SECOND, 1)  # and sequential mode
+    run_both(FIRST, 0, land=True)  # landing the token rows in the launch, twice in a row
+    run_both(SECOND, 0, land=True)
 
 
 def test_noalloc_rejects_what_does_not_fit():
