@@ -64,6 +64,27 @@ __device__ __forceinline__ int32_t load_status(const int32_t* status) {
   return __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// One thread: waits until the n flags fl[0 .. n) all equal epoch, taking them one at a time and sleeping longer while
+// one stays unset (up to max_nap + 1 sleeps of ~512 clocks between loads), so that a long wait sends few loads to the flags' lines (every
+// workgroup of a launch polls a handful of lines: polling every flag of a segment from every thread each ~0.1 us
+// slowed the producers' own loads).  The status word is looked at every 16 loads.  0: all set; 1: the spin budget
+// ran out; 2: another workgroup reported an error.
+__device__ inline int poll_flags(const uint32_t* fl, int n, uint32_t epoch, uint64_t budget, const int32_t* status,
+                                  int max_nap) {
+  const uint64_t t0 = moe_clock();
+  int polls = 0;
+  for (int i = 0; i < n; ++i) {
+    int nap = 0;
+    while (__hip_atomic_load(&fl[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
+      if (moe_clock() - t0 > budget) return 1;
+      if ((++polls & 15) == 0 && load_status(status) != 0) return 2;
+      for (int k = 0; k <= nap; ++k) __builtin_amdgcn_s_sleep(8);  // ~512 clocks each
+      nap = nap < max_nap ? nap + 1 : max_nap;
+    }
+  }
+  return 0;
+}
+
 // ---- the in-launch publish protocol ----------------------------------------------------------------------
 // Results one workgroup hands to another inside a launch (h tiles, split-K partial sums, y tiles) go out with
 // device-scope stores, which write through to the level shared by the XCDs; the producer waits for their

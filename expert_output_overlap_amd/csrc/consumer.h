@@ -128,18 +128,11 @@ __device__ void consumer_role(const ConsumerArgs& a) {
       const int mt0 = a.seg_mtiles[2 * s], mcnt = a.seg_mtiles[2 * s + 1];
       const int nflags = mcnt * a.n_nt;
       const uint32_t* fl = a.flags + (int64_t)mt0 * a.n_nt;
-      for (;;) {
-        int ok = 1;
-        for (int i = tid; i < nflags; i += nthr)
-          ok &= __hip_atomic_load(&fl[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch;
-        if (__syncthreads_and(ok)) break;
-        if (tid == 0) s_stop = (moe_clock() - t0 > a.budget) ? 1 : (load_status(a.status) != 0 ? 2 : 0);
-        __syncthreads();
-        if (s_stop) {
-          if (s_stop == 1 && tid == 0) set_status(a.status, MOE_ETIMEOUT);
-          return;
-        }
-        __builtin_amdgcn_s_sleep(1);
+      if (tid == 0) s_stop = poll_flags(fl, nflags, a.epoch, a.budget, a.status, 3);
+      __syncthreads();
+      if (s_stop) {
+        if (s_stop == 1 && tid == 0) set_status(a.status, MOE_ETIMEOUT);
+        return;
       }
       flag_acquire();  // the launch_acquire of this launch left no stale copy of these rows (common.h)
       seen = s;

@@ -385,19 +385,12 @@ __device__ __forceinline__ unsigned long long* obs64(uint32_t* obs, int w) { ret
 // publish protocol in common.h).  False if the spin budget ran
 // out (status set to MOE_ETIMEOUT) or another workgroup reported an error.
 __device__ bool wait_flags(const uint32_t* fl, int n, uint32_t epoch, uint64_t budget, int32_t* status, int* s_stop) {
-  const uint64_t t0 = moe_clock();
-  for (;;) {
-    int ok = 1;
-    for (int i = threadIdx.x; i < n; i += blockDim.x)
-      ok &= __hip_atomic_load(&fl[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
-    if (__syncthreads_and(ok)) break;
-    if (threadIdx.x == 0) *s_stop = (moe_clock() - t0 > budget) ? 1 : (load_status(status) != 0 ? 2 : 0);
-    __syncthreads();
-    if (*s_stop) {
-      if (*s_stop == 1 && threadIdx.x == 0) set_status(status, MOE_ETIMEOUT);
-      return false;
-    }
-    __builtin_amdgcn_s_sleep(2);
+  __syncthreads();  // every thread has read *s_stop of the previous wait
+  if (threadIdx.x == 0) *s_stop = poll_flags(fl, n, epoch, budget, status, 1);  // a producer waits briefly
+  __syncthreads();
+  if (*s_stop) {
+    if (*s_stop == 1 && threadIdx.x == 0) set_status(status, MOE_ETIMEOUT);
+    return false;
   }
   flag_acquire();  // no stale copies to drop: the publish protocol in common.h
   return true;
@@ -858,22 +851,23 @@ __device__ void land_unit(const FusedArgs& a, int mt, int sub, int* s_p, int* s_
     __hip_atomic_store(&a.flags0[mt], a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The next number from a counter that holds stamp << 32 | count, once the launch's stamp is there (workgroup 0
+// stores it at the start); -1 if the stamp does not come within the spin budget.  One thread.
+__device__ int claim_stamped(uint64_t* ctr, uint32_t stamp, uint64_t budget) {
+  const uint64_t t0 = moe_clock();
+  while ((uint32_t)(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 32) != stamp) {
+    if (moe_clock() - t0 > budget) return -1;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return (int)(uint32_t)__hip_atomic_fetch_add(ctr, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Takes the next landing unit and lands it; false once every unit has been handed out (or the stamp never came).
 // All threads; s_u is workgroup-shared.
 template <typename OrderOf>
 __device__ bool land_next(const FusedArgs& a, int n_mt, OrderOf mt_of, int* s_u, int* s_p, int* s_t) {
   __syncthreads();  // s_u of the previous call has been read
-  if (threadIdx.x == 0) {
-    const uint64_t t0 = moe_clock();
-    int u = -1;
-    while ((uint32_t)(__hip_atomic_load(a.gclaim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 32) != a.gstamp) {
-      if (moe_clock() - t0 > a.budget) break;
-      __builtin_amdgcn_s_sleep(1);
-    }
-    if ((uint32_t)(__hip_atomic_load(a.gclaim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 32) == a.gstamp)
-      u = (int)(uint32_t)__hip_atomic_fetch_add(a.gclaim, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *s_u = u;
-  }
+  if (threadIdx.x == 0) *s_u = claim_stamped(a.gclaim, a.gstamp, a.budget);
   __syncthreads();
   const int u = *s_u;
   if (u < 0 || u >= n_mt * LAND_UNITS_PER_TILE) return false;
@@ -1008,8 +1002,12 @@ __global__ __launch_bounds__(FFN_THREADS, 1) void k_ffn_bf16(FusedArgs a) {
     return false;
   };
   // Producer workgroups move through the list in step, a run of consecutive items on one XCD, whose workgroups share
-  // operand tiles in its L2.  (Claiming items from a counter instead balances the end better but loses that
-  // locality, and the clock drops with the extra off-XCD traffic: measured slower.)
+  // operand tiles in its L2.  Two ways of balancing the end were measured and dropped: taking items (or XCD-sized
+  // runs of them) from counters at run time costs 4-16% in claim latency and lost L2 sharing; handing runs to the
+  // XCDs by a cost model shortens the producers' span (the round-robin leaves the workgroups that take one more
+  // first-GEMM item, each ~d / (f / S) second-GEMM items long, behind at the end) by 6% on the DeepSeek-V3-like
+  // shard, but the workgroups that finish early under the round-robin are the ones that run the return while the
+  // others finish, and with the producers balanced that return is exposed: no faster overall.
   int i0, i1, step;
   ffn_list_range(L, (int)blockIdx.x, &i0, &i1, &step);
   if (a.item_begin > i0) i0 += (a.item_begin - i0 + step - 1) / step * step;  // this launch's chunk of the list
@@ -1089,7 +1087,7 @@ int ffn_splits(int dtype, int d, int f) {
 
 namespace {
 struct FlagCarve {
-  int64_t flags2, flags1, scount, partial, claim, flags0, gcount, gclaim, obs, total;  // 4-byte words
+  int64_t flags2, flags1, scount, partial, claim, flags0, gcount, gclaim, obs, total;  // offsets and size in words
 };
 FlagCarve flag_carve(int dtype, int d, int f, int64_t cap_mtiles) {
   FlagCarve c;
@@ -1243,22 +1241,23 @@ int ffn_schedule_host(int d, int f, int E, int n_cons, int n_producers, int band
     *rc = mt_hdr[4 * mt + 3];
   };
   auto order = [&](int p) { return (int)mt_order[p]; };
+  auto put = [&](int idx, int b, int seq) {
+    const FfnItem it = ffn_list_item(L, idx, run_of, order);
+    int32_t* o = items + 8 * (int64_t)idx;
+    o[0] = b;
+    o[1] = seq;
+    o[2] = it.kind;
+    o[3] = it.mt;
+    o[4] = it.nt;
+    o[5] = it.s;
+    o[6] = it.half;
+    o[7] = it.target;
+  };
   for (int b = 0; b < n_cons + n_producers; ++b) {
     int i0, i1, step;
     ffn_list_range(L, b, &i0, &i1, &step);
     int seq = 0;
-    for (int idx = i0; idx < i1; idx += step, ++seq) {
-      const FfnItem it = ffn_list_item(L, idx, run_of, order);
-      int32_t* o = items + 8 * (int64_t)idx;
-      o[0] = b;
-      o[1] = seq;
-      o[2] = it.kind;
-      o[3] = it.mt;
-      o[4] = it.nt;
-      o[5] = it.s;
-      o[6] = it.half;
-      o[7] = it.target;
-    }
+    for (int idx = i0; idx < i1; idx += step, ++seq) put(idx, b, seq);
   }
   return 0;
 }
