@@ -54,16 +54,21 @@ def overlap_stats(ts: np.ndarray, n_segs: int, tick_ns: float = 10.0) -> dict:
     }
 
 
-def hbm_traffic(s, cus: int, band_window: int):
+def hbm_traffic(s, cus: int, band_window: int, land: bool, mode: int):
     """HBM bytes per launch of the FFN kernel from the committed counter summary (FETCH_SIZE and WRITE_SIZE, each
-    scaled by the same counter's reading for a plain copy of known size), if it covers this workload and
+    scaled by the same counter's reading for a plain copy of known size), if one covers this workload and launch
     configuration and the kernel sources are the ones it was taken on; else None."""
     import hashlib
 
-    path = os.path.join(ROOT, "profiles", "k_ffn_bf16_mixtral_hbm_bytes.json")
-    if s.name != "mixtral" or s.mgb != 1 or cus != 8 or band_window not in (0, 4) or not os.path.exists(path):
+    path = os.path.join(ROOT, "profiles", "k_ffn_bf16_%s_hbm_bytes.json" % s.name)
+    if not os.path.exists(path):
         return None
     rec = json.load(open(path))
+    c = rec["configuration"]
+    want = {"config": s.name, "mgb": s.mgb, "consumer_cus_option": cus, "band_window": band_window or 4,
+            "token_rows_landed_by": "the FFN launch" if land else "the layout's gather kernel", "mode": mode}
+    if any(c.get(k) != v for k, v in want.items()):
+        return None
     h = hashlib.sha256()
     for p in rec["sources"]:
         h.update(open(os.path.join(ROOT, p), "rb").read())
@@ -336,7 +341,8 @@ def main():
                                 if s.dtype == "bf16" else "k_gemm<float> first GEMM"),
                      "achieved": round(roof_flops / (g1_avg * 1e-3) / 1e12, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(roof_flops / (g1_avg * 1e-3) / 1e12 / peak, 4),
-                     "traffic": hbm_traffic(s, cus, args.band_window), "traffic_unit": "HBM bytes per launch"},
+                     "traffic": hbm_traffic(s, cus, args.band_window, land, args.mode),
+                     "traffic_unit": "HBM bytes per launch"},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(s, inp, args.cpu_seconds)
