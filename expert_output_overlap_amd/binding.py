@@ -74,7 +74,7 @@ def lib():
             "moe_layout_build": ([ps, vp, vp, pl, vp, vp], i32),
             "moe_read_status": ([pl, vp], i32), "moe_ffn_flags_count": ([ps], i64),
             "moe_pick_consumer_cus": ([ps, i32], i32),
-            "moe_pick_consumer_cus_observed": ([ps, i32, i64, i64, ctypes.c_float, ctypes.c_float], i32),
+            "moe_pick_consumer_cus_observed": ([ps, i32, i64, i64, i32, ctypes.c_float, ctypes.c_float], i32),
             "moe_expert_ffn_overlap": ([ps, pl, vp, vp, vp, vp, vp, vp, vp, pc, vp], i32),
             "moe_expert_ffn_overlap_noalloc": ([ps, pl, vp, vp, vp, vp, vp, vp, pc, vp], i32),
             "moe_combine": ([ps, pl, vp, vp, vp, vp], i32),
@@ -158,10 +158,10 @@ def moe_pick_consumer_cus(shape: moe_shape, n_cu: int) -> int:
     return lib().moe_pick_consumer_cus(ctypes.byref(shape), n_cu)
 
 
-def moe_pick_consumer_cus_observed(shape: moe_shape, n_cu: int, rows_routed: int, rows_returned: int, ffn_rate: float,
-                                   copy_rate: float) -> int:
-    return lib().moe_pick_consumer_cus_observed(ctypes.byref(shape), n_cu, rows_routed, rows_returned, ffn_rate,
-                                                copy_rate)
+def moe_pick_consumer_cus_observed(shape: moe_shape, n_cu: int, rows_routed: int, rows_returned: int, n_mtiles: int,
+                                   ffn_rate: float, copy_rate: float) -> int:
+    return lib().moe_pick_consumer_cus_observed(ctypes.byref(shape), n_cu, rows_routed, rows_returned, n_mtiles,
+                                                ffn_rate, copy_rate)
 
 
 def moe_expert_ffn_overlap(shape: moe_shape, layout: moe_layout, x_pad, w_gate_up, w_down, h_ws, y_pad, recv,

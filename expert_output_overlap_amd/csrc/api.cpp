@@ -283,17 +283,23 @@ int32_t moe_pick_consumer_cus(const moe_shape* s, int32_t n_cu) {
   if (!check_shape(s).empty() || n_cu < 2) return -1;
   if (s->dtype != MOE_BF16) return std::min(8, std::max(1, std::min(32, n_cu / 4)));
   // the launch's own rule (ffn_adaptive_consumers) before any observation, with the rows of R - 1 of the R owners
-  // returned (uniform routing)
+  // returned (uniform routing), in full row tiles
   const int64_t m = 1000000;
-  return ffn_adaptive_consumers(n_cu, m, m * (s->R - 1) / s->R, s->d, s->f, 0.f, 0.f);
+  int n1 = 0, n2 = 0, S = 0;
+  ffn_list_dims(s->d, s->f, &n1, &n2, &S);
+  return ffn_adaptive_consumers(n_cu, m, m * (s->R - 1) / s->R, s->d, s->f, (m + 255) / 256 * n1, 0.f, 0.f);
 }
 
 int32_t moe_pick_consumer_cus_observed(const moe_shape* s, int32_t n_cu, int64_t rows_routed, int64_t rows_returned,
-                                       float ffn_rate, float copy_rate) {
-  if (!check_shape(s).empty() || n_cu < 2 || rows_routed < 0 || rows_returned < 0 || rows_returned > rows_routed)
+                                       int32_t n_mtiles, float ffn_rate, float copy_rate) {
+  if (!check_shape(s).empty() || n_cu < 2 || rows_routed < 0 || rows_returned < 0 || rows_returned > rows_routed ||
+      n_mtiles < 0)
     return -1;
   if (s->dtype != MOE_BF16) return moe_pick_consumer_cus(s, n_cu);
-  return ffn_adaptive_consumers(n_cu, rows_routed, rows_returned, s->d, s->f, ffn_rate, copy_rate);
+  int n1 = 0, n2 = 0, S = 0;
+  ffn_list_dims(s->d, s->f, &n1, &n2, &S);
+  return ffn_adaptive_consumers(n_cu, rows_routed, rows_returned, s->d, s->f, (int64_t)n_mtiles * n1, ffn_rate,
+                                copy_rate);
 }
 
 }  // extern "C"
@@ -594,6 +600,8 @@ int moe_ffn_schedule(const moe_shape* s, int32_t n_cu, const moe_overlap_cfg* cf
       (cfg->tile_order != 0 && cfg->tile_order != 1))
     return fail(MOE_EINVAL, "consumer_cus, band_window or tile_order out of range");
   std::vector<int32_t> ident;
+  const int32_t* mt_order_in = mt_order;
+  const int n_remote_in = n_remote_mtiles;
   if (cfg->tile_order == 1) {  // row-tile numbering: no boundary
     ident.resize(n_mtiles);
     for (int i = 0; i < n_mtiles; ++i) ident[i] = i;
@@ -606,8 +614,20 @@ int moe_ffn_schedule(const moe_shape* s, int32_t n_cu, const moe_overlap_cfg* cf
         mt_order[i] >= n_mtiles)
       return fail(MOE_EINVAL, "row-tile headers or order out of range");
   }
-  const int C = cfg->mode != 0 || cfg->consumer_cus < 0 ? 0
-                : cfg->consumer_cus > 0 ? cfg->consumer_cus : moe_pick_consumer_cus(s, n_cu);
+  // consumer_cus 0: the launch's own rule with default rates, taking every row of the row tiles that hold another
+  // owner's row as returned
+  int C = cfg->mode != 0 || cfg->consumer_cus < 0 ? 0 : cfg->consumer_cus;
+  if (cfg->mode == 0 && cfg->consumer_cus == 0) {
+    int64_t m_real = 0, m_ret = 0;
+    for (int i = 0; i < n_mtiles; ++i) m_real += mt_hdr[4 * (int64_t)i + 1];
+    for (int p = 0; p < n_remote_in; ++p) {
+      if (mt_order_in[p] < 0 || mt_order_in[p] >= n_mtiles) return fail(MOE_EINVAL, "row-tile order out of range");
+      m_ret += mt_hdr[4 * (int64_t)mt_order_in[p] + 1];
+    }
+    int n1 = 0, n2 = 0, S = 0;
+    ffn_list_dims(s->d, s->f, &n1, &n2, &S);
+    C = ffn_adaptive_consumers(n_cu, m_real, m_ret, s->d, s->f, (int64_t)n_mtiles * n1, 0.f, 0.f);
+  }
   if (ffn_schedule_host(s->d, s->f, s->num_local_experts, C, n_cu - C, cfg->band_window, n_mtiles, n_remote_mtiles,
                         mt_hdr, mt_order, items, cap, n_items))
     return items == nullptr && cap == 0 ? MOE_OK : fail(MOE_EINVAL, "cap is below the list length");

@@ -929,7 +929,7 @@ __global__ __launch_bounds__(FFN_THREADS, 1) void k_ffn_bf16(FusedArgs a) {
   if (C < 0) {  // the launch picks its consumer partition: every workgroup computes the same value
     // a rate never observed reads 0 (the buffer starts zeroed) and the rule takes its default
     const float fr = (a.obs[13] & 1) ? __uint_as_float(a.obs[10]) : 0.f, cr = (a.obs[13] & 2) ? __uint_as_float(a.obs[11]) : 0.f;
-    C = ffn_adaptive_consumers(gridDim.x, m_real, m_real - m_self, a.d, a.f, fr, cr);
+    C = ffn_adaptive_consumers(gridDim.x, m_real, m_real - m_self, a.d, a.f, (int64_t)n_mt * a.n_nt1, fr, cr);
     interleave = ffn_interleave(C, a.d, a.f, a.E);
     if (blockIdx.x == 0 && threadIdx.x == 0) a.obs[12] = (uint32_t)C;
   }

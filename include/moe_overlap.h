@@ -195,19 +195,20 @@ int64_t moe_ffn_flags_count(const moe_shape* s);
  * cfg->consumer_cus = 0, an overlapped bf16 launch picks it itself, on the device, from this batch's routing (rows
  * routed to the local experts, rows to return to other owners: the layout's per-owner counts) and from rates it
  * observed in earlier calls on the same flag buffer: the producers' flops per CU and the consumers' copied bytes per
- * CU, per 100 MHz tick.  The rule: c = the smallest multiple of 8 in [8, min(32, n_cu/4)] at which the consumers
- * alone would return 4 d bytes per returned row in half the time the other CUs take for 6 d f flops per routed row;
- * then 0 (no partition: every workgroup takes copy units once its own items are done, the return at the launch's
- * tail) if the whole chip copies those bytes (at 50000 bytes per tick, or n_cu times the consumer rate if lower) in
- * no more time than the c CUs would add to the FFN.
+ * CU, per 100 MHz tick.  The rule: 0 (no partition: every workgroup takes copy units once its own items are
+ * done) when, with the first-GEMM items (n_mtiles times f / 128 of them, each 2 x 256 x 256 x d flops) filling their
+ * last round over the n_cu workgroups only in part, the workgroups without one of that round copy 4 d bytes per
+ * returned row (at 50000 bytes per tick over the chip, or their own copy rate if lower) within one first-GEMM item's
+ * time; else the smallest multiple of 8 in [8, min(32, n_cu/4)] at which the consumers alone would return the rows
+ * in half the time the other CUs take for 6 d f flops per routed row.
  * The choice of the last overlapped call is word MOE_OBS_WORDS - 4 counted from the end of the flag buffer.
- * moe_pick_consumer_cus_observed evaluates the rule for given rows and rates (a rate <= 0 takes its default:
- * 450 bytes and 31250 flops per CU-tick, ~45 GB/s and ~0.8 PFLOP/s over 256 CUs); moe_pick_consumer_cus for the
- * defaults with R - 1 of every R rows returned.  fp32: 8 (at most a quarter of the CUs).  Host only; -1 for an
- * invalid shape or arguments, or n_cu < 2. */
+ * moe_pick_consumer_cus_observed evaluates the rule for given rows, row tiles and rates (a rate <= 0 takes its
+ * default: 450 bytes and 31250 flops per CU-tick, ~45 GB/s and ~0.8 PFLOP/s over 256 CUs); moe_pick_consumer_cus for
+ * the defaults with R - 1 of every R rows returned, in full row tiles.  fp32: 8 (at most a quarter of the CUs).  Host
+ * only; -1 for an invalid shape or arguments, or n_cu < 2. */
 int32_t moe_pick_consumer_cus(const moe_shape* s, int32_t n_cu);
 int32_t moe_pick_consumer_cus_observed(const moe_shape* s, int32_t n_cu, int64_t rows_routed, int64_t rows_returned,
-                                       float ffn_rate, float copy_rate);
+                                       int32_t n_mtiles, float ffn_rate, float copy_rate);
 #define MOE_OBS_WORDS 16
 
 /* Expert SwiGLU FFN over the padded layout with the return of each finished row-band segment to its
@@ -258,7 +259,8 @@ int moe_expert_ffn_overlap_noalloc(const moe_shape* s, const moe_layout* L, cons
 
 /* The work-item list of the bf16 FFN launch (host only, no device call; for inspection and tests): which
  * workgroup runs which item, in what order, for a launch on n_cu CUs with cfg's mode, consumer_cus, band_window and
- * tile_order (the library's pick when consumer_cus is 0).  The review page ("Core claim", "What carries the argument")
+ * tile_order (consumer_cus 0: the launch's rule with default rates, every row of the row tiles at positions before
+ * n_remote_mtiles counted as returned).  The review page ("Core claim", "What carries the argument")
  * describes one persistent GEMM over all local experts whose remote-bound tiles are scheduled first; the list is
  * the kernel's own (a header both compile).  Inputs are the layout's row tiles as the device built them:
  * mt_hdr [n_mtiles][4] = the first four fields of each mtile_desc entry {expert, rows, run_first, run_count},

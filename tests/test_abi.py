@@ -48,32 +48,40 @@ def test_capacity_matches_bound(kw):
     assert cap == oracle.capacity_rows(s.R, s.tokens_per_owner, s.num_local_experts, s.top_k, s.tile_m)
 
 
-@pytest.mark.parametrize("kw,c_copy,want", [
-    # (kw, the partition the consumers' copy rate asks for, the pick)
-    (dict(), 8, 0),                                                    # f = 14336
-    (dict(tokens_per_owner=4096, num_global_experts=8, num_local_experts=2, f=4096), 8, 0),
-    (dict(R=8, tokens_per_owner=2048, num_global_experts=256, num_local_experts=32, top_k=8, d=7168, f=2048), 16, 0),
+def _tail_fits(n_cu, m_ret, d, n_g1, ffn_rate=31250.0, copy_rate=450.0):
+    """The rule's no-partition test, restated: the workgroups without a first-GEMM item in the last, partly filled,
+    round copy the returned rows (4 d bytes each, at 50000 bytes per tick or their own rate if lower) within one
+    first-GEMM item's time (2 x 256 x 256 x d flops at the producers' rate)."""
+    q1 = n_g1 % n_cu
+    if q1 == 0 or m_ret == 0:
+        return m_ret == 0
+    return 4.0 * m_ret * d / min(50000.0, (n_cu - q1) * copy_rate) <= 2.0 * 256 * 256 * d / ffn_rate
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(), 8),                                                       # f = 14336
+    (dict(tokens_per_owner=4096, num_global_experts=8, num_local_experts=2, f=4096), 8),
+    (dict(R=8, tokens_per_owner=2048, num_global_experts=256, num_local_experts=32, top_k=8, d=7168, f=2048), 16),
     (dict(tokens_per_owner=2048, num_global_experts=64, num_local_experts=16, top_k=6, d=2048, f=1408,
-          tile_m=64), 16, 0),
-    (dict(d=64, f=128, tile_m=16), 32, 32),                            # capped at 32; the tail return costs more
-    (dict(d=64, f=128, tile_m=16, dtype=B.MOE_F32), 8, 8),
+          tile_m=64), 16),
+    (dict(d=64, f=128, tile_m=16), 32),                                # capped at 32
+    (dict(d=64, f=128, tile_m=16, dtype=B.MOE_F32), 8),
 ])
-def test_consumer_partition_pick(kw, c_copy, want):
-    """The shape-only partition estimate: the launch's rule with default rates and R - 1 of every R rows returned.
-    The partition size is the smallest multiple of 8 at which the consumers alone return the rows in half the FFN's
-    time, within [8, min(32, CUs/4)]; the pick is 0 (no partition, the return at the launch's tail) when the chip
-    copies the rows in less time than those CUs add to the FFN; a device with under 32 CUs takes a quarter of them."""
+def test_consumer_partition_pick(kw, want):
+    """The shape-only partition estimate: the launch's rule with default rates, R - 1 of every R of a nominal 10^6
+    rows returned, in full row tiles.  So many returned rows never fit in the round-robin's slack, so the pick is the
+    partition: the smallest multiple of 8 at which the consumers alone return the rows in half the FFN's time, within
+    [8, min(32, CUs/4)]; a device with under 32 CUs takes a quarter of them."""
     s = shape(**kw)
     c = B.moe_pick_consumer_cus(s, 256)
     assert c == want
     if s.dtype == B.MOE_BF16:
         ratio = lambda c: 4.0 * (s.R - 1) / s.R * 31250.0 * (256 - c) / (6.0 * 450.0 * c * s.f)
-        assert ratio(c_copy) <= 0.5 or c_copy == 32
-        assert c_copy == 8 or ratio(c_copy - 8) > 0.5
-        m = 1e6  # the rule's nominal rows
-        tail = 4.0 * m * (s.R - 1) / s.R * s.d / 50000.0
-        ffn0 = 6.0 * m * s.d * s.f / (256 * 31250.0)
-        assert (tail <= ffn0 * c_copy / (256 - c_copy)) == (want == 0)
+        assert ratio(c) <= 0.5 or c == 32
+        assert c == 8 or ratio(c - 8) > 0.5
+        m = 10 ** 6
+        n1 = s.f // (128 if s.f % 128 == 0 else 64)
+        assert not _tail_fits(256, m * (s.R - 1) // s.R, s.d, (m + 255) // 256 * n1)
     assert B.moe_pick_consumer_cus(s, 16) == 4   # a quarter of a small device's CUs
     assert B.moe_pick_consumer_cus(s, 4) == 1
     assert B.moe_pick_consumer_cus(s, 1) == -1
@@ -194,36 +202,35 @@ def test_full_size_parity_runs_in_the_bench_configuration():
 
 
 def test_partition_rule():
-    """The consumer-partition rule (the launch's own code, compiled for the host): more returned rows take more
-    consumer CUs, a faster FFN too; nothing to return, or a return cheaper at the launch's tail than the CUs
-    a partition takes, takes none (0); otherwise multiples of 8 within [8, min(32, CUs / 4)]; defaults for rates <= 0."""
+    """The consumer-partition rule (the launch's own code, compiled for the host).  No partition (0) when nothing is
+    returned, or when the first-GEMM items fill their last round over the CUs only in part and the workgroups left
+    without one copy the returned rows within one first-GEMM item's time; else the partition: more returned rows or a
+    faster FFN take more consumer CUs, multiples of 8 within [8, min(32, CUs / 4)]; defaults for rates <= 0."""
     s = shape(d=2048, f=1408, R=4)
-    pick = lambda routed, ret, fr=0.0, cr=0.0, n=256: B.moe_pick_consumer_cus_observed(s, n, routed, ret, fr, cr)
-    assert pick(15000, 0) == 0
-    vals = [pick(15000, r) for r in (0, 3000, 6000, 9000, 12000, 15000)]
-    assert vals == sorted(vals) and vals[0] == 0 and vals[-1] >= 16
-    assert all(v == 0 or (v % 8 == 0 and 8 <= v <= 32) for v in vals)
-    # the tail return against the partition, by the rule's own terms: 4 d bytes per returned row over the chip at
-    # 50000 bytes per tick, against the c CUs' share of 6 d f flops per routed row at the default rate
-    tail = lambda ret: 4.0 * ret * 2048 / 50000.0
-    ffn0 = 6.0 * 15000 * 2048 * 1408 / (256 * 31250.0)
-    assert pick(15000, 15000) == 16 and tail(15000) > ffn0 * 16 / 240
-    assert pick(15000, 3000) == 0 and tail(3000) <= ffn0 * 8 / 248
-    # the Mixtral-like and DeepSeek-V3-like shards return less than that costs: no partition
+    n1 = 1408 // 128
+    pick = lambda routed, ret, n_mt, fr=0.0, cr=0.0, n=256: B.moe_pick_consumer_cus_observed(s, n, routed, ret, n_mt,
+                                                                                              fr, cr)
+    assert pick(15000, 0, 60) == 0
+    # 60 row tiles x 11 = 660 first-GEMM items: 148 in the last round over 256 CUs, 108 workgroups free
+    assert 660 % 256 == 148 and _tail_fits(256, 3000, 2048, 660) and pick(15000, 3000, 60) == 0
+    assert not _tail_fits(256, 60000, 2048, 660) and pick(65536, 60000, 60) in (8, 16, 24, 32)
+    # full rounds (256 row tiles x 11 = 2816 = 11 x 256): no slack, a partition whatever is returned
+    assert pick(65536, 100, 256) == 8 and not _tail_fits(256, 100, 2048, 2816)
+    vals = [pick(15000, r, 256) for r in (3000, 6000, 9000, 12000, 15000)]
+    assert vals == sorted(vals) and vals[-1] > vals[0] and all(v % 8 == 0 and 8 <= v <= 32 for v in vals)
+    assert pick(15000, 15000, 256, cr=100.0) > pick(15000, 15000, 256, cr=450.0) > pick(15000, 15000, 256, cr=2000.0)
+    assert pick(15000, 12000, 256, fr=60000.0) >= pick(15000, 12000, 256, fr=31250.0)
+    assert pick(15000, 12000, 60, 0.0, 0.0) == pick(15000, 12000, 60, 31250.0, 450.0)
+    assert pick(15000, 15000, 256, cr=1.0, n=64) == 16  # capped at a quarter of the CUs
+    # the workloads as routed: the Mixtral-like and DeepSeek-V3-like shards return within the slack; d = f = 4096
+    # with one expert fills its first-GEMM rounds
     mix = shape()
-    assert B.moe_pick_consumer_cus_observed(mix, 256, 2048, 1536, 0.0, 0.0) == 0
+    assert B.moe_pick_consumer_cus_observed(mix, 256, 2043, 1510, 9, 0.0, 0.0) == 0
     ds = shape(R=8, tokens_per_owner=2048, num_global_experts=256, num_local_experts=32, top_k=8, d=7168, f=2048)
-    assert B.moe_pick_consumer_cus_observed(ds, 256, 24232, 21203, 0.0, 0.0) == 0
-    # slower copies take more consumers (where the return stays with a partition: faster copies also make a small
-    # partition cheaper than the tail return, so they can turn a pick of 0 into 8)
-    assert pick(15000, 15000, cr=100.0) > pick(15000, 15000, cr=450.0) > pick(15000, 15000, cr=2000.0) == 8
-    assert pick(15000, 12000, cr=450.0) == 0 and pick(15000, 12000, cr=2000.0) == 8
-    assert pick(15000, 12000, fr=60000.0) >= pick(15000, 12000, fr=31250.0)
-    assert pick(15000, 12000, 0.0, 0.0) == pick(15000, 12000, 31250.0, 450.0)
-    assert pick(15000, 15000, cr=1.0, n=64) == 16  # capped at a quarter of the CUs
-    # the shape-only estimate is the rule with 3 of 4 owners' rows returned and default rates
-    assert B.moe_pick_consumer_cus(s, 256) == pick(4000, 3000)
-    assert pick(100, 200) == -1
+    assert B.moe_pick_consumer_cus_observed(ds, 256, 24232, 21203, 114, 0.0, 0.0) == 0
+    sw1 = shape(tokens_per_owner=4096, num_global_experts=4, num_local_experts=1, d=4096, f=4096)
+    assert B.moe_pick_consumer_cus_observed(sw1, 256, 8181, 6076, 32, 0.0, 0.0) == 8
+    assert pick(100, 200, 1) == -1 and pick(100, 50, -1) == -1
 
 
 def test_landing_rejected_where_it_does_not_apply():

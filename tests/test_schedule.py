@@ -53,18 +53,37 @@ def schedule(s, mode, cus=0, window=0, self_rank=0, tile_order=0):
     return items, hdr, pure if tile_order == 0 else np.zeros_like(pure)
 
 
+def consumers_of(s, mode, cus, self_rank=0):
+    """The consumer count of the schedule: consumer_cus, or for 0 the launch's rule with default rates on the
+    batch (every row of the row tiles holding another owner's row counted as returned), as moe_ffn_schedule takes."""
+    if mode != 0 or cus < 0:
+        return 0
+    if cus > 0:
+        return cus
+    hdr, _, pure, order = tiles_of(s, self_rank)
+    m_real = int(hdr[:, 1].sum())
+    m_ret = int(hdr[order[: int((~pure).sum())], 1].sum())
+    return B.moe_pick_consumer_cus_observed(shape_of(s, self_rank), N_CU, m_real, m_ret, len(hdr), 0.0, 0.0)
+
+
 @pytest.mark.parametrize("mode,cus", [(0, 0), (1, 0), (0, 16)])
 @pytest.mark.parametrize("name", FULL)
 def test_full_workload_lists(name, mode, cus):
-    """The bench's launch configuration (the library's consumer partition, default band window) on every workload,
-    and a 16-CU partition."""
+    """The bench's launch configuration (the launch's consumer partition, default band window) on every workload,
+    and a 16-CU partition; the consumer count the schedule reports for the launch's rule is the rule's."""
     s = mi.spec(name)
     items, hdr, pure = schedule(s, mode, cus)
     waits = sm.check_list(items, len(hdr), s.d, s.f, pure)
     sm.simulate(items, waits, seed=1)
+    C = consumers_of(s, mode, cus)
+    assert items[:, 0].max() + 1 == N_CU  # every workgroup appears: C consumers first, then the producers
     if mode == 0:  # the consumer workgroups' own share is GEMM1 items only (they wait on nothing)
-        cons = items[:, 0] < (cus or B.moe_pick_consumer_cus(shape_of(s), N_CU))
+        cons = items[:, 0] < C
         assert (items[cons, 2] == 1).all()
+        if cus == 0 and name in ("deepseek", "mixtral", "skew", "sweep4", "sweep8", "sweep16"):
+            assert C == 0  # the return fits in the round-robin's slack
+        if cus == 0 and name in ("sweep1", "sweep2"):
+            assert C == 8  # full first-GEMM rounds: a partition
 
 
 @pytest.mark.parametrize("window", [0, 2, 16])
