@@ -29,6 +29,7 @@ _LIB = os.path.join(_HERE, "libmoe_inputs.so")
 STREAM_LOGITS = 1
 STREAM_BIAS = 2
 STREAM_X = 3
+STREAM_DOUT = 4  # the output gradient of the backward pass
 STREAM_W0 = 16  # expert e uses 16+3e (gate), 16+3e+1 (up), 16+3e+2 (down)
 
 
@@ -192,6 +193,13 @@ def weights(s: Spec, experts=None):
         fill(s.seed, base + 1, n, 0.0, sig, w1[i, s.f:].ctypes.data)    # up
         fill(s.seed, base + 2, n, 0.0, sig, w2[i].ctypes.data)          # down
     return w1, w2
+
+
+def d_out(s: Spec) -> np.ndarray:
+    """Gradient of the combined output dOut [T, d] for the backward pass, N(0,1): uint16 bf16 bits, or float32."""
+    if s.dtype == "bf16":
+        return normal_bf16(s.seed, STREAM_DOUT, (s.T, s.d))
+    return normal_f32(s.seed, STREAM_DOUT, (s.T, s.d))
 
 
 def inputs(s: Spec) -> dict:

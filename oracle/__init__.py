@@ -84,6 +84,8 @@ def _bind(lib):
     lib.orc_deliver.restype = i32
     lib.orc_combine.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp]
     lib.orc_combine.restype = i32
+    lib.orc_bwd_rows.argtypes = [i64, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.orc_bwd_rows.restype = i32
     lib.orc_round_bf16.argtypes = [ctypes.c_double]
     lib.orc_round_bf16.restype = ctypes.c_double
     lib.orc_bf16_bits.argtypes = [ctypes.c_double]
@@ -260,6 +262,71 @@ def combine(lay: dict, topk_w, recv, R: int, T_o: int, k: int, is_bf16: bool, li
 
 def round_bf16(v: float, lib=None) -> float:
     return (lib or load()).orc_round_bf16(float(v))
+
+
+def bwd_rows(tok, expert, w, x, w_gate_up, w_down, d_out, is_bf16: bool, want_y: bool = True,
+             want_parts: bool = True, lib=None) -> dict:
+    """Backward of the expert FFN for rows (token tok[i], local expert expert[i], routing weight w[i]): the row
+    gradient dX [n, d], and (want_parts) dY [n, d], h [n, f], dG | dU [n, 2f]; (want_y) the forward output y [n, d]
+    (orc_bwd_rows)."""
+    lib = lib or load()
+    tok = np.ascontiguousarray(tok, dtype=np.int32)
+    expert = np.ascontiguousarray(expert, dtype=np.int32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n = tok.size
+    _, d = x.shape
+    f = w_down.shape[2]
+    out = {"dx": np.empty((n, d))}
+    if want_parts:
+        out.update(dy=np.empty((n, d)), h=np.empty((n, f)), dgu=np.empty((n, 2 * f)))
+    if want_y:
+        out["y"] = np.empty((n, d))
+    g = lambda k: _p(out[k]) if k in out else None
+    rc = lib.orc_bwd_rows(n, _p(tok), _p(expert), _p(w), d, f, int(is_bf16), _p(np.ascontiguousarray(x)),
+                          _p(np.ascontiguousarray(w_gate_up)), _p(np.ascontiguousarray(w_down)),
+                          _p(np.ascontiguousarray(d_out)), _p(out["dx"]), g("dy"), g("h"), g("dgu"), g("y"))
+    assert rc == 0
+    return out
+
+
+def backward(s, inputs: dict, d_out: np.ndarray, lib=None) -> dict:
+    """Gradients of the MoE layer for the local experts, given dOut = dL/d(combined output) [T, d] (the review page,
+    "Where Pith is reading between the lines": MoE training's backward pass): dx [T, d] = sum over the token's
+    local slots of the rows' dX (rounded once in bf16 mode, as the combined output is), the routing weights'
+    gradient dw [T, k] = <dOut_t, y> (0 for slots routed elsewhere), and the weight gradients
+    dw_gate_up [E, 2f, d] = sum over the expert's rows of (dG | dU) x^T and dw_down [E, d, f] = sum of dY h^T
+    (numpy matmuls of the rows' parts, in double)."""
+    lib = lib or load()
+    idx, w = route(inputs["logits"], s.k, lib)
+    lo = 0  # self_rank 0 owns experts [0, E_l)
+    t, j = np.nonzero((idx >= lo) & (idx < lo + s.E_l))
+    e = idx[t, j] - lo
+    is_bf16 = s.dtype == "bf16"
+    x = inputs["x"]
+    r = bwd_rows(t, e, w[t, j], x, inputs["w_gate_up"], inputs["w_down"], d_out, is_bf16, lib=lib)
+    dx = np.zeros((s.T, s.d))
+    np.add.at(dx, t, r["dx"])
+    if is_bf16:
+        dx = round_bf16_array(dx, lib)
+    dout = _as_f64(d_out)
+    dw = np.zeros((s.T, s.k))
+    dw[t, j] = np.einsum("ic,ic->i", dout[t], r["y"])
+    xs = _as_f64(x)[t]
+    dwgu = np.zeros((s.E_l, 2 * s.f, s.d))
+    dwd = np.zeros((s.E_l, s.d, s.f))
+    for ee in range(s.E_l):
+        m = e == ee
+        dwgu[ee] = r["dgu"][m].T @ xs[m]
+        dwd[ee] = r["dy"][m].T @ r["h"][m]
+    return {"dx": dx, "dw": dw, "dw_gate_up": dwgu, "dw_down": dwd, "rows": (t, j), "parts": r,
+            "topk_idx": idx, "topk_w": w}
+
+
+def _as_f64(a: np.ndarray) -> np.ndarray:
+    """bf16 bits (uint16) or float32 to float64."""
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
 
 
 def run(s, inputs: dict, lib=None) -> dict:

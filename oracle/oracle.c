@@ -395,6 +395,81 @@ int orc_ffn_rows(int64_t nrows, const int32_t* src_row, const int32_t* expert, i
 }
 
 /* ------------------------------------------------------------------------------------------------ */
+/* Backward of the expert FFN for a list of rows (the review page, "Where Pith is reading between the lines": the same */
+/* signalling applied to MoE training's backward pass).  Row i is token tok[i] routed to local expert expert[i]      */
+/* with weight w[i]; d_out is the gradient of the combined output.  The combine made out = sum_j w_j y_j, so the     */
+/* row's output gradient is dY = w dOut[tok], and through y = h Wd^T, h = silu(g) u, g = x Wg^T, u = x Wu^T:        */
+/*   dH_n = sum_m dY_m Wd[m][n],  dU_n = dH_n silu(g_n),  dG_n = dH_n u_n silu'(g_n),                              */
+/*   silu'(g) = s (1 + g (1 - s)) with s = 1 / (1 + exp(-g)),                                                       */
+/*   dX_c = sum_n dG_n Wg[n][c] + dU_n Wu[n][c],                                                                    */
+/* and the routing weight's gradient is <dOut[tok], y>.  The weight gradients are sums over an expert's rows of     */
+/* dY h^T (Wd), dG x^T (Wg) and dU x^T (Wu); the caller forms them from the rows' dY, h and dG | dU.                */
+/* is_bf16: the GPU feeds its GEMMs bf16 operands, so the values it rounds are rounded here at the same points:    */
+/* dY = bf16(fp32(w * dOut)) (an fp32 product, then bf16), h = bf16(silu(g) u) as in the forward, dG and dU to      */
+/* bf16, and the row dX to bf16 (the rows the return delivers); y = bf16(...) as delivered.  fp32: no rounding.    */
+/* Every sum in double.                                                                                             */
+int orc_bwd_rows(int64_t nrows, const int32_t* tok, const int32_t* expert, const float* w, int d, int f, int is_bf16,
+                 const void* x, const void* w_gate_up, const void* w_down, const void* d_out, double* dx_row,
+                 double* dy_out, double* h_out, double* dgu_out, double* y_out) {
+  if (nrows < 0 || d <= 0 || f <= 0) return -1;
+#pragma omp parallel
+  {
+    double* xr = (double*)malloc(sizeof(double) * (size_t)d);
+    double* dy = (double*)malloc(sizeof(double) * (size_t)d);
+    double* h = (double*)malloc(sizeof(double) * (size_t)f);
+    double* dg = (double*)malloc(sizeof(double) * (size_t)f);
+    double* du = (double*)malloc(sizeof(double) * (size_t)f);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t i = 0; i < nrows; ++i) {
+      const int64_t t = tok[i], e = expert[i];
+      for (int c = 0; c < d; ++c) {
+        xr[c] = orc_ld(x, t * d + c, is_bf16);
+        const double o = orc_ld(d_out, t * d + c, is_bf16);
+        dy[c] = is_bf16 ? orc_round_bf16((double)(float)(w[i] * (float)o)) : (double)w[i] * o;
+      }
+      const int64_t wg0 = e * 2 * (int64_t)f * d, wu0 = wg0 + (int64_t)f * d, wd0 = e * (int64_t)d * f;
+      for (int n = 0; n < f; ++n) {
+        double g = 0.0, u = 0.0, dh = 0.0;
+        for (int c = 0; c < d; ++c) {
+          g += xr[c] * orc_ld(w_gate_up, wg0 + (int64_t)n * d + c, is_bf16);
+          u += xr[c] * orc_ld(w_gate_up, wu0 + (int64_t)n * d + c, is_bf16);
+        }
+        for (int m = 0; m < d; ++m) dh += dy[m] * orc_ld(w_down, wd0 + (int64_t)m * f + n, is_bf16);
+        const double s = 1.0 / (1.0 + exp(-g)), silu = g * s, dsilu = s * (1.0 + g * (1.0 - s));
+        h[n] = is_bf16 ? orc_round_bf16(silu * u) : silu * u;
+        du[n] = is_bf16 ? orc_round_bf16(dh * silu) : dh * silu;
+        dg[n] = is_bf16 ? orc_round_bf16(dh * u * dsilu) : dh * u * dsilu;
+      }
+      for (int c = 0; c < d; ++c) {
+        double acc = 0.0;
+        for (int n = 0; n < f; ++n)
+          acc += dg[n] * orc_ld(w_gate_up, wg0 + (int64_t)n * d + c, is_bf16) +
+                 du[n] * orc_ld(w_gate_up, wu0 + (int64_t)n * d + c, is_bf16);
+        dx_row[i * d + c] = is_bf16 ? orc_round_bf16(acc) : acc;
+      }
+      if (y_out != NULL)
+        for (int m = 0; m < d; ++m) {
+          double acc = 0.0;
+          for (int n = 0; n < f; ++n) acc += h[n] * orc_ld(w_down, wd0 + (int64_t)m * f + n, is_bf16);
+          y_out[i * d + m] = is_bf16 ? orc_round_bf16(acc) : acc;
+        }
+      if (dy_out != NULL) memcpy(dy_out + i * (int64_t)d, dy, sizeof(double) * (size_t)d);
+      if (h_out != NULL) memcpy(h_out + i * (int64_t)f, h, sizeof(double) * (size_t)f);
+      if (dgu_out != NULL) {
+        memcpy(dgu_out + i * 2 * (int64_t)f, dg, sizeof(double) * (size_t)f);
+        memcpy(dgu_out + i * 2 * (int64_t)f + f, du, sizeof(double) * (size_t)f);
+      }
+    }
+    free(xr);
+    free(dy);
+    free(h);
+    free(dg);
+    free(du);
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------------------------------ */
 /* Delivery: owner r receives, at row recv_off_{e,r} + i of its buffer, row padded_off_{e,r} + i of    */
 /* the expert output, for the n_{e,r} real rows of each group only.                                    */
 

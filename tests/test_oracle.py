@@ -674,3 +674,126 @@ def test_combine_allowance_admits_one_step_of_each_row_and_no_more(orc):
     # the ulp helper: bf16 spacing at binade edges and below the normal range
     np.testing.assert_array_equal(tolerance.bf16_ulp(np.array([1.0, 1.5, 2.0, -0.75, 0.0, 1e-40])),
                                   [2.0 ** -7, 2.0 ** -7, 2.0 ** -6, 2.0 ** -8, 2.0 ** -133, 2.0 ** -133])
+
+
+# ---- backward of the layer (orc_bwd_rows and oracle.backward) -----------------------------------------------------
+BWD_SPEC = mi.Spec("bwd_tiny", R=3, T_o=12, G=6, E_l=2, k=2, d=32, f=48, M=16, dtype="f32", seed=31)
+
+
+def _forward_loss(orc, s, lay, x, w1, w2, topk_w, d_out, is_bf16=False):
+    """L = <dOut, out> through the oracle's own forward (FFN over the layout, delivery, combine) at fixed routing."""
+    y_pad = oracle.ffn_layout(lay, x, w1, w2, is_bf16, s.M, orc)
+    recv = oracle.deliver(lay, y_pad, s.R, s.E_l, orc)
+    out = oracle.combine(lay, topk_w, recv, s.R, s.T_o, s.k, is_bf16, orc)
+    return float((d_out.astype(np.float64) * out).sum())
+
+
+def test_backward_matches_finite_differences_of_the_forward(orc):
+    """Each gradient of oracle.backward against central differences of the forward oracle (fp32 mode, no rounding):
+    L(theta + v) - L(theta - v) equals <grad, 2 v> up to third-order terms, for random directions v in x, the gate /
+    up weights, the down weights and the routing weights.  A dropped term, a wrong sign or a transposed operand in
+    any gradient fails this."""
+    s = BWD_SPEC
+    inp = mi.inputs(s)
+    d_out = mi.d_out(s)
+    b = oracle.backward(s, inp, d_out, orc)
+    idx, w = b["topk_idx"], b["topk_w"]
+    lay = oracle.layout(idx, s.R, s.T_o, s.G, s.E_l, s.k, s.M, s.mgb, 0, orc)
+    rng = np.random.default_rng(5)
+    base = dict(x=inp["x"], w1=inp["w_gate_up"], w2=inp["w_down"], topk_w=w)
+    grads = dict(x=b["dx"], w1=b["dw_gate_up"], w2=b["dw_down"], topk_w=b["dw"])
+    for name, g in grads.items():
+        a = base[name]
+        v = rng.standard_normal(a.shape) * 1e-3 * (np.abs(a).mean() + 1e-3)
+        if name == "topk_w":
+            v *= (idx < s.E_l)  # only slots routed to a local expert enter the local combine
+        plus, minus = (a + v).astype(np.float32), (a - v).astype(np.float32)
+        args_p, args_m = dict(base), dict(base)
+        args_p[name], args_m[name] = plus, minus
+        dl = _forward_loss(orc, s, lay, d_out=d_out, **args_p) - _forward_loss(orc, s, lay, d_out=d_out, **args_m)
+        pred = float((g * (plus.astype(np.float64) - minus.astype(np.float64))).sum())
+        assert abs(dl - pred) <= 1e-6 * abs(pred) + 1e-12, (name, dl, pred)
+
+
+def test_backward_matches_torch_autograd_fp64(orc):
+    """The same gradients from torch autograd over an independent float64 forward of the layer (per token: the sum
+    over its local slots of w * FFN_e(x)), fp32 mode."""
+    s = BWD_SPEC
+    inp = mi.inputs(s)
+    d_out = mi.d_out(s)
+    b = oracle.backward(s, inp, d_out, orc)
+    idx, w = b["topk_idx"], b["topk_w"]
+    x = torch.tensor(inp["x"], dtype=torch.float64, requires_grad=True)
+    w1 = torch.tensor(inp["w_gate_up"], dtype=torch.float64, requires_grad=True)
+    w2 = torch.tensor(inp["w_down"], dtype=torch.float64, requires_grad=True)
+    tw = torch.tensor(w, dtype=torch.float64, requires_grad=True)
+    out = torch.zeros(s.T, s.d, dtype=torch.float64)
+    for t in range(s.T):
+        for j in range(s.k):
+            e = int(idx[t, j])
+            if e >= s.E_l:
+                continue
+            g = w1[e, : s.f] @ x[t]
+            u = w1[e, s.f:] @ x[t]
+            out[t] = out[t] + tw[t, j] * (w2[e] @ (torch.nn.functional.silu(g) * u))
+    (out * torch.tensor(d_out, dtype=torch.float64)).sum().backward()
+    for got, ref in ((b["dx"], x.grad), (b["dw_gate_up"], w1.grad), (b["dw_down"], w2.grad), (b["dw"], tw.grad)):
+        np.testing.assert_allclose(got, ref.numpy(), rtol=1e-9, atol=1e-12)
+
+
+def _bf16(a):
+    return torch.tensor(np.asarray(a, dtype=np.float64)).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def test_backward_bf16_rounding_points(orc):
+    """bf16 mode rounds where the GPU rounds, and only there, checked against independent evaluations (numpy products,
+    torch's bf16 conversion): dY = bf16 of the fp32 product w * dOut, exactly; h equals the forward oracle's h bit for
+    bit; dG, dU and the rows' dX are bf16 roundings of numpy's double evaluation from the rounded operands (one bf16
+    step allowed where numpy's summation order lands on the other side of a tie); dx is the rounded sum of the rows."""
+    s = mi.spec("tiny")
+    inp = mi.inputs(s)
+    d_out = mi.d_out(s)
+    b = oracle.backward(s, inp, d_out, orc)
+    t, j = b["rows"]
+    r = b["parts"]
+    w, idx = b["topk_w"], b["topk_idx"]
+    dout32 = oracle._as_f64(d_out).astype(np.float32)
+    np.testing.assert_array_equal(r["dy"], _bf16(w[t, j][:, None].astype(np.float32) * dout32[t]))
+    fwd = oracle.ffn_rows_ex(t.astype(np.int32), idx[t, j].astype(np.int32), inp["x"], inp["w_gate_up"],
+                             inp["w_down"], True, max_cand=0, want_h=True, want_vec=False, lib=orc)
+    np.testing.assert_array_equal(r["h"], fwd["h"])
+    np.testing.assert_array_equal(r["y"], fwd["y"])
+    x = oracle._as_f64(inp["x"])[t]
+    w1 = oracle._as_f64(inp["w_gate_up"])
+    w2 = oracle._as_f64(inp["w_down"])
+    e = idx[t, j]
+    g = np.einsum("ind,id->in", w1[e, : s.f], x)
+    u = np.einsum("ind,id->in", w1[e, s.f:], x)
+    dh = np.einsum("imn,im->in", w2[e], r["dy"])
+    sg = 1.0 / (1.0 + np.exp(-g))
+    step = lambda v: np.abs(v) * 2.0 ** -7 + 1e-40
+    for got, exact in ((r["dgu"][:, : s.f], dh * u * sg * (1 + g * (1 - sg))), (r["dgu"][:, s.f:], dh * g * sg)):
+        assert (np.abs(got - _bf16(exact)) <= step(exact)).all()
+        assert (got == _bf16(got)).all()
+    dxr = np.einsum("ind,in->id", w1[e], r["dgu"])
+    assert (np.abs(r["dx"] - _bf16(dxr)) <= step(dxr)).all() and (r["dx"] == _bf16(r["dx"])).all()
+    summed = np.zeros((s.T, s.d))
+    np.add.at(summed, t, r["dx"])
+    np.testing.assert_array_equal(b["dx"], _bf16(summed))
+
+
+def test_backward_no_local_slot_gives_zero(orc):
+    """A token none of whose slots is routed to a local expert gets a zero dx row and zero routing gradients; an
+    expert with no rows gets zero weight gradients."""
+    s = BWD_SPEC
+    inp = mi.inputs(s)
+    lg = inp["logits"].copy()
+    lg[0, :] = -10.0
+    lg[0, 2:4] = 10.0  # token 0 to experts 2 and 3, both on another rank
+    lg[:, 1] = -50.0   # local expert 1 chosen by nobody
+    inp["logits"] = lg
+    b = oracle.backward(s, inp, mi.d_out(s), orc)
+    assert (b["topk_idx"][0] >= s.E_l).all()
+    assert (b["dx"][0] == 0).all() and (b["dw"][0] == 0).all()
+    assert (b["topk_idx"] != 1).all()
+    assert (b["dw_gate_up"][1] == 0).all() and (b["dw_down"][1] == 0).all()
