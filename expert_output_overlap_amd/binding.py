@@ -24,7 +24,8 @@ EXPORTS = ["moe_last_error", "moe_version", "moe_route", "moe_layout_capacity_ro
            "moe_layout_bind", "moe_layout_build", "moe_read_status", "moe_ffn_flags_count", "moe_pick_consumer_cus",
            "moe_pick_consumer_cus_observed",
            "moe_expert_ffn_overlap", "moe_expert_ffn_overlap_noalloc", "moe_ffn_schedule",
-           "moe_combine", "moe_set_kernel_timing", "moe_kernel_times"]
+           "moe_combine", "moe_set_kernel_timing", "moe_kernel_times", "moe_bwd_flags_count",
+           "moe_expert_ffn_backward", "moe_combine_backward"]
 
 
 class moe_shape(ctypes.Structure):
@@ -46,6 +47,14 @@ class moe_overlap_cfg(ctypes.Structure):
     _fields_ = [("consumer_cus", ctypes.c_int32), ("mode", ctypes.c_int32), ("epoch", ctypes.c_uint32),
                 ("band_window", ctypes.c_int32), ("watchdog_ticks", ctypes.c_uint64),
                 ("timestamps", ctypes.c_void_p), ("tile_order", ctypes.c_int32), ("x_tokens", ctypes.c_void_p)]
+
+
+BWD_FIELDS = ["topk_idx", "topk_w", "x_pad", "w_gate_up", "w_down", "d_out", "dy_pad", "dh_ws", "h_ws", "dgu_ws",
+              "dx_pad", "dx_recv", "dw_gate_up", "dw_down"]
+
+
+class moe_bwd_args(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in BWD_FIELDS]
 
 
 class MoeError(RuntimeError):
@@ -80,6 +89,9 @@ def lib():
             "moe_combine": ([ps, pl, vp, vp, vp, vp], i32),
             "moe_ffn_schedule": ([ps, i32, pc, i32, i32, vp, vp, vp, i64, ctypes.POINTER(ctypes.c_int64)], i32),
             "moe_set_kernel_timing": ([i32], i32), "moe_kernel_times": ([ctypes.POINTER(ctypes.c_double)], i32),
+            "moe_bwd_flags_count": ([ps], i64),
+            "moe_expert_ffn_backward": ([ps, pl, ctypes.POINTER(moe_bwd_args), vp, pc, vp], i32),
+            "moe_combine_backward": ([ps, pl, vp, vp, vp, vp, vp, vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -208,3 +220,23 @@ def moe_kernel_times():
     out = (ctypes.c_double * 4)()
     _check("moe_kernel_times", lib().moe_kernel_times(out))
     return out[0], out[1], out[2], int(out[3])
+
+
+def moe_bwd_flags_count(shape: moe_shape) -> int:
+    return lib().moe_bwd_flags_count(ctypes.byref(shape))
+
+
+def moe_expert_ffn_backward(shape: moe_shape, layout: moe_layout, tensors: dict, dx_recv, flags, cfg: moe_overlap_cfg,
+                            stream=None) -> int:
+    """tensors: the moe_bwd_args fields other than dx_recv, as device tensors."""
+    ptrs = _ptr_array(dx_recv)
+    a = moe_bwd_args(**{k: (ctypes.cast(ptrs, ctypes.c_void_p) if k == "dx_recv" else _ptr(tensors[k]))
+                        for k in BWD_FIELDS})
+    return _check("moe_expert_ffn_backward", lib().moe_expert_ffn_backward(
+        ctypes.byref(shape), ctypes.byref(layout), ctypes.byref(a), _ptr(flags), ctypes.byref(cfg), _stream(stream)))
+
+
+def moe_combine_backward(shape: moe_shape, layout: moe_layout, d_out, y_recv, dx_recv, dx, dw_route, stream=None) -> int:
+    return _check("moe_combine_backward", lib().moe_combine_backward(
+        ctypes.byref(shape), ctypes.byref(layout), _ptr(d_out), _ptr_array(y_recv), _ptr_array(dx_recv), _ptr(dx),
+        _ptr(dw_route), _stream(stream)))

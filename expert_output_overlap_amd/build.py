@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_overlap.so")
-SOURCES = ["api.cpp", "route.hip", "layout.hip", "ffn.hip", "combine.hip"]
+SOURCES = ["api.cpp", "route.hip", "layout.hip", "ffn.hip", "bwd.hip", "combine.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # packed fp32 vector ops stay off in every GPU code object

@@ -657,4 +657,116 @@ int moe_combine(const moe_shape* s, const moe_layout* L, const float* topk_w, vo
   return MOE_OK;
 }
 
+int64_t moe_bwd_flags_count(const moe_shape* s) {
+  if (!check_shape(s).empty() || s->dtype != MOE_BF16 || s->f % 128) return -1;
+  return bwd_flag_words(s->d, s->f, layout_offsets(s).cap_mtiles);
+}
+
+int moe_expert_ffn_backward(const moe_shape* s, const moe_layout* L, const moe_bwd_args* b, uint32_t* flags,
+                            const moe_overlap_cfg* cfg, void* stream) {
+  const std::string e = check_shape(s);
+  if (!e.empty()) return fail(MOE_EINVAL, e);
+  if (s->dtype != MOE_BF16) return fail(MOE_EINVAL, "the backward pass is for bf16");
+  if (s->f % 128) return fail(MOE_EINVAL, "the backward pass needs f to be a multiple of 128");
+  if (!layout_ok(L) || !b || !cfg || !flags) return fail(MOE_EINVAL, "null layout, arguments, flags or cfg");
+  if (L->cap_tiles * s->tile_m != L->cap_rows) return fail(MOE_EINVAL, "layout bound for another tile_m");
+  if ((L->cap_rows + 256) * 4ll * s->f >= (1ll << 32)) return fail(MOE_EINVAL, "rows x 2f too large for 32-bit offsets");
+  const int64_t T = (int64_t)s->R * s->tokens_per_owner;
+  if (!b->x_pad || !b->w_gate_up || !b->w_down || !b->dy_pad || !b->dh_ws || !b->h_ws || !b->dgu_ws || !b->dx_pad ||
+      !b->dx_recv || !b->dw_gate_up || !b->dw_down || (T > 0 && (!b->topk_idx || !b->topk_w || !b->d_out)))
+    return fail(MOE_EINVAL, "null pointer");
+  for (int r = 0; r < s->R; ++r)
+    if (!b->dx_recv[r]) return fail(MOE_EINVAL, "null receive buffer");
+  if ((uintptr_t)flags % 8 != 0) return fail(MOE_EINVAL, "flags must be 8-byte aligned");
+  if (cfg->epoch == 0) return fail(MOE_EINVAL, "epoch must be nonzero");
+  if (cfg->mode != 0 && cfg->mode != 1) return fail(MOE_EINVAL, "the backward pass runs in mode 0 or 1");
+  if (cfg->x_tokens) return fail(MOE_EINVAL, "x_tokens is for the forward call");
+  hipStream_t st = (hipStream_t)stream;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MOE_EHIP, "hipGetDevice failed");
+  const int n_cu = device_cus(dev);
+  if (n_cu <= 0) return fail(MOE_EHIP, "cannot query the CU count");
+  if (cfg->consumer_cus < -1 || cfg->consumer_cus > n_cu / 2)
+    return fail(MOE_EINVAL, "consumer_cus must be -1 (none), 0 (library default) or in [1, CUs/2]");
+  // the default partition: 8 CUs (a quarter of a small device's), which return the dX rows while the producers run
+  // the weight-gradient items that end the list
+  const int C_def = std::max(1, std::min(8, n_cu / 4));
+  const int C = cfg->consumer_cus > 0 ? cfg->consumer_cus : cfg->consumer_cus == 0 ? C_def : 0;
+  BwdLaunch p;
+  p.R = s->R;
+  p.E = s->num_local_experts;
+  p.d = s->d;
+  p.f = s->f;
+  p.k = s->top_k;
+  p.M = s->tile_m;
+  p.lo = s->self_rank * s->num_local_experts;
+  p.self_rank = s->self_rank;
+  p.L = L;
+  p.x_pad = b->x_pad;
+  p.w_gate_up = b->w_gate_up;
+  p.w_down = b->w_down;
+  p.topk_idx = b->topk_idx;
+  p.topk_w = b->topk_w;
+  p.d_out = b->d_out;
+  p.dy_pad = b->dy_pad;
+  p.dh_ws = b->dh_ws;
+  p.h_ws = b->h_ws;
+  p.dgu_ws = b->dgu_ws;
+  p.dx_pad = b->dx_pad;
+  p.dx_recv = b->dx_recv;
+  p.dw_gate_up = b->dw_gate_up;
+  p.dw_down = b->dw_down;
+  p.flags = flags;
+  p.epoch = cfg->epoch;
+  p.watchdog_ticks = cfg->watchdog_ticks ? cfg->watchdog_ticks : 200000000ull;
+  p.cap_mtiles = layout_offsets(s).cap_mtiles;
+  if (launch_bwd_dy(p, st)) return fail(MOE_EHIP, "dY launch failed");
+  CallEvents ce;
+  const bool timed = g_timing && timing_begin(&ce) == 0;
+  hipEvent_t ev0 = timed ? ce.e[0] : nullptr, ev1 = timed ? ce.e[1] : nullptr;
+  if (timed) ce.n = 1;
+  const int n_cons = cfg->mode == 0 ? C : 0;
+  if (launch_bwd_ffn(p, n_cu, n_cons, cfg->mode == 0, st, ev0, ev1)) {
+    if (timed) ce.destroy();
+    return fail(MOE_EHIP, "backward launch failed");
+  }
+  if (cfg->mode == 1) {
+    if (timed) {
+      ce.n = 2;
+      ce.cons = true;
+    }
+    if (launch_bwd_consumer(p, n_cu, st, timed ? ce.e[2] : nullptr, timed ? ce.e[3] : nullptr)) {
+      if (timed) ce.destroy();
+      return fail(MOE_EHIP, "consumer launch failed");
+    }
+  }
+  if (timed) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_events.push_back(ce);
+  }
+  return MOE_OK;
+}
+
+int moe_combine_backward(const moe_shape* s, const moe_layout* L, const void* d_out, void* const* y_recv,
+                         void* const* dx_recv, void* dx, float* dw_route, void* stream) {
+  const std::string e = check_shape(s);
+  if (!e.empty()) return fail(MOE_EINVAL, e);
+  if (s->dtype != MOE_BF16) return fail(MOE_EINVAL, "the backward pass is for bf16");
+  if (!layout_ok(L)) return fail(MOE_EINVAL, "layout not bound");
+  const int64_t T = (int64_t)s->R * s->tokens_per_owner;
+  if (T > 0 && (!d_out || !y_recv || !dx_recv || !dx || !dw_route)) return fail(MOE_EINVAL, "null pointer");
+  for (int r = 0; T > 0 && r < s->R; ++r)
+    if (!y_recv[r] || !dx_recv[r]) return fail(MOE_EINVAL, "null receive buffer");
+  BwdLaunch p{};
+  p.R = s->R;
+  p.d = s->d;
+  p.k = s->top_k;
+  p.L = L;
+  p.d_out = d_out;
+  p.dx_recv = dx_recv;
+  if (launch_bwd_combine(p, s->tokens_per_owner, L->combine_plan, y_recv, dx, dw_route, (hipStream_t)stream))
+    return fail(MOE_EHIP, "combine backward launch failed");
+  return MOE_OK;
+}
+
 }  // extern "C"

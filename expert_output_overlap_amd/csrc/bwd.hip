@@ -1,0 +1,710 @@
+// The backward pass of the expert FFN (review page, "Where Pith is reading between the lines": the producer-consumer
+// signalling applied to MoE training's backward pass, which has the same GEMM-then-transfer structure).  Given the
+// gradient of the combined output, per routed row p of token t, slot weight w and local expert e:
+//   dY = bf16(w dOut[t])                                   (k_bwd_dy: the gradient's dispatch into the padded layout)
+//   dH = dY Wd,  g = x Wg^T,  u = x Wu^T                   (recomputed, as the forward computes them)
+//   h = bf16(silu(g) u),  dU = bf16(dH silu(g)),  dG = bf16(dH u silu'(g))
+//   dX = (dG | dU) (Wg | Wu)                                (rows returned to their owners: the overlapped transfer)
+//   dWd[e] = sum_p dY^T h,  dWgu[e] = sum_p (dG | dU)^T x   (fp32, over the expert's rows)
+// and the combine's backward (k_bwd_combine): dx[t] = sum of the token's delivered dX rows, and the routing weight's
+// gradient <dOut[t], y> from the forward's delivered rows.
+//
+// One persistent launch runs four kinds of items, each a 256 x 256 output tile of bf16 MFMAs (32x32x16) over
+// k-tiles of 64, in list order: H (row tile, 256 columns of f) -> dH, fp32, flag fh; G (row tile, 128 columns of f)
+// -> h, dG, dU after its dH tile's flag, flag fg; X (row tile, 256 columns of d, k-split) -> dX rows after the fg
+// flags of its split, split-K partial sums summed in split order by the last to arrive, flag fx, which the
+// consumer role waits on to copy the other owners' rows (the self owner's rows are stored straight into its buffer,
+// as in the forward); W (expert, 256 x 256 tile of dWd or dWgu, k over the expert's rows) after the fg flags of the
+// expert's row tiles.  Every wait is on an earlier item of the list, and each workgroup runs its items in list
+// order, so the earliest unfinished item can always run.
+//
+// Operands whose k runs along rows of memory (x, dY, (dG | dU) as the rows of a row tile; Wgu rows for g and u) are
+// staged as in the forward.  Operands whose k runs down columns (Wd and Wgu as the second operand of dH and dX; all
+// four operands of the weight gradients, whose k is the expert's rows) are staged as 64 rows x 256 columns, and
+// their MFMA fragments are read with the LDS transpose read (ds_read_b64_tr_b16): in a group of 16 lanes, lane j
+// gives the address of row r0 + j / 4, columns c0 + 4 (j % 4) .. + 3, and lane l receives column c0 + l of rows
+// r0 .. r0 + 3, so two reads give a lane the 8 consecutive k of its column that the MFMA takes.  Such a tile keeps
+// 32-byte column granule g of row r at granule g ^ (r & 3), so that the four rows of a read fall in different banks.
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "common.h"
+#include "consumer.h"
+#include "launch.h"
+#include "tile_util.h"
+
+#define BWD_THREADS 512  // 8 waves: 2 (rows) x 4 (columns) of 128 x 64 wave tiles
+#define BWD_BM 256
+#define BWD_BK 64
+#define BWD_STAGE (2 * BWD_BM * BWD_BK * 2)  // A and B tiles of one k-tile, 64 KB
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+struct BwdArgs {
+  const unsigned char* x;    // x_pad [cap_rows, d] bf16
+  const unsigned char* w1;   // w_gate_up [E, 2f, d]
+  const unsigned char* w2;   // w_down [E, d, f]
+  const unsigned char* dy;   // dY rows [cap_rows, d]
+  float* dh;                 // [cap_rows, f]
+  unsigned char* h;          // [cap_rows, f] bf16
+  unsigned char* dgu;        // [cap_rows, 2f] bf16: dG | dU
+  unsigned char* dxp;        // dX rows of the other owners [cap_rows, d]
+  unsigned char* self_recv;  // the self owner's dX buffer
+  float* dw1;                // [E, 2f, d]
+  float* dw2;                // [E, d, f]
+  int d, f, E, S;            // S: k-splits of the dX items
+  int n_h, n_g, n_x;         // column tiles of H (256 of f), G (128 of f), X (256 of d) items
+  const int32_t* mtile_desc;
+  const int32_t* mt_order;
+  const int32_t* scalars;
+  int sc_nmt;
+  int32_t* status;
+  uint32_t* fh;
+  uint32_t* fg;
+  uint32_t* fx;
+  uint64_t* scount;  // [cap_mtiles][n_x] arrivals of the dX k-splits
+  float* partial;    // [cap_mtiles][n_x][S][256 x 256] fp32 partial sums
+  uint32_t epoch;
+  uint64_t budget;
+  int n_cons;  // consumer workgroups (the first n_cons of the grid)
+  int join;    // producers take copy units once their items are done
+  ConsumerArgs cons;
+};
+
+// 4-byte and 2-byte stores with the device-scope cache policy (data other workgroups read inside the launch)
+__device__ __forceinline__ void store4_coherent(void* p, float v) {
+  asm volatile("global_store_dword %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void store2_coherent(void* p, uint32_t v) {
+  asm volatile("global_store_short %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
+
+__device__ __forceinline__ uint32_t bf16_bits(float v) {  // round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+// Fragment of a transposed-staged tile (64 rows of k x 256 columns) at column cb, k-step ks: the 8 consecutive k of
+// column cb + lane % 32 starting at 16 ks + 8 (lane / 32), as the MFMA takes them.
+__device__ __forceinline__ bf16x8_t frag_tr(const unsigned char* st, int cb, int ks, int lane) {
+  const int gi = lane >> 4, j = lane & 15;
+  const int n = cb + 16 * (gi & 1) + 4 * (j & 3);
+  s16x4_t v[2];
+#pragma unroll
+  for (int hk = 0; hk < 2; ++hk) {
+    const int k = 16 * ks + 8 * (gi >> 1) + 4 * hk + (j >> 2);
+    const unsigned char* p = st + k * 512 + ((((n >> 4) ^ (k & 3)) << 5) | ((n & 15) << 1));
+    v[hk] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
+  }
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Fragment of a row-staged tile (256 rows x 64 k, 16-byte k-chunk c of row r at slot c ^ (r & 7) ^ ((r >> 3) & 1)):
+// row rb + lane % 32, k 16 ks + 8 (lane / 32) ..
+__device__ __forceinline__ bf16x8_t frag_row(const unsigned char* st, int rb, int ks, int lane) {
+  const int swz = (lane & 7) ^ ((lane >> 3) & 1);
+  return __builtin_bit_cast(bf16x8_t,
+                            *(const u32x4_t*)(st + (rb + (lane & 31)) * 128 + (((2 * ks + (lane >> 5)) ^ swz) << 4)));
+}
+
+// Item kinds
+enum { BK_H = 1, BK_G = 2, BK_X = 3, BK_WD = 4, BK_WGU = 5 };
+
+struct BwdItem {
+  int kind, mt, nt, s;  // H/G/X: row tile, column tile, split
+  int e, it, jt;        // W: expert, output row tile, output column tile
+};
+
+__device__ __forceinline__ BwdItem bwd_item(const BwdArgs& a, int n_mt, int i) {
+  BwdItem it{};
+  const int NH = n_mt * a.n_h, NG = n_mt * a.n_g, NX = n_mt * a.n_x * a.S;
+  const int nd = (a.d + 255) / 256, nf = (a.f + 255) / 256, n2 = 2 * a.f / 256;
+  if (i < NH) {
+    it.kind = BK_H;
+    it.mt = i / a.n_h;
+    it.nt = i - it.mt * a.n_h;
+  } else if ((i -= NH) < NG) {
+    it.kind = BK_G;
+    it.mt = i / a.n_g;
+    it.nt = i - it.mt * a.n_g;
+  } else if ((i -= NG) < NX) {
+    it.kind = BK_X;
+    const int per = a.n_x * a.S, p = i / per, r = i - p * per;
+    it.mt = a.mt_order[p];  // remote first: the row tiles holding another owner's rows come first
+    it.s = r / a.n_x;
+    it.nt = r - it.s * a.n_x;
+  } else {
+    i -= NX;
+    const int per = nd * nf + n2 * nd;
+    it.e = i / per;
+    const int r = i - it.e * per;
+    if (r < nd * nf) {
+      it.kind = BK_WD;
+      it.it = r / nf;
+      it.jt = r - it.it * nf;
+    } else {
+      it.kind = BK_WGU;
+      it.it = (r - nd * nf) / nd;
+      it.jt = (r - nd * nf) - it.it * nd;
+    }
+  }
+  return it;
+}
+
+__device__ __forceinline__ int bwd_n_items(const BwdArgs& a, int n_mt) {
+  const int nd = (a.d + 255) / 256, nf = (a.f + 255) / 256, n2 = 2 * a.f / 256;
+  return n_mt * (a.n_h + a.n_g + a.n_x * a.S) + a.E * (nd * nf + n2 * nd);
+}
+
+// Shared state of an item (in LDS)
+struct BwdShared {
+  int rows[BWD_BM];  // padded rows of the row tile
+  int hdr[MOE_MT_HDR];
+  int run_first, run_count, k_rows;  // W items: the expert's run of row tiles and its row count
+  int stop;
+};
+
+template <int KIND>
+__device__ __forceinline__ bool bwd_tile(const BwdArgs& a, unsigned char* smem, BwdShared& sh, const BwdItem& it) {
+  constexpr bool A_TR = KIND == BK_WD || KIND == BK_WGU;        // A staged by columns (k along rows of memory)
+  constexpr bool B_TR = KIND != BK_G;                            // B staged by columns
+  constexpr int MI = 4, NI = 2, A_BYTES = BWD_BM * BWD_BK * 2;
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int d = a.d, f = a.f;
+  const int e = (KIND == BK_WD || KIND == BK_WGU) ? it.e : sh.hdr[0];
+  const int n_rows = (KIND == BK_WD || KIND == BK_WGU) ? 0 : sh.hdr[1];
+
+  // ---- operand geometry ------------------------------------------------------------------------------------
+  // A: H dY rows (K = d); G x rows (K = d); X (dG | dU) rows (K = 2f, split s); WD dY by columns, WGU (dG | dU) by
+  // columns (K = the expert's rows).  B: H Wd by columns (k = d index, columns of f); G Wgu rows (gate | up);
+  // X Wgu by columns (k = 2f index, columns of d); WD h by columns; WGU x by columns.
+  int K, k0 = 0;
+  if (KIND == BK_H || KIND == BK_G) K = d;
+  else if (KIND == BK_X) {
+    K = 2 * f / a.S;
+    k0 = it.s * K;
+  } else K = sh.k_rows;
+  const int nk = (K + BWD_BK - 1) / BWD_BK;
+  const unsigned char* Abase;
+  uint32_t a_stride;  // bytes per row of A's memory
+  if (KIND == BK_H) { Abase = a.dy; a_stride = d * 2; }
+  else if (KIND == BK_G) { Abase = a.x; a_stride = d * 2; }
+  else if (KIND == BK_X) { Abase = a.dgu; a_stride = 4 * f; }
+  else if (KIND == BK_WD) { Abase = a.dy; a_stride = d * 2; }
+  else { Abase = a.dgu; a_stride = 4 * f; }
+  const unsigned char* Bbase;
+  uint32_t b_stride;
+  int b_cols = 0, b_col0 = 0;  // transposed B: columns of its memory, and this tile's first column
+  if (KIND == BK_H) { Bbase = a.w2 + (int64_t)e * d * f * 2; b_stride = f * 2; b_cols = f; b_col0 = it.nt * 256; }
+  else if (KIND == BK_G) { Bbase = a.w1 + (int64_t)e * 2 * f * d * 2; b_stride = d * 2; }
+  else if (KIND == BK_X) { Bbase = a.w1 + (int64_t)e * 2 * f * d * 2; b_stride = d * 2; b_cols = d; b_col0 = it.nt * 256; }
+  else if (KIND == BK_WD) { Bbase = a.h; b_stride = f * 2; b_cols = f; b_col0 = it.jt * 256; }
+  else { Bbase = a.x; b_stride = d * 2; b_cols = d; b_col0 = it.jt * 256; }
+  const int a_cols = KIND == BK_WD ? d : 2 * f, a_col0 = it.it * 256;  // transposed A
+
+  // the memory row of k index kk (0 .. nk*64) of a transposed operand whose k runs over memory rows: weights (H, X)
+  // by k directly; W items through the expert's row list (absent rows read the expert's first row; zeroed below)
+  auto krow = [&](int kk) -> int64_t {
+    if (KIND == BK_H || KIND == BK_X) return (int64_t)(k0 + kk);
+    const int r = kk < sh.k_rows ? kk : 0, t = sh.run_first + (r >> 8);
+    return a.mtile_desc[(int64_t)t * MOE_MT_FIELDS + MOE_MT_HDR + (r & 255)];
+  };
+
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  // row-staged loads: wave instruction q (0..31) fills rows 8q .. 8q+7, lane -> row 8q + lane/8, slot lane & 7
+  // holding k-chunk (lane & 7) ^ (lane >> 3) ^ (q & 1)
+  const uint32_t chunk0 = (uint32_t)(((lane & 7) ^ (lane >> 3)) << 4);
+  auto load_row_tile = [&](const unsigned char* base, uint32_t stride, int kt, uint32_t dst, bool glu) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int q = wave * 4 + jj, r = 8 * q + (lane >> 3);
+      int64_t mrow;
+      if (glu) mrow = r < 128 ? it.nt * 128 + r : f + it.nt * 128 + (r - 128);  // gate rows, then up rows
+      else mrow = sh.rows[r < n_rows ? r : 0];                                   // absent rows read a real row
+      const uint32_t off = (uint32_t)(mrow * stride) + (uint32_t)(k0 + kt * BWD_BK) * 2 + (chunk0 ^ ((q & 1) << 4));
+      dma16(base, off, dst + q * 1024);
+    }
+  };
+  // column-staged loads: wave instruction q (0..31) fills k-rows 2q, 2q+1 (lanes 0-31, 32-63), slot lane & 31 of
+  // the row holding 16-byte column chunk c with (c / 2) ^ (k & 3) = slot / 2; columns past the matrix read column 0
+  auto load_col_tile = [&](const unsigned char* base, uint32_t stride, int cols, int col0, int kt, uint32_t dst) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int q = wave * 4 + jj, k = 2 * q + (lane >> 5), cs = lane & 31;
+      const int c = (((cs >> 1) ^ (k & 3)) << 1) | (cs & 1);
+      const int col = col0 + 8 * c < cols ? col0 + 8 * c : 0;
+      dma16(base, (uint32_t)(krow(kt * BWD_BK + k) * stride) + (uint32_t)col * 2u, dst + q * 1024);
+    }
+  };
+  auto load_tile = [&](int kt, int stage) {
+    const uint32_t sa = lds0 + stage * BWD_STAGE, sb = sa + A_BYTES;
+    if (A_TR) load_col_tile(Abase, a_stride, a_cols, a_col0, kt, sa);
+    else load_row_tile(Abase, a_stride, kt, sa, false);
+    if (B_TR) load_col_tile(Bbase, b_stride, b_cols, b_col0, kt, sb);
+    else load_row_tile(Bbase, b_stride, kt, sb, true);
+  };
+  // W items: the k-rows of the last k-tile past the expert's rows hold real rows' values; zero them in both tiles
+  auto zero_tail = [&](int stage) {
+    const int cnt = sh.k_rows - (nk - 1) * BWD_BK;
+    if (!A_TR || cnt >= BWD_BK) return;
+    unsigned char* st = smem + stage * BWD_STAGE;
+    for (int i = tid; i < (BWD_BK - cnt) * 2 * 32; i += BWD_THREADS) {  // 16-byte chunks of the rows, A then B
+      const int t = i / ((BWD_BK - cnt) * 32), r = cnt + (i / 32) % (BWD_BK - cnt), c = i & 31;
+      *(u32x4_t*)(st + t * A_BYTES + r * 512 + c * 16) = u32x4_t{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+  };
+
+  f32x16_t acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.f;
+
+  if (nk > 0) {
+    load_tile(0, 0);
+    wait_loads_barrier();
+    if (nk == 1) zero_tail(0);
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) load_tile(kt + 1, (kt + 1) & 1);
+    const unsigned char* sa = smem + (kt & 1) * BWD_STAGE;
+    const unsigned char* sb = sa + A_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8_t fa[MI], fb[NI];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+        fa[mi] = A_TR ? frag_tr(sa, wm * 128 + mi * 32, ks, lane) : frag_row(sa, wm * 128 + mi * 32, ks, lane);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        if (B_TR) fb[ni] = frag_tr(sb, wn * 64 + ni * 32, ks, lane);
+        else fb[ni] = frag_row(sb, ni == 0 ? wn * 32 : 128 + wn * 32, ks, lane);  // gate block, up block
+      }
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+    }
+    // this wave's fragment reads of k-tile kt and loads of k-tile kt+1 are done; then everyone's are
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (kt + 2 == nk) zero_tail((kt + 1) & 1);
+  }
+
+  // ---- epilogues ---------------------------------------------------------------------------------------------
+  // accumulator (mi, ni), element q: row wm*128 + mi*32 + 8 (q / 4) + 4 (lane / 32) + q % 4, column
+  // wn*64 + ni*32 + lane % 32 (G: ni = 0 the gate block, 1 the up block of columns wn*32 + lane % 32)
+  auto row_of = [&](int mi, int q) { return wm * 128 + mi * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3); };
+  if (KIND == BK_H) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int r = row_of(mi, q);
+        if (r >= n_rows) continue;
+        float* rowp = a.dh + (int64_t)sh.rows[r] * f;
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const int col = it.nt * 256 + wn * 64 + ni * 32 + (lane & 31);
+          if (col < f) store4_coherent(rowp + col, acc[mi][ni][q]);
+        }
+      }
+    publish(&a.fh[(int64_t)it.mt * a.n_h + it.nt], a.epoch);
+    return true;
+  }
+  if (KIND == BK_G) {
+    // dH of these columns comes from the H item of the 256 columns that hold them
+    if (tid == 0) sh.stop = poll_flags(&a.fh[(int64_t)it.mt * a.n_h + (it.nt * 128) / 256], 1, a.epoch, a.budget,
+                                       a.status, 1);
+    __syncthreads();
+    if (sh.stop) {
+      if (sh.stop == 1 && tid == 0) set_status(a.status, MOE_ETIMEOUT);
+      return false;
+    }
+    flag_acquire();
+    const int col = it.nt * 128 + wn * 32 + (lane & 31);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int r = row_of(mi, q);
+        if (r >= n_rows) continue;
+        const int64_t p = sh.rows[r];
+        const float g = acc[mi][0][q], u = acc[mi][1][q];
+        const float dh = a.dh[p * f + col];
+        const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+        const float silu = silu_fast(g);  // the forward's h, bit for bit
+        const float dsilu = sg * (1.0f + g * (1.0f - sg));
+        store2_coherent(a.h + (p * f + col) * 2, bf16_bits(silu * u));
+        store2_coherent(a.dgu + (p * 2 * f + col) * 2, bf16_bits(dh * u * dsilu));
+        store2_coherent(a.dgu + (p * 2 * f + f + col) * 2, bf16_bits(dh * silu));
+      }
+    publish(&a.fg[(int64_t)it.mt * a.n_g + it.nt], a.epoch);
+    return true;
+  }
+  if (KIND == BK_X) {
+    const int64_t tile = (int64_t)it.mt * a.n_x + it.nt;
+    if (a.S > 1) {
+      // every split stores its fp32 partial sums (thread t keeps its accumulators at float4 chunk
+      // ((mi * 2 + ni) * 4 + q4) * 512 + t of its slot) and counts itself in; the last to arrive sums the slots in
+      // split order, the same association whichever split completes the tile
+      f32x4_t* slot = (f32x4_t*)(a.partial + tile * a.S * (256 * 256)) + (int64_t)it.s * (256 * 256 / 4);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x16_t v = acc[mi][ni];
+            const f32x4_t w4 = {v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3]};
+            store16_coherent(slot + ((mi * NI + ni) * 4 + q4) * BWD_THREADS + tid, __builtin_bit_cast(u32x4_t, w4));
+          }
+      wait_stores();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __syncthreads();
+      if (tid == 0) sh.stop = (int)arrive(&a.scount[tile], a.epoch);
+      __syncthreads();
+      if (sh.stop != a.S - 1) return true;  // not the last split
+      flag_acquire();
+      const f32x4_t* slots = (const f32x4_t*)(a.partial + tile * a.S * (256 * 256));
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int o = ((mi * NI + ni) * 4 + q4) * BWD_THREADS + tid;
+            f32x4_t t = __builtin_nontemporal_load(slots + o);
+            for (int sp = 1; sp < a.S; ++sp) t += __builtin_nontemporal_load(slots + (int64_t)sp * (256 * 256 / 4) + o);
+            acc[mi][ni][4 * q4] = t[0];
+            acc[mi][ni][4 * q4 + 1] = t[1];
+            acc[mi][ni][4 * q4 + 2] = t[2];
+            acc[mi][ni][4 * q4 + 3] = t[3];
+          }
+    }
+    // bf16 rows: the self owner's rows straight into its buffer, the other owners' into the padded layout
+    const int lo = sh.hdr[MT_SELF_LO], ns = sh.hdr[MT_SELF_N], delta = sh.hdr[MT_SELF_DELTA];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int r = row_of(mi, q);
+        if (r >= n_rows) continue;
+        const int p = sh.rows[r];
+        const bool self = (unsigned)(p - lo) < (unsigned)ns;
+        unsigned char* rowp = self ? a.self_recv + (int64_t)(p + delta) * d * 2 : a.dxp + (int64_t)p * d * 2;
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const int col = it.nt * 256 + wn * 64 + ni * 32 + (lane & 31);
+          if (col < d) store2_coherent(rowp + col * 2, bf16_bits(acc[mi][ni][q]));
+        }
+      }
+    publish(&a.fx[tile], a.epoch);
+    return true;
+  }
+  // W items: the fp32 tile into the weight gradient (read by nobody inside the launch)
+  float* out = KIND == BK_WD ? a.dw2 + (int64_t)e * d * f : a.dw1 + (int64_t)e * 2 * f * d;
+  const int out_rows = KIND == BK_WD ? d : 2 * f, out_cols = KIND == BK_WD ? f : d;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int r = it.it * 256 + row_of(mi, q);
+      if (r >= out_rows) continue;
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const int col = it.jt * 256 + wn * 64 + ni * 32 + (lane & 31);
+        if (col < out_cols) out[(int64_t)r * out_cols + col] = acc[mi][ni][q];
+      }
+    }
+  return true;
+}
+
+__global__ __launch_bounds__(BWD_THREADS, 1) void k_bwd_ffn(BwdArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ BwdShared sh;
+  launch_acquire();  // drop cache lines older than this launch (the publish protocol in common.h)
+  if (load_status(a.status) != 0) return;
+  const int C = a.n_cons, tid = threadIdx.x;
+  if (a.join && blockIdx.x == 0) consumer_stamp(a.cons);
+  const int n_mt = a.scalars[a.sc_nmt];
+  // producers only (a consumer workgroup's index minus C is negative, and would start a negative item index)
+  const int n_items = (int)blockIdx.x < C ? 0 : bwd_n_items(a, n_mt);
+  const int G = gridDim.x - C;
+  int bid = (int)blockIdx.x < C ? n_items : (int)blockIdx.x - C;
+  if ((int)blockIdx.x >= C && (G & 7) == 0 && (C & 7) == 0) bid = (bid & 7) * (G >> 3) + (bid >> 3);  // one XCD
+  for (int i = bid; i < n_items; i += G) {
+    const BwdItem it = bwd_item(a, n_mt, i);
+    __syncthreads();  // the previous item is done with sh
+    bool ok = true;
+    if (it.kind <= BK_X) {
+      const int32_t* dsc = a.mtile_desc + (int64_t)it.mt * MOE_MT_FIELDS;
+      if (tid < MOE_MT_HDR) sh.hdr[tid] = dsc[tid];
+      if (tid < BWD_BM) sh.rows[tid] = dsc[MOE_MT_HDR + tid];
+      __syncthreads();
+      if (it.kind == BK_X) {  // the (dG | dU) columns of this split: the G items of their 128-column blocks
+        if (tid == 0) {
+          const int kk = 2 * a.f / a.S, c0 = it.s * kk;
+          int st = 0;
+          for (int c = c0; c < c0 + kk && !st; c += 128)
+            st = poll_flags(&a.fg[(int64_t)it.mt * a.n_g + (c % a.f) / 128], 1, a.epoch, a.budget, a.status, 1);
+          sh.stop = st;
+        }
+        __syncthreads();
+        if (sh.stop) {
+          if (sh.stop == 1 && tid == 0) set_status(a.status, MOE_ETIMEOUT);
+          return;
+        }
+        flag_acquire();
+        ok = bwd_tile<BK_X>(a, smem, sh, it);
+      } else if (it.kind == BK_H) {
+        ok = bwd_tile<BK_H>(a, smem, sh, it);
+      } else {
+        ok = bwd_tile<BK_G>(a, smem, sh, it);
+      }
+    } else {
+      // the expert's run of row tiles (none: no rows, a zero tile)
+      if (tid == 0) {
+        sh.run_first = 0;
+        sh.run_count = 0;
+        sh.k_rows = 0;
+      }
+      __syncthreads();
+      for (int t = tid; t < n_mt; t += BWD_THREADS) {
+        const int32_t* dsc = a.mtile_desc + (int64_t)t * MOE_MT_FIELDS;
+        if (dsc[0] == it.e && dsc[2] == t) {  // the first tile of the expert's run
+          sh.run_first = t;
+          sh.run_count = dsc[3];
+        }
+      }
+      __syncthreads();
+      if (tid == 0 && sh.run_count > 0) {
+        const int last = sh.run_first + sh.run_count - 1;
+        sh.k_rows = (sh.run_count - 1) * MOE_MT_ROWS + a.mtile_desc[(int64_t)last * MOE_MT_FIELDS + 1];
+        // WD reads h columns jt*256 ..; WGU reads (dG | dU) columns it*256 ..: their G items in every row tile
+        int st = 0;
+        const int c0 = it.kind == BK_WD ? it.jt * 256 : it.it * 256, c1 = min(c0 + 256, it.kind == BK_WD ? a.f : 2 * a.f);
+        for (int t = sh.run_first; t <= last && !st; ++t)
+          for (int c = c0; c < c1 && !st; c += 128)
+            st = poll_flags(&a.fg[(int64_t)t * a.n_g + (c % a.f) / 128], 1, a.epoch, a.budget, a.status, 1);
+        sh.stop = st;
+      } else if (tid == 0) {
+        sh.stop = 0;
+      }
+      __syncthreads();
+      if (sh.stop) {
+        if (sh.stop == 1 && tid == 0) set_status(a.status, MOE_ETIMEOUT);
+        return;
+      }
+      flag_acquire();
+      ok = it.kind == BK_WD ? bwd_tile<BK_WD>(a, smem, sh, it) : bwd_tile<BK_WGU>(a, smem, sh, it);
+    }
+    if (!ok) return;
+  }
+  // the consumer workgroups return dX rows from the start; with join, producers too once their items are done
+  if (a.join || (int)blockIdx.x < C) consumer_role(a.cons);
+}
+
+// dY rows of the padded layout: row p (token t, local expert e of its band) = bf16(w dOut[t]) with w the weight of
+// t's slot routed to e (an fp32 product, then bf16).  One wavefront per row, 16-byte lanes.
+__global__ __launch_bounds__(256) void k_bwd_dy(const uint16_t* __restrict__ d_out, const int32_t* __restrict__ topk_idx,
+                                                const float* __restrict__ topk_w, const int32_t* __restrict__ row_src,
+                                                const int32_t* __restrict__ tile_expert, const int32_t* scalars, int M,
+                                                int k, int lo, int d, uint16_t* __restrict__ dy) {
+  const int64_t n_pad = scalars[SC_MPAD];
+  const int lane = threadIdx.x & 63;
+  for (int64_t p = blockIdx.x * 4 + (threadIdx.x >> 6); p < n_pad; p += (int64_t)gridDim.x * 4) {
+    const int t = row_src[p];
+    if (t < 0) continue;  // padding
+    const int eg = lo + tile_expert[p / M];
+    float w = 0.f;
+    for (int j = 0; j < k; ++j)
+      if (topk_idx[(int64_t)t * k + j] == eg) w = topk_w[(int64_t)t * k + j];
+    const uint4* src = (const uint4*)(d_out + (int64_t)t * d);
+    uint4* dst = (uint4*)(dy + p * d);
+    for (int c = lane; c < d / 8; c += 64) {
+      const uint4 v = src[c];
+      const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float lo16 = __uint_as_float(in[q] << 16) * w, hi16 = __uint_as_float(in[q] & 0xffff0000u) * w;
+        o[q] = bf16_bits(lo16) | (bf16_bits(hi16) << 16);
+      }
+      dst[c] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
+// The combine's backward, one workgroup per token (owner r = t / T_o): dx[t] = bf16 of the fp32 sum of the token's
+// delivered dX rows (slot order), dw[t, j] = <dOut[t], y> over the forward's delivered row of slot j (fp32), 0 for a
+// slot routed elsewhere.
+__global__ __launch_bounds__(256) void k_bwd_combine(const uint16_t* __restrict__ d_out, const int32_t* __restrict__ plan,
+                                                     RecvPtrs y_recv, RecvPtrs dx_recv, int T_o, int k, int d,
+                                                     uint16_t* __restrict__ dx, float* __restrict__ dw) {
+  const int64_t t = blockIdx.x;
+  const int r = (int)(t / T_o), tid = threadIdx.x;
+  __shared__ float s_part[8][4];
+  const uint16_t* o = d_out + t * d;
+  for (int c = tid; c < d; c += 256) {
+    float acc = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int pr = plan[t * k + j];
+      if (pr >= 0) acc += bf16_to_f32(((const uint16_t*)dx_recv.p[r])[(int64_t)pr * d + c]);
+    }
+    dx[t * d + c] = (uint16_t)bf16_bits(acc);
+  }
+  for (int j = 0; j < k; ++j) {
+    const int pr = plan[t * k + j];
+    if (pr < 0) {
+      if (tid == 0) dw[t * k + j] = 0.f;
+      continue;
+    }
+    const uint16_t* y = (const uint16_t*)y_recv.p[r] + (int64_t)pr * d;
+    float s = 0.f;
+    for (int c = tid; c < d; c += 256) s += bf16_to_f32(o[c]) * bf16_to_f32(y[c]);
+    s = wave_sum_f(s);
+    if ((tid & 63) == 0) s_part[j & 7][tid >> 6] = s;
+    __syncthreads();
+    if (tid == 0) dw[t * k + j] = (s_part[j & 7][0] + s_part[j & 7][1]) + (s_part[j & 7][2] + s_part[j & 7][3]);
+    __syncthreads();
+  }
+}
+
+// ---- host side -------------------------------------------------------------------------------------------------
+
+namespace {
+void bwd_fill_consumer(ConsumerArgs& c, const BwdLaunch& p, const uint32_t* flags, uint64_t* claim, int n_x) {
+  c.y = (const uint4*)p.dx_pad;
+  for (int r = 0; r < MOE_MAX_OWNERS; ++r) c.recv.p[r] = r < p.R ? p.dx_recv[r] : nullptr;
+  c.seg_desc = p.L->seg_desc;
+  c.seg_mtiles = p.L->seg_mtiles;
+  c.seg_sched = p.L->seg_sched;
+  c.scalars = p.L->scalars;
+  c.status = p.L->status;
+  c.flags = flags;
+  c.claim = claim;
+  c.stamp = next_stamp();
+  c.epoch = p.epoch;
+  c.n_nt = n_x;
+  c.row_vec = p.d * 2 / 16;
+  c.budget = p.watchdog_ticks;
+  c.ts = nullptr;
+  c.self_rank = p.self_rank;
+  c.obs = nullptr;
+}
+
+// the dX items' k-splits: about as many 256 x 256 output tiles as CUs, each split a multiple of 128 columns of
+// (dG | dU) (the G items' width), at most 8
+int bwd_splits(int d, int f) {
+  const int want = std::min(8, std::max(1, (4 * f + d) / (2 * d)));
+  for (int c = want; c > 1; --c)
+    if ((2 * f / 128) % c == 0) return c;
+  return 1;
+}
+
+struct BwdCarve {
+  int64_t fh, fg, fx, scount, partial, claim, total;  // 4-byte words
+};
+BwdCarve bwd_carve(int d, int f, int64_t cap_mtiles) {
+  auto up = [](int64_t v) { return (v + 63) / 64 * 64; };
+  const int64_t n_h = (f + 255) / 256, n_g = f / 128, n_x = (d + 255) / 256, S = bwd_splits(d, f);
+  BwdCarve c;
+  c.fx = 0;  // the consumer's flags first (consumer_role indexes them from its flag pointer)
+  c.fh = up(cap_mtiles * n_x);
+  c.fg = c.fh + up(cap_mtiles * n_h);
+  c.scount = c.fg + up(cap_mtiles * n_g);
+  c.partial = c.scount + up(2 * cap_mtiles * n_x);
+  c.claim = c.partial + (S > 1 ? cap_mtiles * n_x * S * 256 * 256 : 0);
+  c.total = c.claim + 2;
+  return c;
+}
+}  // namespace
+
+int64_t bwd_flag_words(int d, int f, int64_t cap_mtiles) { return bwd_carve(d, f, cap_mtiles).total; }
+
+int launch_bwd_dy(const BwdLaunch& p, hipStream_t st) {
+  int64_t blocks = (p.L->cap_rows + 3) / 4;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks > 0)
+    hipLaunchKernelGGL(k_bwd_dy, dim3((unsigned)blocks), dim3(256), 0, st, (const uint16_t*)p.d_out, p.topk_idx,
+                       p.topk_w, p.L->row_src, p.L->tile_expert, p.L->scalars, p.M, p.k, p.lo, p.d,
+                       (uint16_t*)p.dy_pad);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_bwd_ffn(const BwdLaunch& p, int grid, int n_cons, int join, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  const BwdCarve c = bwd_carve(p.d, p.f, p.cap_mtiles);
+  BwdArgs a;
+  a.x = (const unsigned char*)p.x_pad;
+  a.w1 = (const unsigned char*)p.w_gate_up;
+  a.w2 = (const unsigned char*)p.w_down;
+  a.dy = (const unsigned char*)p.dy_pad;
+  a.dh = p.dh_ws;
+  a.h = (unsigned char*)p.h_ws;
+  a.dgu = (unsigned char*)p.dgu_ws;
+  a.dxp = (unsigned char*)p.dx_pad;
+  a.self_recv = (unsigned char*)p.dx_recv[p.self_rank];
+  a.dw1 = p.dw_gate_up;
+  a.dw2 = p.dw_down;
+  a.d = p.d;
+  a.f = p.f;
+  a.E = p.E;
+  a.S = bwd_splits(p.d, p.f);
+  a.n_h = (p.f + 255) / 256;
+  a.n_g = p.f / 128;
+  a.n_x = (p.d + 255) / 256;
+  a.mtile_desc = p.L->mtile_desc;
+  a.mt_order = p.L->mt_order;
+  a.scalars = p.L->scalars;
+  a.sc_nmt = SC_NR + p.R;
+  a.status = p.L->status;
+  a.fh = p.flags + c.fh;
+  a.fg = p.flags + c.fg;
+  a.fx = p.flags + c.fx;
+  a.scount = (uint64_t*)(p.flags + c.scount);
+  a.partial = (float*)(p.flags + c.partial);
+  a.epoch = p.epoch;
+  a.budget = p.watchdog_ticks;
+  a.n_cons = n_cons;
+  a.join = join;
+  bwd_fill_consumer(a.cons, p, p.flags + c.fx, (uint64_t*)(p.flags + c.claim), a.n_x);
+  hipExtLaunchKernelGGL(k_bwd_ffn, dim3(grid), dim3(BWD_THREADS), 2 * BWD_STAGE, st, ev0, ev1, 0, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+__global__ __launch_bounds__(256) void k_bwd_consumer(ConsumerArgs c) {
+  launch_acquire();
+  if (blockIdx.x == 0) consumer_stamp(c);
+  consumer_role(c);
+}
+
+int launch_bwd_consumer(const BwdLaunch& p, int n_cons, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  const BwdCarve c = bwd_carve(p.d, p.f, p.cap_mtiles);
+  ConsumerArgs cons;
+  bwd_fill_consumer(cons, p, p.flags + c.fx, (uint64_t*)(p.flags + c.claim), (p.d + 255) / 256);
+  hipExtLaunchKernelGGL(k_bwd_consumer, dim3(n_cons), dim3(256), 0, st, ev0, ev1, 0, cons);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_bwd_combine(const BwdLaunch& p, int T_o, const int32_t* plan, void* const* y_recv, void* dx, float* dw,
+                       hipStream_t st) {
+  RecvPtrs yr, xr;
+  for (int r = 0; r < MOE_MAX_OWNERS; ++r) {
+    yr.p[r] = r < p.R ? y_recv[r] : nullptr;
+    xr.p[r] = r < p.R ? p.dx_recv[r] : nullptr;
+  }
+  const int64_t T = (int64_t)p.R * T_o;
+  if (T > 0)
+    hipLaunchKernelGGL(k_bwd_combine, dim3((unsigned)T), dim3(256), 0, st, (const uint16_t*)p.d_out, plan, yr, xr, T_o,
+                       p.k, p.d, (uint16_t*)dx, dw);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}

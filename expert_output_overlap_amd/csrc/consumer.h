@@ -55,7 +55,7 @@ __device__ __forceinline__ void consumer_stamp(const ConsumerArgs& a) {
 #define CONSUMER_MAX_THREADS 512
 
 // Runs in a workgroup of up to CONSUMER_MAX_THREADS threads (whole waves) until every unit has been handed out.
-__device__ void consumer_role(const ConsumerArgs& a) {
+__device__ __forceinline__ void consumer_role(const ConsumerArgs& a) {
   // a window of up to blockDim.x scheduled segments: their ids and, relative to the window, the units before them
   __shared__ int s_seg[CONSUMER_MAX_THREADS];
   __shared__ uint32_t s_pre[CONSUMER_MAX_THREADS + 1];

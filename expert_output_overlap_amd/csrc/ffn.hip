@@ -27,10 +27,8 @@
 #include "consumer.h"
 #include "item_list.h"
 #include "launch.h"
+#include "tile_util.h"
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // 16-byte chunk (native vector: stays in VGPRs)
 
 template <typename T>
 struct Mfma;
@@ -296,30 +294,6 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_gemm(GemmArgs a) {
 #define FFN_THREADS 512  // 8 waves, two per SIMD
 #define FFN_WAVES (FFN_THREADS / 64)
 
-// global_load_lds_dwordx4 in its scalar-base form: lane i moves 16 bytes from base + off into LDS at
-// m0 + 16 * i.  The statement leaves M0 as it found it: it saves M0 in a scratch SGPR, sets it, issues the load
-// (which reads M0 when it issues) and restores it, so no code outside depends on the compiler honouring an M0
-// clobber (M0 is a reserved register, which an inline-asm clobber list may not name).
-__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_addr) {
-  // base and lds_addr are the same in every lane; readfirstlane puts them in scalar registers.  The load takes its
-  // LDS address from M0, which needs one wait state after an SALU write (the first s_nop); the second covers a
-  // read of M0 right after the statement (the compiler inserts such wait states only around its own M0 writes)
-  const uint64_t b = (uint64_t)base;
-  const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
-                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0\n\ts_nop 0"
-      : "=&s"(saved)
-      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(off), "s"((const void*)sb)
-      : "memory");
-}
-
-// this wave's loads have landed in LDS, then the workgroup barrier: after it every wave's have
-__device__ __forceinline__ void wait_loads_barrier() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// SiLU with the hardware reciprocal (about 1 ulp), rounded to bf16 right after
-__device__ __forceinline__ float silu_fast(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 
 // The expert FFN as one persistent launch.  Work items:
@@ -404,39 +378,6 @@ __device__ bool wait_flags(const uint32_t* fl, int n, uint32_t epoch, uint64_t b
 // write back the whole L2 of the XCD instead, once per published tile, which stalls every workgroup on that XCD
 // (nothing the tile needs is dirty in L2: its data went out with device-scope stores).  The reader's side is in
 // common.h.
-// 16 bytes with the device-scope cache policy (the one agent-scope atomic stores use), as one dwordx4 store:
-// two 8-byte atomic stores per 16 bytes measured 2-3 times slower.  The compiler does not count this store, so
-// whoever needs it complete waits with an explicit vmcnt(0) (wait_stores).  Nor does it see that the registers of
-// v are store data: on this chip a VALU write to the data registers of a store wider than 8 bytes needs two wait
-// states after the store (else the store can send the new value), which the compiler inserts only for stores it
-// recognises, so the s_nop is part of the statement.
-__device__ __forceinline__ void store16_coherent(void* p, u32x4_t v) {
-  asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(p), "v"(v) : "memory");
-}
-
-__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-__device__ __forceinline__ void publish(uint32_t* flag, uint32_t epoch) {
-  wait_stores();  // this wave's stores are complete
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __syncthreads();  // and every wave's
-  if (threadIdx.x == 0) __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Arrival count of this call at a counter that holds (epoch << 32) | count: returns how many arrived before.  A
-// counter that still carries another call's epoch counts from zero, so no reset between calls is needed.
-__device__ __forceinline__ uint32_t arrive(uint64_t* ctr, uint32_t epoch) {
-  uint64_t old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  for (;;) {
-    const bool cur = (uint32_t)(old >> 32) == epoch;
-    const uint64_t nw = cur ? old + 1 : (((uint64_t)epoch << 32) | 1u);
-    if (__hip_atomic_compare_exchange_strong(ctr, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT))
-      return cur ? (uint32_t)old : 0u;
-  }
-}
-
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x8_t __attribute__((ext_vector_type(8)));
 
 // 16 fp32 partial sums of one thread in one 32 x 32 accumulator block (the layout the splits store them in:
@@ -1085,6 +1026,15 @@ int ffn_splits(int dtype, int d, int f) {
   return 1;
 }
 
+// A nonzero value distinct for every launch that runs the consumer role (the unit counter's stamp).
+uint32_t next_stamp() {
+  static std::atomic<uint32_t> seq{0};
+  uint32_t v;
+  do v = ++seq;
+  while (v == 0);
+  return v;
+}
+
 namespace {
 struct FlagCarve {
   int64_t flags2, flags1, scount, partial, claim, flags0, gcount, gclaim, obs, total;  // offsets and size in words
@@ -1116,14 +1066,6 @@ FlagCarve flag_carve(int dtype, int d, int f, int64_t cap_mtiles) {
   return c;
 }
 
-// A nonzero value distinct for every launch that runs the consumer role (the unit counter's stamp).
-uint32_t next_stamp() {
-  static std::atomic<uint32_t> seq{0};
-  uint32_t v;
-  do v = ++seq;
-  while (v == 0);
-  return v;
-}
 
 void fill_consumer(ConsumerArgs& c, const FfnLaunch& p, int n_nt2) {
   c.y = (const uint4*)p.y_pad;

@@ -89,3 +89,43 @@ int launch_flags_clear(int dtype, int d, int f, int64_t cap_mtiles, uint32_t* fl
 // Resets the n timestamp entries of a call (starts to the largest value, ends to zero).
 int launch_ts_init(uint64_t* timestamps, int64_t n, hipStream_t st);
 int launch_combine(const CombineLaunch& p, hipStream_t st);
+
+// Backward pass of the expert FFN (bwd.hip).
+struct BwdLaunch {
+  int R, E, d, f, k, M, lo, self_rank;
+  const moe_layout* L;
+  const void* x_pad;
+  const void* w_gate_up;
+  const void* w_down;
+  const int32_t* topk_idx;
+  const float* topk_w;
+  const void* d_out;
+  void* dy_pad;
+  float* dh_ws;
+  void* h_ws;
+  void* dgu_ws;
+  void* dx_pad;
+  void* const* dx_recv;
+  float* dw_gate_up;
+  float* dw_down;
+  uint32_t* flags;
+  uint32_t epoch;
+  uint64_t watchdog_ticks;
+  int64_t cap_mtiles;
+};
+// 4-byte words of the backward flag buffer.
+int64_t bwd_flag_words(int d, int f, int64_t cap_mtiles);
+// dY rows of the padded layout (bf16 of w dOut).
+int launch_bwd_dy(const BwdLaunch& p, hipStream_t st);
+// The backward launch on `grid` CUs: the first n_cons workgroups run the dX return only; with join, the others take
+// copy units once their items are done.
+int launch_bwd_ffn(const BwdLaunch& p, int grid, int n_cons, int join, hipStream_t st, hipEvent_t ev0 = nullptr,
+                   hipEvent_t ev1 = nullptr);
+// The dX return alone (`n_cons` workgroups).
+int launch_bwd_consumer(const BwdLaunch& p, int n_cons, hipStream_t st, hipEvent_t ev0 = nullptr,
+                        hipEvent_t ev1 = nullptr);
+// The combine's backward: dx (bf16 [T, d]) and the routing weights' gradient dw (fp32 [T, k]).
+int launch_bwd_combine(const BwdLaunch& p, int T_o, const int32_t* plan, void* const* y_recv, void* dx, float* dw,
+                       hipStream_t st);
+// A nonzero value distinct for every launch that opens a copy-unit counter.
+uint32_t next_stamp();

@@ -83,6 +83,51 @@ class MoePath:
                                  self.flags, cfg, stream)
         return epoch
 
+    # ---- backward ---------------------------------------------------------------------------------------------
+    def bwd_buffers(self):
+        """The backward call's workspaces and outputs, allocated on first use (bf16 only)."""
+        if getattr(self, "_bwd", None) is None:
+            cap, d, f, z = self.L.cap_rows, self.d, self.f, dict(device=self.device)
+            n = B.moe_bwd_flags_count(self.shape)
+            if n < 0:
+                raise B.MoeError("moe_bwd_flags_count", -1, "shape has no backward pass")
+            self._bwd = {
+                "dy_pad": torch.empty(cap, d, dtype=torch.bfloat16, **z),
+                "dh_ws": torch.empty(cap, f, dtype=torch.float32, **z),
+                "dgu_ws": torch.empty(cap, 2 * f, dtype=torch.bfloat16, **z),
+                "dx_pad": torch.empty(cap, d, dtype=torch.bfloat16, **z),
+                "dx_recv": [torch.empty(max(self.recv_cap, 1), d, dtype=torch.bfloat16, **z) for _ in range(self.R)],
+                "dw_gate_up": torch.empty(self.E_l, 2 * f, d, dtype=torch.float32, **z),
+                "dw_down": torch.empty(self.E_l, d, f, dtype=torch.float32, **z),
+                "flags": torch.zeros(n, dtype=torch.int32, **z),
+                "dx": torch.empty(max(self.T, 1), d, dtype=torch.bfloat16, **z),
+                "dw_route": torch.empty(max(self.T, 1), self.k, dtype=torch.float32, **z),
+            }
+            self.bwd_epoch = 0
+        return self._bwd
+
+    def backward(self, d_out: torch.Tensor, w_gate_up, w_down, mode=0, consumer_cus=0, watchdog_ticks=0, epoch=None,
+                 stream=None):
+        """The expert FFN's backward with the dX return (moe_expert_ffn_backward), for the routing, layout and x_pad
+        of the last forward; the forward's h workspace receives the recomputed h."""
+        b = self.bwd_buffers()
+        if epoch is None:
+            self.bwd_epoch += 1
+            epoch = self.bwd_epoch
+        cfg = B.moe_overlap_cfg(consumer_cus, mode, epoch, 0, watchdog_ticks, None, 0, None)
+        t = {"topk_idx": self.topk_idx, "topk_w": self.topk_w, "x_pad": self.x_pad, "w_gate_up": w_gate_up,
+             "w_down": w_down, "d_out": d_out, "h_ws": self.h, **{k: b[k] for k in
+                                                                   ("dy_pad", "dh_ws", "dgu_ws", "dx_pad",
+                                                                    "dw_gate_up", "dw_down")}}
+        B.moe_expert_ffn_backward(self.shape, self.L, t, b["dx_recv"], b["flags"], cfg, stream)
+        return epoch
+
+    def combine_backward(self, d_out: torch.Tensor, stream=None):
+        """dx and the routing weights' gradient (moe_combine_backward) from the delivered dX rows and the forward's
+        delivered y rows."""
+        b = self.bwd_buffers()
+        B.moe_combine_backward(self.shape, self.L, d_out, self.recv, b["dx_recv"], b["dx"], b["dw_route"], stream)
+
     def combine(self, topk_w: torch.Tensor | None = None, stream=None):
         B.moe_combine(self.shape, self.L, self.topk_w if topk_w is None else topk_w, self.recv, self.out, stream)
 

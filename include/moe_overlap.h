@@ -285,8 +285,59 @@ int moe_combine(const moe_shape* s, const moe_layout* L, const float* topk_w, vo
 
 /* ---- kernel timing ------------------------------------------------------------------------------- */
 
-/* While enabled (nonzero), every moe_expert_ffn_overlap call of this process times each of its launches with
- * a pair of HIP events that the launch itself records (hipExtLaunchKernel: the kernel's start and end, no marker
+/* ---- backward pass ------------------------------------------------------------------------------
+ * The review page ("Where Pith is reading between the lines") notes that MoE training's backward pass has the
+ * forward's GEMM-then-transfer structure, so the same tile signalling applies.  Given dOut = dL/d(out) of the
+ * combined output, per routed row (token t, slot weight w, local expert e), with g = x Wg^T, u = x Wu^T, s =
+ * silu(g), h = bf16(s u) as in the forward:
+ *   dY = bf16(w dOut[t]) (fp32 product),  dH = dY Wd,  dU = bf16(dH s),  dG = bf16(dH u silu'(g)),
+ *   dX = bf16((dG | dU) (Wg | Wu)),  dWd[e] = sum dY^T h,  dWgu[e] = sum (dG | dU)^T x (fp32 over e's rows);
+ * the rows' dX are returned to their token owners (the overlapped transfer), and the combine's backward gives
+ * dx[t] = bf16(sum of t's delivered dX rows) and the routing weights' gradient <dOut[t], y>.  bf16 only; f a
+ * multiple of 128. */
+typedef struct {
+  const int32_t* topk_idx; /* (device) [T, k] the forward's routing */
+  const float* topk_w;     /* (device) [T, k] */
+  const void* x_pad;       /* (device) [cap_rows, d] the forward's input rows (gathered or landed) */
+  const void* w_gate_up;   /* (device) [E_l, 2f, d] */
+  const void* w_down;      /* (device) [E_l, d, f] */
+  const void* d_out;       /* (device) [T, d] bf16 gradient of the combined output */
+  void* dy_pad;            /* (device) [cap_rows, d] workspace: dY rows in the padded layout */
+  float* dh_ws;            /* (device) [cap_rows, f] fp32 workspace: dH */
+  void* h_ws;              /* (device) [cap_rows, f] workspace: h, recomputed */
+  void* dgu_ws;            /* (device) [cap_rows, 2f] workspace: dG | dU */
+  void* dx_pad;            /* (device) [cap_rows, d] workspace: dX rows of the other owners */
+  void* const* dx_recv;    /* host array of R device pointers: owner r receives the dX of its rows at the rows where
+                              the forward delivered their y (recv_off layout) */
+  float* dw_gate_up;       /* (device) [E_l, 2f, d] fp32 weight gradient, written (not accumulated) */
+  float* dw_down;          /* (device) [E_l, d, f] fp32 weight gradient, written */
+} moe_bwd_args;
+
+/* Size, in 4-byte words, of the backward call's flag buffer (dX tile flags first, then dH and h flags, the k-split
+ * arrival counters and fp32 partial sums of dX, the copy-unit counter); -1 for an invalid shape, fp32, or f not a
+ * multiple of 128.  Zero it once; afterwards it is epoch-valued like the forward's. */
+int64_t moe_bwd_flags_count(const moe_shape* s);
+
+/* The backward of the expert FFN with the return of the rows' dX to their owners: the dY rows (k_bwd_dy), then one
+ * persistent launch of tile items (dH, then h / dG / dU, then dX with the split-K partial sums summed in split
+ * order, then the weight gradients), each publishing an epoch-valued flag that later items and the consumer role
+ * wait on; the consumer copies each finished segment's dX rows into dx_recv[owner] (the self owner's rows are
+ * stored there by the dX items).  cfg: mode 0 = overlapped (consumer_cus workgroups return rows from the start,
+ * every other workgroup joins once its items are done; 0 = library default, 8 CUs; -1 = none), mode 1 =
+ * sequential (the producers, then the return on every CU); epoch and watchdog_ticks as in the forward; results
+ * are identical in both modes.  The layout must be the forward's (moe_layout_build of the same routing). */
+int moe_expert_ffn_backward(const moe_shape* s, const moe_layout* L, const moe_bwd_args* b, uint32_t* flags,
+                            const moe_overlap_cfg* cfg, void* stream);
+
+/* The combine's backward: dx (device, bf16 [T, d]) = per token the fp32 sum, in slot order, of its delivered dX rows
+ * (dx_recv, as moe_expert_ffn_backward fills them), rounded once; dw_route (device, fp32 [T, k]) = <dOut[t], y_j>
+ * over the forward's delivered rows y_recv (0 for slots routed elsewhere).  Tokens with no local slot get zero
+ * rows.  bf16 only. */
+int moe_combine_backward(const moe_shape* s, const moe_layout* L, const void* d_out, void* const* y_recv,
+                         void* const* dx_recv, void* dx, float* dw_route, void* stream);
+
+/* While enabled (nonzero), every moe_expert_ffn_overlap and moe_expert_ffn_backward call of this process times
+ * each of its launches with a pair of HIP events that the launch itself records (hipExtLaunchKernel: the kernel's start and end, no marker
  * in the caller's stream).  Disabled by default.  Returns MOE_OK. */
 int moe_set_kernel_timing(int enable);
 

@@ -84,7 +84,7 @@ def _bind(lib):
     lib.orc_deliver.restype = i32
     lib.orc_combine.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp]
     lib.orc_combine.restype = i32
-    lib.orc_bwd_rows.argtypes = [i64, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.orc_bwd_rows.argtypes = [i64, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.orc_bwd_rows.restype = i32
     lib.orc_round_bf16.argtypes = [ctypes.c_double]
     lib.orc_round_bf16.restype = ctypes.c_double
@@ -265,10 +265,10 @@ def round_bf16(v: float, lib=None) -> float:
 
 
 def bwd_rows(tok, expert, w, x, w_gate_up, w_down, d_out, is_bf16: bool, want_y: bool = True,
-             want_parts: bool = True, lib=None) -> dict:
+             want_parts: bool = True, want_adm: bool = False, lib=None) -> dict:
     """Backward of the expert FFN for rows (token tok[i], local expert expert[i], routing weight w[i]): the row
-    gradient dX [n, d], and (want_parts) dY [n, d], h [n, f], dG | dU [n, 2f]; (want_y) the forward output y [n, d]
-    (orc_bwd_rows)."""
+    gradient dX [n, d], and (want_parts) dY [n, d], h [n, f], dG | dU [n, 2f]; (want_y) the forward output y [n, d];
+    (want_adm, bf16) the least and greatest admitted roundings of h, dG and dU, [n, 3, 2, f] (orc_bwd_rows)."""
     lib = lib or load()
     tok = np.ascontiguousarray(tok, dtype=np.int32)
     expert = np.ascontiguousarray(expert, dtype=np.int32)
@@ -281,10 +281,13 @@ def bwd_rows(tok, expert, w, x, w_gate_up, w_down, d_out, is_bf16: bool, want_y:
         out.update(dy=np.empty((n, d)), h=np.empty((n, f)), dgu=np.empty((n, 2 * f)))
     if want_y:
         out["y"] = np.empty((n, d))
+    if want_adm:
+        out["adm"] = np.zeros((n, 3, 2, f))
     g = lambda k: _p(out[k]) if k in out else None
     rc = lib.orc_bwd_rows(n, _p(tok), _p(expert), _p(w), d, f, int(is_bf16), _p(np.ascontiguousarray(x)),
                           _p(np.ascontiguousarray(w_gate_up)), _p(np.ascontiguousarray(w_down)),
-                          _p(np.ascontiguousarray(d_out)), _p(out["dx"]), g("dy"), g("h"), g("dgu"), g("y"))
+                          _p(np.ascontiguousarray(d_out)), _p(out["dx"]), g("dy"), g("h"), g("dgu"), g("y"),
+                          g("adm"))
     assert rc == 0
     return out
 
@@ -295,31 +298,54 @@ def backward(s, inputs: dict, d_out: np.ndarray, lib=None) -> dict:
     local slots of the rows' dX (rounded once in bf16 mode, as the combined output is), the routing weights'
     gradient dw [T, k] = <dOut_t, y> (0 for slots routed elsewhere), and the weight gradients
     dw_gate_up [E, 2f, d] = sum over the expert's rows of (dG | dU) x^T and dw_down [E, d, f] = sum of dY h^T
-    (numpy matmuls of the rows' parts, in double)."""
+    (numpy matmuls of the rows' parts, in double; backward_reduce)."""
     lib = lib or load()
     idx, w = route(inputs["logits"], s.k, lib)
     lo = 0  # self_rank 0 owns experts [0, E_l)
     t, j = np.nonzero((idx >= lo) & (idx < lo + s.E_l))
     e = idx[t, j] - lo
     is_bf16 = s.dtype == "bf16"
-    x = inputs["x"]
-    r = bwd_rows(t, e, w[t, j], x, inputs["w_gate_up"], inputs["w_down"], d_out, is_bf16, lib=lib)
+    r = bwd_rows(t, e, w[t, j], inputs["x"], inputs["w_gate_up"], inputs["w_down"], d_out, is_bf16,
+                 want_adm=is_bf16, lib=lib)
+    out = backward_reduce(s, inputs, d_out, (t, j), e, r, lib=lib)
+    out.update({"rows": (t, j), "parts": r, "topk_idx": idx, "topk_w": w})
+    return out
+
+
+def backward_reduce(s, inputs: dict, d_out: np.ndarray, rows, e, parts: dict, dx_from_dgu: bool = False,
+                    lib=None) -> dict:
+    """The sums over rows of the backward: dx, dw, dw_gate_up and dw_down (see backward) from the rows' parts (dy, h,
+    dgu, y, dx).  With dx_from_dgu the rows' dX are taken afresh as (dG | dU) [Wg; Wu] of the expert from the parts'
+    dgu (so that parts whose h, dG or dU took an admitted other rounding give the dX, dx and weight gradients that
+    follow from those values)."""
+    lib = lib or load()
+    t, j = rows
+    is_bf16 = s.dtype == "bf16"
+    wgu = _as_f64(inputs["w_gate_up"])
+    if dx_from_dgu:
+        dx_rows = np.zeros((len(t), s.d))
+        for ee in range(s.E_l):
+            m = e == ee
+            dx_rows[m] = parts["dgu"][m] @ wgu[ee]
+        if is_bf16:
+            dx_rows = round_bf16_array(dx_rows, lib)
+    else:
+        dx_rows = parts["dx"]
     dx = np.zeros((s.T, s.d))
-    np.add.at(dx, t, r["dx"])
+    np.add.at(dx, t, dx_rows)
     if is_bf16:
         dx = round_bf16_array(dx, lib)
     dout = _as_f64(d_out)
     dw = np.zeros((s.T, s.k))
-    dw[t, j] = np.einsum("ic,ic->i", dout[t], r["y"])
-    xs = _as_f64(x)[t]
+    dw[t, j] = np.einsum("ic,ic->i", dout[t], parts["y"])
+    xs = _as_f64(inputs["x"])[t]
     dwgu = np.zeros((s.E_l, 2 * s.f, s.d))
     dwd = np.zeros((s.E_l, s.d, s.f))
     for ee in range(s.E_l):
         m = e == ee
-        dwgu[ee] = r["dgu"][m].T @ xs[m]
-        dwd[ee] = r["dy"][m].T @ r["h"][m]
-    return {"dx": dx, "dw": dw, "dw_gate_up": dwgu, "dw_down": dwd, "rows": (t, j), "parts": r,
-            "topk_idx": idx, "topk_w": w}
+        dwgu[ee] = parts["dgu"][m].T @ xs[m]
+        dwd[ee] = parts["dy"][m].T @ parts["h"][m]
+    return {"dx": dx, "dx_rows": dx_rows, "dw": dw, "dw_gate_up": dwgu, "dw_down": dwd}
 
 
 def _as_f64(a: np.ndarray) -> np.ndarray:

@@ -408,9 +408,15 @@ int orc_ffn_rows(int64_t nrows, const int32_t* src_row, const int32_t* expert, i
 /* dY = bf16(fp32(w * dOut)) (an fp32 product, then bf16), h = bf16(silu(g) u) as in the forward, dG and dU to      */
 /* bf16, and the row dX to bf16 (the rows the return delivers); y = bf16(...) as delivered.  fp32: no rounding.    */
 /* Every sum in double.                                                                                             */
+/* adm_out (optional, bf16 mode, [nrows][3][2][f]): for h, dG and dU (in that order), the least and the greatest    */
+/* bf16 values that an fp32 evaluation within its error bound can round to: the bf16 roundings of the exact value   */
+/* minus and plus the bound (rounding is monotone, so every bf16 value between them is one such rounding).  The      */
+/* bound adds, for each fp32 input of the value, the error of a d-term fp32 sum (2^-21 sqrt(d) times the root sum of */
+/* squares of its terms, as in orc_ffn_rows_ex) times the value's derivative in that input, plus 2^-20 of the value  */
+/* for its own evaluation: g, u and dH feed h = silu(g) u, dU = dH silu(g) and dG = dH u silu'(g).                  */
 int orc_bwd_rows(int64_t nrows, const int32_t* tok, const int32_t* expert, const float* w, int d, int f, int is_bf16,
                  const void* x, const void* w_gate_up, const void* w_down, const void* d_out, double* dx_row,
-                 double* dy_out, double* h_out, double* dgu_out, double* y_out) {
+                 double* dy_out, double* h_out, double* dgu_out, double* y_out, double* adm_out) {
   if (nrows < 0 || d <= 0 || f <= 0) return -1;
 #pragma omp parallel
   {
@@ -429,16 +435,39 @@ int orc_bwd_rows(int64_t nrows, const int32_t* tok, const int32_t* expert, const
       }
       const int64_t wg0 = e * 2 * (int64_t)f * d, wu0 = wg0 + (int64_t)f * d, wd0 = e * (int64_t)d * f;
       for (int n = 0; n < f; ++n) {
-        double g = 0.0, u = 0.0, dh = 0.0;
+        double g = 0.0, u = 0.0, dh = 0.0, qg = 0.0, qu = 0.0, qh = 0.0;
         for (int c = 0; c < d; ++c) {
-          g += xr[c] * orc_ld(w_gate_up, wg0 + (int64_t)n * d + c, is_bf16);
-          u += xr[c] * orc_ld(w_gate_up, wu0 + (int64_t)n * d + c, is_bf16);
+          const double tg = xr[c] * orc_ld(w_gate_up, wg0 + (int64_t)n * d + c, is_bf16);
+          const double tu = xr[c] * orc_ld(w_gate_up, wu0 + (int64_t)n * d + c, is_bf16);
+          g += tg;
+          u += tu;
+          qg += tg * tg;
+          qu += tu * tu;
         }
-        for (int m = 0; m < d; ++m) dh += dy[m] * orc_ld(w_down, wd0 + (int64_t)m * f + n, is_bf16);
+        for (int m = 0; m < d; ++m) {
+          const double th = dy[m] * orc_ld(w_down, wd0 + (int64_t)m * f + n, is_bf16);
+          dh += th;
+          qh += th * th;
+        }
         const double s = 1.0 / (1.0 + exp(-g)), silu = g * s, dsilu = s * (1.0 + g * (1.0 - s));
-        h[n] = is_bf16 ? orc_round_bf16(silu * u) : silu * u;
-        du[n] = is_bf16 ? orc_round_bf16(dh * silu) : dh * silu;
-        dg[n] = is_bf16 ? orc_round_bf16(dh * u * dsilu) : dh * u * dsilu;
+        const double hv = silu * u, duv = dh * silu, dgv = dh * u * dsilu;
+        h[n] = is_bf16 ? orc_round_bf16(hv) : hv;
+        du[n] = is_bf16 ? orc_round_bf16(duv) : duv;
+        dg[n] = is_bf16 ? orc_round_bf16(dgv) : dgv;
+        if (adm_out != NULL && is_bf16) {
+          const double eg = ldexp(sqrt((double)d * qg), -21), eu = ldexp(sqrt((double)d * qu), -21);
+          const double eh = ldexp(sqrt((double)d * qh), -21);
+          const double d2silu = s * (1.0 - s) * (2.0 + g * (1.0 - 2.0 * s)); /* silu''(g) */
+          const double bound[3] = {
+              fabs(dsilu * u) * eg + fabs(silu) * eu + ldexp(fabs(hv), -20),
+              fabs(u * dsilu) * eh + fabs(dh * dsilu) * eu + fabs(dh * u * d2silu) * eg + ldexp(fabs(dgv), -20),
+              fabs(silu) * eh + fabs(dh * dsilu) * eg + ldexp(fabs(duv), -20)};
+          const double exact[3] = {hv, dgv, duv};
+          for (int q = 0; q < 3; ++q) {
+            adm_out[((i * 3 + q) * 2 + 0) * (int64_t)f + n] = orc_round_bf16(exact[q] - bound[q]);
+            adm_out[((i * 3 + q) * 2 + 1) * (int64_t)f + n] = orc_round_bf16(exact[q] + bound[q]);
+          }
+        }
       }
       for (int c = 0; c < d; ++c) {
         double acc = 0.0;

@@ -782,6 +782,50 @@ def test_backward_bf16_rounding_points(orc):
     np.testing.assert_array_equal(b["dx"], _bf16(summed))
 
 
+def test_backward_admitted_roundings_cover_fp32_evaluations(orc):
+    """The admitted interval of h, dG and dU (the least and greatest bf16 values an fp32 evaluation within the error
+    bound can round to) holds the bf16 rounding of fp32 evaluations in several summation orders (left to right, right
+    to left, numpy's pairwise sum, 16 lanes of 16 terms then a lane sum), and the oracle's own rounding; most values
+    admit one rounding only, so the interval is no blanket allowance."""
+    s = mi.Spec("bwd_adm", R=2, T_o=48, G=4, E_l=2, k=2, d=256, f=128, M=16, seed=37)
+    inp = mi.inputs(s)
+    d_out = mi.d_out(s)
+    b = oracle.backward(s, inp, d_out, orc)
+    t, j = b["rows"]
+    r = b["parts"]
+    e = b["topk_idx"][t, j]
+    x = oracle._as_f64(inp["x"]).astype(np.float32)[t]
+    w1 = oracle._as_f64(inp["w_gate_up"]).astype(np.float32)[e]
+    w2 = oracle._as_f64(inp["w_down"]).astype(np.float32)[e]
+    dy = r["dy"].astype(np.float32)
+    tg = w1[:, : s.f] * x[:, None, :]            # [n, f, d], exact in fp32 (bf16 operands)
+    tu = w1[:, s.f:] * x[:, None, :]
+    th = np.swapaxes(w2 * dy[:, :, None], 1, 2)  # [n, f, d]
+
+    def seq(tm, rev=False):
+        acc = np.zeros(tm.shape[:2], np.float32)
+        for c in (range(tm.shape[2] - 1, -1, -1) if rev else range(tm.shape[2])):
+            acc = acc + tm[:, :, c]
+        return acc
+
+    def lanes(tm):
+        return seq(np.stack([seq(tm[:, :, i::16]) for i in range(16)], axis=2))
+
+    orders = (seq, lambda tm: seq(tm, True), lambda tm: tm.sum(axis=2, dtype=np.float32), lanes)
+    lo, hi = r["adm"][:, :, 0], r["adm"][:, :, 1]
+    for q, own in enumerate((r["h"], r["dgu"][:, : s.f], r["dgu"][:, s.f:])):
+        assert (lo[:, q] <= own).all() and (own <= hi[:, q]).all()
+        assert (lo[:, q] == hi[:, q]).mean() > 0.9
+    for order in orders:
+        g, u, dh = order(tg), order(tu), order(th)
+        sg = np.float32(1) / (np.float32(1) + np.exp(-g))
+        silu = g * sg
+        vals = (silu * u, dh * u * (sg * (np.float32(1) + g * (np.float32(1) - sg))), dh * silu)
+        for q, v in enumerate(vals):
+            v = _bf16(v.astype(np.float64))
+            assert ((lo[:, q] <= v) & (v <= hi[:, q])).all(), q
+
+
 def test_backward_no_local_slot_gives_zero(orc):
     """A token none of whose slots is routed to a local expert gets a zero dx row and zero routing gradients; an
     expert with no rows gets zero weight gradients."""
