@@ -166,6 +166,64 @@ def cpu_baseline(s, inp, target_s: float):
             "one_thread": one}
 
 
+def bench_backward(P, s, w1, w2, reps: int, M_real: int) -> dict:
+    """The backward pass for the last forward's routing and layout: dY dispatch, the persistent launch (dH, h / dG /
+    dU, dX with its return to the owners, the weight gradients) and the combine's backward, as one call; overlapped
+    (consumer workgroups return dX rows while the weight gradients run) and sequential (the return after the launch).
+    Flops: 12 M d f for the gradients (dH 2, dX 4, dW_down 2, dW_gate_up 4), 16 M d f with the launch's recompute of
+    the gate and up projections."""
+    import torch
+
+    import moe_inputs as mi
+    from expert_output_overlap_amd import binding as B
+    from expert_output_overlap_amd.runtime import to_device
+
+    d_out = to_device(mi.d_out(s), s.dtype)
+    P.bwd_buffers()
+
+    def call(mode):
+        P.backward(d_out, w1, w2, mode=mode)
+        P.combine_backward(d_out)
+
+    for _ in range(3):
+        call(0)
+    torch.cuda.synchronize()
+    assert P.status() == B.MOE_OK
+
+    def timed(mode):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        B.moe_set_kernel_timing(True)
+        B.moe_kernel_times()
+        ts = []
+        for _ in range(reps):
+            ev0.record()
+            call(mode)
+            ev1.record()
+            ev1.synchronize()
+            ts.append(ev0.elapsed_time(ev1))
+        k_ms, _, c_ms, n = B.moe_kernel_times()
+        B.moe_set_kernel_timing(False)
+        assert P.status() == B.MOE_OK
+        return float(np.median(ts)), k_ms / n, c_ms / n
+
+    t_ovl, k_ovl, _ = timed(0)
+    t_seq, k_seq, c_seq = timed(1)
+    grads = 12.0 * M_real * s.d * s.f
+    executed = 16.0 * M_real * s.d * s.f
+    ret_bytes = 2.0 * (M_real - int(P.scalars()["N_r"][P.shape.self_rank])) * s.d * 2
+    return {
+        "ms": round(t_ovl, 4), "ms_sequential": round(t_seq, 4),
+        "saved_vs_sequential_us": round(1e3 * (t_seq - t_ovl), 1),
+        "tflops_gradients": round(grads / (t_ovl * 1e-3) / 1e12, 2),
+        "pct_bf16_peak_gradients": round(100 * grads / (t_ovl * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 2),
+        "launch_ms": {"overlapped": round(k_ovl, 4), "sequential_producer": round(k_seq, 4),
+                      "sequential_return": round(c_seq, 4)},
+        "launch_tflops_executed": round(executed / (k_ovl * 1e-3) / 1e12, 2),
+        "launch_pct_bf16_peak_executed": round(100 * executed / (k_ovl * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 2),
+        "return_gbs_sequential": round(ret_bytes / (c_seq * 1e-3) / 1e9, 1),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -183,6 +241,8 @@ def main():
     ap.add_argument("--mode", type=int, default=0, choices=(0, 1, 3),
                     help="FFN mode of the timed steps: 0 overlapped, 1 sequential (the consumer alone after the "
                          "producer, for profiling the copy), 3 the return on the DMA engines")
+    ap.add_argument("--backward", type=int, default=1, choices=(0, 1),
+                    help="1 (default, bf16): also time the layer's backward pass after the forward steps")
     ap.add_argument("--land", type=int, default=1, choices=(0, 1),
                     help="where x_pad's token rows come from: 1 (default) the FFN launch lands them itself, row tile "
                          "by row tile, while its first GEMM starts; 0 the layout's gather kernel")
@@ -344,6 +404,8 @@ def main():
                      "traffic": hbm_traffic(s, cus, args.band_window, land, args.mode),
                      "traffic_unit": "HBM bytes per launch"},
     }
+    if args.backward and s.dtype == "bf16":
+        res["backward"] = bench_backward(P, s, w1, w2, reps, M_real)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(s, inp, args.cpu_seconds)
     print(json.dumps(res))

@@ -84,7 +84,8 @@ def _bind(lib):
     lib.orc_deliver.restype = i32
     lib.orc_combine.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp]
     lib.orc_combine.restype = i32
-    lib.orc_bwd_rows.argtypes = [i64, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.orc_bwd_rows.argtypes = [i64, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                 ctypes.c_double, vp]
     lib.orc_bwd_rows.restype = i32
     lib.orc_round_bf16.argtypes = [ctypes.c_double]
     lib.orc_round_bf16.restype = ctypes.c_double
@@ -265,10 +266,11 @@ def round_bf16(v: float, lib=None) -> float:
 
 
 def bwd_rows(tok, expert, w, x, w_gate_up, w_down, d_out, is_bf16: bool, want_y: bool = True,
-             want_parts: bool = True, want_adm: bool = False, lib=None) -> dict:
+             want_parts: bool = True, want_adm: bool = False, w_rel: float = 0.0, lib=None) -> dict:
     """Backward of the expert FFN for rows (token tok[i], local expert expert[i], routing weight w[i]): the row
     gradient dX [n, d], and (want_parts) dY [n, d], h [n, f], dG | dU [n, 2f]; (want_y) the forward output y [n, d];
-    (want_adm, bf16) the least and greatest admitted roundings of h, dG and dU, [n, 3, 2, f] (orc_bwd_rows)."""
+    (want_adm, bf16) the least and greatest admitted values of h, dG and dU, [n, 3, 2, f], and of dY, [n, 2, d], for
+    routing weights correct to relative w_rel (orc_bwd_rows)."""
     lib = lib or load()
     tok = np.ascontiguousarray(tok, dtype=np.int32)
     expert = np.ascontiguousarray(expert, dtype=np.int32)
@@ -283,22 +285,24 @@ def bwd_rows(tok, expert, w, x, w_gate_up, w_down, d_out, is_bf16: bool, want_y:
         out["y"] = np.empty((n, d))
     if want_adm:
         out["adm"] = np.zeros((n, 3, 2, f))
+        out["dy_adm"] = np.zeros((n, 2, d))
     g = lambda k: _p(out[k]) if k in out else None
     rc = lib.orc_bwd_rows(n, _p(tok), _p(expert), _p(w), d, f, int(is_bf16), _p(np.ascontiguousarray(x)),
                           _p(np.ascontiguousarray(w_gate_up)), _p(np.ascontiguousarray(w_down)),
                           _p(np.ascontiguousarray(d_out)), _p(out["dx"]), g("dy"), g("h"), g("dgu"), g("y"),
-                          g("adm"))
+                          g("adm"), float(w_rel), g("dy_adm"))
     assert rc == 0
     return out
 
 
-def backward(s, inputs: dict, d_out: np.ndarray, lib=None) -> dict:
+def backward(s, inputs: dict, d_out: np.ndarray, lib=None, *, w_rel: float = 0.0) -> dict:
     """Gradients of the MoE layer for the local experts, given dOut = dL/d(combined output) [T, d] (the review page,
     "Where Pith is reading between the lines": MoE training's backward pass): dx [T, d] = sum over the token's
     local slots of the rows' dX (rounded once in bf16 mode, as the combined output is), the routing weights'
     gradient dw [T, k] = <dOut_t, y> (0 for slots routed elsewhere), and the weight gradients
     dw_gate_up [E, 2f, d] = sum over the expert's rows of (dG | dU) x^T and dw_down [E, d, f] = sum of dY h^T
-    (numpy matmuls of the rows' parts, in double; backward_reduce)."""
+    (numpy matmuls of the rows' parts, in double; backward_reduce).  w_rel: the relative bound to which routing
+    weights are taken as correct, for the admitted values of the parts (bwd_rows)."""
     lib = lib or load()
     idx, w = route(inputs["logits"], s.k, lib)
     lo = 0  # self_rank 0 owns experts [0, E_l)
@@ -306,31 +310,20 @@ def backward(s, inputs: dict, d_out: np.ndarray, lib=None) -> dict:
     e = idx[t, j] - lo
     is_bf16 = s.dtype == "bf16"
     r = bwd_rows(t, e, w[t, j], inputs["x"], inputs["w_gate_up"], inputs["w_down"], d_out, is_bf16,
-                 want_adm=is_bf16, lib=lib)
+                 want_adm=is_bf16, w_rel=w_rel, lib=lib)
     out = backward_reduce(s, inputs, d_out, (t, j), e, r, lib=lib)
     out.update({"rows": (t, j), "parts": r, "topk_idx": idx, "topk_w": w})
     return out
 
 
-def backward_reduce(s, inputs: dict, d_out: np.ndarray, rows, e, parts: dict, dx_from_dgu: bool = False,
-                    lib=None) -> dict:
+def backward_reduce(s, inputs: dict, d_out: np.ndarray, rows, e, parts: dict, experts=None, lib=None) -> dict:
     """The sums over rows of the backward: dx, dw, dw_gate_up and dw_down (see backward) from the rows' parts (dy, h,
-    dgu, y, dx).  With dx_from_dgu the rows' dX are taken afresh as (dG | dU) [Wg; Wu] of the expert from the parts'
-    dgu (so that parts whose h, dG or dU took an admitted other rounding give the dX, dx and weight gradients that
-    follow from those values)."""
+    dgu, y, dx).  experts: the local experts whose weight gradients are formed (all by default); the weight gradients
+    are then indexed like that list."""
     lib = lib or load()
     t, j = rows
     is_bf16 = s.dtype == "bf16"
-    wgu = _as_f64(inputs["w_gate_up"])
-    if dx_from_dgu:
-        dx_rows = np.zeros((len(t), s.d))
-        for ee in range(s.E_l):
-            m = e == ee
-            dx_rows[m] = parts["dgu"][m] @ wgu[ee]
-        if is_bf16:
-            dx_rows = round_bf16_array(dx_rows, lib)
-    else:
-        dx_rows = parts["dx"]
+    dx_rows = parts["dx"]
     dx = np.zeros((s.T, s.d))
     np.add.at(dx, t, dx_rows)
     if is_bf16:
@@ -338,13 +331,14 @@ def backward_reduce(s, inputs: dict, d_out: np.ndarray, rows, e, parts: dict, dx
     dout = _as_f64(d_out)
     dw = np.zeros((s.T, s.k))
     dw[t, j] = np.einsum("ic,ic->i", dout[t], parts["y"])
-    xs = _as_f64(inputs["x"])[t]
-    dwgu = np.zeros((s.E_l, 2 * s.f, s.d))
-    dwd = np.zeros((s.E_l, s.d, s.f))
-    for ee in range(s.E_l):
+    experts = list(range(s.E_l)) if experts is None else list(experts)
+    xs = _as_f64(inputs["x"][t])
+    dwgu = np.zeros((len(experts), 2 * s.f, s.d))
+    dwd = np.zeros((len(experts), s.d, s.f))
+    for i, ee in enumerate(experts):
         m = e == ee
-        dwgu[ee] = parts["dgu"][m].T @ xs[m]
-        dwd[ee] = parts["dy"][m].T @ parts["h"][m]
+        dwgu[i] = parts["dgu"][m].T @ xs[m]
+        dwd[i] = parts["dy"][m].T @ parts["h"][m]
     return {"dx": dx, "dx_rows": dx_rows, "dw": dw, "dw_gate_up": dwgu, "dw_down": dwd}
 
 

@@ -413,15 +413,21 @@ int orc_ffn_rows(int64_t nrows, const int32_t* src_row, const int32_t* expert, i
 /* minus and plus the bound (rounding is monotone, so every bf16 value between them is one such rounding).  The      */
 /* bound adds, for each fp32 input of the value, the error of a d-term fp32 sum (2^-21 sqrt(d) times the root sum of */
 /* squares of its terms, as in orc_ffn_rows_ex) times the value's derivative in that input, plus 2^-20 of the value  */
-/* for its own evaluation: g, u and dH feed h = silu(g) u, dU = dH silu(g) and dG = dH u silu'(g).                  */
+/* for its own evaluation: g, u and dH feed h = silu(g) u, dU = dH silu(g) and dG = dH u silu'(g).  dH's bound also */
+/* holds sum_m |Wd[m][n]| times the widest step of dY[m] within its own admitted interval (below).                  */
+/* dy_adm_out (optional, bf16 mode, [nrows][2][d]): dY's least and greatest admitted values, the bf16 roundings of  */
+/* w dOut (1 -+ (w_rel + 2^-24)): a routing weight within relative w_rel of w (an fp32 softmax's weights are correct */
+/* to that bound), times dOut, rounded to fp32.                                                                     */
 int orc_bwd_rows(int64_t nrows, const int32_t* tok, const int32_t* expert, const float* w, int d, int f, int is_bf16,
                  const void* x, const void* w_gate_up, const void* w_down, const void* d_out, double* dx_row,
-                 double* dy_out, double* h_out, double* dgu_out, double* y_out, double* adm_out) {
-  if (nrows < 0 || d <= 0 || f <= 0) return -1;
+                 double* dy_out, double* h_out, double* dgu_out, double* y_out, double* adm_out, double w_rel,
+                 double* dy_adm_out) {
+  if (nrows < 0 || d <= 0 || f <= 0 || !(w_rel >= 0.0)) return -1;
 #pragma omp parallel
   {
     double* xr = (double*)malloc(sizeof(double) * (size_t)d);
     double* dy = (double*)malloc(sizeof(double) * (size_t)d);
+    double* wdy = (double*)malloc(sizeof(double) * (size_t)d); /* widest step of dY within its admitted interval */
     double* h = (double*)malloc(sizeof(double) * (size_t)f);
     double* dg = (double*)malloc(sizeof(double) * (size_t)f);
     double* du = (double*)malloc(sizeof(double) * (size_t)f);
@@ -432,10 +438,20 @@ int orc_bwd_rows(int64_t nrows, const int32_t* tok, const int32_t* expert, const
         xr[c] = orc_ld(x, t * d + c, is_bf16);
         const double o = orc_ld(d_out, t * d + c, is_bf16);
         dy[c] = is_bf16 ? orc_round_bf16((double)(float)(w[i] * (float)o)) : (double)w[i] * o;
+        wdy[c] = 0.0;
+        if (is_bf16 && (adm_out != NULL || dy_adm_out != NULL)) {
+          const double v = (double)w[i] * o, b = fabs(v) * (w_rel + ldexp(1.0, -24));
+          const double lo = orc_round_bf16(v - b), hi = orc_round_bf16(v + b);
+          wdy[c] = fmax(hi - dy[c], dy[c] - lo);
+          if (dy_adm_out != NULL) {
+            dy_adm_out[(i * 2 + 0) * (int64_t)d + c] = lo;
+            dy_adm_out[(i * 2 + 1) * (int64_t)d + c] = hi;
+          }
+        }
       }
       const int64_t wg0 = e * 2 * (int64_t)f * d, wu0 = wg0 + (int64_t)f * d, wd0 = e * (int64_t)d * f;
       for (int n = 0; n < f; ++n) {
-        double g = 0.0, u = 0.0, dh = 0.0, qg = 0.0, qu = 0.0, qh = 0.0;
+        double g = 0.0, u = 0.0, dh = 0.0, qg = 0.0, qu = 0.0, qh = 0.0, sh = 0.0;
         for (int c = 0; c < d; ++c) {
           const double tg = xr[c] * orc_ld(w_gate_up, wg0 + (int64_t)n * d + c, is_bf16);
           const double tu = xr[c] * orc_ld(w_gate_up, wu0 + (int64_t)n * d + c, is_bf16);
@@ -445,9 +461,10 @@ int orc_bwd_rows(int64_t nrows, const int32_t* tok, const int32_t* expert, const
           qu += tu * tu;
         }
         for (int m = 0; m < d; ++m) {
-          const double th = dy[m] * orc_ld(w_down, wd0 + (int64_t)m * f + n, is_bf16);
+          const double wd = orc_ld(w_down, wd0 + (int64_t)m * f + n, is_bf16), th = dy[m] * wd;
           dh += th;
           qh += th * th;
+          sh += fabs(wd) * wdy[m];
         }
         const double s = 1.0 / (1.0 + exp(-g)), silu = g * s, dsilu = s * (1.0 + g * (1.0 - s));
         const double hv = silu * u, duv = dh * silu, dgv = dh * u * dsilu;
@@ -456,7 +473,7 @@ int orc_bwd_rows(int64_t nrows, const int32_t* tok, const int32_t* expert, const
         dg[n] = is_bf16 ? orc_round_bf16(dgv) : dgv;
         if (adm_out != NULL && is_bf16) {
           const double eg = ldexp(sqrt((double)d * qg), -21), eu = ldexp(sqrt((double)d * qu), -21);
-          const double eh = ldexp(sqrt((double)d * qh), -21);
+          const double eh = ldexp(sqrt((double)d * qh), -21) + sh;
           const double d2silu = s * (1.0 - s) * (2.0 + g * (1.0 - 2.0 * s)); /* silu''(g) */
           const double bound[3] = {
               fabs(dsilu * u) * eg + fabs(silu) * eu + ldexp(fabs(hv), -20),
@@ -491,6 +508,7 @@ int orc_bwd_rows(int64_t nrows, const int32_t* tok, const int32_t* expert, const
     }
     free(xr);
     free(dy);
+    free(wdy);
     free(h);
     free(dg);
     free(du);

@@ -102,7 +102,7 @@ def check_route_and_layout(run):
     torch.cuda.synchronize()
     assert P.status() == B.MOE_OK
     np.testing.assert_array_equal(P.topk_idx[: s.T].cpu().numpy(), run.idx)
-    np.testing.assert_allclose(P.topk_w[: s.T].cpu().numpy(), run.w, rtol=2e-6, atol=1e-9)
+    np.testing.assert_allclose(P.topk_w[: s.T].cpu().numpy(), run.w, rtol=tolerance.ROUTE_W_RTOL, atol=1e-9)
     for n in LAYOUT_INT:
         np.testing.assert_array_equal(P.array(n).cpu().numpy(), lay[n], err_msg=n)
     sc = P.scalars()

@@ -783,24 +783,35 @@ def test_backward_bf16_rounding_points(orc):
 
 
 def test_backward_admitted_roundings_cover_fp32_evaluations(orc):
-    """The admitted interval of h, dG and dU (the least and greatest bf16 values an fp32 evaluation within the error
-    bound can round to) holds the bf16 rounding of fp32 evaluations in several summation orders (left to right, right
-    to left, numpy's pairwise sum, 16 lanes of 16 terms then a lane sum), and the oracle's own rounding; most values
-    admit one rounding only, so the interval is no blanket allowance."""
+    """The admitted intervals of dY (routing weights correct to relative w_rel) and of h, dG and dU (the least and
+    greatest bf16 values an fp32 evaluation within the error bound can round to) hold: dY = bf16(fp32(w' dOut)) for
+    weights w' at both ends of their bound, and the bf16 rounding of fp32 evaluations of h, dG and dU in several
+    summation orders (left to right, right to left, numpy's pairwise sum, 16 lanes of 16 terms then a lane sum) from
+    dY at the least, the oracle's and the greatest admitted values; the oracle's own roundings lie in them; most values
+    admit one rounding only, so the intervals are no blanket allowance."""
     s = mi.Spec("bwd_adm", R=2, T_o=48, G=4, E_l=2, k=2, d=256, f=128, M=16, seed=37)
     inp = mi.inputs(s)
     d_out = mi.d_out(s)
-    b = oracle.backward(s, inp, d_out, orc)
+    w_rel = 2e-6
+    b = oracle.backward(s, inp, d_out, orc, w_rel=w_rel)
     t, j = b["rows"]
     r = b["parts"]
     e = b["topk_idx"][t, j]
+    wt = b["topk_w"][t, j].astype(np.float64)
+    dout = oracle._as_f64(d_out)[t]
+    for sgn in (-1, 1):
+        w_end = (wt * (1 + sgn * w_rel)).astype(np.float32)
+        v = _bf16((w_end[:, None] * dout.astype(np.float32)).astype(np.float64))
+        assert ((r["dy_adm"][:, 0] <= v) & (v <= r["dy_adm"][:, 1])).all()
+    assert ((r["dy_adm"][:, 0] <= r["dy"]) & (r["dy"] <= r["dy_adm"][:, 1])).all()
+    assert (r["dy_adm"][:, 0] == r["dy_adm"][:, 1]).mean() > 0.99
     x = oracle._as_f64(inp["x"]).astype(np.float32)[t]
     w1 = oracle._as_f64(inp["w_gate_up"]).astype(np.float32)[e]
     w2 = oracle._as_f64(inp["w_down"]).astype(np.float32)[e]
-    dy = r["dy"].astype(np.float32)
     tg = w1[:, : s.f] * x[:, None, :]            # [n, f, d], exact in fp32 (bf16 operands)
     tu = w1[:, s.f:] * x[:, None, :]
-    th = np.swapaxes(w2 * dy[:, :, None], 1, 2)  # [n, f, d]
+    ths = [np.swapaxes(w2 * dy.astype(np.float32)[:, :, None], 1, 2)  # [n, f, d]
+           for dy in (r["dy_adm"][:, 0], r["dy"], r["dy_adm"][:, 1])]
 
     def seq(tm, rev=False):
         acc = np.zeros(tm.shape[:2], np.float32)
@@ -816,7 +827,7 @@ def test_backward_admitted_roundings_cover_fp32_evaluations(orc):
     for q, own in enumerate((r["h"], r["dgu"][:, : s.f], r["dgu"][:, s.f:])):
         assert (lo[:, q] <= own).all() and (own <= hi[:, q]).all()
         assert (lo[:, q] == hi[:, q]).mean() > 0.9
-    for order in orders:
+    for order, th in [(o, ths[1]) for o in orders] + [(orders[0], ths[0]), (orders[3], ths[2])]:
         g, u, dh = order(tg), order(tu), order(th)
         sg = np.float32(1) / (np.float32(1) + np.exp(-g))
         silu = g * sg

@@ -5,6 +5,9 @@ import numpy as np
 RTOL = 2e-2
 ATOL = 1e-3
 NORM_RTOL = 5e-3
+# routing weights: an fp32 softmax's weights against the oracle's, relative (their error bound over the workloads'
+# expert counts, well above the few fp32 steps they differ by)
+ROUTE_W_RTOL = 2e-6
 
 
 def check(got, ref, what="", slack=None):
@@ -105,3 +108,42 @@ def combine_slack(plan, w, y_rows, row_of):
             if plan[i, j] >= 0:
                 out[i] += abs(float(w[i, j])) * bf16_ulp(y_rows[row_of(i, j)])
     return out
+
+
+def _f64(a):
+    """bf16 bits (uint16) or float32 to float64."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def _width(v, adm_lo, adm_hi):
+    """The widest step from v to another admitted value."""
+    return np.maximum(adm_hi - v, v - adm_lo)
+
+
+def backward_slack(parts, e, w_gate_up, x_rows, experts):
+    """Allowances of the backward's sums beyond the stated tolerance, from the admitted values of the rows' parts
+    (oracle.bwd_rows with want_adm): a part the GPU may take anywhere in its interval moves each sum it feeds by at
+    most the interval's width times the other factor's magnitude; the dX rows add one step of their own final bf16
+    rounding (either neighbour near a midpoint, as for y).
+    parts: for rows with local expert e [n]; w_gate_up [E, 2f, d] (bf16 bits as uint16, or float32; converted one
+    expert at a time); x_rows [n, d] (float64); experts: the experts whose weight gradients are checked.  Returns
+    {"dx_rows" [n, d], "dw_down" [len, d, f], "dw_gate_up" [len, 2f, d]}."""
+    adm, dadm = parts["adm"], parts["dy_adm"]
+    f = parts["h"].shape[1]
+    wh = _width(parts["h"], adm[:, 0, 0], adm[:, 0, 1])
+    wgu = np.concatenate([_width(parts["dgu"][:, :f], adm[:, 1, 0], adm[:, 1, 1]),
+                          _width(parts["dgu"][:, f:], adm[:, 2, 0], adm[:, 2, 1])], axis=1)
+    wdy = _width(parts["dy"], dadm[:, 0], dadm[:, 1])
+    dx = bf16_ulp(parts["dx"])
+    for ee in np.unique(e):
+        m = e == ee
+        dx[m] += wgu[m] @ np.abs(_f64(w_gate_up[ee]))
+    dwd = np.stack([np.abs(parts["dy"][e == ee]).T @ wh[e == ee] + wdy[e == ee].T @ (np.abs(parts["h"][e == ee])
+                                                                                     + wh[e == ee])
+                    for ee in experts]) if len(experts) else np.zeros((0, wdy.shape[1], f))
+    dwgu = np.stack([wgu[e == ee].T @ np.abs(x_rows[e == ee]) for ee in experts]) if len(experts) else \
+        np.zeros((0, 2 * f, wdy.shape[1]))
+    return {"dx_rows": dx, "dw_down": dwd, "dw_gate_up": dwgu}
