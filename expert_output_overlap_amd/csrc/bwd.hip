@@ -230,6 +230,14 @@ __device__ __forceinline__ bool bwd_tile(const BwdArgs& a, unsigned char* smem, 
       dma16(base, off, dst + q * 1024);
     }
   };
+  // W items: the memory rows of this lane's four k-rows (k = 2 (4 wave + jj) + lane / 32) of a k-tile.  The
+  // expert's row list is in the row-tile descriptors in global memory, so it is read one k-tile ahead of the loads
+  // that use it (a read just before each load put a global-memory latency in front of every k-tile's loads)
+  int wrow[4] = {0, 0, 0, 0};
+  auto fetch_wrows = [&](int kt) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) wrow[jj] = (int)krow(kt * BWD_BK + 2 * (wave * 4 + jj) + (lane >> 5));
+  };
   // column-staged loads: wave instruction q (0..31) fills k-rows 2q, 2q+1 (lanes 0-31, 32-63), slot lane & 31 of
   // the row holding 16-byte column chunk c with (c / 2) ^ (k & 3) = slot / 2; columns past the matrix read column 0
   auto load_col_tile = [&](const unsigned char* base, uint32_t stride, int cols, int col0, int kt, uint32_t dst) {
@@ -238,7 +246,8 @@ __device__ __forceinline__ bool bwd_tile(const BwdArgs& a, unsigned char* smem, 
       const int q = wave * 4 + jj, k = 2 * q + (lane >> 5), cs = lane & 31;
       const int c = (((cs >> 1) ^ (k & 3)) << 1) | (cs & 1);
       const int col = col0 + 8 * c < cols ? col0 + 8 * c : 0;
-      dma16(base, (uint32_t)(krow(kt * BWD_BK + k) * stride) + (uint32_t)col * 2u, dst + q * 1024);
+      const int64_t mrow = A_TR ? (int64_t)wrow[jj] : krow(kt * BWD_BK + k);
+      dma16(base, (uint32_t)(mrow * stride) + (uint32_t)col * 2u, dst + q * 1024);
     }
   };
   auto load_tile = [&](int kt, int stage) {
@@ -269,12 +278,17 @@ __device__ __forceinline__ bool bwd_tile(const BwdArgs& a, unsigned char* smem, 
       for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.f;
 
   if (nk > 0) {
+    if (A_TR) fetch_wrows(0);
     load_tile(0, 0);
+    if (A_TR && nk > 1) fetch_wrows(1);
     wait_loads_barrier();
     if (nk == 1) zero_tail(0);
   }
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) load_tile(kt + 1, (kt + 1) & 1);
+    if (kt + 1 < nk) {
+      load_tile(kt + 1, (kt + 1) & 1);
+      if (A_TR && kt + 2 < nk) fetch_wrows(kt + 2);  // lands under this k-tile's MFMAs
+    }
     const unsigned char* sa = smem + (kt & 1) * BWD_STAGE;
     const unsigned char* sb = sa + A_BYTES;
 #pragma unroll
