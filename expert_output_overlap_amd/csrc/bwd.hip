@@ -67,6 +67,8 @@ struct BwdArgs {
   uint32_t* fx;
   uint64_t* scount;  // [cap_mtiles][n_x] arrivals of the dX k-splits
   float* partial;    // [cap_mtiles][n_x][S][256 x 256] fp32 partial sums
+  uint64_t* wclaim;  // weight-gradient tiles handed out: this launch's stamp << 32 | count
+  uint32_t wstamp;
   uint32_t epoch;
   uint64_t budget;
   int n_cons;  // consumer workgroups (the first n_cons of the grid)
@@ -80,6 +82,29 @@ __device__ __forceinline__ void store4_coherent(void* p, float v) {
 }
 __device__ __forceinline__ void store2_coherent(void* p, uint32_t v) {
   asm volatile("global_store_short %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store8_coherent(void* p, u32x2_t v) {
+  asm volatile("global_store_dwordx2 %0, %1, off sc1\n\ts_nop 1" ::"v"(p), "v"(v) : "memory");
+}
+
+// 4 x 4 transpose inside each quad of lanes (DPP quad permutations; every lane of the quad takes part): lane p's
+// v[r] becomes lane r's v[p].  Two exchange steps, with lane p ^ 1 for the registers whose bit 0 differs from p's,
+// then with lane p ^ 2 for bit 1.
+template <int CTRL>
+__device__ __forceinline__ float quad_perm(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ f32x4_t quad_transpose(f32x4_t v, int lane) {
+  constexpr int X1 = 0xB1, X2 = 0x4E;  // quad_perm [1,0,3,2] and [2,3,0,1]
+  const bool o1 = lane & 1, o2 = lane & 2;
+  float t0 = quad_perm<X1>(v[1]), t1 = quad_perm<X1>(v[0]), t2 = quad_perm<X1>(v[3]), t3 = quad_perm<X1>(v[2]);
+  v = f32x4_t{o1 ? t0 : v[0], o1 ? v[1] : t1, o1 ? t2 : v[2], o1 ? v[3] : t3};
+  t0 = quad_perm<X2>(v[2]);
+  t1 = quad_perm<X2>(v[3]);
+  t2 = quad_perm<X2>(v[0]);
+  t3 = quad_perm<X2>(v[1]);
+  return f32x4_t{o2 ? t0 : v[0], o2 ? t1 : v[1], o2 ? v[2] : t2, o2 ? v[3] : t3};
 }
 
 __device__ __forceinline__ uint32_t bf16_bits(float v) {  // round to nearest even
@@ -117,10 +142,10 @@ struct BwdItem {
   int e, it, jt;        // W: expert, output row tile, output column tile
 };
 
+// Items H, G and X, in list order (assigned round-robin before the run starts): i < bwd_n_static
 __device__ __forceinline__ BwdItem bwd_item(const BwdArgs& a, int n_mt, int i) {
   BwdItem it{};
-  const int NH = n_mt * a.n_h, NG = n_mt * a.n_g, NX = n_mt * a.n_x * a.S;
-  const int nd = (a.d + 255) / 256, nf = (a.f + 255) / 256, n2 = 2 * a.f / 256;
+  const int NH = n_mt * a.n_h, NG = n_mt * a.n_g;
   if (i < NH) {
     it.kind = BK_H;
     it.mt = i / a.n_h;
@@ -129,33 +154,23 @@ __device__ __forceinline__ BwdItem bwd_item(const BwdArgs& a, int n_mt, int i) {
     it.kind = BK_G;
     it.mt = i / a.n_g;
     it.nt = i - it.mt * a.n_g;
-  } else if ((i -= NG) < NX) {
+  } else {
+    i -= NG;
     it.kind = BK_X;
     const int per = a.n_x * a.S, p = i / per, r = i - p * per;
     it.mt = a.mt_order[p];  // remote first: the row tiles holding another owner's rows come first
     it.s = r / a.n_x;
     it.nt = r - it.s * a.n_x;
-  } else {
-    i -= NX;
-    const int per = nd * nf + n2 * nd;
-    it.e = i / per;
-    const int r = i - it.e * per;
-    if (r < nd * nf) {
-      it.kind = BK_WD;
-      it.it = r / nf;
-      it.jt = r - it.it * nf;
-    } else {
-      it.kind = BK_WGU;
-      it.it = (r - nd * nf) / nd;
-      it.jt = (r - nd * nf) - it.it * nd;
-    }
   }
   return it;
 }
 
-__device__ __forceinline__ int bwd_n_items(const BwdArgs& a, int n_mt) {
+__device__ __forceinline__ int bwd_n_static(const BwdArgs& a, int n_mt) { return n_mt * (a.n_h + a.n_g + a.n_x * a.S); }
+
+// Weight-gradient tiles per expert: every dW_down and every dW_gate_up tile
+__device__ __forceinline__ int bwd_w_per_expert(const BwdArgs& a) {
   const int nd = (a.d + 255) / 256, nf = (a.f + 255) / 256, n2 = 2 * a.f / 256;
-  return n_mt * (a.n_h + a.n_g + a.n_x * a.S) + a.E * (nd * nf + n2 * nd);
+  return nd * nf + n2 * nd;
 }
 
 // Shared state of an item (in LDS)
@@ -163,8 +178,55 @@ struct BwdShared {
   int rows[BWD_BM];  // padded rows of the row tile
   int hdr[MOE_MT_HDR];
   int run_first, run_count, k_rows;  // W items: the expert's run of row tiles and its row count
-  int stop;
+  int stop, claim;
+  // per local expert, built once by a workgroup before its first W item: rows, first row tile and tile count of its
+  // run, and the experts by decreasing rows (the order W tiles are handed out in)
+  int e_rows[MOE_MAX_LOCAL_EXPERTS], e_first[MOE_MAX_LOCAL_EXPERTS], e_count[MOE_MAX_LOCAL_EXPERTS];
+  int e_order[MOE_MAX_LOCAL_EXPERTS];
 };
+
+// W tile number w (0 .. E x per): expert e_order[w / per], then its dW_down tiles, then its dW_gate_up tiles
+__device__ __forceinline__ BwdItem bwd_w_item(const BwdArgs& a, const BwdShared& sh, int w) {
+  BwdItem it{};
+  const int nd = (a.d + 255) / 256, nf = (a.f + 255) / 256, per = bwd_w_per_expert(a);
+  const int k = w / per, r = w - k * per;
+  it.e = sh.e_order[k];
+  if (r < nd * nf) {
+    it.kind = BK_WD;
+    it.it = r / nf;
+    it.jt = r - it.it * nf;
+  } else {
+    it.kind = BK_WGU;
+    it.it = (r - nd * nf) / nd;
+    it.jt = (r - nd * nf) - it.it * nd;
+  }
+  return it;
+}
+
+// Wave 0: waits until *flag_at(j) == epoch for every j < n, with one load per lane in flight (64 at a time) and a
+// sleep between rounds while one stays unset.  0: all set; 1: the spin budget ran out; 2: another workgroup
+// reported an error.  (One thread taking the flags one at a time put a memory latency per flag in front of items
+// that wait on dozens of them.)
+template <typename FlagAt>
+__device__ __forceinline__ int poll_flags_wave(FlagAt flag_at, int n, uint32_t epoch, uint64_t budget,
+                                               const int32_t* status) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t t0 = moe_clock();
+  int polls = 0;
+  for (int base = 0; base < n; base += 64) {
+    bool done = base + lane >= n;
+    int nap = 0;
+    for (;;) {
+      if (!done) done = __hip_atomic_load(flag_at(base + lane), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
+      if (__ballot(!done) == 0) break;
+      if (moe_clock() - t0 > budget) return 1;
+      if ((++polls & 15) == 0 && load_status(status) != 0) return 2;
+      for (int k = 0; k <= nap; ++k) __builtin_amdgcn_s_sleep(8);  // ~512 clocks each
+      nap = nap < 1 ? nap + 1 : 1;
+    }
+  }
+  return 0;
+}
 
 template <int KIND>
 __device__ __forceinline__ bool bwd_tile(const BwdArgs& a, unsigned char* smem, BwdShared& sh, const BwdItem& it) {
@@ -315,20 +377,30 @@ __device__ __forceinline__ bool bwd_tile(const BwdArgs& a, unsigned char* smem, 
 
   // ---- epilogues ---------------------------------------------------------------------------------------------
   // accumulator (mi, ni), element q: row wm*128 + mi*32 + 8 (q / 4) + 4 (lane / 32) + q % 4, column
-  // wn*64 + ni*32 + lane % 32 (G: ni = 0 the gate block, 1 the up block of columns wn*32 + lane % 32)
-  auto row_of = [&](int mi, int q) { return wm * 128 + mi * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3); };
+  // wn*64 + ni*32 + lane % 32 (G: ni = 0 the gate block, 1 the up block of columns wn*32 + lane % 32).  Each group
+  // of four q (q4 = q / 4) is transposed inside its quad of lanes (quad_transpose), after which lane l holds row
+  // wm*128 + mi*32 + 8 q4 + 4 (l / 32) + l % 4 at the four consecutive columns from wn*64 + ni*32 + 4 ((l % 32) / 4):
+  // one wave store then writes eight rows of 32 consecutive columns (16 bytes per lane for fp32, 8 for bf16)
+  auto row_t = [&](int mi, int q4) { return wm * 128 + mi * 32 + 8 * q4 + 4 * (lane >> 5) + (lane & 3); };
+  const int col_t = 4 * ((lane & 31) >> 2);  // + wn*64 + ni*32 (G: + wn*32)
+  auto quad = [&](const f32x16_t& v, int q4) {
+    return quad_transpose(f32x4_t{v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3]}, lane);
+  };
+  auto bf16x4 = [&](float v0, float v1, float v2, float v3) {
+    return u32x2_t{bf16_bits(v0) | (bf16_bits(v1) << 16), bf16_bits(v2) | (bf16_bits(v3) << 16)};
+  };
   if (KIND == BK_H) {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int r = row_of(mi, q);
-        if (r >= n_rows) continue;
-        float* rowp = a.dh + (int64_t)sh.rows[r] * f;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int r = row_t(mi, q4);
+        const int64_t p = sh.rows[r < n_rows ? r : 0];
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
-          const int col = it.nt * 256 + wn * 64 + ni * 32 + (lane & 31);
-          if (col < f) store4_coherent(rowp + col, acc[mi][ni][q]);
+          const f32x4_t v = quad(acc[mi][ni], q4);
+          const int col = it.nt * 256 + wn * 64 + ni * 32 + col_t;
+          if (r < n_rows && col < f) store16_coherent(a.dh + p * f + col, __builtin_bit_cast(u32x4_t, v));
         }
       }
     publish(&a.fh[(int64_t)it.mt * a.n_h + it.nt], a.epoch);
@@ -344,22 +416,30 @@ __device__ __forceinline__ bool bwd_tile(const BwdArgs& a, unsigned char* smem, 
       return false;
     }
     flag_acquire();
-    const int col = it.nt * 128 + wn * 32 + (lane & 31);
+    const int col = it.nt * 128 + wn * 32 + col_t;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int r = row_of(mi, q);
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4_t g4 = quad(acc[mi][0], q4), u4 = quad(acc[mi][1], q4);
+        const int r = row_t(mi, q4);
         if (r >= n_rows) continue;
         const int64_t p = sh.rows[r];
-        const float g = acc[mi][0][q], u = acc[mi][1][q];
-        const float dh = a.dh[p * f + col];
-        const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-        const float silu = silu_fast(g);  // the forward's h, bit for bit
-        const float dsilu = sg * (1.0f + g * (1.0f - sg));
-        store2_coherent(a.h + (p * f + col) * 2, bf16_bits(silu * u));
-        store2_coherent(a.dgu + (p * 2 * f + col) * 2, bf16_bits(dh * u * dsilu));
-        store2_coherent(a.dgu + (p * 2 * f + f + col) * 2, bf16_bits(dh * silu));
+        const f32x4_t dh = *(const f32x4_t*)(a.dh + p * f + col);
+        float hv[4], dg[4], du[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float g = g4[c], u = u4[c];
+          const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+          const float silu = silu_fast(g);  // the forward's h, bit for bit
+          const float dsilu = sg * (1.0f + g * (1.0f - sg));
+          hv[c] = silu * u;
+          dg[c] = dh[c] * u * dsilu;
+          du[c] = dh[c] * silu;
+        }
+        store8_coherent(a.h + (p * f + col) * 2, bf16x4(hv[0], hv[1], hv[2], hv[3]));
+        store8_coherent(a.dgu + (p * 2 * f + col) * 2, bf16x4(dg[0], dg[1], dg[2], dg[3]));
+        store8_coherent(a.dgu + (p * 2 * f + f + col) * 2, bf16x4(du[0], du[1], du[2], du[3]));
       }
     publish(&a.fg[(int64_t)it.mt * a.n_g + it.nt], a.epoch);
     return true;
@@ -409,16 +489,16 @@ __device__ __forceinline__ bool bwd_tile(const BwdArgs& a, unsigned char* smem, 
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int r = row_of(mi, q);
-        if (r >= n_rows) continue;
-        const int p = sh.rows[r];
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int r = row_t(mi, q4);
+        const int p = sh.rows[r < n_rows ? r : 0];
         const bool self = (unsigned)(p - lo) < (unsigned)ns;
         unsigned char* rowp = self ? a.self_recv + (int64_t)(p + delta) * d * 2 : a.dxp + (int64_t)p * d * 2;
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
-          const int col = it.nt * 256 + wn * 64 + ni * 32 + (lane & 31);
-          if (col < d) store2_coherent(rowp + col * 2, bf16_bits(acc[mi][ni][q]));
+          const f32x4_t v = quad(acc[mi][ni], q4);
+          const int col = it.nt * 256 + wn * 64 + ni * 32 + col_t;
+          if (r < n_rows && col < d) store8_coherent(rowp + col * 2, bf16x4(v[0], v[1], v[2], v[3]));
         }
       }
     publish(&a.fx[tile], a.epoch);
@@ -430,13 +510,13 @@ __device__ __forceinline__ bool bwd_tile(const BwdArgs& a, unsigned char* smem, 
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int r = it.it * 256 + row_of(mi, q);
-      if (r >= out_rows) continue;
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int r = it.it * 256 + row_t(mi, q4);
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
-        const int col = it.jt * 256 + wn * 64 + ni * 32 + (lane & 31);
-        if (col < out_cols) out[(int64_t)r * out_cols + col] = acc[mi][ni][q];
+        const f32x4_t v = quad(acc[mi][ni], q4);
+        const int col = it.jt * 256 + wn * 64 + ni * 32 + col_t;
+        if (r < out_rows && col < out_cols) *(f32x4_t*)(out + (int64_t)r * out_cols + col) = v;
       }
     }
   return true;
@@ -446,82 +526,117 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void k_bwd_ffn(BwdArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ BwdShared sh;
   launch_acquire();  // drop cache lines older than this launch (the publish protocol in common.h)
-  if (load_status(a.status) != 0) return;
   const int C = a.n_cons, tid = threadIdx.x;
+  if (blockIdx.x == 0 && tid == 0)  // the W-tile counter starts at zero for this launch
+    __hip_atomic_store(a.wclaim, (uint64_t)a.wstamp << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (load_status(a.status) != 0) return;
   if (a.join && blockIdx.x == 0) consumer_stamp(a.cons);
   const int n_mt = a.scalars[a.sc_nmt];
-  // producers only (a consumer workgroup's index minus C is negative, and would start a negative item index)
-  const int n_items = (int)blockIdx.x < C ? 0 : bwd_n_items(a, n_mt);
+  const bool producer = (int)blockIdx.x >= C;
+  // H, G and X items: round-robin over the producers, consecutive items on the workgroups of one XCD (a consumer
+  // workgroup's index minus C is negative, and would start a negative item index)
+  const int n_static = producer ? bwd_n_static(a, n_mt) : 0;
   const int G = gridDim.x - C;
-  int bid = (int)blockIdx.x < C ? n_items : (int)blockIdx.x - C;
-  if ((int)blockIdx.x >= C && (G & 7) == 0 && (C & 7) == 0) bid = (bid & 7) * (G >> 3) + (bid >> 3);  // one XCD
-  for (int i = bid; i < n_items; i += G) {
+  int bid = producer ? (int)blockIdx.x - C : 0;
+  if (producer && (G & 7) == 0 && (C & 7) == 0) bid = (bid & 7) * (G >> 3) + (bid >> 3);
+  auto stop_on = [&](int st) {  // after a wait: true when the workgroup must end (status set)
+    if (st == 1 && tid == 0) set_status(a.status, MOE_ETIMEOUT);
+    return st != 0;
+  };
+  for (int i = bid; i < n_static; i += G) {
     const BwdItem it = bwd_item(a, n_mt, i);
     __syncthreads();  // the previous item is done with sh
+    const int32_t* dsc = a.mtile_desc + (int64_t)it.mt * MOE_MT_FIELDS;
+    if (tid < MOE_MT_HDR) sh.hdr[tid] = dsc[tid];
+    if (tid < BWD_BM) sh.rows[tid] = dsc[MOE_MT_HDR + tid];
     bool ok = true;
-    if (it.kind <= BK_X) {
-      const int32_t* dsc = a.mtile_desc + (int64_t)it.mt * MOE_MT_FIELDS;
-      if (tid < MOE_MT_HDR) sh.hdr[tid] = dsc[tid];
-      if (tid < BWD_BM) sh.rows[tid] = dsc[MOE_MT_HDR + tid];
-      __syncthreads();
-      if (it.kind == BK_X) {  // the (dG | dU) columns of this split: the G items of their 128-column blocks
-        if (tid == 0) {
-          const int kk = 2 * a.f / a.S, c0 = it.s * kk;
-          int st = 0;
-          for (int c = c0; c < c0 + kk && !st; c += 128)
-            st = poll_flags(&a.fg[(int64_t)it.mt * a.n_g + (c % a.f) / 128], 1, a.epoch, a.budget, a.status, 1);
-          sh.stop = st;
-        }
-        __syncthreads();
-        if (sh.stop) {
-          if (sh.stop == 1 && tid == 0) set_status(a.status, MOE_ETIMEOUT);
-          return;
-        }
-        flag_acquire();
-        ok = bwd_tile<BK_X>(a, smem, sh, it);
-      } else if (it.kind == BK_H) {
-        ok = bwd_tile<BK_H>(a, smem, sh, it);
-      } else {
-        ok = bwd_tile<BK_G>(a, smem, sh, it);
-      }
-    } else {
-      // the expert's run of row tiles (none: no rows, a zero tile)
-      if (tid == 0) {
-        sh.run_first = 0;
-        sh.run_count = 0;
-        sh.k_rows = 0;
+    if (it.kind == BK_X) {  // the (dG | dU) columns of this split: the G items of their 128-column blocks
+      if (tid < 64) {
+        const int kk = 2 * a.f / a.S, c0 = it.s * kk;
+        const uint32_t* fg = a.fg + (int64_t)it.mt * a.n_g;
+        const int st = poll_flags_wave([&](int j) { return &fg[((c0 + 128 * j) % a.f) / 128]; }, kk / 128, a.epoch,
+                                       a.budget, a.status);
+        if (tid == 0) sh.stop = st;
       }
       __syncthreads();
-      for (int t = tid; t < n_mt; t += BWD_THREADS) {
-        const int32_t* dsc = a.mtile_desc + (int64_t)t * MOE_MT_FIELDS;
-        if (dsc[0] == it.e && dsc[2] == t) {  // the first tile of the expert's run
-          sh.run_first = t;
-          sh.run_count = dsc[3];
-        }
-      }
-      __syncthreads();
-      if (tid == 0 && sh.run_count > 0) {
-        const int last = sh.run_first + sh.run_count - 1;
-        sh.k_rows = (sh.run_count - 1) * MOE_MT_ROWS + a.mtile_desc[(int64_t)last * MOE_MT_FIELDS + 1];
-        // WD reads h columns jt*256 ..; WGU reads (dG | dU) columns it*256 ..: their G items in every row tile
-        int st = 0;
-        const int c0 = it.kind == BK_WD ? it.jt * 256 : it.it * 256, c1 = min(c0 + 256, it.kind == BK_WD ? a.f : 2 * a.f);
-        for (int t = sh.run_first; t <= last && !st; ++t)
-          for (int c = c0; c < c1 && !st; c += 128)
-            st = poll_flags(&a.fg[(int64_t)t * a.n_g + (c % a.f) / 128], 1, a.epoch, a.budget, a.status, 1);
-        sh.stop = st;
-      } else if (tid == 0) {
-        sh.stop = 0;
-      }
-      __syncthreads();
-      if (sh.stop) {
-        if (sh.stop == 1 && tid == 0) set_status(a.status, MOE_ETIMEOUT);
-        return;
-      }
+      if (stop_on(sh.stop)) return;
       flag_acquire();
-      ok = it.kind == BK_WD ? bwd_tile<BK_WD>(a, smem, sh, it) : bwd_tile<BK_WGU>(a, smem, sh, it);
+      ok = bwd_tile<BK_X>(a, smem, sh, it);
+    } else {
+      __syncthreads();
+      ok = it.kind == BK_H ? bwd_tile<BK_H>(a, smem, sh, it) : bwd_tile<BK_G>(a, smem, sh, it);
     }
     if (!ok) return;
+  }
+  // W tiles: nobody waits on them, and their lengths follow the experts' row counts, so they are handed out at run
+  // time from the launch's counter, longest experts first (a static share left some workgroups 20-25% more work
+  // than others)
+  if (producer) {
+    __syncthreads();
+    if (tid < a.E) {
+      sh.e_rows[tid] = 0;
+      sh.e_first[tid] = 0;
+      sh.e_count[tid] = 0;
+    }
+    __syncthreads();
+    for (int t = tid; t < n_mt; t += BWD_THREADS) {
+      const int32_t* dsc = a.mtile_desc + (int64_t)t * MOE_MT_FIELDS;
+      atomicAdd(&sh.e_rows[dsc[0]], dsc[1]);
+      if (dsc[2] == t) {  // the first tile of the expert's run
+        sh.e_first[dsc[0]] = t;
+        sh.e_count[dsc[0]] = dsc[3];
+      }
+    }
+    __syncthreads();
+    if (tid < a.E) {
+      int rank = 0;
+      for (int e = 0; e < a.E; ++e)
+        rank += sh.e_rows[e] > sh.e_rows[tid] || (sh.e_rows[e] == sh.e_rows[tid] && e < tid);
+      sh.e_order[rank] = tid;
+    }
+    const int n_w = a.E * bwd_w_per_expert(a);
+    for (;;) {
+      __syncthreads();  // the previous item is done with sh (and the table is complete)
+      if (tid == 0) {
+        const uint64_t t0 = moe_clock();
+        int w = -1;
+        bool stamped;
+        while (!(stamped = (uint32_t)(__hip_atomic_load(a.wclaim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 32) ==
+                           a.wstamp) &&
+               moe_clock() - t0 <= a.budget)
+          __builtin_amdgcn_s_sleep(1);
+        if (stamped)
+          w = (int)(uint32_t)__hip_atomic_fetch_add(a.wclaim, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+          set_status(a.status, MOE_ETIMEOUT);
+        sh.claim = w;
+      }
+      __syncthreads();
+      const int w = sh.claim;
+      if (w < 0 || w >= n_w) break;
+      const BwdItem it = bwd_w_item(a, sh, w);
+      // the expert's run of row tiles (none: no rows, a zero tile); WD reads h columns jt*256 .., WGU (dG | dU)
+      // columns it*256 ..: their G items in every row tile of the run
+      if (tid == 0) {
+        sh.run_first = sh.e_first[it.e];
+        sh.run_count = sh.e_count[it.e];
+        sh.k_rows = sh.e_rows[it.e];
+      }
+      if (tid < 64) {
+        const int c0 = it.kind == BK_WD ? it.jt * 256 : it.it * 256;
+        const int nc = (min(c0 + 256, it.kind == BK_WD ? a.f : 2 * a.f) - c0 + 127) / 128;
+        const int first = sh.e_first[it.e];
+        const int st = poll_flags_wave(
+            [&](int j) { return &a.fg[(int64_t)(first + j / nc) * a.n_g + ((c0 + 128 * (j % nc)) % a.f) / 128]; },
+            sh.e_count[it.e] * nc, a.epoch, a.budget, a.status);
+        if (tid == 0) sh.stop = st;
+      }
+      __syncthreads();
+      if (stop_on(sh.stop)) return;
+      flag_acquire();
+      const bool ok = it.kind == BK_WD ? bwd_tile<BK_WD>(a, smem, sh, it) : bwd_tile<BK_WGU>(a, smem, sh, it);
+      if (!ok) return;
+    }
   }
   // the consumer workgroups return dX rows from the start; with join, producers too once their items are done
   if (a.join || (int)blockIdx.x < C) consumer_role(a.cons);
@@ -626,7 +741,7 @@ int bwd_splits(int d, int f) {
 }
 
 struct BwdCarve {
-  int64_t fh, fg, fx, scount, partial, claim, total;  // 4-byte words
+  int64_t fh, fg, fx, scount, partial, claim, wclaim, total;  // 4-byte words
 };
 BwdCarve bwd_carve(int d, int f, int64_t cap_mtiles) {
   auto up = [](int64_t v) { return (v + 63) / 64 * 64; };
@@ -638,7 +753,8 @@ BwdCarve bwd_carve(int d, int f, int64_t cap_mtiles) {
   c.scount = c.fg + up(cap_mtiles * n_g);
   c.partial = c.scount + up(2 * cap_mtiles * n_x);
   c.claim = c.partial + (S > 1 ? cap_mtiles * n_x * S * 256 * 256 : 0);
-  c.total = c.claim + 2;
+  c.wclaim = c.claim + 2;
+  c.total = c.wclaim + 2;
   return c;
 }
 }  // namespace
@@ -686,6 +802,8 @@ int launch_bwd_ffn(const BwdLaunch& p, int grid, int n_cons, int join, hipStream
   a.fx = p.flags + c.fx;
   a.scount = (uint64_t*)(p.flags + c.scount);
   a.partial = (float*)(p.flags + c.partial);
+  a.wclaim = (uint64_t*)(p.flags + c.wclaim);
+  a.wstamp = next_stamp();
   a.epoch = p.epoch;
   a.budget = p.watchdog_ticks;
   a.n_cons = n_cons;
