@@ -278,46 +278,55 @@ __device__ __forceinline__ bool bwd_tile(const BwdArgs& a, unsigned char* smem, 
   };
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  // row-staged loads: wave instruction q (0..31) fills rows 8q .. 8q+7, lane -> row 8q + lane/8, slot lane & 7
-  // holding k-chunk (lane & 7) ^ (lane >> 3) ^ (q & 1)
+  // ---- loads: per k-tile each wave issues 4 A and 4 B 16-byte LDS-DMA loads (load u < 4: A instruction
+  // q = 4 wave + u, else B instruction q = 4 wave + u - 4; one instruction fills 1 KB of the stage).
+  // Row-staged tiles (256 rows x 64 k): lane -> row 8q + lane/8, slot lane & 7 holding k-chunk
+  // (lane & 7) ^ (lane >> 3) ^ (q & 1).  Column-staged tiles (64 k x 256 columns): lanes 0-31 k-row 2q, 32-63 k-row
+  // 2q + 1, slot lane & 31 of the row holding 16-byte column chunk c with (c / 2) ^ (k & 3) = slot / 2; columns
+  // past the matrix read column 0.  A lane's offsets are fixed but for the k-tile: + kt * step, or, for the W
+  // items (k over the expert's rows), + the memory row of each of its four k-rows times the stride, read from the
+  // row-tile descriptors in global memory three k-tiles ahead (a read just before each load put a global-memory
+  // latency in front of every k-tile's loads).
   const uint32_t chunk0 = (uint32_t)(((lane & 7) ^ (lane >> 3)) << 4);
-  auto load_row_tile = [&](const unsigned char* base, uint32_t stride, int kt, uint32_t dst, bool glu) {
+  uint32_t aoff[4], boff[4];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int q = wave * 4 + jj, r = 8 * q + (lane >> 3);
-      int64_t mrow;
-      if (glu) mrow = r < 128 ? it.nt * 128 + r : f + it.nt * 128 + (r - 128);  // gate rows, then up rows
-      else mrow = sh.rows[r < n_rows ? r : 0];                                   // absent rows read a real row
-      const uint32_t off = (uint32_t)(mrow * stride) + (uint32_t)(k0 + kt * BWD_BK) * 2 + (chunk0 ^ ((q & 1) << 4));
-      dma16(base, off, dst + q * 1024);
+  for (int jj = 0; jj < 4; ++jj) {
+    const int q = wave * 4 + jj;
+    const int r = 8 * q + (lane >> 3);                                // row-staged row
+    const int kq = 2 * q + (lane >> 5), cs = lane & 31;               // column-staged k-row and slot
+    const int c = (((cs >> 1) ^ (kq & 3)) << 1) | (cs & 1);
+    const uint32_t rchunk = (uint32_t)k0 * 2u + (chunk0 ^ ((uint32_t)(q & 1) << 4));
+    if (A_TR) {
+      aoff[jj] = (uint32_t)(a_col0 + 8 * c < a_cols ? a_col0 + 8 * c : 0) * 2u;
+    } else {
+      aoff[jj] = (uint32_t)sh.rows[r < n_rows ? r : 0] * a_stride + rchunk;  // absent rows read a real row
     }
-  };
-  // W items: the memory rows of this lane's four k-rows (k = 2 (4 wave + jj) + lane / 32) of a k-tile.  The
-  // expert's row list is in the row-tile descriptors in global memory, so it is read one k-tile ahead of the loads
-  // that use it (a read just before each load put a global-memory latency in front of every k-tile's loads)
-  int wrow[4] = {0, 0, 0, 0};
-  auto fetch_wrows = [&](int kt) {
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) wrow[jj] = (int)krow(kt * BWD_BK + 2 * (wave * 4 + jj) + (lane >> 5));
-  };
-  // column-staged loads: wave instruction q (0..31) fills k-rows 2q, 2q+1 (lanes 0-31, 32-63), slot lane & 31 of
-  // the row holding 16-byte column chunk c with (c / 2) ^ (k & 3) = slot / 2; columns past the matrix read column 0
-  auto load_col_tile = [&](const unsigned char* base, uint32_t stride, int cols, int col0, int kt, uint32_t dst) {
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int q = wave * 4 + jj, k = 2 * q + (lane >> 5), cs = lane & 31;
-      const int c = (((cs >> 1) ^ (k & 3)) << 1) | (cs & 1);
-      const int col = col0 + 8 * c < cols ? col0 + 8 * c : 0;
-      const int64_t mrow = A_TR ? (int64_t)wrow[jj] : krow(kt * BWD_BK + k);
-      dma16(base, (uint32_t)(mrow * stride) + (uint32_t)col * 2u, dst + q * 1024);
+    if (B_TR) {
+      const uint32_t cpart = (uint32_t)(b_col0 + 8 * c < b_cols ? b_col0 + 8 * c : 0) * 2u;
+      boff[jj] = A_TR ? cpart : (uint32_t)(k0 + kq) * b_stride + cpart;  // weights: k runs over their rows
+    } else {  // G: gate rows, then up rows of the column tile
+      const int wr = r < 128 ? it.nt * 128 + r : f + it.nt * 128 + (r - 128);
+      boff[jj] = (uint32_t)wr * b_stride + rchunk;
     }
+  }
+  const uint32_t a_step = A_TR ? 0u : (uint32_t)BWD_BK * 2u;
+  const uint32_t b_step = A_TR ? 0u : B_TR ? (uint32_t)BWD_BK * b_stride : (uint32_t)BWD_BK * 2u;
+  // W: memory rows of this lane's k-rows: ids1 of the k-tile whose loads go out next, ids2 and ids3 of the next two
+  int ids1[4] = {0, 0, 0, 0}, ids2[4] = {0, 0, 0, 0}, ids3[4] = {0, 0, 0, 0};
+  auto fetch_ids = [&](int kt, int (&ids)[4]) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) ids[jj] = (int)krow(kt * BWD_BK + 2 * (wave * 4 + jj) + (lane >> 5));
   };
-  auto load_tile = [&](int kt, int stage) {
-    const uint32_t sa = lds0 + stage * BWD_STAGE, sb = sa + A_BYTES;
-    if (A_TR) load_col_tile(Abase, a_stride, a_cols, a_col0, kt, sa);
-    else load_row_tile(Abase, a_stride, kt, sa, false);
-    if (B_TR) load_col_tile(Bbase, b_stride, b_cols, b_col0, kt, sb);
-    else load_row_tile(Bbase, b_stride, kt, sb, true);
+  // load u of k-tile kt into the stage at LDS address st (ids: the W item's rows of k-tile kt)
+  auto dma1 = [&](int kt, uint32_t st, int u, const int (&ids)[4]) {
+    if (u < 4) {
+      const uint32_t off = aoff[u] + (A_TR ? (uint32_t)ids[u] * a_stride : (uint32_t)kt * a_step);
+      dma16(Abase, off, st + (wave * 4 + u) * 1024);
+    } else {
+      const int jj = u - 4;
+      const uint32_t off = boff[jj] + (A_TR ? (uint32_t)ids[jj] * b_stride : (uint32_t)kt * b_step);
+      dma16(Bbase, off, st + A_BYTES + (wave * 4 + jj) * 1024);
+    }
   };
   // W items: the k-rows of the last k-tile past the expert's rows hold real rows' values; zero them in both tiles
   auto zero_tail = [&](int stage) {
@@ -339,40 +348,101 @@ __device__ __forceinline__ bool bwd_tile(const BwdArgs& a, unsigned char* smem, 
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.f;
 
+  // ---- the k-loop (the forward's pipeline): a k-tile is four k-steps of MI x NI MFMAs per wave; the fragments of
+  // k-step s+1 are read in the first two MFMA slots of k-step s (two register sets); one barrier per k-tile, between
+  // k-steps 2 and 3, after which k-tile kt+1 is in LDS and the stage of kt is free: the A loads of k-tile kt+2 go
+  // into it during k-step 3 and the B loads of kt+1 went out during k-step 0, so every load has about three k-steps
+  // to land.  Each slot's work is pinned with sched_barrier.
+  constexpr int NSLOT = MI * NI, RS = 2, RPS = (MI + NI + RS - 1) / RS, FIRST = RS, HALF = 4;
+  constexpr int DPS = (HALF + (NSLOT - FIRST) - 1) / (NSLOT - FIRST);
+  bf16x8_t fa[2][MI], fb[2][NI];
+  auto frag1 = [&](const unsigned char* sa, int ks, int i, bf16x8_t* A_, bf16x8_t* B_) {
+    const unsigned char* sb = sa + A_BYTES;
+    if (i < MI) {
+      A_[i] = A_TR ? frag_tr(sa, wm * 128 + i * 32, ks, lane) : frag_row(sa, wm * 128 + i * 32, ks, lane);
+    } else {
+      const int ni = i - MI;
+      if (B_TR) B_[ni] = frag_tr(sb, wn * 64 + ni * 32, ks, lane);
+      else B_[ni] = frag_row(sb, ni == 0 ? wn * 32 : 128 + wn * 32, ks, lane);  // gate block, up block
+    }
+  };
+  auto step = [&](auto ks_tag, auto m1_tag, auto m2_tag, int kt) {
+    constexpr int ks = decltype(ks_tag)::value;
+    constexpr bool M1 = decltype(m1_tag)::value, M2 = decltype(m2_tag)::value;
+    constexpr int c = ks & 1;
+    const unsigned char* sa = smem + (kt & 1) * BWD_STAGE;
+    const unsigned char* nsa = smem + ((kt + 1) & 1) * BWD_STAGE;
+#pragma unroll
+    for (int i = 0; i < NSLOT; ++i) {
+      const int mi = i / NI, ni = i % NI;
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][mi], fb[c][ni], acc[mi][ni], 0, 0, 0);
+      if (i < RS) {
+#pragma unroll
+        for (int r = i * RPS; r < (i + 1) * RPS && r < MI + NI; ++r) {
+          if (ks < 3) frag1(sa, ks + 1, r, fa[c ^ 1], fb[c ^ 1]);
+          else if (M1) frag1(nsa, 0, r, fa[c ^ 1], fb[c ^ 1]);
+        }
+      }
+      if (i >= FIRST && ((ks == 3 && M2) || (ks == 0 && M1))) {
+#pragma unroll
+        for (int t = 0; t < DPS; ++t) {
+          const int v = (i - FIRST) * DPS + t;
+          if (v < HALF) {
+            if (ks == 3) dma1(kt + 2, lds0 + (kt & 1) * BWD_STAGE, v, ids1);             // A of kt+2
+            else dma1(kt + 1, lds0 + ((kt + 1) & 1) * BWD_STAGE, HALF + v, ids1);        // B of kt+1
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (ks == 1 && A_TR) fetch_ids(kt + 3, ids3);  // lands under k-step 2, before the barrier's vmcnt(0)
+    if (ks == 2) {
+      // this wave's fragment reads of k-tile kt and loads of k-tile kt+1 are done; then everyone's are
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      if (M1 && !M2) zero_tail((kt + 1) & 1);  // k-tile kt+1 is the last
+      if (A_TR) {
+        // W rows: kt+2's for the A loads of k-step 3 and the B loads of the next k-step 0, and kt+3's; moved here,
+        // where nothing is in flight, so that waiting for the row reads stalls no load
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          ids1[jj] = ids2[jj];
+          ids2[jj] = ids3[jj];
+        }
+      }
+    }
+  };
+  auto tile = [&](auto m1, auto m2, int kt) {
+    step(std::integral_constant<int, 0>{}, m1, m2, kt);
+    step(std::integral_constant<int, 1>{}, m1, m2, kt);
+    step(std::integral_constant<int, 2>{}, m1, m2, kt);
+    step(std::integral_constant<int, 3>{}, m1, m2, kt);
+  };
   if (nk > 0) {
-    if (A_TR) fetch_wrows(0);
-    load_tile(0, 0);
-    if (A_TR && nk > 1) fetch_wrows(1);
+    // prologue: k-tile 0 whole, the A loads of k-tile 1 (its B loads go out in k-step 0 of k-tile 0)
+    int ids0[4] = {0, 0, 0, 0};
+    if (A_TR) {
+      fetch_ids(0, ids0);
+      fetch_ids(1, ids1);
+      fetch_ids(2, ids2);
+    }
+#pragma unroll
+    for (int u = 0; u < 2 * HALF; ++u) dma1(0, lds0, u, ids0);
     wait_loads_barrier();
     if (nk == 1) zero_tail(0);
-  }
-  for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+    for (int i = 0; i < MI + NI; ++i) frag1(smem, 0, i, fa[0], fb[0]);
+    if (nk > 1) {
+#pragma unroll
+      for (int u = 0; u < HALF; ++u) dma1(1, lds0 + BWD_STAGE, u, ids1);
+    }
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) tile(std::true_type{}, std::true_type{}, kt);
     if (kt + 1 < nk) {
-      load_tile(kt + 1, (kt + 1) & 1);
-      if (A_TR && kt + 2 < nk) fetch_wrows(kt + 2);  // lands under this k-tile's MFMAs
+      tile(std::true_type{}, std::false_type{}, kt);
+      ++kt;
     }
-    const unsigned char* sa = smem + (kt & 1) * BWD_STAGE;
-    const unsigned char* sb = sa + A_BYTES;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8_t fa[MI], fb[NI];
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-        fa[mi] = A_TR ? frag_tr(sa, wm * 128 + mi * 32, ks, lane) : frag_row(sa, wm * 128 + mi * 32, ks, lane);
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        if (B_TR) fb[ni] = frag_tr(sb, wn * 64 + ni * 32, ks, lane);
-        else fb[ni] = frag_row(sb, ni == 0 ? wn * 32 : 128 + wn * 32, ks, lane);  // gate block, up block
-      }
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
-    }
-    // this wave's fragment reads of k-tile kt and loads of k-tile kt+1 are done; then everyone's are
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (kt + 2 == nk) zero_tail((kt + 1) & 1);
+    tile(std::false_type{}, std::false_type{}, kt);
   }
 
   // ---- epilogues ---------------------------------------------------------------------------------------------
