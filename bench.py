@@ -308,7 +308,20 @@ def main():
     ms_step = wall * 1e3 / args.steps
     print("timed %d steps: %.3f ms/step" % (args.steps, ms_step), file=sys.stderr, flush=True)
     if args.kernels_only:
-        print(json.dumps({"ms_per_step": ms_step}))
+        line = {"ms_per_step": ms_step}
+        if args.backward and s.dtype == "bf16":  # the backward calls too, for profiles of their kernels
+            d_out = to_device(mi.d_out(s), s.dtype)
+            P.bwd_buffers()
+            for i in range(args.warmup + args.steps):
+                if i == args.warmup:
+                    torch.cuda.synchronize()
+                    t0 = time.perf_counter()
+                P.backward(d_out, w1, w2, mode=0)
+                P.combine_backward(d_out)
+            torch.cuda.synchronize()
+            assert P.status() == B.MOE_OK
+            line["backward_ms"] = (time.perf_counter() - t0) * 1e3 / max(args.steps, 1)
+        print(json.dumps(line))
         return
 
     # FFN call alone, overlapped and sequential (events on the caller stream around the call)

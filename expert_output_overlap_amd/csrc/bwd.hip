@@ -111,8 +111,23 @@ __device__ __forceinline__ uint32_t bf16_bits(float v) {  // round to nearest ev
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
-// Fragment of a transposed-staged tile (64 rows of k x 256 columns) at column cb, k-step ks: the 8 consecutive k of
-// column cb + lane % 32 starting at 16 ks + 8 (lane / 32), as the MFMA takes them.
+// Column-staged tiles (64 k-rows x 256 columns, 512 bytes per row): the 32-byte granule g (16 columns) of k-row r
+// sits at granule col_swz(g, r) of the row.  A transposed fragment read has lanes 0-15 and 16-31 on columns 16
+// apart (granules g and g + 1, g even) of the same four k-rows; col_swz puts g and g + 1 in opposite halves of the
+// 64 banks (bit 2 of the granule, from bit 0 of g) and the four rows of each in distinct granules of that half
+// (XOR with r & 3), so each half-wave reads 64 distinct banks.  (Granule g ^ (r & 3) kept g and g + 1 in one half:
+// 31% of the launch's LDS cycles were bank conflicts.)
+__device__ __forceinline__ int col_swz(int g, int r) {
+  const int x = g & 7;
+  return (g & 8) | ((((x & 1) << 2) | (x >> 1)) ^ (r & 3));
+}
+__device__ __forceinline__ int col_unswz(int p, int r) {  // the logical granule at granule p of k-row r
+  const int y = (p & 7) ^ (r & 3);
+  return (p & 8) | (((y & 3) << 1) | (y >> 2));
+}
+
+// Fragment of a column-staged tile at column cb (a multiple of 32), k-step ks: the 8 consecutive k of column
+// cb + lane % 32 starting at 16 ks + 8 (lane / 32), as the MFMA takes them.
 __device__ __forceinline__ bf16x8_t frag_tr(const unsigned char* st, int cb, int ks, int lane) {
   const int gi = lane >> 4, j = lane & 15;
   const int n = cb + 16 * (gi & 1) + 4 * (j & 3);
@@ -120,7 +135,7 @@ __device__ __forceinline__ bf16x8_t frag_tr(const unsigned char* st, int cb, int
 #pragma unroll
   for (int hk = 0; hk < 2; ++hk) {
     const int k = 16 * ks + 8 * (gi >> 1) + 4 * hk + (j >> 2);
-    const unsigned char* p = st + k * 512 + ((((n >> 4) ^ (k & 3)) << 5) | ((n & 15) << 1));
+    const unsigned char* p = st + k * 512 + ((col_swz(n >> 4, k) << 5) | ((n & 15) << 1));
     v[hk] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
   }
   return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
@@ -282,8 +297,8 @@ __device__ __forceinline__ bool bwd_tile(const BwdArgs& a, unsigned char* smem, 
   // q = 4 wave + u, else B instruction q = 4 wave + u - 4; one instruction fills 1 KB of the stage).
   // Row-staged tiles (256 rows x 64 k): lane -> row 8q + lane/8, slot lane & 7 holding k-chunk
   // (lane & 7) ^ (lane >> 3) ^ (q & 1).  Column-staged tiles (64 k x 256 columns): lanes 0-31 k-row 2q, 32-63 k-row
-  // 2q + 1, slot lane & 31 of the row holding 16-byte column chunk c with (c / 2) ^ (k & 3) = slot / 2; columns
-  // past the matrix read column 0.  A lane's offsets are fixed but for the k-tile: + kt * step, or, for the W
+  // 2q + 1, slot lane & 31 of the row holding 16-byte column chunk c of granule c / 2 = col_unswz(slot / 2, k);
+  // columns past the matrix read column 0.  A lane's offsets are fixed but for the k-tile: + kt * step, or, for the W
   // items (k over the expert's rows), + the memory row of each of its four k-rows times the stride, read from the
   // row-tile descriptors in global memory three k-tiles ahead (a read just before each load put a global-memory
   // latency in front of every k-tile's loads).
@@ -294,7 +309,7 @@ __device__ __forceinline__ bool bwd_tile(const BwdArgs& a, unsigned char* smem, 
     const int q = wave * 4 + jj;
     const int r = 8 * q + (lane >> 3);                                // row-staged row
     const int kq = 2 * q + (lane >> 5), cs = lane & 31;               // column-staged k-row and slot
-    const int c = (((cs >> 1) ^ (kq & 3)) << 1) | (cs & 1);
+    const int c = (col_unswz(cs >> 1, kq) << 1) | (cs & 1);           // the 16-byte column chunk it holds
     const uint32_t rchunk = (uint32_t)k0 * 2u + (chunk0 ^ ((uint32_t)(q & 1) << 4));
     if (A_TR) {
       aoff[jj] = (uint32_t)(a_col0 + 8 * c < a_cols ? a_col0 + 8 * c : 0) * 2u;
