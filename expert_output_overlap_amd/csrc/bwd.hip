@@ -371,9 +371,13 @@ __device__ __forceinline__ bool bwd_tile(const BwdArgs& a, unsigned char* smem, 
   constexpr int NSLOT = MI * NI, RS = 2, RPS = (MI + NI + RS - 1) / RS, FIRST = RS, HALF = 4;
   constexpr int DPS = (HALF + (NSLOT - FIRST) - 1) / (NSLOT - FIRST);
   bf16x8_t fa[2][MI], fb[2][NI];
-  auto frag1 = [&](const unsigned char* sa, int ks, int i, bf16x8_t* A_, bf16x8_t* B_) {
+  // 32-row MFMA blocks of this wave that hold real rows of the row tile (all MI for W items and full tiles): the
+  // others' MFMAs and A fragment reads are skipped (an expert's last row tile is partly empty)
+  const int mact = A_TR ? MI : min(MI, max(0, (n_rows - wm * 128 + 31) / 32));
+  auto frag1 = [&](const unsigned char* sa, int ks, int i, bf16x8_t* A_, bf16x8_t* B_, bool full) {
     const unsigned char* sb = sa + A_BYTES;
     if (i < MI) {
+      if (!full && i >= mact) return;
       A_[i] = A_TR ? frag_tr(sa, wm * 128 + i * 32, ks, lane) : frag_row(sa, wm * 128 + i * 32, ks, lane);
     } else {
       const int ni = i - MI;
@@ -381,21 +385,23 @@ __device__ __forceinline__ bool bwd_tile(const BwdArgs& a, unsigned char* smem, 
       else B_[ni] = frag_row(sb, ni == 0 ? wn * 32 : 128 + wn * 32, ks, lane);  // gate block, up block
     }
   };
-  auto step = [&](auto ks_tag, auto m1_tag, auto m2_tag, int kt) {
+  auto step = [&](auto ks_tag, auto m1_tag, auto m2_tag, auto full_tag, int kt) {
     constexpr int ks = decltype(ks_tag)::value;
     constexpr bool M1 = decltype(m1_tag)::value, M2 = decltype(m2_tag)::value;
+    constexpr bool FULL = decltype(full_tag)::value;
     constexpr int c = ks & 1;
     const unsigned char* sa = smem + (kt & 1) * BWD_STAGE;
     const unsigned char* nsa = smem + ((kt + 1) & 1) * BWD_STAGE;
 #pragma unroll
     for (int i = 0; i < NSLOT; ++i) {
       const int mi = i / NI, ni = i % NI;
-      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][mi], fb[c][ni], acc[mi][ni], 0, 0, 0);
+      if (FULL || mi < mact)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[c][mi], fb[c][ni], acc[mi][ni], 0, 0, 0);
       if (i < RS) {
 #pragma unroll
         for (int r = i * RPS; r < (i + 1) * RPS && r < MI + NI; ++r) {
-          if (ks < 3) frag1(sa, ks + 1, r, fa[c ^ 1], fb[c ^ 1]);
-          else if (M1) frag1(nsa, 0, r, fa[c ^ 1], fb[c ^ 1]);
+          if (ks < 3) frag1(sa, ks + 1, r, fa[c ^ 1], fb[c ^ 1], FULL);
+          else if (M1) frag1(nsa, 0, r, fa[c ^ 1], fb[c ^ 1], FULL);
         }
       }
       if (i >= FIRST && ((ks == 3 && M2) || (ks == 0 && M1))) {
@@ -427,13 +433,13 @@ __device__ __forceinline__ bool bwd_tile(const BwdArgs& a, unsigned char* smem, 
       }
     }
   };
-  auto tile = [&](auto m1, auto m2, int kt) {
-    step(std::integral_constant<int, 0>{}, m1, m2, kt);
-    step(std::integral_constant<int, 1>{}, m1, m2, kt);
-    step(std::integral_constant<int, 2>{}, m1, m2, kt);
-    step(std::integral_constant<int, 3>{}, m1, m2, kt);
+  auto tile = [&](auto m1, auto m2, auto full, int kt) {
+    step(std::integral_constant<int, 0>{}, m1, m2, full, kt);
+    step(std::integral_constant<int, 1>{}, m1, m2, full, kt);
+    step(std::integral_constant<int, 2>{}, m1, m2, full, kt);
+    step(std::integral_constant<int, 3>{}, m1, m2, full, kt);
   };
-  if (nk > 0) {
+  auto kloop = [&](auto full) {
     // prologue: k-tile 0 whole, the A loads of k-tile 1 (its B loads go out in k-step 0 of k-tile 0)
     int ids0[4] = {0, 0, 0, 0};
     if (A_TR) {
@@ -446,18 +452,22 @@ __device__ __forceinline__ bool bwd_tile(const BwdArgs& a, unsigned char* smem, 
     wait_loads_barrier();
     if (nk == 1) zero_tail(0);
 #pragma unroll
-    for (int i = 0; i < MI + NI; ++i) frag1(smem, 0, i, fa[0], fb[0]);
+    for (int i = 0; i < MI + NI; ++i) frag1(smem, 0, i, fa[0], fb[0], decltype(full)::value);
     if (nk > 1) {
 #pragma unroll
       for (int u = 0; u < HALF; ++u) dma1(1, lds0 + BWD_STAGE, u, ids1);
     }
     int kt = 0;
-    for (; kt + 2 < nk; ++kt) tile(std::true_type{}, std::true_type{}, kt);
+    for (; kt + 2 < nk; ++kt) tile(std::true_type{}, std::true_type{}, full, kt);
     if (kt + 1 < nk) {
-      tile(std::true_type{}, std::false_type{}, kt);
+      tile(std::true_type{}, std::false_type{}, full, kt);
       ++kt;
     }
-    tile(std::false_type{}, std::false_type{}, kt);
+    tile(std::false_type{}, std::false_type{}, full, kt);
+  };
+  if (nk > 0) {
+    if (mact == MI) kloop(std::true_type{});
+    else kloop(std::false_type{});
   }
 
   // ---- epilogues ---------------------------------------------------------------------------------------------
@@ -816,10 +826,11 @@ void bwd_fill_consumer(ConsumerArgs& c, const BwdLaunch& p, const uint32_t* flag
   c.obs = nullptr;
 }
 
-// the dX items' k-splits: about as many 256 x 256 output tiles as CUs, each split a multiple of 128 columns of
-// (dG | dU) (the G items' width), at most 8
+// the dX items' k-splits: an item's k about d (2f / S ~ d, as long as the H and G items'), each split a multiple of
+// 128 columns of (dG | dU) (the G items' width), at most 4: the last split to arrive reads every slot alone, and
+// 7 splits on the Mixtral-like shard (2 MB of partial sums per tile) cost the dX items 17% more CU time than 4
 int bwd_splits(int d, int f) {
-  const int want = std::min(8, std::max(1, (4 * f + d) / (2 * d)));
+  const int want = std::min(4, std::max(1, (4 * f + d) / (2 * d)));
   for (int c = want; c > 1; --c)
     if ((2 * f / 128) % c == 0) return c;
   return 1;

@@ -23,7 +23,7 @@ BWD_SMALL = [
     mi.Spec("bwd_small", R=4, T_o=240, G=8, E_l=2, k=2, d=256, f=256, M=32, seed=41),
     # d and f not multiples of 256 (masked columns), three experts, ragged row tiles
     mi.Spec("bwd_ragged", R=3, T_o=300, G=6, E_l=3, k=2, d=192, f=384, M=16, seed=42),
-    # f = 8 d: the dX items split 8 ways over k (partial sums, last arrival sums), skewed routing
+    # f = 8 d: the dX items split 4 ways over k (partial sums, last arrival sums), skewed routing
     mi.Spec("bwd_splitk", R=4, T_o=200, G=8, E_l=2, k=2, d=128, f=1024, M=32, seed=43, bias="zipf", bias_param=1.2),
     # an expert with no rows (zero weight gradients) and tokens with no local slot
     mi.Spec("bwd_sparse", R=2, T_o=64, G=16, E_l=4, k=1, d=128, f=128, M=16, seed=44, bias="zipf", bias_param=3.0),
