@@ -688,10 +688,11 @@ int moe_expert_ffn_backward(const moe_shape* s, const moe_layout* L, const moe_b
   if (n_cu <= 0) return fail(MOE_EHIP, "cannot query the CU count");
   if (cfg->consumer_cus < -1 || cfg->consumer_cus > n_cu / 2)
     return fail(MOE_EINVAL, "consumer_cus must be -1 (none), 0 (library default) or in [1, CUs/2]");
-  // the default partition: 8 CUs (a quarter of a small device's), which return the dX rows while the producers run
-  // the weight-gradient items that end the list
-  const int C_def = std::max(1, std::min(8, n_cu / 4));
-  const int C = cfg->consumer_cus > 0 ? cfg->consumer_cus : cfg->consumer_cus == 0 ? C_def : 0;
+  // the default: no consumer workgroups (every workgroup takes the copy units once the weight-gradient tiles are
+  // handed out).  On one device the dX return is an HBM copy of about 2% of the launch's time on the whole chip, and
+  // C workgroups returning rows during the weight-gradient tiles slowed the launch more than that (DeepSeek-V3-like
+  // shard: 7.17 ms with 8 against 6.97 + 0.17 ms for the producers alone and then the return)
+  const int C = cfg->consumer_cus > 0 ? cfg->consumer_cus : 0;
   BwdLaunch p;
   p.R = s->R;
   p.E = s->num_local_experts;

@@ -625,15 +625,13 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void k_bwd_ffn(BwdArgs a) {
   if (blockIdx.x == 0 && tid == 0)  // the W-tile counter starts at zero for this launch
     __hip_atomic_store(a.wclaim, (uint64_t)a.wstamp << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (load_status(a.status) != 0) return;
-  if (a.join && blockIdx.x == 0) consumer_stamp(a.cons);
+  if ((a.join || C > 0) && blockIdx.x == 0) consumer_stamp(a.cons);
   const int n_mt = a.scalars[a.sc_nmt];
-  const bool producer = (int)blockIdx.x >= C;
-  // H, G and X items: round-robin over the producers, consecutive items on the workgroups of one XCD (a consumer
-  // workgroup's index minus C is negative, and would start a negative item index)
-  const int n_static = producer ? bwd_n_static(a, n_mt) : 0;
-  const int G = gridDim.x - C;
-  int bid = producer ? (int)blockIdx.x - C : 0;
-  if (producer && (G & 7) == 0 && (C & 7) == 0) bid = (bid & 7) * (G >> 3) + (bid >> 3);
+  // H, G and X items: round-robin over every workgroup, consecutive items on the workgroups of one XCD
+  const int n_static = bwd_n_static(a, n_mt);
+  const int G = gridDim.x;
+  int bid = blockIdx.x;
+  if ((G & 7) == 0) bid = (bid & 7) * (G >> 3) + (bid >> 3);
   auto stop_on = [&](int st) {  // after a wait: true when the workgroup must end (status set)
     if (st == 1 && tid == 0) set_status(a.status, MOE_ETIMEOUT);
     return st != 0;
@@ -663,10 +661,15 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void k_bwd_ffn(BwdArgs a) {
     }
     if (!ok) return;
   }
+  // The first C workgroups return dX rows now, while the others start on the weight-gradient tiles (the dX tiles
+  // complete with the static items), and take W tiles too once every copy unit is handed out.  (C workgroups
+  // returning from the start and running no static items cost the launch more than the return takes on the
+  // whole chip after it.)
+  if ((int)blockIdx.x < C) consumer_role(a.cons);
   // W tiles: nobody waits on them, and their lengths follow the experts' row counts, so they are handed out at run
   // time from the launch's counter, longest experts first (a static share left some workgroups 20-25% more work
   // than others)
-  if (producer) {
+  {
     __syncthreads();
     if (tid < a.E) {
       sh.e_rows[tid] = 0;
@@ -733,8 +736,8 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void k_bwd_ffn(BwdArgs a) {
       if (!ok) return;
     }
   }
-  // the consumer workgroups return dX rows from the start; with join, producers too once their items are done
-  if (a.join || (int)blockIdx.x < C) consumer_role(a.cons);
+  // with join, every workgroup takes the copy units left once the W tiles are handed out
+  if (a.join) consumer_role(a.cons);
 }
 
 // dY rows of the padded layout: row p (token t, local expert e of its band) = bf16(w dOut[t]) with w the weight of
@@ -771,35 +774,79 @@ __global__ __launch_bounds__(256) void k_bwd_dy(const uint16_t* __restrict__ d_o
 // The combine's backward, one workgroup per token (owner r = t / T_o): dx[t] = bf16 of the fp32 sum of the token's
 // delivered dX rows (slot order), dw[t, j] = <dOut[t], y> over the forward's delivered row of slot j (fp32), 0 for a
 // slot routed elsewhere.
+// The combine's backward, one wave per token (out = sum_j w_j y_j over the token's local slots): dx = bf16 of the sum
+// of the slots' returned dX rows in ascending slot order, and the routing weights' gradient dw[t][j] = <dOut_t, y_j>
+// over the delivered forward row (0 for slots routed elsewhere).  16-byte loads, two chunks per lane at a time; the
+// dOut chunk is loaded once for all the token's slots, and each slot's dot product stays in a register until one
+// wave sum at the end.  (A workgroup per token with 2-byte loads and a barrier per slot ran at 1.9 TB/s.)
+#define BWD_MAX_K 16
 __global__ __launch_bounds__(256) void k_bwd_combine(const uint16_t* __restrict__ d_out, const int32_t* __restrict__ plan,
-                                                     RecvPtrs y_recv, RecvPtrs dx_recv, int T_o, int k, int d,
+                                                     RecvPtrs y_recv, RecvPtrs dx_recv, int T, int T_o, int k, int d,
                                                      uint16_t* __restrict__ dx, float* __restrict__ dw) {
-  const int64_t t = blockIdx.x;
-  const int r = (int)(t / T_o), tid = threadIdx.x;
-  __shared__ float s_part[8][4];
-  const uint16_t* o = d_out + t * d;
-  for (int c = tid; c < d; c += 256) {
-    float acc = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int pr = plan[t * k + j];
-      if (pr >= 0) acc += bf16_to_f32(((const uint16_t*)dx_recv.p[r])[(int64_t)pr * d + c]);
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int r = (int)(t / T_o), rv = d / 8;  // 16-byte chunks per row
+  int pj[BWD_MAX_K];
+#pragma unroll
+  for (int j = 0; j < BWD_MAX_K; ++j) pj[j] = j < k ? plan[t * k + j] : -1;
+  const uint4* o = (const uint4*)(d_out + t * d);
+  const uint4* yb = (const uint4*)y_recv.p[r];
+  const uint4* xb = (const uint4*)dx_recv.p[r];
+  uint4* dst = (uint4*)(dx + t * d);
+  auto lo = [](uint32_t v) { return __uint_as_float(v << 16); };
+  auto hi = [](uint32_t v) { return __uint_as_float(v & 0xffff0000u); };
+  float dot[BWD_MAX_K];
+#pragma unroll
+  for (int j = 0; j < BWD_MAX_K; ++j) dot[j] = 0.f;
+  constexpr int U = 2;
+  for (int c0 = lane; c0 < rv; c0 += U * 64) {
+    uint4 ov[U];
+    float acc[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * 64;
+      ov[u] = c < rv ? o[c] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[u][i] = 0.f;
     }
-    dx[t * d + c] = (uint16_t)bf16_bits(acc);
+#pragma unroll
+    for (int j = 0; j < BWD_MAX_K; ++j) {
+      if (pj[j] < 0) continue;  // the same for the whole wave
+      uint4 yv[U], xv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * 64;
+        yv[u] = c < rv ? yb[(int64_t)pj[j] * rv + c] : make_uint4(0, 0, 0, 0);
+        xv[u] = c < rv ? xb[(int64_t)pj[j] * rv + c] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t oq[4] = {ov[u].x, ov[u].y, ov[u].z, ov[u].w}, yq[4] = {yv[u].x, yv[u].y, yv[u].z, yv[u].w};
+        const uint32_t xq[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dot[j] += lo(oq[i]) * lo(yq[i]) + hi(oq[i]) * hi(yq[i]);
+          acc[u][2 * i] += lo(xq[i]);
+          acc[u][2 * i + 1] += hi(xq[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * 64;
+      if (c < rv)
+        dst[c] = make_uint4(bf16_bits(acc[u][0]) | (bf16_bits(acc[u][1]) << 16),
+                            bf16_bits(acc[u][2]) | (bf16_bits(acc[u][3]) << 16),
+                            bf16_bits(acc[u][4]) | (bf16_bits(acc[u][5]) << 16),
+                            bf16_bits(acc[u][6]) | (bf16_bits(acc[u][7]) << 16));
+    }
   }
-  for (int j = 0; j < k; ++j) {
-    const int pr = plan[t * k + j];
-    if (pr < 0) {
-      if (tid == 0) dw[t * k + j] = 0.f;
-      continue;
-    }
-    const uint16_t* y = (const uint16_t*)y_recv.p[r] + (int64_t)pr * d;
-    float s = 0.f;
-    for (int c = tid; c < d; c += 256) s += bf16_to_f32(o[c]) * bf16_to_f32(y[c]);
-    s = wave_sum_f(s);
-    if ((tid & 63) == 0) s_part[j & 7][tid >> 6] = s;
-    __syncthreads();
-    if (tid == 0) dw[t * k + j] = (s_part[j & 7][0] + s_part[j & 7][1]) + (s_part[j & 7][2] + s_part[j & 7][3]);
-    __syncthreads();
+#pragma unroll
+  for (int j = 0; j < BWD_MAX_K; ++j) {
+    if (j >= k) break;
+    const float sj = pj[j] >= 0 ? wave_sum_f(dot[j]) : 0.f;
+    if (lane == 0) dw[t * k + j] = sj;
   }
 }
 
@@ -932,7 +979,7 @@ int launch_bwd_combine(const BwdLaunch& p, int T_o, const int32_t* plan, void* c
   }
   const int64_t T = (int64_t)p.R * T_o;
   if (T > 0)
-    hipLaunchKernelGGL(k_bwd_combine, dim3((unsigned)T), dim3(256), 0, st, (const uint16_t*)p.d_out, plan, yr, xr, T_o,
-                       p.k, p.d, (uint16_t*)dx, dw);
+    hipLaunchKernelGGL(k_bwd_combine, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, (const uint16_t*)p.d_out, plan, yr,
+                       xr, (int)T, T_o, p.k, p.d, (uint16_t*)dx, dw);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -322,8 +322,10 @@ int64_t moe_bwd_flags_count(const moe_shape* s);
  * persistent launch of tile items (dH, then h / dG / dU, then dX with the split-K partial sums summed in split
  * order, then the weight gradients), each publishing an epoch-valued flag that later items and the consumer role
  * wait on; the consumer copies each finished segment's dX rows into dx_recv[owner] (the self owner's rows are
- * stored there by the dX items).  cfg: mode 0 = overlapped (consumer_cus workgroups return rows from the start,
- * every other workgroup joins once its items are done; 0 = library default, 8 CUs; -1 = none), mode 1 =
+ * stored there by the dX items).  cfg: mode 0 = overlapped (every workgroup runs its share of the dH, h / dG / dU
+ * and dX items; then the first consumer_cus workgroups return rows while the others take weight-gradient tiles, and
+ * join those once every copy unit is handed out; every workgroup takes the copy units left at the end; 0 and -1 =
+ * none: the return after the weight-gradient tiles, on every workgroup, which on one device is the faster), mode 1 =
  * sequential (the producers, then the return on every CU); epoch and watchdog_ticks as in the forward; results
  * are identical in both modes.  The layout must be the forward's (moe_layout_build of the same routing). */
 int moe_expert_ffn_backward(const moe_shape* s, const moe_layout* L, const moe_bwd_args* b, uint32_t* flags,
