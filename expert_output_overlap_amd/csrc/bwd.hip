@@ -218,30 +218,6 @@ __device__ __forceinline__ BwdItem bwd_w_item(const BwdArgs& a, const BwdShared&
   return it;
 }
 
-// Wave 0: waits until *flag_at(j) == epoch for every j < n, with one load per lane in flight (64 at a time) and a
-// sleep between rounds while one stays unset.  0: all set; 1: the spin budget ran out; 2: another workgroup
-// reported an error.  (One thread taking the flags one at a time put a memory latency per flag in front of items
-// that wait on dozens of them.)
-template <typename FlagAt>
-__device__ __forceinline__ int poll_flags_wave(FlagAt flag_at, int n, uint32_t epoch, uint64_t budget,
-                                               const int32_t* status) {
-  const int lane = threadIdx.x & 63;
-  const uint64_t t0 = moe_clock();
-  int polls = 0;
-  for (int base = 0; base < n; base += 64) {
-    bool done = base + lane >= n;
-    int nap = 0;
-    for (;;) {
-      if (!done) done = __hip_atomic_load(flag_at(base + lane), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
-      if (__ballot(!done) == 0) break;
-      if (moe_clock() - t0 > budget) return 1;
-      if ((++polls & 15) == 0 && load_status(status) != 0) return 2;
-      for (int k = 0; k <= nap; ++k) __builtin_amdgcn_s_sleep(8);  // ~512 clocks each
-      nap = nap < 1 ? nap + 1 : 1;
-    }
-  }
-  return 0;
-}
 
 template <int KIND>
 __device__ __forceinline__ bool bwd_tile(const BwdArgs& a, unsigned char* smem, BwdShared& sh, const BwdItem& it) {
@@ -648,7 +624,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void k_bwd_ffn(BwdArgs a) {
         const int kk = 2 * a.f / a.S, c0 = it.s * kk;
         const uint32_t* fg = a.fg + (int64_t)it.mt * a.n_g;
         const int st = poll_flags_wave([&](int j) { return &fg[((c0 + 128 * j) % a.f) / 128]; }, kk / 128, a.epoch,
-                                       a.budget, a.status);
+                                       a.budget, a.status, 1);
         if (tid == 0) sh.stop = st;
       }
       __syncthreads();
@@ -726,7 +702,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void k_bwd_ffn(BwdArgs a) {
         const int first = sh.e_first[it.e];
         const int st = poll_flags_wave(
             [&](int j) { return &a.fg[(int64_t)(first + j / nc) * a.n_g + ((c0 + 128 * (j % nc)) % a.f) / 128]; },
-            sh.e_count[it.e] * nc, a.epoch, a.budget, a.status);
+            sh.e_count[it.e] * nc, a.epoch, a.budget, a.status, 1);
         if (tid == 0) sh.stop = st;
       }
       __syncthreads();

@@ -85,6 +85,32 @@ __device__ inline int poll_flags(const uint32_t* fl, int n, uint32_t epoch, uint
   return 0;
 }
 
+// The first wave of a workgroup: waits until *flag_at(j) == epoch for every j < n, with one load per lane in flight
+// (64 at a time; flags that sit side by side share a cache line, so one wave load reads them all) and a sleep
+// between rounds while one stays unset (up to max_nap + 1 sleeps of ~512 clocks).  The status word is looked at
+// every 16 rounds.  0: all set; 1: the spin budget ran out; 2: another workgroup reported an error.  (One thread
+// taking the flags one at a time put a memory round trip per flag in front of items that wait on dozens of them.)
+template <typename FlagAt>
+__device__ __forceinline__ int poll_flags_wave(FlagAt flag_at, int n, uint32_t epoch, uint64_t budget,
+                                               const int32_t* status, int max_nap) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t t0 = moe_clock();
+  int polls = 0;
+  for (int base = 0; base < n; base += 64) {
+    bool done = base + lane >= n;
+    int nap = 0;
+    for (;;) {
+      if (!done) done = __hip_atomic_load(flag_at(base + lane), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
+      if (__ballot(!done) == 0) break;
+      if (moe_clock() - t0 > budget) return 1;
+      if ((++polls & 15) == 0 && load_status(status) != 0) return 2;
+      for (int k = 0; k <= nap; ++k) __builtin_amdgcn_s_sleep(8);  // ~512 clocks each
+      nap = nap < max_nap ? nap + 1 : max_nap;
+    }
+  }
+  return 0;
+}
+
 // ---- the in-launch publish protocol ----------------------------------------------------------------------
 // Results one workgroup hands to another inside a launch (h tiles, split-K partial sums, y tiles) go out with
 // device-scope stores, which write through to the level shared by the XCDs; the producer waits for their

@@ -128,7 +128,10 @@ __device__ __forceinline__ void consumer_role(const ConsumerArgs& a) {
       const int mt0 = a.seg_mtiles[2 * s], mcnt = a.seg_mtiles[2 * s + 1];
       const int nflags = mcnt * a.n_nt;
       const uint32_t* fl = a.flags + (int64_t)mt0 * a.n_nt;
-      if (tid == 0) s_stop = poll_flags(fl, nflags, a.epoch, a.budget, a.status, 3);
+      if (tid < 64) {
+        const int st = poll_flags_wave([&](int j) { return &fl[j]; }, nflags, a.epoch, a.budget, a.status, 3);
+        if (tid == 0) s_stop = st;
+      }
       __syncthreads();
       if (s_stop) {
         if (s_stop == 1 && tid == 0) set_status(a.status, MOE_ETIMEOUT);

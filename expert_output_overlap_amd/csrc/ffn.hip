@@ -360,7 +360,10 @@ __device__ __forceinline__ unsigned long long* obs64(uint32_t* obs, int w) { ret
 // out (status set to MOE_ETIMEOUT) or another workgroup reported an error.
 __device__ bool wait_flags(const uint32_t* fl, int n, uint32_t epoch, uint64_t budget, int32_t* status, int* s_stop) {
   __syncthreads();  // every thread has read *s_stop of the previous wait
-  if (threadIdx.x == 0) *s_stop = poll_flags(fl, n, epoch, budget, status, 1);  // a producer waits briefly
+  if (threadIdx.x < 64) {  // a producer waits briefly
+    const int st = poll_flags_wave([&](int j) { return &fl[j]; }, n, epoch, budget, status, 1);
+    if (threadIdx.x == 0) *s_stop = st;
+  }
   __syncthreads();
   if (*s_stop) {
     if (*s_stop == 1 && threadIdx.x == 0) set_status(status, MOE_ETIMEOUT);
