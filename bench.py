@@ -115,6 +115,28 @@ def _oracle_ffn_sample(s, inp, lay, target_s: float, seed: int = 1):
         n = min(real.size, int(n * max(2.0, 1.2 * target_s / max(dt, 1e-3))))
 
 
+def _oracle_bwd_sample(s, inp, lay, idx, w, target_s: float, seed: int = 3):
+    """The oracle's backward rows (dY, dH, h, dG, dU, dX; no forward y) on a random sample of local slots grown until
+    it takes about target_s; (rows, seconds)."""
+    import moe_inputs as mi
+    import oracle
+
+    t_all, j_all = np.nonzero(idx < s.E_l)
+    d_out = mi.d_out(s)
+    rng = np.random.default_rng(seed)
+    n = 4
+    while True:
+        pick = rng.choice(t_all.size, min(n, t_all.size), replace=False)
+        t, j = t_all[pick], j_all[pick]
+        t0 = time.perf_counter()
+        oracle.bwd_rows(t, idx[t, j], w[t, j], inp["x"], inp["w_gate_up"], inp["w_down"], d_out, s.dtype == "bf16",
+                        want_y=False)
+        dt = time.perf_counter() - t0
+        if dt >= target_s or n >= t_all.size:
+            return pick.size, dt
+        n = min(t_all.size, int(n * max(2.0, 1.2 * target_s / max(dt, 1e-3))))
+
+
 def cpu_baseline(s, inp, target_s: float):
     """The CPU oracle on the same workload: routing, layout, delivery and combine on the full batch, the FFN on a
     bounded random sample of real rows (useful TFLOP/s), every stage timed, all host threads; plus the whole oracle
@@ -144,6 +166,11 @@ def cpu_baseline(s, inp, target_s: float):
     oracle.combine(lay, w, recv, s.R, s.T_o, s.k, s.dtype == "bf16")
     st["combine_s"] = time.perf_counter() - t0
     st["ffn_full_batch_s_extrapolated"] = dt * n_real / n_rows
+    bwd = None
+    if s.dtype == "bf16":  # the backward rows on a sample: 10 d f flops per row (dH 2, g and u 4, dX 4)
+        nb, db = _oracle_bwd_sample(s, inp, lay, idx, w, min(5.0, target_s / 2))
+        bwd = {"value": 10.0 * nb * s.d * s.f / db / 1e12, "unit": "TFLOP/s",
+               "sample": "oracle backward rows (dY, dH, h, dG, dU, dX; fp64) for %d local slots, %.1f s" % (nb, db)}
     # one thread: the whole oracle on Tiny, and the FFN of Skewed on a sample
     _omp_threads(1)
     ts = mi.spec("tiny")
@@ -163,7 +190,7 @@ def cpu_baseline(s, inp, target_s: float):
             "sample": "oracle FFN (fp64, h and y rounded to bf16) on %d of %d real rows, %.1f s; routing, layout, "
                       "delivery and combine of the full batch" % (n_rows, n_real, dt),
             "cpu_model": _cpu_model(), "stages_s": {k: round(v, 4) for k, v in st.items()},
-            "one_thread": one}
+            "one_thread": one, "backward_rows": bwd}
 
 
 def bench_backward(P, s, w1, w2, reps: int, M_real: int) -> dict:
