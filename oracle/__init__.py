@@ -295,17 +295,18 @@ def bwd_rows(tok, expert, w, x, w_gate_up, w_down, d_out, is_bf16: bool, want_y:
     return out
 
 
-def backward(s, inputs: dict, d_out: np.ndarray, lib=None, *, w_rel: float = 0.0) -> dict:
+def backward(s, inputs: dict, d_out: np.ndarray, lib=None, *, w_rel: float = 0.0, self_rank: int = 0) -> dict:
     """Gradients of the MoE layer for the local experts, given dOut = dL/d(combined output) [T, d] (the review page,
     "Where Pith is reading between the lines": MoE training's backward pass): dx [T, d] = sum over the token's
     local slots of the rows' dX (rounded once in bf16 mode, as the combined output is), the routing weights'
     gradient dw [T, k] = <dOut_t, y> (0 for slots routed elsewhere), and the weight gradients
     dw_gate_up [E, 2f, d] = sum over the expert's rows of (dG | dU) x^T and dw_down [E, d, f] = sum of dY h^T
     (numpy matmuls of the rows' parts, in double; backward_reduce).  w_rel: the relative bound to which routing
-    weights are taken as correct, for the admitted values of the parts (bwd_rows)."""
+    weights are taken as correct, for the admitted values of the parts (bwd_rows).  self_rank: the rank whose local
+    experts [self_rank E_l, (self_rank + 1) E_l) the gradients are of."""
     lib = lib or load()
     idx, w = route(inputs["logits"], s.k, lib)
-    lo = 0  # self_rank 0 owns experts [0, E_l)
+    lo = self_rank * s.E_l
     t, j = np.nonzero((idx >= lo) & (idx < lo + s.E_l))
     e = idx[t, j] - lo
     is_bf16 = s.dtype == "bf16"

@@ -49,12 +49,13 @@ def check_in(got, lo, hi, what):
 class BwdRun:
     """One workload on the GPU: forward (route, layout, FFN, combine), then the backward calls."""
 
-    def __init__(self, s):
+    def __init__(self, s, self_rank=0):
         assert torch.cuda.is_available(), "the gpu tests need the MI355X"
-        print("case", s, flush=True)
+        print("case", s, "self_rank", self_rank, flush=True)
         self.s = s
+        self.lo = self_rank * s.E_l  # the local experts' first global id
         self.inp = mi.inputs(s)
-        self.P = MoePath.from_spec(s)
+        self.P = MoePath(s.R, s.T_o, s.G, s.E_l, s.k, s.d, s.f, s.M, s.mgb, s.dtype, self_rank)
         self.dev = {k: to_device(v, s.dtype) for k, v in self.inp.items()}
         self.d_out_h = mi.d_out(s)
         self.d_out = to_device(self.d_out_h, s.dtype)
@@ -67,7 +68,7 @@ class BwdRun:
         assert P.status() == B.MOE_OK
         self.idx, self.w = oracle.route(self.inp["logits"], s.k)
         np.testing.assert_array_equal(P.topk_idx[: s.T].cpu().numpy(), self.idx)
-        self.lay = oracle.layout(self.idx, s.R, s.T_o, s.G, s.E_l, s.k, s.M, s.mgb, 0)
+        self.lay = oracle.layout(self.idx, s.R, s.T_o, s.G, s.E_l, s.k, s.M, s.mgb, self_rank)
 
     def backward(self, **kw):
         P = self.P
@@ -88,7 +89,7 @@ class BwdRun:
         s, lay = self.s, self.lay
         plan = lay["combine_plan"]
         t, j = np.nonzero(sel & (plan >= 0))
-        e = self.idx[t, j]
+        e = self.idx[t, j] - self.lo
         r = t // s.T_o
         g = e * s.R + r
         p = lay["padded_off"][g] + plan[t, j] - lay["recv_off"][g]
@@ -140,12 +141,14 @@ class BwdRun:
                             "dW_gate_up[%d]" % ee, slack=sl["dw_gate_up"][i])
 
 
-@pytest.mark.parametrize("s", BWD_SMALL, ids=lambda v: v.name)
-def test_backward_parity(s):
+@pytest.mark.parametrize("s,self_rank", [(s, 0) for s in BWD_SMALL] + [(BWD_SMALL[1], 1), (BWD_SMALL[2], 1), (BWD_SMALL[3], 3)],
+                         ids=lambda v: v.name if hasattr(v, "name") else "rank%d" % v)
+def test_backward_parity(s, self_rank):
     """Whole backward (dY dispatch, dH, h / dG / dU, dX with its return, the weight gradients, the combine's
-    backward) against the oracle on every row, token and expert; then the sequential call, and the overlapped call
-    with no consumer partition and with one of 16, give the same bits."""
-    run = BwdRun(s)
+    backward) against the oracle on every row, token and expert, at rank 0 and at ranks 1 and 3 (whose own dX rows
+    the dX items store straight into their receive buffer); then the sequential call, and the overlapped call with
+    no consumer partition and with one of 16, give the same bits."""
+    run = BwdRun(s, self_rank)
     b = run.backward(mode=0, consumer_cus=8)
     t, j, e, r, p = run.rows_of(np.ones((s.T, s.k), bool))
     run.check(b, t, j, e, r, p, np.arange(s.T), list(range(s.E_l)))

@@ -837,6 +837,24 @@ def test_backward_admitted_roundings_cover_fp32_evaluations(orc):
             assert ((lo[:, q] <= v) & (v <= hi[:, q])).all(), q
 
 
+def test_backward_at_another_rank(orc):
+    """Rank 1's gradients (its local experts are the global [E_l, 2 E_l)) of a batch whose routing logits swap global
+    experts [0, E_l) and [E_l, 2 E_l) equal rank 0's gradients of the original batch: only the offset of the local
+    experts changes."""
+    s = BWD_SPEC
+    inp = mi.inputs(s)
+    d_out = mi.d_out(s)
+    sw = dict(inp)
+    lg = inp["logits"].copy()
+    E = s.E_l
+    lg[:, [*range(E, 2 * E), *range(0, E)]] = inp["logits"][:, : 2 * E]
+    sw["logits"] = lg
+    a = oracle.backward(s, inp, d_out, orc)
+    b = oracle.backward(s, sw, d_out, orc, self_rank=1)
+    for k in ("dx", "dw", "dw_gate_up", "dw_down"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
 def test_backward_no_local_slot_gives_zero(orc):
     """A token none of whose slots is routed to a local expert gets a zero dx row and zero routing gradients; an
     expert with no rows gets zero weight gradients."""
