@@ -51,6 +51,8 @@ def overlap_stats(ts: np.ndarray, n_segs: int, tick_ns: float = 10.0) -> dict:
         "copy_time_us": float(tot) * tick_ns / 1e3,
         "exposed_tail_us": max(0, int(e.max()) - p1) * tick_ns / 1e3 if n_segs else 0.0,
         "first_copy_after_start_us": (int(s.min()) - p0) * tick_ns / 1e3 if n_segs else None,
+        # from the first copy start to the last copy end: the window the overlapped return took
+        "copy_window_us": (int(e.max()) - int(s.min())) * tick_ns / 1e3 if n_segs else 0.0,
     }
 
 
@@ -354,11 +356,12 @@ def main():
     # FFN call alone, overlapped and sequential (events on the caller stream around the call)
     def time_ffn(mode, reps, xt=None):
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        P.ffn(w1, w2, mode=mode, consumer_cus=cus, band_window=args.band_window, x_tokens=xt)
+        c = cus if mode != 3 else max(cus, 0)  # the DMA return has no consumer workgroups to leave out
+        P.ffn(w1, w2, mode=mode, consumer_cus=c, band_window=args.band_window, x_tokens=xt)
         ts = []
         for _ in range(reps):
             ev0.record()
-            P.ffn(w1, w2, mode=mode, consumer_cus=cus, band_window=args.band_window, x_tokens=xt)
+            P.ffn(w1, w2, mode=mode, consumer_cus=c, band_window=args.band_window, x_tokens=xt)
             ev1.record()
             ev1.synchronize()
             ts.append(ev0.elapsed_time(ev1))
@@ -386,7 +389,7 @@ def main():
         ovl.append(overlap_stats(P.timestamps.cpu().numpy().view(np.uint64), sc["n_segs"]))
     ratio = float(np.median([o["overlap_ratio"] for o in ovl if o["overlap_ratio"] is not None]))
     o_med = {k: float(np.median([o[k] for o in ovl])) for k in ("producer_span_us", "copy_time_us",
-                                                                   "exposed_tail_us")}
+                                                                   "exposed_tail_us", "copy_window_us")}
     torch.cuda.synchronize()
     assert P.status() == B.MOE_OK
 
@@ -422,6 +425,12 @@ def main():
         "speedup_seq_over_ovl": round(t_seq[0] / t_ovl[0], 4),
         "copy_ms_sequential": round(copy_seq_ms, 4),
         "copy_gbs_sequential": round(copy_bytes / (copy_seq_ms * 1e-3) / 1e9, 1),
+        "copy_pct_hbm_peak_sequential": round(100 * copy_bytes / (copy_seq_ms * 1e-3) / 8e12, 2),
+        # the overlapped return over the window it took (first copy start to last copy end), and what share of the
+        # sequential return's time the overlapped call saved
+        "copy_gbs_overlapped_window": round(copy_bytes / (o_med["copy_window_us"] * 1e-6) / 1e9, 1)
+        if o_med["copy_window_us"] > 0 else None,
+        "hidden_fraction_of_sequential_copy": round((t_seq[0] - t_ovl[0]) / copy_seq_ms, 3) if copy_seq_ms > 0 else None,
         # sequential = the FFN launch on every CU, then the return alone on every CU: its two parts, and what the
         # overlapped launch saves against their sum (medians)
         "sequential_parts_ms": {"ffn": round(s1 / sn, 4), "return": round(copy_seq_ms, 4)},
