@@ -216,3 +216,33 @@ def test_backward_full_size(name):
     b = run.backward(mode=1)
     for k, v in keep.items():
         np.testing.assert_array_equal(bits(b[k]), v, err_msg="sequential %s" % k)
+
+
+def test_backward_ordering_stress():
+    """Publish/acquire ordering of the backward launch under stress (the page's "What would settle it", as for the
+    forward): 300 overlapped calls on a split-K shape over consumer partitions {none, 1, 2, 4, 8, 16, 32} and shuffled
+    epochs; every call's dx, weight gradients and returned dX rows equal the sequential call's bit for bit.  Stops at
+    the first mismatch (and names the call)."""
+    s = BWD_SMALL[3]
+    run = BwdRun(s)
+    b = run.backward(mode=1)
+    keys = ("dx", "dw_route", "dw_gate_up", "dw_down")
+    ref = {k: b[k].clone() for k in keys}
+    ref_recv = [b["dx_recv"][r][: int(run.lay["N_r"][r])].clone() for r in range(s.R)]
+    rng = np.random.default_rng(77)
+    last = run.P.bwd_epoch
+    for it in range(300):
+        cus = int(rng.choice([-1, 1, 2, 4, 8, 16, 32]))
+        ep = last
+        while ep == last:  # shuffled, but never the value the flags hold from the previous call
+            ep = int(rng.integers(1, 1 << 31))
+        last = ep
+        b = run.backward(mode=0, consumer_cus=cus, epoch=ep)
+        for k in keys:
+            if not torch.equal(b[k].view(torch.int32 if b[k].element_size() == 4 else torch.int16),
+                               ref[k].view(torch.int32 if ref[k].element_size() == 4 else torch.int16)):
+                raise AssertionError("call %d (consumer_cus %d, epoch %d): %s differs" % (it, cus, ep, k))
+        for r in range(s.R):
+            got = b["dx_recv"][r][: ref_recv[r].shape[0]]
+            if not torch.equal(got.view(torch.int16), ref_recv[r].view(torch.int16)):
+                raise AssertionError("call %d (consumer_cus %d, epoch %d): dX rows of owner %d differ" % (it, cus, ep, r))
