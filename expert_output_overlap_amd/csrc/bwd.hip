@@ -15,8 +15,9 @@
 // flags of its split, split-K partial sums summed in split order by the last to arrive, flag fx, which the
 // consumer role waits on to copy the other owners' rows (the self owner's rows are stored straight into its buffer,
 // as in the forward); W (expert, 256 x 256 tile of dWd or dWgu, k over the expert's rows) after the fg flags of the
-// expert's row tiles.  Every wait is on an earlier item of the list, and each workgroup runs its items in list
-// order, so the earliest unfinished item can always run.
+// expert's row tiles.  H, G and X go round-robin over the workgroups, each in list order, and every wait of one is
+// on an earlier item, so the earliest unfinished item can always run; W tiles, which nobody waits on, are handed out
+// at run time once a workgroup's H, G and X items are done.
 //
 // Operands whose k runs along rows of memory (x, dY, (dG | dU) as the rows of a row tile; Wgu rows for g and u) are
 // staged as in the forward.  Operands whose k runs down columns (Wd and Wgu as the second operand of dH and dX; all
@@ -24,7 +25,8 @@
 // their MFMA fragments are read with the LDS transpose read (ds_read_b64_tr_b16): in a group of 16 lanes, lane j
 // gives the address of row r0 + j / 4, columns c0 + 4 (j % 4) .. + 3, and lane l receives column c0 + l of rows
 // r0 .. r0 + 3, so two reads give a lane the 8 consecutive k of its column that the MFMA takes.  Such a tile keeps
-// 32-byte column granule g of row r at granule g ^ (r & 3), so that the four rows of a read fall in different banks.
+// 32-byte column granule g of row r at granule col_swz(g, r), so that each half-wave of a read hits 64 distinct
+// banks.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -76,13 +78,8 @@ struct BwdArgs {
   ConsumerArgs cons;
 };
 
-// 4-byte and 2-byte stores with the device-scope cache policy (data other workgroups read inside the launch)
-__device__ __forceinline__ void store4_coherent(void* p, float v) {
-  asm volatile("global_store_dword %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
-}
-__device__ __forceinline__ void store2_coherent(void* p, uint32_t v) {
-  asm volatile("global_store_short %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
-}
+// 8-byte stores with the device-scope cache policy (data other workgroups read inside the launch; the s_nop as in
+// store16_coherent)
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void store8_coherent(void* p, u32x2_t v) {
   asm volatile("global_store_dwordx2 %0, %1, off sc1\n\ts_nop 1" ::"v"(p), "v"(v) : "memory");
