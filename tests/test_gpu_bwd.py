@@ -49,12 +49,14 @@ def check_in(got, lo, hi, what):
 class BwdRun:
     """One workload on the GPU: forward (route, layout, FFN, combine), then the backward calls."""
 
-    def __init__(self, s, self_rank=0):
+    def __init__(self, s, self_rank=0, logits=None):
         assert torch.cuda.is_available(), "the gpu tests need the MI355X"
         print("case", s, "self_rank", self_rank, flush=True)
         self.s = s
         self.lo = self_rank * s.E_l  # the local experts' first global id
         self.inp = mi.inputs(s)
+        if logits is not None:
+            self.inp["logits"] = logits
         self.P = MoePath(s.R, s.T_o, s.G, s.E_l, s.k, s.d, s.f, s.M, s.mgb, s.dtype, self_rank)
         self.dev = {k: to_device(v, s.dtype) for k, v in self.inp.items()}
         self.d_out_h = mi.d_out(s)
@@ -246,3 +248,42 @@ def test_backward_ordering_stress():
             got = b["dx_recv"][r][: ref_recv[r].shape[0]]
             if not torch.equal(got.view(torch.int16), ref_recv[r].view(torch.int16)):
                 raise AssertionError("call %d (consumer_cus %d, epoch %d): dX rows of owner %d differ" % (it, cus, ep, r))
+
+
+def test_backward_empty_and_degenerate_inputs():
+    """No tokens (every weight-gradient tile is still written, as zeros); no token routed to a local expert (every
+    gradient zero); every token routed to local expert 0 (which then holds a slot of every token) against the
+    oracle."""
+    s = mi.spec("tiny", T_o=0)
+    P = MoePath.from_spec(s)
+    P.route(torch.empty(0, s.G, device="cuda"))
+    P.layout(torch.empty(0, s.d, dtype=torch.bfloat16, device="cuda"))
+    w1, w2 = (to_device(a, s.dtype) for a in mi.weights(s))
+    P.ffn(w1, w2)
+    P.combine()
+    b = P.bwd_buffers()
+    b["dw_gate_up"].fill_(float("nan"))
+    b["dw_down"].fill_(float("nan"))
+    d_out = torch.empty(0, s.d, dtype=torch.bfloat16, device="cuda")
+    P.backward(d_out, w1, w2)
+    P.combine_backward(d_out)
+    torch.cuda.synchronize()
+    assert P.status() == B.MOE_OK
+    assert (b["dw_gate_up"] == 0).all() and (b["dw_down"] == 0).all()
+    # no token routed to a local expert
+    s = mi.spec("tiny")
+    lg = mi.logits(s)
+    lg[:, : s.E_l] -= 100.0
+    run = BwdRun(s, logits=lg)
+    b = run.backward(mode=0)
+    assert int(run.lay["M_pad"]) == 0
+    assert (f64(b["dx"][: s.T]) == 0).all() and (b["dw_route"][: s.T] == 0).all()
+    assert (b["dw_gate_up"] == 0).all() and (b["dw_down"] == 0).all()
+    # every token routed to local expert 0
+    lg = mi.logits(s)
+    lg[:, 0] += 100.0
+    run = BwdRun(s, logits=lg)
+    b = run.backward(mode=0)
+    t, j, e, r, p = run.rows_of(np.ones((s.T, s.k), bool))
+    assert (e == 0).sum() == s.T  # expert 0 holds one slot of every token
+    run.check(b, t, j, e, r, p, np.arange(s.T), list(range(s.E_l)))
