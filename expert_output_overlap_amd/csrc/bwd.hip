@@ -730,16 +730,24 @@ __global__ __launch_bounds__(256) void k_bwd_dy(const uint16_t* __restrict__ d_o
       if (topk_idx[(int64_t)t * k + j] == eg) w = topk_w[(int64_t)t * k + j];
     const uint4* src = (const uint4*)(d_out + (int64_t)t * d);
     uint4* dst = (uint4*)(dy + p * d);
-    for (int c = lane; c < d / 8; c += 64) {
-      const uint4 v = src[c];
-      const uint32_t in[4] = {v.x, v.y, v.z, v.w};
-      uint32_t o[4];
+    constexpr int U = 4;  // chunks per lane whose loads all go out before any is used
+    const int rv = d / 8;
+    for (int c0 = lane; c0 < rv; c0 += U * 64) {
+      uint4 v[U];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float lo16 = __uint_as_float(in[q] << 16) * w, hi16 = __uint_as_float(in[q] & 0xffff0000u) * w;
-        o[q] = bf16_bits(lo16) | (bf16_bits(hi16) << 16);
+      for (int u = 0; u < U; ++u) v[u] = c0 + u * 64 < rv ? src[c0 + u * 64] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (c0 + u * 64 >= rv) break;
+        const uint32_t in[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        uint32_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float lo16 = __uint_as_float(in[q] << 16) * w, hi16 = __uint_as_float(in[q] & 0xffff0000u) * w;
+          o[q] = bf16_bits(lo16) | (bf16_bits(hi16) << 16);
+        }
+        dst[c0 + u * 64] = make_uint4(o[0], o[1], o[2], o[3]);
       }
-      dst[c] = make_uint4(o[0], o[1], o[2], o[3]);
     }
   }
 }
