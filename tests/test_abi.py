@@ -153,6 +153,33 @@ def test_flag_count_covers_row_tiles():
     assert B.moe_ffn_flags_count(sf) == (Lf.cap_mtiles * (256 // 64) + 63) // 64 * 64 + 2
 
 
+def _cap_mtiles(s):
+    L = B.moe_layout()
+    nbytes = B.moe_layout_workspace_bytes(s)
+    buf = np.zeros(nbytes + 256, np.uint8)
+    base = (buf.ctypes.data + 255) // 256 * 256
+    assert B.lib().moe_layout_bind(ctypes.byref(s), ctypes.c_void_p(base), nbytes, ctypes.byref(L)) == 0
+    return L.cap_mtiles
+
+
+def test_backward_flag_count():
+    """The backward's flag buffer holds a flag per dX, dH and h / dG / dU tile, the k-split arrival counters, the
+    split-K partial sums (4 splits where f = 3.5 d, none where f < d), the copy-unit and weight-gradient counters;
+    fp32 shapes and f not a multiple of 128 have no backward."""
+    s = shape(d=4096, f=14336)
+    cap = _cap_mtiles(s)
+    n = B.moe_bwd_flags_count(s)
+    n_x, n_h, n_g = 4096 // 256, 14336 // 256, 14336 // 128
+    assert n >= cap * (n_x + n_h + n_g + 2 * n_x) + cap * n_x * 4 * 256 * 256 + 4
+    assert n < cap * (n_x + n_h + n_g + 2 * n_x) + cap * n_x * 5 * 256 * 256  # 4 splits, not more
+    s1 = shape(d=7168, f=2048)
+    cap1 = _cap_mtiles(s1)
+    n1 = B.moe_bwd_flags_count(s1)
+    assert cap1 * (7168 // 256 + 2048 // 256 + 2048 // 128) <= n1 < cap1 * 256 * 256  # no partial sums
+    assert B.moe_bwd_flags_count(shape(d=256, f=192)) == -1
+    assert B.moe_bwd_flags_count(shape(dtype=B.MOE_F32, d=256, f=512)) == -1
+
+
 CSRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "expert_output_overlap_amd", "csrc")
 
 
