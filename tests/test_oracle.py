@@ -676,6 +676,56 @@ def test_combine_allowance_admits_one_step_of_each_row_and_no_more(orc):
                                   [2.0 ** -7, 2.0 ** -7, 2.0 ** -6, 2.0 ** -8, 2.0 ** -133, 2.0 ** -133])
 
 
+def test_backward_allowance_admits_the_intervals_and_no_more(orc):
+    """The backward's allowance (tolerance.backward_slack): sums whose parts took other admitted values (dY, h, dG and
+    dU each at the far end of its interval with probability 1/2, the rows' dX recomputed from the moved dG | dU and
+    rounded as returned) pass the check, and some fail it without the allowance; an error planted past the stated
+    tolerance plus the allowance fails."""
+    import tolerance
+
+    s = mi.Spec("bwd_slack", R=2, T_o=160, G=4, E_l=2, k=2, d=256, f=256, M=32, seed=39)
+    inp = mi.inputs(s)
+    d_out = mi.d_out(s)
+    ref = oracle.backward(s, inp, d_out, orc, w_rel=2e-6)
+    t, j = ref["rows"]
+    p = ref["parts"]
+    e = ref["topk_idx"][t, j]
+    f = s.f
+    rng = np.random.default_rng(9)
+
+    def far(v, lo, hi):
+        end = np.where(hi - v >= v - lo, hi, lo)
+        return np.where(rng.random(v.shape) < 0.5, end, v)
+
+    adm = p["adm"]
+    moved = dict(p)
+    moved["dy"] = far(p["dy"], p["dy_adm"][:, 0], p["dy_adm"][:, 1])
+    moved["h"] = far(p["h"], adm[:, 0, 0], adm[:, 0, 1])
+    moved["dgu"] = np.concatenate([far(p["dgu"][:, :f], adm[:, 1, 0], adm[:, 1, 1]),
+                                   far(p["dgu"][:, f:], adm[:, 2, 0], adm[:, 2, 1])], axis=1)
+    assert (moved["h"] != p["h"]).sum() > 100 and (moved["dgu"] != p["dgu"]).sum() > 100
+    wgu = oracle._as_f64(inp["w_gate_up"])
+    moved["dx"] = np.zeros_like(p["dx"])
+    for ee in range(s.E_l):
+        m = e == ee
+        moved["dx"][m] = oracle.round_bf16_array(moved["dgu"][m] @ wgu[ee], orc)
+    got = oracle.backward_reduce(s, inp, d_out, (t, j), e, moved, lib=orc)
+    sl = tolerance.backward_slack(p, e, inp["w_gate_up"], oracle._as_f64(inp["x"][t]), list(range(s.E_l)))
+    failed_without = 0
+    for k in ("dx_rows", "dw_down", "dw_gate_up"):
+        tolerance.check(got[k], ref[k], k, slack=sl[k])
+        try:
+            tolerance.check(got[k], ref[k], k)
+        except AssertionError:
+            failed_without += 1
+    assert failed_without > 0
+    i = np.unravel_index(np.argmax(sl["dw_down"]), sl["dw_down"].shape)
+    bad = got["dw_down"].copy()
+    bad[i] = ref["dw_down"][i] + 1.5 * (max(tolerance.RTOL * abs(ref["dw_down"][i]), tolerance.ATOL) + sl["dw_down"][i])
+    with pytest.raises(AssertionError):
+        tolerance.check(bad, ref["dw_down"], "planted", slack=sl["dw_down"])
+
+
 # ---- backward of the layer (orc_bwd_rows and oracle.backward) -----------------------------------------------------
 BWD_SPEC = mi.Spec("bwd_tiny", R=3, T_o=12, G=6, E_l=2, k=2, d=32, f=48, M=16, dtype="f32", seed=31)
 
