@@ -649,6 +649,8 @@ int moe_combine(const moe_shape* s, const moe_layout* L, const float* topk_w, vo
   p.T_o = s->tokens_per_owner;
   p.k = s->top_k;
   p.d = s->d;
+  p.E = s->num_local_experts;
+  p.G = s->num_global_experts;
   p.L = L;
   p.topk_w = topk_w;
   p.recv = recv;

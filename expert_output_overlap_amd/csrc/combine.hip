@@ -2,11 +2,15 @@
 // plan, is known before the return): out[r*T_o+t] = sum_j w[t,j] * recv[r][plan[t,j]] over the slots with a
 // local expert, fp32 accumulation in ascending j, rounded once to the element type.
 // One wavefront per token, 16-byte lanes along the hidden dimension, four 16-byte chunks of two slots per lane
-// in flight.
+// in flight.  The token index is wave-uniform, so its plan and weights come through scalar loads.  Every row is
+// read once and every output row written once: the launch streams one side past the caches (nontemporal), the
+// reads when the rows moved exceed the last-level cache, the stores otherwise (see launch_combine).
 #include "common.h"
 #include "launch.h"
 
 #define COMBINE_MAX_K 16
+
+typedef uint32_t cmb_u32x4 __attribute__((ext_vector_type(4)));
 
 struct CombineArgs {
   const float* w;
@@ -17,10 +21,10 @@ struct CombineArgs {
   int T, T_o, k, row_vec;
 };
 
-template <typename T>
+template <typename T, bool NT_LOAD, bool NT_STORE>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   constexpr int VEC = 16 / sizeof(T);
-  const int wave = threadIdx.x / MOE_WAVE, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / MOE_WAVE), lane = lane_id();
   const int tok = blockIdx.x * 4 + wave;
   // the status word and the token's plan and weights are independent loads: one round trip for all
   const int32_t st = load_status(a.status);
@@ -39,21 +43,26 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
     }
   }
   if (st != 0) return;
-  const uint4* src = (const uint4*)a.recv.p[r];
-  uint4* dst = (uint4*)a.out + (int64_t)tok * a.row_vec;
-  auto add = [&](float (&acc)[VEC], const uint4& v, float wj) {
+  const cmb_u32x4* src = (const cmb_u32x4*)a.recv.p[r];
+  cmb_u32x4* dst = (cmb_u32x4*)a.out + (int64_t)tok * a.row_vec;
+  auto ld = [&](int slot, int c) -> cmb_u32x4 {
+    if (c >= a.row_vec) return cmb_u32x4{0u, 0u, 0u, 0u};
+    const cmb_u32x4* q = src + (int64_t)p[slot] * a.row_vec + c;
+    return NT_LOAD ? __builtin_nontemporal_load(q) : *q;
+  };
+  auto add = [&](float (&acc)[VEC], const cmb_u32x4& v, float wj) {
     if (sizeof(T) == 2) {
-      const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+      const uint32_t q[4] = {v[0], v[1], v[2], v[3]};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc[2 * i] += wj * bf16_to_f32((bf16_t)(q[i] & 0xffffu));
         acc[2 * i + 1] += wj * bf16_to_f32((bf16_t)(q[i] >> 16));
       }
     } else {
-      acc[0] += wj * __uint_as_float(v.x);
-      acc[1] += wj * __uint_as_float(v.y);
-      acc[2] += wj * __uint_as_float(v.z);
-      acc[3] += wj * __uint_as_float(v.w);
+      acc[0] += wj * __uint_as_float(v[0]);
+      acc[1] += wj * __uint_as_float(v[1]);
+      acc[2] += wj * __uint_as_float(v[2]);
+      acc[3] += wj * __uint_as_float(v[3]);
     }
   };
   // U chunks of the row per lane, for two slots at a time: all their loads go out before any is used; the
@@ -67,12 +76,11 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
       for (int i = 0; i < VEC; ++i) acc[u][i] = 0.f;
     int j = 0;
     for (; j + 1 < nloc; j += 2) {
-      uint4 v0[U], v1[U];
+      cmb_u32x4 v0[U], v1[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int c = c0 + u * MOE_WAVE;
-        v0[u] = c < a.row_vec ? src[(int64_t)p[j] * a.row_vec + c] : make_uint4(0, 0, 0, 0);
-        v1[u] = c < a.row_vec ? src[(int64_t)p[j + 1] * a.row_vec + c] : make_uint4(0, 0, 0, 0);
+        v0[u] = ld(j, c0 + u * MOE_WAVE);
+        v1[u] = ld(j + 1, c0 + u * MOE_WAVE);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) add(acc[u], v0[u], w[j]);
@@ -80,12 +88,9 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
       for (int u = 0; u < U; ++u) add(acc[u], v1[u], w[j + 1]);
     }
     if (j < nloc) {
-      uint4 v0[U];
+      cmb_u32x4 v0[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = c0 + u * MOE_WAVE;
-        v0[u] = c < a.row_vec ? src[(int64_t)p[j] * a.row_vec + c] : make_uint4(0, 0, 0, 0);
-      }
+      for (int u = 0; u < U; ++u) v0[u] = ld(j, c0 + u * MOE_WAVE);
 #pragma unroll
       for (int u = 0; u < U; ++u) add(acc[u], v0[u], w[j]);
     }
@@ -93,19 +98,16 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
     for (int u = 0; u < U; ++u) {
       const int c = c0 + u * MOE_WAVE;
       if (c >= a.row_vec) break;
-      uint4 o;
+      cmb_u32x4 o;
       if (sizeof(T) == 2) {
-        o.x = pack_bf16x2(acc[u][0], acc[u][1]);
-        o.y = pack_bf16x2(acc[u][2], acc[u][3]);
-        o.z = pack_bf16x2(acc[u][4], acc[u][5]);
-        o.w = pack_bf16x2(acc[u][6], acc[u][7]);
+        o = cmb_u32x4{pack_bf16x2(acc[u][0], acc[u][1]), pack_bf16x2(acc[u][2], acc[u][3]),
+                      pack_bf16x2(acc[u][4], acc[u][5]), pack_bf16x2(acc[u][6], acc[u][7])};
       } else {
-        o.x = __float_as_uint(acc[u][0]);
-        o.y = __float_as_uint(acc[u][1]);
-        o.z = __float_as_uint(acc[u][2]);
-        o.w = __float_as_uint(acc[u][3]);
+        o = cmb_u32x4{__float_as_uint(acc[u][0]), __float_as_uint(acc[u][1]), __float_as_uint(acc[u][2]),
+                      __float_as_uint(acc[u][3])};
       }
-      dst[c] = o;
+      if (NT_STORE) __builtin_nontemporal_store(o, &dst[c]);
+      else dst[c] = o;
     }
   }
 }
@@ -124,7 +126,19 @@ int launch_combine(const CombineLaunch& p, hipStream_t st) {
   a.k = p.k;
   a.row_vec = p.d * (p.dtype == MOE_BF16 ? 2 : 4) / 16;
   const dim3 grid((T + 3) / 4);
-  if (p.dtype == MOE_BF16) hipLaunchKernelGGL(k_combine<bf16_t>, grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(k_combine<float>, grid, dim3(256), 0, st, a);
+  // The rows this combine moves, at the routing's expected share of local slots (T k E_l / G rows read, T
+  // written): past the 256 MB last-level cache, the row reads stream (DeepSeek-V3-like shard, ~470 MB: 123 -> 97
+  // us; streaming the stores as well, 111 us); below it the rows read are still in the cache that the return just
+  // wrote them through, and the stores stream instead (Mixtral-like, ~50 MB: 11 -> 8.7 us; skewed 19 -> 17 us;
+  // streaming the reads there cost 10-15%).
+  const double elem = p.dtype == MOE_BF16 ? 2.0 : 4.0;
+  const bool big = ((double)T * p.k * p.E / p.G + (double)T) * p.d * elem > 256.0 * 1024 * 1024;
+  if (p.dtype == MOE_BF16) {
+    if (big) hipLaunchKernelGGL((k_combine<bf16_t, true, false>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_combine<bf16_t, false, true>), grid, dim3(256), 0, st, a);
+  } else {
+    if (big) hipLaunchKernelGGL((k_combine<float, true, false>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_combine<float, false, true>), grid, dim3(256), 0, st, a);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -43,6 +43,7 @@ struct FfnLaunch {
 struct CombineLaunch {
   int dtype;
   int R, T_o, k, d;
+  int E, G;  // local and global experts (the expected share of local slots)
   const moe_layout* L;
   const float* topk_w;
   void* const* recv;
