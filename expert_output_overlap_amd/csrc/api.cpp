@@ -762,12 +762,14 @@ int moe_combine_backward(const moe_shape* s, const moe_layout* L, const void* d_
     if (!y_recv[r] || !dx_recv[r]) return fail(MOE_EINVAL, "null receive buffer");
   BwdLaunch p{};
   p.R = s->R;
+  p.E = s->num_local_experts;
   p.d = s->d;
   p.k = s->top_k;
   p.L = L;
   p.d_out = d_out;
   p.dx_recv = dx_recv;
-  if (launch_bwd_combine(p, s->tokens_per_owner, L->combine_plan, y_recv, dx, dw_route, (hipStream_t)stream))
+  if (launch_bwd_combine(p, s->tokens_per_owner, s->num_global_experts, L->combine_plan, y_recv, dx, dw_route,
+                         (hipStream_t)stream))
     return fail(MOE_EHIP, "combine backward launch failed");
   return MOE_OK;
 }

@@ -752,15 +752,19 @@ __global__ __launch_bounds__(256) void k_bwd_dy(const uint16_t* __restrict__ d_o
   }
 }
 
-// The combine's backward, one workgroup per token (owner r = t / T_o): dx[t] = bf16 of the fp32 sum of the token's
-// delivered dX rows (slot order), dw[t, j] = <dOut[t], y> over the forward's delivered row of slot j (fp32), 0 for a
-// slot routed elsewhere.
 // The combine's backward, one wave per token (out = sum_j w_j y_j over the token's local slots): dx = bf16 of the sum
 // of the slots' returned dX rows in ascending slot order, and the routing weights' gradient dw[t][j] = <dOut_t, y_j>
 // over the delivered forward row (0 for slots routed elsewhere).  16-byte loads, two chunks per lane at a time; the
 // dOut chunk is loaded once for all the token's slots, and each slot's dot product stays in a register until one
-// wave sum at the end.  (A workgroup per token with 2-byte loads and a barrier per slot ran at 1.9 TB/s.)
+// wave sum at the end.  (A workgroup per token with 2-byte loads and a barrier per slot ran at 1.9 TB/s.)  NT: every
+// row read streams past the caches (nontemporal), for row sets larger than the last-level cache.
 #define BWD_MAX_K 16
+__device__ __forceinline__ uint4 load16(const uint4* p, bool nt) {
+  if (!nt) return *p;
+  const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+template <bool NT>
 __global__ __launch_bounds__(256) void k_bwd_combine(const uint16_t* __restrict__ d_out, const int32_t* __restrict__ plan,
                                                      RecvPtrs y_recv, RecvPtrs dx_recv, int T, int T_o, int k, int d,
                                                      uint16_t* __restrict__ dx, float* __restrict__ dw) {
@@ -787,7 +791,7 @@ __global__ __launch_bounds__(256) void k_bwd_combine(const uint16_t* __restrict_
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = c0 + u * 64;
-      ov[u] = c < rv ? o[c] : make_uint4(0, 0, 0, 0);
+      ov[u] = c < rv ? load16(&o[c], NT) : make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[u][i] = 0.f;
     }
@@ -798,8 +802,8 @@ __global__ __launch_bounds__(256) void k_bwd_combine(const uint16_t* __restrict_
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int c = c0 + u * 64;
-        yv[u] = c < rv ? yb[(int64_t)pj[j] * rv + c] : make_uint4(0, 0, 0, 0);
-        xv[u] = c < rv ? xb[(int64_t)pj[j] * rv + c] : make_uint4(0, 0, 0, 0);
+        yv[u] = c < rv ? load16(&yb[(int64_t)pj[j] * rv + c], NT) : make_uint4(0, 0, 0, 0);
+        xv[u] = c < rv ? load16(&xb[(int64_t)pj[j] * rv + c], NT) : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -951,16 +955,25 @@ int launch_bwd_consumer(const BwdLaunch& p, int n_cons, hipStream_t st, hipEvent
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int launch_bwd_combine(const BwdLaunch& p, int T_o, const int32_t* plan, void* const* y_recv, void* dx, float* dw,
-                       hipStream_t st) {
+int launch_bwd_combine(const BwdLaunch& p, int T_o, int G, const int32_t* plan, void* const* y_recv, void* dx,
+                       float* dw, hipStream_t st) {
   RecvPtrs yr, xr;
   for (int r = 0; r < MOE_MAX_OWNERS; ++r) {
     yr.p[r] = r < p.R ? y_recv[r] : nullptr;
     xr.p[r] = r < p.R ? p.dx_recv[r] : nullptr;
   }
   const int64_t T = (int64_t)p.R * T_o;
-  if (T > 0)
-    hipLaunchKernelGGL(k_bwd_combine, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, (const uint16_t*)p.d_out, plan, yr,
-                       xr, (int)T, T_o, p.k, p.d, (uint16_t*)dx, dw);
+  // rows read and written at the routing's expected share of local slots (T k E_l / G): dOut, y and dX rows, dx.
+  // Past the 256 MB last-level cache the reads stream (DeepSeek-V3-like shard, ~0.9 GB: 253 -> 215 us)
+  const bool nt = (2.0 * T * p.k * p.E / G + 2.0 * T) * p.d * 2.0 > 256.0 * 1024 * 1024;
+  if (T > 0) {
+    const dim3 grid((unsigned)((T + 3) / 4));
+    if (nt)
+      hipLaunchKernelGGL(k_bwd_combine<true>, grid, dim3(256), 0, st, (const uint16_t*)p.d_out, plan, yr, xr, (int)T,
+                         T_o, p.k, p.d, (uint16_t*)dx, dw);
+    else
+      hipLaunchKernelGGL(k_bwd_combine<false>, grid, dim3(256), 0, st, (const uint16_t*)p.d_out, plan, yr, xr, (int)T,
+                         T_o, p.k, p.d, (uint16_t*)dx, dw);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -125,8 +125,9 @@ int launch_bwd_ffn(const BwdLaunch& p, int grid, int n_cons, int join, hipStream
 // The dX return alone (`n_cons` workgroups).
 int launch_bwd_consumer(const BwdLaunch& p, int n_cons, hipStream_t st, hipEvent_t ev0 = nullptr,
                         hipEvent_t ev1 = nullptr);
-// The combine's backward: dx (bf16 [T, d]) and the routing weights' gradient dw (fp32 [T, k]).
-int launch_bwd_combine(const BwdLaunch& p, int T_o, const int32_t* plan, void* const* y_recv, void* dx, float* dw,
-                       hipStream_t st);
+// The combine's backward: dx (bf16 [T, d]) and the routing weights' gradient dw (fp32 [T, k]); G global experts (with
+// p.E, the expected share of local slots, which sets the loads' cache policy).
+int launch_bwd_combine(const BwdLaunch& p, int T_o, int G, const int32_t* plan, void* const* y_recv, void* dx,
+                       float* dw, hipStream_t st);
 // A nonzero value distinct for every launch that opens a copy-unit counter.
 uint32_t next_stamp();
