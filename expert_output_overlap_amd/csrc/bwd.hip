@@ -190,7 +190,8 @@ struct BwdShared {
   int rows[BWD_BM];  // padded rows of the row tile
   int hdr[MOE_MT_HDR];
   int run_first, run_count, k_rows;  // W items: the expert's run of row tiles and its row count
-  int stop, claim;
+  int stop;
+  int next;  // W items: the tile the workgroup claimed during its current one
   // per local expert, built once by a workgroup before its first W item: rows, first row tile and tile count of its
   // run, and the experts by decreasing rows (the order W tiles are handed out in)
   int e_rows[MOE_MAX_LOCAL_EXPERTS], e_first[MOE_MAX_LOCAL_EXPERTS], e_count[MOE_MAX_LOCAL_EXPERTS];
@@ -572,7 +573,10 @@ __device__ __forceinline__ bool bwd_tile(const BwdArgs& a, unsigned char* smem, 
     publish(&a.fx[tile], a.epoch);
     return true;
   }
-  // W items: the fp32 tile into the weight gradient (read by nobody inside the launch)
+  // W items: the fp32 tile into the weight gradient (read by nobody inside the launch).  Thread 0 claims the
+  // workgroup's next tile first, so that the atomic's round trip overlaps these stores
+  int nxt = 0;
+  if (tid == 0) nxt = (int)(uint32_t)__hip_atomic_fetch_add(a.wclaim, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   float* out = KIND == BK_WD ? a.dw2 + (int64_t)e * d * f : a.dw1 + (int64_t)e * 2 * f * d;
   const int out_rows = KIND == BK_WD ? d : 2 * f, out_cols = KIND == BK_WD ? f : d;
 #pragma unroll
@@ -587,6 +591,7 @@ __device__ __forceinline__ bool bwd_tile(const BwdArgs& a, unsigned char* smem, 
         if (r < out_rows && col < out_cols) *(f32x4_t*)(out + (int64_t)r * out_cols + col) = v;
       }
     }
+  if (tid == 0) sh.next = nxt;
   return true;
 }
 
@@ -666,24 +671,28 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void k_bwd_ffn(BwdArgs a) {
       sh.e_order[rank] = tid;
     }
     const int n_w = a.E * bwd_w_per_expert(a);
-    for (;;) {
-      __syncthreads();  // the previous item is done with sh (and the table is complete)
-      if (tid == 0) {
-        const uint64_t t0 = moe_clock();
-        int w = -1;
-        bool stamped;
-        while (!(stamped = (uint32_t)(__hip_atomic_load(a.wclaim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 32) ==
-                           a.wstamp) &&
-               moe_clock() - t0 <= a.budget)
-          __builtin_amdgcn_s_sleep(1);
-        if (stamped)
-          w = (int)(uint32_t)__hip_atomic_fetch_add(a.wclaim, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        else
-          set_status(a.status, MOE_ETIMEOUT);
-        sh.claim = w;
+    // Each tile's thread 0 claims the workgroup's next tile before its epilogue's stores (bwd_tile), so the
+    // atomic's round trip overlaps them; the counter's stamp is looked at only before the first claim (DeepSeek-V3-
+    // and Mixtral-shaped and skewed backward 0.7-4% shorter).  Claiming a whole tile ahead held long tiles back
+    // from idle workgroups at the end (skewed 8-10% slower); one wait per expert for all of its G flags instead of
+    // one per tile for the columns it reads gained nothing.
+    if (tid == 0) {
+      const uint64_t t0 = moe_clock();
+      bool stamped;
+      while (!(stamped = (uint32_t)(__hip_atomic_load(a.wclaim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 32) ==
+                         a.wstamp) &&
+             moe_clock() - t0 <= a.budget)
+        __builtin_amdgcn_s_sleep(1);
+      if (stamped)
+        sh.next = (int)(uint32_t)__hip_atomic_fetch_add(a.wclaim, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else {
+        sh.next = -1;
+        set_status(a.status, MOE_ETIMEOUT);
       }
-      __syncthreads();
-      const int w = sh.claim;
+    }
+    for (;;) {
+      __syncthreads();  // the previous item is done with sh (and the table and the claim are complete)
+      const int w = sh.next;
       if (w < 0 || w >= n_w) break;
       const BwdItem it = bwd_w_item(a, sh, w);
       // the expert's run of row tiles (none: no rows, a zero tile); WD reads h columns jt*256 .., WGU (dG | dU)
