@@ -46,11 +46,12 @@ class moe_layout(ctypes.Structure):
 class moe_overlap_cfg(ctypes.Structure):
     _fields_ = [("consumer_cus", ctypes.c_int32), ("mode", ctypes.c_int32), ("epoch", ctypes.c_uint32),
                 ("band_window", ctypes.c_int32), ("watchdog_ticks", ctypes.c_uint64),
-                ("timestamps", ctypes.c_void_p), ("tile_order", ctypes.c_int32), ("x_tokens", ctypes.c_void_p)]
+                ("timestamps", ctypes.c_void_p), ("tile_order", ctypes.c_int32), ("x_tokens", ctypes.c_void_p),
+                ("gu_out", ctypes.c_void_p)]
 
 
 BWD_FIELDS = ["topk_idx", "topk_w", "x_pad", "w_gate_up", "w_down", "d_out", "dy_pad", "dh_ws", "h_ws", "dgu_ws",
-              "dx_pad", "dx_recv", "dw_gate_up", "dw_down"]
+              "dx_pad", "dx_recv", "dw_gate_up", "dw_down", "gu"]
 
 
 class moe_bwd_args(ctypes.Structure):
@@ -228,10 +229,10 @@ def moe_bwd_flags_count(shape: moe_shape) -> int:
 
 def moe_expert_ffn_backward(shape: moe_shape, layout: moe_layout, tensors: dict, dx_recv, flags, cfg: moe_overlap_cfg,
                             stream=None) -> int:
-    """tensors: the moe_bwd_args fields other than dx_recv, as device tensors."""
+    """tensors: the moe_bwd_args fields other than dx_recv, as device tensors ("gu" optional)."""
     ptrs = _ptr_array(dx_recv)
-    a = moe_bwd_args(**{k: (ctypes.cast(ptrs, ctypes.c_void_p) if k == "dx_recv" else _ptr(tensors[k]))
-                        for k in BWD_FIELDS})
+    a = moe_bwd_args(**{k: (ctypes.cast(ptrs, ctypes.c_void_p) if k == "dx_recv" else
+                            _ptr(tensors.get(k) if k == "gu" else tensors[k])) for k in BWD_FIELDS})
     return _check("moe_expert_ffn_backward", lib().moe_expert_ffn_backward(
         ctypes.byref(shape), ctypes.byref(layout), ctypes.byref(a), _ptr(flags), ctypes.byref(cfg), _stream(stream)))
 

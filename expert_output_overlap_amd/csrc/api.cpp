@@ -452,6 +452,8 @@ int ffn_overlap(const moe_shape* s, const moe_layout* L, const void* x_pad, cons
   if (cfg->tile_order != 0 && cfg->tile_order != 1) return fail(MOE_EINVAL, "tile_order must be 0 or 1");
   if (cfg->x_tokens && (s->dtype != MOE_BF16 || (cfg->mode != 0 && cfg->mode != 1)))
     return fail(MOE_EINVAL, "x_tokens (rows landed by the launch) is for bf16 in mode 0 or 1");
+  if (cfg->gu_out && (s->dtype != MOE_BF16 || cfg->mode == 2))
+    return fail(MOE_EINVAL, "gu_out (the first GEMM's pre-activations) is for bf16 in mode 0, 1 or 3");
   hipStream_t st = (hipStream_t)stream;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(MOE_EHIP, "hipGetDevice failed");
@@ -497,6 +499,7 @@ int ffn_overlap(const moe_shape* s, const moe_layout* L, const void* x_pad, cons
   p.band_window = cfg->band_window;
   p.tile_order = cfg->tile_order;
   p.x_tokens = cfg->x_tokens;
+  p.gu_out = cfg->gu_out;
   p.join = cfg->mode == 0 && s->dtype == MOE_BF16;
   p.watchdog_ticks = cfg->watchdog_ticks ? cfg->watchdog_ticks : 200000000ull;
   p.timestamps = cfg->timestamps;
@@ -682,7 +685,7 @@ int moe_expert_ffn_backward(const moe_shape* s, const moe_layout* L, const moe_b
   if ((uintptr_t)flags % 8 != 0) return fail(MOE_EINVAL, "flags must be 8-byte aligned");
   if (cfg->epoch == 0) return fail(MOE_EINVAL, "epoch must be nonzero");
   if (cfg->mode != 0 && cfg->mode != 1) return fail(MOE_EINVAL, "the backward pass runs in mode 0 or 1");
-  if (cfg->x_tokens) return fail(MOE_EINVAL, "x_tokens is for the forward call");
+  if (cfg->x_tokens || cfg->gu_out) return fail(MOE_EINVAL, "x_tokens and gu_out are for the forward call");
   hipStream_t st = (hipStream_t)stream;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(MOE_EHIP, "hipGetDevice failed");
@@ -715,6 +718,7 @@ int moe_expert_ffn_backward(const moe_shape* s, const moe_layout* L, const moe_b
   p.dh_ws = b->dh_ws;
   p.h_ws = b->h_ws;
   p.dgu_ws = b->dgu_ws;
+  p.gu = b->gu;
   p.dx_pad = b->dx_pad;
   p.dx_recv = b->dx_recv;
   p.dw_gate_up = b->dw_gate_up;

@@ -53,6 +53,7 @@ struct BwdArgs {
   float* dh;                 // [cap_rows, f]
   unsigned char* h;          // [cap_rows, f] bf16
   unsigned char* dgu;        // [cap_rows, 2f] bf16: dG | dU
+  const float* gu;           // null, or [cap_rows, 2f] fp32: g | u as the forward stored them (G items skip the GEMM)
   unsigned char* dxp;        // dX rows of the other owners [cap_rows, d]
   unsigned char* self_recv;  // the self owner's dX buffer
   float* dw1;                // [E, 2f, d]
@@ -77,36 +78,6 @@ struct BwdArgs {
   int join;    // producers take copy units once their items are done
   ConsumerArgs cons;
 };
-
-// 8-byte stores with the device-scope cache policy (data other workgroups read inside the launch; the s_nop as in
-// store16_coherent)
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void store8_coherent(void* p, u32x2_t v) {
-  asm volatile("global_store_dwordx2 %0, %1, off sc1\n\ts_nop 1" ::"v"(p), "v"(v) : "memory");
-}
-
-// 4 x 4 transpose inside each quad of lanes (DPP quad permutations; every lane of the quad takes part): lane p's
-// v[r] becomes lane r's v[p].  Two exchange steps, with lane p ^ 1 for the registers whose bit 0 differs from p's,
-// then with lane p ^ 2 for bit 1.
-template <int CTRL>
-__device__ __forceinline__ float quad_perm(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
-}
-__device__ __forceinline__ f32x4_t quad_transpose(f32x4_t v, int lane) {
-  constexpr int X1 = 0xB1, X2 = 0x4E;  // quad_perm [1,0,3,2] and [2,3,0,1]
-  const bool o1 = lane & 1, o2 = lane & 2;
-  float t0 = quad_perm<X1>(v[1]), t1 = quad_perm<X1>(v[0]), t2 = quad_perm<X1>(v[3]), t3 = quad_perm<X1>(v[2]);
-  v = f32x4_t{o1 ? t0 : v[0], o1 ? v[1] : t1, o1 ? t2 : v[2], o1 ? v[3] : t3};
-  t0 = quad_perm<X2>(v[2]);
-  t1 = quad_perm<X2>(v[3]);
-  t2 = quad_perm<X2>(v[0]);
-  t3 = quad_perm<X2>(v[1]);
-  return f32x4_t{o2 ? t0 : v[0], o2 ? t1 : v[1], o2 ? v[2] : t2, o2 ? v[3] : t3};
-}
-
-__device__ __forceinline__ uint32_t bf16_bits(float v) {  // round to nearest even
-  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v);
-}
 
 // Column-staged tiles (64 k-rows x 256 columns, 512 bytes per row): the 32-byte granule g (16 columns) of k-row r
 // sits at granule col_swz(g, r) of the row.  A transposed fragment read has lanes 0-15 and 16-31 on columns 16
@@ -235,7 +206,8 @@ __device__ __forceinline__ bool bwd_tile(const BwdArgs& a, unsigned char* smem, 
   // columns (K = the expert's rows).  B: H Wd by columns (k = d index, columns of f); G Wgu rows (gate | up);
   // X Wgu by columns (k = 2f index, columns of d); WD h by columns; WGU x by columns.
   int K, k0 = 0;
-  if (KIND == BK_H || KIND == BK_G) K = d;
+  if (KIND == BK_H) K = d;
+  else if (KIND == BK_G) K = a.gu != nullptr ? 0 : d;  // with g | u from the forward, no GEMM
   else if (KIND == BK_X) {
     K = 2 * f / a.S;
     k0 = it.s * K;
@@ -486,14 +458,25 @@ __device__ __forceinline__ bool bwd_tile(const BwdArgs& a, unsigned char* smem, 
     }
     flag_acquire();
     const int col = it.nt * 128 + wn * 32 + col_t;
+    const bool saved = a.gu != nullptr;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4_t g4 = quad(acc[mi][0], q4), u4 = quad(acc[mi][1], q4);
+        // g and u of row r at columns col ..: the accumulators, transposed, or the forward's stored values (the
+        // same bits: the same k-tiles in the same order)
+        f32x4_t g4, u4;
+        if (!saved) {
+          g4 = quad(acc[mi][0], q4);
+          u4 = quad(acc[mi][1], q4);
+        }
         const int r = row_t(mi, q4);
         if (r >= n_rows) continue;
         const int64_t p = sh.rows[r];
+        if (saved) {
+          g4 = *(const f32x4_t*)(a.gu + p * 2 * f + col);
+          u4 = *(const f32x4_t*)(a.gu + p * 2 * f + f + col);
+        }
         const f32x4_t dh = *(const f32x4_t*)(a.dh + p * f + col);
         float hv[4], dg[4], du[4];
 #pragma unroll
@@ -918,6 +901,7 @@ int launch_bwd_ffn(const BwdLaunch& p, int grid, int n_cons, int join, hipStream
   a.dh = p.dh_ws;
   a.h = (unsigned char*)p.h_ws;
   a.dgu = (unsigned char*)p.dgu_ws;
+  a.gu = p.gu;
   a.dxp = (unsigned char*)p.dx_pad;
   a.self_recv = (unsigned char*)p.dx_recv[p.self_rank];
   a.dw1 = p.dw_gate_up;

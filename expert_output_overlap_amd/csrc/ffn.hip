@@ -339,6 +339,7 @@ struct FusedArgs {
   uint32_t* obs;   // the partition record (MOE_OBS_WORDS words, see obs_*), or null
   // dispatch landing inside the launch (xtok non-null): the token rows of x_pad are copied here, row tile by row tile
   const unsigned char* xtok;  // token rows X [T, d]
+  float* gu;                  // null, or [cap_rows, 2f] fp32: the first GEMM's items store g | u of their rows here
   const int32_t* row_src;     // padded row -> token row
   uint32_t* flags0;           // [cap_mtiles]: the row tile's input rows have landed
   uint64_t* gcount;           // [cap_mtiles]: landed units of the row tile (epoch << 32 | count)
@@ -670,6 +671,32 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
   int tid_e = tid;
   asm volatile("" : "+v"(tid_e));
   const int lane_e = tid_e & 63;
+  if constexpr (GLU) {
+    if (a.gu != nullptr) {
+      // the pre-activations g | u of the real rows, fp32, for a backward call that takes them instead of
+      // recomputing this GEMM: each group of four accumulator rows q4 is transposed inside its quad of lanes, after
+      // which lane l holds row 8 q4 + 4 (l / 32) + l % 4 of the block at the four consecutive columns from
+      // 4 ((l % 32) / 4), so one wave store writes eight rows of 128 bytes
+      const int64_t ld = 2 * (int64_t)a.f;
+      const int col = nt * (BN / 2) + wn * 32 + 4 * ((lane_e & 31) >> 2);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x16_t& g = acc[mi][0];
+          const f32x16_t& u = acc[mi][1];
+          const f32x4_t gq = quad_transpose(f32x4_t{g[4 * q4], g[4 * q4 + 1], g[4 * q4 + 2], g[4 * q4 + 3]}, lane_e);
+          const f32x4_t uq = quad_transpose(f32x4_t{u[4 * q4], u[4 * q4 + 1], u[4 * q4 + 2], u[4 * q4 + 3]}, lane_e);
+          const int r = wm * WM + mi * 32 + 8 * q4 + 4 * (lane_e >> 5) + (lane_e & 3);
+          if (r < n_rows) {
+            float* row = a.gu + (int64_t)s_rows[r] * ld;
+            *(f32x4_t*)(row + col) = gq;
+            *(f32x4_t*)(row + a.f + col) = uq;
+          }
+          __builtin_amdgcn_sched_barrier(0);  // one row group at a time
+        }
+    }
+  }
   auto stage = [&](int mi, int ni, const f32x16_t& v, const f32x16_t& up) {  // one 32 x 32 block into LDS
     const int col = (GLU ? wn * 32 : wn * 64 + ni * 32) + (lane_e & 31);
 #pragma unroll
@@ -1144,6 +1171,7 @@ int launch_bf16(const FfnLaunch& p, int grid, int n_cons, hipStream_t st, hipEve
   a.E = p.E;
   a.obs = p.item_end >= 0 ? nullptr : p.flags + fc.obs;  // a chunk of the list observes no whole-call rate
   a.xtok = (const unsigned char*)p.x_tokens;
+  a.gu = p.gu_out;
   a.row_src = p.L->row_src;
   a.flags0 = p.flags + fc.flags0;
   a.gcount = (uint64_t*)(p.flags + fc.gcount);

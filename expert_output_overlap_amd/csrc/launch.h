@@ -33,6 +33,7 @@ struct FfnLaunch {
   int tile_order;  // 0: remote first (the layout's mt_order), 1: row-tile numbering
   int join = 0;  // bf16: the producer launch runs the return too (overlapped mode)
   const void* x_tokens = nullptr;  // bf16: token rows; non-null: the launch lands x_pad's rows itself
+  float* gu_out = nullptr;         // bf16: non-null: the first GEMM's items also store g | u (fp32) of their rows
   int item_begin = 0, item_end = -1;  // bf16: run list indices [item_begin, item_end) only (GEMM1 first, no
                                       // half-width round); item_end < 0: the whole list
   uint64_t watchdog_ticks;
@@ -105,6 +106,7 @@ struct BwdLaunch {
   float* dh_ws;
   void* h_ws;
   void* dgu_ws;
+  const float* gu = nullptr;  // g | u stored by the forward (null: recomputed)
   void* dx_pad;
   void* const* dx_recv;
   float* dw_gate_up;

@@ -1,5 +1,6 @@
 // Device helpers shared by the forward and backward FFN launches: operand vector types, the LDS DMA load, stores
-// with the device-scope cache policy, the tile publish and arrival counters, SiLU.
+// with the device-scope cache policy, the quad transpose of MFMA accumulators, the tile publish and arrival
+// counters, SiLU.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -31,6 +32,37 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t l
 
 // this wave's loads have landed in LDS, then the workgroup barrier: after it every wave's have
 __device__ __forceinline__ void wait_loads_barrier() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// 8-byte stores with the device-scope cache policy (data other workgroups read inside the launch; the s_nop as in
+// store16_coherent below)
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store8_coherent(void* p, u32x2_t v) {
+  asm volatile("global_store_dwordx2 %0, %1, off sc1\n\ts_nop 1" ::"v"(p), "v"(v) : "memory");
+}
+
+// 4 x 4 transpose inside each quad of lanes (DPP quad permutations; every lane of the quad takes part): lane p's
+// v[r] becomes lane r's v[p].  Two exchange steps, with lane p ^ 1 for the registers whose bit 0 differs from p's,
+// then with lane p ^ 2 for bit 1.  In an MFMA 32 x 32 accumulator a lane holds four consecutive rows of one column
+// in each group of four registers; after the transpose it holds one row at four consecutive columns.
+template <int CTRL>
+__device__ __forceinline__ float quad_perm(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ f32x4_t quad_transpose(f32x4_t v, int lane) {
+  constexpr int X1 = 0xB1, X2 = 0x4E;  // quad_perm [1,0,3,2] and [2,3,0,1]
+  const bool o1 = lane & 1, o2 = lane & 2;
+  float t0 = quad_perm<X1>(v[1]), t1 = quad_perm<X1>(v[0]), t2 = quad_perm<X1>(v[3]), t3 = quad_perm<X1>(v[2]);
+  v = f32x4_t{o1 ? t0 : v[0], o1 ? v[1] : t1, o1 ? t2 : v[2], o1 ? v[3] : t3};
+  t0 = quad_perm<X2>(v[2]);
+  t1 = quad_perm<X2>(v[3]);
+  t2 = quad_perm<X2>(v[0]);
+  t3 = quad_perm<X2>(v[1]);
+  return f32x4_t{o2 ? t0 : v[0], o2 ? t1 : v[1], o2 ? v[2] : t2, o2 ? v[3] : t3};
+}
+
+__device__ __forceinline__ uint32_t bf16_bits(float v) {  // round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v);
+}
 
 // SiLU with the hardware reciprocal (about 1 ulp), rounded to bf16 right after
 __device__ __forceinline__ float silu_fast(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }

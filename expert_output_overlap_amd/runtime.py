@@ -72,13 +72,17 @@ class MoePath:
         B.moe_layout_build(self.shape, self.topk_idx if topk_idx is None else topk_idx, x, self.L, self.x_pad, stream)
 
     def ffn(self, w_gate_up, w_down, mode=0, consumer_cus=0, band_window=0, timestamps=False, watchdog_ticks=0,
-            epoch=None, tile_order=0, x_tokens: torch.Tensor | None = None, stream=None):
+            epoch=None, tile_order=0, x_tokens: torch.Tensor | None = None, gu_out: torch.Tensor | None = None,
+            stream=None):
+        """gu_out: None, or [cap_rows, 2f] fp32 (gu_buffer()) for the first GEMM's pre-activations g | u, which a
+        backward call can take instead of recomputing them."""
         if epoch is None:
             self.epoch += 1
             epoch = self.epoch
         cfg = B.moe_overlap_cfg(consumer_cus, mode, epoch, band_window, watchdog_ticks,
                                 self.timestamps.data_ptr() if timestamps else None, tile_order,
-                                None if x_tokens is None else x_tokens.data_ptr())
+                                None if x_tokens is None else x_tokens.data_ptr(),
+                                None if gu_out is None else gu_out.data_ptr())
         B.moe_expert_ffn_overlap(self.shape, self.L, self.x_pad, w_gate_up, w_down, self.h, self.y_pad, self.recv,
                                  self.flags, cfg, stream)
         return epoch
@@ -106,19 +110,25 @@ class MoePath:
             self.bwd_epoch = 0
         return self._bwd
 
+    def gu_buffer(self):
+        """[cap_rows, 2f] fp32 for the forward's g | u (ffn(gu_out=...), backward(gu=...)), allocated on first use."""
+        if getattr(self, "_gu", None) is None:
+            self._gu = torch.empty(self.L.cap_rows, 2 * self.f, dtype=torch.float32, device=self.device)
+        return self._gu
+
     def backward(self, d_out: torch.Tensor, w_gate_up, w_down, mode=0, consumer_cus=0, watchdog_ticks=0, epoch=None,
-                 stream=None):
+                 gu: torch.Tensor | None = None, stream=None):
         """The expert FFN's backward with the dX return (moe_expert_ffn_backward), for the routing, layout and x_pad
-        of the last forward; the forward's h workspace receives the recomputed h."""
+        of the last forward; the forward's h workspace receives the recomputed h.  gu: None, or the g | u that forward
+        stored (ffn(gu_out=...)), which the h / dG / dU items then read instead of recomputing the first GEMM."""
         b = self.bwd_buffers()
         if epoch is None:
             self.bwd_epoch += 1
             epoch = self.bwd_epoch
         cfg = B.moe_overlap_cfg(consumer_cus, mode, epoch, 0, watchdog_ticks, None, 0, None)
         t = {"topk_idx": self.topk_idx, "topk_w": self.topk_w, "x_pad": self.x_pad, "w_gate_up": w_gate_up,
-             "w_down": w_down, "d_out": d_out, "h_ws": self.h, **{k: b[k] for k in
-                                                                   ("dy_pad", "dh_ws", "dgu_ws", "dx_pad",
-                                                                    "dw_gate_up", "dw_down")}}
+             "w_down": w_down, "d_out": d_out, "h_ws": self.h, "gu": gu,
+             **{k: b[k] for k in ("dy_pad", "dh_ws", "dgu_ws", "dx_pad", "dw_gate_up", "dw_down")}}
         B.moe_expert_ffn_backward(self.shape, self.L, t, b["dx_recv"], b["flags"], cfg, stream)
         return epoch
 

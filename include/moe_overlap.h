@@ -137,6 +137,11 @@ typedef struct {
                               first GEMM needs them, each row tile's first-GEMM items waiting for that tile's rows
                               (review page, "Where Pith is reading between the lines": the dispatch side of the same
                               tile signalling).  For a layout built with x == NULL; NULL: x_pad already holds them */
+  float* gu_out;           /* optional (device) [cap_rows, 2f] fp32 (bf16, modes 0, 1 and 3): the first GEMM's
+                              pre-activations of every real row at its padded row, g = x Wg^T in columns [0, f) and
+                              u = x Wu^T in [f, 2f), as the fp32 accumulators hold them, for a backward call that takes
+                              them (moe_bwd_args.gu) instead of recomputing that GEMM; rows of no real row are not
+                              written.  NULL: not stored */
 } moe_overlap_cfg;
 
 /* Last host-side error message of the calling thread ("" if none). */
@@ -315,6 +320,10 @@ typedef struct {
                               the forward delivered their y (recv_off layout) */
   float* dw_gate_up;       /* (device) [E_l, 2f, d] fp32 weight gradient, written (not accumulated) */
   float* dw_down;          /* (device) [E_l, d, f] fp32 weight gradient, written */
+  const float* gu;         /* optional (device) [cap_rows, 2f] fp32: g | u as the forward call of this layout and these
+                              weights stored them (moe_overlap_cfg.gu_out); the h / dG / dU items then read them
+                              instead of recomputing the first GEMM, with the same bits (the forward's first GEMM
+                              and the recompute run the same k-tiles in the same order).  NULL: recompute */
 } moe_bwd_args;
 
 /* Size, in 4-byte words, of the backward call's flag buffer (dX tile flags first, then dH and h flags, the k-split

@@ -166,6 +166,64 @@ def test_backward_parity(s, self_rank):
             np.testing.assert_array_equal(bits(b2["dx_recv"][q]), ref_recv[q], err_msg="dx_recv %d %s" % (q, kw))
 
 
+GU_CASES = BWD_SMALL[1:4] + [mi.spec("deepseek"), mi.spec("mixtral")]
+
+
+def same_bits(a, b):
+    return bool(torch.equal(a.contiguous().view(torch.int16 if a.element_size() == 2 else torch.int32),
+                            b.contiguous().view(torch.int16 if b.element_size() == 2 else torch.int32)))
+
+
+@pytest.mark.parametrize("s", GU_CASES, ids=lambda v: v.name)
+def test_backward_with_the_forwards_preactivations(s):
+    """The forward storing g | u (moe_overlap_cfg.gu_out) and the backward taking them (moe_bwd_args.gu): the
+    forward's own outputs keep their bits; the stored rows are every real row's, and nothing else is written; and h,
+    dG | dU, the returned dX rows, both weight gradients, dx and the routing weights' gradient are the same bits as
+    the recomputing call's (whose values test_backward_parity and test_backward_full_size check against the oracle),
+    overlapped and sequential.  Then the calls that would misuse them are rejected."""
+    run = BwdRun(s)
+    P = run.P
+    t, j, e, r, p = run.rows_of(np.ones((s.T, s.k), bool))
+    pd = torch.as_tensor(p, device=P.h.device)
+    b = run.backward(mode=0)
+    ref = {k: b[k].clone() for k in ("dw_gate_up", "dw_down", "dx", "dw_route")}
+    ref["h"], ref["dgu"] = P.h[pd].clone(), b["dgu_ws"][pd].clone()
+    ref_recv = [x.clone() for x in b["dx_recv"]]
+    y_ref, out_ref = [x.clone() for x in P.recv], P.out.clone()
+    gu = P.gu_buffer()
+    gu.fill_(float("nan"))
+    P.ffn(run.dev["w_gate_up"], run.dev["w_down"], mode=0, gu_out=gu)
+    P.combine()
+    torch.cuda.synchronize()
+    assert P.status() == B.MOE_OK
+    assert all(same_bits(a, b_) for a, b_ in zip(P.recv, y_ref)) and same_bits(P.out, out_ref), \
+        "storing g | u changed the forward's outputs"
+    real = torch.zeros(gu.shape[0], dtype=torch.bool, device=gu.device)
+    real[pd] = True
+    assert not torch.isnan(gu[real]).any(), "a real row's g | u was not stored"
+    assert torch.isnan(gu[~real]).all(), "g | u stored past the real rows"
+    for kw in (dict(mode=0), dict(mode=1)):
+        b2 = run.backward(gu=gu, **kw)
+        got = {k: b2[k] for k in ("dw_gate_up", "dw_down", "dx", "dw_route")}
+        got["h"], got["dgu"] = P.h[pd], b2["dgu_ws"][pd]
+        for k, v in ref.items():
+            assert same_bits(got[k], v), "%s differs from the recomputing call's (%s)" % (k, kw)
+        for q in range(s.R):
+            assert same_bits(b2["dx_recv"][q], ref_recv[q]), "dx_recv %d differs (%s)" % (q, kw)
+    # misuse: g | u stored by a return-only call, or passed to the backward's cfg
+    cfg = B.moe_overlap_cfg(8, 2, 99, 0, 0, None, 0, None, gu.data_ptr())
+    with pytest.raises(B.MoeError):
+        B.moe_expert_ffn_overlap(P.shape, P.L, P.x_pad, run.dev["w_gate_up"], run.dev["w_down"], P.h, P.y_pad,
+                                 P.recv, P.flags, cfg)
+    bb = P.bwd_buffers()
+    cfg = B.moe_overlap_cfg(0, 0, 99, 0, 0, None, 0, None, gu.data_ptr())
+    tens = {"topk_idx": P.topk_idx, "topk_w": P.topk_w, "x_pad": P.x_pad, "w_gate_up": run.dev["w_gate_up"],
+            "w_down": run.dev["w_down"], "d_out": run.d_out, "h_ws": P.h,
+            **{k: bb[k] for k in ("dy_pad", "dh_ws", "dgu_ws", "dx_pad", "dw_gate_up", "dw_down")}}
+    with pytest.raises(B.MoeError):
+        B.moe_expert_ffn_backward(P.shape, P.L, tens, bb["dx_recv"], bb["flags"], cfg)
+
+
 def test_backward_repeats_and_rejects_bad_calls():
     """Repeated calls on the same flag buffer (new epochs) give the same bits; fp32 shapes, f not a multiple of 128
     and a spin budget that ends every wait are reported."""
