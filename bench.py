@@ -195,12 +195,14 @@ def cpu_baseline(s, inp, target_s: float):
             "one_thread": one, "backward_rows": bwd}
 
 
-def bench_backward(P, s, w1, w2, reps: int, M_real: int) -> dict:
+def bench_backward(P, s, w1, w2, reps: int, M_real: int, ffn_call) -> dict:
     """The backward pass for the last forward's routing and layout: dY dispatch, the persistent launch (dH, h / dG /
     dU, dX with its return to the owners, the weight gradients) and the combine's backward, as one call; overlapped
     (consumer workgroups return dX rows while the weight gradients run) and sequential (the return after the launch).
     Flops: 12 M d f for the gradients (dH 2, dX 4, dW_down 2, dW_gate_up 4), 16 M d f with the launch's recompute of
-    the gate and up projections."""
+    the gate and up projections.  Then the same with the gate and up pre-activations stored by the forward
+    (ffn_call(gu_out), the step's FFN call) instead of recomputed: that forward call's time with and without storing
+    them, the backward taking them, and the two forward + backward sums."""
     import torch
 
     import moe_inputs as mi
@@ -210,8 +212,10 @@ def bench_backward(P, s, w1, w2, reps: int, M_real: int) -> dict:
     d_out = to_device(mi.d_out(s), s.dtype)
     P.bwd_buffers()
 
+    gu = None
+
     def call(mode):
-        P.backward(d_out, w1, w2, mode=mode)
+        P.backward(d_out, w1, w2, mode=mode, gu=gu)
         P.combine_backward(d_out)
 
     for _ in range(3):
@@ -240,6 +244,32 @@ def bench_backward(P, s, w1, w2, reps: int, M_real: int) -> dict:
     grads = 12.0 * M_real * s.d * s.f
     executed = 16.0 * M_real * s.d * s.f
     ret_bytes = 2.0 * (M_real - int(P.scalars()["N_r"][P.shape.self_rank])) * s.d * 2
+
+    def time_fwd(g):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ffn_call(g)
+        ts = []
+        for _ in range(reps):
+            ev0.record()
+            ffn_call(g)
+            ev1.record()
+            ev1.synchronize()
+            ts.append(ev0.elapsed_time(ev1))
+        assert P.status() == B.MOE_OK
+        return float(np.median(ts))
+
+    f_plain = time_fwd(None)
+    gu = P.gu_buffer()
+    f_gu = time_fwd(gu)  # leaves this routing's g | u in gu for the calls below
+    t_gu, k_gu, _ = timed(0)
+    saved = {
+        "ms": round(t_gu, 4), "launch_ms": round(k_gu, 4),
+        "tflops_gradients": round(grads / (t_gu * 1e-3) / 1e12, 2),
+        "launch_tflops_executed": round(grads / (k_gu * 1e-3) / 1e12, 2),
+        "forward_ffn_ms": round(f_plain, 4), "forward_ffn_ms_storing": round(f_gu, 4),
+        "forward_plus_backward_ms_recompute": round(f_plain + t_ovl, 4),
+        "forward_plus_backward_ms_stored": round(f_gu + t_gu, 4),
+    }
     return {
         "ms": round(t_ovl, 4), "ms_sequential": round(t_seq, 4),
         "saved_vs_sequential_us": round(1e3 * (t_seq - t_ovl), 1),
@@ -250,6 +280,7 @@ def bench_backward(P, s, w1, w2, reps: int, M_real: int) -> dict:
         "launch_tflops_executed": round(executed / (k_ovl * 1e-3) / 1e12, 2),
         "launch_pct_bf16_peak_executed": round(100 * executed / (k_ovl * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 2),
         "return_gbs_sequential": round(ret_bytes / (c_seq * 1e-3) / 1e9, 1),
+        "with_stored_preactivations": saved,
     }
 
 
@@ -454,7 +485,10 @@ def main():
                      "traffic_unit": "HBM bytes per launch"},
     }
     if args.backward and s.dtype == "bf16":
-        res["backward"] = bench_backward(P, s, w1, w2, reps, M_real)
+        res["backward"] = bench_backward(
+            P, s, w1, w2, reps, M_real,
+            lambda g: P.ffn(w1, w2, mode=0, consumer_cus=cus, band_window=args.band_window,
+                            x_tokens=dev["x"] if land else None, gu_out=g))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(s, inp, args.cpu_seconds)
     print(json.dumps(res))

@@ -2,7 +2,8 @@
 // signalling applied to MoE training's backward pass, which has the same GEMM-then-transfer structure).  Given the
 // gradient of the combined output, per routed row p of token t, slot weight w and local expert e:
 //   dY = bf16(w dOut[t])                                   (k_bwd_dy: the gradient's dispatch into the padded layout)
-//   dH = dY Wd,  g = x Wg^T,  u = x Wu^T                   (recomputed, as the forward computes them)
+//   dH = dY Wd,  g = x Wg^T,  u = x Wu^T                   (recomputed as the forward computes them, or read from
+//                                                           the forward's stored copy: the same bits)
 //   h = bf16(silu(g) u),  dU = bf16(dH silu(g)),  dG = bf16(dH u silu'(g))
 //   dX = (dG | dU) (Wg | Wu)                                (rows returned to their owners: the overlapped transfer)
 //   dWd[e] = sum_p dY^T h,  dWgu[e] = sum_p (dG | dU)^T x   (fp32, over the expert's rows)
