@@ -452,8 +452,9 @@ int ffn_overlap(const moe_shape* s, const moe_layout* L, const void* x_pad, cons
   if (cfg->tile_order != 0 && cfg->tile_order != 1) return fail(MOE_EINVAL, "tile_order must be 0 or 1");
   if (cfg->x_tokens && (s->dtype != MOE_BF16 || (cfg->mode != 0 && cfg->mode != 1)))
     return fail(MOE_EINVAL, "x_tokens (rows landed by the launch) is for bf16 in mode 0 or 1");
-  if (cfg->gu_out && (s->dtype != MOE_BF16 || cfg->mode == 2))
-    return fail(MOE_EINVAL, "gu_out (the first GEMM's pre-activations) is for bf16 in mode 0, 1 or 3");
+  if (cfg->gu_out && (s->dtype != MOE_BF16 || cfg->mode == 2 || s->f % 128))
+    return fail(MOE_EINVAL, "gu_out (the first GEMM's pre-activations, for the backward) is for bf16 shapes with f a "
+                            "multiple of 128, in mode 0, 1 or 3");
   hipStream_t st = (hipStream_t)stream;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(MOE_EHIP, "hipGetDevice failed");

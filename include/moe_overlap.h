@@ -137,11 +137,11 @@ typedef struct {
                               first GEMM needs them, each row tile's first-GEMM items waiting for that tile's rows
                               (review page, "Where Pith is reading between the lines": the dispatch side of the same
                               tile signalling).  For a layout built with x == NULL; NULL: x_pad already holds them */
-  float* gu_out;           /* optional (device) [cap_rows, 2f] fp32 (bf16, modes 0, 1 and 3): the first GEMM's
-                              pre-activations of every real row at its padded row, g = x Wg^T in columns [0, f) and
-                              u = x Wu^T in [f, 2f), as the fp32 accumulators hold them, for a backward call that takes
-                              them (moe_bwd_args.gu) instead of recomputing that GEMM; rows of no real row are not
-                              written.  NULL: not stored */
+  float* gu_out;           /* optional (device) [cap_rows, 2f] fp32 (bf16 with f a multiple of 128, as the backward
+                              needs; modes 0, 1 and 3): the first GEMM's pre-activations of every real row at its
+                              padded row, g = x Wg^T in columns [0, f) and u = x Wu^T in [f, 2f), as the fp32
+                              accumulators hold them, for a backward call that takes them (moe_bwd_args.gu) instead of
+                              recomputing that GEMM; rows of no real row are not written.  NULL: not stored */
 } moe_overlap_cfg;
 
 /* Last host-side error message of the calling thread ("" if none). */
