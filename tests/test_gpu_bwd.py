@@ -281,10 +281,13 @@ def test_backward_full_size(name):
 def test_backward_ordering_stress():
     """Publish/acquire ordering of the backward launch under stress (the page's "What would settle it", as for the
     forward): 300 overlapped calls on a split-K shape over consumer partitions {none, 1, 2, 4, 8, 16, 32} and shuffled
-    epochs; every call's dx, weight gradients and returned dX rows equal the sequential call's bit for bit.  Stops at
-    the first mismatch (and names the call)."""
+    epochs, every other call taking the forward's stored g | u (whose h / dG / dU items then publish as soon as dH
+    is in); every call's dx, weight gradients and returned dX rows equal the sequential recomputing call's bit for
+    bit.  Stops at the first mismatch (and names the call)."""
     s = BWD_SMALL[3]
     run = BwdRun(s)
+    gu = run.P.gu_buffer()
+    run.P.ffn(run.dev["w_gate_up"], run.dev["w_down"], mode=0, gu_out=gu)
     b = run.backward(mode=1)
     keys = ("dx", "dw_route", "dw_gate_up", "dw_down")
     ref = {k: b[k].clone() for k in keys}
@@ -297,11 +300,12 @@ def test_backward_ordering_stress():
         while ep == last:  # shuffled, but never the value the flags hold from the previous call
             ep = int(rng.integers(1, 1 << 31))
         last = ep
-        b = run.backward(mode=0, consumer_cus=cus, epoch=ep)
+        b = run.backward(mode=0, consumer_cus=cus, epoch=ep, gu=gu if it % 2 else None)
         for k in keys:
             if not torch.equal(b[k].view(torch.int32 if b[k].element_size() == 4 else torch.int16),
                                ref[k].view(torch.int32 if ref[k].element_size() == 4 else torch.int16)):
-                raise AssertionError("call %d (consumer_cus %d, epoch %d): %s differs" % (it, cus, ep, k))
+                raise AssertionError("call %d (consumer_cus %d, epoch %d, stored g | u %s): %s differs"
+                                     % (it, cus, ep, bool(it % 2), k))
         for r in range(s.R):
             got = b["dx_recv"][r][: ref_recv[r].shape[0]]
             if not torch.equal(got.view(torch.int16), ref_recv[r].view(torch.int16)):
