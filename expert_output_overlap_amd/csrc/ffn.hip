@@ -674,24 +674,22 @@ __device__ __forceinline__ bool ffn_tile(const FusedArgs& a, unsigned char* smem
   if constexpr (GLU) {
     if (a.gu != nullptr) {
       // the pre-activations g | u of the real rows, fp32, for a backward call that takes them instead of
-      // recomputing this GEMM: each group of four accumulator rows q4 is transposed inside its quad of lanes, after
-      // which lane l holds row 8 q4 + 4 (l / 32) + l % 4 of the block at the four consecutive columns from
-      // 4 ((l % 32) / 4), so one wave store writes eight rows of 128 bytes
+      // recomputing this GEMM.  Accumulator element q of a lane is row 8 (q / 4) + 4 (lane / 32) + q % 4 of the
+      // block at column lane % 32, so for each q the 4-byte stores of lanes 0-31 and of lanes 32-63 each write 128
+      // consecutive bytes of one row: no transpose needed (a DPP quad transpose and 16-byte stores made this part
+      // of the epilogue ~25% longer).  The stores stream past the caches (nontemporal): nothing reads them in this
+      // launch, and cached they would push the GEMMs' operand tiles out of L2.
       const int64_t ld = 2 * (int64_t)a.f;
-      const int col = nt * (BN / 2) + wn * 32 + 4 * ((lane_e & 31) >> 2);
+      const int col = nt * (BN / 2) + wn * 32 + (lane_e & 31);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x16_t& g = acc[mi][0];
-          const f32x16_t& u = acc[mi][1];
-          const f32x4_t gq = quad_transpose(f32x4_t{g[4 * q4], g[4 * q4 + 1], g[4 * q4 + 2], g[4 * q4 + 3]}, lane_e);
-          const f32x4_t uq = quad_transpose(f32x4_t{u[4 * q4], u[4 * q4 + 1], u[4 * q4 + 2], u[4 * q4 + 3]}, lane_e);
-          const int r = wm * WM + mi * 32 + 8 * q4 + 4 * (lane_e >> 5) + (lane_e & 3);
+        for (int q = 0; q < 16; ++q) {
+          const int r = wm * WM + mi * 32 + 8 * (q >> 2) + 4 * (lane_e >> 5) + (q & 3);
           if (r < n_rows) {
             float* row = a.gu + (int64_t)s_rows[r] * ld;
-            *(f32x4_t*)(row + col) = gq;
-            *(f32x4_t*)(row + a.f + col) = uq;
+            __builtin_nontemporal_store(acc[mi][0][q], &row[col]);
+            __builtin_nontemporal_store(acc[mi][1][q], &row[a.f + col]);
           }
           __builtin_amdgcn_sched_barrier(0);  // one row group at a time
         }
