@@ -277,3 +277,35 @@ def test_landing_rejected_where_it_does_not_apply():
         rc = B.lib().moe_expert_ffn_overlap(ctypes.byref(s), ctypes.byref(L), p, p, p, p, p, recv, p,
                                             ctypes.byref(cfg), None)
         assert rc == B.MOE_EINVAL and "x_tokens" in B.moe_last_error(), (dtype, mode, B.moe_last_error())
+
+
+def test_preactivation_store_rejected_where_the_backward_cannot_take_it():
+    """The forward stores g | u (cfg.gu_out) for bf16 shapes with f a multiple of 128 in modes 0, 1 and 3 only, and
+    the backward takes them through its argument struct, not its cfg; both calls reject the rest before any device
+    work."""
+    fake = np.zeros(64, np.uint64)  # never dereferenced: the calls fail their checks first
+    p = ctypes.c_void_p(fake.ctypes.data)
+    for dtype, f, mode in ((B.MOE_F32, 512, 0), (B.MOE_BF16, 192, 0), (B.MOE_BF16, 512, 2)):
+        s = shape(dtype=dtype, d=256, f=f)
+        nbytes = B.moe_layout_workspace_bytes(s)
+        buf = np.zeros(nbytes + 256, np.uint8)
+        base = (buf.ctypes.data + 255) // 256 * 256
+        L = B.moe_layout()
+        assert B.lib().moe_layout_bind(ctypes.byref(s), ctypes.c_void_p(base), nbytes, ctypes.byref(L)) == 0
+        recv = (ctypes.c_void_p * s.R)(*([fake.ctypes.data] * s.R))
+        cfg = B.moe_overlap_cfg(4, mode, 1, 0, 0, None, 0, None, fake.ctypes.data)
+        rc = B.lib().moe_expert_ffn_overlap(ctypes.byref(s), ctypes.byref(L), p, p, p, p, p, recv, p,
+                                            ctypes.byref(cfg), None)
+        assert rc == B.MOE_EINVAL and "gu_out" in B.moe_last_error(), (dtype, f, mode, B.moe_last_error())
+    s = shape(d=256, f=512)
+    nbytes = B.moe_layout_workspace_bytes(s)
+    buf = np.zeros(nbytes + 256, np.uint8)
+    base = (buf.ctypes.data + 255) // 256 * 256
+    L = B.moe_layout()
+    assert B.lib().moe_layout_bind(ctypes.byref(s), ctypes.c_void_p(base), nbytes, ctypes.byref(L)) == 0
+    recv = (ctypes.c_void_p * s.R)(*([fake.ctypes.data] * s.R))
+    args = B.moe_bwd_args(**{k: (ctypes.cast(recv, ctypes.c_void_p) if k == "dx_recv" else p) for k in B.BWD_FIELDS})
+    cfg = B.moe_overlap_cfg(0, 0, 1, 0, 0, None, 0, None, fake.ctypes.data)
+    rc = B.lib().moe_expert_ffn_backward(ctypes.byref(s), ctypes.byref(L), ctypes.byref(args), p, ctypes.byref(cfg),
+                                         None)
+    assert rc == B.MOE_EINVAL and "gu_out" in B.moe_last_error(), B.moe_last_error()
