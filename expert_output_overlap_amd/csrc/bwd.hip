@@ -565,7 +565,7 @@ __device__ __forceinline__ bool bwd_tile(const BwdArgs& a, unsigned char* smem, 
   const int out_rows = KIND == BK_WD ? d : 2 * f, out_cols = KIND == BK_WD ? f : d;
   // straight from the accumulators: for each element q, the 4-byte stores of lanes 0-31 and of lanes 32-63 each
   // write 128 consecutive bytes of one row (the quad transpose and 16-byte stores took the DeepSeek-V3-shaped
-  // backward 3.6% longer; streaming these stores past the caches won 2% more there and lost 5% with skewed routing)
+  // backward 3.6% longer; streaming these stores past the caches made no difference on six workloads)
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
