@@ -365,7 +365,7 @@ int ffn_dma(const moe_shape* s, const moe_layout* L, FfnLaunch& p, int n_cu, int
   int n1, n2, S;
   ffn_list_dims(s->d, s->f, &n1, &n2, &S);
   const int W = p.band_window > 0 ? p.band_window : 4;
-  const FfnList Lst = ffn_list_make(n_mt, p.tile_order == 0 ? n_rem : n_mt, n1, n2, S, W, 0, 0, n_cu, false, false);
+  const FfnList Lst = ffn_list_make(n_mt, p.tile_order == 0 ? n_rem : n_mt, n1, n2, S, W, 0, 0, n_cu, false);
   const int64_t g1 = (int64_t)n_mt * n1;
   const int nw = (n_mt + W - 1) / W, K = std::min(4, nw);
   auto wstart = [&](int w) { return g1 + (int64_t)std::min(w * W, n_mt) * n2 * S; };

@@ -925,7 +925,7 @@ __global__ __launch_bounds__(FFN_THREADS, 1) void k_ffn_bf16(FusedArgs a) {
   // the item list (item_list.h): the consumers' share of GEMM1 items, the producers' round-robin share, and the
   // half-width items of a last round at most half full
   const FfnList L = ffn_list_make(n_mt, a.mt_order ? a.scalars[a.sc_nmt + 1] : n_mt, a.n_nt1, a.n_nt2, a.S, a.window,
-                                  interleave, C, G, BN2 >= 128 && a.halves, a.halves);
+                                  interleave, C, G, BN2 >= 128 && a.halves);
   auto run_of = [&](int mt, int* r0, int* rc) {
     const int32_t* d = a.mtile_desc + (int64_t)mt * MOE_MT_FIELDS;
     *r0 = d[2];
@@ -971,22 +971,18 @@ __global__ __launch_bounds__(FFN_THREADS, 1) void k_ffn_bf16(FusedArgs a) {
     return false;
   };
   // Producer workgroups move through the list in step, a run of consecutive items on one XCD, whose workgroups share
-  // operand tiles in its L2.  The workgroups that take one more first-GEMM item (each ~d / (f / S) second-GEMM
-  // items long) skip slots after the GEMM1 part, so that the others take the second-GEMM items there and end about
-  // one such item ahead, room for the return (ffn_list_make; DeepSeek-V3-like step 2.42 -> 2.33 ms; also skipping
-  // that last item's slot: 2.34).  Two other ways of balancing the end were measured and dropped: taking items (or
-  // XCD-sized runs of them) from counters at run time costs 4-16% in claim latency and lost L2 sharing; handing runs
-  // to the XCDs by a cost model shortened the producers' span by 6%, but left no workgroup early for the return,
-  // which then ran exposed at the end: no faster overall.
-  int u0, u1, step;
-  ffn_list_range(L, (int)blockIdx.x, &u0, &u1, &step);
-  // this launch's chunk of the list (a chunked list skips no slot: slot u is list index u)
-  if (a.item_begin > u0) u0 += (a.item_begin - u0 + step - 1) / step * step;
-  u1 = min(u1, a.item_end);
-  for (int u = u0; u < u1; u += step) {
-    const int item = ffn_list_index(L, u);
-    if (item >= 0 && !run(item)) return;
-  }
+  // operand tiles in its L2.  Two ways of balancing the end were measured and dropped: taking items (or XCD-sized
+  // runs of them) from counters at run time costs 4-16% in claim latency and lost L2 sharing; handing runs to the
+  // XCDs by a cost model shortens the producers' span (the round-robin leaves the workgroups that take one more
+  // first-GEMM item, each ~d / (f / S) second-GEMM items long, behind at the end) by 6% on the DeepSeek-V3-like
+  // shard, but the workgroups that finish early under the round-robin are the ones that run the return while the
+  // others finish, and with the producers balanced that return is exposed: no faster overall.
+  int i0, i1, step;
+  ffn_list_range(L, (int)blockIdx.x, &i0, &i1, &step);
+  if (a.item_begin > i0) i0 += (a.item_begin - i0 + step - 1) / step * step;  // this launch's chunk of the list
+  i1 = min(i1, a.item_end);
+  for (int item = i0; item < i1; item += step)
+    if (!run(item)) return;
   __syncthreads();
   flush();
   // the consumer workgroups, done with their share of first-GEMM items (none when interleaved), land the token
@@ -1208,7 +1204,7 @@ int ffn_schedule_host(int d, int f, int E, int n_cons, int n_producers, int band
   const int n_nt1 = f / (bn1 / 2), n_nt2 = d / bn2, S = ffn_splits(MOE_BF16, d, f);
   const int W = band_window > 0 ? band_window : 4;
   const FfnList L = ffn_list_make(n_mt, n_rem, n_nt1, n_nt2, S, W, ffn_interleave(n_cons, d, f, E), n_cons,
-                                  n_producers, bn2 >= 128, true);
+                                  n_producers, bn2 >= 128);
   *n_out = L.n_list;
   if (cap < L.n_list) return -1;
   auto run_of = [&](int mt, int* r0, int* rc) {
@@ -1229,13 +1225,10 @@ int ffn_schedule_host(int d, int f, int E, int n_cons, int n_producers, int band
     o[7] = it.target;
   };
   for (int b = 0; b < n_cons + n_producers; ++b) {
-    int u0, u1, step;
-    ffn_list_range(L, b, &u0, &u1, &step);
+    int i0, i1, step;
+    ffn_list_range(L, b, &i0, &i1, &step);
     int seq = 0;
-    for (int u = u0; u < u1; u += step) {
-      const int idx = ffn_list_index(L, u);
-      if (idx >= 0) put(idx, b, seq++);
-    }
+    for (int idx = i0; idx < i1; idx += step, ++seq) put(idx, b, seq);
   }
   return 0;
 }

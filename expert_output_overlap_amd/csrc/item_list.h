@@ -18,11 +18,10 @@
 //    row tile.
 // In both, every GEMM2 item follows the GEMM1 items it reads, and the last split of a y tile follows its others.
 // Workgroups: the first C run the consumer role and first take kc GEMM1 items each from the head of the list; the
-// G producer workgroups take the rest round-robin by slot, producer b taking slots C kc + b', C kc + b' + G, ...
-// with b' remapped so that a run of consecutive items goes to one XCD (workgroup b sits on XCD b % 8); a slot is a
-// list index, except that the workgroups with one GEMM1 item more than the others skip a few slots after the GEMM1
-// part (ffn_list_make).  When the producers' last round is at most half full and holds only GEMM2 items, each of
-// its items becomes two half-width items (list indices >= i_tail, two per item).
+// G producer workgroups take the rest round-robin, producer b taking items C kc + b', C kc + b' + G, ... with b'
+// remapped so that a run of consecutive items goes to one XCD (workgroup b sits on XCD b % 8).  When the producers'
+// last round is at most half full and holds only GEMM2 items, each of its items becomes two half-width items
+// (list indices >= i_tail, two per item).
 #pragma once
 
 #include <stdint.h>
@@ -36,7 +35,6 @@ struct FfnList {
   int n_rem;                                 // positions [0, n_rem) hold the row tiles with another owner's rows
   int C, G;                                  // consumer and producer workgroups
   int n_items, kc, i_tail, n_list;           // items, consumers' GEMM1 share, first half item, list length
-  int hb, hh, hr;                            // slot rounds [hb, hb + hr) of the producers' part skip their first hh
 };
 
 // Interleave when the return is large next to the FFN and re-streaming weights is cheap.  At about 45 GB/s of copy
@@ -52,7 +50,7 @@ MOE_HD int ffn_interleave(int n_cons, int d, int f, int E) {
 }
 
 MOE_HD FfnList ffn_list_make(int n_mt, int n_rem, int n_nt1, int n_nt2, int S, int W, int interleave, int C, int G,
-                             bool halves, bool balance) {
+                             bool halves) {
   FfnList L;
   L.n_mt = n_mt;
   L.n_rem = n_rem;
@@ -77,29 +75,10 @@ MOE_HD FfnList ffn_list_make(int n_mt, int n_rem, int n_nt1, int n_nt2, int S, i
   // The producers' last round holds q items.  When they are GEMM2 items and at most half a round, each becomes two
   // items of half the tile width, so that the round keeps twice as many CUs busy (a half-width tile takes ~0.7 of
   // a full one's time).  Every output element is accumulated as before, so results do not change.
-  // Round-robin slots: producer slot u (list index C kc + u, before any skipped slot) is workgroup u % G's.  When
-  // the GEMM1 items fill their last round only in part, its first hh workgroups run one GEMM1 item more than the
-  // others, ~(4 n_nt2 + 4) / (2 n_nt1 / S + 4) GEMM2 items long (k-tiles, plus about four k-tiles' time for the
-  // epilogue), and end the launch behind them.  Those workgroups therefore skip their slots in the hr slot rounds
-  // after the GEMM1 part (the slots are not list items: the list indices after them move down), so the others take
-  // the GEMM2 items there.  The others keep about one GEMM2 item of slack, where they return rows before the
-  // launch ends.  Each workgroup still runs its items in list order, so every wait still ends.
-  L.hb = L.hh = L.hr = 0;
-  const int n1p = n_mt * n_nt1 - C * L.kc, np0 = L.n_items - C * L.kc;
-  if (balance && interleave == 0 && n1p > 0 && n1p % G != 0) {
-    const int hh = n1p % G, hb = n1p / G + 1, c2 = 2 * n_nt1 / S + 4;
-    int hr = (4 * n_nt2 + 4 + c2 / 2) / c2 - 2;
-    while (hr > 0 && np0 + hr * hh <= (hb + hr) * G) --hr;  // the last round comes after the skipped slots
-    if (hr > 0) {
-      L.hb = hb;
-      L.hh = hh;
-      L.hr = hr;
-    }
-  }
   L.i_tail = L.n_items;
   L.n_list = L.n_items;
   if (halves && L.n_items > C * L.kc) {
-    const int np = L.n_items - C * L.kc + L.hh * L.hr, q = np - (np - 1) / G * G;
+    const int np = L.n_items - C * L.kc, q = np - (np - 1) / G * G;
     const int nw = (n_mt + W - 1) / W, Wl = n_mt - (nw - 1) * W;
     const int g2_tail = interleave == 0 ? n_mt * n_nt2 * S : (Wl + (nw > 1 ? W : 0)) * n_nt2 * S;
     if (2 * q <= G && q <= g2_tail) {
@@ -110,28 +89,19 @@ MOE_HD FfnList ffn_list_make(int n_mt, int n_rem, int n_nt1, int n_nt2, int S, i
   return L;
 }
 
-// The slots workgroup `block` runs: u0, u0 + step, ... while < u1; ffn_list_index maps a slot to its list index.
-MOE_HD void ffn_list_range(const FfnList& L, int block, int* u0, int* u1, int* step) {
+// The list indices workgroup `block` runs: i0, i0 + step, ... while < i1.
+MOE_HD void ffn_list_range(const FfnList& L, int block, int* i0, int* i1, int* step) {
   if (block < L.C) {
-    *u0 = block * L.kc;
-    *u1 = *u0 + L.kc;
+    *i0 = block * L.kc;
+    *i1 = *i0 + L.kc;
     *step = 1;
     return;
   }
   int bid = block - L.C;
   if ((L.G & 7) == 0 && (L.C & 7) == 0) bid = (bid & 7) * (L.G >> 3) + (bid >> 3);
-  *u0 = L.C * L.kc + bid;
-  *u1 = L.n_list + L.hh * L.hr;
+  *i0 = L.C * L.kc + bid;
+  *i1 = L.n_list;
   *step = L.G;
-}
-
-// The list index of slot u, -1 for a skipped slot.
-MOE_HD int ffn_list_index(const FfnList& L, int u) {
-  const int base = L.C * L.kc;
-  if (L.hr == 0 || u < base + L.hb * L.G) return u;
-  const int j = (u - base) / L.G, l = u - base - j * L.G;
-  if (j < L.hb + L.hr) return l < L.hh ? -1 : u - L.hh * (j - L.hb + 1);
-  return u - L.hh * L.hr;
 }
 
 struct FfnItem {
@@ -257,10 +227,7 @@ MOE_HD FfnItem ffn_list_item(const FfnList& L, int idx, RunOf run_of, OrderOf or
 // round-robin leaves anyway: when the first-GEMM items (n_g1, each 2 x 256 x 256 x d flops) fill their last round only
 // in part, the workgroups without one run a whole first-GEMM item ahead of the others, and each takes copy units once
 // its own items are done, so a return that those workgroups finish within one first-GEMM item's time runs behind the
-// others' GEMM at no cost, and every CU produces.  (Where a first-GEMM item is several second-GEMM items long, the
-// list hands those workgroups second-GEMM items in that time but one (ffn_list_make), and the rest of the return runs
-// at the launch's tail on every CU: the DeepSeek-V3-like shard's step 2.39 ms so, 2.50-2.52 ms with 8 to 24
-// consumer CUs.)  On one device the return is a copy in HBM, at up to
+// others' GEMM at no cost, and every CU produces.  On one device the return is a copy in HBM, at up to
 // MOE_TAIL_COPY_RATE over the chip or the free CUs' copy rate if lower.  Measured: the DeepSeek-V3-like and
 // Mixtral-like shards run 1-4% faster with the return hidden this way than with the best partition (100% of the copy
 // inside the producers' span); with d = f = 4096 and one or two experts the first-GEMM rounds are full, the copy
