@@ -301,8 +301,9 @@ def main():
     ap.add_argument("--mode", type=int, default=0, choices=(0, 1, 3),
                     help="FFN mode of the timed steps: 0 overlapped, 1 sequential (the consumer alone after the "
                          "producer, for profiling the copy), 3 the return on the DMA engines")
-    ap.add_argument("--backward", type=int, default=1, choices=(0, 1),
-                    help="1 (default, bf16): also time the layer's backward pass after the forward steps")
+    ap.add_argument("--backward", type=int, default=1, choices=(0, 1, 2),
+                    help="1 (default, bf16): also time the layer's backward pass after the forward steps; 2: with "
+                         "--kernels-only, the backward calls take the forward's stored pre-activations")
     ap.add_argument("--land", type=int, default=1, choices=(0, 1),
                     help="where x_pad's token rows come from: 1 (default) the FFN launch lands them itself, row tile "
                          "by row tile, while its first GEMM starts; 0 the layout's gather kernel")
@@ -372,11 +373,16 @@ def main():
         if args.backward and s.dtype == "bf16":  # the backward calls too, for profiles of their kernels
             d_out = to_device(mi.d_out(s), s.dtype)
             P.bwd_buffers()
+            gu = None
+            if args.backward == 2:  # one forward call that stores g | u, which every backward call then reads
+                gu = P.gu_buffer()
+                P.ffn(w1, w2, mode=0, consumer_cus=cus, band_window=args.band_window,
+                      x_tokens=dev["x"] if land else None, gu_out=gu)
             for i in range(args.warmup + args.steps):
                 if i == args.warmup:
                     torch.cuda.synchronize()
                     t0 = time.perf_counter()
-                P.backward(d_out, w1, w2, mode=0)
+                P.backward(d_out, w1, w2, mode=0, gu=gu)
                 P.combine_backward(d_out)
             torch.cuda.synchronize()
             assert P.status() == B.MOE_OK
